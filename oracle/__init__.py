@@ -1,0 +1,184 @@
+"""fp64 CPU oracle of the causal dot product -- TEST INFRASTRUCTURE ONLY.
+
+Only the tests, the smoke check in ``__graft_entry__`` and the CPU-baseline leg
+of ``bench.py`` may import this package.  The product library
+(``prefix_sum_causal_amd``) never imports it and shares no code with it.
+
+The arithmetic lives in ``oracle.c`` (plain C, double precision, compiled with
+gcc).  This module only builds that file, marshals numpy arrays to it and
+defines the error metric the parity tests use.
+
+Method (causal dot product of "Transformers are RNNs", Algorithm 1, as named in
+the opening post of "Dot Product Computes Wrong Values", triton-lang/triton
+issue 217): per (n, h) slice, S_i = S_{i-1} + k_i v_i^T and out_i = q_i^T S_i,
+inclusive of token i (the state is updated before the row is read in the loop
+excerpt later on that page).  The normalised form divides by
+phi(q_i) . sum_{j<=i} phi(k_j) + eps with phi = elu + 1.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import tempfile
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "oracle.c")
+LIB = os.path.join(HERE, "liboracle.so")
+
+_f32p = ctypes.POINTER(ctypes.c_float)
+_f64p = ctypes.POINTER(ctypes.c_double)
+_i64 = ctypes.c_int64
+
+
+def build(src: str = SRC, out: str = LIB) -> str:
+    """Compile ``src`` into the shared library ``out`` with gcc (portable -O2,
+    no host-specific instruction set, so the library runs on any x86-64 host)."""
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-std=c99", "-O2", "-fPIC", "-shared", "-fopenmp", src, "-o", tmp, "-lm"]
+    subprocess.check_call(cmd)
+    os.replace(tmp, out)
+    return out
+
+
+def _as_f32(x) -> np.ndarray:
+    a = np.ascontiguousarray(x, dtype=np.float32)
+    return a
+
+
+def _ptr32(a: np.ndarray):
+    return a.ctypes.data_as(_f32p)
+
+
+def _ptr64(a: np.ndarray):
+    return a.ctypes.data_as(_f64p)
+
+
+class Oracle:
+    """ctypes front end of one compiled copy of ``oracle.c``."""
+
+    def __init__(self, libpath: str = LIB):
+        self.lib = ctypes.CDLL(libpath)
+        four = [_f32p, _f32p, _f32p, _f64p, _i64, _i64, _i64, _i64]
+        for name in ("oracle_fwd", "oracle_fwd_brute"):
+            fn = getattr(self.lib, name)
+            fn.argtypes = four
+            fn.restype = None
+        for name in ("oracle_linattn", "oracle_linattn_brute"):
+            fn = getattr(self.lib, name)
+            fn.argtypes = four + [ctypes.c_double, ctypes.c_int]
+            fn.restype = None
+        for name in ("oracle_bwd", "oracle_bwd_brute"):
+            fn = getattr(self.lib, name)
+            fn.argtypes = [_f32p] * 4 + [_f64p] * 3 + [_i64] * 4
+            fn.restype = None
+        self.lib.oracle_state.argtypes = [_f32p, _f32p, _f64p, _i64, _i64, _i64, _i64]
+        self.lib.oracle_state.restype = None
+        self.lib.oracle_num_threads.argtypes = []
+        self.lib.oracle_num_threads.restype = ctypes.c_int
+
+    # -- shape helpers -----------------------------------------------------
+    @staticmethod
+    def _dims(Q, V):
+        if Q.ndim < 2 or V.ndim != Q.ndim or Q.shape[:-1] != V.shape[:-1]:
+            raise ValueError("Q is [..., L, E] and V is [..., L, M] with equal leading dims")
+        L, E = Q.shape[-2:]
+        M = V.shape[-1]
+        NH = int(np.prod(Q.shape[:-2], dtype=np.int64)) if Q.ndim > 2 else 1
+        return NH, L, E, M
+
+    def num_threads(self) -> int:
+        return int(self.lib.oracle_num_threads())
+
+    # -- forward -------------------------------------------------------------
+    def _fwd_common(self, fn, Q, K, V, *extra):
+        Q, K, V = _as_f32(Q), _as_f32(K), _as_f32(V)
+        if K.shape != Q.shape:
+            raise ValueError("K must have Q's shape")
+        NH, L, E, M = self._dims(Q, V)
+        out = np.empty(V.shape, dtype=np.float64)
+        fn(_ptr32(Q), _ptr32(K), _ptr32(V), _ptr64(out), NH, L, E, M, *extra)
+        return out
+
+    def fwd(self, Q, K, V) -> np.ndarray:
+        """out_i = q_i^T S_i with S_i = sum_{j<=i} k_j v_j^T (O(L) recurrence)."""
+        return self._fwd_common(self.lib.oracle_fwd, Q, K, V)
+
+    def fwd_brute(self, Q, K, V) -> np.ndarray:
+        """out_i = sum_{j<=i} (q_i.k_j) v_j (O(L^2) masked brute force)."""
+        return self._fwd_common(self.lib.oracle_fwd_brute, Q, K, V)
+
+    def linattn(self, Q, K, V, eps: float = 1e-6, feature_map: int = 1) -> np.ndarray:
+        """Normalised causal linear attention (recurrence with running z)."""
+        return self._fwd_common(self.lib.oracle_linattn, Q, K, V, float(eps), int(feature_map))
+
+    def linattn_brute(self, Q, K, V, eps: float = 1e-6, feature_map: int = 1) -> np.ndarray:
+        """Normalised causal linear attention (masked brute force)."""
+        return self._fwd_common(self.lib.oracle_linattn_brute, Q, K, V, float(eps), int(feature_map))
+
+    # -- backward ------------------------------------------------------------
+    def _bwd_common(self, fn, Q, K, V, dO):
+        Q, K, V, dO = _as_f32(Q), _as_f32(K), _as_f32(V), _as_f32(dO)
+        if K.shape != Q.shape or dO.shape != V.shape:
+            raise ValueError("K must have Q's shape and dO V's shape")
+        NH, L, E, M = self._dims(Q, V)
+        dQ = np.empty(Q.shape, dtype=np.float64)
+        dK = np.empty(Q.shape, dtype=np.float64)
+        dV = np.empty(V.shape, dtype=np.float64)
+        fn(_ptr32(Q), _ptr32(K), _ptr32(V), _ptr32(dO), _ptr64(dQ), _ptr64(dK), _ptr64(dV),
+           NH, L, E, M)
+        return dQ, dK, dV
+
+    def bwd(self, Q, K, V, dO):
+        """(dQ, dK, dV) by a forward sweep of S and a reverse sweep of R."""
+        return self._bwd_common(self.lib.oracle_bwd, Q, K, V, dO)
+
+    def bwd_brute(self, Q, K, V, dO):
+        """(dQ, dK, dV) from the O(L^2) double sum."""
+        return self._bwd_common(self.lib.oracle_bwd_brute, Q, K, V, dO)
+
+    def state(self, K, V) -> np.ndarray:
+        """Final state sum_j k_j v_j^T per slice, shape [..., E, M]."""
+        K, V = _as_f32(K), _as_f32(V)
+        NH, L, E, M = self._dims(K, V)
+        S = np.empty(K.shape[:-2] + (E, M), dtype=np.float64)
+        self.lib.oracle_state(_ptr32(K), _ptr32(V), _ptr64(S), NH, L, E, M)
+        return S
+
+
+_DEFAULT: Oracle | None = None
+
+
+def default() -> Oracle:
+    """The oracle built from this directory's ``oracle.c`` (built on first use
+    when no library is present)."""
+    global _DEFAULT
+    if _DEFAULT is None:
+        if not os.path.exists(LIB):
+            build()
+        _DEFAULT = Oracle(LIB)
+    return _DEFAULT
+
+
+def build_variant(source_text: str, workdir: str | None = None) -> Oracle:
+    """Compile a modified copy of the oracle source (used by the tests that
+    plant mistakes in the oracle to show that the pins catch them)."""
+    d = workdir or tempfile.mkdtemp(prefix="oracle_variant_")
+    src = os.path.join(d, "variant.c")
+    with open(src, "w") as f:
+        f.write(source_text)
+    return Oracle(build(src, os.path.join(d, "libvariant.so")))
+
+
+def max_rel_err(x, ref) -> float:
+    """max |x - ref| / max |ref| over the whole tensor, in fp64 (the parity
+    metric; 0 when both are all zero)."""
+    x = np.asarray(x, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    num = float(np.max(np.abs(x - ref))) if x.size else 0.0
+    den = float(np.max(np.abs(ref))) if ref.size else 0.0
+    if den == 0.0:
+        return 0.0 if num == 0.0 else float("inf")
+    return num / den

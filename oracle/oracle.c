@@ -1,0 +1,249 @@
+/*
+ * oracle.c -- plain fp64 CPU oracle of the causal dot product of linear
+ * attention.  TEST INFRASTRUCTURE ONLY: tests, the smoke check and the
+ * CPU-baseline leg of the benchmark call it; the product library never links,
+ * loads or calls anything here, and nothing here is shared with the HIP code.
+ *
+ * Method.  The opening post of "Dot Product Computes Wrong Values"
+ * (github.com/triton-lang/triton issue 217) names the computation: the causal
+ * dot product of "Transformers are RNNs" (Algorithm 1), a batch-parallel O(n)
+ * for-loop computing a prefix sum.  Per (n, h) slice, with q_i, k_i in R^E and
+ * v_i in R^M:
+ *     S_i   = S_{i-1} + k_i v_i^T          (E x M running state, S_{-1} = 0)
+ *     out_i = q_i^T S_i                    (M-vector)
+ * The later comment on the same page with the author's loop excerpt adds the
+ * current row to the state before the output row is read, so the sum is
+ * inclusive: out_i = sum_{j<=i} (q_i . k_j) v_j.
+ *
+ * The normalised form (linear attention proper) divides by
+ *     den_i = phi(q_i) . z_i + eps,   z_i = sum_{j<=i} phi(k_j),
+ * with phi = elu + 1 (alpha = 1): phi(x) = x + 1 for x > 0, exp(x) otherwise.
+ *
+ * Layout: Q, K are [NH][L][E] and V, dO are [NH][L][M], row-major, contiguous,
+ * given as float (fp32 values, or bf16 values widened exactly to fp32).  All
+ * arithmetic is double precision.  Outputs are double arrays of the same
+ * shapes.  Every function loops over the NH slices independently (OpenMP over
+ * slices); within a slice the loops are the plain definitions below.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* phi = elu + 1 with alpha = 1 (the feature map of linear attention). */
+static double phi(double x) { return x > 0.0 ? x + 1.0 : exp(x); }
+
+/* ---------------------------------------------------------------------------
+ * Forward, O(L E M) recurrence: S += k_i v_i^T, then out_i = q_i^T S.
+ * ------------------------------------------------------------------------- */
+void oracle_fwd(const float *Q, const float *K, const float *V, double *Out,
+                int64_t NH, int64_t L, int64_t E, int64_t M) {
+#pragma omp parallel for schedule(static)
+    for (int64_t s = 0; s < NH; ++s) {
+        const float *q = Q + s * L * E, *k = K + s * L * E, *v = V + s * L * M;
+        double *out = Out + s * L * M;
+        double *S = (double *)calloc((size_t)(E * M), sizeof(double));
+        for (int64_t i = 0; i < L; ++i) {
+            for (int64_t e = 0; e < E; ++e)
+                for (int64_t m = 0; m < M; ++m)
+                    S[e * M + m] += (double)k[i * E + e] * (double)v[i * M + m];
+            for (int64_t m = 0; m < M; ++m) {
+                double acc = 0.0;
+                for (int64_t e = 0; e < E; ++e) acc += (double)q[i * E + e] * S[e * M + m];
+                out[i * M + m] = acc;
+            }
+        }
+        free(S);
+    }
+}
+
+/* ---------------------------------------------------------------------------
+ * Forward, O(L^2 (E + M)) masked brute force: out_i = sum_{j<=i} (q_i.k_j) v_j.
+ * ------------------------------------------------------------------------- */
+void oracle_fwd_brute(const float *Q, const float *K, const float *V, double *Out,
+                      int64_t NH, int64_t L, int64_t E, int64_t M) {
+#pragma omp parallel for schedule(static)
+    for (int64_t s = 0; s < NH; ++s) {
+        const float *q = Q + s * L * E, *k = K + s * L * E, *v = V + s * L * M;
+        double *out = Out + s * L * M;
+        for (int64_t i = 0; i < L; ++i) {
+            for (int64_t m = 0; m < M; ++m) out[i * M + m] = 0.0;
+            for (int64_t j = 0; j <= i; ++j) {
+                double a = 0.0;
+                for (int64_t e = 0; e < E; ++e) a += (double)q[i * E + e] * (double)k[j * E + e];
+                for (int64_t m = 0; m < M; ++m) out[i * M + m] += a * (double)v[j * M + m];
+            }
+        }
+    }
+}
+
+/* ---------------------------------------------------------------------------
+ * Normalised forward, recurrence.  feature_map = 1 applies phi to the raw Q, K
+ * values; feature_map = 0 uses Q, K as given.
+ *   S += phi(k_i) v_i^T;  z += phi(k_i);
+ *   out_i = (phi(q_i)^T S) / (phi(q_i) . z + eps)
+ * ------------------------------------------------------------------------- */
+void oracle_linattn(const float *Q, const float *K, const float *V, double *Out,
+                    int64_t NH, int64_t L, int64_t E, int64_t M, double eps,
+                    int feature_map) {
+#pragma omp parallel for schedule(static)
+    for (int64_t s = 0; s < NH; ++s) {
+        const float *q = Q + s * L * E, *k = K + s * L * E, *v = V + s * L * M;
+        double *out = Out + s * L * M;
+        double *S = (double *)calloc((size_t)(E * M), sizeof(double));
+        double *z = (double *)calloc((size_t)E, sizeof(double));
+        double *fq = (double *)malloc((size_t)E * sizeof(double));
+        double *fk = (double *)malloc((size_t)E * sizeof(double));
+        for (int64_t i = 0; i < L; ++i) {
+            for (int64_t e = 0; e < E; ++e) {
+                fq[e] = feature_map ? phi((double)q[i * E + e]) : (double)q[i * E + e];
+                fk[e] = feature_map ? phi((double)k[i * E + e]) : (double)k[i * E + e];
+            }
+            for (int64_t e = 0; e < E; ++e) {
+                z[e] += fk[e];
+                for (int64_t m = 0; m < M; ++m) S[e * M + m] += fk[e] * (double)v[i * M + m];
+            }
+            double den = eps;
+            for (int64_t e = 0; e < E; ++e) den += fq[e] * z[e];
+            for (int64_t m = 0; m < M; ++m) {
+                double num = 0.0;
+                for (int64_t e = 0; e < E; ++e) num += fq[e] * S[e * M + m];
+                out[i * M + m] = num / den;
+            }
+        }
+        free(S); free(z); free(fq); free(fk);
+    }
+}
+
+/* ---------------------------------------------------------------------------
+ * Normalised forward, brute force:
+ *   out_i = sum_{j<=i} a_ij v_j / (sum_{j<=i} a_ij + eps),  a_ij = phi(q_i).phi(k_j)
+ * ------------------------------------------------------------------------- */
+void oracle_linattn_brute(const float *Q, const float *K, const float *V, double *Out,
+                          int64_t NH, int64_t L, int64_t E, int64_t M, double eps,
+                          int feature_map) {
+#pragma omp parallel for schedule(static)
+    for (int64_t s = 0; s < NH; ++s) {
+        const float *q = Q + s * L * E, *k = K + s * L * E, *v = V + s * L * M;
+        double *out = Out + s * L * M;
+        for (int64_t i = 0; i < L; ++i) {
+            double den = eps;
+            for (int64_t m = 0; m < M; ++m) out[i * M + m] = 0.0;
+            for (int64_t j = 0; j <= i; ++j) {
+                double a = 0.0;
+                for (int64_t e = 0; e < E; ++e) {
+                    double fq = feature_map ? phi((double)q[i * E + e]) : (double)q[i * E + e];
+                    double fk = feature_map ? phi((double)k[j * E + e]) : (double)k[j * E + e];
+                    a += fq * fk;
+                }
+                den += a;
+                for (int64_t m = 0; m < M; ++m) out[i * M + m] += a * (double)v[j * M + m];
+            }
+            for (int64_t m = 0; m < M; ++m) out[i * M + m] /= den;
+        }
+    }
+}
+
+/* ---------------------------------------------------------------------------
+ * Backward of out = causal_product(Q, K, V) for an upstream gradient dO,
+ * i.e. the gradient of f = sum_i sum_{j<=i} (q_i.k_j)(v_j.dO_i).
+ * Forward sweep:  S += k_i v_i^T;  dq_i = S dO_i.
+ * Reverse sweep:  R += q_i dO_i^T (i descending);  dk_i = R v_i;  dv_i = R^T k_i.
+ * ------------------------------------------------------------------------- */
+void oracle_bwd(const float *Q, const float *K, const float *V, const float *dO,
+                double *dQ, double *dK, double *dV,
+                int64_t NH, int64_t L, int64_t E, int64_t M) {
+#pragma omp parallel for schedule(static)
+    for (int64_t s = 0; s < NH; ++s) {
+        const float *q = Q + s * L * E, *k = K + s * L * E, *v = V + s * L * M;
+        const float *go = dO + s * L * M;
+        double *dq = dQ + s * L * E, *dk = dK + s * L * E, *dv = dV + s * L * M;
+        double *S = (double *)calloc((size_t)(E * M), sizeof(double));
+        for (int64_t i = 0; i < L; ++i) {
+            for (int64_t e = 0; e < E; ++e)
+                for (int64_t m = 0; m < M; ++m)
+                    S[e * M + m] += (double)k[i * E + e] * (double)v[i * M + m];
+            for (int64_t e = 0; e < E; ++e) {
+                double acc = 0.0;
+                for (int64_t m = 0; m < M; ++m) acc += S[e * M + m] * (double)go[i * M + m];
+                dq[i * E + e] = acc;
+            }
+        }
+        memset(S, 0, (size_t)(E * M) * sizeof(double));
+        double *R = S;
+        for (int64_t i = L - 1; i >= 0; --i) {
+            for (int64_t e = 0; e < E; ++e)
+                for (int64_t m = 0; m < M; ++m)
+                    R[e * M + m] += (double)q[i * E + e] * (double)go[i * M + m];
+            for (int64_t e = 0; e < E; ++e) {
+                double acc = 0.0;
+                for (int64_t m = 0; m < M; ++m) acc += R[e * M + m] * (double)v[i * M + m];
+                dk[i * E + e] = acc;
+            }
+            for (int64_t m = 0; m < M; ++m) {
+                double acc = 0.0;
+                for (int64_t e = 0; e < E; ++e) acc += R[e * M + m] * (double)k[i * E + e];
+                dv[i * M + m] = acc;
+            }
+        }
+        free(S);
+    }
+}
+
+/* ---------------------------------------------------------------------------
+ * Backward, brute force from the double sum f = sum_i sum_{j<=i} (q_i.k_j)(v_j.dO_i):
+ *   dq_i = sum_{j<=i} (dO_i.v_j) k_j
+ *   dk_j = sum_{i>=j} (dO_i.v_j) q_i
+ *   dv_j = sum_{i>=j} (q_i.k_j) dO_i
+ * ------------------------------------------------------------------------- */
+void oracle_bwd_brute(const float *Q, const float *K, const float *V, const float *dO,
+                      double *dQ, double *dK, double *dV,
+                      int64_t NH, int64_t L, int64_t E, int64_t M) {
+#pragma omp parallel for schedule(static)
+    for (int64_t s = 0; s < NH; ++s) {
+        const float *q = Q + s * L * E, *k = K + s * L * E, *v = V + s * L * M;
+        const float *go = dO + s * L * M;
+        double *dq = dQ + s * L * E, *dk = dK + s * L * E, *dv = dV + s * L * M;
+        for (int64_t x = 0; x < L * E; ++x) { dq[x] = 0.0; dk[x] = 0.0; }
+        for (int64_t x = 0; x < L * M; ++x) dv[x] = 0.0;
+        for (int64_t i = 0; i < L; ++i) {
+            for (int64_t j = 0; j <= i; ++j) {
+                double gv = 0.0, qk = 0.0;
+                for (int64_t m = 0; m < M; ++m) gv += (double)go[i * M + m] * (double)v[j * M + m];
+                for (int64_t e = 0; e < E; ++e) qk += (double)q[i * E + e] * (double)k[j * E + e];
+                for (int64_t e = 0; e < E; ++e) {
+                    dq[i * E + e] += gv * (double)k[j * E + e];
+                    dk[j * E + e] += gv * (double)q[i * E + e];
+                }
+                for (int64_t m = 0; m < M; ++m) dv[j * M + m] += qk * (double)go[i * M + m];
+            }
+        }
+    }
+}
+
+/* Final running state S_{L-1} = sum_j k_j v_j^T of every slice, [NH][E][M]. */
+void oracle_state(const float *K, const float *V, double *S_out,
+                  int64_t NH, int64_t L, int64_t E, int64_t M) {
+#pragma omp parallel for schedule(static)
+    for (int64_t s = 0; s < NH; ++s) {
+        const float *k = K + s * L * E, *v = V + s * L * M;
+        double *S = S_out + s * E * M;
+        for (int64_t x = 0; x < E * M; ++x) S[x] = 0.0;
+        for (int64_t j = 0; j < L; ++j)
+            for (int64_t e = 0; e < E; ++e)
+                for (int64_t m = 0; m < M; ++m)
+                    S[e * M + m] += (double)k[j * E + e] * (double)v[j * M + m];
+    }
+}

@@ -1,0 +1,43 @@
+"""Seeded input generator: determinism, shapes, distributions, bf16 rounding."""
+import numpy as np
+import torch
+
+import workloads as W
+
+
+def test_round_bf16_matches_torch():
+    rng = np.random.default_rng(0)
+    x = np.concatenate([rng.standard_normal(10000).astype(np.float32) * 100,
+                        np.array([0.0, -0.0, 1.0, 1.00390625, 1.01171875, 3.3895314e38], np.float32)])
+    ours = W.round_bf16(x)
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float32).numpy()
+    assert np.array_equal(ours.view(np.uint32), ref.view(np.uint32))
+
+
+def test_generate_is_deterministic_and_shaped():
+    w = W.WORKLOADS["fwd_f32_l64_e16"]
+    a, b = W.generate(w), W.generate(w)
+    assert set(a) == {"Q", "K", "V"}
+    for k in a:
+        assert np.array_equal(a[k], b[k]) and a[k].dtype == np.float32
+    assert a["Q"].shape == (1, 1, 64, 16) and a["V"].shape == (1, 1, 64, 16)
+    assert (a["Q"] > 0).all() and (a["K"] > 0).all()
+
+
+def test_bf16_workload_values_are_bf16():
+    w = W.WORKLOADS["fwdbwd_bf16_l4096_e64"].with_shape(N=1, H=2, L=128)
+    d = W.generate(w)
+    assert set(d) == {"Q", "K", "V", "dO"}
+    for x in d.values():
+        assert np.array_equal(W.round_bf16(x), x)
+
+
+def test_raw_and_scaled_recipes():
+    w = W.WORKLOADS["linattn_bf16_l16384_e128"].with_shape(N=1, H=1, L=2048)
+    d = W.generate(w)
+    assert (d["Q"] < 0).any()  # raw N(0,1), feature map applied inside the op
+    w4 = W.WORKLOADS["fwdbwd_f32_l2048_e32_m128"].with_shape(N=1, H=2, L=4096)
+    d4 = W.generate(w4)
+    assert abs(float(d4["V"].std()) - 0.5) < 0.01 and abs(float(d4["dO"].std()) - 0.5) < 0.01
+    # E[elu(x)+1] for x ~ N(0,1) is 1.1605
+    assert abs(float(d4["Q"].mean()) - 1.1605) < 0.01
