@@ -1,0 +1,193 @@
+"""Throughput of the causal dot product on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--gpus 1]
+
+A step is one forward (writing the final state) plus one backward (reading
+it) over the whole batch of the workload, inputs resident in HBM.  W untimed
+steps, then K timed steps between device synchronisations.  Prints one JSON
+line with the whole-job tokens*heads/s, the roofline of the dominant kernel
+(algorithmic bytes per launch / average launch time, from HIP events on the
+stream the kernels run on) and the fp64 CPU oracle timed on a bounded sample
+of the same workload on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "causal-product fwd+bwd tokens·heads/s and % HBM/MFMA roofline, L=4096 E=M=64"
+UNIT = "tokens·heads/s"
+COUNTERS = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+KERNEL_SOURCES = ["cp_device.hpp", "cp_fwd.hpp", "cp_bwd.hpp", "cp_tune.hpp"]
+
+
+def kernel_digest() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "prefix_sum_causal_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(w, kind: str) -> int:
+    """Bytes a launch must move at minimum: read every input once, write every
+    output once (plus the fp32 final state passed from forward to backward)."""
+    s = 2 if w.dtype == "bf16" else 4
+    th = w.N * w.H * w.L
+    state = w.N * w.H * w.E * w.M * 4
+    if kind == "fwd":
+        return th * s * (2 * w.E + 2 * w.M) + state
+    if kind == "bwd":
+        return th * s * (4 * w.E + 3 * w.M) + state
+    if kind == "linattn":
+        return th * s * (2 * w.E + 2 * w.M)
+    raise ValueError(kind)
+
+
+def traffic_for(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources; else None."""
+    try:
+        with open(COUNTERS) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_digest") != kernel_digest():
+        return None
+    entry = rec.get("kernels", {}).get(f"{workload}:{kernel}")
+    return None if entry is None else entry.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, target_seconds: float = 15.0) -> dict:
+    """The fp64 oracle (forward recurrence + backward sweeps) on a bounded
+    sample of the workload's slices, scaled to tokens*heads/s."""
+    import numpy as np
+
+    import oracle
+    import workloads as W
+
+    orc = oracle.default()
+    threads = orc.num_threads()
+    ws = w.with_shape(N=1, H=threads)
+    d = W.generate(ws, need_do=True)
+    slices = 0
+    t0 = time.perf_counter()
+    while True:
+        if w.op == "linattn":
+            orc.linattn(d["Q"], d["K"], d["V"], 1e-6, 1)
+        else:
+            orc.fwd(d["Q"], d["K"], d["V"])
+            if w.op == "fwd+bwd":
+                orc.bwd(d["Q"], d["K"], d["V"], d["dO"])
+        slices += ws.H
+        el = time.perf_counter() - t0
+        if el >= target_seconds or slices >= w.N * w.H:
+            break
+    return {"value": slices * w.L / el, "unit": UNIT, "cores": threads, "kind": "oracle",
+            "sample": f"{slices} of {w.N * w.H} (n,h) slices at full L={w.L}, fp64 recurrence "
+                      f"({'fwd+bwd' if w.op == 'fwd+bwd' else w.op}), {el:.1f} s on {threads} threads"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the path shards over (n, h) slices "
+              "with no communication, so run it per GPU.", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import prefix_sum_causal_amd as cp
+    import workloads as W
+
+    name = args.workload or W.HEADLINE
+    w = W.WORKLOADS[name]
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    d = W.generate(w, need_do=(w.op == "fwd+bwd"))
+    dev = {k: torch.from_numpy(v).to("cuda").to(tdt) for k, v in d.items()}
+    del d
+    q, k, v = dev["Q"], dev["K"], dev["V"]
+    out = torch.empty_like(v)
+    state = torch.empty((w.N, w.H, w.E, w.M), device="cuda", dtype=torch.float32)
+    if w.op == "fwd+bwd":
+        g = dev["dO"]
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+
+    def step(evs=None):
+        if evs:
+            evs[0].record()
+        if w.op == "linattn":
+            cp.linear_attn_fwd(q, k, v, 1e-6, 1, out=out)
+        else:
+            cp.causal_product_fwd(q, k, v, out=out, state_out=state)
+        if evs:
+            evs[1].record()
+        if w.op == "fwd+bwd":
+            cp.causal_product_bwd(q, k, v, g, state_in=state, dq=dq, dk=dk, dv=dv)
+            if evs:
+                evs[2].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    t_first = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps * 1e-3
+    kinds = {"fwd+bwd": ["fwd", "bwd"], "fwd": ["fwd"], "linattn": ["linattn"]}[w.op]
+    times = {kinds[0]: t_first}
+    if w.op == "fwd+bwd":
+        times["bwd"] = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps * 1e-3
+    per_kernel = {}
+    for kind in kinds:
+        b = algorithmic_bytes(w, kind)
+        per_kernel[kind] = {"avg_us": times[kind] * 1e6, "alg_bytes": b, "GBps": b / times[kind] / 1e9}
+    dom = max(kinds, key=lambda k: times[k])
+    achieved = per_kernel[dom]["GBps"]
+    kernel_name = {"fwd": "cp_fwd_kernel", "bwd": "cp_bwd_kernel", "linattn": "cp_fwd_kernel"}[dom]
+    rec = {
+        "metric": METRIC,
+        "value": args.steps * w.token_heads / elapsed,
+        "unit": UNIT,
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": elapsed / args.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) draws; Q,K = elu(x)+1)",
+        "config": {"workload": name, "op": w.op, "N": w.N, "H": w.H, "L": w.L, "E": w.E, "M": w.M},
+        "roofline": {"bound": "hbm", "kernel": kernel_name, "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": traffic_for(dom, name)},
+        "kernels": per_kernel,
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

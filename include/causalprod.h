@@ -1,0 +1,119 @@
+/*
+ * causalprod.h -- C ABI of the MI355X (gfx950) causal dot product of linear
+ * attention.
+ *
+ * The operation is the causal dot product of "Transformers are RNNs",
+ * Algorithm 1, named in the opening post of "Dot Product Computes Wrong Values"
+ * (github.com/triton-lang/triton issue 217): a batch-parallel O(n) loop that
+ * keeps a running prefix sum of outer products.  For every (n, h) slice and
+ * token i = 0 .. L-1:
+ *
+ *     S_i   = S_{i-1} + k_i v_i^T        (E x M state, S_{-1} = 0)
+ *     out_i = q_i^T S_i                  (inclusive of token i)
+ *
+ * The inclusive order (state updated with row i before row i is read) is the
+ * order of the loop excerpt in a later comment on that page.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  * Tensors are contiguous and row-major: Q, K, dQ, dK are [N][H][L][E];
+ *    V, Out, dOut, dV are [N][H][L][M].  One element type per call (dtype):
+ *    CP_F32 (fp32 in and out) or CP_BF16 (bf16 in and out).  Arithmetic
+ *    accumulates in fp32 in both cases; results are rounded once to the I/O
+ *    type (round to nearest even).
+ *  * All tensor pointers are DEVICE pointers owned by the caller, 16-byte
+ *    aligned.  Outputs are fully overwritten (they need not be zeroed) and
+ *    must not overlap any input or each other.  The library keeps no pointer
+ *    after a call returns and allocates no device memory.
+ *  * stream is a hipStream_t (NULL = the default stream).  Calls only enqueue
+ *    work: they never synchronise the host, and buffers must stay alive until
+ *    the stream has run the work.  Calls are stateless, thread-safe and
+ *    deterministic (no atomics; the same inputs give the same bits).
+ *  * Supported head sizes: E, M in {16, 32, 64, 128}.  Any L >= 1.
+ *  * Errors are returned as cp_status values, never thrown.  Arguments are
+ *    validated before anything is enqueued, so a call that fails validation
+ *    has no side effect.  CP_ERR_HIP reports a failed kernel launch.
+ */
+#ifndef CAUSALPROD_H
+#define CAUSALPROD_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { CP_F32 = 0, CP_BF16 = 1 } cp_dtype;
+
+typedef enum {
+    CP_OK = 0,
+    CP_ERR_NULL = 1,        /* a required pointer is NULL                     */
+    CP_ERR_DIM = 2,         /* a size <= 0, L > 2^31-1, or a size overflow    */
+    CP_ERR_UNSUPPORTED = 3, /* E or M not in {16,32,64,128}, bad dtype/flag   */
+    CP_ERR_ALIGN = 4,       /* a pointer not 16-byte aligned                  */
+    CP_ERR_ALIAS = 5,       /* an output overlaps an input or another output  */
+    CP_ERR_HIP = 6          /* the HIP runtime reported an error at launch    */
+} cp_status;
+
+/*
+ * causal_product_fwd: Out[n][h][i] = sum_{j<=i} (Q_i . K_j) V_j for every
+ * slice, i.e. out_i = q_i^T S_i with S_i the inclusive prefix sum of k_j v_j^T
+ * (the recurrence above).  Q and K are used as given (a feature map, if any,
+ * is applied by the caller).
+ *
+ * state_out (optional, may be NULL): fp32 [N][H][E][M], receives the final
+ * state S_{L-1} = sum_j k_j v_j^T of every slice.  causal_product_bwd can
+ * take it to run its query gradient in the same reverse sweep as the key and
+ * value gradients.
+ */
+int causal_product_fwd(const void *Q, const void *K, const void *V, void *Out,
+                       float *state_out,
+                       int64_t N, int64_t H, int64_t L, int64_t E, int64_t M,
+                       int dtype, void *stream);
+
+/*
+ * causal_product_bwd: gradients of f = sum_i Out_i . dOut_i with respect to
+ * Q, K and V of causal_product_fwd (Q, K as given, no feature map):
+ *     dQ_i = sum_{j<=i} (dOut_i . V_j) K_j   = S_i dOut_i
+ *     dK_j = sum_{i>=j} (dOut_i . V_j) Q_i   = R_j V_j
+ *     dV_j = sum_{i>=j} (Q_i . K_j) dOut_i   = R_j^T K_j
+ * with S_i the inclusive prefix sum of k v^T and R_j = sum_{i>=j} q_i dOut_i^T
+ * the inclusive suffix sum.  Out is not needed.
+ *
+ * state_in (optional, may be NULL): fp32 [N][H][E][M], the final state that
+ * causal_product_fwd wrote to state_out for the same K and V.  With it every
+ * gradient is produced by reverse sweeps that read each input once; with
+ * NULL the query gradient runs its own forward sweep (more input traffic,
+ * same result up to rounding).
+ */
+int causal_product_bwd(const void *Q, const void *K, const void *V, const void *dOut,
+                       const float *state_in,
+                       void *dQ, void *dK, void *dV,
+                       int64_t N, int64_t H, int64_t L, int64_t E, int64_t M,
+                       int dtype, void *stream);
+
+/*
+ * linear_attn_fwd: causal linear attention with its normaliser,
+ *     out_i = phi(q_i)^T S_i / (phi(q_i) . z_i + eps),
+ *     S_i = sum_{j<=i} phi(k_j) v_j^T,   z_i = sum_{j<=i} phi(k_j),
+ * where phi is applied elementwise to the raw Q and K:
+ *     feature_map = 1: phi(x) = elu(x) + 1 = (x > 0 ? x + 1 : exp(x))
+ *     feature_map = 0: phi(x) = x (the caller has already mapped Q and K)
+ * eps >= 0 is added to the denominator as given (1e-6 is the usual value).
+ * Any other feature_map value, or eps < 0 or not finite, is CP_ERR_UNSUPPORTED.
+ */
+int linear_attn_fwd(const void *Q, const void *K, const void *V, void *Out,
+                    int64_t N, int64_t H, int64_t L, int64_t E, int64_t M,
+                    float eps, int feature_map, int dtype, void *stream);
+
+/* Static, NUL-terminated description of a cp_status value (never NULL). */
+const char *cp_status_string(int status);
+
+/* Version of this ABI: (major << 16) | minor. */
+int cp_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CAUSALPROD_H */

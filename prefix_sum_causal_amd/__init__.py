@@ -1,0 +1,190 @@
+"""MI355X (gfx950) causal dot product of linear attention.
+
+Thin Python binding of the C ABI in ``include/causalprod.h`` (library
+``libcausalprod.so`` built next to this file by ``build.py``).  Every step of
+the computation runs in the HIP kernels behind that ABI; this module only
+checks tensors, allocates outputs through PyTorch and passes raw device
+pointers and the current HIP stream.  There is no fallback: if the library is
+missing the import fails.
+
+Functions with the ABI's names:
+    causal_product_fwd(q, k, v, out=None, state_out=None)
+    causal_product_bwd(q, k, v, dout, state_in=None, dq=None, dk=None, dv=None)
+    linear_attn_fwd(q, k, v, eps=1e-6, feature_map=1, out=None)
+and autograd wrappers ``causal_product(q, k, v)`` and
+``linear_attention(q, k, v, eps=1e-6, feature_map="elu+1")``.
+
+Tensors are [N, H, L, E] (q, k) and [N, H, L, M] (v), contiguous, on the GPU,
+all float32 or all bfloat16, with E, M in {16, 32, 64, 128}.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libcausalprod.so")
+
+CP_F32, CP_BF16 = 0, 1
+STATUS = {0: "CP_OK", 1: "CP_ERR_NULL", 2: "CP_ERR_DIM", 3: "CP_ERR_UNSUPPORTED", 4: "CP_ERR_ALIGN",
+          5: "CP_ERR_ALIAS", 6: "CP_ERR_HIP"}
+SUPPORTED_HEAD_SIZES = (16, 32, 64, 128)
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m prefix_sum_causal_amd.build`")
+lib = ctypes.CDLL(LIB_PATH)
+
+_vp, _i64, _int = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+lib.causal_product_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _int, _vp]
+lib.causal_product_fwd.restype = _int
+lib.causal_product_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _int, _vp]
+lib.causal_product_bwd.restype = _int
+lib.linear_attn_fwd.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, ctypes.c_float, _int, _int, _vp]
+lib.linear_attn_fwd.restype = _int
+lib.cp_status_string.argtypes = [_int]
+lib.cp_status_string.restype = ctypes.c_char_p
+lib.cp_abi_version.argtypes = []
+lib.cp_abi_version.restype = _int
+
+
+class CausalProductError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        msg = lib.cp_status_string(status).decode()
+        super().__init__(f"{fn}: {STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise CausalProductError(fn, status)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return CP_F32
+    if t.dtype == torch.bfloat16:
+        return CP_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}; use float32 or bfloat16")
+
+
+def _dims(q: torch.Tensor, v: torch.Tensor):
+    if q.dim() != 4 or v.dim() != 4 or q.shape[:3] != v.shape[:3]:
+        raise ValueError(f"expected q [N,H,L,E] and v [N,H,L,M], got {tuple(q.shape)} and {tuple(v.shape)}")
+    N, H, L, E = q.shape
+    return N, H, L, E, v.shape[3]
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _check_tensors(*ts):
+    dev, dt = ts[0].device, ts[0].dtype
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("tensors must be on the GPU")
+        if t.device != dev or t.dtype != dt:
+            raise ValueError("all tensors must share one device and one dtype")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+def causal_product_fwd(q, k, v, out=None, state_out=None):
+    """out[n,h,i] = sum_{j<=i} (q_i . k_j) v_j.  ``state_out`` (fp32
+    [N,H,E,M], optional) receives the final state sum_j k_j v_j^T."""
+    N, H, L, E, M = _dims(q, v)
+    if k.shape != q.shape:
+        raise ValueError("k must have q's shape")
+    if out is None:
+        out = torch.empty_like(v)
+    _check_tensors(q, k, v, out)
+    if state_out is not None and (state_out.dtype != torch.float32 or not state_out.is_contiguous()
+                                  or tuple(state_out.shape) != (N, H, E, M) or state_out.device != q.device):
+        raise ValueError("state_out must be a contiguous float32 [N,H,E,M] tensor on q's device")
+    _check("causal_product_fwd", lib.causal_product_fwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(state_out), N, H, L, E, M, _dtype_code(q), _stream(q.device)))
+    return out
+
+
+def causal_product_bwd(q, k, v, dout, state_in=None, dq=None, dk=None, dv=None):
+    """Gradients (dq, dk, dv) of sum(out * dout) for out = causal_product_fwd(q, k, v).
+    ``state_in``: optional final state from causal_product_fwd's state_out."""
+    N, H, L, E, M = _dims(q, v)
+    if k.shape != q.shape or dout.shape != v.shape:
+        raise ValueError("k must have q's shape and dout v's shape")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    _check_tensors(q, k, v, dout, dq, dk, dv)
+    if state_in is not None and (state_in.dtype != torch.float32 or not state_in.is_contiguous()
+                                 or tuple(state_in.shape) != (N, H, E, M) or state_in.device != q.device):
+        raise ValueError("state_in must be a contiguous float32 [N,H,E,M] tensor on q's device")
+    _check("causal_product_bwd", lib.causal_product_bwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(state_in), _ptr(dq), _ptr(dk), _ptr(dv),
+        N, H, L, E, M, _dtype_code(q), _stream(q.device)))
+    return dq, dk, dv
+
+
+def linear_attn_fwd(q, k, v, eps: float = 1e-6, feature_map: int = 1, out=None):
+    """out_i = phi(q_i)^T S_i / (phi(q_i) . z_i + eps) with phi = elu + 1
+    (feature_map=1) or the identity (feature_map=0) applied to the raw q, k."""
+    N, H, L, E, M = _dims(q, v)
+    if k.shape != q.shape:
+        raise ValueError("k must have q's shape")
+    if out is None:
+        out = torch.empty_like(v)
+    _check_tensors(q, k, v, out)
+    _check("linear_attn_fwd", lib.linear_attn_fwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), N, H, L, E, M, float(eps), int(feature_map),
+        _dtype_code(q), _stream(q.device)))
+    return out
+
+
+class CausalProduct(torch.autograd.Function):
+    """Autograd wrapper: the forward keeps the final state so that the
+    backward runs its query gradient in the same reverse sweep as the others."""
+
+    @staticmethod
+    def forward(ctx, q, k, v):
+        q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
+        N, H, L, E, M = _dims(q, v)
+        state = torch.empty((N, H, E, M), device=q.device, dtype=torch.float32)
+        out = causal_product_fwd(q, k, v, state_out=state)
+        ctx.save_for_backward(q, k, v, state)
+        return out
+
+    @staticmethod
+    def backward(ctx, dout):
+        q, k, v, state = ctx.saved_tensors
+        return causal_product_bwd(q, k, v, dout.contiguous(), state_in=state)
+
+
+def causal_product(q, k, v):
+    """Differentiable causal dot product (q, k already feature-mapped)."""
+    return CausalProduct.apply(q, k, v)
+
+
+class LinearAttention(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, q, k, v, eps, feature_map):
+        return linear_attn_fwd(q.contiguous(), k.contiguous(), v.contiguous(), eps, feature_map)
+
+    @staticmethod
+    def backward(ctx, dout):
+        raise NotImplementedError("the backward of the normalised form is not implemented")
+
+
+def linear_attention(q, k, v, eps: float = 1e-6, feature_map: str = "elu+1"):
+    """Normalised causal linear attention; feature_map "elu+1" or "identity"."""
+    fm = {"elu+1": 1, "identity": 0}[feature_map]
+    return LinearAttention.apply(q, k, v, eps, fm)
+
+
+__all__ = ["causal_product_fwd", "causal_product_bwd", "linear_attn_fwd", "causal_product", "linear_attention",
+           "CausalProductError", "lib", "LIB_PATH"]

@@ -1,0 +1,161 @@
+// cp_api.cpp -- the C ABI declared in include/causalprod.h: argument
+// validation, kernel selection by (dtype, E, M) and launch on the caller's
+// stream.  Validation runs before any HIP call, so invalid calls have no side
+// effect and need no device.
+#include "causalprod.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstdlib>
+
+#include "cp_launch.hpp"
+
+namespace {
+
+constexpr int kAbiMajor = 1, kAbiMinor = 0;
+
+struct Range {
+    uintptr_t lo, hi;  // [lo, hi)
+};
+
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Shape checks shared by every entry point.  On success fills the element
+// counts of the [N][H][L][E] and [N][H][L][M] tensors.
+int check_dims(int64_t N, int64_t H, int64_t L, int64_t E, int64_t M, int dtype, int parts_per_slice_max,
+               int64_t &ne, int64_t &nm) {
+    if (N <= 0 || H <= 0 || L <= 0 || E <= 0 || M <= 0) return CP_ERR_DIM;
+    if (dtype != CP_F32 && dtype != CP_BF16) return CP_ERR_UNSUPPORTED;
+    if (cp::size_index(E) < 0 || cp::size_index(M) < 0) return CP_ERR_UNSUPPORTED;
+    if (L > INT32_MAX) return CP_ERR_DIM;
+    // N*H slices, each launched as up to parts_per_slice_max workgroups
+    if (N > INT32_MAX / H) return CP_ERR_DIM;
+    const int64_t NS = N * H;
+    if (NS > INT32_MAX / parts_per_slice_max) return CP_ERR_DIM;
+    // element counts in bytes must fit in int64
+    const int64_t limit = INT64_MAX / 8 / 128;
+    if (NS > limit / L) return CP_ERR_DIM;
+    ne = NS * L * E;
+    nm = NS * L * M;
+    return CP_OK;
+}
+
+int check_ptrs(std::initializer_list<const void *> ptrs) {
+    for (const void *p : ptrs)
+        if (!p) return CP_ERR_NULL;
+    for (const void *p : ptrs)
+        if (!aligned16(p)) return CP_ERR_ALIGN;
+    return CP_OK;
+}
+
+// Every output must be disjoint from every input and from the other outputs.
+int check_alias(std::initializer_list<Range> ins, std::initializer_list<Range> outs) {
+    for (auto o = outs.begin(); o != outs.end(); ++o) {
+        for (const Range &i : ins)
+            if (overlap(*o, i)) return CP_ERR_ALIAS;
+        for (auto p = o + 1; p != outs.end(); ++p)
+            if (overlap(*o, *p)) return CP_ERR_ALIAS;
+    }
+    return CP_OK;
+}
+
+Range span(const void *p, int64_t bytes) {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+    return Range{a, a + static_cast<uintptr_t>(bytes)};
+}
+
+int launch_status(hipError_t e) { return e == hipSuccess ? CP_OK : CP_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int cp_abi_version(void) { return (kAbiMajor << 16) | kAbiMinor; }
+
+const char *cp_status_string(int status) {
+    switch (status) {
+        case CP_OK: return "success";
+        case CP_ERR_NULL: return "a required pointer is NULL";
+        case CP_ERR_DIM: return "invalid size: N, H, L, E, M must be > 0, L <= 2^31-1, and the sizes must not overflow";
+        case CP_ERR_UNSUPPORTED: return "unsupported argument: E and M must be in {16, 32, 64, 128}; dtype, feature_map or eps out of range";
+        case CP_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
+        case CP_ERR_ALIAS: return "an output overlaps an input or another output";
+        case CP_ERR_HIP: return "the HIP runtime reported an error when launching the kernel";
+        default: return "unknown status";
+    }
+}
+
+int causal_product_fwd(const void *Q, const void *K, const void *V, void *Out, float *state_out, int64_t N,
+                       int64_t H, int64_t L, int64_t E, int64_t M, int dtype, void *stream) {
+    int64_t ne = 0, nm = 0;
+    int st = check_dims(N, H, L, E, M, dtype, 128 / 16 * 3, ne, nm);
+    if (st != CP_OK) return st;
+    st = check_ptrs({Q, K, V, Out});
+    if (st != CP_OK) return st;
+    if (state_out && !aligned16(state_out)) return CP_ERR_ALIGN;
+    const int64_t es = dtype == CP_BF16 ? 2 : 4;
+    const Range rq = span(Q, ne * es), rk = span(K, ne * es), rv = span(V, nm * es), ro = span(Out, nm * es);
+    if (state_out) {
+        const Range rs = span(state_out, N * H * E * M * 4);
+        st = check_alias({rq, rk, rv}, {ro, rs});
+    } else {
+        st = check_alias({rq, rk, rv}, {ro});
+    }
+    if (st != CP_OK) return st;
+
+    cp::fwd_fn fn = dtype == CP_BF16 ? cp::fwd_bf16((int)E, (int)M, false) : cp::fwd_f32((int)E, (int)M, false);
+    if (!fn) return CP_ERR_UNSUPPORTED;
+    cp::FwdArgs a{Q, K, V, Out, state_out, (int)L, (int)(N * H), 0.f, 0};
+    return launch_status(fn(a, static_cast<hipStream_t>(stream)));
+}
+
+int causal_product_bwd(const void *Q, const void *K, const void *V, const void *dOut, const float *state_in,
+                       void *dQ, void *dK, void *dV, int64_t N, int64_t H, int64_t L, int64_t E, int64_t M,
+                       int dtype, void *stream) {
+    int64_t ne = 0, nm = 0;
+    int st = check_dims(N, H, L, E, M, dtype, 128 / 16 * 3, ne, nm);
+    if (st != CP_OK) return st;
+    st = check_ptrs({Q, K, V, dOut, dQ, dK, dV});
+    if (st != CP_OK) return st;
+    if (state_in && !aligned16(state_in)) return CP_ERR_ALIGN;
+    const int64_t es = dtype == CP_BF16 ? 2 : 4;
+    const Range rq = span(Q, ne * es), rk = span(K, ne * es), rv = span(V, nm * es), rg = span(dOut, nm * es);
+    const Range rdq = span(dQ, ne * es), rdk = span(dK, ne * es), rdv = span(dV, nm * es);
+    if (state_in) {
+        const Range rs = span(state_in, N * H * E * M * 4);
+        st = check_alias({rq, rk, rv, rg, rs}, {rdq, rdk, rdv});
+    } else {
+        st = check_alias({rq, rk, rv, rg}, {rdq, rdk, rdv});
+    }
+    if (st != CP_OK) return st;
+
+    cp::bwd_fn fn = dtype == CP_BF16 ? cp::bwd_bf16((int)E, (int)M) : cp::bwd_f32((int)E, (int)M);
+    if (!fn) return CP_ERR_UNSUPPORTED;
+    cp::BwdArgs a{Q, K, V, dOut, state_in, dQ, dK, dV, (int)L, (int)(N * H)};
+    return launch_status(fn(a, static_cast<hipStream_t>(stream)));
+}
+
+int linear_attn_fwd(const void *Q, const void *K, const void *V, void *Out, int64_t N, int64_t H, int64_t L,
+                    int64_t E, int64_t M, float eps, int feature_map, int dtype, void *stream) {
+    int64_t ne = 0, nm = 0;
+    int st = check_dims(N, H, L, E, M, dtype, 128 / 16 * 3, ne, nm);
+    if (st != CP_OK) return st;
+    if (feature_map != 0 && feature_map != 1) return CP_ERR_UNSUPPORTED;
+    if (!(eps >= 0.f) || !std::isfinite(eps)) return CP_ERR_UNSUPPORTED;
+    st = check_ptrs({Q, K, V, Out});
+    if (st != CP_OK) return st;
+    const int64_t es = dtype == CP_BF16 ? 2 : 4;
+    st = check_alias({span(Q, ne * es), span(K, ne * es), span(V, nm * es)}, {span(Out, nm * es)});
+    if (st != CP_OK) return st;
+
+    cp::fwd_fn fn = dtype == CP_BF16 ? cp::fwd_bf16((int)E, (int)M, true) : cp::fwd_f32((int)E, (int)M, true);
+    if (!fn) return CP_ERR_UNSUPPORTED;
+    cp::FwdArgs a{Q, K, V, Out, nullptr, (int)L, (int)(N * H), eps, feature_map};
+    return launch_status(fn(a, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,46 @@
+// cp_launch.hpp -- host-side launch table between the C ABI and the kernels.
+// Each dtype/direction lives in its own translation unit; the C ABI picks a
+// launcher by (dtype, E, M) and passes sizes already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace cp {
+
+struct FwdArgs {
+    const void *Q, *K, *V;
+    void *Out;
+    float *state_out;
+    int L, NS;
+    float eps;
+    int fmap;
+};
+
+struct BwdArgs {
+    const void *Q, *K, *V, *G;
+    const float *state_in;
+    void *dQ, *dK, *dV;
+    int L, NS;
+};
+
+// Each launcher enqueues one kernel on stream and returns hipSuccess or the
+// launch error.  NULL when (E, M) is not instantiated.
+typedef hipError_t (*fwd_fn)(const FwdArgs &, hipStream_t);
+typedef hipError_t (*bwd_fn)(const BwdArgs &, hipStream_t);
+
+fwd_fn fwd_f32(int E, int M, bool norm);
+fwd_fn fwd_bf16(int E, int M, bool norm);
+bwd_fn bwd_f32(int E, int M);
+bwd_fn bwd_bf16(int E, int M);
+
+// Waves per (n, h) slice of each kernel.
+inline int fwd_parts(int E, int M) { (void)E; return M / 16; }
+inline int bwd_parts(int E, int M) { return 2 * (E / 16) + M / 16; }
+
+// Index 0..3 of a head size in {16, 32, 64, 128}, -1 otherwise.
+inline int size_index(int64_t x) {
+    return x == 16 ? 0 : x == 32 ? 1 : x == 64 ? 2 : x == 128 ? 3 : -1;
+}
+
+}  // namespace cp

@@ -1,0 +1,131 @@
+"""The C ABI on the CPU: the library loads, exports every function that
+include/causalprod.h declares, and rejects invalid arguments with the
+documented status before touching a device (fake, never dereferenced
+addresses; every case here fails validation)."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "causalprod.h")
+LIB = os.path.join(ROOT, "prefix_sum_causal_amd", "libcausalprod.so")
+
+OK, NULL, DIM, UNSUP, ALIGN, ALIAS, HIP = range(7)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.skip("libcausalprod.so not built")
+    lib = ctypes.CDLL(LIB)
+    vp, i64, i = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    lib.causal_product_fwd.argtypes = [vp] * 5 + [i64] * 5 + [i, vp]
+    lib.causal_product_bwd.argtypes = [vp] * 8 + [i64] * 5 + [i, vp]
+    lib.linear_attn_fwd.argtypes = [vp] * 4 + [i64] * 5 + [ctypes.c_float, i, i, vp]
+    lib.cp_status_string.restype = ctypes.c_char_p
+    return lib
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == sorted(
+        ["causal_product_fwd", "causal_product_bwd", "linear_attn_fwd", "cp_status_string", "cp_abi_version"])
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings_and_version(lib):
+    seen = set()
+    for s in range(7):
+        msg = lib.cp_status_string(s).decode()
+        assert msg and msg not in seen
+        seen.add(msg)
+    assert lib.cp_status_string(99).decode() == "unknown status"
+    assert lib.cp_abi_version() == (1 << 16)
+
+
+# fake, 16-byte aligned, disjoint addresses (never dereferenced)
+A = [0x10_0000_0000 + n * 0x1_0000_0000 for n in range(8)]
+SHAPE = (2, 3, 100, 64, 32)
+
+
+def fwd(lib, q=A[0], k=A[1], v=A[2], o=A[3], st=None, shape=SHAPE, dtype=1):
+    return lib.causal_product_fwd(q, k, v, o, st, *shape, dtype, None)
+
+
+def bwd(lib, q=A[0], k=A[1], v=A[2], g=A[3], st=None, dq=A[4], dk=A[5], dv=A[6], shape=SHAPE, dtype=1):
+    return lib.causal_product_bwd(q, k, v, g, st, dq, dk, dv, *shape, dtype, None)
+
+
+def lin(lib, q=A[0], k=A[1], v=A[2], o=A[3], shape=SHAPE, eps=1e-6, fm=1, dtype=1):
+    return lib.linear_attn_fwd(q, k, v, o, *shape, eps, fm, dtype, None)
+
+
+@pytest.mark.parametrize("which", range(4))
+def test_null_pointers(lib, which):
+    args = dict(q=A[0], k=A[1], v=A[2], o=A[3])
+    args[list(args)[which]] = None
+    assert fwd(lib, **args) == NULL
+    assert lin(lib, **args) == NULL
+
+
+def test_null_backward_pointers(lib):
+    for name in ("q", "k", "v", "g", "dq", "dk", "dv"):
+        assert bwd(lib, **{name: None}) == NULL, name
+
+
+@pytest.mark.parametrize("shape", [(0, 3, 100, 64, 32), (2, -1, 100, 64, 32), (2, 3, 0, 64, 32),
+                                   (2, 3, 100, 0, 32), (2, 3, 100, 64, -16), (1, 1, 2 ** 31, 64, 64),
+                                   (2 ** 40, 2 ** 30, 4, 16, 16)])
+def test_bad_dims(lib, shape):
+    assert fwd(lib, shape=shape) == DIM
+    assert bwd(lib, shape=shape) == DIM
+    assert lin(lib, shape=shape) == DIM
+
+
+@pytest.mark.parametrize("E,M", [(48, 64), (64, 8), (256, 64), (64, 17)])
+def test_unsupported_head_sizes(lib, E, M):
+    shape = (2, 3, 100, E, M)
+    assert fwd(lib, shape=shape) == UNSUP
+    assert bwd(lib, shape=shape) == UNSUP
+    assert lin(lib, shape=shape) == UNSUP
+
+
+def test_unsupported_dtype_flag_eps(lib):
+    assert fwd(lib, dtype=2) == UNSUP
+    assert bwd(lib, dtype=-1) == UNSUP
+    assert lin(lib, fm=2) == UNSUP
+    assert lin(lib, eps=-1e-3) == UNSUP
+    assert lin(lib, eps=math.nan) == UNSUP
+    assert lin(lib, eps=math.inf) == UNSUP
+
+
+def test_misaligned(lib):
+    assert fwd(lib, v=A[2] + 8) == ALIGN
+    assert fwd(lib, st=A[4] + 4) == ALIGN
+    assert bwd(lib, dk=A[5] + 2) == ALIGN
+    assert bwd(lib, st=A[7] + 8) == ALIGN
+    assert lin(lib, o=A[3] + 8) == ALIGN
+
+
+def test_aliasing(lib):
+    # SHAPE bf16: q, k are 2*3*100*64*2 = 76800 bytes; v, out 38400 bytes
+    assert fwd(lib, o=A[0]) == ALIAS
+    assert fwd(lib, o=A[1] + 76800 - 16) == ALIAS
+    assert fwd(lib, st=A[3]) == ALIAS            # state_out overlaps out
+    assert fwd(lib, st=A[2] + 16) == ALIAS       # state_out overlaps v
+    assert bwd(lib, dq=A[5]) == ALIAS            # dq == dk
+    assert bwd(lib, dv=A[3]) == ALIAS            # dv == dout
+    assert bwd(lib, st=A[4]) == ALIAS            # state_in overlaps dq
+    assert lin(lib, o=A[2]) == ALIAS
