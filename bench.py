@@ -89,11 +89,12 @@ def cpu_baseline(w, target_seconds: float = 15.0) -> dict:
                 orc.bwd(d["Q"], d["K"], d["V"], d["dO"])
         slices += ws.H
         el = time.perf_counter() - t0
-        if el >= target_seconds or slices >= w.N * w.H:
+        if el >= target_seconds:
             break
     return {"value": slices * w.L / el, "unit": UNIT, "cores": threads, "kind": "oracle",
-            "sample": f"{slices} of {w.N * w.H} (n,h) slices at full L={w.L}, fp64 recurrence "
-                      f"({'fwd+bwd' if w.op == 'fwd+bwd' else w.op}), {el:.1f} s on {threads} threads"}
+            "sample": f"{slices} (n,h) slices at full L={w.L} ({threads} distinct slices of the workload, "
+                      f"repeated), fp64 recurrence ({'fwd+bwd' if w.op == 'fwd+bwd' else w.op}), "
+                      f"{el:.1f} s on {threads} threads"}
 
 
 def main() -> int:
@@ -103,6 +104,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="run one plain device-to-device copy of this many MiB first (reference for the "
+                         "HBM byte counters of a profiler run)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the path shards over (n, h) slices "
@@ -140,6 +144,15 @@ def main() -> int:
             cp.causal_product_bwd(q, k, v, g, state_in=state, dq=dq, dk=dk, dv=dv)
             if evs:
                 evs[2].record()
+
+    if args.calibrate_copy_mib:
+        n = args.calibrate_copy_mib * (1 << 20) // 4
+        src = torch.ones(n, device="cuda", dtype=torch.float32)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     for _ in range(args.warmup):
         step()

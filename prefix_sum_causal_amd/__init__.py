@@ -25,7 +25,9 @@ import os
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libcausalprod.so")
+# CAUSALPROD_LIB selects another build of the same library (e.g. one built
+# with other tuning parameters by build.build(out=..., defines=...)).
+LIB_PATH = os.environ.get("CAUSALPROD_LIB") or os.path.join(HERE, "libcausalprod.so")
 
 CP_F32, CP_BF16 = 0, 1
 STATUS = {0: "CP_OK", 1: "CP_ERR_NULL", 2: "CP_ERR_DIM", 3: "CP_ERR_UNSUPPORTED", 4: "CP_ERR_ALIGN",

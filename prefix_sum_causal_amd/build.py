@@ -29,29 +29,35 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, 
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wno-unused-command-line-argument"]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, build_dir: str, defines: dict) -> str:
+    obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
+    dflags = [f"-D{k}={v}" for k, v in sorted(defines.items())]
+    cmd = [HIPCC, *FLAGS, *dflags, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
+def build(verbose: bool = False, out: str = LIB, defines: dict | None = None) -> str:
+    """Compile and link the library to ``out``.  ``defines`` overrides the
+    tuning macros of cp_tune.hpp (e.g. {"CP_BF16_NBUF": 4})."""
+    defines = dict(defines or {})
+    build_dir = BUILD_DIR if not defines else os.path.join(BUILD_DIR, "_".join(f"{k}{v}" for k, v in
+                                                                               sorted(defines.items())))
+    os.makedirs(build_dir, exist_ok=True)
     jobs = min(len(SOURCES), max(1, min(os.cpu_count() or 1, 8)))
     with cf.ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp%d" % os.getpid()
+        objs = list(ex.map(lambda s: _compile(s, build_dir, defines), SOURCES))
+    tmp = out + ".tmp%d" % os.getpid()
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {out}")
+    return out
 
 
 if __name__ == "__main__":

@@ -43,15 +43,17 @@ struct BwdChunk {
     F x[CB][XB];
     F y[CB][YB];
     F z[CB];
+    // Rows outside [0, L) (and whole chunks outside the sequence) load as zero.
     __device__ __forceinline__ void load(const T *x_, const T *y_, const T *z_, int zld, int zcb, int row0,
                                          int L) {
+        const Rows<T> rx(x_, XW, row0, L, C), ry(y_, YW, row0, L, C), rz(z_, zld, row0, L, C);
 #pragma unroll
         for (int b = 0; b < CB; ++b) {
 #pragma unroll
-            for (int e = 0; e < XB; ++e) x[b][e] = ld_nat<T>(x_, XW, row0, L, b, e);
+            for (int e = 0; e < XB; ++e) x[b][e] = ld_nat<T>(rx, b, e);
 #pragma unroll
-            for (int e = 0; e < YB; ++e) y[b][e] = ld_nat<T>(y_, YW, row0, L, b, e);
-            z[b] = ld_nat<T>(z_, zld, row0, L, b, zcb);
+            for (int e = 0; e < YB; ++e) y[b][e] = ld_nat<T>(ry, b, e);
+            z[b] = ld_nat<T>(rz, b, zcb);
         }
     }
 };
@@ -76,18 +78,22 @@ __device__ __forceinline__ void bwd_dq(const T *k_, const T *v_, const T *g_, co
             for (int t = 0; t < 4; ++t) W[m][t] = st[(16 * eb + r) * M + 16 * m + 4 * g + t];
         }
     }
+    // steps padded to a multiple of NBUF; padded chunks lie outside the
+    // sequence, load as zero and store nothing
     const int n = (L + C - 1) / C;
+    const int nsteps = (n + NBUF - 1) / NBUF * NBUF;
     BwdChunk<T, M, M, C> buf[NBUF];
     auto chunk_of = [&](int s) { return REV ? n - 1 - s : s; };
 #pragma unroll
-    for (int s = 0; s < NBUF - 1; ++s)
-        if (s < n) buf[s].load(v_, g_, k_, E, eb, chunk_of(s) * C, L);
+    for (int s = 0; s < NBUF - 1; ++s) {
+        buf[s].load(v_, g_, k_, E, eb, chunk_of(s) * C, L);
+        __builtin_amdgcn_sched_barrier(0);  // buffers complete in order
+    }
 
-    for (int s0 = 0; s0 < n; s0 += NBUF) {
+    for (int s0 = 0; s0 < nsteps; s0 += NBUF) {
 #pragma unroll
         for (int s = 0; s < NBUF; ++s) {
             const int step = s0 + s;
-            if (step >= n) break;
             const int row0 = chunk_of(step) * C;
             BwdChunk<T, M, M, C> &cur = buf[s];
 #pragma unroll
@@ -96,7 +102,7 @@ __device__ __forceinline__ void bwd_dq(const T *k_, const T *v_, const T *g_, co
                 for (int m = 0; m < MB; ++m) st_lds<T>(ldsV, RSY, b, m, cur.x[b][m]);
                 st_lds<T>(ldsK, RSZ, b, 0, cur.z[b]);
             }
-            __syncthreads();
+            wave_lds_sync();
             F vt[CB][MB], kt[CB];
 #pragma unroll
             for (int b = 0; b < CB; ++b) {
@@ -104,15 +110,16 @@ __device__ __forceinline__ void bwd_dq(const T *k_, const T *v_, const T *g_, co
                 for (int m = 0; m < MB; ++m) vt[b][m] = O::tr_frag(ldsV, RSY, b, m);
                 kt[b] = O::tr_frag(ldsK, RSZ, b, 0);
             }
-            {
-                const int sn = step + NBUF - 1;
-                if (sn < n) buf[(s + NBUF - 1) % NBUF].load(v_, g_, k_, E, eb, chunk_of(sn) * C, L);
-            }
+            buf[(s + NBUF - 1) % NBUF].load(v_, g_, k_, E, eb, chunk_of(step + NBUF - 1) * C, L);
+            // keep the prefetch here: sunk towards the loop end it would be
+            // the youngest load at the next chunk and stall the pipeline
+            __builtin_amdgcn_sched_barrier(0);
             if (REV) {  // W = S_{c-1}^T = S_{L-1}^T - sum_{chunks >= c} V^T K
 #pragma unroll
                 for (int m = 0; m < MB; ++m)
                     dotk<T>(W[m], 0, CB, [&](int J) { return vt[J][m]; }, [&](int J) { return O::neg(kt[J]); });
             }
+            const Rows<T> rdq(dq_, E, row0, L, C);
             F wh[MB], wl[MB];  // A = S (rows e, k = m)
 #pragma unroll
             for (int m = 0; m < MB; ++m) {
@@ -137,14 +144,14 @@ __device__ __forceinline__ void bwd_dq(const T *k_, const T *v_, const T *g_, co
                 }
                 // dQ^T += K^T P^T
                 dotk<T>(d, 0, I + 1, [&](int J) { return kt[J]; }, [&](int J) { return pt[J]; });
-                st_out<T>(dq_, E, row0, L, I, eb, d);
+                st_out<T>(rdq, I, eb, d);
             }
             if (!REV) {  // W = S_c^T = S_{c-1}^T + V_c^T K_c
 #pragma unroll
                 for (int m = 0; m < MB; ++m)
                     dotk<T>(W[m], 0, CB, [&](int J) { return vt[J][m]; }, [&](int J) { return kt[J]; });
             }
-            __syncthreads();
+            wave_lds_sync();
         }
     }
 }
@@ -162,16 +169,18 @@ __device__ __forceinline__ void bwd_dk(const T *q_, const T *v_, const T *g_, T 
 #pragma unroll
     for (int m = 0; m < MB; ++m) Rt[m] = zero4();
     const int n = (L + C - 1) / C;
+    const int nsteps = (n + NBUF - 1) / NBUF * NBUF;
     BwdChunk<T, M, M, C> buf[NBUF];
 #pragma unroll
-    for (int s = 0; s < NBUF - 1; ++s)
-        if (s < n) buf[s].load(g_, v_, q_, E, eb, (n - 1 - s) * C, L);
+    for (int s = 0; s < NBUF - 1; ++s) {
+        buf[s].load(g_, v_, q_, E, eb, (n - 1 - s) * C, L);
+        __builtin_amdgcn_sched_barrier(0);  // buffers complete in order
+    }
 
-    for (int s0 = 0; s0 < n; s0 += NBUF) {
+    for (int s0 = 0; s0 < nsteps; s0 += NBUF) {
 #pragma unroll
         for (int s = 0; s < NBUF; ++s) {
             const int step = s0 + s;
-            if (step >= n) break;
             const int row0 = (n - 1 - step) * C;
             BwdChunk<T, M, M, C> &cur = buf[s];
 #pragma unroll
@@ -180,7 +189,7 @@ __device__ __forceinline__ void bwd_dk(const T *q_, const T *v_, const T *g_, T 
                 for (int m = 0; m < MB; ++m) st_lds<T>(ldsG, RSX, b, m, cur.x[b][m]);
                 st_lds<T>(ldsQ, RSZ, b, 0, cur.z[b]);
             }
-            __syncthreads();
+            wave_lds_sync();
             F gt[CB][MB], qt[CB];
 #pragma unroll
             for (int b = 0; b < CB; ++b) {
@@ -188,10 +197,11 @@ __device__ __forceinline__ void bwd_dk(const T *q_, const T *v_, const T *g_, T 
                 for (int m = 0; m < MB; ++m) gt[b][m] = O::tr_frag(ldsG, RSX, b, m);
                 qt[b] = O::tr_frag(ldsQ, RSZ, b, 0);
             }
-            {
-                const int sn = step + NBUF - 1;
-                if (sn < n) buf[(s + NBUF - 1) % NBUF].load(g_, v_, q_, E, eb, (n - 1 - sn) * C, L);
-            }
+            buf[(s + NBUF - 1) % NBUF].load(g_, v_, q_, E, eb, (n - 1 - (step + NBUF - 1)) * C, L);
+            // keep the prefetch here: sunk towards the loop end it would be
+            // the youngest load at the next chunk and stall the pipeline
+            __builtin_amdgcn_sched_barrier(0);
+            const Rows<T> rdk(dk_, E, row0, L, C);
             F rh[MB], rl[MB];  // A = R (rows e, k = m)
 #pragma unroll
             for (int m = 0; m < MB; ++m) {
@@ -216,13 +226,13 @@ __device__ __forceinline__ void bwd_dk(const T *q_, const T *v_, const T *g_, T 
                 }
                 // dK^T += Q^T P
                 dotk<T>(d, J, CB, [&](int I) { return qt[I]; }, [&](int I) { return p[I]; });
-                st_out<T>(dk_, E, row0, L, J, eb, d);
+                st_out<T>(rdk, J, eb, d);
             }
             // R^T += dO_c^T Q_c
 #pragma unroll
             for (int m = 0; m < MB; ++m)
                 dotk<T>(Rt[m], 0, CB, [&](int I) { return gt[I][m]; }, [&](int I) { return qt[I]; });
-            __syncthreads();
+            wave_lds_sync();
         }
     }
 }
@@ -240,16 +250,18 @@ __device__ __forceinline__ void bwd_dv(const T *q_, const T *k_, const T *g_, T 
 #pragma unroll
     for (int e = 0; e < EB; ++e) R[e] = zero4();
     const int n = (L + C - 1) / C;
+    const int nsteps = (n + NBUF - 1) / NBUF * NBUF;
     BwdChunk<T, E, E, C> buf[NBUF];
 #pragma unroll
-    for (int s = 0; s < NBUF - 1; ++s)
-        if (s < n) buf[s].load(q_, k_, g_, M, mb, (n - 1 - s) * C, L);
+    for (int s = 0; s < NBUF - 1; ++s) {
+        buf[s].load(q_, k_, g_, M, mb, (n - 1 - s) * C, L);
+        __builtin_amdgcn_sched_barrier(0);  // buffers complete in order
+    }
 
-    for (int s0 = 0; s0 < n; s0 += NBUF) {
+    for (int s0 = 0; s0 < nsteps; s0 += NBUF) {
 #pragma unroll
         for (int s = 0; s < NBUF; ++s) {
             const int step = s0 + s;
-            if (step >= n) break;
             const int row0 = (n - 1 - step) * C;
             BwdChunk<T, E, E, C> &cur = buf[s];
 #pragma unroll
@@ -258,7 +270,7 @@ __device__ __forceinline__ void bwd_dv(const T *q_, const T *k_, const T *g_, T 
                 for (int e = 0; e < EB; ++e) st_lds<T>(ldsQ, RSX, b, e, cur.x[b][e]);
                 st_lds<T>(ldsG, RSZ, b, 0, cur.z[b]);
             }
-            __syncthreads();
+            wave_lds_sync();
             F qt[CB][EB], gt[CB];
 #pragma unroll
             for (int b = 0; b < CB; ++b) {
@@ -266,10 +278,11 @@ __device__ __forceinline__ void bwd_dv(const T *q_, const T *k_, const T *g_, T 
                 for (int e = 0; e < EB; ++e) qt[b][e] = O::tr_frag(ldsQ, RSX, b, e);
                 gt[b] = O::tr_frag(ldsG, RSZ, b, 0);
             }
-            {
-                const int sn = step + NBUF - 1;
-                if (sn < n) buf[(s + NBUF - 1) % NBUF].load(q_, k_, g_, M, mb, (n - 1 - sn) * C, L);
-            }
+            buf[(s + NBUF - 1) % NBUF].load(q_, k_, g_, M, mb, (n - 1 - (step + NBUF - 1)) * C, L);
+            // keep the prefetch here: sunk towards the loop end it would be
+            // the youngest load at the next chunk and stall the pipeline
+            __builtin_amdgcn_sched_barrier(0);
+            const Rows<T> rdv(dv_, M, row0, L, C);
             F rh[EB], rl[EB];  // A = R^T (rows m, k = e)
 #pragma unroll
             for (int e = 0; e < EB; ++e) {
@@ -294,13 +307,13 @@ __device__ __forceinline__ void bwd_dv(const T *q_, const T *k_, const T *g_, T 
                 }
                 // dV^T += dO^T A
                 dotk<T>(d, J, CB, [&](int I) { return gt[I]; }, [&](int I) { return a[I]; });
-                st_out<T>(dv_, M, row0, L, J, mb, d);
+                st_out<T>(rdv, J, mb, d);
             }
             // R += Q_c^T dO_c
 #pragma unroll
             for (int e = 0; e < EB; ++e)
                 dotk<T>(R[e], 0, CB, [&](int I) { return qt[I][e]; }, [&](int I) { return gt[I]; });
-            __syncthreads();
+            wave_lds_sync();
         }
     }
 }

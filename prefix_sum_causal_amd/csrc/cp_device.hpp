@@ -20,7 +20,8 @@
 //
 // Three fragment sources are used:
 //   natural  (ld_nat):  lane (g, r) <- X[row0 + 16 rb + r][16 cb + 4g + t]
-//            4 consecutive elements of one row, read straight from HBM.
+//            4 consecutive elements of one row, read straight from HBM with
+//            a buffer load.
 //            As an A operand this is X, as a B operand X^T.
 //   transposed (tr_frag): lane (g, r) <- X[16 tb + 4g + t][16 cb + r]
 //            4 consecutive rows of one column, read from a natural copy of
@@ -99,12 +100,6 @@ template <> struct Ops<bf16> {
         for (int t = 0; t < 4; ++t) x[t] = (float)a[t];
         return x;
     }
-    __device__ static __forceinline__ frag load(const bf16 *p) {
-        return *reinterpret_cast<const frag *>(p);
-    }
-    __device__ static __forceinline__ void store(bf16 *p, f32x4 v) {
-        *reinterpret_cast<frag *>(p) = cvt(v);
-    }
     // lane (g, r) <- X[16 tb + 4g + t][16 cb + r] from a natural LDS copy
     // with row stride rs (elements).
     __device__ static __forceinline__ frag tr_frag(const bf16 *lds, int rs, int tb, int cb) {
@@ -142,12 +137,6 @@ template <> struct Ops<float> {
     }
     __device__ static __forceinline__ frag neg(frag a) { return -a; }
     __device__ static __forceinline__ f32x4 widen(frag a) { return a; }
-    __device__ static __forceinline__ frag load(const float *p) {
-        return *reinterpret_cast<const frag *>(p);
-    }
-    __device__ static __forceinline__ void store(float *p, f32x4 v) {
-        *reinterpret_cast<frag *>(p) = v;
-    }
     __device__ static __forceinline__ frag tr_frag(const float *lds, int rs, int tb, int cb) {
         const int g = lane_g(), r = lane_r();
         f32x4 v;
@@ -168,14 +157,54 @@ __device__ __forceinline__ void dotk(f32x4 &acc, int b0, int b1, FA fa, FB fb) {
     if (b < b1) O::mma1(acc, fa(b), fb(b));
 }
 
-// Natural fragment of row-major X (leading dimension ld) for the 16-row
-// block rb of the chunk starting at row0: lane (g, r) <- X[row][16 cb + 4g + t]
-// with row = row0 + 16 rb + r; rows at or past L read as zero.
+// A chunk of C rows of one row-major slice (leading dimension ld elements),
+// addressed through a buffer resource whose range ends at row L: loads past
+// the range return zero and stores past it are dropped by the hardware, so
+// every access is issued unconditionally (no divergent branches around
+// memory operations, which keeps the load pipeline's wait counts exact) and
+// rows outside [0, L) never touch memory.
+constexpr int kBufferDword3 = 0x00020000;  // gfx9-family raw buffer, no swizzle
+
 template <typename T>
-__device__ __forceinline__ typename Ops<T>::frag ld_nat(const T *X, int ld, int row0, int L, int rb, int cb) {
-    const int row = row0 + 16 * rb + lane_r();
-    if (row < L) return Ops<T>::load(X + (int64_t)row * ld + 16 * cb + 4 * lane_g());
-    return Ops<T>::zero();
+struct Rows {
+    __amdgpu_buffer_rsrc_t rsrc;
+    int ld;
+    // rows [row0, row0 + C) of the slice at base; rows < 0 or >= L are void
+    __device__ __forceinline__ Rows(const T *base, int ld_, int row0, int L, int C) : ld(ld_) {
+        int n = (row0 < 0) ? 0 : L - row0;
+        n = n < 0 ? 0 : (n > C ? C : n);
+        // the range is the same for every lane: keep it in scalar registers
+        n = __builtin_amdgcn_readfirstlane(n);
+        const T *p = base + (int64_t)(row0 > 0 ? row0 : 0) * ld;
+        rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<T *>(p), (short)0, n * ld * (int)sizeof(T),
+                                                 kBufferDword3);
+    }
+};
+
+// Natural fragment of the 16-row block rb: lane (g, r) <- X[16 rb + r][16 cb + 4g + t].
+template <typename T>
+__device__ __forceinline__ typename Ops<T>::frag ld_nat(const Rows<T> &X, int rb, int cb) {
+    const int off = ((16 * rb + lane_r()) * X.ld + 16 * cb + 4 * lane_g()) * (int)sizeof(T);
+    if constexpr (sizeof(T) == 2) {
+        auto v = __builtin_amdgcn_raw_buffer_load_b64(X.rsrc, off, 0, 0);
+        return __builtin_bit_cast(typename Ops<T>::frag, v);
+    } else {
+        auto v = __builtin_amdgcn_raw_buffer_load_b128(X.rsrc, off, 0, 0);
+        return __builtin_bit_cast(typename Ops<T>::frag, v);
+    }
+}
+
+// Store a transposed result tile: lane (g, r) holds X[16 rb + r][16 cb + 4g + t].
+template <typename T>
+__device__ __forceinline__ void st_out(const Rows<T> &X, int rb, int cb, f32x4 v) {
+    const int off = ((16 * rb + lane_r()) * X.ld + 16 * cb + 4 * lane_g()) * (int)sizeof(T);
+    if constexpr (sizeof(T) == 2) {
+        typedef int i32x2 __attribute__((__vector_size__(2 * sizeof(int))));
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(i32x2, Ops<T>::cvt(v)), X.rsrc, off, 0, 0);
+    } else {
+        typedef int i32x4 __attribute__((__vector_size__(4 * sizeof(int))));
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), X.rsrc, off, 0, 0);
+    }
 }
 
 // Store a natural fragment into an LDS copy of the chunk (row stride rs).
@@ -184,12 +213,13 @@ __device__ __forceinline__ void st_lds(T *lds, int rs, int rb, int cb, typename 
     *reinterpret_cast<typename Ops<T>::frag *>(lds + (16 * rb + lane_r()) * rs + 16 * cb + 4 * lane_g()) = f;
 }
 
-// Store a transposed result tile: lane (g, r) holds X[row][16 cb + 4g + t]
-// for row = row0 + 16 rb + r (the D^T layout of an output tile).
-template <typename T>
-__device__ __forceinline__ void st_out(T *X, int ld, int row0, int L, int rb, int cb, f32x4 v) {
-    const int row = row0 + 16 * rb + lane_r();
-    if (row < L) Ops<T>::store(X + (int64_t)row * ld + 16 * cb + 4 * lane_g(), v);
+// Order this wave's LDS writes before its later LDS reads of other lanes'
+// data and vice versa.  A workgroup here is a single wave, so this is all the
+// synchronisation LDS needs (no s_barrier, no wait on global loads).
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 // Causal mask of a diagonal tile in the layout D[j][i] (rows = keys j,

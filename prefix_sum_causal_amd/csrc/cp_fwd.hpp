@@ -40,15 +40,17 @@ struct FwdChunk {
     F k[CB][EB];  // K[row0 + 16 J + r][16 eb + 4g + t]
     F v[CB];      // V[row0 + 16 J + r][16 mb + 4g + t]
 
+    // Rows at or past L (and whole chunks past the end) load as zero.
     __device__ __forceinline__ void load(const T *q_, const T *k_, const T *v_, int row0, int L, int mb) {
+        const Rows<T> rq(q_, E, row0, L, C), rk(k_, E, row0, L, C), rv(v_, M, row0, L, C);
 #pragma unroll
         for (int b = 0; b < CB; ++b) {
 #pragma unroll
             for (int e = 0; e < EB; ++e) {
-                q[b][e] = ld_nat<T>(q_, E, row0, L, b, e);
-                k[b][e] = ld_nat<T>(k_, E, row0, L, b, e);
+                q[b][e] = ld_nat<T>(rq, b, e);
+                k[b][e] = ld_nat<T>(rk, b, e);
             }
-            v[b] = ld_nat<T>(v_, M, row0, L, b, mb);
+            v[b] = ld_nat<T>(rv, b, mb);
         }
     }
 };
@@ -58,6 +60,7 @@ __global__ __launch_bounds__(64) void cp_fwd_kernel(const T *__restrict__ Q, con
                                                     const T *__restrict__ V, T *__restrict__ Out,
                                                     float *__restrict__ state_out, int L, int NS,
                                                     float eps, int fmap) {
+    static_assert(NBUF >= 2, "the pipeline needs at least two chunk buffers");
     using O = Ops<T>;
     using F = typename O::frag;
     constexpr int EB = E / 16, MB = M / 16, CB = C / 16;
@@ -81,38 +84,35 @@ __global__ __launch_bounds__(64) void cp_fwd_kernel(const T *__restrict__ Q, con
         z[e] = zero4();
     }
 
+    // The chunk loop is padded to a multiple of NBUF; padded chunks lie past
+    // L, load as zero and store nothing, so every step issues the same loads.
     const int nchunks = (L + C - 1) / C;
+    const int nsteps = (nchunks + NBUF - 1) / NBUF * NBUF;
     FwdChunk<T, E, M, C> buf[NBUF];
 #pragma unroll
-    for (int s = 0; s < NBUF - 1; ++s)
-        if (s < nchunks) buf[s].load(q_, k_, v_, s * C, L, mb);
+    for (int s = 0; s < NBUF - 1; ++s) {
+        buf[s].load(q_, k_, v_, s * C, L, mb);
+        __builtin_amdgcn_sched_barrier(0);  // buffers complete in order
+    }
 
-    for (int c0 = 0; c0 < nchunks; c0 += NBUF) {
+    for (int c0 = 0; c0 < nsteps; c0 += NBUF) {
 #pragma unroll
         for (int s = 0; s < NBUF; ++s) {
             const int c = c0 + s;
-            if (c >= nchunks) break;
             const int row0 = c * C;
             FwdChunk<T, E, M, C> &cur = buf[s];
             if constexpr (NORM) {
                 if (fmap) {
+                    // phi(0) = 1, so rows past L are zeroed again after the map
 #pragma unroll
-                    for (int b = 0; b < CB; ++b)
+                    for (int b = 0; b < CB; ++b) {
+                        const bool valid = row0 + 16 * b + r < L;
 #pragma unroll
                         for (int e = 0; e < EB; ++e) {
-                            cur.q[b][e] = phi_frag<T>(cur.q[b][e]);
-                            cur.k[b][e] = phi_frag<T>(cur.k[b][e]);
+                            const F pq = phi_frag<T>(cur.q[b][e]), pk = phi_frag<T>(cur.k[b][e]);
+                            cur.q[b][e] = valid ? pq : O::zero();
+                            cur.k[b][e] = valid ? pk : O::zero();
                         }
-                    // rows past L must stay zero after the map (phi(0) = 1)
-                    if (row0 + C > L) {
-#pragma unroll
-                        for (int b = 0; b < CB; ++b)
-                            if (row0 + 16 * b + r >= L)
-#pragma unroll
-                                for (int e = 0; e < EB; ++e) {
-                                    cur.q[b][e] = O::zero();
-                                    cur.k[b][e] = O::zero();
-                                }
                     }
                 }
             }
@@ -124,7 +124,7 @@ __global__ __launch_bounds__(64) void cp_fwd_kernel(const T *__restrict__ Q, con
                 for (int e = 0; e < EB; ++e) st_lds<T>(ldsK, RSK, b, e, cur.k[b][e]);
                 st_lds<T>(ldsV, RSV, b, 0, cur.v[b]);
             }
-            __syncthreads();
+            wave_lds_sync();
             F kt[CB][EB], vt[CB];  // K[16 J + 4g + t][16 eb + r], V[16 J + 4g + t][16 mb + r]
 #pragma unroll
             for (int b = 0; b < CB; ++b) {
@@ -133,10 +133,10 @@ __global__ __launch_bounds__(64) void cp_fwd_kernel(const T *__restrict__ Q, con
                 vt[b] = O::tr_frag(ldsV, RSV, b, 0);
             }
             // keep NBUF-1 chunks in flight while this one is computed
-            {
-                const int cn = c + NBUF - 1;
-                if (cn < nchunks) buf[(s + NBUF - 1) % NBUF].load(q_, k_, v_, cn * C, L, mb);
-            }
+            buf[(s + NBUF - 1) % NBUF].load(q_, k_, v_, (c + NBUF - 1) * C, L, mb);
+            // keep the prefetch here: sunk towards the loop end it would be
+            // the youngest load at the next chunk and stall the pipeline
+            __builtin_amdgcn_sched_barrier(0);
 
             // S_{c-1} (and z_{c-1}) as A operands: A = S^T (rows m, k = e)
             F sh[EB], sl[EB], zh[EB], zl[EB];
@@ -147,6 +147,7 @@ __global__ __launch_bounds__(64) void cp_fwd_kernel(const T *__restrict__ Q, con
                 if constexpr (NORM) O::split(z[e], zh[e], zl[e]);
             }
 
+            const Rows<T> ro(o_, M, row0, L, C);
 #pragma unroll
             for (int I = 0; I < CB; ++I) {
                 f32x4 o = zero4(), d = zero4();
@@ -174,7 +175,7 @@ __global__ __launch_bounds__(64) void cp_fwd_kernel(const T *__restrict__ Q, con
 #pragma unroll
                     for (int t = 0; t < 4; ++t) o[t] = o[t] / (d[t] + eps);
                 }
-                st_out<T>(o_, M, row0, L, I, mb, o);
+                st_out<T>(ro, I, mb, o);
             }
 
             // S_c = S_{c-1} + K_c^T V_c  (and z_c = z_{c-1} + K_c^T 1)
@@ -184,7 +185,7 @@ __global__ __launch_bounds__(64) void cp_fwd_kernel(const T *__restrict__ Q, con
                 if constexpr (NORM)
                     dotk<T>(z[e], 0, CB, [&](int J) { return kt[J][e]; }, [&](int) { return O::ones(); });
             }
-            __syncthreads();
+            wave_lds_sync();
         }
     }
 
