@@ -24,9 +24,12 @@ SOURCES = ["cp_api.cpp", "cp_fwd_f32.hip", "cp_fwd_bf16.hip", "cp_bwd_f32.hip", 
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
-# Packed fp32 instructions are kept out of the generated code.
+# Packed fp32 instructions are kept out of the generated code; MFMA results
+# stay in ordinary VGPRs (no copies between accumulation registers and VGPRs
+# when tiles are converted and fed back as operands).
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
-         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wno-unused-command-line-argument"]
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-mllvm", "-amdgpu-mfma-vgpr-form",
+         "-Wno-unused-command-line-argument"]
 
 
 def _compile(src: str, build_dir: str, defines: dict) -> str:

@@ -1,9 +1,9 @@
 // cp_device.hpp -- wave-level building blocks of the causal-product kernels
-// for gfx950 (CDNA4): 16x16 MFMA tiles, operand fragments and their loads.
+// for gfx950 (CDNA4): 16x16 MFMA tiles, operand fragments, and the staging of
+// chunks of the inputs through LDS.
 //
-// Every kernel in this library runs one 64-lane wave per workgroup and splits
-// lane l into g = l / 16 (0..3) and r = l % 16.  All matrix products are
-// 16 x 16 output tiles D += A * B computed by MFMA:
+// Lane l of a 64-lane wave is split into g = l / 16 (0..3) and r = l % 16.
+// All matrix products are 16 x 16 output tiles D += A * B computed by MFMA:
 //   bf16 I/O: v_mfma_f32_16x16x32_bf16 (A 16x32, B 32x16, fp32 accumulate)
 //   fp32 I/O: v_mfma_f32_16x16x4_f32   (A 16x4,  B 4x16)
 // with these lane layouts (checked on gfx950):
@@ -18,18 +18,18 @@
 // rows 4g + t in lane (g, r), a result tile D can be fed back without any
 // lane shuffle: as a B operand it is D itself, as an A operand it is D^T.
 //
-// Three fragment sources are used:
-//   natural  (ld_nat):  lane (g, r) <- X[row0 + 16 rb + r][16 cb + 4g + t]
-//            4 consecutive elements of one row, read straight from HBM with
-//            a buffer load.
-//            As an A operand this is X, as a B operand X^T.
+// Inputs reach the waves through LDS: every thread of a workgroup copies
+// 16-byte pieces of a chunk of rows from HBM (buffer loads, kept in registers
+// while the previous chunk is computed) into a natural row-major copy in LDS.
+// Fragments are then read from that copy in two ways:
+//   natural  (lds_nat): lane (g, r) <- X[16 rb + r][16 cb + 4g + t]
+//            (four consecutive elements of one row).  As an A operand this is
+//            X, as a B operand X^T.
 //   transposed (tr_frag): lane (g, r) <- X[16 tb + 4g + t][16 cb + r]
-//            4 consecutive rows of one column, read from a natural copy of
-//            the chunk in LDS (bf16: one ds_read_b64_tr_b16, which hands lane
-//            i of each 16-lane group element i of the four 16-element rows
-//            addressed by lanes 4a..4a+3).  As an A operand this is X^T, as a
-//            B operand X.
-//   result tiles, as above.
+//            (four consecutive rows of one column; bf16: one
+//            ds_read_b64_tr_b16, which hands lane i of each 16-lane group
+//            element i of the four 16-element rows addressed by lanes
+//            4a..4a+3).  As an A operand this is X^T, as a B operand X.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -57,7 +57,6 @@ template <typename T> struct Ops;
 // bf16 I/O: fragments are 4 bf16; MFMA over two k-blocks at a time.
 template <> struct Ops<bf16> {
     using frag = bf16x4;
-    static constexpr int kPad = 8;  // LDS row padding (elements)
 
     __device__ static __forceinline__ frag zero() {
         s16x4 z = {0, 0, 0, 0};
@@ -75,6 +74,13 @@ template <> struct Ops<bf16> {
     __device__ static __forceinline__ void mma1(f32x4 &acc, frag a0, frag b0) {
         mma2(acc, a0, zero(), b0, zero());
     }
+    // the same products into a fresh accumulator (inline zero operand)
+    __device__ static __forceinline__ f32x4 mma2z(frag a0, frag a1, frag b0, frag b1) {
+        bf16x8 a = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
+        bf16x8 b = __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7);
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, zero4(), 0, 0, 0);
+    }
+    __device__ static __forceinline__ f32x4 mma1z(frag a0, frag b0) { return mma2z(a0, zero(), b0, zero()); }
     __device__ static __forceinline__ frag cvt(f32x4 x) {
         frag f;
 #pragma unroll
@@ -115,7 +121,6 @@ template <> struct Ops<bf16> {
 // so a k-block is four MFMAs (t = 0..3 pairs k = 4g + t on both operands).
 template <> struct Ops<float> {
     using frag = f32x4;
-    static constexpr int kPad = 4;
 
     __device__ static __forceinline__ frag zero() { return zero4(); }
     __device__ static __forceinline__ frag ones() {
@@ -129,6 +134,17 @@ template <> struct Ops<float> {
     __device__ static __forceinline__ void mma2(f32x4 &acc, frag a0, frag a1, frag b0, frag b1) {
         mma1(acc, a0, b0);
         mma1(acc, a1, b1);
+    }
+    __device__ static __forceinline__ f32x4 mma1z(frag a, frag b) {
+        f32x4 acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[0], b[0], zero4(), 0, 0, 0);
+#pragma unroll
+        for (int t = 1; t < 4; ++t) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[t], b[t], acc, 0, 0, 0);
+        return acc;
+    }
+    __device__ static __forceinline__ f32x4 mma2z(frag a0, frag a1, frag b0, frag b1) {
+        f32x4 acc = mma1z(a0, b0);
+        mma1(acc, a1, b1);
+        return acc;
     }
     __device__ static __forceinline__ frag cvt(f32x4 x) { return x; }
     __device__ static __forceinline__ void split(f32x4 x, frag &hi, frag &lo) {
@@ -146,6 +162,14 @@ template <> struct Ops<float> {
     }
 };
 
+// lane (g, r) <- X[16 rb + r][16 cb + 4g + t] from a natural LDS copy with
+// row stride rs (elements).
+template <typename T>
+__device__ __forceinline__ typename Ops<T>::frag lds_nat(const T *lds, int rs, int rb, int cb) {
+    return *reinterpret_cast<const typename Ops<T>::frag *>(lds + (16 * rb + lane_r()) * rs + 16 * cb +
+                                                             4 * lane_g());
+}
+
 // acc += sum over k-blocks b in [b0, b1) of A_b * B_b.  For bf16 the blocks
 // go to the MFMA in pairs; an odd count is padded with a zero block.
 template <typename T, typename FA, typename FB>
@@ -156,6 +180,18 @@ __device__ __forceinline__ void dotk(f32x4 &acc, int b0, int b1, FA fa, FB fb) {
     for (; b + 1 < b1; b += 2) O::mma2(acc, fa(b), fa(b + 1), fb(b), fb(b + 1));
     if (b < b1) O::mma1(acc, fa(b), fb(b));
 }
+
+// sum over k-blocks b in [b0, b1) of A_b * B_b into a fresh tile (b1 > b0).
+template <typename T, typename FA, typename FB>
+__device__ __forceinline__ f32x4 dotz(int b0, int b1, FA fa, FB fb) {
+    using O = Ops<T>;
+    f32x4 acc = (b0 + 1 < b1) ? O::mma2z(fa(b0), fa(b0 + 1), fb(b0), fb(b0 + 1)) : O::mma1z(fa(b0), fb(b0));
+    dotk<T>(acc, b0 + 2, b1, fa, fb);
+    return acc;
+}
+
+// phi(x) = elu(x) + 1 = x + 1 for x > 0, exp(x) otherwise.
+__device__ __forceinline__ float phi(float x) { return x > 0.f ? x + 1.f : __expf(x); }
 
 // A chunk of C rows of one row-major slice (leading dimension ld elements),
 // addressed through a buffer resource whose range ends at row L: loads past
@@ -181,19 +217,6 @@ struct Rows {
     }
 };
 
-// Natural fragment of the 16-row block rb: lane (g, r) <- X[16 rb + r][16 cb + 4g + t].
-template <typename T>
-__device__ __forceinline__ typename Ops<T>::frag ld_nat(const Rows<T> &X, int rb, int cb) {
-    const int off = ((16 * rb + lane_r()) * X.ld + 16 * cb + 4 * lane_g()) * (int)sizeof(T);
-    if constexpr (sizeof(T) == 2) {
-        auto v = __builtin_amdgcn_raw_buffer_load_b64(X.rsrc, off, 0, 0);
-        return __builtin_bit_cast(typename Ops<T>::frag, v);
-    } else {
-        auto v = __builtin_amdgcn_raw_buffer_load_b128(X.rsrc, off, 0, 0);
-        return __builtin_bit_cast(typename Ops<T>::frag, v);
-    }
-}
-
 // Store a transposed result tile: lane (g, r) holds X[16 rb + r][16 cb + 4g + t].
 template <typename T>
 __device__ __forceinline__ void st_out(const Rows<T> &X, int rb, int cb, f32x4 v) {
@@ -207,11 +230,61 @@ __device__ __forceinline__ void st_out(const Rows<T> &X, int rb, int cb, f32x4 v
     }
 }
 
-// Store a natural fragment into an LDS copy of the chunk (row stride rs).
-template <typename T>
-__device__ __forceinline__ void st_lds(T *lds, int rs, int rb, int cb, typename Ops<T>::frag f) {
-    *reinterpret_cast<typename Ops<T>::frag *>(lds + (16 * rb + lane_r()) * rs + 16 * cb + 4 * lane_g()) = f;
-}
+// Row stride (elements) of the LDS copy of a W-column chunk: padded by 16
+// bytes so that consecutive rows start in different banks; a multiple of 16
+// bytes so that every row starts 16-byte aligned.
+template <typename T, int W>
+constexpr int lds_stride() { return W + 16 / (int)sizeof(T); }
+
+typedef int i32x4 __attribute__((__vector_size__(4 * sizeof(int))));
+
+// One thread's share of a chunk copy: rows [row0, row0 + C) and columns
+// [col0, col0 + W) of a row-major slice, as 16-byte pieces spread over the NT
+// threads of the workgroup (piece p = row * W*sizeof(T)/16 + column piece).
+// load() issues the buffer loads (rows outside [0, L) read as zero); store()
+// writes the pieces into the LDS copy, optionally through phi (the
+// elementwise feature map, with rows at or past L kept zero).
+template <typename T, int NT, int C, int W>
+struct Stage {
+    static constexpr int PPR = W * (int)sizeof(T) / 16;  // pieces per row
+    static constexpr int P = C * PPR;
+    static constexpr int NP = (P + NT - 1) / NT;
+    static constexpr int RS = lds_stride<T, W>();
+    static_assert(W * (int)sizeof(T) % 16 == 0, "rows must be whole 16-byte pieces");
+    i32x4 v[NP];
+
+    __device__ __forceinline__ void load(const Rows<T> &X, int col0) {
+#pragma unroll
+        for (int i = 0; i < NP; ++i) {
+            const int p = (int)threadIdx.x + i * NT;
+            const int row = p / PPR, cp = p % PPR;
+            int off = (row * X.ld + col0) * (int)sizeof(T) + cp * 16;
+            if constexpr (P % NT != 0) off = p < P ? off : 0x7FFFFFF0;  // past the range: zero
+            v[i] = __builtin_amdgcn_raw_buffer_load_b128(X.rsrc, off, 0, 0);
+        }
+    }
+
+    template <bool PHI = false>
+    __device__ __forceinline__ void store(T *lds, int row0 = 0, int L = 0) const {
+#pragma unroll
+        for (int i = 0; i < NP; ++i) {
+            const int p = (int)threadIdx.x + i * NT;
+            const int row = p / PPR, cp = p % PPR;
+            if (P % NT != 0 && p >= P) continue;
+            i32x4 x = v[i];
+            if constexpr (PHI) {
+                constexpr int n = 16 / (int)sizeof(T);
+                typedef T tn __attribute__((__vector_size__(16)));
+                tn e = __builtin_bit_cast(tn, x);
+                const bool valid = row0 + row < L;
+#pragma unroll
+                for (int j = 0; j < n; ++j) e[j] = valid ? (T)phi((float)e[j]) : (T)0.f;
+                x = __builtin_bit_cast(i32x4, e);
+            }
+            *reinterpret_cast<i32x4 *>(lds + row * RS + cp * (16 / (int)sizeof(T))) = x;
+        }
+    }
+};
 
 // Order this wave's LDS writes before its later LDS reads of other lanes'
 // data and vice versa.  A workgroup here is a single wave, so this is all the
@@ -222,25 +295,30 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Causal mask of a diagonal tile in the layout D[j][i] (rows = keys j,
-// columns = queries i): keep j <= i, i.e. 4g + t <= r.
-__device__ __forceinline__ f32x4 mask_keys_rows(f32x4 a) {
-    const int g = lane_g(), r = lane_r();
+// Causal masks of a diagonal 16x16 tile.  Lane (g, r) holds rows 4g + t of
+// column r; the keep-predicates depend on the lane only and are computed once.
+struct Diag {
+    bool keys_rows[4];   // layout D[j][i] (rows = keys, columns = queries): keep j <= i
+    bool query_rows[4];  // layout D[i][j] (rows = queries, columns = keys): keep j <= i
+    __device__ __forceinline__ Diag() {
+        const int g = lane_g(), r = lane_r();
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
-        if (4 * g + t > r) a[t] = 0.f;
-    return a;
-}
-
-// Causal mask of a diagonal tile in the layout D[i][j] (rows = queries i,
-// columns = keys j): keep j <= i, i.e. r <= 4g + t.
-__device__ __forceinline__ f32x4 mask_query_rows(f32x4 a) {
-    const int g = lane_g(), r = lane_r();
+        for (int t = 0; t < 4; ++t) {
+            keys_rows[t] = 4 * g + t <= r;
+            query_rows[t] = r <= 4 * g + t;
+        }
+    }
+    __device__ __forceinline__ f32x4 keys(f32x4 a) const {
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
-        if (r > 4 * g + t) a[t] = 0.f;
-    return a;
-}
+        for (int t = 0; t < 4; ++t) a[t] = keys_rows[t] ? a[t] : 0.f;
+        return a;
+    }
+    __device__ __forceinline__ f32x4 query(f32x4 a) const {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) a[t] = query_rows[t] ? a[t] : 0.f;
+        return a;
+    }
+};
 
 // Workgroup id -> (slice, part).  The P parts of one (n, h) slice read the
 // same rows of the inputs, so they are kept on one XCD (workgroups are
@@ -256,15 +334,6 @@ __device__ __forceinline__ void map_block(int b, int NS, int P, int &slice, int 
     }
 }
 
-// phi(x) = elu(x) + 1 = x + 1 for x > 0, exp(x) otherwise.
-__device__ __forceinline__ float phi(float x) { return x > 0.f ? x + 1.f : __expf(x); }
 
-template <typename T>
-__device__ __forceinline__ typename Ops<T>::frag phi_frag(typename Ops<T>::frag f) {
-    f32x4 x = Ops<T>::widen(f);
-#pragma unroll
-    for (int t = 0; t < 4; ++t) x[t] = phi(x[t]);
-    return Ops<T>::cvt(x);
-}
 
 }  // namespace cp

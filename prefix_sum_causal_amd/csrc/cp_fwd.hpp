@@ -12,70 +12,63 @@
 // with T the inclusive lower-triangular mask: the prefix sum runs serially
 // over chunks and in parallel (as small dense products) inside a chunk.
 //
-// One wave owns one (n, h) slice and one 16-column block mb of the output.
-// It streams Q and K in full (the other column blocks of the slice run on the
-// same XCD and take the same rows from L2), V only for its columns, keeps the
-// E x 16 block of the state in MFMA accumulators across all chunks, and works
-// in the transposed output orientation Out^T = V^T A^T + S^T Q^T so that every
-// operand comes either from a natural load, from an LDS transpose read, or
-// from an accumulator tile without shuffles (see cp_device.hpp).
+// A workgroup owns one (n, h) slice and one 16-column block mb of the output
+// and runs RS waves.  Per chunk, all its threads copy Q, K (all E columns) and
+// the V column block into LDS (double buffered, one barrier per chunk) while
+// the next chunk's loads are in flight; each wave then keeps the E x 16 block
+// of the state in MFMA accumulators (every wave carries the same state, which
+// costs a few MFMAs and saves any exchange), and computes the output rows of
+// its share of the chunk's 16-row blocks.  The shares are balanced pairs
+// (block k and C/16-1-k carry equal causal work), so all workgroups do the
+// same work per chunk and the M/16 workgroups of a slice, placed on one XCD,
+// stay in step and take the slice's Q and K rows from its L2.  Products run
+// in the transposed orientation Out^T = V^T A^T + S^T Q^T so that every
+// operand is a natural or transposed LDS read or an accumulator tile.
 //
 // Normalised form (NORM): out_i = phi(q_i)^T S_i / (phi(q_i) . z_i + eps) with
-// z_i = sum_{j<=i} phi(k_j).  Per chunk, the denominator of token i is the
-// masked row sum of the chunk's scores plus phi(q_i) . z_{c-1}; both are one
-// extra MFMA row computed next to the numerator, z is carried across chunks
-// like S (z_c = z_{c-1} + column sums of phi(K_c)), and the division happens
-// in registers before the store.
+// z_i = sum_{j<=i} phi(k_j).  phi is applied while the chunk is copied into
+// LDS.  The denominator of token i is the masked row sum of the chunk's scores
+// plus phi(q_i) . z_{c-1} (one extra MFMA row beside the numerator); z is
+// carried like S (z_c = z_{c-1} + column sums of phi(K_c), the running
+// inclusive sum of phi(k)); the division happens before the store.
 #pragma once
 
 #include "cp_device.hpp"
 
 namespace cp {
 
-template <typename T, int E, int M, int C>
-struct FwdChunk {
-    using F = typename Ops<T>::frag;
-    static constexpr int EB = E / 16, CB = C / 16;
-    F q[CB][EB];  // Q[row0 + 16 I + r][16 eb + 4g + t]
-    F k[CB][EB];  // K[row0 + 16 J + r][16 eb + 4g + t]
-    F v[CB];      // V[row0 + 16 J + r][16 mb + 4g + t]
+// Query row block handled by wave w in round k: a snake over the waves, so
+// that each wave gets block k and block C/16-1-k worth of causal work.
+template <int RS>
+__device__ __forceinline__ int owned_block(int k, int w) {
+    return (k & 1) ? k * RS + (RS - 1 - w) : k * RS + w;
+}
 
-    // Rows at or past L (and whole chunks past the end) load as zero.
-    __device__ __forceinline__ void load(const T *q_, const T *k_, const T *v_, int row0, int L, int mb) {
-        const Rows<T> rq(q_, E, row0, L, C), rk(k_, E, row0, L, C), rv(v_, M, row0, L, C);
-#pragma unroll
-        for (int b = 0; b < CB; ++b) {
-#pragma unroll
-            for (int e = 0; e < EB; ++e) {
-                q[b][e] = ld_nat<T>(rq, b, e);
-                k[b][e] = ld_nat<T>(rk, b, e);
-            }
-            v[b] = ld_nat<T>(rv, b, mb);
-        }
-    }
-};
-
-template <typename T, int E, int M, int C, int NBUF, bool NORM, bool HILO>
-__global__ __launch_bounds__(64) void cp_fwd_kernel(const T *__restrict__ Q, const T *__restrict__ K,
-                                                    const T *__restrict__ V, T *__restrict__ Out,
-                                                    float *__restrict__ state_out, int L, int NS,
-                                                    float eps, int fmap) {
-    static_assert(NBUF >= 2, "the pipeline needs at least two chunk buffers");
+template <typename T, int E, int M, int C, int RS, bool NORM, bool FMAP, bool HILO>
+__global__ __launch_bounds__(64 * RS) void cp_fwd_kernel(const T *__restrict__ Q, const T *__restrict__ K,
+                                                         const T *__restrict__ V, T *__restrict__ Out,
+                                                         float *__restrict__ state_out, int L, int NS,
+                                                         float eps) {
     using O = Ops<T>;
     using F = typename O::frag;
-    constexpr int EB = E / 16, MB = M / 16, CB = C / 16;
-    constexpr int RSK = E + O::kPad, RSV = 16 + O::kPad;
-    __shared__ __attribute__((aligned(16))) T ldsK[C * RSK];
-    __shared__ __attribute__((aligned(16))) T ldsV[C * RSV];
+    constexpr int NT = 64 * RS, EB = E / 16, MB = M / 16, CB = C / 16;
+    static_assert(CB % RS == 0, "the chunk's row blocks are shared evenly by the waves");
+    using SQ = Stage<T, NT, C, E>;
+    using SV = Stage<T, NT, C, 16>;
+    constexpr int RQ = SQ::RS, RV = SV::RS;
+    constexpr int BUF = 2 * C * RQ + C * RV;  // Q, K, V block
+    __shared__ __attribute__((aligned(16))) T lds[2 * BUF];
 
     int slice, mb;
     map_block(blockIdx.x, NS, MB, slice, mb);
+    const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
     const int g = lane_g(), r = lane_r();
     const T *q_ = Q + (int64_t)slice * L * E;
     const T *k_ = K + (int64_t)slice * L * E;
     const T *v_ = V + (int64_t)slice * L * M;
     T *o_ = Out + (int64_t)slice * L * M;
 
+    const Diag diag;
     f32x4 S[EB];  // S[16 eb + 4g + t][16 mb + r]
     f32x4 z[EB];  // z[16 eb + 4g + t] (same in every lane r)
 #pragma unroll
@@ -84,113 +77,107 @@ __global__ __launch_bounds__(64) void cp_fwd_kernel(const T *__restrict__ Q, con
         z[e] = zero4();
     }
 
-    // The chunk loop is padded to a multiple of NBUF; padded chunks lie past
-    // L, load as zero and store nothing, so every step issues the same loads.
+    SQ sq, sk;
+    SV sv;
+    sq.load(Rows<T>(q_, E, 0, L, C), 0);
+    sk.load(Rows<T>(k_, E, 0, L, C), 0);
+    sv.load(Rows<T>(v_, M, 0, L, C), 16 * mb);
+
+    // Output tiles of a chunk are stored at the start of the next step,
+    // before its prefetch: vector memory operations complete in issue order,
+    // so waiting for the prefetched rows never waits for stores.
+    constexpr int KB = CB / RS;  // row blocks per wave
+    f32x4 pend[KB];
+#pragma unroll
+    for (int k = 0; k < KB; ++k) pend[k] = zero4();
+
     const int nchunks = (L + C - 1) / C;
-    const int nsteps = (nchunks + NBUF - 1) / NBUF * NBUF;
-    FwdChunk<T, E, M, C> buf[NBUF];
+    for (int c = 0; c < nchunks; ++c) {
+        const int row0 = c * C;
+        T *Qs = lds + (c & 1) * BUF, *Ks = Qs + C * RQ, *Vs = Ks + C * RQ;
+        sq.template store<NORM && FMAP>(Qs, row0, L);
+        sk.template store<NORM && FMAP>(Ks, row0, L);
+        sv.store(Vs);
+        __syncthreads();
+        {
+            const Rows<T> rp(o_, M, row0 - C, L, C);  // previous chunk (none at c = 0: dropped)
 #pragma unroll
-    for (int s = 0; s < NBUF - 1; ++s) {
-        buf[s].load(q_, k_, v_, s * C, L, mb);
-        __builtin_amdgcn_sched_barrier(0);  // buffers complete in order
-    }
+            for (int k = 0; k < KB; ++k) st_out<T>(rp, owned_block<RS>(k, w), mb, pend[k]);
+        }
+        // the next chunk's loads stay in flight while this one is computed
+        sq.load(Rows<T>(q_, E, row0 + C, L, C), 0);
+        sk.load(Rows<T>(k_, E, row0 + C, L, C), 0);
+        sv.load(Rows<T>(v_, M, row0 + C, L, C), 16 * mb);
+        __builtin_amdgcn_sched_barrier(0);
 
-    for (int c0 = 0; c0 < nsteps; c0 += NBUF) {
+        // S_{c-1} (and z_{c-1}) as A operands: A = S^T (rows m, k = e)
+        F sh[EB], sl[EB], zh[EB], zl[EB];
 #pragma unroll
-        for (int s = 0; s < NBUF; ++s) {
-            const int c = c0 + s;
-            const int row0 = c * C;
-            FwdChunk<T, E, M, C> &cur = buf[s];
+        for (int e = 0; e < EB; ++e) {
+            if constexpr (HILO) O::split(S[e], sh[e], sl[e]);
+            else sh[e] = O::cvt(S[e]);
+            if constexpr (NORM) O::split(z[e], zh[e], zl[e]);
+        }
+
+#pragma unroll
+        for (int k = 0; k < KB; ++k) {
+            const int I = owned_block<RS>(k, w);
+            F qI[EB];  // Q[16 I + r][16 eb + 4g + t]
+#pragma unroll
+            for (int e = 0; e < EB; ++e) qI[e] = lds_nat<T>(Qs, RQ, I, e);
+            f32x4 o = zero4(), d = zero4();
+            // inter-chunk: Out^T += S^T Q_I^T
+            dotk<T>(o, 0, EB, [&](int e) { return sh[e]; }, [&](int e) { return qI[e]; });
+            if constexpr (HILO)
+                dotk<T>(o, 0, EB, [&](int e) { return sl[e]; }, [&](int e) { return qI[e]; });
             if constexpr (NORM) {
-                if (fmap) {
-                    // phi(0) = 1, so rows past L are zeroed again after the map
-#pragma unroll
-                    for (int b = 0; b < CB; ++b) {
-                        const bool valid = row0 + 16 * b + r < L;
-#pragma unroll
-                        for (int e = 0; e < EB; ++e) {
-                            const F pq = phi_frag<T>(cur.q[b][e]), pk = phi_frag<T>(cur.k[b][e]);
-                            cur.q[b][e] = valid ? pq : O::zero();
-                            cur.k[b][e] = valid ? pk : O::zero();
-                        }
-                    }
+                dotk<T>(d, 0, EB, [&](int e) { return zh[e]; }, [&](int e) { return qI[e]; });
+                dotk<T>(d, 0, EB, [&](int e) { return zl[e]; }, [&](int e) { return qI[e]; });
+            }
+            // intra-chunk: Out^T += V^T A^T with A^T(J, I) = K_J Q_I^T masked
+            // on the diagonal, key blocks J <= I taken in pairs
+            for (int J0 = 0; J0 <= I; J0 += 2) {
+                f32x4 a0 = dotz<T>(0, EB, [&](int e) { return lds_nat<T>(Ks, RQ, J0, e); },
+                                   [&](int e) { return qI[e]; });
+                if (J0 == I) a0 = diag.keys(a0);
+                F at1 = O::zero(), vt1 = O::zero();
+                if (J0 + 1 <= I) {
+                    f32x4 a1 = dotz<T>(0, EB, [&](int e) { return lds_nat<T>(Ks, RQ, J0 + 1, e); },
+                                       [&](int e) { return qI[e]; });
+                    if (J0 + 1 == I) a1 = diag.keys(a1);
+                    at1 = O::cvt(a1);
+                    vt1 = O::tr_frag(Vs, RV, J0 + 1, 0);
                 }
+                const F at0 = O::cvt(a0);
+                O::mma2(o, O::tr_frag(Vs, RV, J0, 0), vt1, at0, at1);
+                if constexpr (NORM) O::mma2(d, O::ones(), O::ones(), at0, at1);
             }
-            // natural copies of K (all columns) and V (this block) for the
-            // transposed reads of the state update and of V^T A^T
+            if constexpr (NORM) {
 #pragma unroll
-            for (int b = 0; b < CB; ++b) {
-#pragma unroll
-                for (int e = 0; e < EB; ++e) st_lds<T>(ldsK, RSK, b, e, cur.k[b][e]);
-                st_lds<T>(ldsV, RSV, b, 0, cur.v[b]);
+                for (int t = 0; t < 4; ++t) o[t] = o[t] / (d[t] + eps);
             }
-            wave_lds_sync();
-            F kt[CB][EB], vt[CB];  // K[16 J + 4g + t][16 eb + r], V[16 J + 4g + t][16 mb + r]
-#pragma unroll
-            for (int b = 0; b < CB; ++b) {
-#pragma unroll
-                for (int e = 0; e < EB; ++e) kt[b][e] = O::tr_frag(ldsK, RSK, b, e);
-                vt[b] = O::tr_frag(ldsV, RSV, b, 0);
-            }
-            // keep NBUF-1 chunks in flight while this one is computed
-            buf[(s + NBUF - 1) % NBUF].load(q_, k_, v_, (c + NBUF - 1) * C, L, mb);
-            // keep the prefetch here: sunk towards the loop end it would be
-            // the youngest load at the next chunk and stall the pipeline
-            __builtin_amdgcn_sched_barrier(0);
+            pend[k] = o;
+        }
 
-            // S_{c-1} (and z_{c-1}) as A operands: A = S^T (rows m, k = e)
-            F sh[EB], sl[EB], zh[EB], zl[EB];
+        // S_c = S_{c-1} + K_c^T V_c  (and z_c = z_{c-1} + K_c^T 1)
 #pragma unroll
-            for (int e = 0; e < EB; ++e) {
-                if constexpr (HILO) O::split(S[e], sh[e], sl[e]);
-                else sh[e] = O::cvt(S[e]);
-                if constexpr (NORM) O::split(z[e], zh[e], zl[e]);
-            }
-
-            const Rows<T> ro(o_, M, row0, L, C);
-#pragma unroll
-            for (int I = 0; I < CB; ++I) {
-                f32x4 o = zero4(), d = zero4();
-                // inter-chunk: Out^T += S^T Q_I^T
-                dotk<T>(o, 0, EB, [&](int e) { return sh[e]; }, [&](int e) { return cur.q[I][e]; });
-                if constexpr (HILO)
-                    dotk<T>(o, 0, EB, [&](int e) { return sl[e]; }, [&](int e) { return cur.q[I][e]; });
-                if constexpr (NORM) {
-                    dotk<T>(d, 0, EB, [&](int e) { return zh[e]; }, [&](int e) { return cur.q[I][e]; });
-                    dotk<T>(d, 0, EB, [&](int e) { return zl[e]; }, [&](int e) { return cur.q[I][e]; });
-                }
-                // intra-chunk scores A^T(J, I) = K_J Q_I^T, causal on the diagonal
-                F at[CB];
-#pragma unroll
-                for (int J = 0; J <= I; ++J) {
-                    f32x4 a = zero4();
-                    dotk<T>(a, 0, EB, [&](int e) { return cur.k[J][e]; }, [&](int e) { return cur.q[I][e]; });
-                    if (J == I) a = mask_keys_rows(a);
-                    at[J] = O::cvt(a);
-                }
-                // Out^T += V^T A^T
-                dotk<T>(o, 0, I + 1, [&](int J) { return vt[J]; }, [&](int J) { return at[J]; });
-                if constexpr (NORM) {
-                    dotk<T>(d, 0, I + 1, [&](int) { return O::ones(); }, [&](int J) { return at[J]; });
-#pragma unroll
-                    for (int t = 0; t < 4; ++t) o[t] = o[t] / (d[t] + eps);
-                }
-                st_out<T>(ro, I, mb, o);
-            }
-
-            // S_c = S_{c-1} + K_c^T V_c  (and z_c = z_{c-1} + K_c^T 1)
-#pragma unroll
-            for (int e = 0; e < EB; ++e) {
-                dotk<T>(S[e], 0, CB, [&](int J) { return kt[J][e]; }, [&](int J) { return vt[J]; });
-                if constexpr (NORM)
-                    dotk<T>(z[e], 0, CB, [&](int J) { return kt[J][e]; }, [&](int) { return O::ones(); });
-            }
-            wave_lds_sync();
+        for (int e = 0; e < EB; ++e) {
+            dotk<T>(S[e], 0, CB, [&](int J) { return O::tr_frag(Ks, RQ, J, e); },
+                    [&](int J) { return O::tr_frag(Vs, RV, J, 0); });
+            if constexpr (NORM)
+                dotk<T>(z[e], 0, CB, [&](int J) { return O::tr_frag(Ks, RQ, J, e); },
+                        [&](int) { return O::ones(); });
         }
     }
 
+    {
+        const Rows<T> rp(o_, M, (nchunks - 1) * C, L, C);
+#pragma unroll
+        for (int k = 0; k < KB; ++k) st_out<T>(rp, owned_block<RS>(k, w), mb, pend[k]);
+    }
+
     if constexpr (!NORM) {
-        if (state_out) {
+        if (state_out && w == 0) {
             float *st = state_out + (int64_t)slice * E * M;
 #pragma unroll
             for (int e = 0; e < EB; ++e)

@@ -34,9 +34,9 @@ fwd_fn fwd_bf16(int E, int M, bool norm);
 bwd_fn bwd_f32(int E, int M);
 bwd_fn bwd_bf16(int E, int M);
 
-// Waves per (n, h) slice of each kernel.
+// Workgroups per (n, h) slice of each kernel.
 inline int fwd_parts(int E, int M) { (void)E; return M / 16; }
-inline int bwd_parts(int E, int M) { return 2 * (E / 16) + M / 16; }
+inline int bwd_parts(int E, int M) { return (E > M ? E : M) / 16; }
 
 // Index 0..3 of a head size in {16, 32, 64, 128}, -1 otherwise.
 inline int size_index(int64_t x) {

@@ -1,28 +1,37 @@
 // cp_tune.hpp -- compile-time launch parameters of each kernel instance:
-// chunk length C (tokens per step of the scan), NBUF (register buffers of
-// the load pipeline: NBUF-1 chunks are in flight while one is computed) and
-// HILO (carried states enter the bf16 MFMA as a hi + lo pair of bf16 values,
-// 16 significant bits instead of 8).  Each value can be overridden when the
-// library is built (-DCP_BF16_C=64 ...) for tuning sweeps.
+//   FC   forward chunk length (tokens per step of the scan),
+//   RS   forward waves per workgroup (they share a chunk's query row blocks),
+//   BC   backward chunk length,
+//   HILO carried states enter the bf16 MFMA as a hi + lo pair of bf16 values
+//        (16 significant bits instead of 8).  Off by default: the bf16 score
+//        tiles dominate the error either way (measured max relative error at
+//        L=4096, E=M=64: forward 2.7e-3 without, 2.3e-3 with; backward
+//        3.6e-3 without, 2.6e-3 with), and the split costs a quarter of the
+//        forward's time.
+// Each value can be overridden when the library is built (-DCP_BF16_FC=32 ...)
+// for tuning sweeps.
 #pragma once
 
-#ifndef CP_BF16_C
-#define CP_BF16_C 32
+#ifndef CP_BF16_FC
+#define CP_BF16_FC 64
 #endif
-#ifndef CP_BF16_NBUF
-#define CP_BF16_NBUF 2
+#ifndef CP_BF16_RS
+#define CP_BF16_RS 2
+#endif
+#ifndef CP_BF16_BC
+#define CP_BF16_BC 32
 #endif
 #ifndef CP_BF16_HILO
-#define CP_BF16_HILO 1
+#define CP_BF16_HILO 0
 #endif
-#ifndef CP_F32_C
-#define CP_F32_C 32
+#ifndef CP_F32_FC
+#define CP_F32_FC 32
 #endif
-#ifndef CP_F32_C_WIDE
-#define CP_F32_C_WIDE 16
+#ifndef CP_F32_RS
+#define CP_F32_RS 2
 #endif
-#ifndef CP_F32_NBUF
-#define CP_F32_NBUF 2
+#ifndef CP_F32_BC
+#define CP_F32_BC 32
 #endif
 
 namespace cp {
@@ -30,14 +39,19 @@ namespace cp {
 template <typename T, int E, int M> struct Tune;
 
 template <int E, int M> struct Tune<__bf16, E, M> {
-    static constexpr int C = CP_BF16_C;
-    static constexpr int NBUF = CP_BF16_NBUF;
+    static constexpr int FC = CP_BF16_FC;
+    static constexpr int RS = CP_BF16_RS;
+    static constexpr int BC = CP_BF16_BC;
     static constexpr bool HILO = CP_BF16_HILO != 0;
 };
 
+// fp32 tiles are twice as large in LDS and registers: the widest heads use
+// shorter chunks.
 template <int E, int M> struct Tune<float, E, M> {
-    static constexpr int C = (E > 64 || M > 64) ? CP_F32_C_WIDE : CP_F32_C;
-    static constexpr int NBUF = CP_F32_NBUF;
+    static constexpr bool wide = E > 64 || M > 64;
+    static constexpr int FC = wide ? 16 : CP_F32_FC;
+    static constexpr int RS = wide ? 1 : CP_F32_RS;
+    static constexpr int BC = wide ? 16 : CP_F32_BC;
     static constexpr bool HILO = false;
 };
 
