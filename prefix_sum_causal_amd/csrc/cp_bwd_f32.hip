@@ -10,7 +10,7 @@ template <int E, int M>
 hipError_t launch_bwd(const BwdArgs &a, hipStream_t s) {
     using T = float;
     using P = Tune<T, E, M>;
-    auto kern = cp_bwd_kernel<T, E, M, P::BC, P::HILO>;
+    auto kern = cp_bwd_kernel<T, E, M, P::BC, P::BNPF, P::HILO>;
     const T *q = static_cast<const T *>(a.Q), *k = static_cast<const T *>(a.K), *v = static_cast<const T *>(a.V),
             *g = static_cast<const T *>(a.G);
     const float *st = a.state_in;

@@ -170,6 +170,32 @@ __device__ __forceinline__ typename Ops<T>::frag lds_nat(const T *lds, int rs, i
                                                              4 * lane_g());
 }
 
+// Score-type tile D = X_xb Y_yb^T, D[i][j] = sum_k X[16 xb + i][k] Y[16 yb + j][k]
+// over KB k-blocks, with both operands natural rows of LDS copies.  Only the
+// pairing of k between the operands matters here, so bf16 reads 8
+// consecutive elements per lane (one 16-byte read, k = 32 p + 8g + v) instead
+// of two 4-element fragments.
+template <typename T, int KB>
+__device__ __forceinline__ f32x4 nn_tile(const T *X, int rx, int xb, const T *Y, int ry, int yb) {
+    using O = Ops<T>;
+    if constexpr (sizeof(T) == 2 && KB >= 2) {
+        const int g = lane_g(), r = lane_r();
+        const bf16x8 *xp = reinterpret_cast<const bf16x8 *>(X + (16 * xb + r) * rx + 8 * g);
+        const bf16x8 *yp = reinterpret_cast<const bf16x8 *>(Y + (16 * yb + r) * ry + 8 * g);
+        f32x4 acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xp[0], yp[0], zero4(), 0, 0, 0);
+#pragma unroll
+        for (int p = 1; p < KB / 2; ++p)
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xp[4 * p], yp[4 * p], acc, 0, 0, 0);
+        if constexpr (KB & 1) O::mma1(acc, lds_nat<T>(X, rx, xb, KB - 1), lds_nat<T>(Y, ry, yb, KB - 1));
+        return acc;
+    } else {
+        f32x4 acc = O::mma1z(lds_nat<T>(X, rx, xb, 0), lds_nat<T>(Y, ry, yb, 0));
+#pragma unroll
+        for (int b = 1; b < KB; ++b) O::mma1(acc, lds_nat<T>(X, rx, xb, b), lds_nat<T>(Y, ry, yb, b));
+        return acc;
+    }
+}
+
 // acc += sum over k-blocks b in [b0, b1) of A_b * B_b.  For bf16 the blocks
 // go to the MFMA in pairs; an odd count is padded with a zero block.
 template <typename T, typename FA, typename FB>

@@ -44,7 +44,7 @@ __device__ __forceinline__ int owned_block(int k, int w) {
     return (k & 1) ? k * RS + (RS - 1 - w) : k * RS + w;
 }
 
-template <typename T, int E, int M, int C, int RS, bool NORM, bool FMAP, bool HILO>
+template <typename T, int E, int M, int C, int RS, int NPF, bool NORM, bool FMAP, bool HILO>
 __global__ __launch_bounds__(64 * RS) void cp_fwd_kernel(const T *__restrict__ Q, const T *__restrict__ K,
                                                          const T *__restrict__ V, T *__restrict__ Out,
                                                          float *__restrict__ state_out, int L, int NS,
@@ -53,6 +53,7 @@ __global__ __launch_bounds__(64 * RS) void cp_fwd_kernel(const T *__restrict__ Q
     using F = typename O::frag;
     constexpr int NT = 64 * RS, EB = E / 16, MB = M / 16, CB = C / 16;
     static_assert(CB % RS == 0, "the chunk's row blocks are shared evenly by the waves");
+    static_assert(NPF >= 2, "the load ring needs at least two stages");
     using SQ = Stage<T, NT, C, E>;
     using SV = Stage<T, NT, C, 16>;
     constexpr int RQ = SQ::RS, RV = SV::RS;
@@ -77,37 +78,40 @@ __global__ __launch_bounds__(64 * RS) void cp_fwd_kernel(const T *__restrict__ Q
         z[e] = zero4();
     }
 
-    SQ sq, sk;
-    SV sv;
-    sq.load(Rows<T>(q_, E, 0, L, C), 0);
-    sk.load(Rows<T>(k_, E, 0, L, C), 0);
-    sv.load(Rows<T>(v_, M, 0, L, C), 16 * mb);
-
-    // Output tiles of a chunk are stored at the start of the next step,
-    // before its prefetch: vector memory operations complete in issue order,
-    // so waiting for the prefetched rows never waits for stores.
-    constexpr int KB = CB / RS;  // row blocks per wave
-    f32x4 pend[KB];
+    // Ring of NPF register stages: NPF-1 chunks are in flight while one is
+    // computed.  The step loop is padded to a multiple of NPF; padded chunks
+    // lie past L, load as zero and store nothing.
+    struct Stages {
+        SQ q, k;
+        SV v;
+        __device__ __forceinline__ void load(const T *q_, const T *k_, const T *v_, int row0, int L, int mb) {
+            q.load(Rows<T>(q_, E, row0, L, C), 0);
+            k.load(Rows<T>(k_, E, row0, L, C), 0);
+            v.load(Rows<T>(v_, M, row0, L, C), 16 * mb);
+        }
+    };
+    Stages st[NPF];
 #pragma unroll
-    for (int k = 0; k < KB; ++k) pend[k] = zero4();
+    for (int s = 0; s < NPF - 1; ++s) {
+        st[s].load(q_, k_, v_, s * C, L, mb);
+        __builtin_amdgcn_sched_barrier(0);  // stages complete in order
+    }
+
+    constexpr int KB = CB / RS;  // row blocks per wave
 
     const int nchunks = (L + C - 1) / C;
-    for (int c = 0; c < nchunks; ++c) {
+    const int nsteps = (nchunks + NPF - 1) / NPF * NPF;
+    for (int c0 = 0; c0 < nsteps; c0 += NPF) {
+#pragma unroll
+      for (int s = 0; s < NPF; ++s) {
+        const int c = c0 + s;
         const int row0 = c * C;
         T *Qs = lds + (c & 1) * BUF, *Ks = Qs + C * RQ, *Vs = Ks + C * RQ;
-        sq.template store<NORM && FMAP>(Qs, row0, L);
-        sk.template store<NORM && FMAP>(Ks, row0, L);
-        sv.store(Vs);
+        st[s].q.template store<NORM && FMAP>(Qs, row0, L);
+        st[s].k.template store<NORM && FMAP>(Ks, row0, L);
+        st[s].v.store(Vs);
         __syncthreads();
-        {
-            const Rows<T> rp(o_, M, row0 - C, L, C);  // previous chunk (none at c = 0: dropped)
-#pragma unroll
-            for (int k = 0; k < KB; ++k) st_out<T>(rp, owned_block<RS>(k, w), mb, pend[k]);
-        }
-        // the next chunk's loads stay in flight while this one is computed
-        sq.load(Rows<T>(q_, E, row0 + C, L, C), 0);
-        sk.load(Rows<T>(k_, E, row0 + C, L, C), 0);
-        sv.load(Rows<T>(v_, M, row0 + C, L, C), 16 * mb);
+        st[(s + NPF - 1) % NPF].load(q_, k_, v_, row0 + (NPF - 1) * C, L, mb);
         __builtin_amdgcn_sched_barrier(0);
 
         // S_{c-1} (and z_{c-1}) as A operands: A = S^T (rows m, k = e)
@@ -119,6 +123,7 @@ __global__ __launch_bounds__(64 * RS) void cp_fwd_kernel(const T *__restrict__ Q
             if constexpr (NORM) O::split(z[e], zh[e], zl[e]);
         }
 
+        f32x4 pend[KB];
 #pragma unroll
         for (int k = 0; k < KB; ++k) {
             const int I = owned_block<RS>(k, w);
@@ -137,13 +142,11 @@ __global__ __launch_bounds__(64 * RS) void cp_fwd_kernel(const T *__restrict__ Q
             // intra-chunk: Out^T += V^T A^T with A^T(J, I) = K_J Q_I^T masked
             // on the diagonal, key blocks J <= I taken in pairs
             for (int J0 = 0; J0 <= I; J0 += 2) {
-                f32x4 a0 = dotz<T>(0, EB, [&](int e) { return lds_nat<T>(Ks, RQ, J0, e); },
-                                   [&](int e) { return qI[e]; });
+                f32x4 a0 = nn_tile<T, EB>(Ks, RQ, J0, Qs, RQ, I);
                 if (J0 == I) a0 = diag.keys(a0);
                 F at1 = O::zero(), vt1 = O::zero();
                 if (J0 + 1 <= I) {
-                    f32x4 a1 = dotz<T>(0, EB, [&](int e) { return lds_nat<T>(Ks, RQ, J0 + 1, e); },
-                                       [&](int e) { return qI[e]; });
+                    f32x4 a1 = nn_tile<T, EB>(Ks, RQ, J0 + 1, Qs, RQ, I);
                     if (J0 + 1 == I) a1 = diag.keys(a1);
                     at1 = O::cvt(a1);
                     vt1 = O::tr_frag(Vs, RV, J0 + 1, 0);
@@ -158,6 +161,14 @@ __global__ __launch_bounds__(64 * RS) void cp_fwd_kernel(const T *__restrict__ Q
             }
             pend[k] = o;
         }
+        // Stores go after this step's prefetch: memory operations complete in
+        // issue order, so the rows waited for at a later step were issued
+        // before these stores and never wait for them.
+        {
+            const Rows<T> ro(o_, M, row0, L, C);
+#pragma unroll
+            for (int k = 0; k < KB; ++k) st_out<T>(ro, owned_block<RS>(k, w), mb, pend[k]);
+        }
 
         // S_c = S_{c-1} + K_c^T V_c  (and z_c = z_{c-1} + K_c^T 1)
 #pragma unroll
@@ -168,12 +179,7 @@ __global__ __launch_bounds__(64 * RS) void cp_fwd_kernel(const T *__restrict__ Q
                 dotk<T>(z[e], 0, CB, [&](int J) { return O::tr_frag(Ks, RQ, J, e); },
                         [&](int) { return O::ones(); });
         }
-    }
-
-    {
-        const Rows<T> rp(o_, M, (nchunks - 1) * C, L, C);
-#pragma unroll
-        for (int k = 0; k < KB; ++k) st_out<T>(rp, owned_block<RS>(k, w), mb, pend[k]);
+      }
     }
 
     if constexpr (!NORM) {

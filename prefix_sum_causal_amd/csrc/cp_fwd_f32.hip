@@ -10,7 +10,7 @@ template <int E, int M, bool NORM, bool FMAP>
 hipError_t launch_fwd(const FwdArgs &a, hipStream_t s) {
     using T = float;
     using P = Tune<T, E, M>;
-    auto kern = cp_fwd_kernel<T, E, M, P::FC, P::RS, NORM, FMAP, P::HILO>;
+    auto kern = cp_fwd_kernel<T, E, M, P::FC, P::RS, P::FNPF, NORM, FMAP, P::HILO>;
     const T *q = static_cast<const T *>(a.Q), *k = static_cast<const T *>(a.K), *v = static_cast<const T *>(a.V);
     T *o = static_cast<T *>(a.Out);
     float *st = a.state_out;

@@ -2,6 +2,8 @@
 //   FC   forward chunk length (tokens per step of the scan),
 //   RS   forward waves per workgroup (they share a chunk's query row blocks),
 //   BC   backward chunk length,
+//   FNPF, BNPF  stages of the forward / backward load ring (NPF-1 chunks are
+//        in flight while one is computed),
 //   HILO carried states enter the bf16 MFMA as a hi + lo pair of bf16 values
 //        (16 significant bits instead of 8).  Off by default: the bf16 score
 //        tiles dominate the error either way (measured max relative error at
@@ -16,13 +18,25 @@
 #define CP_BF16_FC 64
 #endif
 #ifndef CP_BF16_RS
-#define CP_BF16_RS 2
+#define CP_BF16_RS 4
 #endif
 #ifndef CP_BF16_BC
-#define CP_BF16_BC 32
+#define CP_BF16_BC 64
+#endif
+#ifndef CP_BF16_FNPF
+#define CP_BF16_FNPF 3
+#endif
+#ifndef CP_BF16_BNPF
+#define CP_BF16_BNPF 3
 #endif
 #ifndef CP_BF16_HILO
 #define CP_BF16_HILO 0
+#endif
+#ifndef CP_F32_FNPF
+#define CP_F32_FNPF 2
+#endif
+#ifndef CP_F32_BNPF
+#define CP_F32_BNPF 2
 #endif
 #ifndef CP_F32_FC
 #define CP_F32_FC 32
@@ -38,10 +52,14 @@ namespace cp {
 
 template <typename T, int E, int M> struct Tune;
 
+// 128-wide heads halve the backward chunk so that two workgroups fit a CU's LDS.
 template <int E, int M> struct Tune<__bf16, E, M> {
+    static constexpr bool wide = E > 64 || M > 64;
     static constexpr int FC = CP_BF16_FC;
     static constexpr int RS = CP_BF16_RS;
-    static constexpr int BC = CP_BF16_BC;
+    static constexpr int BC = wide && CP_BF16_BC > 32 ? 32 : CP_BF16_BC;
+    static constexpr int FNPF = CP_BF16_FNPF;
+    static constexpr int BNPF = CP_BF16_BNPF;
     static constexpr bool HILO = CP_BF16_HILO != 0;
 };
 
@@ -52,6 +70,8 @@ template <int E, int M> struct Tune<float, E, M> {
     static constexpr int FC = wide ? 16 : CP_F32_FC;
     static constexpr int RS = wide ? 1 : CP_F32_RS;
     static constexpr int BC = wide ? 16 : CP_F32_BC;
+    static constexpr int FNPF = CP_F32_FNPF;
+    static constexpr int BNPF = CP_F32_BNPF;
     static constexpr bool HILO = false;
 };
 
