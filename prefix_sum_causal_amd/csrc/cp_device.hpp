@@ -35,6 +35,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace cp {
 
 typedef __bf16 bf16;
@@ -312,6 +314,38 @@ struct Stage {
     }
 };
 
+// Output staging: result tiles go into a natural LDS copy of the chunk's
+// output rows (C rows x W columns), and the workgroup then writes whole rows
+// to HBM as 16-byte pieces -- the same coalesced pattern as the input copy.
+// Stores of 16-row tiles straight from the MFMA layout touch 16 lines per
+// instruction with 8 bytes per lane and stream far slower.
+template <typename T, int NT, int C, int W>
+struct OutStage {
+    static constexpr int PPR = W * (int)sizeof(T) / 16;  // pieces per row
+    static constexpr int P = C * PPR;
+    static constexpr int NP = (P + NT - 1) / NT;
+    static constexpr int RS = lds_stride<T, W>();
+    static_assert(W * (int)sizeof(T) % 16 == 0, "rows must be whole 16-byte pieces");
+
+    // tile lane (g, r) holds X[16 rb + r][16 cb + 4g + t]
+    __device__ static __forceinline__ void put(T *lds, int rb, int cb, f32x4 v) {
+        T *p = lds + (16 * rb + lane_r()) * RS + 16 * cb + 4 * lane_g();
+        *reinterpret_cast<typename Ops<T>::frag *>(p) = Ops<T>::cvt(v);
+    }
+    // rows of X (rows outside the range are dropped), columns [col0, col0 + W)
+    __device__ static __forceinline__ void flush(const T *lds, const Rows<T> &X, int col0) {
+#pragma unroll
+        for (int i = 0; i < NP; ++i) {
+            const int p = (int)threadIdx.x + i * NT;
+            if (P % NT != 0 && p >= P) continue;
+            const int row = p / PPR, cp = p % PPR;
+            const i32x4 x = *reinterpret_cast<const i32x4 *>(lds + row * RS + cp * (16 / (int)sizeof(T)));
+            const int off = (row * X.ld + col0) * (int)sizeof(T) + cp * 16;
+            __builtin_amdgcn_raw_buffer_store_b128(x, X.rsrc, off, 0, 0);
+        }
+    }
+};
+
 // Order this wave's LDS writes before its later LDS reads of other lanes'
 // data and vice versa.  A workgroup here is a single wave, so this is all the
 // synchronisation LDS needs (no s_barrier, no wait on global loads).
@@ -343,6 +377,92 @@ struct Diag {
 #pragma unroll
         for (int t = 0; t < 4; ++t) a[t] = query_rows[t] ? a[t] : 0.f;
         return a;
+    }
+};
+
+// Operands contracted over the feature index e (E columns of Q or K rows).
+// A k-step is one MFMA's worth of features: bf16 with E >= 32 takes 32 per
+// step as 8 consecutive elements per lane (one 16-byte LDS read), bf16 with
+// E = 16 takes 16 (four per lane, padded with zeros), fp32 takes 16 (four per
+// lane, four MFMAs).  Lane (g, r) of step s holds features
+//     e = col0(s) + estride * g + v,   v < 8 (bf16, E >= 32) or v < 4.
+// Carried states S (E x 16 column block) are kept as E/16 accumulator tiles
+// whose rows follow the same order: tile eb holds, in lane (g, r), rows
+//     e = ecol(eb) + estride * g + t,   t = 0..3,
+// so the tiles of step s, converted, are directly that step's operand.  The
+// transposed read tr_e() produces the matching K^T fragments for updating
+// those tiles.
+template <typename T, int E> struct EOps;
+
+template <int E> struct EOps<bf16, E> {
+    static constexpr int EB = E / 16;
+    static constexpr bool WIDE = EB >= 2;
+    static constexpr int STEPS = WIDE ? EB / 2 : 1;
+    static constexpr int estride = WIDE ? 8 : 4;
+    using rf = typename std::conditional<WIDE, bf16x8, bf16x4>::type;
+
+    __device__ static __forceinline__ int ecol(int eb) { return WIDE ? 32 * (eb >> 1) + 4 * (eb & 1) : 16 * eb; }
+    // lane (g, r) <- X[16 rb + r][features of step s]
+    __device__ static __forceinline__ rf load(const bf16 *lds, int rs, int rb, int s) {
+        const bf16 *p = lds + (16 * rb + lane_r()) * rs + (WIDE ? 32 * s : 0) + estride * lane_g();
+        return *reinterpret_cast<const rf *>(p);
+    }
+    __device__ static __forceinline__ void mma(f32x4 &acc, rf a, rf b) {
+        if constexpr (WIDE) {
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+        } else {
+            Ops<bf16>::mma1(acc, a, b);
+        }
+    }
+    // operand of step s from the state tiles
+    __device__ static __forceinline__ rf state(const f32x4 *tiles, int s) {
+        if constexpr (WIDE) {
+            const bf16x4 lo = Ops<bf16>::cvt(tiles[2 * s]), hi = Ops<bf16>::cvt(tiles[2 * s + 1]);
+            return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        } else {
+            return Ops<bf16>::cvt(tiles[0]);
+        }
+    }
+    __device__ static __forceinline__ void state_split(const f32x4 *tiles, int s, rf &hi, rf &lo) {
+        if constexpr (WIDE) {
+            bf16x4 h0, l0, h1, l1;
+            Ops<bf16>::split(tiles[2 * s], h0, l0);
+            Ops<bf16>::split(tiles[2 * s + 1], h1, l1);
+            hi = __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7);
+            lo = __builtin_shufflevector(l0, l1, 0, 1, 2, 3, 4, 5, 6, 7);
+        } else {
+            Ops<bf16>::split(tiles[0], hi, lo);
+        }
+    }
+    // lane (g, r) <- X[16 tb + 4g + t][ecol(eb) + estride * (r / 4) + r % 4]:
+    // K^T fragment (rows e in state-tile order, k = tokens of block tb).
+    __device__ static __forceinline__ bf16x4 tr_e(const bf16 *lds, int rs, int tb, int eb) {
+        const int g = lane_g(), i = lane_r();
+        const bf16 *p = lds + (16 * tb + 4 * g + (i >> 2)) * rs + ecol(eb) + estride * (i & 3);
+        s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4 *)((__attribute__((address_space(3))) char *)(p)));
+        return __builtin_bit_cast(bf16x4, v);
+    }
+};
+
+template <int E> struct EOps<float, E> {
+    static constexpr int EB = E / 16;
+    static constexpr int STEPS = EB;
+    static constexpr int estride = 4;
+    using rf = f32x4;
+
+    __device__ static __forceinline__ int ecol(int eb) { return 16 * eb; }
+    __device__ static __forceinline__ rf load(const float *lds, int rs, int rb, int s) {
+        return *reinterpret_cast<const f32x4 *>(lds + (16 * rb + lane_r()) * rs + 16 * s + 4 * lane_g());
+    }
+    __device__ static __forceinline__ void mma(f32x4 &acc, rf a, rf b) { Ops<float>::mma1(acc, a, b); }
+    __device__ static __forceinline__ rf state(const f32x4 *tiles, int s) { return tiles[s]; }
+    __device__ static __forceinline__ void state_split(const f32x4 *tiles, int s, rf &hi, rf &lo) {
+        hi = tiles[s];
+        lo = zero4();
+    }
+    __device__ static __forceinline__ f32x4 tr_e(const float *lds, int rs, int tb, int eb) {
+        return Ops<float>::tr_frag(lds, rs, tb, eb);
     }
 };
 

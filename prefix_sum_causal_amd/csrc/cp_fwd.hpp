@@ -12,71 +12,76 @@
 // with T the inclusive lower-triangular mask: the prefix sum runs serially
 // over chunks and in parallel (as small dense products) inside a chunk.
 //
-// A workgroup owns one (n, h) slice and one 16-column block mb of the output
-// and runs RS waves.  Per chunk, all its threads copy Q, K (all E columns) and
-// the V column block into LDS (double buffered, one barrier per chunk) while
-// the next chunk's loads are in flight; each wave then keeps the E x 16 block
-// of the state in MFMA accumulators (every wave carries the same state, which
-// costs a few MFMAs and saves any exchange), and computes the output rows of
-// its share of the chunk's 16-row blocks.  The shares are balanced pairs
-// (block k and C/16-1-k carry equal causal work), so all workgroups do the
-// same work per chunk and the M/16 workgroups of a slice, placed on one XCD,
-// stay in step and take the slice's Q and K rows from its L2.  Products run
-// in the transposed orientation Out^T = V^T A^T + S^T Q^T so that every
-// operand is a natural or transposed LDS read or an accumulator tile.
+// A workgroup owns one (n, h) slice and a group of NW 16-column blocks of V
+// and Out; wave w owns column block w of the group for every row of the
+// chunk.  Per chunk all threads copy Q, K (all E columns) and the group's V
+// columns into LDS (double buffered, one barrier per chunk) while the next
+// chunks' loads are in flight.  Each wave then
+//   - reads the chunk's Q and K rows (16-byte natural reads),
+//   - forms the causal score tiles A^T(J, I) = K_J Q_I^T, J <= I (every wave
+//     forms all of them: cheaper than exchanging them through LDS),
+//   - accumulates its output block Out^T = V^T A^T + S^T Q^T into an LDS
+//     copy of the chunk's output rows, which the workgroup writes to HBM as
+//     whole rows after the next barrier, and
+//   - updates its E x 16 block of the state, S += K^T V (transposed reads).
+// So each row of the inputs enters LDS once per workgroup and the state is
+// updated once, by the wave that owns its columns.  Products run in the
+// transposed orientation so that every operand is a natural or transposed
+// LDS read or an accumulator tile.
 //
 // Normalised form (NORM): out_i = phi(q_i)^T S_i / (phi(q_i) . z_i + eps) with
 // z_i = sum_{j<=i} phi(k_j).  phi is applied while the chunk is copied into
-// LDS.  The denominator of token i is the masked row sum of the chunk's scores
-// plus phi(q_i) . z_{c-1} (one extra MFMA row beside the numerator); z is
-// carried like S (z_c = z_{c-1} + column sums of phi(K_c), the running
-// inclusive sum of phi(k)); the division happens before the store.
+// LDS.  The denominator of token i is the masked column sum of the chunk's
+// score tiles plus phi(q_i) . z_{c-1} (one extra MFMA row beside the
+// numerator, in every wave); z is carried like S (z_c = z_{c-1} + column sums
+// of phi(K_c)) and enters the product as a hi + lo pair of operands; the
+// division happens before the store.
 #pragma once
 
 #include "cp_device.hpp"
 
 namespace cp {
 
-// Query row block handled by wave w in round k: a snake over the waves, so
-// that each wave gets block k and block C/16-1-k worth of causal work.
-template <int RS>
-__device__ __forceinline__ int owned_block(int k, int w) {
-    return (k & 1) ? k * RS + (RS - 1 - w) : k * RS + w;
+// Query row blocks of a chunk owned by row set h of RSPLIT: the blocks are
+// taken in balanced pairs (k, CB-1-k) -- equal causal work -- dealt round
+// robin to the row sets.
+template <int CB, int RSPLIT>
+constexpr bool owns_block(int h, int I) {
+    const int k = I < CB / 2 ? I : CB - 1 - I;
+    return RSPLIT == 1 || k % RSPLIT == h;
+}
+template <int CB, int RSPLIT>
+constexpr int last_block(int h) {
+    int last = -1;
+    for (int I = 0; I < CB; ++I)
+        if (owns_block<CB, RSPLIT>(h, I)) last = I;
+    return last;
 }
 
-template <typename T, int E, int M, int C, int RS, int NPF, bool NORM, bool FMAP, bool HILO>
-__global__ __launch_bounds__(64 * RS) void cp_fwd_kernel(const T *__restrict__ Q, const T *__restrict__ K,
-                                                         const T *__restrict__ V, T *__restrict__ Out,
-                                                         float *__restrict__ state_out, int L, int NS,
-                                                         float eps) {
+// The chunk loop of one wave: output column block cb of the workgroup's
+// group, query row blocks of row set H.  Every wave runs the same staging
+// and barriers; the state is carried (redundantly) by every row set.
+template <typename T, int E, int M, int C, int NW, int RSPLIT, int NPF, bool OST, bool NORM, bool FMAP, int H>
+__device__ __forceinline__ void fwd_sweep(const T *q_, const T *k_, const T *v_, T *o_, int L, int grp, int cb,
+                                          float eps, T *lds, f32x4 (&S)[E / 16]) {
     using O = Ops<T>;
     using F = typename O::frag;
-    constexpr int NT = 64 * RS, EB = E / 16, MB = M / 16, CB = C / 16;
-    static_assert(CB % RS == 0, "the chunk's row blocks are shared evenly by the waves");
-    static_assert(NPF >= 2, "the load ring needs at least two stages");
+    using EO = EOps<T, E>;
+    using RF = typename EO::rf;
+    constexpr int EB = E / 16, CB = C / 16, KS = EO::STEPS;
+    constexpr int NT = 64 * NW * RSPLIT, MW = 16 * NW;
     using SQ = Stage<T, NT, C, E>;
-    using SV = Stage<T, NT, C, 16>;
+    using SV = Stage<T, NT, C, MW>;
     constexpr int RQ = SQ::RS, RV = SV::RS;
-    constexpr int BUF = 2 * C * RQ + C * RV;  // Q, K, V block
-    __shared__ __attribute__((aligned(16))) T lds[2 * BUF];
-
-    int slice, mb;
-    map_block(blockIdx.x, NS, MB, slice, mb);
-    const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
-    const int g = lane_g(), r = lane_r();
-    const T *q_ = Q + (int64_t)slice * L * E;
-    const T *k_ = K + (int64_t)slice * L * E;
-    const T *v_ = V + (int64_t)slice * L * M;
-    T *o_ = Out + (int64_t)slice * L * M;
+    using SO = OutStage<T, NT, C, MW>;
+    constexpr int BUF = 2 * C * RQ + C * RV;  // Q, K, V columns of the group
+    T *const obuf = lds + 2 * BUF;             // two output row buffers of C * SO::RS
+    constexpr int JMAX = last_block<CB, RSPLIT>(H);  // key blocks this wave scores: J <= JMAX
 
     const Diag diag;
-    f32x4 S[EB];  // S[16 eb + 4g + t][16 mb + r]
-    f32x4 z[EB];  // z[16 eb + 4g + t] (same in every lane r)
+    f32x4 z[EB];  // z[ecol(eb) + estride g + t] (same in every lane r)
 #pragma unroll
-    for (int e = 0; e < EB; ++e) {
-        S[e] = zero4();
-        z[e] = zero4();
-    }
+    for (int e = 0; e < EB; ++e) z[e] = zero4();
 
     // Ring of NPF register stages: NPF-1 chunks are in flight while one is
     // computed.  The step loop is padded to a multiple of NPF; padded chunks
@@ -84,111 +89,190 @@ __global__ __launch_bounds__(64 * RS) void cp_fwd_kernel(const T *__restrict__ Q
     struct Stages {
         SQ q, k;
         SV v;
-        __device__ __forceinline__ void load(const T *q_, const T *k_, const T *v_, int row0, int L, int mb) {
+        __device__ __forceinline__ void load(const T *q_, const T *k_, const T *v_, int row0, int L, int col0) {
             q.load(Rows<T>(q_, E, row0, L, C), 0);
             k.load(Rows<T>(k_, E, row0, L, C), 0);
-            v.load(Rows<T>(v_, M, row0, L, C), 16 * mb);
+            v.load(Rows<T>(v_, M, row0, L, C), col0);
         }
     };
+    const int col0 = 16 * grp * NW;
     Stages st[NPF];
 #pragma unroll
     for (int s = 0; s < NPF - 1; ++s) {
-        st[s].load(q_, k_, v_, s * C, L, mb);
+        st[s].load(q_, k_, v_, s * C, L, col0);
         __builtin_amdgcn_sched_barrier(0);  // stages complete in order
     }
-
-    constexpr int KB = CB / RS;  // row blocks per wave
 
     const int nchunks = (L + C - 1) / C;
     const int nsteps = (nchunks + NPF - 1) / NPF * NPF;
     for (int c0 = 0; c0 < nsteps; c0 += NPF) {
 #pragma unroll
-      for (int s = 0; s < NPF; ++s) {
-        const int c = c0 + s;
-        const int row0 = c * C;
-        T *Qs = lds + (c & 1) * BUF, *Ks = Qs + C * RQ, *Vs = Ks + C * RQ;
-        st[s].q.template store<NORM && FMAP>(Qs, row0, L);
-        st[s].k.template store<NORM && FMAP>(Ks, row0, L);
-        st[s].v.store(Vs);
-        __syncthreads();
-        st[(s + NPF - 1) % NPF].load(q_, k_, v_, row0 + (NPF - 1) * C, L, mb);
-        __builtin_amdgcn_sched_barrier(0);
-
-        // S_{c-1} (and z_{c-1}) as A operands: A = S^T (rows m, k = e)
-        F sh[EB], sl[EB], zh[EB], zl[EB];
+        for (int s = 0; s < NPF; ++s) {
+            const int c = c0 + s;
+            const int row0 = c * C;
+            T *Qs = lds + (c & 1) * BUF, *Ks = Qs + C * RQ, *Vs = Ks + C * RQ;
+            st[s].q.template store<NORM && FMAP>(Qs, row0, L);
+            st[s].k.template store<NORM && FMAP>(Ks, row0, L);
+            st[s].v.store(Vs);
+            __syncthreads();
+            // The next chunk's loads are issued one array at a time between
+            // the products below, and the output rows (this chunk's tiles, or
+            // with OST the previous chunk's rows staged in LDS before this
+            // barrier) in the middle of the state update, so that the vector
+            // memory unit drains while the matrix cores work.  Stores go after
+            // the step's loads: memory operations complete in issue order, so
+            // the rows waited for at a later step never wait for these stores.
+            Stages &nx = st[(s + NPF - 1) % NPF];
+            const int nrow0 = row0 + (NPF - 1) * C;
+            f32x4 pend[CB];  // this step's output tiles (owned row blocks)
+            int nload = 0;   // arrays of the next chunk whose loads are issued
+            auto issue_load = [&]() {
+                if (nload == 0) nx.q.load(Rows<T>(q_, E, nrow0, L, C), 0);
+                if (nload == 1) nx.k.load(Rows<T>(k_, E, nrow0, L, C), 0);
+                if (nload == 2) nx.v.load(Rows<T>(v_, M, nrow0, L, C), col0);
+                ++nload;
+                __builtin_amdgcn_sched_barrier(0);
+            };
+            // the step's output rows (after every owned row block is done)
+            auto issue_store = [&]() {
+                if constexpr (OST) {
+                    SO::flush(obuf + ((c - 1) & 1) * C * SO::RS, Rows<T>(o_, M, row0 - C, L, C), col0);
+                } else {
+                    const Rows<T> ro(o_, M, row0, L, C);
 #pragma unroll
-        for (int e = 0; e < EB; ++e) {
-            if constexpr (HILO) O::split(S[e], sh[e], sl[e]);
-            else sh[e] = O::cvt(S[e]);
-            if constexpr (NORM) O::split(z[e], zh[e], zl[e]);
-        }
-
-        f32x4 pend[KB];
-#pragma unroll
-        for (int k = 0; k < KB; ++k) {
-            const int I = owned_block<RS>(k, w);
-            F qI[EB];  // Q[16 I + r][16 eb + 4g + t]
-#pragma unroll
-            for (int e = 0; e < EB; ++e) qI[e] = lds_nat<T>(Qs, RQ, I, e);
-            f32x4 o = zero4(), d = zero4();
-            // inter-chunk: Out^T += S^T Q_I^T
-            dotk<T>(o, 0, EB, [&](int e) { return sh[e]; }, [&](int e) { return qI[e]; });
-            if constexpr (HILO)
-                dotk<T>(o, 0, EB, [&](int e) { return sl[e]; }, [&](int e) { return qI[e]; });
-            if constexpr (NORM) {
-                dotk<T>(d, 0, EB, [&](int e) { return zh[e]; }, [&](int e) { return qI[e]; });
-                dotk<T>(d, 0, EB, [&](int e) { return zl[e]; }, [&](int e) { return qI[e]; });
-            }
-            // intra-chunk: Out^T += V^T A^T with A^T(J, I) = K_J Q_I^T masked
-            // on the diagonal, key blocks J <= I taken in pairs
-            for (int J0 = 0; J0 <= I; J0 += 2) {
-                f32x4 a0 = nn_tile<T, EB>(Ks, RQ, J0, Qs, RQ, I);
-                if (J0 == I) a0 = diag.keys(a0);
-                F at1 = O::zero(), vt1 = O::zero();
-                if (J0 + 1 <= I) {
-                    f32x4 a1 = nn_tile<T, EB>(Ks, RQ, J0 + 1, Qs, RQ, I);
-                    if (J0 + 1 == I) a1 = diag.keys(a1);
-                    at1 = O::cvt(a1);
-                    vt1 = O::tr_frag(Vs, RV, J0 + 1, 0);
+                    for (int I = 0; I < CB; ++I)
+                        if (owns_block<CB, RSPLIT>(H, I)) st_out<T>(ro, I, grp * NW + cb, pend[I]);
                 }
-                const F at0 = O::cvt(a0);
-                O::mma2(o, O::tr_frag(Vs, RV, J0, 0), vt1, at0, at1);
-                if constexpr (NORM) O::mma2(d, O::ones(), O::ones(), at0, at1);
-            }
-            if constexpr (NORM) {
-#pragma unroll
-                for (int t = 0; t < 4; ++t) o[t] = o[t] / (d[t] + eps);
-            }
-            pend[k] = o;
-        }
-        // Stores go after this step's prefetch: memory operations complete in
-        // issue order, so the rows waited for at a later step were issued
-        // before these stores and never wait for them.
-        {
-            const Rows<T> ro(o_, M, row0, L, C);
-#pragma unroll
-            for (int k = 0; k < KB; ++k) st_out<T>(ro, owned_block<RS>(k, w), mb, pend[k]);
-        }
+                __builtin_amdgcn_sched_barrier(0);
+            };
+            issue_load();
 
-        // S_c = S_{c-1} + K_c^T V_c  (and z_c = z_{c-1} + K_c^T 1)
+            RF kf[CB][KS];
 #pragma unroll
-        for (int e = 0; e < EB; ++e) {
-            dotk<T>(S[e], 0, CB, [&](int J) { return O::tr_frag(Ks, RQ, J, e); },
-                    [&](int J) { return O::tr_frag(Vs, RV, J, 0); });
-            if constexpr (NORM)
-                dotk<T>(z[e], 0, CB, [&](int J) { return O::tr_frag(Ks, RQ, J, e); },
-                        [&](int) { return O::ones(); });
+            for (int b = 0; b <= JMAX; ++b)
+#pragma unroll
+                for (int k = 0; k < KS; ++k) kf[b][k] = EO::load(Ks, RQ, b, k);
+            F vt[CB];  // V_J^T fragments of this wave's columns
+#pragma unroll
+            for (int b = 0; b < CB; ++b) vt[b] = O::tr_frag(Vs, RV, b, cb);
+            // S_{c-1} (and z_{c-1}) as A operands
+            RF sa[KS], zh[KS], zl[KS];
+#pragma unroll
+            for (int k = 0; k < KS; ++k) {
+                sa[k] = EO::state(S, k);
+                if constexpr (NORM) EO::state_split(z, k, zh[k], zl[k]);
+            }
+
+#pragma unroll
+            for (int I = 0; I < CB; ++I) {
+                if (!owns_block<CB, RSPLIT>(H, I)) continue;
+                RF qf[KS];
+#pragma unroll
+                for (int k = 0; k < KS; ++k) qf[k] = EO::load(Qs, RQ, I, k);
+                f32x4 o = zero4(), d = zero4();
+                // inter-chunk: Out^T += S^T Q_I^T
+#pragma unroll
+                for (int k = 0; k < KS; ++k) EO::mma(o, sa[k], qf[k]);
+                if constexpr (NORM) {
+#pragma unroll
+                    for (int k = 0; k < KS; ++k) {
+                        EO::mma(d, zh[k], qf[k]);
+                        EO::mma(d, zl[k], qf[k]);
+                    }
+                }
+                // intra-chunk: Out^T += V^T A^T with A^T(J, I) = K_J Q_I^T
+                // masked on the diagonal, key blocks J <= I taken in pairs
+#pragma unroll
+                for (int J0 = 0; J0 <= I; J0 += 2) {
+                    f32x4 a0 = zero4();
+#pragma unroll
+                    for (int k = 0; k < KS; ++k) EO::mma(a0, kf[J0][k], qf[k]);
+                    if (J0 == I) a0 = diag.keys(a0);
+                    F at1 = O::zero(), vt1 = O::zero();
+                    if (J0 + 1 <= I) {
+                        f32x4 a1 = zero4();
+#pragma unroll
+                        for (int k = 0; k < KS; ++k) EO::mma(a1, kf[J0 + 1][k], qf[k]);
+                        if (J0 + 1 == I) a1 = diag.keys(a1);
+                        at1 = O::cvt(a1);
+                        vt1 = vt[J0 + 1];
+                    }
+                    const F at0 = O::cvt(a0);
+                    O::mma2(o, vt[J0], vt1, at0, at1);
+                    if constexpr (NORM) O::mma2(d, O::ones(), O::ones(), at0, at1);
+                }
+                if constexpr (NORM) {
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) o[t] = o[t] / (d[t] + eps);
+                }
+                pend[I] = o;
+                issue_load();
+            }
+            while (nload < 3) issue_load();
+            if constexpr (OST) {
+#pragma unroll
+                for (int I = 0; I < CB; ++I)
+                    if (owns_block<CB, RSPLIT>(H, I)) SO::put(obuf + (c & 1) * C * SO::RS, I, cb, pend[I]);
+            }
+
+            // S_c = S_{c-1} + K_c^T V_c  (and z_c = z_{c-1} + K_c^T 1)
+#pragma unroll
+            for (int e = 0; e < EB; ++e) {
+                dotk<T>(S[e], 0, CB, [&](int J) { return EO::tr_e(Ks, RQ, J, e); }, [&](int J) { return vt[J]; });
+                if constexpr (NORM)
+                    dotk<T>(z[e], 0, CB, [&](int J) { return EO::tr_e(Ks, RQ, J, e); },
+                            [&](int) { return O::ones(); });
+                if (e == (EB - 1) / 2) issue_store();
+            }
         }
-      }
     }
+    if constexpr (OST) {  // the last chunk's output rows
+        __syncthreads();
+        SO::flush(obuf + ((nsteps - 1) & 1) * C * SO::RS, Rows<T>(o_, M, (nsteps - 1) * C, L, C), col0);
+    }
+}
+
+template <typename T, int E, int M, int C, int G, int RSPLIT, int NPF, bool OST, bool NORM, bool FMAP>
+__global__ __launch_bounds__(64 * (M / 16 / G) * RSPLIT) void cp_fwd_kernel(
+    const T *__restrict__ Q, const T *__restrict__ K, const T *__restrict__ V, T *__restrict__ Out,
+    float *__restrict__ state_out, int L, int NS, float eps) {
+    using EO = EOps<T, E>;
+    constexpr int EB = E / 16, MB = M / 16, CB = C / 16;
+    static_assert(MB % G == 0, "column groups split the column blocks evenly");
+    static_assert(NPF >= 2, "the load ring needs at least two stages");
+    static_assert(RSPLIT == 1 || (RSPLIT == 2 && CB >= 4 && CB % 2 == 0), "row sets need pairs of row blocks");
+    constexpr int NW = MB / G, NT = 64 * NW * RSPLIT, MW = 16 * NW;
+    constexpr int RQ = Stage<T, NT, C, E>::RS, RV = Stage<T, NT, C, MW>::RS;
+    constexpr int BUF = 2 * C * RQ + C * RV;
+    constexpr int OBUF = OST ? C * OutStage<T, NT, C, MW>::RS : 0;
+    __shared__ __attribute__((aligned(16))) T lds[2 * BUF + 2 * OBUF];
+
+    int slice, grp;
+    map_block(blockIdx.x, NS, G, slice, grp);
+    const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    const int cb = w % NW, h = w / NW;
+    const int g = lane_g(), r = lane_r();
+    const T *q_ = Q + (int64_t)slice * L * E;
+    const T *k_ = K + (int64_t)slice * L * E;
+    const T *v_ = V + (int64_t)slice * L * M;
+    T *o_ = Out + (int64_t)slice * L * M;
+
+    f32x4 S[EB];  // S[ecol(eb) + estride g + t][16 mb + r]
+#pragma unroll
+    for (int e = 0; e < EB; ++e) S[e] = zero4();
+    if (h == 0)
+        fwd_sweep<T, E, M, C, NW, RSPLIT, NPF, OST, NORM, FMAP, 0>(q_, k_, v_, o_, L, grp, cb, eps, lds, S);
+    else
+        fwd_sweep<T, E, M, C, NW, RSPLIT, NPF, OST, NORM, FMAP, 1>(q_, k_, v_, o_, L, grp, cb, eps, lds, S);
+    const int mb = grp * NW + cb;
 
     if constexpr (!NORM) {
-        if (state_out && w == 0) {
-            float *st = state_out + (int64_t)slice * E * M;
+        if (state_out && h == 0) {
+            float *st_ = state_out + (int64_t)slice * E * M;
 #pragma unroll
             for (int e = 0; e < EB; ++e)
 #pragma unroll
-                for (int t = 0; t < 4; ++t) st[(16 * e + 4 * g + t) * M + 16 * mb + r] = S[e][t];
+                for (int t = 0; t < 4; ++t) st_[(EO::ecol(e) + EO::estride * g + t) * M + 16 * mb + r] = S[e][t];
         }
     }
 }

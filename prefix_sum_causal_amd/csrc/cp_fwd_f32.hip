@@ -10,14 +10,14 @@ template <int E, int M, bool NORM, bool FMAP>
 hipError_t launch_fwd(const FwdArgs &a, hipStream_t s) {
     using T = float;
     using P = Tune<T, E, M>;
-    auto kern = cp_fwd_kernel<T, E, M, P::FC, P::RS, P::FNPF, NORM, FMAP, P::HILO>;
+    auto kern = cp_fwd_kernel<T, E, M, P::FC, P::FG, P::FRS, P::FNPF, P::FOST, NORM, FMAP>;
     const T *q = static_cast<const T *>(a.Q), *k = static_cast<const T *>(a.K), *v = static_cast<const T *>(a.V);
     T *o = static_cast<T *>(a.Out);
     float *st = a.state_out;
     int L = a.L, NS = a.NS;
     float eps = a.eps;
     void *args[] = {&q, &k, &v, &o, &st, &L, &NS, &eps};
-    return hipLaunchKernel(reinterpret_cast<const void *>(kern), dim3(NS * fwd_parts(E, M)), dim3(64 * P::RS), args,
+    return hipLaunchKernel(reinterpret_cast<const void *>(kern), dim3(NS * P::FG), dim3(64 * (M / 16 / P::FG) * P::FRS), args,
                            0, s);
 }
 

@@ -1,7 +1,12 @@
 // cp_tune.hpp -- compile-time launch parameters of each kernel instance:
 //   FC   forward chunk length (tokens per step of the scan),
-//   RS   forward waves per workgroup (they share a chunk's query row blocks),
+//   FG   forward workgroups per (n, h) slice; each owns M/16/FG column blocks
+//        of the output, one wave per block,
 //   BC   backward chunk length,
+//   FRS  forward row sets: waves per output column block, which split the
+//        chunk's query row blocks,
+//   FOST forward output rows go through LDS and leave as whole rows (else
+//        the result tiles are stored from registers),
 //   FNPF, BNPF  stages of the forward / backward load ring (NPF-1 chunks are
 //        in flight while one is computed),
 //   HILO carried states enter the bf16 MFMA as a hi + lo pair of bf16 values
@@ -17,11 +22,17 @@
 #ifndef CP_BF16_FC
 #define CP_BF16_FC 64
 #endif
-#ifndef CP_BF16_RS
-#define CP_BF16_RS 4
+#ifndef CP_BF16_FG
+#define CP_BF16_FG 2
 #endif
 #ifndef CP_BF16_BC
 #define CP_BF16_BC 64
+#endif
+#ifndef CP_BF16_FRS
+#define CP_BF16_FRS 2
+#endif
+#ifndef CP_BF16_FOST
+#define CP_BF16_FOST 0
 #endif
 #ifndef CP_BF16_FNPF
 #define CP_BF16_FNPF 3
@@ -41,8 +52,8 @@
 #ifndef CP_F32_FC
 #define CP_F32_FC 32
 #endif
-#ifndef CP_F32_RS
-#define CP_F32_RS 2
+#ifndef CP_F32_FG
+#define CP_F32_FG 1
 #endif
 #ifndef CP_F32_BC
 #define CP_F32_BC 32
@@ -55,10 +66,16 @@ template <typename T, int E, int M> struct Tune;
 // 128-wide heads halve the backward chunk so that two workgroups fit a CU's LDS.
 template <int E, int M> struct Tune<__bf16, E, M> {
     static constexpr bool wide = E > 64 || M > 64;
-    static constexpr int FC = CP_BF16_FC;
-    static constexpr int RS = CP_BF16_RS;
+    // one-wave workgroups with wide features hold a whole chunk per thread:
+    // shorter chunks keep them in registers
+    static constexpr int FC = ((M == 16 && E >= 64) || (E == 128 && M == 32)) && CP_BF16_FC > 32 ? 32 : CP_BF16_FC;
+    // 128 output columns: two workgroups of four waves (registers per wave)
+    static constexpr int FG0 = M > 64 && CP_BF16_FG < 2 ? 2 : CP_BF16_FG;
+    static constexpr int FG = FG0 > M / 16 ? M / 16 : FG0;
     static constexpr int BC = wide && CP_BF16_BC > 32 ? 32 : CP_BF16_BC;
+    static constexpr int FRS = FC >= 64 ? CP_BF16_FRS : 1;
     static constexpr int FNPF = CP_BF16_FNPF;
+    static constexpr bool FOST = CP_BF16_FOST != 0;
     static constexpr int BNPF = CP_BF16_BNPF;
     static constexpr bool HILO = CP_BF16_HILO != 0;
 };
@@ -68,9 +85,12 @@ template <int E, int M> struct Tune<__bf16, E, M> {
 template <int E, int M> struct Tune<float, E, M> {
     static constexpr bool wide = E > 64 || M > 64;
     static constexpr int FC = wide ? 16 : CP_F32_FC;
-    static constexpr int RS = wide ? 1 : CP_F32_RS;
+    static constexpr int FG0 = M > 64 && CP_F32_FG < 2 ? 2 : CP_F32_FG;
+    static constexpr int FG = FG0 > M / 16 ? M / 16 : FG0;
     static constexpr int BC = wide ? 16 : CP_F32_BC;
+    static constexpr int FRS = 1;
     static constexpr int FNPF = CP_F32_FNPF;
+    static constexpr bool FOST = false;
     static constexpr int BNPF = CP_F32_BNPF;
     static constexpr bool HILO = false;
 };
