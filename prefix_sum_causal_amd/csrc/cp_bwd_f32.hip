@@ -10,14 +10,14 @@ template <int E, int M>
 hipError_t launch_bwd(const BwdArgs &a, hipStream_t s) {
     using T = float;
     using P = Tune<T, E, M>;
-    auto kern = cp_bwd_kernel<T, E, M, P::BC, P::BNPF, P::HILO>;
+    auto kern = cp_bwd_kernel<T, E, M, P::BC, P::BG, P::BNPF>;
     const T *q = static_cast<const T *>(a.Q), *k = static_cast<const T *>(a.K), *v = static_cast<const T *>(a.V),
             *g = static_cast<const T *>(a.G);
     const float *st = a.state_in;
     T *dq = static_cast<T *>(a.dQ), *dk = static_cast<T *>(a.dK), *dv = static_cast<T *>(a.dV);
     int L = a.L, NS = a.NS;
     void *args[] = {&q, &k, &v, &g, &st, &dq, &dk, &dv, &L, &NS};
-    return hipLaunchKernel(reinterpret_cast<const void *>(kern), dim3(NS * bwd_parts(E, M)), dim3(192), args, 0, s);
+    return hipLaunchKernel(reinterpret_cast<const void *>(kern), dim3(NS * P::BG), dim3(bwd_threads<T, E, M, P::BG>()), args, 0, s);
 }
 
 }  // namespace

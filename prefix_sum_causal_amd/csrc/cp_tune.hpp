@@ -3,18 +3,14 @@
 //   FG   forward workgroups per (n, h) slice; each owns M/16/FG column blocks
 //        of the output, one wave per block,
 //   BC   backward chunk length,
+//   BG   backward workgroups per (n, h) slice; each owns every BG-th column
+//        block of dQ, dK and dV, one wave per block,
 //   FRS  forward row sets: waves per output column block, which split the
 //        chunk's query row blocks,
 //   FOST forward output rows go through LDS and leave as whole rows (else
 //        the result tiles are stored from registers),
 //   FNPF, BNPF  stages of the forward / backward load ring (NPF-1 chunks are
 //        in flight while one is computed),
-//   HILO carried states enter the bf16 MFMA as a hi + lo pair of bf16 values
-//        (16 significant bits instead of 8).  Off by default: the bf16 score
-//        tiles dominate the error either way (measured max relative error at
-//        L=4096, E=M=64: forward 2.7e-3 without, 2.3e-3 with; backward
-//        3.6e-3 without, 2.6e-3 with), and the split costs a quarter of the
-//        forward's time.
 // Each value can be overridden when the library is built (-DCP_BF16_FC=32 ...)
 // for tuning sweeps.
 #pragma once
@@ -40,8 +36,11 @@
 #ifndef CP_BF16_BNPF
 #define CP_BF16_BNPF 3
 #endif
-#ifndef CP_BF16_HILO
-#define CP_BF16_HILO 0
+#ifndef CP_BF16_BG
+#define CP_BF16_BG 2
+#endif
+#ifndef CP_F32_BG
+#define CP_F32_BG 2
 #endif
 #ifndef CP_F32_FNPF
 #define CP_F32_FNPF 2
@@ -61,6 +60,15 @@
 
 namespace cp {
 
+// Backward workgroups per slice: the preferred count, at most one per column
+// block, and enough that a workgroup has at most 16 waves.
+constexpr int bwd_groups(int E, int M, int pref) {
+    const int eb = E / 16, mb = M / 16, most = eb > mb ? eb : mb;
+    int g = pref < most ? pref : most;
+    while (64 * (2 * ((eb + g - 1) / g) + (mb + g - 1) / g) > 1024) ++g;
+    return g;
+}
+
 template <typename T, int E, int M> struct Tune;
 
 // 128-wide heads halve the backward chunk so that two workgroups fit a CU's LDS.
@@ -77,7 +85,7 @@ template <int E, int M> struct Tune<__bf16, E, M> {
     static constexpr int FNPF = CP_BF16_FNPF;
     static constexpr bool FOST = CP_BF16_FOST != 0;
     static constexpr int BNPF = CP_BF16_BNPF;
-    static constexpr bool HILO = CP_BF16_HILO != 0;
+    static constexpr int BG = bwd_groups(E, M, CP_BF16_BG);
 };
 
 // fp32 tiles are twice as large in LDS and registers: the widest heads use
@@ -92,7 +100,7 @@ template <int E, int M> struct Tune<float, E, M> {
     static constexpr int FNPF = CP_F32_FNPF;
     static constexpr bool FOST = false;
     static constexpr int BNPF = CP_F32_BNPF;
-    static constexpr bool HILO = false;
+    static constexpr int BG = bwd_groups(E, M, CP_F32_BG);
 };
 
 }  // namespace cp
