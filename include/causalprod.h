@@ -112,6 +112,27 @@ const char *cp_status_string(int status);
 /* Version of this ABI: (major << 16) | minor. */
 int cp_abi_version(void);
 
+/*
+ * Kernel timing, for measurement (not part of the computation).
+ *
+ * cp_timing_begin(capacity): from now on, each kernel launched by the calling
+ * thread through this library records its own start and end time (the
+ * timestamps of its dispatch, as a profiler's kernel trace reports them), for
+ * at most `capacity` launches (1 <= capacity <= 65536).  Event objects are
+ * created on the current device; a previous unfinished timing of this thread
+ * is discarded.  CP_ERR_DIM for a bad capacity, CP_ERR_HIP if events cannot be
+ * created.
+ *
+ * cp_timing_end(ms, count): waits for the recorded launches, writes the
+ * duration in milliseconds of each, in launch order, to ms[0 .. *count) (ms
+ * holds at least `capacity` floats, owned by the caller), releases the events
+ * and stops recording.  *count is the number of launches recorded (launches
+ * beyond the capacity are not timed).  CP_ERR_NULL for NULL arguments or when
+ * no timing was begun; CP_ERR_HIP if waiting fails.
+ */
+int cp_timing_begin(int capacity);
+int cp_timing_end(float *ms, int *count);
+
 #ifdef __cplusplus
 }
 #endif

@@ -49,6 +49,10 @@ lib.cp_status_string.argtypes = [_int]
 lib.cp_status_string.restype = ctypes.c_char_p
 lib.cp_abi_version.argtypes = []
 lib.cp_abi_version.restype = _int
+lib.cp_timing_begin.argtypes = [_int]
+lib.cp_timing_begin.restype = _int
+lib.cp_timing_end.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.POINTER(_int)]
+lib.cp_timing_end.restype = _int
 
 
 class CausalProductError(RuntimeError):
@@ -95,6 +99,26 @@ def _check_tensors(*ts):
             raise ValueError("all tensors must share one device and one dtype")
         if not t.is_contiguous():
             raise ValueError("tensors must be contiguous")
+
+
+def timing_begin(capacity: int) -> None:
+    """Record the start and end of each of the next ``capacity`` kernel
+    launches made by this thread (their dispatch timestamps)."""
+    _check("cp_timing_begin", lib.cp_timing_begin(int(capacity)))
+    global _timing_capacity
+    _timing_capacity = int(capacity)
+
+
+def timing_end() -> list:
+    """Wait for the launches recorded since timing_begin and return their
+    durations in milliseconds, in launch order."""
+    buf = (ctypes.c_float * max(1, _timing_capacity))()
+    n = _int(0)
+    _check("cp_timing_end", lib.cp_timing_end(buf, ctypes.byref(n)))
+    return [buf[i] for i in range(n.value)]
+
+
+_timing_capacity = 0
 
 
 def causal_product_fwd(q, k, v, out=None, state_out=None):
@@ -189,4 +213,4 @@ def linear_attention(q, k, v, eps: float = 1e-6, feature_map: str = "elu+1"):
 
 
 __all__ = ["causal_product_fwd", "causal_product_bwd", "linear_attn_fwd", "causal_product", "linear_attention",
-           "CausalProductError", "lib", "LIB_PATH"]
+           "CausalProductError", "lib", "LIB_PATH", "timing_begin", "timing_end"]

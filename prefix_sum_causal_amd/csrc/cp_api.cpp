@@ -6,15 +6,18 @@
 
 #include <hip/hip_runtime.h>
 
+#include <hip/hip_ext.h>
+
 #include <cmath>
 #include <cstdint>
 #include <cstdlib>
+#include <vector>
 
 #include "cp_launch.hpp"
 
 namespace {
 
-constexpr int kAbiMajor = 1, kAbiMinor = 0;
+constexpr int kAbiMajor = 1, kAbiMinor = 1;  // 1.1: kernel timing
 
 struct Range {
     uintptr_t lo, hi;  // [lo, hi)
@@ -70,11 +73,76 @@ Range span(const void *p, int64_t bytes) {
 
 int launch_status(hipError_t e) { return e == hipSuccess ? CP_OK : CP_ERR_HIP; }
 
+// Per-thread kernel timing (cp_timing_begin / cp_timing_end).
+struct Timing {
+    bool on = false;
+    int used = 0;
+    std::vector<hipEvent_t> start, stop;
+    void release() {
+        for (hipEvent_t e : start) (void)hipEventDestroy(e);
+        for (hipEvent_t e : stop) (void)hipEventDestroy(e);
+        start.clear();
+        stop.clear();
+        on = false;
+        used = 0;
+    }
+};
+thread_local Timing timing;
+
 }  // namespace
+
+namespace cp {
+
+hipError_t launch_kernel(const void *kernel, dim3 grid, dim3 block, void **args, hipStream_t stream) {
+    if (timing.on && timing.used < (int)timing.start.size()) {
+        const int i = timing.used++;
+        return hipExtLaunchKernel(kernel, grid, block, args, 0, stream, timing.start[i], timing.stop[i], 0);
+    }
+    return hipLaunchKernel(kernel, grid, block, args, 0, stream);
+}
+
+}  // namespace cp
 
 extern "C" {
 
 int cp_abi_version(void) { return (kAbiMajor << 16) | kAbiMinor; }
+
+int cp_timing_begin(int capacity) {
+    if (capacity < 1 || capacity > 65536) return CP_ERR_DIM;
+    timing.release();
+    timing.start.reserve(capacity);
+    timing.stop.reserve(capacity);
+    for (int i = 0; i < capacity; ++i) {
+        hipEvent_t a = nullptr, b = nullptr;
+        if (hipEventCreate(&a) != hipSuccess) {
+            timing.release();
+            return CP_ERR_HIP;
+        }
+        if (hipEventCreate(&b) != hipSuccess) {
+            (void)hipEventDestroy(a);
+            timing.release();
+            return CP_ERR_HIP;
+        }
+        timing.start.push_back(a);
+        timing.stop.push_back(b);
+    }
+    timing.on = true;
+    return CP_OK;
+}
+
+int cp_timing_end(float *ms, int *count) {
+    if (!ms || !count || !timing.on) return CP_ERR_NULL;
+    int st = CP_OK;
+    const int n = timing.used;
+    for (int i = 0; i < n && st == CP_OK; ++i) {
+        if (hipEventSynchronize(timing.stop[i]) != hipSuccess ||
+            hipEventElapsedTime(&ms[i], timing.start[i], timing.stop[i]) != hipSuccess)
+            st = CP_ERR_HIP;
+    }
+    *count = st == CP_OK ? n : 0;
+    timing.release();
+    return st;
+}
 
 const char *cp_status_string(int status) {
     switch (status) {

@@ -17,7 +17,7 @@ hipError_t launch_bwd(const BwdArgs &a, hipStream_t s) {
     T *dq = static_cast<T *>(a.dQ), *dk = static_cast<T *>(a.dK), *dv = static_cast<T *>(a.dV);
     int L = a.L, NS = a.NS;
     void *args[] = {&q, &k, &v, &g, &st, &dq, &dk, &dv, &L, &NS};
-    return hipLaunchKernel(reinterpret_cast<const void *>(kern), dim3(NS * P::BG), dim3(bwd_threads<T, E, M, P::BG>()), args, 0, s);
+    return launch_kernel(reinterpret_cast<const void *>(kern), dim3(NS * P::BG), dim3(bwd_threads<T, E, M, P::BG>()), args, s);
 }
 
 }  // namespace

@@ -17,8 +17,8 @@ hipError_t launch_fwd(const FwdArgs &a, hipStream_t s) {
     int L = a.L, NS = a.NS;
     float eps = a.eps;
     void *args[] = {&q, &k, &v, &o, &st, &L, &NS, &eps};
-    return hipLaunchKernel(reinterpret_cast<const void *>(kern), dim3(NS * P::FG), dim3(64 * (M / 16 / P::FG) * P::FRS), args,
-                           0, s);
+    return launch_kernel(reinterpret_cast<const void *>(kern), dim3(NS * P::FG), dim3(64 * (M / 16 / P::FG) * P::FRS), args,
+                         s);
 }
 
 template <int E, int M, bool NORM>

@@ -34,6 +34,11 @@ fwd_fn fwd_bf16(int E, int M, bool norm);
 bwd_fn bwd_f32(int E, int M);
 bwd_fn bwd_bf16(int E, int M);
 
+// Launch a kernel on stream: hipLaunchKernel, or, while the calling thread
+// has a timing in progress (cp_timing_begin), hipExtLaunchKernel with the
+// next pair of timing events.
+hipError_t launch_kernel(const void *kernel, dim3 grid, dim3 block, void **args, hipStream_t stream);
+
 // Workgroups per (n, h) slice of each kernel.
 inline int fwd_parts(int E, int M) { (void)E; return M / 16; }
 inline int bwd_parts(int E, int M) { return (E > M ? E : M) / 16; }

@@ -34,7 +34,7 @@
 #define CP_BF16_FNPF 3
 #endif
 #ifndef CP_BF16_BNPF
-#define CP_BF16_BNPF 3
+#define CP_BF16_BNPF 4
 #endif
 #ifndef CP_BF16_BG
 #define CP_BF16_BG 2

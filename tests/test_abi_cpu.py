@@ -37,7 +37,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(
-        ["causal_product_fwd", "causal_product_bwd", "linear_attn_fwd", "cp_status_string", "cp_abi_version"])
+        ["causal_product_fwd", "causal_product_bwd", "linear_attn_fwd", "cp_status_string", "cp_abi_version",
+         "cp_timing_begin", "cp_timing_end"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -52,7 +53,20 @@ def test_status_strings_and_version(lib):
         assert msg and msg not in seen
         seen.add(msg)
     assert lib.cp_status_string(99).decode() == "unknown status"
-    assert lib.cp_abi_version() == (1 << 16)
+    assert lib.cp_abi_version() == (1 << 16) | 1
+
+
+def test_timing_rejects_bad_arguments_before_any_device_call(lib):
+    lib.cp_timing_begin.argtypes = [ctypes.c_int]
+    lib.cp_timing_end.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    assert lib.cp_timing_begin(0) == DIM
+    assert lib.cp_timing_begin(-3) == DIM
+    assert lib.cp_timing_begin(65537) == DIM
+    ms = (ctypes.c_float * 4)()
+    n = ctypes.c_int(7)
+    assert lib.cp_timing_end(None, ctypes.byref(n)) == NULL
+    assert lib.cp_timing_end(ms, None) == NULL
+    assert lib.cp_timing_end(ms, ctypes.byref(n)) == NULL  # nothing begun
 
 
 # fake, 16-byte aligned, disjoint addresses (never dereferenced)
