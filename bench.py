@@ -155,15 +155,25 @@ def main() -> int:
     # Each launch in the timed region carries its own start/end events (the
     # timestamps of its dispatch on the stream it runs on, as a profiler's
     # kernel trace reports them); the whole-step rate is wall time.
-    cp.timing_begin(args.steps * len(kinds))
+    # Launches per call: a forward over few slices is two launches (segment
+    # states, then the sweep); count them on one untimed step.
+    cp.timing_begin(64)
+    step()
+    per_step = len(cp.timing_end())
+    n_first = per_step - (1 if w.op == "fwd+bwd" else 0)
+    cp.timing_begin(args.steps * per_step)
     t0 = time.perf_counter()
     for i in range(args.steps):
         step()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms = cp.timing_end()
-    assert len(ms) == args.steps * len(kinds), "every timed launch is recorded"
-    times = {kind: sum(ms[j::len(kinds)]) / args.steps * 1e-3 for j, kind in enumerate(kinds)}
+    assert len(ms) == args.steps * per_step, "every timed launch is recorded"
+    # a call's time is the sum of its launches
+    times = {kinds[0]: sum(sum(ms[i * per_step:i * per_step + n_first]) for i in range(args.steps))
+             / args.steps * 1e-3}
+    if w.op == "fwd+bwd":
+        times["bwd"] = sum(ms[i * per_step + n_first] for i in range(args.steps)) / args.steps * 1e-3
     per_kernel = {}
     for kind in kinds:
         b = algorithmic_bytes(w, kind)

@@ -314,38 +314,6 @@ struct Stage {
     }
 };
 
-// Output staging: result tiles go into a natural LDS copy of the chunk's
-// output rows (C rows x W columns), and the workgroup then writes whole rows
-// to HBM as 16-byte pieces -- the same coalesced pattern as the input copy.
-// Stores of 16-row tiles straight from the MFMA layout touch 16 lines per
-// instruction with 8 bytes per lane and stream far slower.
-template <typename T, int NT, int C, int W>
-struct OutStage {
-    static constexpr int PPR = W * (int)sizeof(T) / 16;  // pieces per row
-    static constexpr int P = C * PPR;
-    static constexpr int NP = (P + NT - 1) / NT;
-    static constexpr int RS = lds_stride<T, W>();
-    static_assert(W * (int)sizeof(T) % 16 == 0, "rows must be whole 16-byte pieces");
-
-    // tile lane (g, r) holds X[16 rb + r][16 cb + 4g + t]
-    __device__ static __forceinline__ void put(T *lds, int rb, int cb, f32x4 v) {
-        T *p = lds + (16 * rb + lane_r()) * RS + 16 * cb + 4 * lane_g();
-        *reinterpret_cast<typename Ops<T>::frag *>(p) = Ops<T>::cvt(v);
-    }
-    // rows of X (rows outside the range are dropped), columns [col0, col0 + W)
-    __device__ static __forceinline__ void flush(const T *lds, const Rows<T> &X, int col0) {
-#pragma unroll
-        for (int i = 0; i < NP; ++i) {
-            const int p = (int)threadIdx.x + i * NT;
-            if (P % NT != 0 && p >= P) continue;
-            const int row = p / PPR, cp = p % PPR;
-            const i32x4 x = *reinterpret_cast<const i32x4 *>(lds + row * RS + cp * (16 / (int)sizeof(T)));
-            const int off = (row * X.ld + col0) * (int)sizeof(T) + cp * 16;
-            __builtin_amdgcn_raw_buffer_store_b128(x, X.rsrc, off, 0, 0);
-        }
-    }
-};
-
 // Order this wave's LDS writes before its later LDS reads of other lanes'
 // data and vice versa.  A workgroup here is a single wave, so this is all the
 // synchronisation LDS needs (no s_barrier, no wait on global loads).

@@ -20,9 +20,7 @@
 //   - reads the chunk's Q and K rows (16-byte natural reads),
 //   - forms the causal score tiles A^T(J, I) = K_J Q_I^T, J <= I (every wave
 //     forms all of them: cheaper than exchanging them through LDS),
-//   - accumulates its output block Out^T = V^T A^T + S^T Q^T into an LDS
-//     copy of the chunk's output rows, which the workgroup writes to HBM as
-//     whole rows after the next barrier, and
+//   - accumulates its output block Out^T = V^T A^T + S^T Q^T, and
 //   - updates its E x 16 block of the state, S += K^T V (transposed reads).
 // So each row of the inputs enters LDS once per workgroup and the state is
 // updated once, by the wave that owns its columns.  Products run in the
@@ -58,12 +56,14 @@ constexpr int last_block(int h) {
     return last;
 }
 
-// The chunk loop of one wave: output column block cb of the workgroup's
-// group, query row blocks of row set H.  Every wave runs the same staging
-// and barriers; the state is carried (redundantly) by every row set.
-template <typename T, int E, int M, int C, int NW, int RSPLIT, int NPF, bool OST, bool NORM, bool FMAP, int H>
-__device__ __forceinline__ void fwd_sweep(const T *q_, const T *k_, const T *v_, T *o_, int L, int grp, int cb,
-                                          float eps, T *lds, f32x4 (&S)[E / 16]) {
+// The chunk loop of one wave over rows [rb, re) of its slice: output column
+// block cb of the workgroup's group, query row blocks of row set H.  Every
+// wave runs the same staging and barriers; the state (S, z: carried in and
+// out by reference) is carried by every row set.  SONLY: only the state is
+// accumulated (no Q, no outputs).
+template <typename T, int E, int M, int C, int NW, int RSPLIT, int NPF, bool NORM, bool FMAP, bool SONLY, int H>
+__device__ __forceinline__ void fwd_sweep(const T *q_, const T *k_, const T *v_, T *o_, int rb, int re, int grp,
+                                          int cb, float eps, T *lds, f32x4 (&S)[E / 16], f32x4 (&z)[E / 16]) {
     using O = Ops<T>;
     using F = typename O::frag;
     using EO = EOps<T, E>;
@@ -73,88 +73,80 @@ __device__ __forceinline__ void fwd_sweep(const T *q_, const T *k_, const T *v_,
     using SQ = Stage<T, NT, C, E>;
     using SV = Stage<T, NT, C, MW>;
     constexpr int RQ = SQ::RS, RV = SV::RS;
-    using SO = OutStage<T, NT, C, MW>;
     constexpr int BUF = 2 * C * RQ + C * RV;  // Q, K, V columns of the group
-    T *const obuf = lds + 2 * BUF;             // two output row buffers of C * SO::RS
     constexpr int JMAX = last_block<CB, RSPLIT>(H);  // key blocks this wave scores: J <= JMAX
 
     const Diag diag;
-    f32x4 z[EB];  // z[ecol(eb) + estride g + t] (same in every lane r)
-#pragma unroll
-    for (int e = 0; e < EB; ++e) z[e] = zero4();
 
     // Ring of NPF register stages: NPF-1 chunks are in flight while one is
     // computed.  The step loop is padded to a multiple of NPF; padded chunks
-    // lie past L, load as zero and store nothing.
+    // lie past re, load as zero and store nothing.
     struct Stages {
         SQ q, k;
         SV v;
-        __device__ __forceinline__ void load(const T *q_, const T *k_, const T *v_, int row0, int L, int col0) {
-            q.load(Rows<T>(q_, E, row0, L, C), 0);
-            k.load(Rows<T>(k_, E, row0, L, C), 0);
-            v.load(Rows<T>(v_, M, row0, L, C), col0);
+        __device__ __forceinline__ void load(const T *q_, const T *k_, const T *v_, int row0, int re, int col0) {
+            if constexpr (!SONLY) q.load(Rows<T>(q_, E, row0, re, C), 0);
+            k.load(Rows<T>(k_, E, row0, re, C), 0);
+            v.load(Rows<T>(v_, M, row0, re, C), col0);
         }
     };
     const int col0 = 16 * grp * NW;
     Stages st[NPF];
 #pragma unroll
     for (int s = 0; s < NPF - 1; ++s) {
-        st[s].load(q_, k_, v_, s * C, L, col0);
+        st[s].load(q_, k_, v_, rb + s * C, re, col0);
         __builtin_amdgcn_sched_barrier(0);  // stages complete in order
     }
 
-    const int nchunks = (L + C - 1) / C;
+    const int nchunks = (re - rb + C - 1) / C;
     const int nsteps = (nchunks + NPF - 1) / NPF * NPF;
     for (int c0 = 0; c0 < nsteps; c0 += NPF) {
 #pragma unroll
         for (int s = 0; s < NPF; ++s) {
             const int c = c0 + s;
-            const int row0 = c * C;
+            const int row0 = rb + c * C;
             T *Qs = lds + (c & 1) * BUF, *Ks = Qs + C * RQ, *Vs = Ks + C * RQ;
-            st[s].q.template store<NORM && FMAP>(Qs, row0, L);
-            st[s].k.template store<NORM && FMAP>(Ks, row0, L);
+            if constexpr (!SONLY) st[s].q.template store<NORM && FMAP>(Qs, row0, re);
+            st[s].k.template store<NORM && FMAP>(Ks, row0, re);
             st[s].v.store(Vs);
             __syncthreads();
             // The next chunk's loads are issued one array at a time between
-            // the products below, and the output rows (this chunk's tiles, or
-            // with OST the previous chunk's rows staged in LDS before this
-            // barrier) in the middle of the state update, so that the vector
-            // memory unit drains while the matrix cores work.  Stores go after
-            // the step's loads: memory operations complete in issue order, so
-            // the rows waited for at a later step never wait for these stores.
+            // the products below, and the output tiles in the middle of the
+            // state update, so that the vector memory unit drains while the
+            // matrix cores work.  Stores go after the step's loads: memory
+            // operations complete in issue order, so the rows waited for at a
+            // later step never wait for these stores.
             Stages &nx = st[(s + NPF - 1) % NPF];
             const int nrow0 = row0 + (NPF - 1) * C;
             f32x4 pend[CB];  // this step's output tiles (owned row blocks)
             int nload = 0;   // arrays of the next chunk whose loads are issued
             auto issue_load = [&]() {
-                if (nload == 0) nx.q.load(Rows<T>(q_, E, nrow0, L, C), 0);
-                if (nload == 1) nx.k.load(Rows<T>(k_, E, nrow0, L, C), 0);
-                if (nload == 2) nx.v.load(Rows<T>(v_, M, nrow0, L, C), col0);
+                if constexpr (!SONLY)
+                    if (nload == 0) nx.q.load(Rows<T>(q_, E, nrow0, re, C), 0);
+                if (nload == 1) nx.k.load(Rows<T>(k_, E, nrow0, re, C), 0);
+                if (nload == 2) nx.v.load(Rows<T>(v_, M, nrow0, re, C), col0);
                 ++nload;
                 __builtin_amdgcn_sched_barrier(0);
             };
-            // the step's output rows (after every owned row block is done)
+            // the step's output tiles (after every owned row block is done)
             auto issue_store = [&]() {
-                if constexpr (OST) {
-                    SO::flush(obuf + ((c - 1) & 1) * C * SO::RS, Rows<T>(o_, M, row0 - C, L, C), col0);
-                } else {
-                    const Rows<T> ro(o_, M, row0, L, C);
+                const Rows<T> ro(o_, M, row0, re, C);
 #pragma unroll
-                    for (int I = 0; I < CB; ++I)
-                        if (owns_block<CB, RSPLIT>(H, I)) st_out<T>(ro, I, grp * NW + cb, pend[I]);
-                }
+                for (int I = 0; I < CB; ++I)
+                    if (owns_block<CB, RSPLIT>(H, I)) st_out<T>(ro, I, grp * NW + cb, pend[I]);
                 __builtin_amdgcn_sched_barrier(0);
             };
             issue_load();
+            F vt[CB];  // V_J^T fragments of this wave's columns
+#pragma unroll
+            for (int b = 0; b < CB; ++b) vt[b] = O::tr_frag(Vs, RV, b, cb);
+            if constexpr (!SONLY) {
 
             RF kf[CB][KS];
 #pragma unroll
             for (int b = 0; b <= JMAX; ++b)
 #pragma unroll
                 for (int k = 0; k < KS; ++k) kf[b][k] = EO::load(Ks, RQ, b, k);
-            F vt[CB];  // V_J^T fragments of this wave's columns
-#pragma unroll
-            for (int b = 0; b < CB; ++b) vt[b] = O::tr_frag(Vs, RV, b, cb);
             // S_{c-1} (and z_{c-1}) as A operands
             RF sa[KS], zh[KS], zl[KS];
 #pragma unroll
@@ -208,12 +200,8 @@ __device__ __forceinline__ void fwd_sweep(const T *q_, const T *k_, const T *v_,
                 pend[I] = o;
                 issue_load();
             }
-            while (nload < 3) issue_load();
-            if constexpr (OST) {
-#pragma unroll
-                for (int I = 0; I < CB; ++I)
-                    if (owns_block<CB, RSPLIT>(H, I)) SO::put(obuf + (c & 1) * C * SO::RS, I, cb, pend[I]);
             }
+            while (nload < 3) issue_load();
 
             // S_c = S_{c-1} + K_c^T V_c  (and z_c = z_{c-1} + K_c^T 1)
 #pragma unroll
@@ -222,20 +210,25 @@ __device__ __forceinline__ void fwd_sweep(const T *q_, const T *k_, const T *v_,
                 if constexpr (NORM)
                     dotk<T>(z[e], 0, CB, [&](int J) { return EO::tr_e(Ks, RQ, J, e); },
                             [&](int) { return O::ones(); });
-                if (e == (EB - 1) / 2) issue_store();
+                if constexpr (!SONLY)
+                    if (e == (EB - 1) / 2) issue_store();
             }
         }
     }
-    if constexpr (OST) {  // the last chunk's output rows
-        __syncthreads();
-        SO::flush(obuf + ((nsteps - 1) & 1) * C * SO::RS, Rows<T>(o_, M, (nsteps - 1) * C, L, C), col0);
-    }
 }
 
-template <typename T, int E, int M, int C, int G, int RSPLIT, int NPF, bool OST, bool NORM, bool FMAP>
+// Sequence segments: when slices are too few to fill the GPU, each slice is
+// cut into nseg segments of seg_len rows (a multiple of C) and run in two
+// launches.  The first (SONLY) computes each segment's state increment
+// dS = sum over its rows of k v^T (and dz = sum of phi(k)) into ws; the
+// second starts segment s from the exclusive sum of the increments of the
+// segments before it (the chunked scan's carry, one level up) and sweeps only
+// its own rows.  ws holds, per slice and segment, E*M floats of dS (row e,
+// column m) then E floats of dz.  With one segment, ws is unused (NULL).
+template <typename T, int E, int M, int C, int G, int RSPLIT, int NPF, bool NORM, bool FMAP, bool SONLY>
 __global__ __launch_bounds__(64 * (M / 16 / G) * RSPLIT) void cp_fwd_kernel(
     const T *__restrict__ Q, const T *__restrict__ K, const T *__restrict__ V, T *__restrict__ Out,
-    float *__restrict__ state_out, int L, int NS, float eps) {
+    float *__restrict__ state_out, float *__restrict__ ws, int L, int NS, int seg_len, float eps) {
     using EO = EOps<T, E>;
     constexpr int EB = E / 16, MB = M / 16, CB = C / 16;
     static_assert(MB % G == 0, "column groups split the column blocks evenly");
@@ -244,30 +237,64 @@ __global__ __launch_bounds__(64 * (M / 16 / G) * RSPLIT) void cp_fwd_kernel(
     constexpr int NW = MB / G, NT = 64 * NW * RSPLIT, MW = 16 * NW;
     constexpr int RQ = Stage<T, NT, C, E>::RS, RV = Stage<T, NT, C, MW>::RS;
     constexpr int BUF = 2 * C * RQ + C * RV;
-    constexpr int OBUF = OST ? C * OutStage<T, NT, C, MW>::RS : 0;
-    __shared__ __attribute__((aligned(16))) T lds[2 * BUF + 2 * OBUF];
+    constexpr int WS = E * M + E;  // floats per (slice, segment) in ws
+    __shared__ __attribute__((aligned(16))) T lds[2 * BUF];
 
-    int slice, grp;
-    map_block(blockIdx.x, NS, G, slice, grp);
+    const int nseg = (L + seg_len - 1) / seg_len;
+    int slice, part;
+    map_block(blockIdx.x, NS, G * nseg, slice, part);
+    const int grp = part % G, seg = part / G;
+    if (SONLY && seg == nseg - 1) return;  // the last segment's increment is never needed
     const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
     const int cb = w % NW, h = w / NW;
+    const int mb = grp * NW + cb;
     const int g = lane_g(), r = lane_r();
     const T *q_ = Q + (int64_t)slice * L * E;
     const T *k_ = K + (int64_t)slice * L * E;
     const T *v_ = V + (int64_t)slice * L * M;
     T *o_ = Out + (int64_t)slice * L * M;
+    const int rb = seg * seg_len, re = rb + seg_len < L ? rb + seg_len : L;
+    float *ws_slice = ws ? ws + (int64_t)slice * nseg * WS : nullptr;
 
     f32x4 S[EB];  // S[ecol(eb) + estride g + t][16 mb + r]
+    f32x4 z[EB];  // z[ecol(eb) + estride g + t] (same in every lane r)
 #pragma unroll
-    for (int e = 0; e < EB; ++e) S[e] = zero4();
+    for (int e = 0; e < EB; ++e) {
+        S[e] = zero4();
+        z[e] = zero4();
+    }
+    if (!SONLY && ws_slice) {
+        for (int p = 0; p < seg; ++p) {
+            const float *dS = ws_slice + (int64_t)p * WS, *dz = dS + E * M;
+#pragma unroll
+            for (int e = 0; e < EB; ++e)
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const int row = EO::ecol(e) + EO::estride * g + t;
+                    S[e][t] += dS[row * M + 16 * mb + r];
+                    if constexpr (NORM) z[e][t] += dz[row];
+                }
+        }
+    }
     if (h == 0)
-        fwd_sweep<T, E, M, C, NW, RSPLIT, NPF, OST, NORM, FMAP, 0>(q_, k_, v_, o_, L, grp, cb, eps, lds, S);
+        fwd_sweep<T, E, M, C, NW, RSPLIT, NPF, NORM, FMAP, SONLY, 0>(q_, k_, v_, o_, rb, re, grp, cb, eps, lds, S, z);
     else
-        fwd_sweep<T, E, M, C, NW, RSPLIT, NPF, OST, NORM, FMAP, 1>(q_, k_, v_, o_, L, grp, cb, eps, lds, S);
-    const int mb = grp * NW + cb;
+        fwd_sweep<T, E, M, C, NW, RSPLIT, NPF, NORM, FMAP, SONLY, 1>(q_, k_, v_, o_, rb, re, grp, cb, eps, lds, S, z);
 
-    if constexpr (!NORM) {
-        if (state_out && h == 0) {
+    if constexpr (SONLY) {
+        if (h == 0) {
+            float *dS = ws_slice + (int64_t)seg * WS, *dz = dS + E * M;
+#pragma unroll
+            for (int e = 0; e < EB; ++e)
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const int row = EO::ecol(e) + EO::estride * g + t;
+                    dS[row * M + 16 * mb + r] = S[e][t];
+                    if (NORM && mb == 0 && r == 0) dz[row] = z[e][t];
+                }
+        }
+    } else if constexpr (!NORM) {
+        if (state_out && h == 0 && seg == nseg - 1) {
             float *st_ = state_out + (int64_t)slice * E * M;
 #pragma unroll
             for (int e = 0; e < EB; ++e)

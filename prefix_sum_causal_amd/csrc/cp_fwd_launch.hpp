@@ -1,0 +1,85 @@
+// cp_fwd_launch.hpp -- host side of the forward and normalised-forward
+// launches, shared by the bf16 and fp32 translation units.
+#pragma once
+
+#include "cp_fwd.hpp"
+#include "cp_launch.hpp"
+#include "cp_tune.hpp"
+
+namespace cp {
+
+// Segments per slice for L rows and NS slices: one, unless the slices leave
+// most CUs idle; then enough segments of at least kMinSegChunks chunks for
+// about two workgroups per CU.
+constexpr int kCUs = 256, kMinSegChunks = 4;
+inline int fwd_segments(int L, int NS, int groups, int C) {
+    const long wg = (long)NS * groups;
+    const int nchunks = (L + C - 1) / C;
+    if (wg >= kCUs || nchunks < 2 * kMinSegChunks) return 1;
+    long want = (2L * kCUs + wg - 1) / wg;
+    const long most = nchunks / kMinSegChunks;
+    return (int)(want < most ? want : most);
+}
+
+template <typename T, int E, int M, bool NORM, bool FMAP>
+hipError_t launch_fwd_t(const FwdArgs &a, hipStream_t s) {
+    using P = Tune<T, E, M>;
+    const T *q = static_cast<const T *>(a.Q), *k = static_cast<const T *>(a.K), *v = static_cast<const T *>(a.V);
+    T *o = static_cast<T *>(a.Out);
+    float *st = a.state_out;
+    int L = a.L, NS = a.NS;
+    float eps = a.eps;
+    const dim3 block(64 * (M / 16 / P::FG) * P::FRS);
+
+    const int nseg0 = fwd_segments(L, NS, P::FG, P::FC);
+    const int nchunks = (L + P::FC - 1) / P::FC;
+    int seg_len = (nchunks + nseg0 - 1) / nseg0 * P::FC;
+    const int nseg = (L + seg_len - 1) / seg_len;
+    float *ws = nullptr;
+    hipError_t e = hipSuccess;
+    if (nseg > 1) {
+        // per slice and segment: the E x M increment of the state, then E of z
+        const size_t bytes = (size_t)NS * nseg * (E * M + E) * sizeof(float);
+        e = hipMallocAsync(reinterpret_cast<void **>(&ws), bytes, s);
+        if (e != hipSuccess) return e;
+        auto k1 = cp_fwd_kernel<T, E, M, P::FC, P::FG, P::FRS, P::FNPF, NORM, FMAP, true>;
+        void *args1[] = {&q, &k, &v, &o, &st, &ws, &L, &NS, &seg_len, &eps};
+        e = launch_kernel(reinterpret_cast<const void *>(k1), dim3(NS * P::FG * nseg), block, args1, s);
+    } else {
+        seg_len = L;
+    }
+    if (e == hipSuccess) {
+        auto k2 = cp_fwd_kernel<T, E, M, P::FC, P::FG, P::FRS, P::FNPF, NORM, FMAP, false>;
+        void *args2[] = {&q, &k, &v, &o, &st, &ws, &L, &NS, &seg_len, &eps};
+        e = launch_kernel(reinterpret_cast<const void *>(k2), dim3(NS * P::FG * nseg), block, args2, s);
+    }
+    if (ws) {
+        const hipError_t f = hipFreeAsync(ws, s);
+        if (e == hipSuccess) e = f;
+    }
+    return e;
+}
+
+template <typename T, int E, int M, bool NORM>
+hipError_t launch_fwd_fm(const FwdArgs &a, hipStream_t s) {
+    if (NORM && a.fmap) return launch_fwd_t<T, E, M, NORM, true>(a, s);
+    return launch_fwd_t<T, E, M, NORM, false>(a, s);
+}
+
+template <typename T, bool NORM>
+fwd_fn pick_fwd(int E, int M) {
+    static const fwd_fn table[4][4] = {
+        {launch_fwd_fm<T, 16, 16, NORM>, launch_fwd_fm<T, 16, 32, NORM>, launch_fwd_fm<T, 16, 64, NORM>,
+         launch_fwd_fm<T, 16, 128, NORM>},
+        {launch_fwd_fm<T, 32, 16, NORM>, launch_fwd_fm<T, 32, 32, NORM>, launch_fwd_fm<T, 32, 64, NORM>,
+         launch_fwd_fm<T, 32, 128, NORM>},
+        {launch_fwd_fm<T, 64, 16, NORM>, launch_fwd_fm<T, 64, 32, NORM>, launch_fwd_fm<T, 64, 64, NORM>,
+         launch_fwd_fm<T, 64, 128, NORM>},
+        {launch_fwd_fm<T, 128, 16, NORM>, launch_fwd_fm<T, 128, 32, NORM>, launch_fwd_fm<T, 128, 64, NORM>,
+         launch_fwd_fm<T, 128, 128, NORM>},
+    };
+    const int ie = size_index(E), im = size_index(M);
+    return (ie < 0 || im < 0) ? nullptr : table[ie][im];
+}
+
+}  // namespace cp

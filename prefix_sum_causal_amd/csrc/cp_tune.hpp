@@ -7,8 +7,6 @@
 //        block of dQ, dK and dV, one wave per block,
 //   FRS  forward row sets: waves per output column block, which split the
 //        chunk's query row blocks,
-//   FOST forward output rows go through LDS and leave as whole rows (else
-//        the result tiles are stored from registers),
 //   FNPF, BNPF  stages of the forward / backward load ring (NPF-1 chunks are
 //        in flight while one is computed),
 // Each value can be overridden when the library is built (-DCP_BF16_FC=32 ...)
@@ -26,9 +24,6 @@
 #endif
 #ifndef CP_BF16_FRS
 #define CP_BF16_FRS 2
-#endif
-#ifndef CP_BF16_FOST
-#define CP_BF16_FOST 0
 #endif
 #ifndef CP_BF16_FNPF
 #define CP_BF16_FNPF 3
@@ -76,14 +71,13 @@ template <int E, int M> struct Tune<__bf16, E, M> {
     static constexpr bool wide = E > 64 || M > 64;
     // one-wave workgroups with wide features hold a whole chunk per thread:
     // shorter chunks keep them in registers
-    static constexpr int FC = ((M == 16 && E >= 64) || (E == 128 && M == 32)) && CP_BF16_FC > 32 ? 32 : CP_BF16_FC;
+    static constexpr int FC = ((M == 16 && E >= 64) || (E == 128 && M <= 64)) && CP_BF16_FC > 32 ? 32 : CP_BF16_FC;
     // 128 output columns: two workgroups of four waves (registers per wave)
     static constexpr int FG0 = M > 64 && CP_BF16_FG < 2 ? 2 : CP_BF16_FG;
     static constexpr int FG = FG0 > M / 16 ? M / 16 : FG0;
     static constexpr int BC = wide && CP_BF16_BC > 32 ? 32 : CP_BF16_BC;
-    static constexpr int FRS = FC >= 64 ? CP_BF16_FRS : 1;
+    static constexpr int FRS = FC >= 64 && E <= 64 ? CP_BF16_FRS : 1;  // E = 128: registers
     static constexpr int FNPF = CP_BF16_FNPF;
-    static constexpr bool FOST = CP_BF16_FOST != 0;
     static constexpr int BNPF = CP_BF16_BNPF;
     static constexpr int BG = bwd_groups(E, M, CP_BF16_BG);
 };
@@ -98,7 +92,6 @@ template <int E, int M> struct Tune<float, E, M> {
     static constexpr int BC = wide ? 16 : CP_F32_BC;
     static constexpr int FRS = 1;
     static constexpr int FNPF = CP_F32_FNPF;
-    static constexpr bool FOST = false;
     static constexpr int BNPF = CP_F32_BNPF;
     static constexpr int BG = bwd_groups(E, M, CP_F32_BG);
 };
