@@ -5,7 +5,8 @@
 // Lane l of a 64-lane wave is split into g = l / 16 (0..3) and r = l % 16.
 // All matrix products are 16 x 16 output tiles D += A * B computed by MFMA:
 //   bf16 I/O: v_mfma_f32_16x16x32_bf16 (A 16x32, B 32x16, fp32 accumulate)
-//   fp32 I/O: v_mfma_f32_16x16x4_f32   (A 16x4,  B 4x16)
+//   fp32 I/O: the same MFMA on split hi + lo bf16 operands (see Ops<float>),
+//             or v_mfma_f32_16x16x4_f32 (A 16x4, B 4x16)
 // with these lane layouts (checked on gfx950):
 //   A operand: lane (g, r) holds row r of A,
 //   B operand: lane (g, r) holds column r of B,
@@ -76,13 +77,6 @@ template <> struct Ops<bf16> {
     __device__ static __forceinline__ void mma1(f32x4 &acc, frag a0, frag b0) {
         mma2(acc, a0, zero(), b0, zero());
     }
-    // the same products into a fresh accumulator (inline zero operand)
-    __device__ static __forceinline__ f32x4 mma2z(frag a0, frag a1, frag b0, frag b1) {
-        bf16x8 a = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
-        bf16x8 b = __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7);
-        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, zero4(), 0, 0, 0);
-    }
-    __device__ static __forceinline__ f32x4 mma1z(frag a0, frag b0) { return mma2z(a0, zero(), b0, zero()); }
     __device__ static __forceinline__ frag cvt(f32x4 x) {
         frag f;
 #pragma unroll
@@ -102,12 +96,6 @@ template <> struct Ops<bf16> {
         s16x4 m = {(short)0x8000, (short)0x8000, (short)0x8000, (short)0x8000};
         return __builtin_bit_cast(frag, s ^ m);
     }
-    __device__ static __forceinline__ f32x4 widen(frag a) {
-        f32x4 x;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) x[t] = (float)a[t];
-        return x;
-    }
     // lane (g, r) <- X[16 tb + 4g + t][16 cb + r] from a natural LDS copy
     // with row stride rs (elements).
     __device__ static __forceinline__ frag tr_frag(const bf16 *lds, int rs, int tb, int cb) {
@@ -119,8 +107,19 @@ template <> struct Ops<bf16> {
     }
 };
 
-// fp32 I/O: fragments are 4 floats; the fp32 MFMA takes one k value per lane,
-// so a k-block is four MFMAs (t = 0..3 pairs k = 4g + t on both operands).
+// fp32 I/O: fragments are 4 floats.  Products run as split bf16 by default
+// (CP_F32_SPLIT): each fp32 operand x is cut into hi = bf16(x) and
+// lo = bf16(x - hi), 16 significant bits together, and a product keeps
+// hi*hi + hi*lo + lo*hi (the dropped lo*lo term is below 2^-16 of it), three
+// bf16 MFMAs of 16x16x32 with fp32 accumulation instead of eight fp32 MFMAs of
+// 16x16x4 -- gfx950's fp32 matrix rate is a sixteenth of its bf16 rate.
+// Values with at most 16 significant bits (small integers among them) are
+// split exactly, so their products are exact.  With CP_F32_SPLIT=0 the fp32
+// MFMA is used: a k-block is then four MFMAs (t = 0..3 pairs k = 4g + t on
+// both operands).
+#ifndef CP_F32_SPLIT
+#define CP_F32_SPLIT 1
+#endif
 template <> struct Ops<float> {
     using frag = f32x4;
 
@@ -129,24 +128,39 @@ template <> struct Ops<float> {
         f32x4 o = {1.f, 1.f, 1.f, 1.f};
         return o;
     }
-    __device__ static __forceinline__ void mma1(f32x4 &acc, frag a, frag b) {
+    // two k-blocks of fp32 as hi and lo bf16 operands (8 values per lane)
+    __device__ static __forceinline__ void split8(frag x0, frag x1, bf16x8 &hi, bf16x8 &lo) {
 #pragma unroll
-        for (int t = 0; t < 4; ++t) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[t], b[t], acc, 0, 0, 0);
+        for (int t = 0; t < 4; ++t) {
+            const bf16 h0 = (bf16)x0[t], h1 = (bf16)x1[t];
+            hi[t] = h0;
+            hi[4 + t] = h1;
+            lo[t] = (bf16)(x0[t] - (float)h0);
+            lo[4 + t] = (bf16)(x1[t] - (float)h1);
+        }
     }
     __device__ static __forceinline__ void mma2(f32x4 &acc, frag a0, frag a1, frag b0, frag b1) {
-        mma1(acc, a0, b0);
-        mma1(acc, a1, b1);
-    }
-    __device__ static __forceinline__ f32x4 mma1z(frag a, frag b) {
-        f32x4 acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[0], b[0], zero4(), 0, 0, 0);
+        if constexpr (CP_F32_SPLIT != 0) {
+            bf16x8 ah, al, bh, bl;
+            split8(a0, a1, ah, al);
+            split8(b0, b1, bh, bl);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc, 0, 0, 0);
+        } else {
 #pragma unroll
-        for (int t = 1; t < 4; ++t) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[t], b[t], acc, 0, 0, 0);
-        return acc;
+            for (int t = 0; t < 4; ++t) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a0[t], b0[t], acc, 0, 0, 0);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a1[t], b1[t], acc, 0, 0, 0);
+        }
     }
-    __device__ static __forceinline__ f32x4 mma2z(frag a0, frag a1, frag b0, frag b1) {
-        f32x4 acc = mma1z(a0, b0);
-        mma1(acc, a1, b1);
-        return acc;
+    __device__ static __forceinline__ void mma1(f32x4 &acc, frag a, frag b) {
+        if constexpr (CP_F32_SPLIT != 0) {
+            mma2(acc, a, zero(), b, zero());
+        } else {
+#pragma unroll
+            for (int t = 0; t < 4; ++t) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[t], b[t], acc, 0, 0, 0);
+        }
     }
     __device__ static __forceinline__ frag cvt(f32x4 x) { return x; }
     __device__ static __forceinline__ void split(f32x4 x, frag &hi, frag &lo) {
@@ -154,7 +168,6 @@ template <> struct Ops<float> {
         lo = zero4();
     }
     __device__ static __forceinline__ frag neg(frag a) { return -a; }
-    __device__ static __forceinline__ f32x4 widen(frag a) { return a; }
     __device__ static __forceinline__ frag tr_frag(const float *lds, int rs, int tb, int cb) {
         const int g = lane_g(), r = lane_r();
         f32x4 v;
@@ -172,32 +185,6 @@ __device__ __forceinline__ typename Ops<T>::frag lds_nat(const T *lds, int rs, i
                                                              4 * lane_g());
 }
 
-// Score-type tile D = X_xb Y_yb^T, D[i][j] = sum_k X[16 xb + i][k] Y[16 yb + j][k]
-// over KB k-blocks, with both operands natural rows of LDS copies.  Only the
-// pairing of k between the operands matters here, so bf16 reads 8
-// consecutive elements per lane (one 16-byte read, k = 32 p + 8g + v) instead
-// of two 4-element fragments.
-template <typename T, int KB>
-__device__ __forceinline__ f32x4 nn_tile(const T *X, int rx, int xb, const T *Y, int ry, int yb) {
-    using O = Ops<T>;
-    if constexpr (sizeof(T) == 2 && KB >= 2) {
-        const int g = lane_g(), r = lane_r();
-        const bf16x8 *xp = reinterpret_cast<const bf16x8 *>(X + (16 * xb + r) * rx + 8 * g);
-        const bf16x8 *yp = reinterpret_cast<const bf16x8 *>(Y + (16 * yb + r) * ry + 8 * g);
-        f32x4 acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xp[0], yp[0], zero4(), 0, 0, 0);
-#pragma unroll
-        for (int p = 1; p < KB / 2; ++p)
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xp[4 * p], yp[4 * p], acc, 0, 0, 0);
-        if constexpr (KB & 1) O::mma1(acc, lds_nat<T>(X, rx, xb, KB - 1), lds_nat<T>(Y, ry, yb, KB - 1));
-        return acc;
-    } else {
-        f32x4 acc = O::mma1z(lds_nat<T>(X, rx, xb, 0), lds_nat<T>(Y, ry, yb, 0));
-#pragma unroll
-        for (int b = 1; b < KB; ++b) O::mma1(acc, lds_nat<T>(X, rx, xb, b), lds_nat<T>(Y, ry, yb, b));
-        return acc;
-    }
-}
-
 // acc += sum over k-blocks b in [b0, b1) of A_b * B_b.  For bf16 the blocks
 // go to the MFMA in pairs; an odd count is padded with a zero block.
 template <typename T, typename FA, typename FB>
@@ -207,15 +194,6 @@ __device__ __forceinline__ void dotk(f32x4 &acc, int b0, int b1, FA fa, FB fb) {
 #pragma unroll
     for (; b + 1 < b1; b += 2) O::mma2(acc, fa(b), fa(b + 1), fb(b), fb(b + 1));
     if (b < b1) O::mma1(acc, fa(b), fb(b));
-}
-
-// sum over k-blocks b in [b0, b1) of A_b * B_b into a fresh tile (b1 > b0).
-template <typename T, typename FA, typename FB>
-__device__ __forceinline__ f32x4 dotz(int b0, int b1, FA fa, FB fb) {
-    using O = Ops<T>;
-    f32x4 acc = (b0 + 1 < b1) ? O::mma2z(fa(b0), fa(b0 + 1), fb(b0), fb(b0 + 1)) : O::mma1z(fa(b0), fb(b0));
-    dotk<T>(acc, b0 + 2, b1, fa, fb);
-    return acc;
 }
 
 // phi(x) = elu(x) + 1 = x + 1 for x > 0, exp(x) otherwise.
@@ -314,15 +292,6 @@ struct Stage {
     }
 };
 
-// Order this wave's LDS writes before its later LDS reads of other lanes'
-// data and vice versa.  A workgroup here is a single wave, so this is all the
-// synchronisation LDS needs (no s_barrier, no wait on global loads).
-__device__ __forceinline__ void wave_lds_sync() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
 // Causal masks of a diagonal 16x16 tile.  Lane (g, r) holds rows 4g + t of
 // column r; the keep-predicates depend on the lane only and are computed once.
 struct Diag {
@@ -363,6 +332,7 @@ struct Diag {
 template <typename T, int E> struct EOps;
 
 template <int E> struct EOps<bf16, E> {
+    static constexpr bool SPLIT_STATE = true;  // states enter as hi + lo bf16 pairs where accuracy needs it
     static constexpr int EB = E / 16;
     static constexpr bool WIDE = EB >= 2;
     static constexpr int STEPS = WIDE ? EB / 2 : 1;
@@ -415,19 +385,32 @@ template <int E> struct EOps<bf16, E> {
 
 template <int E> struct EOps<float, E> {
     static constexpr int EB = E / 16;
-    static constexpr int STEPS = EB;
+    static constexpr int STEPS = (EB + 1) / 2;  // two k-blocks per step
     static constexpr int estride = 4;
-    using rf = f32x4;
+    struct rf {
+        f32x4 a, b;
+    };
 
     __device__ static __forceinline__ int ecol(int eb) { return 16 * eb; }
     __device__ static __forceinline__ rf load(const float *lds, int rs, int rb, int s) {
-        return *reinterpret_cast<const f32x4 *>(lds + (16 * rb + lane_r()) * rs + 16 * s + 4 * lane_g());
+        rf x;
+        x.a = lds_nat<float>(lds, rs, rb, 2 * s);
+        x.b = 2 * s + 1 < EB ? lds_nat<float>(lds, rs, rb, 2 * s + 1) : zero4();
+        return x;
     }
-    __device__ static __forceinline__ void mma(f32x4 &acc, rf a, rf b) { Ops<float>::mma1(acc, a, b); }
-    __device__ static __forceinline__ rf state(const f32x4 *tiles, int s) { return tiles[s]; }
+    __device__ static __forceinline__ void mma(f32x4 &acc, rf x, rf y) { Ops<float>::mma2(acc, x.a, x.b, y.a, y.b); }
+    __device__ static __forceinline__ rf state(const f32x4 *tiles, int s) {
+        rf x;
+        x.a = tiles[2 * s];
+        x.b = 2 * s + 1 < EB ? tiles[2 * s + 1] : zero4();
+        return x;
+    }
+    // fp32 states need no hi/lo pair of operands (the product splits them)
+    static constexpr bool SPLIT_STATE = false;
     __device__ static __forceinline__ void state_split(const f32x4 *tiles, int s, rf &hi, rf &lo) {
-        hi = tiles[s];
-        lo = zero4();
+        hi = state(tiles, s);
+        lo.a = zero4();
+        lo.b = zero4();
     }
     __device__ static __forceinline__ f32x4 tr_e(const float *lds, int rs, int tb, int eb) {
         return Ops<float>::tr_frag(lds, rs, tb, eb);

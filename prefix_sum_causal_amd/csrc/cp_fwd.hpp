@@ -169,7 +169,7 @@ __device__ __forceinline__ void fwd_sweep(const T *q_, const T *k_, const T *v_,
 #pragma unroll
                     for (int k = 0; k < KS; ++k) {
                         EO::mma(d, zh[k], qf[k]);
-                        EO::mma(d, zl[k], qf[k]);
+                        if constexpr (EO::SPLIT_STATE) EO::mma(d, zl[k], qf[k]);
                     }
                 }
                 // intra-chunk: Out^T += V^T A^T with A^T(J, I) = K_J Q_I^T
@@ -207,9 +207,11 @@ __device__ __forceinline__ void fwd_sweep(const T *q_, const T *k_, const T *v_,
 #pragma unroll
             for (int e = 0; e < EB; ++e) {
                 dotk<T>(S[e], 0, CB, [&](int J) { return EO::tr_e(Ks, RQ, J, e); }, [&](int J) { return vt[J]; });
+                // (the state-only sweep stores z from the first column block)
                 if constexpr (NORM)
-                    dotk<T>(z[e], 0, CB, [&](int J) { return EO::tr_e(Ks, RQ, J, e); },
-                            [&](int) { return O::ones(); });
+                    if (!SONLY || grp * NW + cb == 0)
+                        dotk<T>(z[e], 0, CB, [&](int J) { return EO::tr_e(Ks, RQ, J, e); },
+                                [&](int) { return O::ones(); });
                 if constexpr (!SONLY)
                     if (e == (EB - 1) / 2) issue_store();
             }

@@ -34,6 +34,12 @@
 #ifndef CP_BF16_BG
 #define CP_BF16_BG 2
 #endif
+#ifndef CP_F32_WIDE_FC
+#define CP_F32_WIDE_FC 32
+#endif
+#ifndef CP_F32_WIDE_BC
+#define CP_F32_WIDE_BC 16
+#endif
 #ifndef CP_F32_BG
 #define CP_F32_BG 2
 #endif
@@ -71,13 +77,13 @@ template <int E, int M> struct Tune<__bf16, E, M> {
     static constexpr bool wide = E > 64 || M > 64;
     // one-wave workgroups with wide features hold a whole chunk per thread:
     // shorter chunks keep them in registers
-    static constexpr int FC = ((M == 16 && E >= 64) || (E == 128 && M <= 64)) && CP_BF16_FC > 32 ? 32 : CP_BF16_FC;
+    static constexpr int FC = ((M == 16 && E >= 64) || E == 128) && CP_BF16_FC > 32 ? 32 : CP_BF16_FC;
     // 128 output columns: two workgroups of four waves (registers per wave)
     static constexpr int FG0 = M > 64 && CP_BF16_FG < 2 ? 2 : CP_BF16_FG;
     static constexpr int FG = FG0 > M / 16 ? M / 16 : FG0;
     static constexpr int BC = wide && CP_BF16_BC > 32 ? 32 : CP_BF16_BC;
     static constexpr int FRS = FC >= 64 && E <= 64 ? CP_BF16_FRS : 1;  // E = 128: registers
-    static constexpr int FNPF = CP_BF16_FNPF;
+    static constexpr int FNPF = E == 128 && CP_BF16_FNPF > 2 ? 2 : CP_BF16_FNPF;  // E = 128: registers
     static constexpr int BNPF = CP_BF16_BNPF;
     static constexpr int BG = bwd_groups(E, M, CP_BF16_BG);
 };
@@ -86,10 +92,10 @@ template <int E, int M> struct Tune<__bf16, E, M> {
 // shorter chunks.
 template <int E, int M> struct Tune<float, E, M> {
     static constexpr bool wide = E > 64 || M > 64;
-    static constexpr int FC = wide ? 16 : CP_F32_FC;
+    static constexpr int FC = wide ? CP_F32_WIDE_FC : CP_F32_FC;
     static constexpr int FG0 = M > 64 && CP_F32_FG < 2 ? 2 : CP_F32_FG;
     static constexpr int FG = FG0 > M / 16 ? M / 16 : FG0;
-    static constexpr int BC = wide ? 16 : CP_F32_BC;
+    static constexpr int BC = wide ? CP_F32_WIDE_BC : CP_F32_BC;
     static constexpr int FRS = 1;
     static constexpr int FNPF = CP_F32_FNPF;
     static constexpr int BNPF = CP_F32_BNPF;
