@@ -61,23 +61,21 @@ class Oracle:
 
     def __init__(self, libpath: str = LIB):
         self.lib = ctypes.CDLL(libpath)
-        four = [_f32p, _f32p, _f32p, _f64p, _i64, _i64, _i64, _i64]
-        for name in ("oracle_fwd", "oracle_fwd_brute"):
-            fn = getattr(self.lib, name)
-            fn.argtypes = four
-            fn.restype = None
-        for name in ("oracle_linattn", "oracle_linattn_brute"):
-            fn = getattr(self.lib, name)
-            fn.argtypes = four + [ctypes.c_double, ctypes.c_int]
-            fn.restype = None
+        L = self.lib
+        dims = [_i64, _i64, _i64, _i64]
+        L.oracle_fwd.argtypes = [_f32p, _f32p, _f32p, _f32p, _f64p, _f64p] + dims
+        L.oracle_fwd_brute.argtypes = [_f32p, _f32p, _f32p, _f32p, _f64p] + dims
+        L.oracle_linattn.argtypes = ([_f32p] * 5 + [_f64p] * 3 + dims + [ctypes.c_double, ctypes.c_int])
+        L.oracle_linattn_brute.argtypes = ([_f32p] * 5 + [_f64p] + dims + [ctypes.c_double, ctypes.c_int])
         for name in ("oracle_bwd", "oracle_bwd_brute"):
-            fn = getattr(self.lib, name)
-            fn.argtypes = [_f32p] * 4 + [_f64p] * 3 + [_i64] * 4
-            fn.restype = None
-        self.lib.oracle_state.argtypes = [_f32p, _f32p, _f64p, _i64, _i64, _i64, _i64]
-        self.lib.oracle_state.restype = None
-        self.lib.oracle_num_threads.argtypes = []
-        self.lib.oracle_num_threads.restype = ctypes.c_int
+            getattr(L, name).argtypes = [_f32p] * 5 + [_f64p] * 4 + dims
+        for name in ("oracle_fwd", "oracle_fwd_brute", "oracle_linattn", "oracle_linattn_brute", "oracle_bwd",
+                     "oracle_bwd_brute"):
+            getattr(L, name).restype = None
+        L.oracle_state.argtypes = [_f32p, _f32p, _f64p] + dims
+        L.oracle_state.restype = None
+        L.oracle_num_threads.argtypes = []
+        L.oracle_num_threads.restype = ctypes.c_int
 
     # -- shape helpers -----------------------------------------------------
     @staticmethod
@@ -89,55 +87,92 @@ class Oracle:
         NH = int(np.prod(Q.shape[:-2], dtype=np.int64)) if Q.ndim > 2 else 1
         return NH, L, E, M
 
+    @staticmethod
+    def _opt32(x, shape):
+        """An optional float input of the given shape (None -> NULL)."""
+        if x is None:
+            return None, None
+        a = _as_f32(x)
+        if a.shape != tuple(shape):
+            raise ValueError(f"expected shape {tuple(shape)}, got {a.shape}")
+        return a, _ptr32(a)
+
     def num_threads(self) -> int:
         return int(self.lib.oracle_num_threads())
 
     # -- forward -------------------------------------------------------------
-    def _fwd_common(self, fn, Q, K, V, *extra):
+    def _prep(self, Q, K, V):
         Q, K, V = _as_f32(Q), _as_f32(K), _as_f32(V)
         if K.shape != Q.shape:
             raise ValueError("K must have Q's shape")
-        NH, L, E, M = self._dims(Q, V)
+        return (Q, K, V) + self._dims(Q, V)
+
+    def fwd(self, Q, K, V, S0=None, return_state: bool = False):
+        """out_i = q_i^T S_i with S_i = S0 + sum_{j<=i} k_j v_j^T (O(L)
+        recurrence; S0 = 0 when None).  With return_state also the final
+        state S_{L-1}, shape [..., E, M]."""
+        Q, K, V, NH, L, E, M = self._prep(Q, K, V)
+        s0, p0 = self._opt32(S0, Q.shape[:-2] + (E, M))
         out = np.empty(V.shape, dtype=np.float64)
-        fn(_ptr32(Q), _ptr32(K), _ptr32(V), _ptr64(out), NH, L, E, M, *extra)
+        Sf = np.empty(Q.shape[:-2] + (E, M), dtype=np.float64)
+        self.lib.oracle_fwd(_ptr32(Q), _ptr32(K), _ptr32(V), p0, _ptr64(out), _ptr64(Sf), NH, L, E, M)
+        return (out, Sf) if return_state else out
+
+    def fwd_brute(self, Q, K, V, S0=None) -> np.ndarray:
+        """out_i = q_i^T S0 + sum_{j<=i} (q_i.k_j) v_j (O(L^2) masked brute force)."""
+        Q, K, V, NH, L, E, M = self._prep(Q, K, V)
+        s0, p0 = self._opt32(S0, Q.shape[:-2] + (E, M))
+        out = np.empty(V.shape, dtype=np.float64)
+        self.lib.oracle_fwd_brute(_ptr32(Q), _ptr32(K), _ptr32(V), p0, _ptr64(out), NH, L, E, M)
         return out
 
-    def fwd(self, Q, K, V) -> np.ndarray:
-        """out_i = q_i^T S_i with S_i = sum_{j<=i} k_j v_j^T (O(L) recurrence)."""
-        return self._fwd_common(self.lib.oracle_fwd, Q, K, V)
+    def linattn(self, Q, K, V, eps: float = 1e-6, feature_map: int = 1, S0=None, z0=None,
+                return_state: bool = False):
+        """Normalised causal linear attention (recurrence with running z, from
+        S0 and z0, zero when None).  With return_state also (S_{L-1}, z_{L-1})."""
+        Q, K, V, NH, L, E, M = self._prep(Q, K, V)
+        s0, p0 = self._opt32(S0, Q.shape[:-2] + (E, M))
+        zz, pz = self._opt32(z0, Q.shape[:-2] + (E,))
+        out = np.empty(V.shape, dtype=np.float64)
+        Sf = np.empty(Q.shape[:-2] + (E, M), dtype=np.float64)
+        zf = np.empty(Q.shape[:-2] + (E,), dtype=np.float64)
+        self.lib.oracle_linattn(_ptr32(Q), _ptr32(K), _ptr32(V), p0, pz, _ptr64(out), _ptr64(Sf), _ptr64(zf),
+                                NH, L, E, M, float(eps), int(feature_map))
+        return (out, Sf, zf) if return_state else out
 
-    def fwd_brute(self, Q, K, V) -> np.ndarray:
-        """out_i = sum_{j<=i} (q_i.k_j) v_j (O(L^2) masked brute force)."""
-        return self._fwd_common(self.lib.oracle_fwd_brute, Q, K, V)
-
-    def linattn(self, Q, K, V, eps: float = 1e-6, feature_map: int = 1) -> np.ndarray:
-        """Normalised causal linear attention (recurrence with running z)."""
-        return self._fwd_common(self.lib.oracle_linattn, Q, K, V, float(eps), int(feature_map))
-
-    def linattn_brute(self, Q, K, V, eps: float = 1e-6, feature_map: int = 1) -> np.ndarray:
+    def linattn_brute(self, Q, K, V, eps: float = 1e-6, feature_map: int = 1, S0=None, z0=None) -> np.ndarray:
         """Normalised causal linear attention (masked brute force)."""
-        return self._fwd_common(self.lib.oracle_linattn_brute, Q, K, V, float(eps), int(feature_map))
+        Q, K, V, NH, L, E, M = self._prep(Q, K, V)
+        s0, p0 = self._opt32(S0, Q.shape[:-2] + (E, M))
+        zz, pz = self._opt32(z0, Q.shape[:-2] + (E,))
+        out = np.empty(V.shape, dtype=np.float64)
+        self.lib.oracle_linattn_brute(_ptr32(Q), _ptr32(K), _ptr32(V), p0, pz, _ptr64(out), NH, L, E, M,
+                                      float(eps), int(feature_map))
+        return out
 
     # -- backward ------------------------------------------------------------
-    def _bwd_common(self, fn, Q, K, V, dO):
+    def _bwd_common(self, fn, Q, K, V, dO, S0, with_dS0):
         Q, K, V, dO = _as_f32(Q), _as_f32(K), _as_f32(V), _as_f32(dO)
         if K.shape != Q.shape or dO.shape != V.shape:
             raise ValueError("K must have Q's shape and dO V's shape")
         NH, L, E, M = self._dims(Q, V)
+        s0, p0 = self._opt32(S0, Q.shape[:-2] + (E, M))
         dQ = np.empty(Q.shape, dtype=np.float64)
         dK = np.empty(Q.shape, dtype=np.float64)
         dV = np.empty(V.shape, dtype=np.float64)
-        fn(_ptr32(Q), _ptr32(K), _ptr32(V), _ptr32(dO), _ptr64(dQ), _ptr64(dK), _ptr64(dV),
+        dS0 = np.empty(Q.shape[:-2] + (E, M), dtype=np.float64)
+        fn(_ptr32(Q), _ptr32(K), _ptr32(V), _ptr32(dO), p0, _ptr64(dQ), _ptr64(dK), _ptr64(dV), _ptr64(dS0),
            NH, L, E, M)
-        return dQ, dK, dV
+        return (dQ, dK, dV, dS0) if with_dS0 else (dQ, dK, dV)
 
-    def bwd(self, Q, K, V, dO):
-        """(dQ, dK, dV) by a forward sweep of S and a reverse sweep of R."""
-        return self._bwd_common(self.lib.oracle_bwd, Q, K, V, dO)
+    def bwd(self, Q, K, V, dO, S0=None, with_dS0: bool = False):
+        """(dQ, dK, dV[, dS0]) by a forward sweep of S (from S0) and a reverse
+        sweep of R; dS0 = sum_i q_i dO_i^T is the gradient of the initial state."""
+        return self._bwd_common(self.lib.oracle_bwd, Q, K, V, dO, S0, with_dS0)
 
-    def bwd_brute(self, Q, K, V, dO):
-        """(dQ, dK, dV) from the O(L^2) double sum."""
-        return self._bwd_common(self.lib.oracle_bwd_brute, Q, K, V, dO)
+    def bwd_brute(self, Q, K, V, dO, S0=None, with_dS0: bool = False):
+        """(dQ, dK, dV[, dS0]) from the O(L^2) double sum."""
+        return self._bwd_common(self.lib.oracle_bwd_brute, Q, K, V, dO, S0, with_dS0)
 
     def state(self, K, V) -> np.ndarray:
         """Final state sum_j k_j v_j^T per slice, shape [..., E, M]."""

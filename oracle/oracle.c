@@ -19,6 +19,15 @@
  *     den_i = phi(q_i) . z_i + eps,   z_i = sum_{j<=i} phi(k_j),
  * with phi = elu + 1 (alpha = 1): phi(x) = x + 1 for x > 0, exp(x) otherwise.
  *
+ * Carried state.  A slice may start from a given state instead of zero:
+ * S_{-1} = S0 (and z_{-1} = z0 in the normalised form), so that a sequence can
+ * be processed in segments, each starting from the final state of the one
+ * before (the loop of the opening post keeps that state explicitly).  Then
+ * out_i = q_i^T (S0 + sum_{j<=i} k_j v_j^T), and the gradient of
+ * f = sum_i out_i . dO_i with respect to S0 is sum_i q_i dO_i^T.  S0, z0 are
+ * [NH][E][M] and [NH][E] floats; NULL means zero.  Final states are written
+ * to [NH][E][M] (and [NH][E]) double arrays when the pointer is not NULL.
+ *
  * Layout: Q, K are [NH][L][E] and V, dO are [NH][L][M], row-major, contiguous,
  * given as float (fp32 values, or bf16 values widened exactly to fp32).  All
  * arithmetic is double precision.  Outputs are double arrays of the same
@@ -48,13 +57,15 @@ static double phi(double x) { return x > 0.0 ? x + 1.0 : exp(x); }
 /* ---------------------------------------------------------------------------
  * Forward, O(L E M) recurrence: S += k_i v_i^T, then out_i = q_i^T S.
  * ------------------------------------------------------------------------- */
-void oracle_fwd(const float *Q, const float *K, const float *V, double *Out,
-                int64_t NH, int64_t L, int64_t E, int64_t M) {
+void oracle_fwd(const float *Q, const float *K, const float *V, const float *S0, double *Out,
+                double *Sfin, int64_t NH, int64_t L, int64_t E, int64_t M) {
 #pragma omp parallel for schedule(static)
     for (int64_t s = 0; s < NH; ++s) {
         const float *q = Q + s * L * E, *k = K + s * L * E, *v = V + s * L * M;
         double *out = Out + s * L * M;
         double *S = (double *)calloc((size_t)(E * M), sizeof(double));
+        if (S0)
+            for (int64_t x = 0; x < E * M; ++x) S[x] = (double)S0[s * E * M + x];
         for (int64_t i = 0; i < L; ++i) {
             for (int64_t e = 0; e < E; ++e)
                 for (int64_t m = 0; m < M; ++m)
@@ -65,21 +76,28 @@ void oracle_fwd(const float *Q, const float *K, const float *V, double *Out,
                 out[i * M + m] = acc;
             }
         }
+        if (Sfin) memcpy(Sfin + s * E * M, S, (size_t)(E * M) * sizeof(double));
         free(S);
     }
 }
 
 /* ---------------------------------------------------------------------------
- * Forward, O(L^2 (E + M)) masked brute force: out_i = sum_{j<=i} (q_i.k_j) v_j.
+ * Forward, O(L^2 (E + M)) masked brute force:
+ *   out_i = q_i^T S0 + sum_{j<=i} (q_i.k_j) v_j.
  * ------------------------------------------------------------------------- */
-void oracle_fwd_brute(const float *Q, const float *K, const float *V, double *Out,
+void oracle_fwd_brute(const float *Q, const float *K, const float *V, const float *S0, double *Out,
                       int64_t NH, int64_t L, int64_t E, int64_t M) {
 #pragma omp parallel for schedule(static)
     for (int64_t s = 0; s < NH; ++s) {
         const float *q = Q + s * L * E, *k = K + s * L * E, *v = V + s * L * M;
         double *out = Out + s * L * M;
         for (int64_t i = 0; i < L; ++i) {
-            for (int64_t m = 0; m < M; ++m) out[i * M + m] = 0.0;
+            for (int64_t m = 0; m < M; ++m) {
+                double c = 0.0;
+                if (S0)
+                    for (int64_t e = 0; e < E; ++e) c += (double)q[i * E + e] * (double)S0[s * E * M + e * M + m];
+                out[i * M + m] = c;
+            }
             for (int64_t j = 0; j <= i; ++j) {
                 double a = 0.0;
                 for (int64_t e = 0; e < E; ++e) a += (double)q[i * E + e] * (double)k[j * E + e];
@@ -95,15 +113,19 @@ void oracle_fwd_brute(const float *Q, const float *K, const float *V, double *Ou
  *   S += phi(k_i) v_i^T;  z += phi(k_i);
  *   out_i = (phi(q_i)^T S) / (phi(q_i) . z + eps)
  * ------------------------------------------------------------------------- */
-void oracle_linattn(const float *Q, const float *K, const float *V, double *Out,
-                    int64_t NH, int64_t L, int64_t E, int64_t M, double eps,
-                    int feature_map) {
+void oracle_linattn(const float *Q, const float *K, const float *V, const float *S0, const float *z0,
+                    double *Out, double *Sfin, double *zfin, int64_t NH, int64_t L, int64_t E, int64_t M,
+                    double eps, int feature_map) {
 #pragma omp parallel for schedule(static)
     for (int64_t s = 0; s < NH; ++s) {
         const float *q = Q + s * L * E, *k = K + s * L * E, *v = V + s * L * M;
         double *out = Out + s * L * M;
         double *S = (double *)calloc((size_t)(E * M), sizeof(double));
         double *z = (double *)calloc((size_t)E, sizeof(double));
+        if (S0)
+            for (int64_t x = 0; x < E * M; ++x) S[x] = (double)S0[s * E * M + x];
+        if (z0)
+            for (int64_t e = 0; e < E; ++e) z[e] = (double)z0[s * E + e];
         double *fq = (double *)malloc((size_t)E * sizeof(double));
         double *fk = (double *)malloc((size_t)E * sizeof(double));
         for (int64_t i = 0; i < L; ++i) {
@@ -123,16 +145,19 @@ void oracle_linattn(const float *Q, const float *K, const float *V, double *Out,
                 out[i * M + m] = num / den;
             }
         }
+        if (Sfin) memcpy(Sfin + s * E * M, S, (size_t)(E * M) * sizeof(double));
+        if (zfin) memcpy(zfin + s * E, z, (size_t)E * sizeof(double));
         free(S); free(z); free(fq); free(fk);
     }
 }
 
 /* ---------------------------------------------------------------------------
- * Normalised forward, brute force:
- *   out_i = sum_{j<=i} a_ij v_j / (sum_{j<=i} a_ij + eps),  a_ij = phi(q_i).phi(k_j)
+ * Normalised forward, brute force, with c_i = phi(q_i):
+ *   out_i = (c_i^T S0 + sum_{j<=i} a_ij v_j) / (c_i . z0 + sum_{j<=i} a_ij + eps),
+ *   a_ij = c_i . phi(k_j)
  * ------------------------------------------------------------------------- */
-void oracle_linattn_brute(const float *Q, const float *K, const float *V, double *Out,
-                          int64_t NH, int64_t L, int64_t E, int64_t M, double eps,
+void oracle_linattn_brute(const float *Q, const float *K, const float *V, const float *S0, const float *z0,
+                          double *Out, int64_t NH, int64_t L, int64_t E, int64_t M, double eps,
                           int feature_map) {
 #pragma omp parallel for schedule(static)
     for (int64_t s = 0; s < NH; ++s) {
@@ -141,6 +166,12 @@ void oracle_linattn_brute(const float *Q, const float *K, const float *V, double
         for (int64_t i = 0; i < L; ++i) {
             double den = eps;
             for (int64_t m = 0; m < M; ++m) out[i * M + m] = 0.0;
+            for (int64_t e = 0; e < E; ++e) {
+                const double c = feature_map ? phi((double)q[i * E + e]) : (double)q[i * E + e];
+                if (z0) den += c * (double)z0[s * E + e];
+                if (S0)
+                    for (int64_t m = 0; m < M; ++m) out[i * M + m] += c * (double)S0[s * E * M + e * M + m];
+            }
             for (int64_t j = 0; j <= i; ++j) {
                 double a = 0.0;
                 for (int64_t e = 0; e < E; ++e) {
@@ -157,13 +188,16 @@ void oracle_linattn_brute(const float *Q, const float *K, const float *V, double
 }
 
 /* ---------------------------------------------------------------------------
- * Backward of out = causal_product(Q, K, V) for an upstream gradient dO,
- * i.e. the gradient of f = sum_i sum_{j<=i} (q_i.k_j)(v_j.dO_i).
- * Forward sweep:  S += k_i v_i^T;  dq_i = S dO_i.
+ * Backward of out = causal_product(Q, K, V) (from state S0) for an upstream
+ * gradient dO, i.e. the gradient of
+ *   f = sum_i [ q_i^T S0 dO_i + sum_{j<=i} (q_i.k_j)(v_j.dO_i) ].
+ * Forward sweep:  S = S0;  S += k_i v_i^T;  dq_i = S dO_i.
  * Reverse sweep:  R += q_i dO_i^T (i descending);  dk_i = R v_i;  dv_i = R^T k_i.
+ * The gradient of S0 is the final R (sum of all q_i dO_i^T), written to dS0
+ * when it is not NULL.
  * ------------------------------------------------------------------------- */
-void oracle_bwd(const float *Q, const float *K, const float *V, const float *dO,
-                double *dQ, double *dK, double *dV,
+void oracle_bwd(const float *Q, const float *K, const float *V, const float *dO, const float *S0,
+                double *dQ, double *dK, double *dV, double *dS0,
                 int64_t NH, int64_t L, int64_t E, int64_t M) {
 #pragma omp parallel for schedule(static)
     for (int64_t s = 0; s < NH; ++s) {
@@ -171,6 +205,8 @@ void oracle_bwd(const float *Q, const float *K, const float *V, const float *dO,
         const float *go = dO + s * L * M;
         double *dq = dQ + s * L * E, *dk = dK + s * L * E, *dv = dV + s * L * M;
         double *S = (double *)calloc((size_t)(E * M), sizeof(double));
+        if (S0)
+            for (int64_t x = 0; x < E * M; ++x) S[x] = (double)S0[s * E * M + x];
         for (int64_t i = 0; i < L; ++i) {
             for (int64_t e = 0; e < E; ++e)
                 for (int64_t m = 0; m < M; ++m)
@@ -198,18 +234,21 @@ void oracle_bwd(const float *Q, const float *K, const float *V, const float *dO,
                 dv[i * M + m] = acc;
             }
         }
+        if (dS0) memcpy(dS0 + s * E * M, R, (size_t)(E * M) * sizeof(double));
         free(S);
     }
 }
 
 /* ---------------------------------------------------------------------------
- * Backward, brute force from the double sum f = sum_i sum_{j<=i} (q_i.k_j)(v_j.dO_i):
- *   dq_i = sum_{j<=i} (dO_i.v_j) k_j
+ * Backward, brute force from
+ *   f = sum_i [ q_i^T S0 dO_i + sum_{j<=i} (q_i.k_j)(v_j.dO_i) ]:
+ *   dq_i = S0 dO_i + sum_{j<=i} (dO_i.v_j) k_j
  *   dk_j = sum_{i>=j} (dO_i.v_j) q_i
  *   dv_j = sum_{i>=j} (q_i.k_j) dO_i
+ *   dS0[e][m] = sum_i q_i[e] dO_i[m]
  * ------------------------------------------------------------------------- */
-void oracle_bwd_brute(const float *Q, const float *K, const float *V, const float *dO,
-                      double *dQ, double *dK, double *dV,
+void oracle_bwd_brute(const float *Q, const float *K, const float *V, const float *dO, const float *S0,
+                      double *dQ, double *dK, double *dV, double *dS0,
                       int64_t NH, int64_t L, int64_t E, int64_t M) {
 #pragma omp parallel for schedule(static)
     for (int64_t s = 0; s < NH; ++s) {
@@ -219,6 +258,19 @@ void oracle_bwd_brute(const float *Q, const float *K, const float *V, const floa
         for (int64_t x = 0; x < L * E; ++x) { dq[x] = 0.0; dk[x] = 0.0; }
         for (int64_t x = 0; x < L * M; ++x) dv[x] = 0.0;
         for (int64_t i = 0; i < L; ++i) {
+            for (int64_t e = 0; e < E; ++e) {
+                double c = 0.0;
+                if (S0)
+                    for (int64_t m = 0; m < M; ++m) c += (double)S0[s * E * M + e * M + m] * (double)go[i * M + m];
+                dq[i * E + e] = c;
+            }
+            if (dS0) {
+                double *g0 = dS0 + s * E * M;
+                if (i == 0)
+                    for (int64_t x = 0; x < E * M; ++x) g0[x] = 0.0;
+                for (int64_t e = 0; e < E; ++e)
+                    for (int64_t m = 0; m < M; ++m) g0[e * M + m] += (double)q[i * E + e] * (double)go[i * M + m];
+            }
             for (int64_t j = 0; j <= i; ++j) {
                 double gv = 0.0, qk = 0.0;
                 for (int64_t m = 0; m < M; ++m) gv += (double)go[i * M + m] * (double)v[j * M + m];

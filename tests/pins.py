@@ -322,6 +322,81 @@ def pin_bwd_recurrence_vs_brute(o):
         _close(a, b, what=f"d{name} O(L) vs O(L^2)")
 
 
+# -- carried state: S0 (and z0) as the state before the first row ----------------
+
+def _carry_inputs(seed, shape=(2, 1, 11, 3, 4)):
+    r = _rng(seed)
+    N, H, L, E, M = shape
+    Q, K = _rand(r, N, H, L, E, positive=True), _rand(r, N, H, L, E, positive=True)
+    V, dO = _rand(r, N, H, L, M), _rand(r, N, H, L, M)
+    S0, z0 = _rand(r, N, H, E, M), _rand(r, N, H, E, positive=True)
+    return Q, K, V, dO, S0, z0
+
+
+def pin_carry_fwd_library(o):
+    """out = Q S0 + tril(Q K^T) V and S_{L-1} = S0 + K^T V (torch, float64)."""
+    Q, K, V, _, S0, _ = _carry_inputs(40)
+    q, k, v, s0 = _t(Q), _t(K), _t(V), _t(S0)
+    out, Sf = o.fwd(Q, K, V, S0=S0, return_state=True)
+    _close(out, (q @ s0 + torch.tril(q @ k.transpose(-1, -2)) @ v).numpy(), what="fwd with S0")
+    _close(Sf, (s0 + k.transpose(-1, -2) @ v).numpy(), what="final state with S0")
+    _close(o.fwd_brute(Q, K, V, S0=S0), out, what="brute with S0")
+
+
+def pin_carry_fwd_composition(o):
+    """Running the rows in two pieces, the second from the first's final
+    state, gives the one-piece result (outputs and final state)."""
+    Q, K, V, _, S0, _ = _carry_inputs(41, (1, 2, 19, 4, 3))
+    full, Sf = o.fwd(Q, K, V, S0=S0, return_state=True)
+    for cut in (1, 7, 18):
+        a, Sa = o.fwd(Q[..., :cut, :], K[..., :cut, :], V[..., :cut, :], S0=S0, return_state=True)
+        b, Sb = o.fwd(Q[..., cut:, :], K[..., cut:, :], V[..., cut:, :], S0=Sa.astype(np.float32),
+                      return_state=True)
+        # the carried state passes through float32 (the boundary's type)
+        _close(np.concatenate([a, b], axis=-2), full, tol=1e-6, what=f"pieces at {cut}")
+        _close(Sb, Sf, tol=1e-6, what=f"final state, pieces at {cut}")
+
+
+def pin_carry_linattn_library(o):
+    """Normalised form from (S0, z0): numerator c_i^T S0 + sum a_ij v_j,
+    denominator c_i.z0 + sum a_ij + eps, final S and z (torch, float64)."""
+    Q, K, V, _, S0, z0 = _carry_inputs(42)
+    for fm in (0, 1):
+        c = torch_phi(_t(Q)) if fm else _t(Q)
+        f = torch_phi(_t(K)) if fm else _t(K)
+        a = torch.tril(c @ f.transpose(-1, -2))
+        num = c @ _t(S0) + a @ _t(V)
+        den = (c * _t(z0)[..., None, :]).sum(-1) + a.sum(-1) + 1e-6
+        out, Sf, zf = o.linattn(Q, K, V, 1e-6, fm, S0=S0, z0=z0, return_state=True)
+        _close(out, (num / den[..., None]).numpy(), what=f"linattn with S0, z0 (fm {fm})")
+        _close(Sf, (_t(S0) + f.transpose(-1, -2) @ _t(V)).numpy(), what="final S")
+        _close(zf, (_t(z0) + f.sum(-2)).numpy(), what="final z")
+        _close(o.linattn_brute(Q, K, V, 1e-6, fm, S0=S0, z0=z0), out, what="brute with S0, z0")
+
+
+def pin_carry_linattn_composition(o):
+    Q, K, V, _, S0, z0 = _carry_inputs(43, (1, 1, 23, 5, 2))
+    full = o.linattn(Q, K, V, 1e-6, 1, S0=S0, z0=z0)
+    a, Sa, za = o.linattn(Q[..., :9, :], K[..., :9, :], V[..., :9, :], 1e-6, 1, S0=S0, z0=z0, return_state=True)
+    b = o.linattn(Q[..., 9:, :], K[..., 9:, :], V[..., 9:, :], 1e-6, 1, S0=Sa.astype(np.float32),
+                  z0=za.astype(np.float32))
+    _close(np.concatenate([a, b], axis=-2), full, tol=1e-6, what="linattn pieces")
+
+
+def pin_carry_bwd_autograd(o):
+    """Gradients of sum(out * dO) with out = Q S0 + tril(Q K^T) V by torch
+    autograd in float64, among them the initial state's sum_i q_i dO_i^T."""
+    Q, K, V, dO, S0, _ = _carry_inputs(44)
+    ts = [_t(x).requires_grad_(True) for x in (Q, K, V, S0)]
+    q, k, v, s0 = ts
+    f = ((q @ s0 + torch.tril(q @ k.transpose(-1, -2)) @ v) * _t(dO)).sum()
+    f.backward()
+    want = [t.grad.numpy() for t in ts]
+    for got in (o.bwd(Q, K, V, dO, S0=S0, with_dS0=True), o.bwd_brute(Q, K, V, dO, S0=S0, with_dS0=True)):
+        for a, b, name in zip(got, want, ("dQ", "dK", "dV", "dS0")):
+            _close(a, b, what=f"{name} with S0")
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
 
 

@@ -39,6 +39,18 @@ MUTANTS = [
     ("oracle_bwd_brute", "dv[j * M + m] += qk * (double)go[i * M + m]", "dv[j * M + m] += qk * (double)go[j * M + m]",
      "dv with the wrong row of dO"),
     ("oracle_state", "(double)v[j * M + m]", "(double)v[(L - 1 - j) * M + m]", "state with reversed v"),
+    ("oracle_fwd", "S[x] = (double)S0[s * E * M + x];", "S[x] = 0.0;", "initial state ignored"),
+    ("oracle_fwd", "if (Sfin) memcpy(Sfin + s * E * M, S,", "if (Sfin) memcpy(Sfin + s * E * M, S + 1,",
+     "final state shifted by one"),
+    ("oracle_fwd_brute", "c += (double)q[i * E + e] * (double)S0", "c += (double)k[i * E + e] * (double)S0",
+     "carried state read with k"),
+    ("oracle_linattn", "z[e] = (double)z0[s * E + e];", "z[e] = 0.0;", "carried z ignored"),
+    ("oracle_linattn_brute", "if (z0) den += c * (double)z0[s * E + e];", "if (z0) den += (double)z0[s * E + e];",
+     "carried z not weighted by phi(q)"),
+    ("oracle_bwd", "S[x] = (double)S0[s * E * M + x];", "S[x] = (double)S0[s * E * M + (x % E) * M + x / E];",
+     "initial state transposed in dq"),
+    ("oracle_bwd_brute", "g0[e * M + m] += (double)q[i * E + e]", "g0[e * M + m] += (double)k[i * E + e]",
+     "gradient of the initial state from k"),
 ]
 
 
