@@ -137,7 +137,7 @@ def main() -> int:
         else:
             cp.causal_product_fwd(q, k, v, out=out, state_out=state)
         if w.op == "fwd+bwd":
-            cp.causal_product_bwd(q, k, v, g, state_in=state, dq=dq, dk=dk, dv=dv)
+            cp.causal_product_bwd(q, k, v, g, state_final=state, dq=dq, dk=dk, dv=dv)
 
     if args.calibrate_copy_mib:
         n = args.calibrate_copy_mib * (1 << 20) // 4

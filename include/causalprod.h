@@ -8,11 +8,15 @@
  * keeps a running prefix sum of outer products.  For every (n, h) slice and
  * token i = 0 .. L-1:
  *
- *     S_i   = S_{i-1} + k_i v_i^T        (E x M state, S_{-1} = 0)
+ *     S_i   = S_{i-1} + k_i v_i^T        (E x M state, S_{-1} = S0, zero by default)
  *     out_i = q_i^T S_i                  (inclusive of token i)
  *
  * The inclusive order (state updated with row i before row i is read) is the
- * order of the loop excerpt in a later comment on that page.
+ * order of the loop excerpt in a later comment on that page, whose loop also
+ * keeps that state explicitly: a caller may start a slice from a given state
+ * S0 and receive the final state, so that a long sequence can be processed in
+ * segments (each starting from the final state of the one before) or token
+ * by token.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -23,8 +27,13 @@
  *    type (round to nearest even).
  *  * All tensor pointers are DEVICE pointers owned by the caller, 16-byte
  *    aligned.  Outputs are fully overwritten (they need not be zeroed) and
- *    must not overlap any input or each other.  The library keeps no pointer
- *    after a call returns and allocates no device memory.
+ *    must not overlap any input or each other.  States are fp32: S as
+ *    [N][H][E][M] (row e, column m), z as [N][H][E].  The library keeps no
+ *    pointer after a call returns.  A forward call over too few slices to
+ *    fill the GPU splits each sequence into segments and takes a scratch
+ *    buffer of N*H*segments*(E*M + E) floats from the stream-ordered
+ *    allocator (hipMallocAsync), freed on the same stream after its last
+ *    use; no other call allocates device memory.
  *  * stream is a hipStream_t (NULL = the default stream).  Calls only enqueue
  *    work: they never synchronise the host, and buffers must stay alive until
  *    the stream has run the work.  Calls are stateless, thread-safe and
@@ -56,18 +65,18 @@ typedef enum {
 } cp_status;
 
 /*
- * causal_product_fwd: Out[n][h][i] = sum_{j<=i} (Q_i . K_j) V_j for every
- * slice, i.e. out_i = q_i^T S_i with S_i the inclusive prefix sum of k_j v_j^T
- * (the recurrence above).  Q and K are used as given (a feature map, if any,
- * is applied by the caller).
+ * causal_product_fwd: out_i = q_i^T S_i for every slice, with
+ * S_i = S0 + sum_{j<=i} k_j v_j^T (the recurrence above), i.e.
+ * Out[n][h][i] = Q_i^T S0 + sum_{j<=i} (Q_i . K_j) V_j.  Q and K are used as
+ * given (a feature map, if any, is applied by the caller).
  *
- * state_out (optional, may be NULL): fp32 [N][H][E][M], receives the final
- * state S_{L-1} = sum_j k_j v_j^T of every slice.  causal_product_bwd can
- * take it to run its query gradient in the same reverse sweep as the key and
- * value gradients.
+ * state_in (optional, NULL = zero): the initial state S0 of every slice.
+ * state_out (optional, may be NULL): receives the final state S_{L-1} of
+ * every slice (S0 included).  causal_product_bwd can take it to run its query
+ * gradient in the same reverse sweep as the key and value gradients.
  */
 int causal_product_fwd(const void *Q, const void *K, const void *V, void *Out,
-                       float *state_out,
+                       const float *state_in, float *state_out,
                        int64_t N, int64_t H, int64_t L, int64_t E, int64_t M,
                        int dtype, void *stream);
 
@@ -77,18 +86,22 @@ int causal_product_fwd(const void *Q, const void *K, const void *V, void *Out,
  *     dQ_i = sum_{j<=i} (dOut_i . V_j) K_j   = S_i dOut_i
  *     dK_j = sum_{i>=j} (dOut_i . V_j) Q_i   = R_j V_j
  *     dV_j = sum_{i>=j} (Q_i . K_j) dOut_i   = R_j^T K_j
- * with S_i the inclusive prefix sum of k v^T and R_j = sum_{i>=j} q_i dOut_i^T
- * the inclusive suffix sum.  Out is not needed.
+ * with S_i = S0 + the inclusive prefix sum of k v^T and
+ * R_j = sum_{i>=j} q_i dOut_i^T the inclusive suffix sum.  Out is not needed.
  *
- * state_in (optional, may be NULL): fp32 [N][H][E][M], the final state that
- * causal_product_fwd wrote to state_out for the same K and V.  With it every
- * gradient is produced by reverse sweeps that read each input once; with
- * NULL the query gradient runs its own forward sweep (more input traffic,
- * same result up to rounding).
+ * state_in (optional, NULL = zero): the initial state S0 the forward started
+ * from.  It is read only when state_final is NULL.
+ * state_final (optional, may be NULL): the final state that causal_product_fwd
+ * wrote to state_out for the same K, V and S0.  With it every gradient is
+ * produced by reverse sweeps that read each input once; with NULL the query
+ * gradient runs its own forward sweep from state_in (more input traffic, same
+ * result up to rounding).
+ * dstate_in (optional, may be NULL): receives the gradient of f with respect
+ * to S0, sum_i q_i dOut_i^T (= R_0), of every slice.
  */
 int causal_product_bwd(const void *Q, const void *K, const void *V, const void *dOut,
-                       const float *state_in,
-                       void *dQ, void *dK, void *dV,
+                       const float *state_in, const float *state_final,
+                       void *dQ, void *dK, void *dV, float *dstate_in,
                        int64_t N, int64_t H, int64_t L, int64_t E, int64_t M,
                        int dtype, void *stream);
 
@@ -101,8 +114,14 @@ int causal_product_bwd(const void *Q, const void *K, const void *V, const void *
  *     feature_map = 0: phi(x) = x (the caller has already mapped Q and K)
  * eps >= 0 is added to the denominator as given (1e-6 is the usual value).
  * Any other feature_map value, or eps < 0 or not finite, is CP_ERR_UNSUPPORTED.
+ *
+ * state_in, z_in (optional, NULL = zero): the state S and normaliser z before
+ * the first row (S_{-1}, z_{-1}); state_out, z_out (optional, may be NULL):
+ * receive S_{L-1} and z_{L-1}.  Sums include phi: S_i = S_{-1} +
+ * sum_{j<=i} phi(k_j) v_j^T, z_i = z_{-1} + sum_{j<=i} phi(k_j).
  */
 int linear_attn_fwd(const void *Q, const void *K, const void *V, void *Out,
+                    const float *state_in, const float *z_in, float *state_out, float *z_out,
                     int64_t N, int64_t H, int64_t L, int64_t E, int64_t M,
                     float eps, int feature_map, int dtype, void *stream);
 

@@ -39,11 +39,11 @@ if not os.path.exists(LIB_PATH):
 lib = ctypes.CDLL(LIB_PATH)
 
 _vp, _i64, _int = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
-lib.causal_product_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _int, _vp]
+lib.causal_product_fwd.argtypes = [_vp] * 6 + [_i64] * 5 + [_int, _vp]
 lib.causal_product_fwd.restype = _int
-lib.causal_product_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _int, _vp]
+lib.causal_product_bwd.argtypes = [_vp] * 10 + [_i64] * 5 + [_int, _vp]
 lib.causal_product_bwd.restype = _int
-lib.linear_attn_fwd.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, ctypes.c_float, _int, _int, _vp]
+lib.linear_attn_fwd.argtypes = [_vp] * 8 + [_i64] * 5 + [ctypes.c_float, _int, _int, _vp]
 lib.linear_attn_fwd.restype = _int
 lib.cp_status_string.argtypes = [_int]
 lib.cp_status_string.restype = ctypes.c_char_p
@@ -121,26 +121,38 @@ def timing_end() -> list:
 _timing_capacity = 0
 
 
-def causal_product_fwd(q, k, v, out=None, state_out=None):
-    """out[n,h,i] = sum_{j<=i} (q_i . k_j) v_j.  ``state_out`` (fp32
-    [N,H,E,M], optional) receives the final state sum_j k_j v_j^T."""
+def _check_state(name, t, shape, device):
+    """An optional fp32 state tensor (None passes)."""
+    if t is not None and (t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != shape
+                          or t.device != device):
+        raise ValueError(f"{name} must be a contiguous float32 {list(shape)} tensor on q's device")
+
+
+def causal_product_fwd(q, k, v, out=None, state_in=None, state_out=None):
+    """out_i = q_i^T S_i with S_i = S0 + sum_{j<=i} k_j v_j^T.  ``state_in``
+    (fp32 [N,H,E,M], optional, None = zero) is S0; ``state_out`` (optional)
+    receives the final state S_{L-1}."""
     N, H, L, E, M = _dims(q, v)
     if k.shape != q.shape:
         raise ValueError("k must have q's shape")
     if out is None:
         out = torch.empty_like(v)
     _check_tensors(q, k, v, out)
-    if state_out is not None and (state_out.dtype != torch.float32 or not state_out.is_contiguous()
-                                  or tuple(state_out.shape) != (N, H, E, M) or state_out.device != q.device):
-        raise ValueError("state_out must be a contiguous float32 [N,H,E,M] tensor on q's device")
+    _check_state("state_in", state_in, (N, H, E, M), q.device)
+    _check_state("state_out", state_out, (N, H, E, M), q.device)
     _check("causal_product_fwd", lib.causal_product_fwd(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(state_out), N, H, L, E, M, _dtype_code(q), _stream(q.device)))
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(state_in), _ptr(state_out), N, H, L, E, M, _dtype_code(q),
+        _stream(q.device)))
     return out
 
 
-def causal_product_bwd(q, k, v, dout, state_in=None, dq=None, dk=None, dv=None):
-    """Gradients (dq, dk, dv) of sum(out * dout) for out = causal_product_fwd(q, k, v).
-    ``state_in``: optional final state from causal_product_fwd's state_out."""
+def causal_product_bwd(q, k, v, dout, state_final=None, state_in=None, dq=None, dk=None, dv=None,
+                       dstate_in=None):
+    """Gradients (dq, dk, dv) of sum(out * dout) for out = causal_product_fwd(q, k, v, state_in=S0).
+    ``state_final``: optional final state from causal_product_fwd's state_out;
+    ``state_in``: the S0 the forward started from (read only without
+    state_final); ``dstate_in`` (optional fp32 [N,H,E,M]) receives the
+    gradient of S0, sum_i q_i dout_i^T."""
     N, H, L, E, M = _dims(q, v)
     if k.shape != q.shape or dout.shape != v.shape:
         raise ValueError("k must have q's shape and dout v's shape")
@@ -148,52 +160,63 @@ def causal_product_bwd(q, k, v, dout, state_in=None, dq=None, dk=None, dv=None):
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
     _check_tensors(q, k, v, dout, dq, dk, dv)
-    if state_in is not None and (state_in.dtype != torch.float32 or not state_in.is_contiguous()
-                                 or tuple(state_in.shape) != (N, H, E, M) or state_in.device != q.device):
-        raise ValueError("state_in must be a contiguous float32 [N,H,E,M] tensor on q's device")
+    for name, t in (("state_final", state_final), ("state_in", state_in), ("dstate_in", dstate_in)):
+        _check_state(name, t, (N, H, E, M), q.device)
     _check("causal_product_bwd", lib.causal_product_bwd(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(state_in), _ptr(dq), _ptr(dk), _ptr(dv),
-        N, H, L, E, M, _dtype_code(q), _stream(q.device)))
+        _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(state_in), _ptr(state_final), _ptr(dq), _ptr(dk), _ptr(dv),
+        _ptr(dstate_in), N, H, L, E, M, _dtype_code(q), _stream(q.device)))
     return dq, dk, dv
 
 
-def linear_attn_fwd(q, k, v, eps: float = 1e-6, feature_map: int = 1, out=None):
+def linear_attn_fwd(q, k, v, eps: float = 1e-6, feature_map: int = 1, out=None, state_in=None, z_in=None,
+                    state_out=None, z_out=None):
     """out_i = phi(q_i)^T S_i / (phi(q_i) . z_i + eps) with phi = elu + 1
-    (feature_map=1) or the identity (feature_map=0) applied to the raw q, k."""
+    (feature_map=1) or the identity (feature_map=0) applied to the raw q, k.
+    Optional fp32 states: state_in [N,H,E,M] and z_in [N,H,E] before the
+    first row (None = zero); state_out, z_out receive the final S and z."""
     N, H, L, E, M = _dims(q, v)
     if k.shape != q.shape:
         raise ValueError("k must have q's shape")
     if out is None:
         out = torch.empty_like(v)
     _check_tensors(q, k, v, out)
+    for name, t, shape in (("state_in", state_in, (N, H, E, M)), ("z_in", z_in, (N, H, E)),
+                           ("state_out", state_out, (N, H, E, M)), ("z_out", z_out, (N, H, E))):
+        _check_state(name, t, shape, q.device)
     _check("linear_attn_fwd", lib.linear_attn_fwd(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(out), N, H, L, E, M, float(eps), int(feature_map),
-        _dtype_code(q), _stream(q.device)))
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(state_in), _ptr(z_in), _ptr(state_out), _ptr(z_out),
+        N, H, L, E, M, float(eps), int(feature_map), _dtype_code(q), _stream(q.device)))
     return out
 
 
 class CausalProduct(torch.autograd.Function):
     """Autograd wrapper: the forward keeps the final state so that the
-    backward runs its query gradient in the same reverse sweep as the others."""
+    backward runs its query gradient in the same reverse sweep as the others.
+    An initial state (fp32 [N,H,E,M]) may be given and receives a gradient."""
 
     @staticmethod
-    def forward(ctx, q, k, v):
+    def forward(ctx, q, k, v, state0):
         q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
+        s0 = state0.contiguous() if state0 is not None else None
         N, H, L, E, M = _dims(q, v)
         state = torch.empty((N, H, E, M), device=q.device, dtype=torch.float32)
-        out = causal_product_fwd(q, k, v, state_out=state)
+        out = causal_product_fwd(q, k, v, state_in=s0, state_out=state)
         ctx.save_for_backward(q, k, v, state)
+        ctx.has_state0 = s0 is not None
         return out
 
     @staticmethod
     def backward(ctx, dout):
         q, k, v, state = ctx.saved_tensors
-        return causal_product_bwd(q, k, v, dout.contiguous(), state_in=state)
+        ds0 = torch.empty_like(state) if ctx.has_state0 and ctx.needs_input_grad[3] else None
+        dq, dk, dv = causal_product_bwd(q, k, v, dout.contiguous(), state_final=state, dstate_in=ds0)
+        return dq, dk, dv, ds0
 
 
-def causal_product(q, k, v):
-    """Differentiable causal dot product (q, k already feature-mapped)."""
-    return CausalProduct.apply(q, k, v)
+def causal_product(q, k, v, state0=None):
+    """Differentiable causal dot product (q, k already feature-mapped),
+    optionally from an initial state state0 (fp32 [N,H,E,M])."""
+    return CausalProduct.apply(q, k, v, state0)
 
 
 class LinearAttention(torch.autograd.Function):

@@ -17,7 +17,7 @@
 
 namespace {
 
-constexpr int kAbiMajor = 1, kAbiMinor = 1;  // 1.1: kernel timing
+constexpr int kAbiMajor = 2, kAbiMinor = 0;  // 2.0: carried state
 
 struct Range {
     uintptr_t lo, hi;  // [lo, hi)
@@ -55,7 +55,15 @@ int check_ptrs(std::initializer_list<const void *> ptrs) {
     return CP_OK;
 }
 
-// Every output must be disjoint from every input and from the other outputs.
+// Optional pointers (may be NULL): when given, 16-byte aligned.
+int check_opt_ptrs(std::initializer_list<const void *> ptrs) {
+    for (const void *p : ptrs)
+        if (p && !aligned16(p)) return CP_ERR_ALIGN;
+    return CP_OK;
+}
+
+// Every output must be disjoint from every input and from the other outputs
+// (a NULL optional pointer has an empty range and overlaps nothing).
 int check_alias(std::initializer_list<Range> ins, std::initializer_list<Range> outs) {
     for (auto o = outs.begin(); o != outs.end(); ++o) {
         for (const Range &i : ins)
@@ -68,7 +76,7 @@ int check_alias(std::initializer_list<Range> ins, std::initializer_list<Range> o
 
 Range span(const void *p, int64_t bytes) {
     const uintptr_t a = reinterpret_cast<uintptr_t>(p);
-    return Range{a, a + static_cast<uintptr_t>(bytes)};
+    return p ? Range{a, a + static_cast<uintptr_t>(bytes)} : Range{0, 0};
 }
 
 int launch_status(hipError_t e) { return e == hipSuccess ? CP_OK : CP_ERR_HIP; }
@@ -157,57 +165,51 @@ const char *cp_status_string(int status) {
     }
 }
 
-int causal_product_fwd(const void *Q, const void *K, const void *V, void *Out, float *state_out, int64_t N,
-                       int64_t H, int64_t L, int64_t E, int64_t M, int dtype, void *stream) {
+int causal_product_fwd(const void *Q, const void *K, const void *V, void *Out, const float *state_in,
+                       float *state_out, int64_t N, int64_t H, int64_t L, int64_t E, int64_t M, int dtype,
+                       void *stream) {
     int64_t ne = 0, nm = 0;
     int st = check_dims(N, H, L, E, M, dtype, 128 / 16 * 3, ne, nm);
     if (st != CP_OK) return st;
     st = check_ptrs({Q, K, V, Out});
     if (st != CP_OK) return st;
-    if (state_out && !aligned16(state_out)) return CP_ERR_ALIGN;
-    const int64_t es = dtype == CP_BF16 ? 2 : 4;
-    const Range rq = span(Q, ne * es), rk = span(K, ne * es), rv = span(V, nm * es), ro = span(Out, nm * es);
-    if (state_out) {
-        const Range rs = span(state_out, N * H * E * M * 4);
-        st = check_alias({rq, rk, rv}, {ro, rs});
-    } else {
-        st = check_alias({rq, rk, rv}, {ro});
-    }
+    st = check_opt_ptrs({state_in, state_out});
+    if (st != CP_OK) return st;
+    const int64_t es = dtype == CP_BF16 ? 2 : 4, ns = N * H * E * M * 4;
+    st = check_alias({span(Q, ne * es), span(K, ne * es), span(V, nm * es), span(state_in, ns)},
+                     {span(Out, nm * es), span(state_out, ns)});
     if (st != CP_OK) return st;
 
     cp::fwd_fn fn = dtype == CP_BF16 ? cp::fwd_bf16((int)E, (int)M, false) : cp::fwd_f32((int)E, (int)M, false);
     if (!fn) return CP_ERR_UNSUPPORTED;
-    cp::FwdArgs a{Q, K, V, Out, state_out, (int)L, (int)(N * H), 0.f, 0};
+    cp::FwdArgs a{Q, K, V, Out, state_in, nullptr, state_out, nullptr, (int)L, (int)(N * H), 0.f, 0};
     return launch_status(fn(a, static_cast<hipStream_t>(stream)));
 }
 
 int causal_product_bwd(const void *Q, const void *K, const void *V, const void *dOut, const float *state_in,
-                       void *dQ, void *dK, void *dV, int64_t N, int64_t H, int64_t L, int64_t E, int64_t M,
-                       int dtype, void *stream) {
+                       const float *state_final, void *dQ, void *dK, void *dV, float *dstate_in, int64_t N,
+                       int64_t H, int64_t L, int64_t E, int64_t M, int dtype, void *stream) {
     int64_t ne = 0, nm = 0;
     int st = check_dims(N, H, L, E, M, dtype, 128 / 16 * 3, ne, nm);
     if (st != CP_OK) return st;
     st = check_ptrs({Q, K, V, dOut, dQ, dK, dV});
     if (st != CP_OK) return st;
-    if (state_in && !aligned16(state_in)) return CP_ERR_ALIGN;
-    const int64_t es = dtype == CP_BF16 ? 2 : 4;
-    const Range rq = span(Q, ne * es), rk = span(K, ne * es), rv = span(V, nm * es), rg = span(dOut, nm * es);
-    const Range rdq = span(dQ, ne * es), rdk = span(dK, ne * es), rdv = span(dV, nm * es);
-    if (state_in) {
-        const Range rs = span(state_in, N * H * E * M * 4);
-        st = check_alias({rq, rk, rv, rg, rs}, {rdq, rdk, rdv});
-    } else {
-        st = check_alias({rq, rk, rv, rg}, {rdq, rdk, rdv});
-    }
+    st = check_opt_ptrs({state_in, state_final, dstate_in});
+    if (st != CP_OK) return st;
+    const int64_t es = dtype == CP_BF16 ? 2 : 4, ns = N * H * E * M * 4;
+    st = check_alias({span(Q, ne * es), span(K, ne * es), span(V, nm * es), span(dOut, nm * es),
+                      span(state_in, ns), span(state_final, ns)},
+                     {span(dQ, ne * es), span(dK, ne * es), span(dV, nm * es), span(dstate_in, ns)});
     if (st != CP_OK) return st;
 
     cp::bwd_fn fn = dtype == CP_BF16 ? cp::bwd_bf16((int)E, (int)M) : cp::bwd_f32((int)E, (int)M);
     if (!fn) return CP_ERR_UNSUPPORTED;
-    cp::BwdArgs a{Q, K, V, dOut, state_in, dQ, dK, dV, (int)L, (int)(N * H)};
+    cp::BwdArgs a{Q, K, V, dOut, state_in, state_final, dQ, dK, dV, dstate_in, (int)L, (int)(N * H)};
     return launch_status(fn(a, static_cast<hipStream_t>(stream)));
 }
 
-int linear_attn_fwd(const void *Q, const void *K, const void *V, void *Out, int64_t N, int64_t H, int64_t L,
+int linear_attn_fwd(const void *Q, const void *K, const void *V, void *Out, const float *state_in,
+                    const float *z_in, float *state_out, float *z_out, int64_t N, int64_t H, int64_t L,
                     int64_t E, int64_t M, float eps, int feature_map, int dtype, void *stream) {
     int64_t ne = 0, nm = 0;
     int st = check_dims(N, H, L, E, M, dtype, 128 / 16 * 3, ne, nm);
@@ -216,13 +218,16 @@ int linear_attn_fwd(const void *Q, const void *K, const void *V, void *Out, int6
     if (!(eps >= 0.f) || !std::isfinite(eps)) return CP_ERR_UNSUPPORTED;
     st = check_ptrs({Q, K, V, Out});
     if (st != CP_OK) return st;
-    const int64_t es = dtype == CP_BF16 ? 2 : 4;
-    st = check_alias({span(Q, ne * es), span(K, ne * es), span(V, nm * es)}, {span(Out, nm * es)});
+    st = check_opt_ptrs({state_in, z_in, state_out, z_out});
+    if (st != CP_OK) return st;
+    const int64_t es = dtype == CP_BF16 ? 2 : 4, ns = N * H * E * M * 4, nz = N * H * E * 4;
+    st = check_alias({span(Q, ne * es), span(K, ne * es), span(V, nm * es), span(state_in, ns), span(z_in, nz)},
+                     {span(Out, nm * es), span(state_out, ns), span(z_out, nz)});
     if (st != CP_OK) return st;
 
     cp::fwd_fn fn = dtype == CP_BF16 ? cp::fwd_bf16((int)E, (int)M, true) : cp::fwd_f32((int)E, (int)M, true);
     if (!fn) return CP_ERR_UNSUPPORTED;
-    cp::FwdArgs a{Q, K, V, Out, nullptr, (int)L, (int)(N * H), eps, feature_map};
+    cp::FwdArgs a{Q, K, V, Out, state_in, z_in, state_out, z_out, (int)L, (int)(N * H), eps, feature_map};
     return launch_status(fn(a, static_cast<hipStream_t>(stream)));
 }
 

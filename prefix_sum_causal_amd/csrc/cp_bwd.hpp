@@ -30,7 +30,9 @@
 // in flight.  The dQ wave starts from the slice's final state S_{L-1} and
 // subtracts each chunk (S_{c-1} = S_{L-1} - sum_{c' >= c} K_c'^T V_c'); the
 // state comes from the forward pass, or, when it is not given, from a
-// forward pre-pass of the workgroup over K and V.  Carried states keep the
+// forward pre-pass of the workgroup over K and V starting at the initial
+// state S0.  At the end the dV waves hold R_0 = sum_i q_i dO_i^T, the
+// gradient of S0.  Carried states keep the
 // rows of their contraction index (m or e) in the order of the 16-byte
 // natural reads of the other operand (see EOps), so no operand is read twice.
 #pragma once
@@ -44,8 +46,8 @@ enum BwdRole { kDQ = 0, kDK = 1, kDV = 2, kIdle = 3 };
 // The whole sweep of one wave role.  Every role runs the same staging and
 // barriers; only the math differs, so each wave's loop is straight-line code.
 template <typename T, int E, int M, int C, int G, int NPF, int ROLE>
-__device__ __forceinline__ void bwd_sweep(const T *q_, const T *k_, const T *v_, const T *g_, const float *st,
-                                          T *out_, int L, int b, T *lds) {
+__device__ __forceinline__ void bwd_sweep(const T *q_, const T *k_, const T *v_, const T *g_, const float *s0,
+                                          const float *st, T *out_, float *ds0, int L, int b, T *lds) {
     using O = Ops<T>;
     using F = typename O::frag;
     using EE = EOps<T, E>;  // contraction over e
@@ -78,7 +80,15 @@ __device__ __forceinline__ void bwd_sweep(const T *q_, const T *k_, const T *v_,
                 for (int t = 0; t < 4; ++t) W[m][t] = st[(16 * b + r) * M + EM::ecol(m) + EM::estride * g + t];
         }
     } else {
-        // forward pre-pass: S_{L-1}^T[:, b] = sum over chunks of V^T K[:, b]
+        // forward pre-pass: S_{L-1}^T[:, b] = S0^T[:, b] + sum over chunks of V^T K[:, b]
+        if constexpr (ROLE == kDQ) {
+            if (s0) {
+#pragma unroll
+                for (int m = 0; m < MB; ++m)
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) W[m][t] = s0[(16 * b + r) * M + EM::ecol(m) + EM::estride * g + t];
+            }
+        }
         SE sk;
         SM sv;
         sk.load(Rows<T>(k_, E, 0, L, C), 0);
@@ -258,6 +268,16 @@ __device__ __forceinline__ void bwd_sweep(const T *q_, const T *k_, const T *v_,
             }
         }
     }
+    // the gradient of the initial state: R_0 = sum_i q_i dO_i^T, held by the
+    // dV waves (column blocks b of M) at the end of the reverse sweep
+    if constexpr (ROLE == kDV) {
+        if (ds0) {
+#pragma unroll
+            for (int e = 0; e < EB; ++e)
+#pragma unroll
+                for (int t = 0; t < 4; ++t) ds0[(EE::ecol(e) + EE::estride * g + t) * M + 16 * b + r] = X[e][t];
+        }
+    }
 }
 
 // Waves of a workgroup: EG dQ waves, EG dK waves and MG dV waves; group grp
@@ -271,7 +291,8 @@ constexpr int bwd_threads() {
 template <typename T, int E, int M, int C, int G, int NPF>
 __global__ __launch_bounds__((bwd_threads<T, E, M, G>())) void cp_bwd_kernel(
     const T *__restrict__ Q, const T *__restrict__ K, const T *__restrict__ V, const T *__restrict__ Gr,
-    const float *__restrict__ state_in, T *__restrict__ dQ, T *__restrict__ dK, T *__restrict__ dV, int L, int NS) {
+    const float *__restrict__ state_in, const float *__restrict__ state_final, T *__restrict__ dQ,
+    T *__restrict__ dK, T *__restrict__ dV, float *__restrict__ dstate_in, int L, int NS) {
     constexpr int EB = E / 16, MB = M / 16;
     constexpr int EG = (EB + G - 1) / G, NT = bwd_threads<T, E, M, G>();
     static_assert(NT <= 1024, "at most 16 waves per workgroup");
@@ -284,17 +305,19 @@ __global__ __launch_bounds__((bwd_threads<T, E, M, G>())) void cp_bwd_kernel(
     const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
     const int64_t oe = (int64_t)slice * L * E, om = (int64_t)slice * L * M;
     const T *q_ = Q + oe, *k_ = K + oe, *v_ = V + om, *g_ = Gr + om;
-    const float *st = state_in ? state_in + (int64_t)slice * E * M : nullptr;
+    const float *s0 = state_in ? state_in + (int64_t)slice * E * M : nullptr;
+    const float *st = state_final ? state_final + (int64_t)slice * E * M : nullptr;
+    float *ds0 = dstate_in ? dstate_in + (int64_t)slice * E * M : nullptr;
     const int role = w < EG ? kDQ : w < 2 * EG ? kDK : kDV;
     const int b = grp + G * (role == kDQ ? w : role == kDK ? w - EG : w - 2 * EG);
     if (role == kDQ && b < EB)
-        bwd_sweep<T, E, M, C, G, NPF, kDQ>(q_, k_, v_, g_, st, dQ + oe, L, b, lds);
+        bwd_sweep<T, E, M, C, G, NPF, kDQ>(q_, k_, v_, g_, s0, st, dQ + oe, nullptr, L, b, lds);
     else if (role == kDK && b < EB)
-        bwd_sweep<T, E, M, C, G, NPF, kDK>(q_, k_, v_, g_, st, dK + oe, L, b, lds);
+        bwd_sweep<T, E, M, C, G, NPF, kDK>(q_, k_, v_, g_, s0, st, dK + oe, nullptr, L, b, lds);
     else if (role == kDV && b < MB)
-        bwd_sweep<T, E, M, C, G, NPF, kDV>(q_, k_, v_, g_, st, dV + om, L, b, lds);
+        bwd_sweep<T, E, M, C, G, NPF, kDV>(q_, k_, v_, g_, s0, st, dV + om, ds0, L, b, lds);
     else
-        bwd_sweep<T, E, M, C, G, NPF, kIdle>(q_, k_, v_, g_, st, nullptr, L, 0, lds);
+        bwd_sweep<T, E, M, C, G, NPF, kIdle>(q_, k_, v_, g_, s0, st, nullptr, nullptr, L, 0, lds);
 }
 
 }  // namespace cp

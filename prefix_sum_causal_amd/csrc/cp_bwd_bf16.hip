@@ -13,10 +13,11 @@ hipError_t launch_bwd(const BwdArgs &a, hipStream_t s) {
     auto kern = cp_bwd_kernel<T, E, M, P::BC, P::BG, P::BNPF>;
     const T *q = static_cast<const T *>(a.Q), *k = static_cast<const T *>(a.K), *v = static_cast<const T *>(a.V),
             *g = static_cast<const T *>(a.G);
-    const float *st = a.state_in;
+    const float *s0 = a.state_in, *st = a.state_final;
     T *dq = static_cast<T *>(a.dQ), *dk = static_cast<T *>(a.dK), *dv = static_cast<T *>(a.dV);
+    float *ds0 = a.dstate_in;
     int L = a.L, NS = a.NS;
-    void *args[] = {&q, &k, &v, &g, &st, &dq, &dk, &dv, &L, &NS};
+    void *args[] = {&q, &k, &v, &g, &s0, &st, &dq, &dk, &dv, &ds0, &L, &NS};
     return launch_kernel(reinterpret_cast<const void *>(kern), dim3(NS * P::BG), dim3(bwd_threads<T, E, M, P::BG>()), args, s);
 }
 

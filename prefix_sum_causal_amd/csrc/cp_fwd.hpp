@@ -223,14 +223,15 @@ __device__ __forceinline__ void fwd_sweep(const T *q_, const T *k_, const T *v_,
 // cut into nseg segments of seg_len rows (a multiple of C) and run in two
 // launches.  The first (SONLY) computes each segment's state increment
 // dS = sum over its rows of k v^T (and dz = sum of phi(k)) into ws; the
-// second starts segment s from the exclusive sum of the increments of the
-// segments before it (the chunked scan's carry, one level up) and sweeps only
-// its own rows.  ws holds, per slice and segment, E*M floats of dS (row e,
+// second starts segment s from the carried-in state (state_in, z_in) plus the
+// exclusive sum of the increments of the segments before it (the chunked
+// scan's carry, one level up) and sweeps only its own rows.  ws holds, per slice and segment, E*M floats of dS (row e,
 // column m) then E floats of dz.  With one segment, ws is unused (NULL).
 template <typename T, int E, int M, int C, int G, int RSPLIT, int NPF, bool NORM, bool FMAP, bool SONLY>
 __global__ __launch_bounds__(64 * (M / 16 / G) * RSPLIT) void cp_fwd_kernel(
     const T *__restrict__ Q, const T *__restrict__ K, const T *__restrict__ V, T *__restrict__ Out,
-    float *__restrict__ state_out, float *__restrict__ ws, int L, int NS, int seg_len, float eps) {
+    const float *__restrict__ state_in, const float *__restrict__ z_in, float *__restrict__ state_out,
+    float *__restrict__ z_out, float *__restrict__ ws, int L, int NS, int seg_len, float eps) {
     using EO = EOps<T, E>;
     constexpr int EB = E / 16, MB = M / 16, CB = C / 16;
     static_assert(MB % G == 0, "column groups split the column blocks evenly");
@@ -265,6 +266,18 @@ __global__ __launch_bounds__(64 * (M / 16 / G) * RSPLIT) void cp_fwd_kernel(
         S[e] = zero4();
         z[e] = zero4();
     }
+    if (!SONLY && (state_in || z_in)) {  // the carried-in state before row 0
+        const float *s0 = state_in ? state_in + (int64_t)slice * E * M : nullptr;
+        const float *z0 = z_in ? z_in + (int64_t)slice * E : nullptr;
+#pragma unroll
+        for (int e = 0; e < EB; ++e)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int row = EO::ecol(e) + EO::estride * g + t;
+                if (s0) S[e][t] = s0[row * M + 16 * mb + r];
+                if (NORM && z0) z[e][t] = z0[row];
+            }
+    }
     if (!SONLY && ws_slice) {
         for (int p = 0; p < seg; ++p) {
             const float *dS = ws_slice + (int64_t)p * WS, *dz = dS + E * M;
@@ -295,13 +308,18 @@ __global__ __launch_bounds__(64 * (M / 16 / G) * RSPLIT) void cp_fwd_kernel(
                     if (NORM && mb == 0 && r == 0) dz[row] = z[e][t];
                 }
         }
-    } else if constexpr (!NORM) {
-        if (state_out && h == 0 && seg == nseg - 1) {
-            float *st_ = state_out + (int64_t)slice * E * M;
+    } else {
+        if (h == 0 && seg == nseg - 1) {  // the final state of the slice
+            float *st_ = state_out ? state_out + (int64_t)slice * E * M : nullptr;
+            float *zt_ = z_out ? z_out + (int64_t)slice * E : nullptr;
 #pragma unroll
             for (int e = 0; e < EB; ++e)
 #pragma unroll
-                for (int t = 0; t < 4; ++t) st_[(EO::ecol(e) + EO::estride * g + t) * M + 16 * mb + r] = S[e][t];
+                for (int t = 0; t < 4; ++t) {
+                    const int row = EO::ecol(e) + EO::estride * g + t;
+                    if (st_) st_[row * M + 16 * mb + r] = S[e][t];
+                    if (NORM && zt_ && mb == 0 && r == 0) zt_[row] = z[e][t];
+                }
         }
     }
 }

@@ -11,7 +11,8 @@ namespace cp {
 struct FwdArgs {
     const void *Q, *K, *V;
     void *Out;
-    float *state_out;
+    const float *state_in, *z_in;  // optional initial S and z
+    float *state_out, *z_out;      // optional final S and z
     int L, NS;
     float eps;
     int fmap;
@@ -19,8 +20,10 @@ struct FwdArgs {
 
 struct BwdArgs {
     const void *Q, *K, *V, *G;
-    const float *state_in;
+    const float *state_in;     // optional initial state S0
+    const float *state_final;  // optional final state S_{L-1}
     void *dQ, *dK, *dV;
+    float *dstate_in;  // optional gradient of S0
     int L, NS;
 };
 

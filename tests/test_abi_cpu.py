@@ -22,9 +22,9 @@ def lib():
         pytest.skip("libcausalprod.so not built")
     lib = ctypes.CDLL(LIB)
     vp, i64, i = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
-    lib.causal_product_fwd.argtypes = [vp] * 5 + [i64] * 5 + [i, vp]
-    lib.causal_product_bwd.argtypes = [vp] * 8 + [i64] * 5 + [i, vp]
-    lib.linear_attn_fwd.argtypes = [vp] * 4 + [i64] * 5 + [ctypes.c_float, i, i, vp]
+    lib.causal_product_fwd.argtypes = [vp] * 6 + [i64] * 5 + [i, vp]
+    lib.causal_product_bwd.argtypes = [vp] * 10 + [i64] * 5 + [i, vp]
+    lib.linear_attn_fwd.argtypes = [vp] * 8 + [i64] * 5 + [ctypes.c_float, i, i, vp]
     lib.cp_status_string.restype = ctypes.c_char_p
     return lib
 
@@ -53,7 +53,7 @@ def test_status_strings_and_version(lib):
         assert msg and msg not in seen
         seen.add(msg)
     assert lib.cp_status_string(99).decode() == "unknown status"
-    assert lib.cp_abi_version() == (1 << 16) | 1
+    assert lib.cp_abi_version() == (2 << 16)
 
 
 def test_timing_rejects_bad_arguments_before_any_device_call(lib):
@@ -70,20 +70,22 @@ def test_timing_rejects_bad_arguments_before_any_device_call(lib):
 
 
 # fake, 16-byte aligned, disjoint addresses (never dereferenced)
-A = [0x10_0000_0000 + n * 0x1_0000_0000 for n in range(8)]
+A = [0x10_0000_0000 + n * 0x1_0000_0000 for n in range(12)]
 SHAPE = (2, 3, 100, 64, 32)
 
 
-def fwd(lib, q=A[0], k=A[1], v=A[2], o=A[3], st=None, shape=SHAPE, dtype=1):
-    return lib.causal_product_fwd(q, k, v, o, st, *shape, dtype, None)
+def fwd(lib, q=A[0], k=A[1], v=A[2], o=A[3], s0=None, st=None, shape=SHAPE, dtype=1):
+    return lib.causal_product_fwd(q, k, v, o, s0, st, *shape, dtype, None)
 
 
-def bwd(lib, q=A[0], k=A[1], v=A[2], g=A[3], st=None, dq=A[4], dk=A[5], dv=A[6], shape=SHAPE, dtype=1):
-    return lib.causal_product_bwd(q, k, v, g, st, dq, dk, dv, *shape, dtype, None)
+def bwd(lib, q=A[0], k=A[1], v=A[2], g=A[3], s0=None, st=None, dq=A[4], dk=A[5], dv=A[6], ds0=None,
+        shape=SHAPE, dtype=1):
+    return lib.causal_product_bwd(q, k, v, g, s0, st, dq, dk, dv, ds0, *shape, dtype, None)
 
 
-def lin(lib, q=A[0], k=A[1], v=A[2], o=A[3], shape=SHAPE, eps=1e-6, fm=1, dtype=1):
-    return lib.linear_attn_fwd(q, k, v, o, *shape, eps, fm, dtype, None)
+def lin(lib, q=A[0], k=A[1], v=A[2], o=A[3], s0=None, z0=None, st=None, zt=None, shape=SHAPE, eps=1e-6, fm=1,
+        dtype=1):
+    return lib.linear_attn_fwd(q, k, v, o, s0, z0, st, zt, *shape, eps, fm, dtype, None)
 
 
 @pytest.mark.parametrize("which", range(4))
@@ -128,9 +130,14 @@ def test_unsupported_dtype_flag_eps(lib):
 def test_misaligned(lib):
     assert fwd(lib, v=A[2] + 8) == ALIGN
     assert fwd(lib, st=A[4] + 4) == ALIGN
+    assert fwd(lib, s0=A[5] + 4) == ALIGN
     assert bwd(lib, dk=A[5] + 2) == ALIGN
     assert bwd(lib, st=A[7] + 8) == ALIGN
+    assert bwd(lib, s0=A[8] + 8) == ALIGN
+    assert bwd(lib, ds0=A[9] + 4) == ALIGN
     assert lin(lib, o=A[3] + 8) == ALIGN
+    assert lin(lib, z0=A[6] + 4) == ALIGN
+    assert lin(lib, zt=A[7] + 8) == ALIGN
 
 
 def test_aliasing(lib):
@@ -141,5 +148,11 @@ def test_aliasing(lib):
     assert fwd(lib, st=A[2] + 16) == ALIAS       # state_out overlaps v
     assert bwd(lib, dq=A[5]) == ALIAS            # dq == dk
     assert bwd(lib, dv=A[3]) == ALIAS            # dv == dout
-    assert bwd(lib, st=A[4]) == ALIAS            # state_in overlaps dq
+    assert bwd(lib, st=A[4]) == ALIAS            # state_final overlaps dq
+    assert bwd(lib, s0=A[7], ds0=A[7] + 16) == ALIAS  # dstate_in overlaps state_in
+    assert bwd(lib, ds0=A[6]) == ALIAS           # dstate_in overlaps dv
+    assert fwd(lib, s0=A[5], st=A[5]) == ALIAS   # no in-place state update
+    assert fwd(lib, s0=A[3]) == ALIAS            # state_in overlaps out
     assert lin(lib, o=A[2]) == ALIAS
+    assert lin(lib, z0=A[5], zt=A[5]) == ALIAS
+    assert lin(lib, st=A[5], zt=A[5] + 64) == ALIAS  # z_out inside state_out

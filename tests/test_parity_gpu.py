@@ -169,7 +169,7 @@ def _bwd_check(cp, orc, d, dtype, use_state, tol=None):
         N, H, L, E = q.shape
         st = torch.empty((N, H, E, v.shape[-1]), device="cuda", dtype=torch.float32)
         cp.causal_product_fwd(q, k, v, state_out=st)
-    dq, dk, dv = cp.causal_product_bwd(q, k, v, g, state_in=st)
+    dq, dk, dv = cp.causal_product_bwd(q, k, v, g, state_final=st)
     torch.cuda.synchronize()
     ref = orc.bwd(d["Q"], d["K"], d["V"], d["dO"])
     errs = [oracle.max_rel_err(host(a), b) for a, b in zip((dq, dk, dv), ref)]
@@ -207,7 +207,7 @@ def test_bwd_integer_bitwise(cp, orc, dtype):
     cp.causal_product_fwd(q, k, v, state_out=st)
     ref = orc.bwd(d["Q"], d["K"], d["V"], d["dO"])
     for state in (st, None):
-        got = cp.causal_product_bwd(q, k, v, g, state_in=state)
+        got = cp.causal_product_bwd(q, k, v, g, state_final=state)
         for a, b in zip(got, ref):
             if dtype == "bf16":
                 b = W.round_bf16(b.astype(np.float32)).astype(np.float64)
@@ -297,7 +297,7 @@ def test_workload_full_size(cp, orc, name):
         assert oracle.max_rel_err(host(out), orc.fwd_brute(d["Q"], d["K"], d["V"])) <= tol
     if w.op == "fwd+bwd":
         g = dev(d["dO"], w.dtype)
-        dq, dk, dv = cp.causal_product_bwd(q, k, v, g, state_in=st)
+        dq, dk, dv = cp.causal_product_bwd(q, k, v, g, state_final=st)
         torch.cuda.synchronize()
         ref = orc.bwd(d["Q"], d["K"], d["V"], d["dO"])
         errs = [oracle.max_rel_err(host(a), b) for a, b in zip((dq, dk, dv), ref)]
