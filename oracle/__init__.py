@@ -72,6 +72,8 @@ class Oracle:
         for name in ("oracle_fwd", "oracle_fwd_brute", "oracle_linattn", "oracle_linattn_brute", "oracle_bwd",
                      "oracle_bwd_brute"):
             getattr(L, name).restype = None
+        L.oracle_linattn_bwd.argtypes = [_f32p] * 6 + [_f64p] * 5 + dims + [ctypes.c_double, ctypes.c_int]
+        L.oracle_linattn_bwd.restype = None
         L.oracle_state.argtypes = [_f32p, _f32p, _f64p] + dims
         L.oracle_state.restype = None
         L.oracle_num_threads.argtypes = []
@@ -173,6 +175,26 @@ class Oracle:
     def bwd_brute(self, Q, K, V, dO, S0=None, with_dS0: bool = False):
         """(dQ, dK, dV[, dS0]) from the O(L^2) double sum."""
         return self._bwd_common(self.lib.oracle_bwd_brute, Q, K, V, dO, S0, with_dS0)
+
+    def linattn_bwd(self, Q, K, V, dO, eps: float = 1e-6, feature_map: int = 1, S0=None, z0=None):
+        """Gradients (dQ, dK, dV, dS0, dz0) of sum(out * dO) for the
+        normalised form out = linattn(Q, K, V, eps, feature_map, S0, z0), with
+        respect to the raw Q and K (through phi), V and the initial states."""
+        Q, K, V, dO = _as_f32(Q), _as_f32(K), _as_f32(V), _as_f32(dO)
+        if K.shape != Q.shape or dO.shape != V.shape:
+            raise ValueError("K must have Q's shape and dO V's shape")
+        NH, L, E, M = self._dims(Q, V)
+        s0, p0 = self._opt32(S0, Q.shape[:-2] + (E, M))
+        zz, pz = self._opt32(z0, Q.shape[:-2] + (E,))
+        dQ = np.empty(Q.shape, dtype=np.float64)
+        dK = np.empty(Q.shape, dtype=np.float64)
+        dV = np.empty(V.shape, dtype=np.float64)
+        dS0 = np.empty(Q.shape[:-2] + (E, M), dtype=np.float64)
+        dz0 = np.empty(Q.shape[:-2] + (E,), dtype=np.float64)
+        self.lib.oracle_linattn_bwd(_ptr32(Q), _ptr32(K), _ptr32(V), _ptr32(dO), p0, pz, _ptr64(dQ), _ptr64(dK),
+                                    _ptr64(dV), _ptr64(dS0), _ptr64(dz0), NH, L, E, M, float(eps),
+                                    int(feature_map))
+        return dQ, dK, dV, dS0, dz0
 
     def state(self, K, V) -> np.ndarray:
         """Final state sum_j k_j v_j^T per slice, shape [..., E, M]."""

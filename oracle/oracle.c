@@ -285,6 +285,95 @@ void oracle_bwd_brute(const float *Q, const float *K, const float *V, const floa
     }
 }
 
+/* ---------------------------------------------------------------------------
+ * Backward of the normalised form out_i = n_i / d_i (from S0, z0) for an
+ * upstream gradient dO, with c_i = phi(q_i), f_j = phi(k_j):
+ *   n_i = c_i^T S_i,  S_i = S0 + sum_{j<=i} f_j v_j^T,
+ *   d_i = c_i . z_i + eps,  z_i = z0 + sum_{j<=i} f_j.
+ * The quotient rule gives the gradients of n_i and d_i,
+ *   dn_i = dO_i / d_i,   dd_i = -(dO_i . n_i) / d_i^2,
+ * and through the two prefix sums
+ *   dc_i = S_i dn_i + dd_i z_i,
+ *   df_j = R_j v_j + r_j,   R_j = sum_{i>=j} c_i dn_i^T,  r_j = sum_{i>=j} dd_i c_i,
+ *   dv_j = R_j^T f_j,
+ *   dS0 = R_0,  dz0 = r_0,
+ * then through phi: dq = dc * phi'(q), dk = df * phi'(k), with phi' = 1 for
+ * x > 0 and exp(x) otherwise (feature_map = 1), or 1 (feature_map = 0).
+ * First a forward sweep (S_i, z_i, n_i, d_i, dc_i), then a reverse sweep.
+ * Outputs dS0 [NH][E][M] and dz0 [NH][E] are written when not NULL.
+ * ------------------------------------------------------------------------- */
+static double dphi(double x) { return x > 0.0 ? 1.0 : exp(x); }
+
+void oracle_linattn_bwd(const float *Q, const float *K, const float *V, const float *dO, const float *S0,
+                        const float *z0, double *dQ, double *dK, double *dV, double *dS0, double *dz0,
+                        int64_t NH, int64_t L, int64_t E, int64_t M, double eps, int feature_map) {
+#pragma omp parallel for schedule(static)
+    for (int64_t s = 0; s < NH; ++s) {
+        const float *q = Q + s * L * E, *k = K + s * L * E, *v = V + s * L * M;
+        const float *go = dO + s * L * M;
+        double *dq = dQ + s * L * E, *dk = dK + s * L * E, *dv = dV + s * L * M;
+        double *S = (double *)calloc((size_t)(E * M), sizeof(double));
+        double *z = (double *)calloc((size_t)E, sizeof(double));
+        double *c = (double *)malloc((size_t)(L * E) * sizeof(double));
+        double *f = (double *)malloc((size_t)(L * E) * sizeof(double));
+        double *dn = (double *)malloc((size_t)(L * M) * sizeof(double));
+        double *dd = (double *)malloc((size_t)L * sizeof(double));
+        if (S0)
+            for (int64_t x = 0; x < E * M; ++x) S[x] = (double)S0[s * E * M + x];
+        if (z0)
+            for (int64_t e = 0; e < E; ++e) z[e] = (double)z0[s * E + e];
+        for (int64_t x = 0; x < L * E; ++x) {
+            c[x] = feature_map ? phi((double)q[x]) : (double)q[x];
+            f[x] = feature_map ? phi((double)k[x]) : (double)k[x];
+        }
+        /* forward sweep */
+        for (int64_t i = 0; i < L; ++i) {
+            for (int64_t e = 0; e < E; ++e) {
+                z[e] += f[i * E + e];
+                for (int64_t m = 0; m < M; ++m) S[e * M + m] += f[i * E + e] * (double)v[i * M + m];
+            }
+            double den = eps;
+            for (int64_t e = 0; e < E; ++e) den += c[i * E + e] * z[e];
+            double gn = 0.0;  /* dO_i . n_i */
+            for (int64_t m = 0; m < M; ++m) {
+                double num = 0.0;
+                for (int64_t e = 0; e < E; ++e) num += c[i * E + e] * S[e * M + m];
+                gn += (double)go[i * M + m] * num;
+                dn[i * M + m] = (double)go[i * M + m] / den;
+            }
+            dd[i] = -gn / (den * den);
+            for (int64_t e = 0; e < E; ++e) {
+                double acc = dd[i] * z[e];
+                for (int64_t m = 0; m < M; ++m) acc += S[e * M + m] * dn[i * M + m];
+                dq[i * E + e] = acc * (feature_map ? dphi((double)q[i * E + e]) : 1.0);
+            }
+        }
+        /* reverse sweep */
+        double *R = S, *r = z;
+        memset(R, 0, (size_t)(E * M) * sizeof(double));
+        memset(r, 0, (size_t)E * sizeof(double));
+        for (int64_t i = L - 1; i >= 0; --i) {
+            for (int64_t e = 0; e < E; ++e) {
+                r[e] += dd[i] * c[i * E + e];
+                for (int64_t m = 0; m < M; ++m) R[e * M + m] += c[i * E + e] * dn[i * M + m];
+            }
+            for (int64_t e = 0; e < E; ++e) {
+                double acc = r[e];
+                for (int64_t m = 0; m < M; ++m) acc += R[e * M + m] * (double)v[i * M + m];
+                dk[i * E + e] = acc * (feature_map ? dphi((double)k[i * E + e]) : 1.0);
+            }
+            for (int64_t m = 0; m < M; ++m) {
+                double acc = 0.0;
+                for (int64_t e = 0; e < E; ++e) acc += R[e * M + m] * f[i * E + e];
+                dv[i * M + m] = acc;
+            }
+        }
+        if (dS0) memcpy(dS0 + s * E * M, R, (size_t)(E * M) * sizeof(double));
+        if (dz0) memcpy(dz0 + s * E, r, (size_t)E * sizeof(double));
+        free(S); free(z); free(c); free(f); free(dn); free(dd);
+    }
+}
+
 /* Final running state S_{L-1} = sum_j k_j v_j^T of every slice, [NH][E][M]. */
 void oracle_state(const float *K, const float *V, double *S_out,
                   int64_t NH, int64_t L, int64_t E, int64_t M) {

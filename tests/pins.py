@@ -58,7 +58,8 @@ def torch_fwd(Q, K, V):
 
 
 def torch_phi(x):
-    return torch.nn.functional.elu(_t(x), alpha=1.0) + 1.0
+    x = x if isinstance(x, torch.Tensor) else _t(x)
+    return torch.nn.functional.elu(x, alpha=1.0) + 1.0
 
 
 def torch_linattn(Q, K, V, eps, feature_map):
@@ -395,6 +396,48 @@ def pin_carry_bwd_autograd(o):
     for got in (o.bwd(Q, K, V, dO, S0=S0, with_dS0=True), o.bwd_brute(Q, K, V, dO, S0=S0, with_dS0=True)):
         for a, b, name in zip(got, want, ("dQ", "dK", "dV", "dS0")):
             _close(a, b, what=f"{name} with S0")
+
+
+# -- backward of the normalised form ------------------------------------------------
+
+def pin_linattn_bwd_autograd(o):
+    """Gradients of sum(out * dO) for the normalised form, through phi and
+    from (S0, z0), by torch autograd in float64 on the brute-force formula;
+    raw Q, K with both signs so that both branches of phi are used."""
+    for fm, seed in ((1, 45), (0, 46)):
+        r = _rng(seed)
+        N, H, L, E, M = 2, 1, 13, 3, 4
+        Q, K = _rand(r, N, H, L, E, positive=not fm), _rand(r, N, H, L, E, positive=not fm)
+        V, dO = _rand(r, N, H, L, M), _rand(r, N, H, L, M)
+        S0, z0 = _rand(r, N, H, E, M), _rand(r, N, H, E, positive=True)
+        ts = [_t(x).requires_grad_(True) for x in (Q, K, V, S0, z0)]
+        q, k, v, s0, z0t = ts
+        c = torch_phi(q) if fm else q
+        f = torch_phi(k) if fm else k
+        a = torch.tril(c @ f.transpose(-1, -2))
+        num = c @ s0 + a @ v
+        den = (c * z0t[..., None, :]).sum(-1) + a.sum(-1) + 1e-6
+        ((num / den[..., None]) * _t(dO)).sum().backward()
+        got = o.linattn_bwd(Q, K, V, dO, 1e-6, fm, S0=S0, z0=z0)
+        for g_, t, name in zip(got, ts, ("dQ", "dK", "dV", "dS0", "dz0")):
+            _close(g_, t.grad.numpy(), what=f"normalised backward {name} (fm {fm})")
+
+
+def pin_linattn_bwd_reduces_to_causal_product(o):
+    """The denominator does not depend on V, so the value gradient of the
+    normalised form equals the causal product's value gradient for the
+    upstream gradient dO_i / d_i (identity feature map, eps = 0, z0 = 0:
+    d_i is the causal row sum of q_i . k_j)."""
+    r = _rng(47)
+    N, H, L, E, M = 1, 2, 9, 4, 3
+    Q, K = _rand(r, N, H, L, E, positive=True), _rand(r, N, H, L, E, positive=True)
+    V, dO = _rand(r, N, H, L, M), _rand(r, N, H, L, M)
+    den = (torch.tril(_t(Q) @ _t(K).transpose(-1, -2))).sum(-1).numpy()
+    scaled = (dO / den[..., None]).astype(np.float32)
+    _, _, dV = o.bwd(Q, K, V, scaled)
+    got = o.linattn_bwd(Q, K, V, dO, 0.0, 0)[2]
+    # dO / d is rounded to float32 on the way into the causal-product oracle
+    _close(got, dV, tol=1e-6, what="dV of the normalised form vs causal product of dO / d")
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

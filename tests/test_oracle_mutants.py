@@ -51,6 +51,14 @@ MUTANTS = [
      "initial state transposed in dq"),
     ("oracle_bwd_brute", "g0[e * M + m] += (double)q[i * E + e]", "g0[e * M + m] += (double)k[i * E + e]",
      "gradient of the initial state from k"),
+    ("oracle_linattn_bwd", "dd[i] = -gn / (den * den);", "dd[i] = gn / (den * den);", "sign of the denominator term"),
+    ("oracle_linattn_bwd", "double acc = dd[i] * z[e];", "double acc = 0.0;", "denominator term of dq dropped"),
+    ("oracle_linattn_bwd", "r[e] += dd[i] * c[i * E + e];", "r[e] += dd[i] * f[i * E + e];", "dk's denominator sum from k"),
+    ("oracle_linattn_bwd", "dq[i * E + e] = acc * (feature_map ? dphi((double)q[i * E + e]) : 1.0);",
+     "dq[i * E + e] = acc;", "chain rule through phi dropped for q"),
+    ("dphi", "exp(x)", "1.0", "phi' = 1 on the negative branch"),
+    ("oracle_linattn_bwd", "acc += R[e * M + m] * f[i * E + e];", "acc += R[e * M + m] * (double)k[i * E + e];",
+     "dv from the raw k"),
 ]
 
 
