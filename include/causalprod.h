@@ -33,7 +33,8 @@
  *    fill the GPU splits each sequence into segments and takes a scratch
  *    buffer of N*H*segments*(E*M + E) floats from the stream-ordered
  *    allocator (hipMallocAsync), freed on the same stream after its last
- *    use; no other call allocates device memory.
+ *    use; linear_attn_bwd does the same for its per-row terms; no other call
+ *    allocates device memory.
  *  * stream is a hipStream_t (NULL = the default stream).  Calls only enqueue
  *    work: they never synchronise the host, and buffers must stay alive until
  *    the stream has run the work.  Calls are stateless, thread-safe and
@@ -119,11 +120,48 @@ int causal_product_bwd(const void *Q, const void *K, const void *V, const void *
  * the first row (S_{-1}, z_{-1}); state_out, z_out (optional, may be NULL):
  * receive S_{L-1} and z_{L-1}.  Sums include phi: S_i = S_{-1} +
  * sum_{j<=i} phi(k_j) v_j^T, z_i = z_{-1} + sum_{j<=i} phi(k_j).
+ * den_out (optional, may be NULL): fp32 [N][H][L], receives the denominators
+ * d_i = phi(q_i) . z_i + eps, which linear_attn_bwd takes.
  */
 int linear_attn_fwd(const void *Q, const void *K, const void *V, void *Out,
                     const float *state_in, const float *z_in, float *state_out, float *z_out,
+                    float *den_out,
                     int64_t N, int64_t H, int64_t L, int64_t E, int64_t M,
                     float eps, int feature_map, int dtype, void *stream);
+
+/*
+ * linear_attn_bwd: gradients of f = sum_i Out_i . dOut_i for the normalised
+ * form out_i = n_i / d_i of linear_attn_fwd, n_i = phi(q_i)^T S_i and
+ * d_i = phi(q_i) . z_i + eps, with respect to the raw Q and K (through phi),
+ * V and the initial states.  With c = phi(q), f = phi(k), dn_i = dOut_i / d_i
+ * and dd_i = -(dOut_i . out_i) / d_i:
+ *     dc_i = S_i dn_i + dd_i z_i
+ *     df_j = R_j v_j + r_j,   R_j = sum_{i>=j} c_i dn_i^T,  r_j = sum_{i>=j} dd_i c_i
+ *     dv_j = R_j^T f_j
+ *     dQ = dc * phi'(Q), dK = df * phi'(K)   (phi' = 1 when feature_map = 0)
+ *     dstate_in = R_0, dz_in = r_0
+ * Out and den (fp32 [N][H][L]) are the forward's output and den_out, both
+ * required.  state_in, z_in: the initial states the forward started from
+ * (optional, NULL = zero); pass them whenever the forward had them, also
+ * together with state_final.  state_final (optional): the forward's final
+ * S, which spares a forward pre-pass; with bf16 I/O it then stands in for
+ * state_in.  With fp32 I/O it is not read: the query gradient, which peaks
+ * at the first rows, recovers the early states by a compensated backward sum
+ * from a compensated pre-pass of its own (the forward's plain fp32 sum would
+ * leave its rounding error in them).  The normaliser before every chunk is summed forward from z_in by
+ * a small scan (recovering it from the final z by subtraction would lose
+ * most of the bits of its early values).  dstate_in, dz_in (optional):
+ * receive the gradients of the initial states.  The call takes a scratch
+ * buffer of N*H*L*M elements (dn) and about 2*N*H*L floats (dd and the
+ * chunk-wise z) from the stream-ordered allocator and frees it on the
+ * stream.
+ */
+int linear_attn_bwd(const void *Q, const void *K, const void *V, const void *Out, const void *dOut,
+                    const float *den, const float *state_in, const float *z_in,
+                    const float *state_final,
+                    void *dQ, void *dK, void *dV, float *dstate_in, float *dz_in,
+                    int64_t N, int64_t H, int64_t L, int64_t E, int64_t M,
+                    int feature_map, int dtype, void *stream);
 
 /* Static, NUL-terminated description of a cp_status value (never NULL). */
 const char *cp_status_string(int status);

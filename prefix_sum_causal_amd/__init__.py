@@ -43,7 +43,9 @@ lib.causal_product_fwd.argtypes = [_vp] * 6 + [_i64] * 5 + [_int, _vp]
 lib.causal_product_fwd.restype = _int
 lib.causal_product_bwd.argtypes = [_vp] * 10 + [_i64] * 5 + [_int, _vp]
 lib.causal_product_bwd.restype = _int
-lib.linear_attn_fwd.argtypes = [_vp] * 8 + [_i64] * 5 + [ctypes.c_float, _int, _int, _vp]
+lib.linear_attn_fwd.argtypes = [_vp] * 9 + [_i64] * 5 + [ctypes.c_float, _int, _int, _vp]
+lib.linear_attn_bwd.argtypes = [_vp] * 14 + [_i64] * 5 + [_int, _int, _vp]
+lib.linear_attn_bwd.restype = _int
 lib.linear_attn_fwd.restype = _int
 lib.cp_status_string.argtypes = [_int]
 lib.cp_status_string.restype = ctypes.c_char_p
@@ -169,11 +171,12 @@ def causal_product_bwd(q, k, v, dout, state_final=None, state_in=None, dq=None, 
 
 
 def linear_attn_fwd(q, k, v, eps: float = 1e-6, feature_map: int = 1, out=None, state_in=None, z_in=None,
-                    state_out=None, z_out=None):
+                    state_out=None, z_out=None, den_out=None):
     """out_i = phi(q_i)^T S_i / (phi(q_i) . z_i + eps) with phi = elu + 1
     (feature_map=1) or the identity (feature_map=0) applied to the raw q, k.
     Optional fp32 states: state_in [N,H,E,M] and z_in [N,H,E] before the
-    first row (None = zero); state_out, z_out receive the final S and z."""
+    first row (None = zero); state_out, z_out receive the final S and z;
+    den_out [N,H,L] receives the denominators (for linear_attn_bwd)."""
     N, H, L, E, M = _dims(q, v)
     if k.shape != q.shape:
         raise ValueError("k must have q's shape")
@@ -181,12 +184,41 @@ def linear_attn_fwd(q, k, v, eps: float = 1e-6, feature_map: int = 1, out=None, 
         out = torch.empty_like(v)
     _check_tensors(q, k, v, out)
     for name, t, shape in (("state_in", state_in, (N, H, E, M)), ("z_in", z_in, (N, H, E)),
-                           ("state_out", state_out, (N, H, E, M)), ("z_out", z_out, (N, H, E))):
+                           ("state_out", state_out, (N, H, E, M)), ("z_out", z_out, (N, H, E)),
+                           ("den_out", den_out, (N, H, L))):
         _check_state(name, t, shape, q.device)
     _check("linear_attn_fwd", lib.linear_attn_fwd(
         _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(state_in), _ptr(z_in), _ptr(state_out), _ptr(z_out),
-        N, H, L, E, M, float(eps), int(feature_map), _dtype_code(q), _stream(q.device)))
+        _ptr(den_out), N, H, L, E, M, float(eps), int(feature_map), _dtype_code(q), _stream(q.device)))
     return out
+
+
+def linear_attn_bwd(q, k, v, out, dout, den, feature_map: int = 1, state_in=None, z_in=None, state_final=None,
+                    dq=None, dk=None, dv=None, dstate_in=None, dz_in=None):
+    """Gradients (dq, dk, dv) of sum(out * dout) for out = linear_attn_fwd(q, k, v, ...),
+    with respect to the raw q, k (through phi), v; ``den`` is the forward's
+    den_out.  state_in / z_in: the initial states the forward started from
+    (pass them whenever it had them); state_final: the forward's final state,
+    an optional shortcut (read for bf16 only); dstate_in [N,H,E,M] and dz_in
+    [N,H,E] receive the gradients of the initial states."""
+    N, H, L, E, M = _dims(q, v)
+    if k.shape != q.shape or dout.shape != v.shape or out.shape != v.shape:
+        raise ValueError("k must have q's shape, out and dout v's shape")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    _check_tensors(q, k, v, out, dout, dq, dk, dv)
+    for name, t, shape in (("den", den, (N, H, L)), ("state_in", state_in, (N, H, E, M)), ("z_in", z_in, (N, H, E)),
+                           ("state_final", state_final, (N, H, E, M)), ("dstate_in", dstate_in, (N, H, E, M)),
+                           ("dz_in", dz_in, (N, H, E))):
+        _check_state(name, t, shape, q.device)
+    if den is None:
+        raise ValueError("den (the forward's den_out) is required")
+    _check("linear_attn_bwd", lib.linear_attn_bwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(den), _ptr(state_in), _ptr(z_in), _ptr(state_final),
+        _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dstate_in), _ptr(dz_in), N, H, L, E, M, int(feature_map),
+        _dtype_code(q), _stream(q.device)))
+    return dq, dk, dv
 
 
 class CausalProduct(torch.autograd.Function):
@@ -220,13 +252,25 @@ def causal_product(q, k, v, state0=None):
 
 
 class LinearAttention(torch.autograd.Function):
+    """Autograd wrapper of the normalised form: the forward keeps its output,
+    denominators and final state for the backward's single reverse sweep."""
+
     @staticmethod
     def forward(ctx, q, k, v, eps, feature_map):
-        return linear_attn_fwd(q.contiguous(), k.contiguous(), v.contiguous(), eps, feature_map)
+        q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
+        N, H, L, E, M = _dims(q, v)
+        st = torch.empty((N, H, E, M), device=q.device, dtype=torch.float32)
+        den = torch.empty((N, H, L), device=q.device, dtype=torch.float32)
+        out = linear_attn_fwd(q, k, v, eps, feature_map, state_out=st, den_out=den)
+        ctx.save_for_backward(q, k, v, out, den, st)
+        ctx.feature_map = feature_map
+        return out
 
     @staticmethod
     def backward(ctx, dout):
-        raise NotImplementedError("the backward of the normalised form is not implemented")
+        q, k, v, out, den, st = ctx.saved_tensors
+        dq, dk, dv = linear_attn_bwd(q, k, v, out, dout.contiguous(), den, ctx.feature_map, state_final=st)
+        return dq, dk, dv, None, None
 
 
 def linear_attention(q, k, v, eps: float = 1e-6, feature_map: str = "elu+1"):
@@ -235,5 +279,5 @@ def linear_attention(q, k, v, eps: float = 1e-6, feature_map: str = "elu+1"):
     return LinearAttention.apply(q, k, v, eps, fm)
 
 
-__all__ = ["causal_product_fwd", "causal_product_bwd", "linear_attn_fwd", "causal_product", "linear_attention",
+__all__ = ["causal_product_fwd", "causal_product_bwd", "linear_attn_fwd", "linear_attn_bwd", "causal_product", "linear_attention",
            "CausalProductError", "lib", "LIB_PATH", "timing_begin", "timing_end"]

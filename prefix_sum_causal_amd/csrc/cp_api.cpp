@@ -17,7 +17,7 @@
 
 namespace {
 
-constexpr int kAbiMajor = 2, kAbiMinor = 0;  // 2.0: carried state
+constexpr int kAbiMajor = 3, kAbiMinor = 0;  // 3.0: carried state, normalised backward
 
 struct Range {
     uintptr_t lo, hi;  // [lo, hi)
@@ -182,7 +182,7 @@ int causal_product_fwd(const void *Q, const void *K, const void *V, void *Out, c
 
     cp::fwd_fn fn = dtype == CP_BF16 ? cp::fwd_bf16((int)E, (int)M, false) : cp::fwd_f32((int)E, (int)M, false);
     if (!fn) return CP_ERR_UNSUPPORTED;
-    cp::FwdArgs a{Q, K, V, Out, state_in, nullptr, state_out, nullptr, (int)L, (int)(N * H), 0.f, 0};
+    cp::FwdArgs a{Q, K, V, Out, state_in, nullptr, state_out, nullptr, nullptr, (int)L, (int)(N * H), 0.f, 0};
     return launch_status(fn(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -202,15 +202,16 @@ int causal_product_bwd(const void *Q, const void *K, const void *V, const void *
                      {span(dQ, ne * es), span(dK, ne * es), span(dV, nm * es), span(dstate_in, ns)});
     if (st != CP_OK) return st;
 
-    cp::bwd_fn fn = dtype == CP_BF16 ? cp::bwd_bf16((int)E, (int)M) : cp::bwd_f32((int)E, (int)M);
+    cp::bwd_fn fn = dtype == CP_BF16 ? cp::bwd_bf16((int)E, (int)M, false) : cp::bwd_f32((int)E, (int)M, false);
     if (!fn) return CP_ERR_UNSUPPORTED;
-    cp::BwdArgs a{Q, K, V, dOut, state_in, state_final, dQ, dK, dV, dstate_in, (int)L, (int)(N * H)};
+    cp::BwdArgs a{Q,   K,    V,       dOut,    state_in, state_final, dQ, dK, dV, dstate_in, (int)L, (int)(N * H),
+                  nullptr, nullptr, nullptr, nullptr, 0};
     return launch_status(fn(a, static_cast<hipStream_t>(stream)));
 }
 
 int linear_attn_fwd(const void *Q, const void *K, const void *V, void *Out, const float *state_in,
-                    const float *z_in, float *state_out, float *z_out, int64_t N, int64_t H, int64_t L,
-                    int64_t E, int64_t M, float eps, int feature_map, int dtype, void *stream) {
+                    const float *z_in, float *state_out, float *z_out, float *den_out, int64_t N, int64_t H,
+                    int64_t L, int64_t E, int64_t M, float eps, int feature_map, int dtype, void *stream) {
     int64_t ne = 0, nm = 0;
     int st = check_dims(N, H, L, E, M, dtype, 128 / 16 * 3, ne, nm);
     if (st != CP_OK) return st;
@@ -218,16 +219,42 @@ int linear_attn_fwd(const void *Q, const void *K, const void *V, void *Out, cons
     if (!(eps >= 0.f) || !std::isfinite(eps)) return CP_ERR_UNSUPPORTED;
     st = check_ptrs({Q, K, V, Out});
     if (st != CP_OK) return st;
-    st = check_opt_ptrs({state_in, z_in, state_out, z_out});
+    st = check_opt_ptrs({state_in, z_in, state_out, z_out, den_out});
     if (st != CP_OK) return st;
-    const int64_t es = dtype == CP_BF16 ? 2 : 4, ns = N * H * E * M * 4, nz = N * H * E * 4;
+    const int64_t es = dtype == CP_BF16 ? 2 : 4, ns = N * H * E * M * 4, nz = N * H * E * 4, nd = N * H * L * 4;
     st = check_alias({span(Q, ne * es), span(K, ne * es), span(V, nm * es), span(state_in, ns), span(z_in, nz)},
-                     {span(Out, nm * es), span(state_out, ns), span(z_out, nz)});
+                     {span(Out, nm * es), span(state_out, ns), span(z_out, nz), span(den_out, nd)});
     if (st != CP_OK) return st;
 
     cp::fwd_fn fn = dtype == CP_BF16 ? cp::fwd_bf16((int)E, (int)M, true) : cp::fwd_f32((int)E, (int)M, true);
     if (!fn) return CP_ERR_UNSUPPORTED;
-    cp::FwdArgs a{Q, K, V, Out, state_in, z_in, state_out, z_out, (int)L, (int)(N * H), eps, feature_map};
+    cp::FwdArgs a{Q, K, V, Out, state_in, z_in, state_out, z_out, den_out, (int)L, (int)(N * H), eps, feature_map};
+    return launch_status(fn(a, static_cast<hipStream_t>(stream)));
+}
+
+int linear_attn_bwd(const void *Q, const void *K, const void *V, const void *Out, const void *dOut,
+                    const float *den, const float *state_in, const float *z_in, const float *state_final,
+                    void *dQ, void *dK, void *dV, float *dstate_in, float *dz_in, int64_t N,
+                    int64_t H, int64_t L, int64_t E, int64_t M, int feature_map, int dtype, void *stream) {
+    int64_t ne = 0, nm = 0;
+    int st = check_dims(N, H, L, E, M, dtype, 128 / 16 * 3, ne, nm);
+    if (st != CP_OK) return st;
+    if (feature_map != 0 && feature_map != 1) return CP_ERR_UNSUPPORTED;
+    st = check_ptrs({Q, K, V, Out, dOut, den, dQ, dK, dV});
+    if (st != CP_OK) return st;
+    st = check_opt_ptrs({state_in, z_in, state_final, dstate_in, dz_in});
+    if (st != CP_OK) return st;
+    const int64_t es = dtype == CP_BF16 ? 2 : 4, ns = N * H * E * M * 4, nz = N * H * E * 4, nd = N * H * L * 4;
+    st = check_alias({span(Q, ne * es), span(K, ne * es), span(V, nm * es), span(Out, nm * es), span(dOut, nm * es),
+                      span(den, nd), span(state_in, ns), span(z_in, nz), span(state_final, ns)},
+                     {span(dQ, ne * es), span(dK, ne * es), span(dV, nm * es), span(dstate_in, ns),
+                      span(dz_in, nz)});
+    if (st != CP_OK) return st;
+
+    cp::bwd_fn fn = dtype == CP_BF16 ? cp::bwd_bf16((int)E, (int)M, true) : cp::bwd_f32((int)E, (int)M, true);
+    if (!fn) return CP_ERR_UNSUPPORTED;
+    cp::BwdArgs a{Q, K,    V,       dOut,    state_in, state_final, dQ, dK, dV, dstate_in, (int)L, (int)(N * H),
+                  Out, den, z_in, dz_in, feature_map};
     return launch_status(fn(a, static_cast<hipStream_t>(stream)));
 }
 

@@ -31,7 +31,8 @@
 // subtracts each chunk (S_{c-1} = S_{L-1} - sum_{c' >= c} K_c'^T V_c'); the
 // state comes from the forward pass, or, when it is not given, from a
 // forward pre-pass of the workgroup over K and V starting at the initial
-// state S0.  At the end the dV waves hold R_0 = sum_i q_i dO_i^T, the
+// state S0 (always so for the normalised form with fp32 I/O, where both
+// directions sum compensated; see EXACT_PREFIX).  At the end the dV waves hold R_0 = sum_i q_i dO_i^T, the
 // gradient of S0.  Carried states keep the
 // rows of their contraction index (m or e) in the order of the 16-byte
 // natural reads of the other operand (see EOps), so no operand is read twice.
@@ -45,9 +46,10 @@ enum BwdRole { kDQ = 0, kDK = 1, kDV = 2, kIdle = 3 };
 
 // The whole sweep of one wave role.  Every role runs the same staging and
 // barriers; only the math differs, so each wave's loop is straight-line code.
-template <typename T, int E, int M, int C, int G, int NPF, int ROLE>
+template <typename T, int E, int M, int C, int G, int NPF, bool NORM, bool FMAP, int ROLE>
 __device__ __forceinline__ void bwd_sweep(const T *q_, const T *k_, const T *v_, const T *g_, const float *s0,
-                                          const float *st, T *out_, float *ds0, int L, int b, T *lds) {
+                                          const float *st, const float *zc_, const float *dd_, int Lpad, T *out_,
+                                          float *ds0, float *dz0, int L, int b, T *lds) {
     using O = Ops<T>;
     using F = typename O::frag;
     using EE = EOps<T, E>;  // contraction over e
@@ -58,6 +60,9 @@ __device__ __forceinline__ void bwd_sweep(const T *q_, const T *k_, const T *v_,
     using SM = Stage<T, NT, C, M>;
     constexpr int RE = SE::RS, RM = SM::RS;
     constexpr int BUF = 2 * C * RE + 2 * C * RM;  // Q, K, V, dO
+    constexpr bool PHI = NORM && FMAP;             // phi applied to Q and K on their way into LDS
+    // NORM: two buffers of the chunk's dd values follow the row buffers
+    float *const ddbuf = reinterpret_cast<float *>(lds + 2 * BUF);
     const int g = lane_g(), r = lane_r();
     const int n = (L + C - 1) / C;
     const Diag diag;
@@ -66,13 +71,31 @@ __device__ __forceinline__ void bwd_sweep(const T *q_, const T *k_, const T *v_,
     //   dQ: W[mt] = S^T[ecol_M(mt) + estride_M g + t][16 b + r]
     //   dK: W[mt] = R^T[ecol_M(mt) + estride_M g + t][16 b + r]
     //   dV: X[et] = R[ecol_E(et) + estride_E g + t][16 b + r]
-    f32x4 W[MB], X[EB];
+    // EXACT_PREFIX (normalised form, fp32 I/O): there dq peaks at the first
+    // rows, where the state recovered backwards from the final one is small
+    // next to it, so plain fp32 would leave there the rounding error of every
+    // later chunk (of the backward and of the forward that produced the final
+    // state).  Instead the dQ waves build the final state in their own
+    // pre-pass as a compensated sum (W + Wlo) of chunk increments computed
+    // exactly as the reverse sweep computes them, and subtract those same
+    // increments, compensated, on the way back: the recovered states are then
+    // the forward prefix sums up to the increments' own rounding.  bf16 I/O
+    // rounds far coarser and keeps the plain update and its registers.
+    constexpr bool EXACT_PREFIX = NORM && std::is_same<T, float>::value;
+    constexpr bool COMP = EXACT_PREFIX && ROLE == kDQ;
+    f32x4 W[MB], X[EB], Wlo[COMP ? MB : 1];
 #pragma unroll
     for (int m = 0; m < MB; ++m) W[m] = zero4();
 #pragma unroll
+    for (int m = 0; m < (COMP ? MB : 1); ++m) Wlo[m] = zero4();
+#pragma unroll
     for (int e = 0; e < EB; ++e) X[e] = zero4();
+    // NORM: dQ holds zb[t] = z_{c-1}[16 b + 4g + t] (prefix of phi(k), read per
+    // chunk); dK carries zb[t] = r[16 b + 4g + t] (suffix of dd_i phi(q_i));
+    // same in every lane r
+    f32x4 zb = zero4();
 
-    if (st) {
+    if (st && !EXACT_PREFIX) {
         if constexpr (ROLE == kDQ) {
 #pragma unroll
             for (int m = 0; m < MB; ++m)
@@ -95,7 +118,7 @@ __device__ __forceinline__ void bwd_sweep(const T *q_, const T *k_, const T *v_,
         sv.load(Rows<T>(v_, M, 0, L, C), 0);
         for (int c = 0; c < n; ++c) {
             T *Ks = lds + (c & 1) * BUF, *Vs = Ks + C * RE;
-            sk.store(Ks);
+            sk.template store<PHI>(Ks, c * C, L);
             sv.store(Vs);
             __syncthreads();
             sk.load(Rows<T>(k_, E, (c + 1) * C, L, C), 0);
@@ -103,9 +126,17 @@ __device__ __forceinline__ void bwd_sweep(const T *q_, const T *k_, const T *v_,
             __builtin_amdgcn_sched_barrier(0);
             if constexpr (ROLE == kDQ) {
 #pragma unroll
-                for (int m = 0; m < MB; ++m)
-                    dotk<T>(W[m], 0, CB, [&](int J) { return EM::tr_e(Vs, RM, J, m); },
-                            [&](int J) { return O::tr_frag(Ks, RE, J, b); });
+                for (int m = 0; m < MB; ++m) {
+                    if constexpr (COMP) {  // the reverse sweep's increment, negated (exactly)
+                        f32x4 dw = zero4();
+                        dotk<T>(dw, 0, CB, [&](int J) { return EM::tr_e(Vs, RM, J, m); },
+                                [&](int J) { return O::tr_frag(Ks, RE, J, b); });
+                        two_sum_acc(W[m], Wlo[m], dw);
+                    } else {
+                        dotk<T>(W[m], 0, CB, [&](int J) { return EM::tr_e(Vs, RM, J, m); },
+                                [&](int J) { return O::tr_frag(Ks, RE, J, b); });
+                    }
+                }
             }
         }
         __syncthreads();  // the main sweep reuses the buffers
@@ -116,35 +147,51 @@ __device__ __forceinline__ void bwd_sweep(const T *q_, const T *k_, const T *v_,
     // Ring of NPF register stages (NPF-1 chunks in flight while one is
     // computed); the step loop is padded to a multiple of NPF with chunks
     // before the start of the sequence, which load as zero and store nothing.
+    // NORM: dd of the chunk's rows, C floats as C/4 16-byte pieces (threads
+    // below C/4); dd_ is padded with zeros to Lpad rows, a multiple of C.
     struct Stages {
         SE q, k;
         SM v, g;
-        __device__ __forceinline__ void load(const T *q_, const T *k_, const T *v_, const T *g_, int row0, int L) {
+        i32x4 dd;
+        __device__ __forceinline__ void load(const T *q_, const T *k_, const T *v_, const T *g_, const float *dd_,
+                                             int row0, int L, int Lpad) {
             q.load(Rows<T>(q_, E, row0, L, C), 0);
             k.load(Rows<T>(k_, E, row0, L, C), 0);
             v.load(Rows<T>(v_, M, row0, L, C), 0);
             g.load(Rows<T>(g_, M, row0, L, C), 0);
+            if constexpr (NORM) {
+                const Rows<float> rd(dd_, 1, row0, Lpad, C);
+                const int t = (int)threadIdx.x;
+                dd = __builtin_amdgcn_raw_buffer_load_b128(rd.rsrc, t < C / 4 ? 16 * t : 0x7FFFFFF0, 0, 0);
+            }
+        }
+        __device__ __forceinline__ void store_dd(float *dst) const {
+            if constexpr (NORM) {
+                if ((int)threadIdx.x < C / 4) *reinterpret_cast<i32x4 *>(dst + 4 * threadIdx.x) = dd;
+            }
         }
     };
     Stages stg[NPF];
 #pragma unroll
     for (int s = 0; s < NPF - 1; ++s) {
-        stg[s].load(q_, k_, v_, g_, (n - 1 - s) * C, L);
+        stg[s].load(q_, k_, v_, g_, dd_, (n - 1 - s) * C, L, Lpad);
         __builtin_amdgcn_sched_barrier(0);  // stages complete in order
     }
     const int nsteps = (n + NPF - 1) / NPF * NPF;
-    for (int s0 = 0; s0 < nsteps; s0 += NPF) {
+    for (int sb = 0; sb < nsteps; sb += NPF) {
 #pragma unroll
         for (int s = 0; s < NPF; ++s) {
-            const int step = s0 + s;
+            const int step = sb + s;
             const int row0 = (n - 1 - step) * C;
             T *Qs = lds + (step & 1) * BUF, *Ks = Qs + C * RE, *Vs = Ks + C * RE, *Gs = Vs + C * RM;
-            stg[s].q.store(Qs);
-            stg[s].k.store(Ks);
+            float *dds = ddbuf + (step & 1) * C;  // NORM: dd_i of row row0 + i
+            stg[s].q.template store<PHI>(Qs, row0, L);
+            stg[s].k.template store<PHI>(Ks, row0, L);
             stg[s].v.store(Vs);
             stg[s].g.store(Gs);
+            stg[s].store_dd(dds);
             __syncthreads();
-            stg[(s + NPF - 1) % NPF].load(q_, k_, v_, g_, row0 - (NPF - 1) * C, L);
+            stg[(s + NPF - 1) % NPF].load(q_, k_, v_, g_, dd_, row0 - (NPF - 1) * C, L, Lpad);
             __builtin_amdgcn_sched_barrier(0);
 
             f32x4 pend[CB];  // this chunk's output tiles (rows 16 I + r)
@@ -154,9 +201,22 @@ __device__ __forceinline__ void bwd_sweep(const T *q_, const T *k_, const T *v_,
 #pragma unroll
                 for (int J = 0; J < CB; ++J) kt[J] = O::tr_frag(Ks, RE, J, b);
 #pragma unroll
-                for (int m = 0; m < MB; ++m)
-                    dotk<T>(W[m], 0, CB, [&](int J) { return EM::tr_e(Vs, RM, J, m); },
-                            [&](int J) { return O::neg(kt[J]); });
+                for (int m = 0; m < MB; ++m) {
+                    if constexpr (COMP) {  // compensated, see EXACT_PREFIX
+                        f32x4 dw = zero4();
+                        dotk<T>(dw, 0, CB, [&](int J) { return EM::tr_e(Vs, RM, J, m); },
+                                [&](int J) { return O::neg(kt[J]); });
+                        two_sum_acc(W[m], Wlo[m], dw);
+                    } else {
+                        dotk<T>(W[m], 0, CB, [&](int J) { return EM::tr_e(Vs, RM, J, m); },
+                                [&](int J) { return O::neg(kt[J]); });
+                    }
+                }
+                if constexpr (NORM) {  // z_{c-1}, summed forward by the scan kernel (no cancellation)
+                    const int c = row0 / C;
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) zb[t] = c >= 0 ? zc_[(int64_t)c * E + 16 * b + 4 * g + t] : 0.f;
+                }
                 typename EM::rf wa[EM::STEPS], vf[CB][EM::STEPS];
 #pragma unroll
                 for (int k = 0; k < EM::STEPS; ++k) wa[k] = EM::state(W, k);
@@ -173,16 +233,32 @@ __device__ __forceinline__ void bwd_sweep(const T *q_, const T *k_, const T *v_,
                     f32x4 d = zero4();
 #pragma unroll
                     for (int k = 0; k < EM::STEPS; ++k) EM::mma(d, wa[k], gf[k]);
+                    // NORM: the ones column of V' = [V 1] against dd: P'^T(j, i) = P^T(j, i) + dd_i,
+                    // and the state's z column: dq_i += dd_i z_{c-1}
+                    const float ddi = NORM ? dds[16 * I + r] : 0.f;
+                    if constexpr (NORM) {
+#pragma unroll
+                        for (int t = 0; t < 4; ++t) d[t] += zb[t] * ddi;
+                    }
                     F pt[CB];
 #pragma unroll
                     for (int J = 0; J <= I; ++J) {
                         f32x4 p = zero4();
 #pragma unroll
                         for (int k = 0; k < EM::STEPS; ++k) EM::mma(p, vf[J][k], gf[k]);
+                        if constexpr (NORM) {
+#pragma unroll
+                            for (int t = 0; t < 4; ++t) p[t] += ddi;
+                        }
                         if (J == I) p = diag.keys(p);
                         pt[J] = O::cvt(p);
                     }
                     dotk<T>(d, 0, I + 1, [&](int J) { return kt[J]; }, [&](int J) { return pt[J]; });
+                    if constexpr (PHI) {  // through phi: phi'(x) = min(phi(x), 1)
+                        const F ph = lds_nat<T>(Qs, RE, I, b);
+#pragma unroll
+                        for (int t = 0; t < 4; ++t) d[t] *= fminf((float)ph[t], 1.f);
+                    }
                     pend[I] = d;
                 }
             } else if constexpr (ROLE == kDK) {
@@ -205,22 +281,48 @@ __device__ __forceinline__ void bwd_sweep(const T *q_, const T *k_, const T *v_,
                     f32x4 d = zero4();
 #pragma unroll
                     for (int k = 0; k < EM::STEPS; ++k) EM::mma(d, wa[k], vf[k]);
+                    if constexpr (NORM) {  // the ones column of V': dk_j += r_{c+1}
+#pragma unroll
+                        for (int t = 0; t < 4; ++t) d[t] += zb[t];
+                    }
                     F pf[CB];
 #pragma unroll
                     for (int I = J; I < CB; ++I) {
                         f32x4 p = zero4();
 #pragma unroll
                         for (int k = 0; k < EM::STEPS; ++k) EM::mma(p, gf[I][k], vf[k]);
+                        if constexpr (NORM) {  // P'(i, j) = P(i, j) + dd_i
+#pragma unroll
+                            for (int t = 0; t < 4; ++t) p[t] += dds[16 * I + 4 * g + t];
+                        }
                         if (I == J) p = diag.query(p);
                         pf[I] = O::cvt(p);
                     }
                     dotk<T>(d, J, CB, [&](int I) { return qt[I]; }, [&](int I) { return pf[I]; });
+                    if constexpr (PHI) {
+                        const F ph = lds_nat<T>(Ks, RE, J, b);
+#pragma unroll
+                        for (int t = 0; t < 4; ++t) d[t] *= fminf((float)ph[t], 1.f);
+                    }
                     pend[J] = d;
                 }
                 // R^T += dO_c^T Q_c[:, b]
 #pragma unroll
                 for (int m = 0; m < MB; ++m)
                     dotk<T>(W[m], 0, CB, [&](int I) { return EM::tr_e(Gs, RM, I, m); }, [&](int I) { return qt[I]; });
+                if constexpr (NORM) {  // r += sum_i dd_i phi(q_i)[b], dd as a hi + lo pair of operands
+                    F dh[CB], dl[CB];
+#pragma unroll
+                    for (int I = 0; I < CB; ++I) {
+                        f32x4 x;
+#pragma unroll
+                        for (int t = 0; t < 4; ++t) x[t] = dds[16 * I + 4 * g + t];
+                        O::split(x, dh[I], dl[I]);
+                    }
+                    dotk<T>(zb, 0, CB, [&](int I) { return qt[I]; }, [&](int I) { return dh[I]; });
+                    if constexpr (sizeof(T) == 2)
+                        dotk<T>(zb, 0, CB, [&](int I) { return qt[I]; }, [&](int I) { return dl[I]; });
+                }
             } else if constexpr (ROLE == kDV) {
                 F gt[CB];  // dO_I[:, b] transposed
 #pragma unroll
@@ -268,6 +370,13 @@ __device__ __forceinline__ void bwd_sweep(const T *q_, const T *k_, const T *v_,
             }
         }
     }
+    // the gradient of the initial z: r_0, held by the dK waves
+    if constexpr (NORM && ROLE == kDK) {
+        if (dz0 && r == 0) {
+#pragma unroll
+            for (int t = 0; t < 4; ++t) dz0[16 * b + 4 * g + t] = zb[t];
+        }
+    }
     // the gradient of the initial state: R_0 = sum_i q_i dO_i^T, held by the
     // dV waves (column blocks b of M) at the end of the reverse sweep
     if constexpr (ROLE == kDV) {
@@ -288,17 +397,24 @@ constexpr int bwd_threads() {
     return 64 * (2 * ((E / 16 + G - 1) / G) + (M / 16 + G - 1) / G);
 }
 
-template <typename T, int E, int M, int C, int G, int NPF>
+// NORM (backward of the normalised form, see the launcher): Q, K are the raw
+// inputs (phi applied on load when FMAP), Gr is dn = dO / den, dd the padded
+// per-row dd = -(dO . out) / den, zc the normaliser z before every chunk
+// ([Lpad / C][E] per slice), dz_in the gradient of the initial z.
+template <typename T, int E, int M, int C, int G, int NPF, bool NORM, bool FMAP>
 __global__ __launch_bounds__((bwd_threads<T, E, M, G>())) void cp_bwd_kernel(
     const T *__restrict__ Q, const T *__restrict__ K, const T *__restrict__ V, const T *__restrict__ Gr,
-    const float *__restrict__ state_in, const float *__restrict__ state_final, T *__restrict__ dQ,
-    T *__restrict__ dK, T *__restrict__ dV, float *__restrict__ dstate_in, int L, int NS) {
+    const float *__restrict__ state_in, const float *__restrict__ state_final, const float *__restrict__ zc,
+    const float *__restrict__ dd, int Lpad, T *__restrict__ dQ,
+    T *__restrict__ dK, T *__restrict__ dV, float *__restrict__ dstate_in, float *__restrict__ dz_in, int L,
+    int NS) {
     constexpr int EB = E / 16, MB = M / 16;
     constexpr int EG = (EB + G - 1) / G, NT = bwd_threads<T, E, M, G>();
     static_assert(NT <= 1024, "at most 16 waves per workgroup");
     constexpr int RE = Stage<T, NT, C, E>::RS, RM = Stage<T, NT, C, M>::RS;
     constexpr int BUF = 2 * C * RE + 2 * C * RM;
-    __shared__ __attribute__((aligned(16))) T lds[2 * BUF];
+    constexpr int DDE = NORM ? 2 * C * 4 / (int)sizeof(T) : 0;  // two dd buffers of C floats
+    __shared__ __attribute__((aligned(16))) T lds[2 * BUF + DDE];
 
     int slice, grp;
     map_block(blockIdx.x, NS, G, slice, grp);
@@ -307,17 +423,24 @@ __global__ __launch_bounds__((bwd_threads<T, E, M, G>())) void cp_bwd_kernel(
     const T *q_ = Q + oe, *k_ = K + oe, *v_ = V + om, *g_ = Gr + om;
     const float *s0 = state_in ? state_in + (int64_t)slice * E * M : nullptr;
     const float *st = state_final ? state_final + (int64_t)slice * E * M : nullptr;
+    const float *zc_ = zc ? zc + (int64_t)slice * (Lpad / C) * E : nullptr;
+    const float *dd_ = dd ? dd + (int64_t)slice * Lpad : nullptr;
     float *ds0 = dstate_in ? dstate_in + (int64_t)slice * E * M : nullptr;
+    float *dz0 = dz_in ? dz_in + (int64_t)slice * E : nullptr;
     const int role = w < EG ? kDQ : w < 2 * EG ? kDK : kDV;
     const int b = grp + G * (role == kDQ ? w : role == kDK ? w - EG : w - 2 * EG);
     if (role == kDQ && b < EB)
-        bwd_sweep<T, E, M, C, G, NPF, kDQ>(q_, k_, v_, g_, s0, st, dQ + oe, nullptr, L, b, lds);
+        bwd_sweep<T, E, M, C, G, NPF, NORM, FMAP, kDQ>(q_, k_, v_, g_, s0, st, zc_, dd_, Lpad, dQ + oe, nullptr,
+                                                       nullptr, L, b, lds);
     else if (role == kDK && b < EB)
-        bwd_sweep<T, E, M, C, G, NPF, kDK>(q_, k_, v_, g_, s0, st, dK + oe, nullptr, L, b, lds);
+        bwd_sweep<T, E, M, C, G, NPF, NORM, FMAP, kDK>(q_, k_, v_, g_, s0, st, zc_, dd_, Lpad, dK + oe, nullptr,
+                                                       dz0, L, b, lds);
     else if (role == kDV && b < MB)
-        bwd_sweep<T, E, M, C, G, NPF, kDV>(q_, k_, v_, g_, s0, st, dV + om, ds0, L, b, lds);
+        bwd_sweep<T, E, M, C, G, NPF, NORM, FMAP, kDV>(q_, k_, v_, g_, s0, st, zc_, dd_, Lpad, dV + om, ds0,
+                                                       nullptr, L, b, lds);
     else
-        bwd_sweep<T, E, M, C, G, NPF, kIdle>(q_, k_, v_, g_, s0, st, nullptr, nullptr, L, 0, lds);
+        bwd_sweep<T, E, M, C, G, NPF, NORM, FMAP, kIdle>(q_, k_, v_, g_, s0, st, zc_, dd_, Lpad, nullptr,
+                                                         nullptr, nullptr, L, 0, lds);
 }
 
 }  // namespace cp

@@ -196,6 +196,22 @@ __device__ __forceinline__ void dotk(f32x4 &acc, int b0, int b1, FA fa, FB fb) {
     if (b < b1) O::mma1(acc, fa(b), fb(b));
 }
 
+// (hi, lo) += d with the rounding error kept in lo (Knuth's two-sum, then a
+// renormalisation so that hi stays the fp32 value nearest hi + lo).  Needs
+// IEEE evaluation as written (no reassociation).
+__device__ __forceinline__ void two_sum_acc(f32x4 &hi, f32x4 &lo, const f32x4 &d) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const float s = hi[t] + d[t];
+        const float bb = s - hi[t];
+        const float err = (hi[t] - (s - bb)) + (d[t] - bb);
+        const float l = lo[t] + err;
+        const float h = s + l;
+        lo[t] = l - (h - s);
+        hi[t] = h;
+    }
+}
+
 // phi(x) = elu(x) + 1 = x + 1 for x > 0, exp(x) otherwise.
 __device__ __forceinline__ float phi(float x) { return x > 0.f ? x + 1.f : __expf(x); }
 

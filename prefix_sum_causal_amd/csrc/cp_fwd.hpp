@@ -62,8 +62,9 @@ constexpr int last_block(int h) {
 // out by reference) is carried by every row set.  SONLY: only the state is
 // accumulated (no Q, no outputs).
 template <typename T, int E, int M, int C, int NW, int RSPLIT, int NPF, bool NORM, bool FMAP, bool SONLY, int H>
-__device__ __forceinline__ void fwd_sweep(const T *q_, const T *k_, const T *v_, T *o_, int rb, int re, int grp,
-                                          int cb, float eps, T *lds, f32x4 (&S)[E / 16], f32x4 (&z)[E / 16]) {
+__device__ __forceinline__ void fwd_sweep(const T *q_, const T *k_, const T *v_, T *o_, float *den_, int rb,
+                                          int re, int grp, int cb, float eps, T *lds, f32x4 (&S)[E / 16],
+                                          f32x4 (&z)[E / 16]) {
     using O = Ops<T>;
     using F = typename O::frag;
     using EO = EOps<T, E>;
@@ -119,6 +120,7 @@ __device__ __forceinline__ void fwd_sweep(const T *q_, const T *k_, const T *v_,
             Stages &nx = st[(s + NPF - 1) % NPF];
             const int nrow0 = row0 + (NPF - 1) * C;
             f32x4 pend[CB];  // this step's output tiles (owned row blocks)
+            float pden[CB];  // NORM: their denominators (row 16 I + r)
             int nload = 0;   // arrays of the next chunk whose loads are issued
             auto issue_load = [&]() {
                 if constexpr (!SONLY)
@@ -134,6 +136,16 @@ __device__ __forceinline__ void fwd_sweep(const T *q_, const T *k_, const T *v_,
 #pragma unroll
                 for (int I = 0; I < CB; ++I)
                     if (owns_block<CB, RSPLIT>(H, I)) st_out<T>(ro, I, grp * NW + cb, pend[I]);
+                if constexpr (NORM) {  // the denominators, from the first column block's waves
+                    if (den_ && grp * NW + cb == 0 && lane_g() == 0) {
+                        const Rows<float> rd(den_, 1, row0, re, C);
+#pragma unroll
+                        for (int I = 0; I < CB; ++I)
+                            if (owns_block<CB, RSPLIT>(H, I))
+                                __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, pden[I]), rd.rsrc,
+                                                                      (16 * I + lane_r()) * 4, 0, 0);
+                    }
+                }
                 __builtin_amdgcn_sched_barrier(0);
             };
             issue_load();
@@ -196,6 +208,7 @@ __device__ __forceinline__ void fwd_sweep(const T *q_, const T *k_, const T *v_,
                 if constexpr (NORM) {
 #pragma unroll
                     for (int t = 0; t < 4; ++t) o[t] = o[t] / (d[t] + eps);
+                    pden[I] = d[0] + eps;  // every row of the tile holds the same column sums
                 }
                 pend[I] = o;
                 issue_load();
@@ -231,7 +244,8 @@ template <typename T, int E, int M, int C, int G, int RSPLIT, int NPF, bool NORM
 __global__ __launch_bounds__(64 * (M / 16 / G) * RSPLIT) void cp_fwd_kernel(
     const T *__restrict__ Q, const T *__restrict__ K, const T *__restrict__ V, T *__restrict__ Out,
     const float *__restrict__ state_in, const float *__restrict__ z_in, float *__restrict__ state_out,
-    float *__restrict__ z_out, float *__restrict__ ws, int L, int NS, int seg_len, float eps) {
+    float *__restrict__ z_out, float *__restrict__ den, float *__restrict__ ws, int L, int NS, int seg_len,
+    float eps) {
     using EO = EOps<T, E>;
     constexpr int EB = E / 16, MB = M / 16, CB = C / 16;
     static_assert(MB % G == 0, "column groups split the column blocks evenly");
@@ -256,6 +270,7 @@ __global__ __launch_bounds__(64 * (M / 16 / G) * RSPLIT) void cp_fwd_kernel(
     const T *k_ = K + (int64_t)slice * L * E;
     const T *v_ = V + (int64_t)slice * L * M;
     T *o_ = Out + (int64_t)slice * L * M;
+    float *den_ = den ? den + (int64_t)slice * L : nullptr;
     const int rb = seg * seg_len, re = rb + seg_len < L ? rb + seg_len : L;
     float *ws_slice = ws ? ws + (int64_t)slice * nseg * WS : nullptr;
 
@@ -292,9 +307,9 @@ __global__ __launch_bounds__(64 * (M / 16 / G) * RSPLIT) void cp_fwd_kernel(
         }
     }
     if (h == 0)
-        fwd_sweep<T, E, M, C, NW, RSPLIT, NPF, NORM, FMAP, SONLY, 0>(q_, k_, v_, o_, rb, re, grp, cb, eps, lds, S, z);
+        fwd_sweep<T, E, M, C, NW, RSPLIT, NPF, NORM, FMAP, SONLY, 0>(q_, k_, v_, o_, den_, rb, re, grp, cb, eps, lds, S, z);
     else
-        fwd_sweep<T, E, M, C, NW, RSPLIT, NPF, NORM, FMAP, SONLY, 1>(q_, k_, v_, o_, rb, re, grp, cb, eps, lds, S, z);
+        fwd_sweep<T, E, M, C, NW, RSPLIT, NPF, NORM, FMAP, SONLY, 1>(q_, k_, v_, o_, den_, rb, re, grp, cb, eps, lds, S, z);
 
     if constexpr (SONLY) {
         if (h == 0) {

@@ -27,7 +27,7 @@ hipError_t launch_fwd_t(const FwdArgs &a, hipStream_t s) {
     const T *q = static_cast<const T *>(a.Q), *k = static_cast<const T *>(a.K), *v = static_cast<const T *>(a.V);
     T *o = static_cast<T *>(a.Out);
     const float *s0 = a.state_in, *z0 = a.z_in;
-    float *st = a.state_out, *zt = a.z_out;
+    float *st = a.state_out, *zt = a.z_out, *dn = a.den_out;
     int L = a.L, NS = a.NS;
     float eps = a.eps;
     const dim3 block(64 * (M / 16 / P::FG) * P::FRS);
@@ -44,14 +44,14 @@ hipError_t launch_fwd_t(const FwdArgs &a, hipStream_t s) {
         e = hipMallocAsync(reinterpret_cast<void **>(&ws), bytes, s);
         if (e != hipSuccess) return e;
         auto k1 = cp_fwd_kernel<T, E, M, P::FC, P::FG, P::FRS, P::FNPF, NORM, FMAP, true>;
-        void *args1[] = {&q, &k, &v, &o, &s0, &z0, &st, &zt, &ws, &L, &NS, &seg_len, &eps};
+        void *args1[] = {&q, &k, &v, &o, &s0, &z0, &st, &zt, &dn, &ws, &L, &NS, &seg_len, &eps};
         e = launch_kernel(reinterpret_cast<const void *>(k1), dim3(NS * P::FG * nseg), block, args1, s);
     } else {
         seg_len = L;
     }
     if (e == hipSuccess) {
         auto k2 = cp_fwd_kernel<T, E, M, P::FC, P::FG, P::FRS, P::FNPF, NORM, FMAP, false>;
-        void *args2[] = {&q, &k, &v, &o, &s0, &z0, &st, &zt, &ws, &L, &NS, &seg_len, &eps};
+        void *args2[] = {&q, &k, &v, &o, &s0, &z0, &st, &zt, &dn, &ws, &L, &NS, &seg_len, &eps};
         e = launch_kernel(reinterpret_cast<const void *>(k2), dim3(NS * P::FG * nseg), block, args2, s);
     }
     if (ws) {

@@ -13,6 +13,7 @@ struct FwdArgs {
     void *Out;
     const float *state_in, *z_in;  // optional initial S and z
     float *state_out, *z_out;      // optional final S and z
+    float *den_out;                // optional denominators (normalised form) [NS][L]
     int L, NS;
     float eps;
     int fmap;
@@ -25,6 +26,12 @@ struct BwdArgs {
     void *dQ, *dK, *dV;
     float *dstate_in;  // optional gradient of S0
     int L, NS;
+    // backward of the normalised form only
+    const void *Out;    // the forward's output
+    const float *den;   // the forward's denominators [NS][L]
+    const float *z_in;  // optional initial z
+    float *dz_in;
+    int fmap;
 };
 
 // Each launcher enqueues one kernel on stream and returns hipSuccess or the
@@ -34,8 +41,8 @@ typedef hipError_t (*bwd_fn)(const BwdArgs &, hipStream_t);
 
 fwd_fn fwd_f32(int E, int M, bool norm);
 fwd_fn fwd_bf16(int E, int M, bool norm);
-bwd_fn bwd_f32(int E, int M);
-bwd_fn bwd_bf16(int E, int M);
+bwd_fn bwd_f32(int E, int M, bool norm);
+bwd_fn bwd_bf16(int E, int M, bool norm);
 
 // Launch a kernel on stream: hipLaunchKernel, or, while the calling thread
 // has a timing in progress (cp_timing_begin), hipExtLaunchKernel with the

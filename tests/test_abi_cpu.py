@@ -24,7 +24,8 @@ def lib():
     vp, i64, i = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
     lib.causal_product_fwd.argtypes = [vp] * 6 + [i64] * 5 + [i, vp]
     lib.causal_product_bwd.argtypes = [vp] * 10 + [i64] * 5 + [i, vp]
-    lib.linear_attn_fwd.argtypes = [vp] * 8 + [i64] * 5 + [ctypes.c_float, i, i, vp]
+    lib.linear_attn_fwd.argtypes = [vp] * 9 + [i64] * 5 + [ctypes.c_float, i, i, vp]
+    lib.linear_attn_bwd.argtypes = [vp] * 14 + [i64] * 5 + [i, i, vp]
     lib.cp_status_string.restype = ctypes.c_char_p
     return lib
 
@@ -37,8 +38,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(
-        ["causal_product_fwd", "causal_product_bwd", "linear_attn_fwd", "cp_status_string", "cp_abi_version",
-         "cp_timing_begin", "cp_timing_end"])
+        ["causal_product_fwd", "causal_product_bwd", "linear_attn_fwd", "linear_attn_bwd", "cp_status_string",
+         "cp_abi_version", "cp_timing_begin", "cp_timing_end"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -53,7 +54,7 @@ def test_status_strings_and_version(lib):
         assert msg and msg not in seen
         seen.add(msg)
     assert lib.cp_status_string(99).decode() == "unknown status"
-    assert lib.cp_abi_version() == (2 << 16)
+    assert lib.cp_abi_version() == (3 << 16)
 
 
 def test_timing_rejects_bad_arguments_before_any_device_call(lib):
@@ -83,9 +84,14 @@ def bwd(lib, q=A[0], k=A[1], v=A[2], g=A[3], s0=None, st=None, dq=A[4], dk=A[5],
     return lib.causal_product_bwd(q, k, v, g, s0, st, dq, dk, dv, ds0, *shape, dtype, None)
 
 
-def lin(lib, q=A[0], k=A[1], v=A[2], o=A[3], s0=None, z0=None, st=None, zt=None, shape=SHAPE, eps=1e-6, fm=1,
-        dtype=1):
-    return lib.linear_attn_fwd(q, k, v, o, s0, z0, st, zt, *shape, eps, fm, dtype, None)
+def lin(lib, q=A[0], k=A[1], v=A[2], o=A[3], s0=None, z0=None, st=None, zt=None, den=None, shape=SHAPE, eps=1e-6,
+        fm=1, dtype=1):
+    return lib.linear_attn_fwd(q, k, v, o, s0, z0, st, zt, den, *shape, eps, fm, dtype, None)
+
+
+def linb(lib, q=A[0], k=A[1], v=A[2], o=A[3], g=A[4], den=A[5], s0=None, z0=None, st=None, dq=A[6], dk=A[7],
+         dv=A[8], ds0=None, dz0=None, shape=SHAPE, fm=1, dtype=1):
+    return lib.linear_attn_bwd(q, k, v, o, g, den, s0, z0, st, dq, dk, dv, ds0, dz0, *shape, fm, dtype, None)
 
 
 @pytest.mark.parametrize("which", range(4))
@@ -156,3 +162,19 @@ def test_aliasing(lib):
     assert lin(lib, o=A[2]) == ALIAS
     assert lin(lib, z0=A[5], zt=A[5]) == ALIAS
     assert lin(lib, st=A[5], zt=A[5] + 64) == ALIAS  # z_out inside state_out
+
+
+def test_linear_attn_bwd_validation(lib):
+    for name in ("q", "k", "v", "o", "g", "den", "dq", "dk", "dv"):
+        assert linb(lib, **{name: None}) == NULL, name
+    assert linb(lib, shape=(2, 3, 0, 64, 32)) == DIM
+    assert linb(lib, shape=(2, 3, 100, 48, 32)) == UNSUP
+    assert linb(lib, fm=3) == UNSUP
+    assert linb(lib, dtype=5) == UNSUP
+    assert linb(lib, den=A[5] + 4) == ALIGN
+    assert linb(lib, dz0=A[9] + 8) == ALIGN
+    assert linb(lib, dq=A[0]) == ALIAS            # dq overlaps q
+    assert linb(lib, dv=A[5]) == ALIAS            # dv overlaps den
+    assert linb(lib, ds0=A[9], s0=A[9]) == ALIAS  # gradient over its own state
+    assert lin(lib, den=A[3]) == ALIAS            # den_out overlaps out
+    assert lin(lib, den=A[5] + 4) == ALIGN
