@@ -39,14 +39,44 @@
 #pragma once
 
 #include "cp_device.hpp"
+#include "cp_tune.hpp"
 
 namespace cp {
 
 enum BwdRole { kDQ = 0, kDK = 1, kDV = 2, kIdle = 3 };
 
+// A k-contraction into NB accumulators that share one operand: acc(x) is the
+// x-th accumulator; fs(i) the shared operand (read once), fo(x, i) the x-th
+// own operand.  SHARED_A puts the shared operand on the A side.
+template <typename T, int NB, bool SHARED_A, typename FACC, typename FS, typename FO>
+__device__ __forceinline__ void dotk_shared(FACC acc, int b0, int b1, FS fs, FO fo) {
+    using O = Ops<T>;
+    int i = b0;
+#pragma unroll
+    for (; i + 1 < b1; i += 2) {
+        const auto s0 = fs(i), s1 = fs(i + 1);
+#pragma unroll
+        for (int x = 0; x < NB; ++x) {
+            if constexpr (SHARED_A) O::mma2(acc(x), s0, s1, fo(x, i), fo(x, i + 1));
+            else O::mma2(acc(x), fo(x, i), fo(x, i + 1), s0, s1);
+        }
+    }
+    if (i < b1) {
+        const auto s0 = fs(i);
+#pragma unroll
+        for (int x = 0; x < NB; ++x) {
+            if constexpr (SHARED_A) O::mma1(acc(x), s0, fo(x, i));
+            else O::mma1(acc(x), fo(x, i), s0);
+        }
+    }
+}
+
 // The whole sweep of one wave role.  Every role runs the same staging and
 // barriers; only the math differs, so each wave's loop is straight-line code.
-template <typename T, int E, int M, int C, int G, int NPF, bool NORM, bool FMAP, int ROLE>
+// The wave owns the NB column blocks b + G x (x = 0 .. NB-1) of its output;
+// the chunk's operand tiles and causal tiles are read and formed once for
+// all of them.
+template <typename T, int E, int M, int C, int G, int NB, int IDLE, int NPF, bool NORM, bool FMAP, int ROLE>
 __device__ __forceinline__ void bwd_sweep(const T *q_, const T *k_, const T *v_, const T *g_, const float *s0,
                                           const float *st, const float *zc_, const float *dd_, int Lpad, T *out_,
                                           float *ds0, float *dz0, int L, int b, T *lds) {
@@ -55,7 +85,7 @@ __device__ __forceinline__ void bwd_sweep(const T *q_, const T *k_, const T *v_,
     using EE = EOps<T, E>;  // contraction over e
     using EM = EOps<T, M>;  // contraction over m
     constexpr int EB = E / 16, MB = M / 16, CB = C / 16;
-    constexpr int EG = (EB + G - 1) / G, MG = (MB + G - 1) / G, NT = 64 * (2 * EG + MG);
+    constexpr int NT = 64 * bwd_waves<E, M, G, NB, IDLE>();
     using SE = Stage<T, NT, C, E>;
     using SM = Stage<T, NT, C, M>;
     constexpr int RE = SE::RS, RM = SM::RS;
@@ -66,11 +96,12 @@ __device__ __forceinline__ void bwd_sweep(const T *q_, const T *k_, const T *v_,
     const int g = lane_g(), r = lane_r();
     const int n = (L + C - 1) / C;
     const Diag diag;
+    auto bk = [&](int x) { return b + G * x; };  // the wave's column blocks
 
-    // carried state (fp32 accumulator tiles)
-    //   dQ: W[mt] = S^T[ecol_M(mt) + estride_M g + t][16 b + r]
-    //   dK: W[mt] = R^T[ecol_M(mt) + estride_M g + t][16 b + r]
-    //   dV: X[et] = R[ecol_E(et) + estride_E g + t][16 b + r]
+    // carried state (fp32 accumulator tiles), per column block bk(x)
+    //   dQ: W[x][mt] = S^T[ecol_M(mt) + estride_M g + t][16 bk(x) + r]
+    //   dK: W[x][mt] = R^T[ecol_M(mt) + estride_M g + t][16 bk(x) + r]
+    //   dV: X[x][et] = R[ecol_E(et) + estride_E g + t][16 bk(x) + r]
     // EXACT_PREFIX (normalised form, fp32 I/O): there dq peaks at the first
     // rows, where the state recovered backwards from the final one is small
     // next to it, so plain fp32 would leave there the rounding error of every
@@ -83,33 +114,48 @@ __device__ __forceinline__ void bwd_sweep(const T *q_, const T *k_, const T *v_,
     // rounds far coarser and keeps the plain update and its registers.
     constexpr bool EXACT_PREFIX = NORM && std::is_same<T, float>::value;
     constexpr bool COMP = EXACT_PREFIX && ROLE == kDQ;
-    f32x4 W[MB], X[EB], Wlo[COMP ? MB : 1];
+    constexpr int NW = ROLE == kDQ || ROLE == kDK ? NB : 1, NX = ROLE == kDV ? NB : 1;
+    f32x4 W[NW][MB], X[NX][EB], Wlo[COMP ? NB : 1][COMP ? MB : 1];
 #pragma unroll
-    for (int m = 0; m < MB; ++m) W[m] = zero4();
+    for (int x = 0; x < NW; ++x)
 #pragma unroll
-    for (int m = 0; m < (COMP ? MB : 1); ++m) Wlo[m] = zero4();
+        for (int m = 0; m < MB; ++m) W[x][m] = zero4();
 #pragma unroll
-    for (int e = 0; e < EB; ++e) X[e] = zero4();
-    // NORM: dQ holds zb[t] = z_{c-1}[16 b + 4g + t] (prefix of phi(k), read per
-    // chunk); dK carries zb[t] = r[16 b + 4g + t] (suffix of dd_i phi(q_i));
-    // same in every lane r
-    f32x4 zb = zero4();
+    for (int x = 0; x < (COMP ? NB : 1); ++x)
+#pragma unroll
+        for (int m = 0; m < (COMP ? MB : 1); ++m) Wlo[x][m] = zero4();
+#pragma unroll
+    for (int x = 0; x < NX; ++x)
+#pragma unroll
+        for (int e = 0; e < EB; ++e) X[x][e] = zero4();
+    // NORM: dQ holds zb[x][t] = z_{c-1}[16 bk(x) + 4g + t] (prefix of phi(k),
+    // read per chunk); dK carries zb[x][t] = r[16 bk(x) + 4g + t] (suffix of
+    // dd_i phi(q_i)); same in every lane r
+    f32x4 zb[NB];
+#pragma unroll
+    for (int x = 0; x < NB; ++x) zb[x] = zero4();
 
     if (st && !EXACT_PREFIX) {
         if constexpr (ROLE == kDQ) {
 #pragma unroll
-            for (int m = 0; m < MB; ++m)
+            for (int x = 0; x < NB; ++x)
 #pragma unroll
-                for (int t = 0; t < 4; ++t) W[m][t] = st[(16 * b + r) * M + EM::ecol(m) + EM::estride * g + t];
+                for (int m = 0; m < MB; ++m)
+#pragma unroll
+                    for (int t = 0; t < 4; ++t)
+                        W[x][m][t] = st[(16 * bk(x) + r) * M + EM::ecol(m) + EM::estride * g + t];
         }
     } else {
         // forward pre-pass: S_{L-1}^T[:, b] = S0^T[:, b] + sum over chunks of V^T K[:, b]
         if constexpr (ROLE == kDQ) {
             if (s0) {
 #pragma unroll
-                for (int m = 0; m < MB; ++m)
+                for (int x = 0; x < NB; ++x)
 #pragma unroll
-                    for (int t = 0; t < 4; ++t) W[m][t] = s0[(16 * b + r) * M + EM::ecol(m) + EM::estride * g + t];
+                    for (int m = 0; m < MB; ++m)
+#pragma unroll
+                        for (int t = 0; t < 4; ++t)
+                            W[x][m][t] = s0[(16 * bk(x) + r) * M + EM::ecol(m) + EM::estride * g + t];
             }
         }
         SE sk;
@@ -125,16 +171,26 @@ __device__ __forceinline__ void bwd_sweep(const T *q_, const T *k_, const T *v_,
             sv.load(Rows<T>(v_, M, (c + 1) * C, L, C), 0);
             __builtin_amdgcn_sched_barrier(0);
             if constexpr (ROLE == kDQ) {
+                F kt[NB][CB];
+#pragma unroll
+                for (int x = 0; x < NB; ++x)
+#pragma unroll
+                    for (int J = 0; J < CB; ++J) kt[x][J] = O::tr_frag(Ks, RE, J, bk(x));
 #pragma unroll
                 for (int m = 0; m < MB; ++m) {
                     if constexpr (COMP) {  // the reverse sweep's increment, negated (exactly)
-                        f32x4 dw = zero4();
-                        dotk<T>(dw, 0, CB, [&](int J) { return EM::tr_e(Vs, RM, J, m); },
-                                [&](int J) { return O::tr_frag(Ks, RE, J, b); });
-                        two_sum_acc(W[m], Wlo[m], dw);
+                        f32x4 dw[NB];
+#pragma unroll
+                        for (int x = 0; x < NB; ++x) dw[x] = zero4();
+                        dotk_shared<T, NB, true>([&](int x) -> f32x4 & { return dw[x]; }, 0, CB,
+                                                 [&](int J) { return EM::tr_e(Vs, RM, J, m); },
+                                                 [&](int x, int J) { return kt[x][J]; });
+#pragma unroll
+                        for (int x = 0; x < NB; ++x) two_sum_acc(W[x][m], Wlo[x][m], dw[x]);
                     } else {
-                        dotk<T>(W[m], 0, CB, [&](int J) { return EM::tr_e(Vs, RM, J, m); },
-                                [&](int J) { return O::tr_frag(Ks, RE, J, b); });
+                        dotk_shared<T, NB, true>([&](int x) -> f32x4 & { return W[x][m]; }, 0, CB,
+                                                 [&](int J) { return EM::tr_e(Vs, RM, J, m); },
+                                                 [&](int x, int J) { return kt[x][J]; });
                     }
                 }
             }
@@ -194,32 +250,44 @@ __device__ __forceinline__ void bwd_sweep(const T *q_, const T *k_, const T *v_,
             stg[(s + NPF - 1) % NPF].load(q_, k_, v_, g_, dd_, row0 - (NPF - 1) * C, L, Lpad);
             __builtin_amdgcn_sched_barrier(0);
 
-            f32x4 pend[CB];  // this chunk's output tiles (rows 16 I + r)
+            f32x4 pend[NB][CB];  // this chunk's output tiles (rows 16 I + r) per column block
             if constexpr (ROLE == kDQ) {
                 // W = S_{c-1}^T = S_c^T - V_c^T K_c[:, b]
-                F kt[CB];  // K_J[:, b] transposed: lane (g, r) <- K[16 J + 4g + t][16 b + r]
+                F kt[NB][CB];  // K_J[:, b] transposed: lane (g, r) <- K[16 J + 4g + t][16 b + r]
 #pragma unroll
-                for (int J = 0; J < CB; ++J) kt[J] = O::tr_frag(Ks, RE, J, b);
+                for (int x = 0; x < NB; ++x)
+#pragma unroll
+                    for (int J = 0; J < CB; ++J) kt[x][J] = O::tr_frag(Ks, RE, J, bk(x));
 #pragma unroll
                 for (int m = 0; m < MB; ++m) {
                     if constexpr (COMP) {  // compensated, see EXACT_PREFIX
-                        f32x4 dw = zero4();
-                        dotk<T>(dw, 0, CB, [&](int J) { return EM::tr_e(Vs, RM, J, m); },
-                                [&](int J) { return O::neg(kt[J]); });
-                        two_sum_acc(W[m], Wlo[m], dw);
+                        f32x4 dw[NB];
+#pragma unroll
+                        for (int x = 0; x < NB; ++x) dw[x] = zero4();
+                        dotk_shared<T, NB, true>([&](int x) -> f32x4 & { return dw[x]; }, 0, CB,
+                                                 [&](int J) { return EM::tr_e(Vs, RM, J, m); },
+                                                 [&](int x, int J) { return O::neg(kt[x][J]); });
+#pragma unroll
+                        for (int x = 0; x < NB; ++x) two_sum_acc(W[x][m], Wlo[x][m], dw[x]);
                     } else {
-                        dotk<T>(W[m], 0, CB, [&](int J) { return EM::tr_e(Vs, RM, J, m); },
-                                [&](int J) { return O::neg(kt[J]); });
+                        dotk_shared<T, NB, true>([&](int x) -> f32x4 & { return W[x][m]; }, 0, CB,
+                                                 [&](int J) { return EM::tr_e(Vs, RM, J, m); },
+                                                 [&](int x, int J) { return O::neg(kt[x][J]); });
                     }
                 }
                 if constexpr (NORM) {  // z_{c-1}, summed forward by the scan kernel (no cancellation)
                     const int c = row0 / C;
 #pragma unroll
-                    for (int t = 0; t < 4; ++t) zb[t] = c >= 0 ? zc_[(int64_t)c * E + 16 * b + 4 * g + t] : 0.f;
-                }
-                typename EM::rf wa[EM::STEPS], vf[CB][EM::STEPS];
+                    for (int x = 0; x < NB; ++x)
 #pragma unroll
-                for (int k = 0; k < EM::STEPS; ++k) wa[k] = EM::state(W, k);
+                        for (int t = 0; t < 4; ++t)
+                            zb[x][t] = c >= 0 ? zc_[(int64_t)c * E + 16 * bk(x) + 4 * g + t] : 0.f;
+                }
+                typename EM::rf wa[NB][EM::STEPS], vf[CB][EM::STEPS];
+#pragma unroll
+                for (int x = 0; x < NB; ++x)
+#pragma unroll
+                    for (int k = 0; k < EM::STEPS; ++k) wa[x][k] = EM::state(W[x], k);
 #pragma unroll
                 for (int J = 0; J < CB; ++J)
 #pragma unroll
@@ -229,17 +297,10 @@ __device__ __forceinline__ void bwd_sweep(const T *q_, const T *k_, const T *v_,
                     typename EM::rf gf[EM::STEPS];
 #pragma unroll
                     for (int k = 0; k < EM::STEPS; ++k) gf[k] = EM::load(Gs, RM, I, k);
-                    // dQ^T = S dO_I^T + K^T P^T with P^T(J, I) = V_J dO_I^T, causal on the diagonal
-                    f32x4 d = zero4();
-#pragma unroll
-                    for (int k = 0; k < EM::STEPS; ++k) EM::mma(d, wa[k], gf[k]);
                     // NORM: the ones column of V' = [V 1] against dd: P'^T(j, i) = P^T(j, i) + dd_i,
                     // and the state's z column: dq_i += dd_i z_{c-1}
                     const float ddi = NORM ? dds[16 * I + r] : 0.f;
-                    if constexpr (NORM) {
-#pragma unroll
-                        for (int t = 0; t < 4; ++t) d[t] += zb[t] * ddi;
-                    }
+                    // P^T(J, I) = V_J dO_I^T, causal on the diagonal (shared by the blocks)
                     F pt[CB];
 #pragma unroll
                     for (int J = 0; J <= I; ++J) {
@@ -253,21 +314,36 @@ __device__ __forceinline__ void bwd_sweep(const T *q_, const T *k_, const T *v_,
                         if (J == I) p = diag.keys(p);
                         pt[J] = O::cvt(p);
                     }
-                    dotk<T>(d, 0, I + 1, [&](int J) { return kt[J]; }, [&](int J) { return pt[J]; });
-                    if constexpr (PHI) {  // through phi: phi'(x) = min(phi(x), 1)
-                        const F ph = lds_nat<T>(Qs, RE, I, b);
+                    // dQ^T = S dO_I^T + K^T P^T
 #pragma unroll
-                        for (int t = 0; t < 4; ++t) d[t] *= fminf((float)ph[t], 1.f);
+                    for (int x = 0; x < NB; ++x) {
+                        f32x4 d = zero4();
+#pragma unroll
+                        for (int k = 0; k < EM::STEPS; ++k) EM::mma(d, wa[x][k], gf[k]);
+                        if constexpr (NORM) {
+#pragma unroll
+                            for (int t = 0; t < 4; ++t) d[t] += zb[x][t] * ddi;
+                        }
+                        dotk<T>(d, 0, I + 1, [&](int J) { return kt[x][J]; }, [&](int J) { return pt[J]; });
+                        if constexpr (PHI) {  // through phi: phi'(x) = min(phi(x), 1)
+                            const F ph = lds_nat<T>(Qs, RE, I, bk(x));
+#pragma unroll
+                            for (int t = 0; t < 4; ++t) d[t] *= fminf((float)ph[t], 1.f);
+                        }
+                        pend[x][I] = d;
                     }
-                    pend[I] = d;
                 }
             } else if constexpr (ROLE == kDK) {
-                F qt[CB];  // Q_I[:, b] transposed
+                F qt[NB][CB];  // Q_I[:, b] transposed
 #pragma unroll
-                for (int I = 0; I < CB; ++I) qt[I] = O::tr_frag(Qs, RE, I, b);
-                typename EM::rf wa[EM::STEPS], gf[CB][EM::STEPS];
+                for (int x = 0; x < NB; ++x)
 #pragma unroll
-                for (int k = 0; k < EM::STEPS; ++k) wa[k] = EM::state(W, k);  // R_{c+1}
+                    for (int I = 0; I < CB; ++I) qt[x][I] = O::tr_frag(Qs, RE, I, bk(x));
+                typename EM::rf wa[NB][EM::STEPS], gf[CB][EM::STEPS];
+#pragma unroll
+                for (int x = 0; x < NB; ++x)
+#pragma unroll
+                    for (int k = 0; k < EM::STEPS; ++k) wa[x][k] = EM::state(W[x], k);  // R_{c+1}
 #pragma unroll
                 for (int I = 0; I < CB; ++I)
 #pragma unroll
@@ -277,14 +353,7 @@ __device__ __forceinline__ void bwd_sweep(const T *q_, const T *k_, const T *v_,
                     typename EM::rf vf[EM::STEPS];
 #pragma unroll
                     for (int k = 0; k < EM::STEPS; ++k) vf[k] = EM::load(Vs, RM, J, k);
-                    // dK^T = R_{c+1} V_J^T + Q^T P with P(I, J) = dO_I V_J^T for I >= J
-                    f32x4 d = zero4();
-#pragma unroll
-                    for (int k = 0; k < EM::STEPS; ++k) EM::mma(d, wa[k], vf[k]);
-                    if constexpr (NORM) {  // the ones column of V': dk_j += r_{c+1}
-#pragma unroll
-                        for (int t = 0; t < 4; ++t) d[t] += zb[t];
-                    }
+                    // P(I, J) = dO_I V_J^T for I >= J (shared by the blocks)
                     F pf[CB];
 #pragma unroll
                     for (int I = J; I < CB; ++I) {
@@ -298,18 +367,31 @@ __device__ __forceinline__ void bwd_sweep(const T *q_, const T *k_, const T *v_,
                         if (I == J) p = diag.query(p);
                         pf[I] = O::cvt(p);
                     }
-                    dotk<T>(d, J, CB, [&](int I) { return qt[I]; }, [&](int I) { return pf[I]; });
-                    if constexpr (PHI) {
-                        const F ph = lds_nat<T>(Ks, RE, J, b);
+                    // dK^T = R_{c+1} V_J^T + Q^T P
 #pragma unroll
-                        for (int t = 0; t < 4; ++t) d[t] *= fminf((float)ph[t], 1.f);
+                    for (int x = 0; x < NB; ++x) {
+                        f32x4 d = zero4();
+#pragma unroll
+                        for (int k = 0; k < EM::STEPS; ++k) EM::mma(d, wa[x][k], vf[k]);
+                        if constexpr (NORM) {  // the ones column of V': dk_j += r_{c+1}
+#pragma unroll
+                            for (int t = 0; t < 4; ++t) d[t] += zb[x][t];
+                        }
+                        dotk<T>(d, J, CB, [&](int I) { return qt[x][I]; }, [&](int I) { return pf[I]; });
+                        if constexpr (PHI) {
+                            const F ph = lds_nat<T>(Ks, RE, J, bk(x));
+#pragma unroll
+                            for (int t = 0; t < 4; ++t) d[t] *= fminf((float)ph[t], 1.f);
+                        }
+                        pend[x][J] = d;
                     }
-                    pend[J] = d;
                 }
                 // R^T += dO_c^T Q_c[:, b]
 #pragma unroll
                 for (int m = 0; m < MB; ++m)
-                    dotk<T>(W[m], 0, CB, [&](int I) { return EM::tr_e(Gs, RM, I, m); }, [&](int I) { return qt[I]; });
+                    dotk_shared<T, NB, true>([&](int x) -> f32x4 & { return W[x][m]; }, 0, CB,
+                                             [&](int I) { return EM::tr_e(Gs, RM, I, m); },
+                                             [&](int x, int I) { return qt[x][I]; });
                 if constexpr (NORM) {  // r += sum_i dd_i phi(q_i)[b], dd as a hi + lo pair of operands
                     F dh[CB], dl[CB];
 #pragma unroll
@@ -319,17 +401,24 @@ __device__ __forceinline__ void bwd_sweep(const T *q_, const T *k_, const T *v_,
                         for (int t = 0; t < 4; ++t) x[t] = dds[16 * I + 4 * g + t];
                         O::split(x, dh[I], dl[I]);
                     }
-                    dotk<T>(zb, 0, CB, [&](int I) { return qt[I]; }, [&](int I) { return dh[I]; });
-                    if constexpr (sizeof(T) == 2)
-                        dotk<T>(zb, 0, CB, [&](int I) { return qt[I]; }, [&](int I) { return dl[I]; });
+#pragma unroll
+                    for (int x = 0; x < NB; ++x) {
+                        dotk<T>(zb[x], 0, CB, [&](int I) { return qt[x][I]; }, [&](int I) { return dh[I]; });
+                        if constexpr (sizeof(T) == 2)
+                            dotk<T>(zb[x], 0, CB, [&](int I) { return qt[x][I]; }, [&](int I) { return dl[I]; });
+                    }
                 }
             } else if constexpr (ROLE == kDV) {
-                F gt[CB];  // dO_I[:, b] transposed
+                F gt[NB][CB];  // dO_I[:, b] transposed
 #pragma unroll
-                for (int I = 0; I < CB; ++I) gt[I] = O::tr_frag(Gs, RM, I, b);
-                typename EE::rf xa[EE::STEPS], qf[CB][EE::STEPS];
+                for (int x = 0; x < NB; ++x)
 #pragma unroll
-                for (int k = 0; k < EE::STEPS; ++k) xa[k] = EE::state(X, k);  // R_{c+1}^T rows
+                    for (int I = 0; I < CB; ++I) gt[x][I] = O::tr_frag(Gs, RM, I, bk(x));
+                typename EE::rf xa[NB][EE::STEPS], qf[CB][EE::STEPS];
+#pragma unroll
+                for (int x = 0; x < NB; ++x)
+#pragma unroll
+                    for (int k = 0; k < EE::STEPS; ++k) xa[x][k] = EE::state(X[x], k);  // R_{c+1}^T rows
 #pragma unroll
                 for (int I = 0; I < CB; ++I)
 #pragma unroll
@@ -339,10 +428,7 @@ __device__ __forceinline__ void bwd_sweep(const T *q_, const T *k_, const T *v_,
                     typename EE::rf kf[EE::STEPS];
 #pragma unroll
                     for (int k = 0; k < EE::STEPS; ++k) kf[k] = EE::load(Ks, RE, J, k);
-                    // dV^T = R^T K_J^T + dO^T A with A(I, J) = Q_I K_J^T for I >= J
-                    f32x4 d = zero4();
-#pragma unroll
-                    for (int k = 0; k < EE::STEPS; ++k) EE::mma(d, xa[k], kf[k]);
+                    // A(I, J) = Q_I K_J^T for I >= J (shared by the blocks)
                     F af[CB];
 #pragma unroll
                     for (int I = J; I < CB; ++I) {
@@ -352,13 +438,22 @@ __device__ __forceinline__ void bwd_sweep(const T *q_, const T *k_, const T *v_,
                         if (I == J) a = diag.query(a);
                         af[I] = O::cvt(a);
                     }
-                    dotk<T>(d, J, CB, [&](int I) { return gt[I]; }, [&](int I) { return af[I]; });
-                    pend[J] = d;
+                    // dV^T = R^T K_J^T + dO^T A
+#pragma unroll
+                    for (int x = 0; x < NB; ++x) {
+                        f32x4 d = zero4();
+#pragma unroll
+                        for (int k = 0; k < EE::STEPS; ++k) EE::mma(d, xa[x][k], kf[k]);
+                        dotk<T>(d, J, CB, [&](int I) { return gt[x][I]; }, [&](int I) { return af[I]; });
+                        pend[x][J] = d;
+                    }
                 }
                 // R += Q_c^T dO_c[:, b]
 #pragma unroll
                 for (int e = 0; e < EB; ++e)
-                    dotk<T>(X[e], 0, CB, [&](int I) { return EE::tr_e(Qs, RE, I, e); }, [&](int I) { return gt[I]; });
+                    dotk_shared<T, NB, true>([&](int x) -> f32x4 & { return X[x][e]; }, 0, CB,
+                                             [&](int I) { return EE::tr_e(Qs, RE, I, e); },
+                                             [&](int x, int I) { return gt[x][I]; });
             }
             // Stores go after this step's prefetch: memory operations complete
             // in issue order, so the rows waited for at a later step were
@@ -366,7 +461,9 @@ __device__ __forceinline__ void bwd_sweep(const T *q_, const T *k_, const T *v_,
             if constexpr (ROLE != kIdle) {
                 const Rows<T> rp(out_, OW, row0, L, C);
 #pragma unroll
-                for (int j = 0; j < CB; ++j) st_out<T>(rp, j, b, pend[j]);
+                for (int x = 0; x < NB; ++x)
+#pragma unroll
+                    for (int j = 0; j < CB; ++j) st_out<T>(rp, j, bk(x), pend[x][j]);
             }
         }
     }
@@ -374,42 +471,42 @@ __device__ __forceinline__ void bwd_sweep(const T *q_, const T *k_, const T *v_,
     if constexpr (NORM && ROLE == kDK) {
         if (dz0 && r == 0) {
 #pragma unroll
-            for (int t = 0; t < 4; ++t) dz0[16 * b + 4 * g + t] = zb[t];
+            for (int x = 0; x < NB; ++x)
+#pragma unroll
+                for (int t = 0; t < 4; ++t) dz0[16 * bk(x) + 4 * g + t] = zb[x][t];
         }
     }
     // the gradient of the initial state: R_0 = sum_i q_i dO_i^T, held by the
-    // dV waves (column blocks b of M) at the end of the reverse sweep
+    // dV waves (column blocks of M) at the end of the reverse sweep
     if constexpr (ROLE == kDV) {
         if (ds0) {
 #pragma unroll
-            for (int e = 0; e < EB; ++e)
+            for (int x = 0; x < NB; ++x)
 #pragma unroll
-                for (int t = 0; t < 4; ++t) ds0[(EE::ecol(e) + EE::estride * g + t) * M + 16 * b + r] = X[e][t];
+                for (int e = 0; e < EB; ++e)
+#pragma unroll
+                    for (int t = 0; t < 4; ++t)
+                        ds0[(EE::ecol(e) + EE::estride * g + t) * M + 16 * bk(x) + r] = X[x][e][t];
         }
     }
-}
-
-// Waves of a workgroup: EG dQ waves, EG dK waves and MG dV waves; group grp
-// takes the column blocks b = grp + G * i (a wave whose block is past E or M
-// only helps copy).
-template <typename T, int E, int M, int G>
-constexpr int bwd_threads() {
-    return 64 * (2 * ((E / 16 + G - 1) / G) + (M / 16 + G - 1) / G);
 }
 
 // NORM (backward of the normalised form, see the launcher): Q, K are the raw
 // inputs (phi applied on load when FMAP), Gr is dn = dO / den, dd the padded
 // per-row dd = -(dO . out) / den, zc the normaliser z before every chunk
 // ([Lpad / C][E] per slice), dz_in the gradient of the initial z.
-template <typename T, int E, int M, int C, int G, int NPF, bool NORM, bool FMAP>
-__global__ __launch_bounds__((bwd_threads<T, E, M, G>())) void cp_bwd_kernel(
+template <typename T, int E, int M, int C, int G, int NB, int IDLE, int NPF, bool NORM, bool FMAP>
+__global__ __launch_bounds__((64 * bwd_waves<E, M, G, NB, IDLE>())) void cp_bwd_kernel(
     const T *__restrict__ Q, const T *__restrict__ K, const T *__restrict__ V, const T *__restrict__ Gr,
     const float *__restrict__ state_in, const float *__restrict__ state_final, const float *__restrict__ zc,
     const float *__restrict__ dd, int Lpad, T *__restrict__ dQ,
     T *__restrict__ dK, T *__restrict__ dV, float *__restrict__ dstate_in, float *__restrict__ dz_in, int L,
     int NS) {
     constexpr int EB = E / 16, MB = M / 16;
-    constexpr int EG = (EB + G - 1) / G, NT = bwd_threads<T, E, M, G>();
+    // with several blocks per wave every wave's blocks all exist
+    static_assert(NB == 1 || (EB % (G * NB) == 0 && MB % (G * NB) == 0), "blocks per wave");
+    constexpr int EG = (EB + G * NB - 1) / (G * NB), MG = (MB + G * NB - 1) / (G * NB);
+    constexpr int NT = 64 * bwd_waves<E, M, G, NB, IDLE>();
     static_assert(NT <= 1024, "at most 16 waves per workgroup");
     constexpr int RE = Stage<T, NT, C, E>::RS, RM = Stage<T, NT, C, M>::RS;
     constexpr int BUF = 2 * C * RE + 2 * C * RM;
@@ -427,20 +524,22 @@ __global__ __launch_bounds__((bwd_threads<T, E, M, G>())) void cp_bwd_kernel(
     const float *dd_ = dd ? dd + (int64_t)slice * Lpad : nullptr;
     float *ds0 = dstate_in ? dstate_in + (int64_t)slice * E * M : nullptr;
     float *dz0 = dz_in ? dz_in + (int64_t)slice * E : nullptr;
-    const int role = w < EG ? kDQ : w < 2 * EG ? kDK : kDV;
-    const int b = grp + G * (role == kDQ ? w : role == kDK ? w - EG : w - 2 * EG);
+    // wave w: role, and the first of its NB column blocks (b, b + G, ...)
+    const int role = w < EG ? kDQ : w < 2 * EG ? kDK : w < 2 * EG + MG ? kDV : kIdle;
+    const int lw = role == kDQ ? w : role == kDK ? w - EG : w - 2 * EG;
+    const int b = grp + G * NB * lw;
     if (role == kDQ && b < EB)
-        bwd_sweep<T, E, M, C, G, NPF, NORM, FMAP, kDQ>(q_, k_, v_, g_, s0, st, zc_, dd_, Lpad, dQ + oe, nullptr,
-                                                       nullptr, L, b, lds);
+        bwd_sweep<T, E, M, C, G, NB, IDLE, NPF, NORM, FMAP, kDQ>(q_, k_, v_, g_, s0, st, zc_, dd_, Lpad, dQ + oe,
+                                                                 nullptr, nullptr, L, b, lds);
     else if (role == kDK && b < EB)
-        bwd_sweep<T, E, M, C, G, NPF, NORM, FMAP, kDK>(q_, k_, v_, g_, s0, st, zc_, dd_, Lpad, dK + oe, nullptr,
-                                                       dz0, L, b, lds);
+        bwd_sweep<T, E, M, C, G, NB, IDLE, NPF, NORM, FMAP, kDK>(q_, k_, v_, g_, s0, st, zc_, dd_, Lpad, dK + oe,
+                                                                 nullptr, dz0, L, b, lds);
     else if (role == kDV && b < MB)
-        bwd_sweep<T, E, M, C, G, NPF, NORM, FMAP, kDV>(q_, k_, v_, g_, s0, st, zc_, dd_, Lpad, dV + om, ds0,
-                                                       nullptr, L, b, lds);
+        bwd_sweep<T, E, M, C, G, NB, IDLE, NPF, NORM, FMAP, kDV>(q_, k_, v_, g_, s0, st, zc_, dd_, Lpad, dV + om,
+                                                                 ds0, nullptr, L, b, lds);
     else
-        bwd_sweep<T, E, M, C, G, NPF, NORM, FMAP, kIdle>(q_, k_, v_, g_, s0, st, zc_, dd_, Lpad, nullptr,
-                                                         nullptr, nullptr, L, 0, lds);
+        bwd_sweep<T, E, M, C, G, NB, IDLE, NPF, NORM, FMAP, kIdle>(q_, k_, v_, g_, s0, st, zc_, dd_, Lpad,
+                                                                   nullptr, nullptr, nullptr, L, 0, lds);
 }
 
 }  // namespace cp

@@ -9,6 +9,11 @@
 //        chunk's query row blocks,
 //   FNPF, BNPF  stages of the forward / backward load ring (NPF-1 chunks are
 //        in flight while one is computed),
+//   BNB  backward column blocks per wave (1 or 2): a wave with two blocks
+//        reads the chunk's operand tiles and forms its causal tiles once for
+//        both,
+//   BIDLE  extra backward waves that only help copy (a workgroup of three
+//        waves gets a fourth, one per SIMD),
 // Each value can be overridden when the library is built (-DCP_BF16_FC=32 ...)
 // for tuning sweeps.
 #pragma once
@@ -33,6 +38,15 @@
 #endif
 #ifndef CP_BF16_BG
 #define CP_BF16_BG 2
+#endif
+#ifndef CP_BF16_BNB
+#define CP_BF16_BNB 2
+#endif
+#ifndef CP_BF16_BIDLE
+#define CP_BF16_BIDLE -1
+#endif
+#ifndef CP_BF16_NB2_BC
+#define CP_BF16_NB2_BC 32
 #endif
 #ifndef CP_F32_WIDE_FC
 #define CP_F32_WIDE_FC 32
@@ -61,6 +75,14 @@
 
 namespace cp {
 
+// Waves per role in a backward workgroup of group count G with NB column
+// blocks per wave: dQ and dK waves cover the E/16 blocks of E, dV waves the
+// M/16 blocks of M; IDLE more waves only help copy.
+template <int E, int M, int G, int NB, int IDLE>
+constexpr int bwd_waves() {
+    return 2 * ((E / 16 + G * NB - 1) / (G * NB)) + (M / 16 + G * NB - 1) / (G * NB) + IDLE;
+}
+
 // Backward workgroups per slice: the preferred count, at most one per column
 // block, and enough that a workgroup has at most 16 waves.
 constexpr int bwd_groups(int E, int M, int pref) {
@@ -81,11 +103,20 @@ template <int E, int M> struct Tune<__bf16, E, M> {
     // 128 output columns: two workgroups of four waves (registers per wave)
     static constexpr int FG0 = M > 64 && CP_BF16_FG < 2 ? 2 : CP_BF16_FG;
     static constexpr int FG = FG0 > M / 16 ? M / 16 : FG0;
-    static constexpr int BC = wide && CP_BF16_BC > 32 ? 32 : CP_BF16_BC;
+    static constexpr int BC0 = wide && CP_BF16_BC > 32 ? 32 : CP_BF16_BC;
     static constexpr int FRS = FC >= 64 && E <= 64 ? CP_BF16_FRS : 1;  // E = 128: registers
     static constexpr int FNPF = E == 128 && CP_BF16_FNPF > 2 ? 2 : CP_BF16_FNPF;  // E = 128: registers
     static constexpr int BNPF = CP_BF16_BNPF;
     static constexpr int BG = bwd_groups(E, M, CP_BF16_BG);
+    // two blocks per wave where they divide evenly and registers allow; such
+    // waves run shorter chunks (their per-chunk work is twice as long)
+    static constexpr int BNB = CP_BF16_BNB == 2 && E <= 64 && M <= 64 && (E / 16) % (2 * BG) == 0 &&
+                                       (M / 16) % (2 * BG) == 0
+                                   ? 2
+                                   : 1;
+    static constexpr int BC = BNB == 2 ? CP_BF16_NB2_BC : BC0;
+    static constexpr int BIDLE =
+        CP_BF16_BIDLE >= 0 ? CP_BF16_BIDLE : BNB == 2 ? (4 - bwd_waves<E, M, BG, BNB, 0>() % 4) % 4 : 0;
 };
 
 // fp32 tiles are twice as large in LDS and registers: the widest heads use
@@ -100,6 +131,8 @@ template <int E, int M> struct Tune<float, E, M> {
     static constexpr int FNPF = CP_F32_FNPF;
     static constexpr int BNPF = CP_F32_BNPF;
     static constexpr int BG = bwd_groups(E, M, CP_F32_BG);
+    static constexpr int BNB = 1;
+    static constexpr int BIDLE = 0;
 };
 
 }  // namespace cp
