@@ -26,7 +26,7 @@ HBM_PEAK_GBS = 8000.0
 METRIC = "causal-product fwd+bwd tokens·heads/s and % HBM/MFMA roofline, L=4096 E=M=64"
 UNIT = "tokens·heads/s"
 COUNTERS = os.path.join(ROOT, "profiles", "hbm_traffic.json")
-KERNEL_SOURCES = ["cp_device.hpp", "cp_fwd.hpp", "cp_bwd.hpp", "cp_tune.hpp"]
+KERNEL_SOURCES = ("cp_device.hpp", "cp_fwd.hpp", "cp_fwd_launch.hpp", "cp_bwd.hpp", "cp_bwd_launch.hpp", "cp_tune.hpp")
 
 
 def kernel_digest() -> str:
@@ -49,6 +49,10 @@ def algorithmic_bytes(w, kind: str) -> int:
         return th * s * (4 * w.E + 3 * w.M) + state
     if kind == "linattn":
         return th * s * (2 * w.E + 2 * w.M)
+    if kind == "linattn_bwd":
+        # read q, k, v, out, dO and the fp32 denominators (and the final state);
+        # write dq, dk, dv
+        return th * (s * (4 * w.E + 4 * w.M) + 4) + state
     raise ValueError(kind)
 
 
@@ -81,8 +85,10 @@ def cpu_baseline(w, target_seconds: float = 15.0) -> dict:
     slices = 0
     t0 = time.perf_counter()
     while True:
-        if w.op == "linattn":
+        if w.op.startswith("linattn"):
             orc.linattn(d["Q"], d["K"], d["V"], 1e-6, 1)
+            if w.op == "linattn+bwd":
+                orc.linattn_bwd(d["Q"], d["K"], d["V"], d["dO"], 1e-6, 1)
         else:
             orc.fwd(d["Q"], d["K"], d["V"])
             if w.op == "fwd+bwd":
@@ -93,7 +99,7 @@ def cpu_baseline(w, target_seconds: float = 15.0) -> dict:
             break
     return {"value": slices * w.L / el, "unit": UNIT, "cores": threads, "kind": "oracle",
             "sample": f"{slices} (n,h) slices at full L={w.L} ({threads} distinct slices of the workload, "
-                      f"repeated), fp64 recurrence ({'fwd+bwd' if w.op == 'fwd+bwd' else w.op}), "
+                      f"repeated), fp64 recurrence ({w.op}), "
                       f"{el:.1f} s on {threads} threads"}
 
 
@@ -121,23 +127,37 @@ def main() -> int:
     name = args.workload or W.HEADLINE
     w = W.WORKLOADS[name]
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
-    d = W.generate(w, need_do=(w.op == "fwd+bwd"))
+    d = W.generate(w, need_do=w.op.endswith("bwd"))
     dev = {k: torch.from_numpy(v).to("cuda").to(tdt) for k, v in d.items()}
     del d
     q, k, v = dev["Q"], dev["K"], dev["V"]
     out = torch.empty_like(v)
     state = torch.empty((w.N, w.H, w.E, w.M), device="cuda", dtype=torch.float32)
-    if w.op == "fwd+bwd":
+    den = torch.empty((w.N, w.H, w.L), device="cuda", dtype=torch.float32)
+    if w.op.endswith("bwd"):
         g = dev["dO"]
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
 
-    def step():
+    # one step = the calls below, in order; kinds[i] names call i
+    def fwd_call():
         if w.op == "linattn":
             cp.linear_attn_fwd(q, k, v, 1e-6, 1, out=out)
+        elif w.op == "linattn+bwd":
+            cp.linear_attn_fwd(q, k, v, 1e-6, 1, out=out, state_out=state, den_out=den)
         else:
             cp.causal_product_fwd(q, k, v, out=out, state_out=state)
+
+    def bwd_call():
         if w.op == "fwd+bwd":
             cp.causal_product_bwd(q, k, v, g, state_final=state, dq=dq, dk=dk, dv=dv)
+        else:
+            cp.linear_attn_bwd(q, k, v, out, g, den, 1, state_final=state, dq=dq, dk=dk, dv=dv)
+
+    calls = [fwd_call] + ([bwd_call] if w.op.endswith("bwd") else [])
+
+    def step():
+        for c in calls:
+            c()
 
     if args.calibrate_copy_mib:
         n = args.calibrate_copy_mib * (1 << 20) // 4
@@ -151,16 +171,20 @@ def main() -> int:
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    kinds = {"fwd+bwd": ["fwd", "bwd"], "fwd": ["fwd"], "linattn": ["linattn"]}[w.op]
+    kinds = {"fwd+bwd": ["fwd", "bwd"], "fwd": ["fwd"], "linattn": ["linattn"],
+             "linattn+bwd": ["linattn", "linattn_bwd"]}[w.op]
     # Each launch in the timed region carries its own start/end events (the
     # timestamps of its dispatch on the stream it runs on, as a profiler's
     # kernel trace reports them); the whole-step rate is wall time.
     # Launches per call: a forward over few slices is two launches (segment
-    # states, then the sweep); count them on one untimed step.
-    cp.timing_begin(64)
-    step()
-    per_step = len(cp.timing_end())
-    n_first = per_step - (1 if w.op == "fwd+bwd" else 0)
+    # states, then the sweep), the normalised backward three (per-row terms,
+    # z scan, sweep); count them on one untimed step.
+    n_launch = []
+    for c in calls:
+        cp.timing_begin(64)
+        c()
+        n_launch.append(len(cp.timing_end()))
+    per_step = sum(n_launch)
     cp.timing_begin(args.steps * per_step)
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -170,17 +194,20 @@ def main() -> int:
     ms = cp.timing_end()
     assert len(ms) == args.steps * per_step, "every timed launch is recorded"
     # a call's time is the sum of its launches
-    times = {kinds[0]: sum(sum(ms[i * per_step:i * per_step + n_first]) for i in range(args.steps))
-             / args.steps * 1e-3}
-    if w.op == "fwd+bwd":
-        times["bwd"] = sum(ms[i * per_step + n_first] for i in range(args.steps)) / args.steps * 1e-3
+    times, off = {}, 0
+    for kind, nl in zip(kinds, n_launch):
+        times[kind] = sum(sum(ms[i * per_step + off:i * per_step + off + nl]) for i in range(args.steps)) \
+            / args.steps * 1e-3
+        off += nl
     per_kernel = {}
     for kind in kinds:
         b = algorithmic_bytes(w, kind)
-        per_kernel[kind] = {"avg_us": times[kind] * 1e6, "alg_bytes": b, "GBps": b / times[kind] / 1e9}
+        per_kernel[kind] = {"avg_us": times[kind] * 1e6, "alg_bytes": b, "GBps": b / times[kind] / 1e9,
+                            "launches": n_launch[kinds.index(kind)]}
     dom = max(kinds, key=lambda k: times[k])
     achieved = per_kernel[dom]["GBps"]
-    kernel_name = {"fwd": "cp_fwd_kernel", "bwd": "cp_bwd_kernel", "linattn": "cp_fwd_kernel"}[dom]
+    kernel_name = {"fwd": "cp_fwd_kernel", "bwd": "cp_bwd_kernel", "linattn": "cp_fwd_kernel",
+                   "linattn_bwd": "cp_lin_prep_kernel + cp_lin_zscan_kernel + cp_bwd_kernel"}[dom]
     rec = {
         "metric": METRIC,
         "value": args.steps * w.token_heads / elapsed,

@@ -271,7 +271,7 @@ def test_linattn_constant_v(cp):
     assert np.max(np.abs(out - 1.5)) <= 1e-5
 
 
-# -- the five workloads at full size ------------------------------------------------------
+# -- the workloads at full size -----------------------------------------------------------
 
 @pytest.mark.parametrize("name", list(W.WORKLOADS))
 def test_workload_full_size(cp, orc, name):
@@ -280,12 +280,22 @@ def test_workload_full_size(cp, orc, name):
     d = W.generate(w)
     q, k, v = (dev(d[n], w.dtype) for n in "QKV")
     tol = TOL[w.dtype]
-    if w.op == "linattn":
-        out = cp.linear_attn_fwd(q, k, v, 1e-6, 1)
+    if w.op.startswith("linattn"):
+        st = torch.empty((w.N, w.H, w.E, w.M), device="cuda", dtype=torch.float32)
+        den = torch.empty((w.N, w.H, w.L), device="cuda", dtype=torch.float32)
+        out = cp.linear_attn_fwd(q, k, v, 1e-6, 1, state_out=st, den_out=den)
         torch.cuda.synchronize()
         err = oracle.max_rel_err(host(out), orc.linattn(d["Q"], d["K"], d["V"], 1e-6, 1))
         say(f"  linattn err {err:.3e}")
         assert err <= tol
+        if w.op == "linattn+bwd":
+            g = dev(d["dO"], w.dtype)
+            got = cp.linear_attn_bwd(q, k, v, out, g, den, 1, state_final=st)
+            torch.cuda.synchronize()
+            ref = orc.linattn_bwd(d["Q"], d["K"], d["V"], d["dO"], 1e-6, 1)
+            errs = [oracle.max_rel_err(host(a), b) for a, b in zip(got, ref)]
+            say(f"  linattn bwd errs {errs}")
+            assert max(errs) <= tol
         return
     st = torch.empty((w.N, w.H, w.E, w.M), device="cuda", dtype=torch.float32)
     out = cp.causal_product_fwd(q, k, v, state_out=st)

@@ -51,9 +51,10 @@ class Workload:
         return replace(self, **kw)
 
 
-# The five workloads: a tiny fp32 forward, an fp32 forward, the bf16
+# The workloads: a tiny fp32 forward, an fp32 forward, the bf16
 # forward+backward at L=4096 E=M=64 (the headline), bf16 normalised linear
-# attention at L=16384 E=M=128, and an fp32 forward+backward with E != M.
+# attention at L=16384 E=M=128, an fp32 forward+backward with E != M, and the
+# normalised form's forward+backward in bf16 at the headline shape.
 WORKLOADS = {
     w.name: w
     for w in (
@@ -64,6 +65,9 @@ WORKLOADS = {
                  qk="raw"),
         Workload("fwdbwd_f32_l2048_e32_m128", "fwd+bwd", "f32", 16, 12, 2048, 32, 128, seed=4,
                  v_std=0.5, do_std=0.5),
+        # the normalised form's forward and backward at the headline shape
+        Workload("linattn_fwdbwd_bf16_l4096_e64", "linattn+bwd", "bf16", 8, 16, 4096, 64, 64, seed=5,
+                 qk="raw"),
     )
 }
 HEADLINE = "fwdbwd_bf16_l4096_e64"
@@ -113,7 +117,7 @@ def generate(w: Workload, need_do: bool | None = None) -> dict:
         raise ValueError(f"unknown qk recipe {w.qk!r}")
     out = {"Q": to_io(xq, w.dtype), "K": to_io(xk, w.dtype), "V": to_io(v, w.dtype)}
     del xq, xk, v
-    if need_do if need_do is not None else (w.op == "fwd+bwd"):
+    if need_do if need_do is not None else w.op.endswith("bwd"):
         out["dO"] = to_io(rng.standard_normal(v_shape) * w.do_std, w.dtype)
     return out
 
