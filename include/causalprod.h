@@ -22,9 +22,15 @@
  * ---------------------------------------
  *  * Tensors are contiguous and row-major: Q, K, dQ, dK are [N][H][L][E];
  *    V, Out, dOut, dV are [N][H][L][M].  One element type per call (dtype):
- *    CP_F32 (fp32 in and out) or CP_BF16 (bf16 in and out).  Arithmetic
- *    accumulates in fp32 in both cases; results are rounded once to the I/O
- *    type (round to nearest even).
+ *    CP_F32 (fp32 in and out), CP_BF16 (bf16 in and out) or CP_F16 (IEEE
+ *    half in and out).  Arithmetic accumulates in fp32 in every case; results
+ *    are rounded once to the I/O type (round to nearest even).  With the
+ *    16-bit types the carried states and the chunk's score tiles enter the
+ *    matrix products rounded to the I/O type, so with CP_F16 every such value
+ *    (and every output) must stay within half's range (|x| < 65504): the
+ *    library does not check this.  linear_attn_bwd does not take CP_F16
+ *    (CP_ERR_UNSUPPORTED): its per-row terms dOut_i / den_i fall below half's
+ *    normal range once den_i (which grows like E * L) is large.
  *  * All tensor pointers are DEVICE pointers owned by the caller, 16-byte
  *    aligned.  Outputs are fully overwritten (they need not be zeroed) and
  *    must not overlap any input or each other.  States are fp32: S as
@@ -53,7 +59,7 @@
 extern "C" {
 #endif
 
-typedef enum { CP_F32 = 0, CP_BF16 = 1 } cp_dtype;
+typedef enum { CP_F32 = 0, CP_BF16 = 1, CP_F16 = 2 } cp_dtype;
 
 typedef enum {
     CP_OK = 0,

@@ -15,7 +15,8 @@ and autograd wrappers ``causal_product(q, k, v)`` and
 ``linear_attention(q, k, v, eps=1e-6, feature_map="elu+1")``.
 
 Tensors are [N, H, L, E] (q, k) and [N, H, L, M] (v), contiguous, on the GPU,
-all float32 or all bfloat16, with E, M in {16, 32, 64, 128}.
+all float32, all bfloat16 or all float16 (float16: not for the normalised
+backward), with E, M in {16, 32, 64, 128}.
 """
 from __future__ import annotations
 
@@ -29,7 +30,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 # with other tuning parameters by build.build(out=..., defines=...)).
 LIB_PATH = os.environ.get("CAUSALPROD_LIB") or os.path.join(HERE, "libcausalprod.so")
 
-CP_F32, CP_BF16 = 0, 1
+CP_F32, CP_BF16, CP_F16 = 0, 1, 2
 STATUS = {0: "CP_OK", 1: "CP_ERR_NULL", 2: "CP_ERR_DIM", 3: "CP_ERR_UNSUPPORTED", 4: "CP_ERR_ALIGN",
           5: "CP_ERR_ALIAS", 6: "CP_ERR_HIP"}
 SUPPORTED_HEAD_SIZES = (16, 32, 64, 128)
@@ -74,7 +75,9 @@ def _dtype_code(t: torch.Tensor) -> int:
         return CP_F32
     if t.dtype == torch.bfloat16:
         return CP_BF16
-    raise TypeError(f"unsupported dtype {t.dtype}; use float32 or bfloat16")
+    if t.dtype == torch.float16:
+        return CP_F16
+    raise TypeError(f"unsupported dtype {t.dtype}; use float32, bfloat16 or float16")
 
 
 def _dims(q: torch.Tensor, v: torch.Tensor):

@@ -20,7 +20,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libcausalprod.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 
-SOURCES = ["cp_api.cpp", "cp_fwd_f32.hip", "cp_fwd_bf16.hip", "cp_bwd_f32.hip", "cp_bwd_bf16.hip"]
+SOURCES = ["cp_api.cpp", "cp_fwd_f32.hip", "cp_fwd_bf16.hip", "cp_fwd_f16.hip", "cp_bwd_f32.hip", "cp_bwd_bf16.hip",
+           "cp_bwd_f16.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -17,7 +17,7 @@
 
 namespace {
 
-constexpr int kAbiMajor = 3, kAbiMinor = 0;  // 3.0: carried state, normalised backward
+constexpr int kAbiMajor = 3, kAbiMinor = 1;  // 3.0: carried state, normalised backward; 3.1: fp16 I/O
 
 struct Range {
     uintptr_t lo, hi;  // [lo, hi)
@@ -32,7 +32,7 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 int check_dims(int64_t N, int64_t H, int64_t L, int64_t E, int64_t M, int dtype, int parts_per_slice_max,
                int64_t &ne, int64_t &nm) {
     if (N <= 0 || H <= 0 || L <= 0 || E <= 0 || M <= 0) return CP_ERR_DIM;
-    if (dtype != CP_F32 && dtype != CP_BF16) return CP_ERR_UNSUPPORTED;
+    if (dtype != CP_F32 && dtype != CP_BF16 && dtype != CP_F16) return CP_ERR_UNSUPPORTED;
     if (cp::size_index(E) < 0 || cp::size_index(M) < 0) return CP_ERR_UNSUPPORTED;
     if (L > INT32_MAX) return CP_ERR_DIM;
     // N*H slices, each launched as up to parts_per_slice_max workgroups
@@ -77,6 +77,14 @@ int check_alias(std::initializer_list<Range> ins, std::initializer_list<Range> o
 Range span(const void *p, int64_t bytes) {
     const uintptr_t a = reinterpret_cast<uintptr_t>(p);
     return p ? Range{a, a + static_cast<uintptr_t>(bytes)} : Range{0, 0};
+}
+
+cp::fwd_fn pick_fwd(int dtype, int E, int M, bool norm) {
+    return dtype == CP_BF16 ? cp::fwd_bf16(E, M, norm) : dtype == CP_F16 ? cp::fwd_f16(E, M, norm) : cp::fwd_f32(E, M, norm);
+}
+
+cp::bwd_fn pick_bwd(int dtype, int E, int M, bool norm) {
+    return dtype == CP_BF16 ? cp::bwd_bf16(E, M, norm) : dtype == CP_F16 ? cp::bwd_f16(E, M, norm) : cp::bwd_f32(E, M, norm);
 }
 
 int launch_status(hipError_t e) { return e == hipSuccess ? CP_OK : CP_ERR_HIP; }
@@ -175,12 +183,12 @@ int causal_product_fwd(const void *Q, const void *K, const void *V, void *Out, c
     if (st != CP_OK) return st;
     st = check_opt_ptrs({state_in, state_out});
     if (st != CP_OK) return st;
-    const int64_t es = dtype == CP_BF16 ? 2 : 4, ns = N * H * E * M * 4;
+    const int64_t es = dtype == CP_F32 ? 4 : 2, ns = N * H * E * M * 4;
     st = check_alias({span(Q, ne * es), span(K, ne * es), span(V, nm * es), span(state_in, ns)},
                      {span(Out, nm * es), span(state_out, ns)});
     if (st != CP_OK) return st;
 
-    cp::fwd_fn fn = dtype == CP_BF16 ? cp::fwd_bf16((int)E, (int)M, false) : cp::fwd_f32((int)E, (int)M, false);
+    cp::fwd_fn fn = pick_fwd(dtype, (int)E, (int)M, false);
     if (!fn) return CP_ERR_UNSUPPORTED;
     cp::FwdArgs a{Q, K, V, Out, state_in, nullptr, state_out, nullptr, nullptr, (int)L, (int)(N * H), 0.f, 0};
     return launch_status(fn(a, static_cast<hipStream_t>(stream)));
@@ -196,13 +204,13 @@ int causal_product_bwd(const void *Q, const void *K, const void *V, const void *
     if (st != CP_OK) return st;
     st = check_opt_ptrs({state_in, state_final, dstate_in});
     if (st != CP_OK) return st;
-    const int64_t es = dtype == CP_BF16 ? 2 : 4, ns = N * H * E * M * 4;
+    const int64_t es = dtype == CP_F32 ? 4 : 2, ns = N * H * E * M * 4;
     st = check_alias({span(Q, ne * es), span(K, ne * es), span(V, nm * es), span(dOut, nm * es),
                       span(state_in, ns), span(state_final, ns)},
                      {span(dQ, ne * es), span(dK, ne * es), span(dV, nm * es), span(dstate_in, ns)});
     if (st != CP_OK) return st;
 
-    cp::bwd_fn fn = dtype == CP_BF16 ? cp::bwd_bf16((int)E, (int)M, false) : cp::bwd_f32((int)E, (int)M, false);
+    cp::bwd_fn fn = pick_bwd(dtype, (int)E, (int)M, false);
     if (!fn) return CP_ERR_UNSUPPORTED;
     cp::BwdArgs a{Q,   K,    V,       dOut,    state_in, state_final, dQ, dK, dV, dstate_in, (int)L, (int)(N * H),
                   nullptr, nullptr, nullptr, nullptr, 0};
@@ -221,12 +229,12 @@ int linear_attn_fwd(const void *Q, const void *K, const void *V, void *Out, cons
     if (st != CP_OK) return st;
     st = check_opt_ptrs({state_in, z_in, state_out, z_out, den_out});
     if (st != CP_OK) return st;
-    const int64_t es = dtype == CP_BF16 ? 2 : 4, ns = N * H * E * M * 4, nz = N * H * E * 4, nd = N * H * L * 4;
+    const int64_t es = dtype == CP_F32 ? 4 : 2, ns = N * H * E * M * 4, nz = N * H * E * 4, nd = N * H * L * 4;
     st = check_alias({span(Q, ne * es), span(K, ne * es), span(V, nm * es), span(state_in, ns), span(z_in, nz)},
                      {span(Out, nm * es), span(state_out, ns), span(z_out, nz), span(den_out, nd)});
     if (st != CP_OK) return st;
 
-    cp::fwd_fn fn = dtype == CP_BF16 ? cp::fwd_bf16((int)E, (int)M, true) : cp::fwd_f32((int)E, (int)M, true);
+    cp::fwd_fn fn = pick_fwd(dtype, (int)E, (int)M, true);
     if (!fn) return CP_ERR_UNSUPPORTED;
     cp::FwdArgs a{Q, K, V, Out, state_in, z_in, state_out, z_out, den_out, (int)L, (int)(N * H), eps, feature_map};
     return launch_status(fn(a, static_cast<hipStream_t>(stream)));
@@ -244,14 +252,14 @@ int linear_attn_bwd(const void *Q, const void *K, const void *V, const void *Out
     if (st != CP_OK) return st;
     st = check_opt_ptrs({state_in, z_in, state_final, dstate_in, dz_in});
     if (st != CP_OK) return st;
-    const int64_t es = dtype == CP_BF16 ? 2 : 4, ns = N * H * E * M * 4, nz = N * H * E * 4, nd = N * H * L * 4;
+    const int64_t es = dtype == CP_F32 ? 4 : 2, ns = N * H * E * M * 4, nz = N * H * E * 4, nd = N * H * L * 4;
     st = check_alias({span(Q, ne * es), span(K, ne * es), span(V, nm * es), span(Out, nm * es), span(dOut, nm * es),
                       span(den, nd), span(state_in, ns), span(z_in, nz), span(state_final, ns)},
                      {span(dQ, ne * es), span(dK, ne * es), span(dV, nm * es), span(dstate_in, ns),
                       span(dz_in, nz)});
     if (st != CP_OK) return st;
 
-    cp::bwd_fn fn = dtype == CP_BF16 ? cp::bwd_bf16((int)E, (int)M, true) : cp::bwd_f32((int)E, (int)M, true);
+    cp::bwd_fn fn = pick_bwd(dtype, (int)E, (int)M, true);
     if (!fn) return CP_ERR_UNSUPPORTED;
     cp::BwdArgs a{Q, K,    V,       dOut,    state_in, state_final, dQ, dK, dV, dstate_in, (int)L, (int)(N * H),
                   Out, den, z_in, dz_in, feature_map};

@@ -1,5 +1,5 @@
 // cp_bwd_launch.hpp -- host side of the backward launches (causal product and
-// normalised form), shared by the bf16 and fp32 translation units.
+// normalised form), shared by the bf16, fp16 and fp32 translation units.
 #pragma once
 
 #include <algorithm>

@@ -5,6 +5,7 @@
 // Lane l of a 64-lane wave is split into g = l / 16 (0..3) and r = l % 16.
 // All matrix products are 16 x 16 output tiles D += A * B computed by MFMA:
 //   bf16 I/O: v_mfma_f32_16x16x32_bf16 (A 16x32, B 32x16, fp32 accumulate)
+//   fp16 I/O: v_mfma_f32_16x16x32_f16 (same shapes and lane layouts)
 //   fp32 I/O: the same MFMA on split hi + lo bf16 operands (see Ops<float>),
 //             or v_mfma_f32_16x16x4_f32 (A 16x4, B 4x16)
 // with these lane layouts (checked on gfx950):
@@ -57,22 +58,49 @@ __device__ __forceinline__ f32x4 zero4() {
 
 template <typename T> struct Ops;
 
-// bf16 I/O: fragments are 4 bf16; MFMA over two k-blocks at a time.
-template <> struct Ops<bf16> {
-    using frag = bf16x4;
+typedef _Float16 f16;
+typedef f16 f16x4 __attribute__((__vector_size__(4 * sizeof(f16))));
+typedef f16 f16x8 __attribute__((__vector_size__(8 * sizeof(f16))));
+
+// The two 16-bit I/O types: their fragment vectors and MFMA (16x16x32, fp32
+// accumulate).  Everything else about them is the same.
+template <typename H> struct Half16;
+template <> struct Half16<bf16> {
+    using x4 = bf16x4;
+    using x8 = bf16x8;
+    static constexpr short one = 0x3F80;  // 1.0
+    __device__ static __forceinline__ f32x4 mfma(x8 a, x8 b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    }
+};
+template <> struct Half16<f16> {
+    using x4 = f16x4;
+    using x8 = f16x8;
+    static constexpr short one = 0x3C00;  // 1.0
+    __device__ static __forceinline__ f32x4 mfma(x8 a, x8 b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+    }
+};
+
+// 16-bit I/O (bf16 or fp16): fragments are 4 values; MFMA over two k-blocks
+// at a time.
+template <typename H> struct Ops16 {
+    using frag = typename Half16<H>::x4;
+    using frag8 = typename Half16<H>::x8;
 
     __device__ static __forceinline__ frag zero() {
         s16x4 z = {0, 0, 0, 0};
         return __builtin_bit_cast(frag, z);
     }
     __device__ static __forceinline__ frag ones() {
-        s16x4 o = {0x3F80, 0x3F80, 0x3F80, 0x3F80};
+        constexpr short o1 = Half16<H>::one;
+        s16x4 o = {o1, o1, o1, o1};
         return __builtin_bit_cast(frag, o);
     }
     __device__ static __forceinline__ void mma2(f32x4 &acc, frag a0, frag a1, frag b0, frag b1) {
-        bf16x8 a = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
-        bf16x8 b = __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+        frag8 a = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
+        frag8 b = __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7);
+        acc = Half16<H>::mfma(a, b, acc);
     }
     __device__ static __forceinline__ void mma1(f32x4 &acc, frag a0, frag b0) {
         mma2(acc, a0, zero(), b0, zero());
@@ -80,15 +108,16 @@ template <> struct Ops<bf16> {
     __device__ static __forceinline__ frag cvt(f32x4 x) {
         frag f;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) f[t] = (bf16)x[t];
+        for (int t = 0; t < 4; ++t) f[t] = (H)x[t];
         return f;
     }
-    // x ~= hi + lo with both halves in bf16 (16 significant bits in total).
+    // x ~= hi + lo with both halves in the 16-bit type (bf16: 16 significant
+    // bits in total; fp16: 22, within its exponent range).
     __device__ static __forceinline__ void split(f32x4 x, frag &hi, frag &lo) {
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            hi[t] = (bf16)x[t];
-            lo[t] = (bf16)(x[t] - (float)hi[t]);
+            hi[t] = (H)x[t];
+            lo[t] = (H)(x[t] - (float)hi[t]);
         }
     }
     __device__ static __forceinline__ frag neg(frag a) {
@@ -98,14 +127,16 @@ template <> struct Ops<bf16> {
     }
     // lane (g, r) <- X[16 tb + 4g + t][16 cb + r] from a natural LDS copy
     // with row stride rs (elements).
-    __device__ static __forceinline__ frag tr_frag(const bf16 *lds, int rs, int tb, int cb) {
+    __device__ static __forceinline__ frag tr_frag(const H *lds, int rs, int tb, int cb) {
         const int g = lane_g(), i = lane_r();
-        const bf16 *p = lds + (16 * tb + 4 * g + (i >> 2)) * rs + 16 * cb + 4 * (i & 3);
+        const H *p = lds + (16 * tb + 4 * g + (i >> 2)) * rs + 16 * cb + 4 * (i & 3);
         s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (lds_s16x4 *)((__attribute__((address_space(3))) char *)(p)));
         return __builtin_bit_cast(frag, v);
     }
 };
+template <> struct Ops<bf16> : Ops16<bf16> {};
+template <> struct Ops<f16> : Ops16<f16> {};
 
 // fp32 I/O: fragments are 4 floats.  Products run as split bf16 by default
 // (CP_F32_SPLIT): each fp32 operand x is cut into hi = bf16(x) and
@@ -347,57 +378,60 @@ struct Diag {
 // those tiles.
 template <typename T, int E> struct EOps;
 
-template <int E> struct EOps<bf16, E> {
+template <typename H, int E> struct EOps16 {
     static constexpr bool SPLIT_STATE = true;  // states enter as hi + lo bf16 pairs where accuracy needs it
     static constexpr int EB = E / 16;
     static constexpr bool WIDE = EB >= 2;
     static constexpr int STEPS = WIDE ? EB / 2 : 1;
     static constexpr int estride = WIDE ? 8 : 4;
-    using rf = typename std::conditional<WIDE, bf16x8, bf16x4>::type;
+    using x4 = typename Half16<H>::x4;
+    using rf = typename std::conditional<WIDE, typename Half16<H>::x8, x4>::type;
 
     __device__ static __forceinline__ int ecol(int eb) { return WIDE ? 32 * (eb >> 1) + 4 * (eb & 1) : 16 * eb; }
     // lane (g, r) <- X[16 rb + r][features of step s]
-    __device__ static __forceinline__ rf load(const bf16 *lds, int rs, int rb, int s) {
-        const bf16 *p = lds + (16 * rb + lane_r()) * rs + (WIDE ? 32 * s : 0) + estride * lane_g();
+    __device__ static __forceinline__ rf load(const H *lds, int rs, int rb, int s) {
+        const H *p = lds + (16 * rb + lane_r()) * rs + (WIDE ? 32 * s : 0) + estride * lane_g();
         return *reinterpret_cast<const rf *>(p);
     }
     __device__ static __forceinline__ void mma(f32x4 &acc, rf a, rf b) {
         if constexpr (WIDE) {
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+            acc = Half16<H>::mfma(a, b, acc);
         } else {
-            Ops<bf16>::mma1(acc, a, b);
+            Ops16<H>::mma1(acc, a, b);
         }
     }
     // operand of step s from the state tiles
     __device__ static __forceinline__ rf state(const f32x4 *tiles, int s) {
         if constexpr (WIDE) {
-            const bf16x4 lo = Ops<bf16>::cvt(tiles[2 * s]), hi = Ops<bf16>::cvt(tiles[2 * s + 1]);
+            const x4 lo = Ops16<H>::cvt(tiles[2 * s]), hi = Ops16<H>::cvt(tiles[2 * s + 1]);
             return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         } else {
-            return Ops<bf16>::cvt(tiles[0]);
+            return Ops16<H>::cvt(tiles[0]);
         }
     }
     __device__ static __forceinline__ void state_split(const f32x4 *tiles, int s, rf &hi, rf &lo) {
         if constexpr (WIDE) {
-            bf16x4 h0, l0, h1, l1;
-            Ops<bf16>::split(tiles[2 * s], h0, l0);
-            Ops<bf16>::split(tiles[2 * s + 1], h1, l1);
+            x4 h0, l0, h1, l1;
+            Ops16<H>::split(tiles[2 * s], h0, l0);
+            Ops16<H>::split(tiles[2 * s + 1], h1, l1);
             hi = __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7);
             lo = __builtin_shufflevector(l0, l1, 0, 1, 2, 3, 4, 5, 6, 7);
         } else {
-            Ops<bf16>::split(tiles[0], hi, lo);
+            Ops16<H>::split(tiles[0], hi, lo);
         }
     }
     // lane (g, r) <- X[16 tb + 4g + t][ecol(eb) + estride * (r / 4) + r % 4]:
     // K^T fragment (rows e in state-tile order, k = tokens of block tb).
-    __device__ static __forceinline__ bf16x4 tr_e(const bf16 *lds, int rs, int tb, int eb) {
+    __device__ static __forceinline__ x4 tr_e(const H *lds, int rs, int tb, int eb) {
         const int g = lane_g(), i = lane_r();
-        const bf16 *p = lds + (16 * tb + 4 * g + (i >> 2)) * rs + ecol(eb) + estride * (i & 3);
+        const H *p = lds + (16 * tb + 4 * g + (i >> 2)) * rs + ecol(eb) + estride * (i & 3);
         s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (lds_s16x4 *)((__attribute__((address_space(3))) char *)(p)));
-        return __builtin_bit_cast(bf16x4, v);
+        return __builtin_bit_cast(x4, v);
     }
 };
+template <int E> struct EOps<bf16, E> : EOps16<bf16, E> {};
+template <int E> struct EOps<f16, E> : EOps16<f16, E> {};
 
 template <int E> struct EOps<float, E> {
     static constexpr int EB = E / 16;

@@ -1,0 +1,8 @@
+// Forward and normalised-forward kernel instances, fp16 I/O.
+#include "cp_fwd_launch.hpp"
+
+namespace cp {
+
+fwd_fn fwd_f16(int E, int M, bool norm) { return norm ? pick_fwd<_Float16, true>(E, M) : pick_fwd<_Float16, false>(E, M); }
+
+}  // namespace cp

@@ -1,5 +1,5 @@
 // cp_fwd_launch.hpp -- host side of the forward and normalised-forward
-// launches, shared by the bf16 and fp32 translation units.
+// launches, shared by the bf16, fp16 and fp32 translation units.
 #pragma once
 
 #include "cp_fwd.hpp"

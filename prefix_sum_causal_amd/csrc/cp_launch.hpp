@@ -41,8 +41,10 @@ typedef hipError_t (*bwd_fn)(const BwdArgs &, hipStream_t);
 
 fwd_fn fwd_f32(int E, int M, bool norm);
 fwd_fn fwd_bf16(int E, int M, bool norm);
+fwd_fn fwd_f16(int E, int M, bool norm);
 bwd_fn bwd_f32(int E, int M, bool norm);
 bwd_fn bwd_bf16(int E, int M, bool norm);
+bwd_fn bwd_f16(int E, int M, bool norm);
 
 // Launch a kernel on stream: hipLaunchKernel, or, while the calling thread
 // has a timing in progress (cp_timing_begin), hipExtLaunchKernel with the

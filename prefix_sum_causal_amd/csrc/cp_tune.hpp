@@ -12,8 +12,8 @@
 //   BNB  backward column blocks per wave (1 or 2): a wave with two blocks
 //        reads the chunk's operand tiles and forms its causal tiles once for
 //        both,
-//   BIDLE  extra backward waves that only help copy (a workgroup of three
-//        waves gets a fourth, one per SIMD),
+//   BIDLE  extra backward waves that only help copy, for two-block waves (by
+//        default a workgroup of three waves gets a fourth, one per SIMD),
 // Each value can be overridden when the library is built (-DCP_BF16_FC=32 ...)
 // for tuning sweeps.
 #pragma once
@@ -116,8 +116,11 @@ template <int E, int M> struct Tune<__bf16, E, M> {
                                    : 1;
     static constexpr int BC = BNB == 2 ? CP_BF16_NB2_BC : BC0;
     static constexpr int BIDLE =
-        CP_BF16_BIDLE >= 0 ? CP_BF16_BIDLE : BNB == 2 ? (4 - bwd_waves<E, M, BG, BNB, 0>() % 4) % 4 : 0;
+        BNB != 2 ? 0 : CP_BF16_BIDLE >= 0 ? CP_BF16_BIDLE : (4 - bwd_waves<E, M, BG, BNB, 0>() % 4) % 4;
 };
+
+// fp16 I/O moves and computes exactly like bf16 I/O.
+template <int E, int M> struct Tune<_Float16, E, M> : Tune<__bf16, E, M> {};
 
 // fp32 tiles are twice as large in LDS and registers: the widest heads use
 // shorter chunks.

@@ -54,7 +54,7 @@ def test_status_strings_and_version(lib):
         assert msg and msg not in seen
         seen.add(msg)
     assert lib.cp_status_string(99).decode() == "unknown status"
-    assert lib.cp_abi_version() == (3 << 16)
+    assert lib.cp_abi_version() == (3 << 16) | 1
 
 
 def test_timing_rejects_bad_arguments_before_any_device_call(lib):
@@ -125,7 +125,7 @@ def test_unsupported_head_sizes(lib, E, M):
 
 
 def test_unsupported_dtype_flag_eps(lib):
-    assert fwd(lib, dtype=2) == UNSUP
+    assert fwd(lib, dtype=3) == UNSUP
     assert bwd(lib, dtype=-1) == UNSUP
     assert lin(lib, fm=2) == UNSUP
     assert lin(lib, eps=-1e-3) == UNSUP
@@ -171,6 +171,7 @@ def test_linear_attn_bwd_validation(lib):
     assert linb(lib, shape=(2, 3, 100, 48, 32)) == UNSUP
     assert linb(lib, fm=3) == UNSUP
     assert linb(lib, dtype=5) == UNSUP
+    assert linb(lib, dtype=2) == UNSUP            # no fp16 normalised backward
     assert linb(lib, den=A[5] + 4) == ALIGN
     assert linb(lib, dz0=A[9] + 8) == ALIGN
     assert linb(lib, dq=A[0]) == ALIAS            # dq overlaps q
@@ -178,3 +179,9 @@ def test_linear_attn_bwd_validation(lib):
     assert linb(lib, ds0=A[9], s0=A[9]) == ALIAS  # gradient over its own state
     assert lin(lib, den=A[3]) == ALIAS            # den_out overlaps out
     assert lin(lib, den=A[5] + 4) == ALIGN
+
+
+def test_f16_aliasing_uses_two_byte_elements(lib):
+    # SHAPE fp16: q is 2*3*100*64*2 = 76800 bytes, as bf16
+    assert fwd(lib, o=A[1] + 76800 - 16, dtype=2) == ALIAS
+    assert bwd(lib, dq=A[5], dtype=2) == ALIAS

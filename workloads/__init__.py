@@ -28,7 +28,7 @@ import numpy as np
 class Workload:
     name: str
     op: str            # "fwd", "fwd+bwd" or "linattn"
-    dtype: str         # "f32" or "bf16"
+    dtype: str         # "f32", "bf16" or "f16"
     N: int
     H: int
     L: int
@@ -88,10 +88,13 @@ def round_bf16(x: np.ndarray) -> np.ndarray:
 
 
 def to_io(x64: np.ndarray, dtype: str) -> np.ndarray:
-    """float64 -> float32, then to bf16 values when dtype == "bf16"."""
+    """float64 -> float32, then to bf16 values when dtype == "bf16", or to IEEE
+    half values when dtype == "f16" (numpy's round to nearest even)."""
     x = np.asarray(x64, dtype=np.float64).astype(np.float32)
     if dtype == "bf16":
         return round_bf16(x)
+    if dtype == "f16":
+        return x.astype(np.float16).astype(np.float32)
     if dtype != "f32":
         raise ValueError(f"unknown dtype {dtype!r}")
     return x
