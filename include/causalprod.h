@@ -45,7 +45,12 @@
  *    work: they never synchronise the host, and buffers must stay alive until
  *    the stream has run the work.  Calls are stateless, thread-safe and
  *    deterministic (no atomics; the same inputs give the same bits).
- *  * Supported head sizes: E, M in {16, 32, 64, 128}.  Any L >= 1.
+ *  * Head sizes: 1 <= E, M <= 128 with rows of whole 16-byte pieces, i.e.
+ *    multiples of 8 for the 16-bit types and of 4 for CP_F32.  The kernels
+ *    run in tiles of 16, 32, 64 or 128 features: a head is computed on the
+ *    smallest tile that holds it, its padding columns are read as zero and
+ *    are never written (so E = 80 costs the arithmetic of E = 128 but only
+ *    its own memory traffic).  Any L >= 1.
  *  * Errors are returned as cp_status values, never thrown.  Arguments are
  *    validated before anything is enqueued, so a call that fails validation
  *    has no side effect.  CP_ERR_HIP reports a failed kernel launch.
@@ -65,7 +70,7 @@ typedef enum {
     CP_OK = 0,
     CP_ERR_NULL = 1,        /* a required pointer is NULL                     */
     CP_ERR_DIM = 2,         /* a size <= 0, L > 2^31-1, or a size overflow    */
-    CP_ERR_UNSUPPORTED = 3, /* E or M not in {16,32,64,128}, bad dtype/flag   */
+    CP_ERR_UNSUPPORTED = 3, /* E or M > 128 or rows not 16-byte pieces, bad dtype/flag */
     CP_ERR_ALIGN = 4,       /* a pointer not 16-byte aligned                  */
     CP_ERR_ALIAS = 5,       /* an output overlaps an input or another output  */
     CP_ERR_HIP = 6          /* the HIP runtime reported an error at launch    */

@@ -16,7 +16,8 @@ and autograd wrappers ``causal_product(q, k, v)`` and
 
 Tensors are [N, H, L, E] (q, k) and [N, H, L, M] (v), contiguous, on the GPU,
 all float32, all bfloat16 or all float16 (float16: not for the normalised
-backward), with E, M in {16, 32, 64, 128}.
+backward), with head sizes E, M <= 128 whose rows are whole 16-byte pieces
+(multiples of 8 for the 16-bit types, of 4 for float32).
 """
 from __future__ import annotations
 
@@ -33,7 +34,9 @@ LIB_PATH = os.environ.get("CAUSALPROD_LIB") or os.path.join(HERE, "libcausalprod
 CP_F32, CP_BF16, CP_F16 = 0, 1, 2
 STATUS = {0: "CP_OK", 1: "CP_ERR_NULL", 2: "CP_ERR_DIM", 3: "CP_ERR_UNSUPPORTED", 4: "CP_ERR_ALIGN",
           5: "CP_ERR_ALIAS", 6: "CP_ERR_HIP"}
-SUPPORTED_HEAD_SIZES = (16, 32, 64, 128)
+# Kernel tile sizes: a head of E (or M) features runs on the smallest tile >= E,
+# its padding columns read as zero and never stored.
+TILE_SIZES = (16, 32, 64, 128)
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with `python -m prefix_sum_causal_amd.build`")

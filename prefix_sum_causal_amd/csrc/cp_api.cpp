@@ -33,7 +33,10 @@ int check_dims(int64_t N, int64_t H, int64_t L, int64_t E, int64_t M, int dtype,
                int64_t &ne, int64_t &nm) {
     if (N <= 0 || H <= 0 || L <= 0 || E <= 0 || M <= 0) return CP_ERR_DIM;
     if (dtype != CP_F32 && dtype != CP_BF16 && dtype != CP_F16) return CP_ERR_UNSUPPORTED;
-    if (cp::size_index(E) < 0 || cp::size_index(M) < 0) return CP_ERR_UNSUPPORTED;
+    // head sizes up to 128 whose rows are whole 16-byte pieces
+    const int64_t es = dtype == CP_F32 ? 4 : 2;
+    if (cp::tile_index(E) < 0 || cp::tile_index(M) < 0 || (E * es) % 16 != 0 || (M * es) % 16 != 0)
+        return CP_ERR_UNSUPPORTED;
     if (L > INT32_MAX) return CP_ERR_DIM;
     // N*H slices, each launched as up to parts_per_slice_max workgroups
     if (N > INT32_MAX / H) return CP_ERR_DIM;
@@ -165,7 +168,7 @@ const char *cp_status_string(int status) {
         case CP_OK: return "success";
         case CP_ERR_NULL: return "a required pointer is NULL";
         case CP_ERR_DIM: return "invalid size: N, H, L, E, M must be > 0, L <= 2^31-1, and the sizes must not overflow";
-        case CP_ERR_UNSUPPORTED: return "unsupported argument: E and M must be in {16, 32, 64, 128}; dtype, feature_map or eps out of range";
+        case CP_ERR_UNSUPPORTED: return "unsupported argument: E and M must be at most 128 with rows of whole 16-byte pieces (multiples of 8 for 16-bit types, of 4 for fp32); dtype, feature_map or eps out of range";
         case CP_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
         case CP_ERR_ALIAS: return "an output overlaps an input or another output";
         case CP_ERR_HIP: return "the HIP runtime reported an error when launching the kernel";
@@ -190,7 +193,8 @@ int causal_product_fwd(const void *Q, const void *K, const void *V, void *Out, c
 
     cp::fwd_fn fn = pick_fwd(dtype, (int)E, (int)M, false);
     if (!fn) return CP_ERR_UNSUPPORTED;
-    cp::FwdArgs a{Q, K, V, Out, state_in, nullptr, state_out, nullptr, nullptr, (int)L, (int)(N * H), 0.f, 0};
+    cp::FwdArgs a{Q,      K,      V, Out, state_in, nullptr, state_out, nullptr, nullptr, (int)L, (int)(N * H), 0.f,
+                  0,      (int)E, (int)M};
     return launch_status(fn(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -213,7 +217,7 @@ int causal_product_bwd(const void *Q, const void *K, const void *V, const void *
     cp::bwd_fn fn = pick_bwd(dtype, (int)E, (int)M, false);
     if (!fn) return CP_ERR_UNSUPPORTED;
     cp::BwdArgs a{Q,   K,    V,       dOut,    state_in, state_final, dQ, dK, dV, dstate_in, (int)L, (int)(N * H),
-                  nullptr, nullptr, nullptr, nullptr, 0};
+                  nullptr, nullptr, nullptr, nullptr, 0, (int)E, (int)M};
     return launch_status(fn(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -236,7 +240,8 @@ int linear_attn_fwd(const void *Q, const void *K, const void *V, void *Out, cons
 
     cp::fwd_fn fn = pick_fwd(dtype, (int)E, (int)M, true);
     if (!fn) return CP_ERR_UNSUPPORTED;
-    cp::FwdArgs a{Q, K, V, Out, state_in, z_in, state_out, z_out, den_out, (int)L, (int)(N * H), eps, feature_map};
+    cp::FwdArgs a{Q,           K,      V,     Out, state_in, z_in, state_out, z_out, den_out, (int)L, (int)(N * H), eps,
+                  feature_map, (int)E, (int)M};
     return launch_status(fn(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -262,7 +267,7 @@ int linear_attn_bwd(const void *Q, const void *K, const void *V, const void *Out
     cp::bwd_fn fn = pick_bwd(dtype, (int)E, (int)M, true);
     if (!fn) return CP_ERR_UNSUPPORTED;
     cp::BwdArgs a{Q, K,    V,       dOut,    state_in, state_final, dQ, dK, dV, dstate_in, (int)L, (int)(N * H),
-                  Out, den, z_in, dz_in, feature_map};
+                  Out, den, z_in, dz_in, feature_map, (int)E, (int)M};
     return launch_status(fn(a, static_cast<hipStream_t>(stream)));
 }
 

@@ -45,6 +45,12 @@ namespace cp {
 
 enum BwdRole { kDQ = 0, kDK = 1, kDV = 2, kIdle = 3 };
 
+// Entry (e, m) of an fp32 [Ea][Ma] state; zero in the padding of a narrower
+// head (e >= Ea or m >= Ma).
+__device__ __forceinline__ float state_at(const float *s, int e, int m, int Ea, int Ma) {
+    return e < Ea && m < Ma ? s[e * Ma + m] : 0.f;
+}
+
 // A k-contraction into NB accumulators that share one operand: acc(x) is the
 // x-th accumulator; fs(i) the shared operand (read once), fo(x, i) the x-th
 // own operand.  SHARED_A puts the shared operand on the A side.
@@ -79,7 +85,7 @@ __device__ __forceinline__ void dotk_shared(FACC acc, int b0, int b1, FS fs, FO 
 template <typename T, int E, int M, int C, int G, int NB, int IDLE, int NPF, bool NORM, bool FMAP, int ROLE>
 __device__ __forceinline__ void bwd_sweep(const T *q_, const T *k_, const T *v_, const T *g_, const float *s0,
                                           const float *st, const float *zc_, const float *dd_, int Lpad, T *out_,
-                                          float *ds0, float *dz0, int L, int b, T *lds) {
+                                          float *ds0, float *dz0, int L, int b, T *lds, int Ea, int Ma) {
     using O = Ops<T>;
     using F = typename O::frag;
     using EE = EOps<T, E>;  // contraction over e
@@ -143,7 +149,7 @@ __device__ __forceinline__ void bwd_sweep(const T *q_, const T *k_, const T *v_,
                 for (int m = 0; m < MB; ++m)
 #pragma unroll
                     for (int t = 0; t < 4; ++t)
-                        W[x][m][t] = st[(16 * bk(x) + r) * M + EM::ecol(m) + EM::estride * g + t];
+                        W[x][m][t] = state_at(st, 16 * bk(x) + r, EM::ecol(m) + EM::estride * g + t, Ea, Ma);
         }
     } else {
         // forward pre-pass: S_{L-1}^T[:, b] = S0^T[:, b] + sum over chunks of V^T K[:, b]
@@ -155,20 +161,20 @@ __device__ __forceinline__ void bwd_sweep(const T *q_, const T *k_, const T *v_,
                     for (int m = 0; m < MB; ++m)
 #pragma unroll
                         for (int t = 0; t < 4; ++t)
-                            W[x][m][t] = s0[(16 * bk(x) + r) * M + EM::ecol(m) + EM::estride * g + t];
+                            W[x][m][t] = state_at(s0, 16 * bk(x) + r, EM::ecol(m) + EM::estride * g + t, Ea, Ma);
             }
         }
         SE sk;
         SM sv;
-        sk.load(Rows<T>(k_, E, 0, L, C), 0);
-        sv.load(Rows<T>(v_, M, 0, L, C), 0);
+        sk.load(Rows<T>(k_, Ea, 0, L, C), 0, Ea);
+        sv.load(Rows<T>(v_, Ma, 0, L, C), 0, Ma);
         for (int c = 0; c < n; ++c) {
             T *Ks = lds + (c & 1) * BUF, *Vs = Ks + C * RE;
-            sk.template store<PHI>(Ks, c * C, L);
+            sk.template store<PHI>(Ks, c * C, L, Ea);
             sv.store(Vs);
             __syncthreads();
-            sk.load(Rows<T>(k_, E, (c + 1) * C, L, C), 0);
-            sv.load(Rows<T>(v_, M, (c + 1) * C, L, C), 0);
+            sk.load(Rows<T>(k_, Ea, (c + 1) * C, L, C), 0, Ea);
+            sv.load(Rows<T>(v_, Ma, (c + 1) * C, L, C), 0, Ma);
             __builtin_amdgcn_sched_barrier(0);
             if constexpr (ROLE == kDQ) {
                 F kt[NB][CB];
@@ -210,11 +216,11 @@ __device__ __forceinline__ void bwd_sweep(const T *q_, const T *k_, const T *v_,
         SM v, g;
         i32x4 dd;
         __device__ __forceinline__ void load(const T *q_, const T *k_, const T *v_, const T *g_, const float *dd_,
-                                             int row0, int L, int Lpad) {
-            q.load(Rows<T>(q_, E, row0, L, C), 0);
-            k.load(Rows<T>(k_, E, row0, L, C), 0);
-            v.load(Rows<T>(v_, M, row0, L, C), 0);
-            g.load(Rows<T>(g_, M, row0, L, C), 0);
+                                             int row0, int L, int Lpad, int Ea, int Ma) {
+            q.load(Rows<T>(q_, Ea, row0, L, C), 0, Ea);
+            k.load(Rows<T>(k_, Ea, row0, L, C), 0, Ea);
+            v.load(Rows<T>(v_, Ma, row0, L, C), 0, Ma);
+            g.load(Rows<T>(g_, Ma, row0, L, C), 0, Ma);
             if constexpr (NORM) {
                 const Rows<float> rd(dd_, 1, row0, Lpad, C);
                 const int t = (int)threadIdx.x;
@@ -230,7 +236,7 @@ __device__ __forceinline__ void bwd_sweep(const T *q_, const T *k_, const T *v_,
     Stages stg[NPF];
 #pragma unroll
     for (int s = 0; s < NPF - 1; ++s) {
-        stg[s].load(q_, k_, v_, g_, dd_, (n - 1 - s) * C, L, Lpad);
+        stg[s].load(q_, k_, v_, g_, dd_, (n - 1 - s) * C, L, Lpad, Ea, Ma);
         __builtin_amdgcn_sched_barrier(0);  // stages complete in order
     }
     const int nsteps = (n + NPF - 1) / NPF * NPF;
@@ -241,13 +247,13 @@ __device__ __forceinline__ void bwd_sweep(const T *q_, const T *k_, const T *v_,
             const int row0 = (n - 1 - step) * C;
             T *Qs = lds + (step & 1) * BUF, *Ks = Qs + C * RE, *Vs = Ks + C * RE, *Gs = Vs + C * RM;
             float *dds = ddbuf + (step & 1) * C;  // NORM: dd_i of row row0 + i
-            stg[s].q.template store<PHI>(Qs, row0, L);
-            stg[s].k.template store<PHI>(Ks, row0, L);
+            stg[s].q.template store<PHI>(Qs, row0, L, Ea);
+            stg[s].k.template store<PHI>(Ks, row0, L, Ea);
             stg[s].v.store(Vs);
             stg[s].g.store(Gs);
             stg[s].store_dd(dds);
             __syncthreads();
-            stg[(s + NPF - 1) % NPF].load(q_, k_, v_, g_, dd_, row0 - (NPF - 1) * C, L, Lpad);
+            stg[(s + NPF - 1) % NPF].load(q_, k_, v_, g_, dd_, row0 - (NPF - 1) * C, L, Lpad, Ea, Ma);
             __builtin_amdgcn_sched_barrier(0);
 
             f32x4 pend[NB][CB];  // this chunk's output tiles (rows 16 I + r) per column block
@@ -459,11 +465,12 @@ __device__ __forceinline__ void bwd_sweep(const T *q_, const T *k_, const T *v_,
             // in issue order, so the rows waited for at a later step were
             // issued before these stores and never wait for them.
             if constexpr (ROLE != kIdle) {
-                const Rows<T> rp(out_, OW, row0, L, C);
+                const int OWa = ROLE == kDV ? Ma : Ea;
+                const Rows<T> rp(out_, OWa, row0, L, C);
 #pragma unroll
                 for (int x = 0; x < NB; ++x)
 #pragma unroll
-                    for (int j = 0; j < CB; ++j) st_out<T>(rp, j, bk(x), pend[x][j]);
+                    for (int j = 0; j < CB; ++j) st_out<T>(rp, j, bk(x), pend[x][j], OWa);
             }
         }
     }
@@ -473,7 +480,8 @@ __device__ __forceinline__ void bwd_sweep(const T *q_, const T *k_, const T *v_,
 #pragma unroll
             for (int x = 0; x < NB; ++x)
 #pragma unroll
-                for (int t = 0; t < 4; ++t) dz0[16 * bk(x) + 4 * g + t] = zb[x][t];
+                for (int t = 0; t < 4; ++t)
+                    if (16 * bk(x) + 4 * g + t < Ea) dz0[16 * bk(x) + 4 * g + t] = zb[x][t];
         }
     }
     // the gradient of the initial state: R_0 = sum_i q_i dO_i^T, held by the
@@ -485,8 +493,10 @@ __device__ __forceinline__ void bwd_sweep(const T *q_, const T *k_, const T *v_,
 #pragma unroll
                 for (int e = 0; e < EB; ++e)
 #pragma unroll
-                    for (int t = 0; t < 4; ++t)
-                        ds0[(EE::ecol(e) + EE::estride * g + t) * M + 16 * bk(x) + r] = X[x][e][t];
+                    for (int t = 0; t < 4; ++t) {
+                        const int row = EE::ecol(e) + EE::estride * g + t, col = 16 * bk(x) + r;
+                        if (row < Ea && col < Ma) ds0[row * Ma + col] = X[x][e][t];
+                    }
         }
     }
 }
@@ -501,7 +511,7 @@ __global__ __launch_bounds__((64 * bwd_waves<E, M, G, NB, IDLE>())) void cp_bwd_
     const float *__restrict__ state_in, const float *__restrict__ state_final, const float *__restrict__ zc,
     const float *__restrict__ dd, int Lpad, T *__restrict__ dQ,
     T *__restrict__ dK, T *__restrict__ dV, float *__restrict__ dstate_in, float *__restrict__ dz_in, int L,
-    int NS) {
+    int NS, int Ea, int Ma) {
     constexpr int EB = E / 16, MB = M / 16;
     // with several blocks per wave every wave's blocks all exist
     static_assert(NB == 1 || (EB % (G * NB) == 0 && MB % (G * NB) == 0), "blocks per wave");
@@ -516,30 +526,31 @@ __global__ __launch_bounds__((64 * bwd_waves<E, M, G, NB, IDLE>())) void cp_bwd_
     int slice, grp;
     map_block(blockIdx.x, NS, G, slice, grp);
     const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
-    const int64_t oe = (int64_t)slice * L * E, om = (int64_t)slice * L * M;
+    // the tensors' own head sizes Ea <= E, Ma <= M (the kernel's tile sizes)
+    const int64_t oe = (int64_t)slice * L * Ea, om = (int64_t)slice * L * Ma, os = (int64_t)slice * Ea * Ma;
     const T *q_ = Q + oe, *k_ = K + oe, *v_ = V + om, *g_ = Gr + om;
-    const float *s0 = state_in ? state_in + (int64_t)slice * E * M : nullptr;
-    const float *st = state_final ? state_final + (int64_t)slice * E * M : nullptr;
+    const float *s0 = state_in ? state_in + os : nullptr;
+    const float *st = state_final ? state_final + os : nullptr;
     const float *zc_ = zc ? zc + (int64_t)slice * (Lpad / C) * E : nullptr;
     const float *dd_ = dd ? dd + (int64_t)slice * Lpad : nullptr;
-    float *ds0 = dstate_in ? dstate_in + (int64_t)slice * E * M : nullptr;
-    float *dz0 = dz_in ? dz_in + (int64_t)slice * E : nullptr;
+    float *ds0 = dstate_in ? dstate_in + os : nullptr;
+    float *dz0 = dz_in ? dz_in + (int64_t)slice * Ea : nullptr;
     // wave w: role, and the first of its NB column blocks (b, b + G, ...)
     const int role = w < EG ? kDQ : w < 2 * EG ? kDK : w < 2 * EG + MG ? kDV : kIdle;
     const int lw = role == kDQ ? w : role == kDK ? w - EG : w - 2 * EG;
     const int b = grp + G * NB * lw;
     if (role == kDQ && b < EB)
         bwd_sweep<T, E, M, C, G, NB, IDLE, NPF, NORM, FMAP, kDQ>(q_, k_, v_, g_, s0, st, zc_, dd_, Lpad, dQ + oe,
-                                                                 nullptr, nullptr, L, b, lds);
+                                                                 nullptr, nullptr, L, b, lds, Ea, Ma);
     else if (role == kDK && b < EB)
         bwd_sweep<T, E, M, C, G, NB, IDLE, NPF, NORM, FMAP, kDK>(q_, k_, v_, g_, s0, st, zc_, dd_, Lpad, dK + oe,
-                                                                 nullptr, dz0, L, b, lds);
+                                                                 nullptr, dz0, L, b, lds, Ea, Ma);
     else if (role == kDV && b < MB)
         bwd_sweep<T, E, M, C, G, NB, IDLE, NPF, NORM, FMAP, kDV>(q_, k_, v_, g_, s0, st, zc_, dd_, Lpad, dV + om,
-                                                                 ds0, nullptr, L, b, lds);
+                                                                 ds0, nullptr, L, b, lds, Ea, Ma);
     else
         bwd_sweep<T, E, M, C, G, NB, IDLE, NPF, NORM, FMAP, kIdle>(q_, k_, v_, g_, s0, st, zc_, dd_, Lpad,
-                                                                   nullptr, nullptr, nullptr, L, 0, lds);
+                                                                   nullptr, nullptr, nullptr, L, 0, lds, Ea, Ma);
 }
 
 }  // namespace cp

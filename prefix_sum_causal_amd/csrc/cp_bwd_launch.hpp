@@ -17,10 +17,12 @@ namespace cp {
 //     cs_c = sum over the chunk's rows of phi(k_i)   (fp32)
 // dn and dd take 16 lanes per row; dd has zeros in rows L .. Lpad-1.  The
 // column sums read K in 16-byte pieces, TPR lanes per row, and apply phi
-// rounded to the I/O type, as the sweeps see it.
+// rounded to the I/O type, as the sweeps see it.  The rows hold Ea <= E and
+// Ma <= M columns; the sums of the padding columns are zero.
 template <typename T, int E, int M, int C, bool FMAP>
 __device__ __forceinline__ void lin_prep_chunk(const T *dO, const T *Out, const T *K, const float *den, T *dn,
-                                               float *dd, float *cs, int c, int L, float (*red)[E + 1]) {
+                                               float *dd, float *cs, int c, int L, float (*red)[E + 1], int Ea,
+                                               int Ma) {
     constexpr int VEC = 16 / sizeof(T), TPR = E / VEC, P = 256 / TPR;
     const int t = threadIdx.x, l = t & 15;
     for (int i = c * C + (t >> 4); i < (c + 1) * C; i += 16) {
@@ -32,9 +34,11 @@ __device__ __forceinline__ void lin_prep_chunk(const T *dO, const T *Out, const 
         float acc = 0.f;
 #pragma unroll
         for (int m = l; m < M; m += 16) {
-            const float gv = (float)dO[(int64_t)i * M + m];
-            acc += gv * (float)Out[(int64_t)i * M + m];
-            dn[(int64_t)i * M + m] = (T)(gv / d);
+            if (m < Ma) {
+                const float gv = (float)dO[(int64_t)i * Ma + m];
+                acc += gv * (float)Out[(int64_t)i * Ma + m];
+                dn[(int64_t)i * Ma + m] = (T)(gv / d);
+            }
         }
 #pragma unroll
         for (int x = 8; x >= 1; x >>= 1) acc += __shfl_xor(acc, x, 16);
@@ -44,9 +48,9 @@ __device__ __forceinline__ void lin_prep_chunk(const T *dO, const T *Out, const 
     float acc[VEC];
 #pragma unroll
     for (int j = 0; j < VEC; ++j) acc[j] = 0.f;
-    for (int i = c * C + p; i < (c + 1) * C && i < L; i += P) {
+    for (int i = c * C + p; i < (c + 1) * C && i < L && cg * VEC < Ea; i += P) {
         T x[VEC];
-        *reinterpret_cast<int4 *>(x) = *reinterpret_cast<const int4 *>(K + (int64_t)i * E + cg * VEC);
+        *reinterpret_cast<int4 *>(x) = *reinterpret_cast<const int4 *>(K + (int64_t)i * Ea + cg * VEC);
 #pragma unroll
         for (int j = 0; j < VEC; ++j) acc[j] += FMAP ? (float)(T)phi((float)x[j]) : (float)x[j];
     }
@@ -67,26 +71,28 @@ template <typename T, int E, int M, int C, bool FMAP>
 __global__ __launch_bounds__(256) void cp_lin_prep_kernel(const T *__restrict__ dO, const T *__restrict__ Out,
                                                           const T *__restrict__ K, const float *__restrict__ den,
                                                           T *__restrict__ dn, float *__restrict__ dd,
-                                                          float *__restrict__ cs, int L, int Lpad, int NS) {
+                                                          float *__restrict__ cs, int L, int Lpad, int NS, int Ea,
+                                                          int Ma) {
     constexpr int VEC = 16 / sizeof(T), TPR = E / VEC, P = 256 / TPR;
     static_assert(E % VEC == 0 && 256 % TPR == 0 && C % 16 == 0, "prep layout");
     __shared__ float red[P][E + 1];
     const int nch = Lpad / C;
     for (int64_t blk = blockIdx.x; blk < (int64_t)nch * NS; blk += gridDim.x) {
         const int64_t sl = blk / nch;
-        lin_prep_chunk<T, E, M, C, FMAP>(dO + sl * L * M, Out + sl * L * M, K + sl * L * E, den + sl * L,
-                                         dn + sl * L * M, dd + sl * Lpad, cs + sl * nch * E, (int)(blk % nch), L,
-                                         red);
+        lin_prep_chunk<T, E, M, C, FMAP>(dO + sl * L * Ma, Out + sl * L * Ma, K + sl * L * Ea, den + sl * L,
+                                         dn + sl * L * Ma, dd + sl * Lpad, cs + sl * nch * E, (int)(blk % nch), L,
+                                         red, Ea, Ma);
     }
 }
 
-// Exclusive prefix over the chunk sums of one slice, in place:
+// Exclusive prefix over the chunk sums of one slice, in place (E columns
+// including any padding; z_in holds Ea):
 // zc_c = z_{-1} + sum of cs_c' for c' < c, the normaliser before chunk c,
 // summed forward in fp32 (recovering early prefixes from the final z by
 // subtraction would lose most of their bits).  Lane (p, e) scans a contiguous
 // range of chunks; the range totals are combined through LDS.
 template <int E>
-__device__ __forceinline__ void lin_zscan_slice(const float *z_in, float *zc, int nch, float (*tot)[E]) {
+__device__ __forceinline__ void lin_zscan_slice(const float *z_in, float *zc, int nch, float (*tot)[E], int Ea) {
     constexpr int P = 256 / E;
     const int e = threadIdx.x % E, p = threadIdx.x / E;
     const int c0 = (int)((int64_t)nch * p / P), c1 = (int)((int64_t)nch * (p + 1) / P);
@@ -95,7 +101,7 @@ __device__ __forceinline__ void lin_zscan_slice(const float *z_in, float *zc, in
     for (int c = c0; c < c1; ++c) sum += col[(int64_t)c * E];
     tot[p][e] = sum;
     __syncthreads();
-    float z = z_in ? z_in[e] : 0.f;
+    float z = z_in && e < Ea ? z_in[e] : 0.f;
     for (int q = 0; q < p; ++q) z += tot[q][e];
     for (int c = c0; c < c1; ++c) {
         const float x = col[(int64_t)c * E];
@@ -108,10 +114,10 @@ __device__ __forceinline__ void lin_zscan_slice(const float *z_in, float *zc, in
 // One workgroup per slice, grid-strided.
 template <int E>
 __global__ __launch_bounds__(256) void cp_lin_zscan_kernel(const float *__restrict__ z_in, float *__restrict__ zc,
-                                                           int nch, int NS) {
+                                                           int nch, int NS, int Ea) {
     __shared__ float tot[256 / E][E];
     for (int64_t sl = blockIdx.x; sl < NS; sl += gridDim.x)
-        lin_zscan_slice<E>(z_in ? z_in + sl * E : nullptr, zc + sl * nch * E, nch, tot);
+        lin_zscan_slice<E>(z_in ? z_in + sl * Ea : nullptr, zc + sl * nch * E, nch, tot, Ea);
 }
 
 template <typename T, int E, int M, bool NORM, bool FMAP>
@@ -123,7 +129,7 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t s) {
     const float *s0 = a.state_in, *st = a.state_final;
     T *dq = static_cast<T *>(a.dQ), *dk = static_cast<T *>(a.dK), *dv = static_cast<T *>(a.dV);
     float *ds0 = a.dstate_in, *dz0 = a.dz_in;
-    int L = a.L, NS = a.NS;
+    int L = a.L, NS = a.NS, Ea = a.Ea, Ma = a.Ma;
     int Lpad = (L + C - 1) / C * C;
     float *dd = nullptr, *zc = nullptr;
     void *scratch = nullptr;
@@ -143,20 +149,20 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t s) {
         const float *z0 = a.z_in;
         int nch = Lpad / C;
         auto prep = cp_lin_prep_kernel<T, E, M, C, FMAP>;
-        void *pargs[] = {&g, &out, &k, &den, &dn, &dd, &zc, &L, &Lpad, &NS};
+        void *pargs[] = {&g, &out, &k, &den, &dn, &dd, &zc, &L, &Lpad, &NS, &Ea, &Ma};
         const int64_t blocks = std::min<int64_t>((int64_t)NS * nch, 1 << 20);
         e = launch_kernel(reinterpret_cast<const void *>(prep), dim3((unsigned)blocks), dim3(256), pargs, s);
         g = dn;  // the sweeps take dn in place of dO
         if (e == hipSuccess) {
             auto scan = cp_lin_zscan_kernel<E>;
-            void *sargs[] = {&z0, &zc, &nch, &NS};
+            void *sargs[] = {&z0, &zc, &nch, &NS, &Ea};
             e = launch_kernel(reinterpret_cast<const void *>(scan), dim3((unsigned)std::min(NS, 1 << 20)), dim3(256),
                               sargs, s);
         }
     }
     if (e == hipSuccess) {
         auto kern = cp_bwd_kernel<T, E, M, C, P::BG, P::BNB, P::BIDLE, P::BNPF, NORM, FMAP>;
-        void *args[] = {&q, &k, &v, &g, &s0, &st, &zc, &dd, &Lpad, &dq, &dk, &dv, &ds0, &dz0, &L, &NS};
+        void *args[] = {&q, &k, &v, &g, &s0, &st, &zc, &dd, &Lpad, &dq, &dk, &dv, &ds0, &dz0, &L, &NS, &Ea, &Ma};
         e = launch_kernel(reinterpret_cast<const void *>(kern), dim3(NS * P::BG),
                           dim3(64 * bwd_waves<E, M, P::BG, P::BNB, P::BIDLE>()),
                           args, s);
@@ -186,7 +192,7 @@ bwd_fn pick_bwd(int E, int M) {
         {launch_bwd_fm<T, 128, 16, NORM>, launch_bwd_fm<T, 128, 32, NORM>, launch_bwd_fm<T, 128, 64, NORM>,
          launch_bwd_fm<T, 128, 128, NORM>},
     };
-    const int ie = size_index(E), im = size_index(M);
+    const int ie = tile_index(E), im = tile_index(M);
     return (ie < 0 || im < 0) ? nullptr : table[ie][im];
 }
 

@@ -270,10 +270,16 @@ struct Rows {
     }
 };
 
+// A byte offset past every buffer range: loads there read zero, stores are
+// dropped.
+constexpr int kVoid = 0x7FFFFFF0;
+
 // Store a transposed result tile: lane (g, r) holds X[16 rb + r][16 cb + 4g + t].
+// Columns at or past wa (the row's width; a multiple of 4) are not stored.
 template <typename T>
-__device__ __forceinline__ void st_out(const Rows<T> &X, int rb, int cb, f32x4 v) {
-    const int off = ((16 * rb + lane_r()) * X.ld + 16 * cb + 4 * lane_g()) * (int)sizeof(T);
+__device__ __forceinline__ void st_out(const Rows<T> &X, int rb, int cb, f32x4 v, int wa) {
+    const int col = 16 * cb + 4 * lane_g();
+    const int off = col < wa ? ((16 * rb + lane_r()) * X.ld + col) * (int)sizeof(T) : kVoid;
     if constexpr (sizeof(T) == 2) {
         typedef int i32x2 __attribute__((__vector_size__(2 * sizeof(int))));
         __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(i32x2, Ops<T>::cvt(v)), X.rsrc, off, 0, 0);
@@ -294,9 +300,11 @@ typedef int i32x4 __attribute__((__vector_size__(4 * sizeof(int))));
 // One thread's share of a chunk copy: rows [row0, row0 + C) and columns
 // [col0, col0 + W) of a row-major slice, as 16-byte pieces spread over the NT
 // threads of the workgroup (piece p = row * W*sizeof(T)/16 + column piece).
-// load() issues the buffer loads (rows outside [0, L) read as zero); store()
-// writes the pieces into the LDS copy, optionally through phi (the
-// elementwise feature map, with rows at or past L kept zero).
+// load() issues the buffer loads (rows outside [0, L) and columns at or past
+// the row's width wa read as zero: a narrower head is padded to W columns);
+// store() writes the pieces into the LDS copy, optionally through phi (the
+// elementwise feature map, with rows at or past L and padded columns kept
+// zero).
 template <typename T, int NT, int C, int W>
 struct Stage {
     static constexpr int PPR = W * (int)sizeof(T) / 16;  // pieces per row
@@ -306,19 +314,22 @@ struct Stage {
     static_assert(W * (int)sizeof(T) % 16 == 0, "rows must be whole 16-byte pieces");
     i32x4 v[NP];
 
-    __device__ __forceinline__ void load(const Rows<T> &X, int col0) {
+    static constexpr int VEC = 16 / (int)sizeof(T);  // elements per piece
+
+    __device__ __forceinline__ void load(const Rows<T> &X, int col0, int wa) {
 #pragma unroll
         for (int i = 0; i < NP; ++i) {
             const int p = (int)threadIdx.x + i * NT;
             const int row = p / PPR, cp = p % PPR;
             int off = (row * X.ld + col0) * (int)sizeof(T) + cp * 16;
-            if constexpr (P % NT != 0) off = p < P ? off : 0x7FFFFFF0;  // past the range: zero
+            if constexpr (P % NT != 0) off = p < P ? off : kVoid;  // past the range: zero
+            off = col0 + cp * VEC < wa ? off : kVoid;                // padded column: zero
             v[i] = __builtin_amdgcn_raw_buffer_load_b128(X.rsrc, off, 0, 0);
         }
     }
 
     template <bool PHI = false>
-    __device__ __forceinline__ void store(T *lds, int row0 = 0, int L = 0) const {
+    __device__ __forceinline__ void store(T *lds, int row0 = 0, int L = 0, int wa = W) const {
 #pragma unroll
         for (int i = 0; i < NP; ++i) {
             const int p = (int)threadIdx.x + i * NT;
@@ -329,7 +340,7 @@ struct Stage {
                 constexpr int n = 16 / (int)sizeof(T);
                 typedef T tn __attribute__((__vector_size__(16)));
                 tn e = __builtin_bit_cast(tn, x);
-                const bool valid = row0 + row < L;
+                const bool valid = row0 + row < L && cp * VEC < wa;
 #pragma unroll
                 for (int j = 0; j < n; ++j) e[j] = valid ? (T)phi((float)e[j]) : (T)0.f;
                 x = __builtin_bit_cast(i32x4, e);

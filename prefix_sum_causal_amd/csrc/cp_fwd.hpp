@@ -64,7 +64,7 @@ constexpr int last_block(int h) {
 template <typename T, int E, int M, int C, int NW, int RSPLIT, int NPF, bool NORM, bool FMAP, bool SONLY, int H>
 __device__ __forceinline__ void fwd_sweep(const T *q_, const T *k_, const T *v_, T *o_, float *den_, int rb,
                                           int re, int grp, int cb, float eps, T *lds, f32x4 (&S)[E / 16],
-                                          f32x4 (&z)[E / 16]) {
+                                          f32x4 (&z)[E / 16], int Ea, int Ma) {
     using O = Ops<T>;
     using F = typename O::frag;
     using EO = EOps<T, E>;
@@ -85,17 +85,18 @@ __device__ __forceinline__ void fwd_sweep(const T *q_, const T *k_, const T *v_,
     struct Stages {
         SQ q, k;
         SV v;
-        __device__ __forceinline__ void load(const T *q_, const T *k_, const T *v_, int row0, int re, int col0) {
-            if constexpr (!SONLY) q.load(Rows<T>(q_, E, row0, re, C), 0);
-            k.load(Rows<T>(k_, E, row0, re, C), 0);
-            v.load(Rows<T>(v_, M, row0, re, C), col0);
+        __device__ __forceinline__ void load(const T *q_, const T *k_, const T *v_, int row0, int re, int col0,
+                                             int Ea, int Ma) {
+            if constexpr (!SONLY) q.load(Rows<T>(q_, Ea, row0, re, C), 0, Ea);
+            k.load(Rows<T>(k_, Ea, row0, re, C), 0, Ea);
+            v.load(Rows<T>(v_, Ma, row0, re, C), col0, Ma);
         }
     };
     const int col0 = 16 * grp * NW;
     Stages st[NPF];
 #pragma unroll
     for (int s = 0; s < NPF - 1; ++s) {
-        st[s].load(q_, k_, v_, rb + s * C, re, col0);
+        st[s].load(q_, k_, v_, rb + s * C, re, col0, Ea, Ma);
         __builtin_amdgcn_sched_barrier(0);  // stages complete in order
     }
 
@@ -107,8 +108,8 @@ __device__ __forceinline__ void fwd_sweep(const T *q_, const T *k_, const T *v_,
             const int c = c0 + s;
             const int row0 = rb + c * C;
             T *Qs = lds + (c & 1) * BUF, *Ks = Qs + C * RQ, *Vs = Ks + C * RQ;
-            if constexpr (!SONLY) st[s].q.template store<NORM && FMAP>(Qs, row0, re);
-            st[s].k.template store<NORM && FMAP>(Ks, row0, re);
+            if constexpr (!SONLY) st[s].q.template store<NORM && FMAP>(Qs, row0, re, Ea);
+            st[s].k.template store<NORM && FMAP>(Ks, row0, re, Ea);
             st[s].v.store(Vs);
             __syncthreads();
             // The next chunk's loads are issued one array at a time between
@@ -124,18 +125,18 @@ __device__ __forceinline__ void fwd_sweep(const T *q_, const T *k_, const T *v_,
             int nload = 0;   // arrays of the next chunk whose loads are issued
             auto issue_load = [&]() {
                 if constexpr (!SONLY)
-                    if (nload == 0) nx.q.load(Rows<T>(q_, E, nrow0, re, C), 0);
-                if (nload == 1) nx.k.load(Rows<T>(k_, E, nrow0, re, C), 0);
-                if (nload == 2) nx.v.load(Rows<T>(v_, M, nrow0, re, C), col0);
+                    if (nload == 0) nx.q.load(Rows<T>(q_, Ea, nrow0, re, C), 0, Ea);
+                if (nload == 1) nx.k.load(Rows<T>(k_, Ea, nrow0, re, C), 0, Ea);
+                if (nload == 2) nx.v.load(Rows<T>(v_, Ma, nrow0, re, C), col0, Ma);
                 ++nload;
                 __builtin_amdgcn_sched_barrier(0);
             };
             // the step's output tiles (after every owned row block is done)
             auto issue_store = [&]() {
-                const Rows<T> ro(o_, M, row0, re, C);
+                const Rows<T> ro(o_, Ma, row0, re, C);
 #pragma unroll
                 for (int I = 0; I < CB; ++I)
-                    if (owns_block<CB, RSPLIT>(H, I)) st_out<T>(ro, I, grp * NW + cb, pend[I]);
+                    if (owns_block<CB, RSPLIT>(H, I)) st_out<T>(ro, I, grp * NW + cb, pend[I], Ma);
                 if constexpr (NORM) {  // the denominators, from the first column block's waves
                     if (den_ && grp * NW + cb == 0 && lane_g() == 0) {
                         const Rows<float> rd(den_, 1, row0, re, C);
@@ -245,7 +246,7 @@ __global__ __launch_bounds__(64 * (M / 16 / G) * RSPLIT) void cp_fwd_kernel(
     const T *__restrict__ Q, const T *__restrict__ K, const T *__restrict__ V, T *__restrict__ Out,
     const float *__restrict__ state_in, const float *__restrict__ z_in, float *__restrict__ state_out,
     float *__restrict__ z_out, float *__restrict__ den, float *__restrict__ ws, int L, int NS, int seg_len,
-    float eps) {
+    float eps, int Ea, int Ma) {
     using EO = EOps<T, E>;
     constexpr int EB = E / 16, MB = M / 16, CB = C / 16;
     static_assert(MB % G == 0, "column groups split the column blocks evenly");
@@ -266,10 +267,11 @@ __global__ __launch_bounds__(64 * (M / 16 / G) * RSPLIT) void cp_fwd_kernel(
     const int cb = w % NW, h = w / NW;
     const int mb = grp * NW + cb;
     const int g = lane_g(), r = lane_r();
-    const T *q_ = Q + (int64_t)slice * L * E;
-    const T *k_ = K + (int64_t)slice * L * E;
-    const T *v_ = V + (int64_t)slice * L * M;
-    T *o_ = Out + (int64_t)slice * L * M;
+    // the tensors' own head sizes Ea <= E, Ma <= M (the kernel's tile sizes)
+    const T *q_ = Q + (int64_t)slice * L * Ea;
+    const T *k_ = K + (int64_t)slice * L * Ea;
+    const T *v_ = V + (int64_t)slice * L * Ma;
+    T *o_ = Out + (int64_t)slice * L * Ma;
     float *den_ = den ? den + (int64_t)slice * L : nullptr;
     const int rb = seg * seg_len, re = rb + seg_len < L ? rb + seg_len : L;
     float *ws_slice = ws ? ws + (int64_t)slice * nseg * WS : nullptr;
@@ -282,15 +284,15 @@ __global__ __launch_bounds__(64 * (M / 16 / G) * RSPLIT) void cp_fwd_kernel(
         z[e] = zero4();
     }
     if (!SONLY && (state_in || z_in)) {  // the carried-in state before row 0
-        const float *s0 = state_in ? state_in + (int64_t)slice * E * M : nullptr;
-        const float *z0 = z_in ? z_in + (int64_t)slice * E : nullptr;
+        const float *s0 = state_in ? state_in + (int64_t)slice * Ea * Ma : nullptr;
+        const float *z0 = z_in ? z_in + (int64_t)slice * Ea : nullptr;
 #pragma unroll
         for (int e = 0; e < EB; ++e)
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
                 const int row = EO::ecol(e) + EO::estride * g + t;
-                if (s0) S[e][t] = s0[row * M + 16 * mb + r];
-                if (NORM && z0) z[e][t] = z0[row];
+                if (s0 && row < Ea && 16 * mb + r < Ma) S[e][t] = s0[row * Ma + 16 * mb + r];
+                if (NORM && z0 && row < Ea) z[e][t] = z0[row];
             }
     }
     if (!SONLY && ws_slice) {
@@ -307,9 +309,11 @@ __global__ __launch_bounds__(64 * (M / 16 / G) * RSPLIT) void cp_fwd_kernel(
         }
     }
     if (h == 0)
-        fwd_sweep<T, E, M, C, NW, RSPLIT, NPF, NORM, FMAP, SONLY, 0>(q_, k_, v_, o_, den_, rb, re, grp, cb, eps, lds, S, z);
+        fwd_sweep<T, E, M, C, NW, RSPLIT, NPF, NORM, FMAP, SONLY, 0>(q_, k_, v_, o_, den_, rb, re, grp, cb, eps, lds, S,
+                                                                     z, Ea, Ma);
     else
-        fwd_sweep<T, E, M, C, NW, RSPLIT, NPF, NORM, FMAP, SONLY, 1>(q_, k_, v_, o_, den_, rb, re, grp, cb, eps, lds, S, z);
+        fwd_sweep<T, E, M, C, NW, RSPLIT, NPF, NORM, FMAP, SONLY, 1>(q_, k_, v_, o_, den_, rb, re, grp, cb, eps, lds, S,
+                                                                     z, Ea, Ma);
 
     if constexpr (SONLY) {
         if (h == 0) {
@@ -325,15 +329,15 @@ __global__ __launch_bounds__(64 * (M / 16 / G) * RSPLIT) void cp_fwd_kernel(
         }
     } else {
         if (h == 0 && seg == nseg - 1) {  // the final state of the slice
-            float *st_ = state_out ? state_out + (int64_t)slice * E * M : nullptr;
-            float *zt_ = z_out ? z_out + (int64_t)slice * E : nullptr;
+            float *st_ = state_out ? state_out + (int64_t)slice * Ea * Ma : nullptr;
+            float *zt_ = z_out ? z_out + (int64_t)slice * Ea : nullptr;
 #pragma unroll
             for (int e = 0; e < EB; ++e)
 #pragma unroll
                 for (int t = 0; t < 4; ++t) {
                     const int row = EO::ecol(e) + EO::estride * g + t;
-                    if (st_) st_[row * M + 16 * mb + r] = S[e][t];
-                    if (NORM && zt_ && mb == 0 && r == 0) zt_[row] = z[e][t];
+                    if (st_ && row < Ea && 16 * mb + r < Ma) st_[row * Ma + 16 * mb + r] = S[e][t];
+                    if (NORM && zt_ && mb == 0 && r == 0 && row < Ea) zt_[row] = z[e][t];
                 }
         }
     }

@@ -28,7 +28,7 @@ hipError_t launch_fwd_t(const FwdArgs &a, hipStream_t s) {
     T *o = static_cast<T *>(a.Out);
     const float *s0 = a.state_in, *z0 = a.z_in;
     float *st = a.state_out, *zt = a.z_out, *dn = a.den_out;
-    int L = a.L, NS = a.NS;
+    int L = a.L, NS = a.NS, Ea = a.Ea, Ma = a.Ma;
     float eps = a.eps;
     const dim3 block(64 * (M / 16 / P::FG) * P::FRS);
 
@@ -44,14 +44,14 @@ hipError_t launch_fwd_t(const FwdArgs &a, hipStream_t s) {
         e = hipMallocAsync(reinterpret_cast<void **>(&ws), bytes, s);
         if (e != hipSuccess) return e;
         auto k1 = cp_fwd_kernel<T, E, M, P::FC, P::FG, P::FRS, P::FNPF, NORM, FMAP, true>;
-        void *args1[] = {&q, &k, &v, &o, &s0, &z0, &st, &zt, &dn, &ws, &L, &NS, &seg_len, &eps};
+        void *args1[] = {&q, &k, &v, &o, &s0, &z0, &st, &zt, &dn, &ws, &L, &NS, &seg_len, &eps, &Ea, &Ma};
         e = launch_kernel(reinterpret_cast<const void *>(k1), dim3(NS * P::FG * nseg), block, args1, s);
     } else {
         seg_len = L;
     }
     if (e == hipSuccess) {
         auto k2 = cp_fwd_kernel<T, E, M, P::FC, P::FG, P::FRS, P::FNPF, NORM, FMAP, false>;
-        void *args2[] = {&q, &k, &v, &o, &s0, &z0, &st, &zt, &dn, &ws, &L, &NS, &seg_len, &eps};
+        void *args2[] = {&q, &k, &v, &o, &s0, &z0, &st, &zt, &dn, &ws, &L, &NS, &seg_len, &eps, &Ea, &Ma};
         e = launch_kernel(reinterpret_cast<const void *>(k2), dim3(NS * P::FG * nseg), block, args2, s);
     }
     if (ws) {
@@ -79,7 +79,7 @@ fwd_fn pick_fwd(int E, int M) {
         {launch_fwd_fm<T, 128, 16, NORM>, launch_fwd_fm<T, 128, 32, NORM>, launch_fwd_fm<T, 128, 64, NORM>,
          launch_fwd_fm<T, 128, 128, NORM>},
     };
-    const int ie = size_index(E), im = size_index(M);
+    const int ie = tile_index(E), im = tile_index(M);
     return (ie < 0 || im < 0) ? nullptr : table[ie][im];
 }
 

@@ -17,6 +17,7 @@ struct FwdArgs {
     int L, NS;
     float eps;
     int fmap;
+    int Ea, Ma;  // head sizes of the tensors (the kernel runs the next tile size up)
 };
 
 struct BwdArgs {
@@ -32,6 +33,7 @@ struct BwdArgs {
     const float *z_in;  // optional initial z
     float *dz_in;
     int fmap;
+    int Ea, Ma;  // head sizes of the tensors (the kernel runs the next tile size up)
 };
 
 // Each launcher enqueues one kernel on stream and returns hipSuccess or the
@@ -51,13 +53,12 @@ bwd_fn bwd_f16(int E, int M, bool norm);
 // next pair of timing events.
 hipError_t launch_kernel(const void *kernel, dim3 grid, dim3 block, void **args, hipStream_t stream);
 
-// Workgroups per (n, h) slice of each kernel.
-inline int fwd_parts(int E, int M) { (void)E; return M / 16; }
-inline int bwd_parts(int E, int M) { return (E > M ? E : M) / 16; }
-
-// Index 0..3 of a head size in {16, 32, 64, 128}, -1 otherwise.
-inline int size_index(int64_t x) {
-    return x == 16 ? 0 : x == 32 ? 1 : x == 64 ? 2 : x == 128 ? 3 : -1;
+// Index 0..3 of the kernel tile size {16, 32, 64, 128} that runs a head of
+// x features: the smallest one >= x; -1 for x outside [1, 128].  A head
+// narrower than its tile is padded with zero columns on load and its padding
+// is never stored.
+inline int tile_index(int64_t x) {
+    return x < 1 ? -1 : x <= 16 ? 0 : x <= 32 ? 1 : x <= 64 ? 2 : x <= 128 ? 3 : -1;
 }
 
 }  // namespace cp

@@ -116,12 +116,23 @@ def test_bad_dims(lib, shape):
     assert lin(lib, shape=shape) == DIM
 
 
-@pytest.mark.parametrize("E,M", [(48, 64), (64, 8), (256, 64), (64, 17)])
+# Head sizes up to 128 whose rows are whole 16-byte pieces: multiples of 8
+# for the 16-bit types, of 4 for fp32.
+@pytest.mark.parametrize("E,M", [(256, 64), (64, 17), (12, 64), (64, 4), (136, 64), (64, 130)])
 def test_unsupported_head_sizes(lib, E, M):
     shape = (2, 3, 100, E, M)
-    assert fwd(lib, shape=shape) == UNSUP
-    assert bwd(lib, shape=shape) == UNSUP
-    assert lin(lib, shape=shape) == UNSUP
+    for dt in (1, 2):
+        assert fwd(lib, shape=shape, dtype=dt) == UNSUP
+        assert bwd(lib, shape=shape, dtype=dt) == UNSUP
+        assert lin(lib, shape=shape, dtype=dt) == UNSUP
+
+
+@pytest.mark.parametrize("E,M", [(256, 64), (64, 17), (6, 64), (64, 2), (132, 64), (64, 130)])
+def test_unsupported_head_sizes_f32(lib, E, M):
+    shape = (2, 3, 100, E, M)
+    assert fwd(lib, shape=shape, dtype=0) == UNSUP
+    assert bwd(lib, shape=shape, dtype=0) == UNSUP
+    assert lin(lib, shape=shape, dtype=0) == UNSUP
 
 
 def test_unsupported_dtype_flag_eps(lib):
@@ -168,7 +179,7 @@ def test_linear_attn_bwd_validation(lib):
     for name in ("q", "k", "v", "o", "g", "den", "dq", "dk", "dv"):
         assert linb(lib, **{name: None}) == NULL, name
     assert linb(lib, shape=(2, 3, 0, 64, 32)) == DIM
-    assert linb(lib, shape=(2, 3, 100, 48, 32)) == UNSUP
+    assert linb(lib, shape=(2, 3, 100, 44, 32)) == UNSUP
     assert linb(lib, fm=3) == UNSUP
     assert linb(lib, dtype=5) == UNSUP
     assert linb(lib, dtype=2) == UNSUP            # no fp16 normalised backward
