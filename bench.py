@@ -40,7 +40,7 @@ def kernel_digest() -> str:
 def algorithmic_bytes(w, kind: str) -> int:
     """Bytes a launch must move at minimum: read every input once, write every
     output once (plus the fp32 final state passed from forward to backward)."""
-    s = 2 if w.dtype == "bf16" else 4
+    s = 4 if w.dtype == "f32" else 2
     th = w.N * w.H * w.L
     state = w.N * w.H * w.E * w.M * 4
     if kind == "fwd":
@@ -126,7 +126,7 @@ def main() -> int:
 
     name = args.workload or W.HEADLINE
     w = W.WORKLOADS[name]
-    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[w.dtype]
     d = W.generate(w, need_do=w.op.endswith("bwd"))
     dev = {k: torch.from_numpy(v).to("cuda").to(tdt) for k, v in d.items()}
     del d

@@ -15,44 +15,56 @@ namespace cp {
 //     dn_i = dO_i / d_i              (stored in the I/O type, like dO)
 //     dd_i = -(dO_i . out_i) / d_i   (= -(dO_i . n_i) / d_i^2; fp32)
 //     cs_c = sum over the chunk's rows of phi(k_i)   (fp32)
-// dn and dd take 16 lanes per row; dd has zeros in rows L .. Lpad-1.  The
-// column sums read K in 16-byte pieces, TPR lanes per row, and apply phi
-// rounded to the I/O type, as the sweeps see it.  The rows hold Ea <= E and
-// Ma <= M columns; the sums of the padding columns are zero.
+// Rows are read and dn written in 16-byte pieces: TPM lanes per row of dO
+// (M, the tile width, of them; lanes past the head's Ma columns idle), the
+// dot product reduced across them; dd has zeros in rows L .. Lpad-1.  The
+// column sums read K the same way, TPR lanes per row, and apply phi rounded
+// to the I/O type, as the sweeps see it; the sums of padding columns (past
+// Ea) are zero.
 template <typename T, int E, int M, int C, bool FMAP>
 __device__ __forceinline__ void lin_prep_chunk(const T *dO, const T *Out, const T *K, const float *den, T *dn,
                                                float *dd, float *cs, int c, int L, float (*red)[E + 1], int Ea,
                                                int Ma) {
-    constexpr int VEC = 16 / sizeof(T), TPR = E / VEC, P = 256 / TPR;
-    const int t = threadIdx.x, l = t & 15;
-    for (int i = c * C + (t >> 4); i < (c + 1) * C; i += 16) {
-        if (i >= L) {
-            if (l == 0) dd[i] = 0.f;
-            continue;
-        }
-        const float d = den[i];
-        float acc = 0.f;
+    constexpr int VEC = 16 / sizeof(T), TPM = M / VEC, RPM = 256 / TPM, TPR = E / VEC, P = 256 / TPR;
+    typedef T tv __attribute__((__vector_size__(16)));
+    const int t = threadIdx.x;
+    {
+        const int cm = t % TPM, pr = t / TPM;
+        const bool mv = cm * VEC < Ma;
 #pragma unroll
-        for (int m = l; m < M; m += 16) {
-            if (m < Ma) {
-                const float gv = (float)dO[(int64_t)i * Ma + m];
-                acc += gv * (float)Out[(int64_t)i * Ma + m];
-                dn[(int64_t)i * Ma + m] = (T)(gv / d);
+        for (int ii = pr; ii < C; ii += RPM) {
+            const int i = c * C + ii;
+            const bool live = i < L && mv;
+            const float d = i < L ? den[i] : 1.f;
+            float acc = 0.f;
+            if (live) {
+                const int64_t off = (int64_t)i * Ma + cm * VEC;
+                const tv gv = *reinterpret_cast<const tv *>(dO + off);
+                const tv ov = *reinterpret_cast<const tv *>(Out + off);
+                tv nv;
+#pragma unroll
+                for (int j = 0; j < VEC; ++j) {
+                    acc += (float)gv[j] * (float)ov[j];
+                    nv[j] = (T)((float)gv[j] / d);
+                }
+                *reinterpret_cast<tv *>(dn + off) = nv;
             }
-        }
 #pragma unroll
-        for (int x = 8; x >= 1; x >>= 1) acc += __shfl_xor(acc, x, 16);
-        if (l == 0) dd[i] = -acc / d;
+            for (int x = TPM / 2; x >= 1; x >>= 1) acc += __shfl_xor(acc, x, TPM);
+            if (cm == 0) dd[i] = i < L ? -acc / d : 0.f;
+        }
     }
     const int cg = t % TPR, p = t / TPR;
+    const bool ev = cg * VEC < Ea;
     float acc[VEC];
 #pragma unroll
     for (int j = 0; j < VEC; ++j) acc[j] = 0.f;
-    for (int i = c * C + p; i < (c + 1) * C && i < L && cg * VEC < Ea; i += P) {
-        T x[VEC];
-        *reinterpret_cast<int4 *>(x) = *reinterpret_cast<const int4 *>(K + (int64_t)i * Ea + cg * VEC);
+    if (ev) {
+        for (int i = c * C + p; i < (c + 1) * C && i < L; i += P) {
+            const tv x = *reinterpret_cast<const tv *>(K + (int64_t)i * Ea + cg * VEC);
 #pragma unroll
-        for (int j = 0; j < VEC; ++j) acc[j] += FMAP ? (float)(T)phi((float)x[j]) : (float)x[j];
+            for (int j = 0; j < VEC; ++j) acc[j] += FMAP ? (float)(T)phi((float)x[j]) : (float)x[j];
+        }
     }
 #pragma unroll
     for (int j = 0; j < VEC; ++j) red[p][cg * VEC + j] = acc[j];
@@ -73,8 +85,9 @@ __global__ __launch_bounds__(256) void cp_lin_prep_kernel(const T *__restrict__ 
                                                           T *__restrict__ dn, float *__restrict__ dd,
                                                           float *__restrict__ cs, int L, int Lpad, int NS, int Ea,
                                                           int Ma) {
-    constexpr int VEC = 16 / sizeof(T), TPR = E / VEC, P = 256 / TPR;
-    static_assert(E % VEC == 0 && 256 % TPR == 0 && C % 16 == 0, "prep layout");
+    constexpr int VEC = 16 / sizeof(T), TPR = E / VEC, P = 256 / TPR, TPM = M / VEC;
+    static_assert(E % VEC == 0 && 256 % TPR == 0 && M % VEC == 0 && TPM <= 64 && 256 % TPM == 0 && C % 16 == 0,
+                  "prep layout");
     __shared__ float red[P][E + 1];
     const int nch = Lpad / C;
     for (int64_t blk = blockIdx.x; blk < (int64_t)nch * NS; blk += gridDim.x) {
@@ -97,12 +110,16 @@ __device__ __forceinline__ void lin_zscan_slice(const float *z_in, float *zc, in
     const int e = threadIdx.x % E, p = threadIdx.x / E;
     const int c0 = (int)((int64_t)nch * p / P), c1 = (int)((int64_t)nch * (p + 1) / P);
     float *col = zc + e;
+    // (the loads of both passes are independent of the running sum: unrolled
+    // so that several are in flight)
     float sum = 0.f;
+#pragma unroll 8
     for (int c = c0; c < c1; ++c) sum += col[(int64_t)c * E];
     tot[p][e] = sum;
     __syncthreads();
     float z = z_in && e < Ea ? z_in[e] : 0.f;
     for (int q = 0; q < p; ++q) z += tot[q][e];
+#pragma unroll 8
     for (int c = c0; c < c1; ++c) {
         const float x = col[(int64_t)c * E];
         col[(int64_t)c * E] = z;

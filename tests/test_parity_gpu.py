@@ -15,8 +15,9 @@ import workloads as W
 
 pytestmark = pytest.mark.gpu
 
-TOL = {"f32": 1e-4, "bf16": 2e-2}
-TORCH = {"f32": torch.float32, "bf16": torch.bfloat16}
+# fp16: the bf16 bar scaled by the ratio of the unit roundoffs (2^-11 / 2^-8)
+TOL = {"f32": 1e-4, "bf16": 2e-2, "f16": 2.5e-3}
+TORCH = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
 
 
 @pytest.fixture(scope="module")

@@ -54,7 +54,8 @@ class Workload:
 # The workloads: a tiny fp32 forward, an fp32 forward, the bf16
 # forward+backward at L=4096 E=M=64 (the headline), bf16 normalised linear
 # attention at L=16384 E=M=128, an fp32 forward+backward with E != M, and the
-# normalised form's forward+backward in bf16 at the headline shape.
+# normalised form's forward+backward in bf16 at the headline shape; the
+# headline shape in fp16 and with 80-wide heads.
 WORKLOADS = {
     w.name: w
     for w in (
@@ -68,6 +69,9 @@ WORKLOADS = {
         # the normalised form's forward and backward at the headline shape
         Workload("linattn_fwdbwd_bf16_l4096_e64", "linattn+bwd", "bf16", 8, 16, 4096, 64, 64, seed=5,
                  qk="raw"),
+        # the headline shape in fp16, and with 80-wide heads (run on 128-wide tiles)
+        Workload("fwdbwd_f16_l4096_e64", "fwd+bwd", "f16", 8, 16, 4096, 64, 64, seed=6),
+        Workload("fwdbwd_bf16_l4096_e80", "fwd+bwd", "bf16", 8, 16, 4096, 80, 80, seed=7),
     )
 }
 HEADLINE = "fwdbwd_bf16_l4096_e64"
