@@ -52,7 +52,7 @@
 #define CP_F32_WIDE_FC 32
 #endif
 #ifndef CP_F32_WIDE_BC
-#define CP_F32_WIDE_BC 16
+#define CP_F32_WIDE_BC 32
 #endif
 #ifndef CP_F32_BG
 #define CP_F32_BG 2
@@ -122,8 +122,10 @@ template <int E, int M> struct Tune<__bf16, E, M> {
 // fp16 I/O moves and computes exactly like bf16 I/O.
 template <int E, int M> struct Tune<_Float16, E, M> : Tune<__bf16, E, M> {};
 
-// fp32 tiles are twice as large in LDS and registers: the widest heads use
-// shorter chunks.
+// fp32 tiles are twice as large in LDS and registers: the forward over the
+// widest heads uses shorter chunks.  (The backward over them keeps 32-row
+// chunks: 16-row chunks measured 545 us against 447 us on the fp32
+// E = 32, M = 128, L = 2048 fwd+bwd workload.)
 template <int E, int M> struct Tune<float, E, M> {
     static constexpr bool wide = E > 64 || M > 64;
     static constexpr int FC = wide ? CP_F32_WIDE_FC : CP_F32_FC;
