@@ -241,8 +241,19 @@ __device__ __forceinline__ void fwd_sweep(const T *q_, const T *k_, const T *v_,
 // exclusive sum of the increments of the segments before it (the chunked
 // scan's carry, one level up) and sweeps only its own rows.  ws holds, per slice and segment, E*M floats of dS (row e,
 // column m) then E floats of dz.  With one segment, ws is unused (NULL).
+#ifndef CP_FWD_WIDE_NORM_MINWG
+#define CP_FWD_WIDE_NORM_MINWG 2
+#endif
+// Workgroups per CU the compiler must leave room for: two for the normalised
+// sweep over 128 x 128 16-bit heads, whose registers otherwise exceed half a
+// SIMD's file (278 VGPRs) and let only one four-wave workgroup onto a CU.
+template <typename T, int E, int M, bool NORM, bool SONLY>
+constexpr int fwd_min_wg() {
+    return NORM && !SONLY && E == 128 && M == 128 && sizeof(T) == 2 ? CP_FWD_WIDE_NORM_MINWG : 1;
+}
+
 template <typename T, int E, int M, int C, int G, int RSPLIT, int NPF, bool NORM, bool FMAP, bool SONLY>
-__global__ __launch_bounds__(64 * (M / 16 / G) * RSPLIT) void cp_fwd_kernel(
+__global__ __launch_bounds__(64 * (M / 16 / G) * RSPLIT, (fwd_min_wg<T, E, M, NORM, SONLY>())) void cp_fwd_kernel(
     const T *__restrict__ Q, const T *__restrict__ K, const T *__restrict__ V, T *__restrict__ Out,
     const float *__restrict__ state_in, const float *__restrict__ z_in, float *__restrict__ state_out,
     float *__restrict__ z_out, float *__restrict__ den, float *__restrict__ ws, int L, int NS, int seg_len,

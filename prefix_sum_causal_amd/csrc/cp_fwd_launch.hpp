@@ -11,12 +11,18 @@ namespace cp {
 // Segments per slice for L rows and NS slices: one, unless the slices leave
 // most CUs idle; then enough segments of at least kMinSegChunks chunks for
 // about two workgroups per CU.
-constexpr int kCUs = 256, kMinSegChunks = 4;
+#ifndef CP_SEG_MIN_CHUNKS
+#define CP_SEG_MIN_CHUNKS 4
+#endif
+#ifndef CP_SEG_WG_PER_CU
+#define CP_SEG_WG_PER_CU 2
+#endif
+constexpr int kCUs = 256, kMinSegChunks = CP_SEG_MIN_CHUNKS, kSegWgPerCU = CP_SEG_WG_PER_CU;
 inline int fwd_segments(int L, int NS, int groups, int C) {
     const long wg = (long)NS * groups;
     const int nchunks = (L + C - 1) / C;
     if (wg >= kCUs || nchunks < 2 * kMinSegChunks) return 1;
-    long want = (2L * kCUs + wg - 1) / wg;
+    long want = ((long)kSegWgPerCU * kCUs + wg - 1) / wg;
     const long most = nchunks / kMinSegChunks;
     return (int)(want < most ? want : most);
 }
