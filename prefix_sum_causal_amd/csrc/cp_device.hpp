@@ -340,9 +340,12 @@ struct Stage {
                 constexpr int n = 16 / (int)sizeof(T);
                 typedef T tn __attribute__((__vector_size__(16)));
                 tn e = __builtin_bit_cast(tn, x);
-                const bool valid = row0 + row < L && cp * VEC < wa;
+                // rows at or past L and padding columns were loaded as zero;
+                // phi(0) = 1 is cancelled by a 0/1 factor rather than a
+                // branch, so the piece is mapped with straight-line code
+                const float keep = row0 + row < L && cp * VEC < wa ? 1.f : 0.f;
 #pragma unroll
-                for (int j = 0; j < n; ++j) e[j] = valid ? (T)phi((float)e[j]) : (T)0.f;
+                for (int j = 0; j < n; ++j) e[j] = (T)(phi((float)e[j]) * keep);
                 x = __builtin_bit_cast(i32x4, e);
             }
             *reinterpret_cast<i32x4 *>(lds + row * RS + cp * (16 / (int)sizeof(T))) = x;
