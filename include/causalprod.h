@@ -177,7 +177,9 @@ int linear_attn_bwd(const void *Q, const void *K, const void *V, const void *Out
 /* Static, NUL-terminated description of a cp_status value (never NULL). */
 const char *cp_status_string(int status);
 
-/* Version of this ABI: (major << 16) | minor. */
+/* Version of this ABI: (major << 16) | minor.  3.0: carried states and the
+ * normalised backward; 3.1: CP_F16 and head sizes between the tile sizes
+ * (both additions: every 3.0 call behaves as before). */
 int cp_abi_version(void);
 
 /*
