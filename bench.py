@@ -110,6 +110,10 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold-steps", type=int, default=5,
+                    help="after the timed region, this many more steps with every call preceded by a 1 GiB "
+                         "read that evicts the caches (the 256 MB MALL included); their per-call times are "
+                         "reported as cold_cache")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="run one plain device-to-device copy of this many MiB first (reference for the "
                          "HBM byte counters of a profiler run)")
@@ -204,6 +208,28 @@ def main() -> int:
         b = algorithmic_bytes(w, kind)
         per_kernel[kind] = {"avg_us": times[kind] * 1e6, "alg_bytes": b, "GBps": b / times[kind] / 1e9,
                             "launches": n_launch[kinds.index(kind)]}
+    # Cold caches: each call again, after reading 1 GiB (more than L2 and
+    # the MALL hold), so that no input is found in a cache.  The eviction is a
+    # read, not a write: a write would leave the caches full of dirty lines
+    # that the call would then have to write back.  Reported beside the
+    # back-to-back figures; `value` and `roofline` stay the latter.
+    cold = None
+    if args.cold_steps > 0:
+        flush = torch.ones(1 << 28, device="cuda", dtype=torch.float32)
+        sink = torch.empty((), device="cuda", dtype=torch.float32)
+        acc = {kind: 0.0 for kind in kinds}
+        for i in range(args.cold_steps):
+            for kind, c, nl in zip(kinds, calls, n_launch):
+                torch.sum(flush, dim=0, out=sink)
+                cp.timing_begin(nl)
+                c()
+                acc[kind] += sum(cp.timing_end()) * 1e-3
+        torch.cuda.synchronize()
+        del flush, sink
+        cold = {kind: {"avg_us": acc[kind] / args.cold_steps * 1e6,
+                       "GBps": algorithmic_bytes(w, kind) / (acc[kind] / args.cold_steps) / 1e9,
+                       "frac": algorithmic_bytes(w, kind) / (acc[kind] / args.cold_steps) / 1e9 / HBM_PEAK_GBS}
+                for kind in kinds}
     dom = max(kinds, key=lambda k: times[k])
     achieved = per_kernel[dom]["GBps"]
     kernel_name = {"fwd": "cp_fwd_kernel", "bwd": "cp_bwd_kernel", "linattn": "cp_fwd_kernel",
@@ -226,6 +252,7 @@ def main() -> int:
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic_for(dom, name)},
         "kernels": per_kernel,
+        "cold_cache": cold,
     }
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w)
