@@ -4,11 +4,16 @@
 
 A step is one forward (writing the final state) plus one backward (reading
 it) over the whole batch of the workload, inputs resident in HBM.  W untimed
-steps, then K timed steps between device synchronisations.  Prints one JSON
-line with the whole-job tokens*heads/s, the roofline of the dominant kernel
-(algorithmic bytes per launch / average launch time, from HIP events on the
-stream the kernels run on) and the fp64 CPU oracle timed on a bounded sample
-of the same workload on this host's cores.
+steps, then K timed steps launched back to back between device
+synchronisations: `value` is K * N*H*L over that wall time.  Per-kernel
+durations come from a second pass of K steps in which every launch carries its
+own start/end events on the stream it runs on (the library's timing hook,
+which costs host time per launch and is therefore kept out of `value`).
+Prints one JSON line with the whole-job tokens*heads/s, the roofline of the
+dominant kernel (algorithmic bytes, and flops, per launch / its average launch
+time), a plain device copy timed in the same run, and the fp64 CPU oracle
+timed on a bounded sample of the same workload's own slices on this host's
+cores (all of them, and one).
 """
 from __future__ import annotations
 
@@ -23,10 +28,14 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+# dense matrix peaks (TFLOP/s) by the type a product is defined in
+MFMA_PEAK_TFS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}
 METRIC = "causal-product fwd+bwd tokens·heads/s and % HBM/MFMA roofline, L=4096 E=M=64"
 UNIT = "tokens·heads/s"
 COUNTERS = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 KERNEL_SOURCES = ("cp_device.hpp", "cp_fwd.hpp", "cp_fwd_launch.hpp", "cp_bwd.hpp", "cp_bwd_launch.hpp", "cp_tune.hpp")
+KERNEL_NAME = {"fwd": "cp_fwd_kernel", "bwd": "cp_bwd_kernel", "linattn": "cp_fwd_kernel",
+               "linattn_bwd": "cp_lin_prep_kernel + cp_lin_zscan_kernel + cp_bwd_kernel"}
 
 
 def kernel_digest() -> str:
@@ -56,6 +65,18 @@ def algorithmic_bytes(w, kind: str) -> int:
     raise ValueError(kind)
 
 
+def algorithmic_flops(w, kind: str) -> int:
+    """Multiply-adds of the recurrence itself (two flops each), per call:
+    forward 4EM per token*head (state update k v^T, read-out q^T S);
+    backward 10EM (S again, dq, the suffix state R, dk, dv); the normaliser
+    adds its running sum, dot product and division (3E + M), and its backward
+    runs the causal-product backward on M + 1 columns plus the per-row terms."""
+    th = w.N * w.H * w.L
+    E, M = w.E, w.M
+    return th * {"fwd": 4 * E * M, "bwd": 10 * E * M, "linattn": 4 * E * M + 3 * E + M,
+                 "linattn_bwd": 10 * E * (M + 1) + 3 * M}[kind]
+
+
 def traffic_for(kernel: str, workload: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it
     was taken on the current kernel sources; else None."""
@@ -70,37 +91,69 @@ def traffic_for(kernel: str, workload: str):
     return None if entry is None else entry.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, target_seconds: float = 15.0) -> dict:
-    """The fp64 oracle (forward recurrence + backward sweeps) on a bounded
-    sample of the workload's slices, scaled to tokens*heads/s."""
+def copy_rate(torch, mib: int = 1024, reps: int = 5) -> dict:
+    """A plain device-to-device copy of `mib` MiB (read + write, larger than
+    the caches), timed with events on the current stream: the practical
+    streaming rate of this GPU in the same run."""
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, device="cuda", dtype=torch.float32)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    ts = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        dst.copy_(src)
+        b.record()
+        b.synchronize()
+        ts.append(a.elapsed_time(b) * 1e-3)
+    del src, dst
+    t = sorted(ts)[len(ts) // 2]
+    moved = 2 * mib * (1 << 20)
+    return {"GBps": moved / t / 1e9, "bytes_moved": moved, "us": t * 1e6, "what": f"torch copy_ of {mib} MiB fp32, "
+            f"median of {reps}"}
+
+
+def cpu_baseline(w, host, target_seconds: float = 15.0) -> dict:
+    """The fp64 oracle (the recurrences the workload's calls compute) on a
+    bounded sample of the workload's own (n, h) slices, scaled to
+    tokens*heads/s: as many slices as the oracle has threads (one slice per
+    thread), repeated for about target_seconds; and one slice on one thread."""
     import numpy as np
 
     import oracle
-    import workloads as W
 
     orc = oracle.default()
     threads = orc.num_threads()
-    ws = w.with_shape(N=1, H=threads)
-    d = W.generate(ws, need_do=True)
-    slices = 0
-    t0 = time.perf_counter()
-    while True:
-        if w.op.startswith("linattn"):
-            orc.linattn(d["Q"], d["K"], d["V"], 1e-6, 1)
-            if w.op == "linattn+bwd":
-                orc.linattn_bwd(d["Q"], d["K"], d["V"], d["dO"], 1e-6, 1)
-        else:
-            orc.fwd(d["Q"], d["K"], d["V"])
-            if w.op == "fwd+bwd":
-                orc.bwd(d["Q"], d["K"], d["V"], d["dO"])
-        slices += ws.H
-        el = time.perf_counter() - t0
-        if el >= target_seconds:
-            break
-    return {"value": slices * w.L / el, "unit": UNIT, "cores": threads, "kind": "oracle",
-            "sample": f"{slices} (n,h) slices at full L={w.L} ({threads} distinct slices of the workload, "
-                      f"repeated), fp64 recurrence ({w.op}), "
-                      f"{el:.1f} s on {threads} threads"}
+    T = min(threads, w.N * w.H)
+
+    def take(name, n):  # host[name] holds the first slices, [slices][L][features]
+        return np.ascontiguousarray(host[name][:n])
+
+    def run(n, seconds):
+        d = {k: take(k, n) for k in host}
+        slices, t0 = 0, time.perf_counter()
+        while True:
+            if w.op.startswith("linattn"):
+                orc.linattn(d["Q"], d["K"], d["V"], 1e-6, 1)
+                if w.op == "linattn+bwd":
+                    orc.linattn_bwd(d["Q"], d["K"], d["V"], d["dO"], 1e-6, 1)
+            else:
+                orc.fwd(d["Q"], d["K"], d["V"])
+                if w.op == "fwd+bwd":
+                    orc.bwd(d["Q"], d["K"], d["V"], d["dO"])
+            slices += n
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                return slices * w.L / el, slices, el
+
+    value, slices, el = run(T, target_seconds)
+    one, slices1, el1 = run(1, max(2.0, target_seconds / 3))
+    return {"value": value, "unit": UNIT, "cores": threads, "kind": "oracle",
+            "sample": f"the workload's first {T} (n,h) slices at full L={w.L}, one per thread, repeated "
+                      f"({slices} slice passes in {el:.1f} s), fp64 recurrences ({w.op})",
+            "one_thread": {"value": one, "unit": UNIT, "cores": 1,
+                           "sample": f"slice (0,0), {slices1} passes in {el1:.1f} s"}}
 
 
 def main() -> int:
@@ -133,6 +186,9 @@ def main() -> int:
     tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[w.dtype]
     d = W.generate(w, need_do=w.op.endswith("bwd"))
     dev = {k: torch.from_numpy(v).to("cuda").to(tdt) for k, v in d.items()}
+    # the host copies of the first slices stay for the CPU baseline
+    keep = min(64, w.N * w.H)
+    host = {k: v.reshape((w.N * w.H,) + v.shape[2:])[:keep].copy() for k, v in d.items()}
     del d
     q, k, v = dev["Q"], dev["K"], dev["V"]
     out = torch.empty_like(v)
@@ -158,6 +214,8 @@ def main() -> int:
             cp.linear_attn_bwd(q, k, v, out, g, den, 1, state_final=state, dq=dq, dk=dk, dv=dv)
 
     calls = [fwd_call] + ([bwd_call] if w.op.endswith("bwd") else [])
+    kinds = {"fwd+bwd": ["fwd", "bwd"], "fwd": ["fwd"], "linattn": ["linattn"],
+             "linattn+bwd": ["linattn", "linattn_bwd"]}[w.op]
 
     def step():
         for c in calls:
@@ -172,17 +230,31 @@ def main() -> int:
         torch.cuda.synchronize()
         del src, dst
 
+    copy = copy_rate(torch)
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    kinds = {"fwd+bwd": ["fwd", "bwd"], "fwd": ["fwd"], "linattn": ["linattn"],
-             "linattn+bwd": ["linattn", "linattn_bwd"]}[w.op]
-    # Each launch in the timed region carries its own start/end events (the
-    # timestamps of its dispatch on the stream it runs on, as a profiler's
-    # kernel trace reports them); the whole-step rate is wall time.
-    # Launches per call: a forward over few slices is two launches (segment
-    # states, then the sweep), the normalised backward three (per-row terms,
-    # z scan, sweep); count them on one untimed step.
+
+    # Timed region: K steps back to back, no timing hook.  Device time of the
+    # region from two events on the stream the calls run on.
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record()
+    for i in range(args.steps):
+        step()
+    ev1.record()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    device_s = ev0.elapsed_time(ev1) * 1e-3
+
+    # Per-kernel durations: the same K steps again, each launch with its own
+    # start/end events (the timestamps of its dispatch on the stream it runs
+    # on, as a profiler's kernel trace reports them).  Launches per call: a
+    # forward over few slices is two launches (segment states, then the
+    # sweep), the normalised backward three (per-row terms, z scan, sweep);
+    # count them on one untimed step.
     n_launch = []
     for c in calls:
         cp.timing_begin(64)
@@ -190,13 +262,11 @@ def main() -> int:
         n_launch.append(len(cp.timing_end()))
     per_step = sum(n_launch)
     cp.timing_begin(args.steps * per_step)
-    t0 = time.perf_counter()
     for i in range(args.steps):
         step()
     torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
     ms = cp.timing_end()
-    assert len(ms) == args.steps * per_step, "every timed launch is recorded"
+    assert len(ms) == args.steps * per_step, "every hooked launch is recorded"
     # a call's time is the sum of its launches
     times, off = {}, 0
     for kind, nl in zip(kinds, n_launch):
@@ -206,7 +276,9 @@ def main() -> int:
     per_kernel = {}
     for kind in kinds:
         b = algorithmic_bytes(w, kind)
+        f = algorithmic_flops(w, kind)
         per_kernel[kind] = {"avg_us": times[kind] * 1e6, "alg_bytes": b, "GBps": b / times[kind] / 1e9,
+                            "alg_flops": f, "TFps": f / times[kind] / 1e12,
                             "launches": n_launch[kinds.index(kind)]}
     # Cold caches: each call again, after reading 1 GiB (more than L2 and
     # the MALL hold), so that no input is found in a cache.  The eviction is a
@@ -232,8 +304,15 @@ def main() -> int:
                 for kind in kinds}
     dom = max(kinds, key=lambda k: times[k])
     achieved = per_kernel[dom]["GBps"]
-    kernel_name = {"fwd": "cp_fwd_kernel", "bwd": "cp_bwd_kernel", "linattn": "cp_fwd_kernel",
-                   "linattn_bwd": "cp_lin_prep_kernel + cp_lin_zscan_kernel + cp_bwd_kernel"}[dom]
+    hbm_frac = achieved / HBM_PEAK_GBS
+    mfma_peak = MFMA_PEAK_TFS[w.dtype]
+    mfma_frac = per_kernel[dom]["TFps"] / mfma_peak
+    hbm = {"bound": "hbm", "kernel": KERNEL_NAME[dom], "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+           "frac": hbm_frac, "traffic": traffic_for(dom, name), "frac_of_copy": achieved / copy["GBps"]}
+    mfma = {"bound": "mfma", "kernel": KERNEL_NAME[dom], "achieved": per_kernel[dom]["TFps"], "peak": mfma_peak,
+            "unit": "TFLOP/s", "frac": mfma_frac}
+    roof = dict(hbm if hbm_frac >= mfma_frac else mfma)
+    roof["other"] = mfma if roof["bound"] == "hbm" else hbm
     rec = {
         "metric": METRIC,
         "value": args.steps * w.token_heads / elapsed,
@@ -242,20 +321,21 @@ def main() -> int:
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": elapsed / args.steps * 1e3,
+        "device_ms_per_step": device_s / args.steps * 1e3,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": w.dtype,
-        "data": "synthetic (seeded N(0,1) draws; Q,K = elu(x)+1)",
+        "data": "synthetic (seeded N(0,1) draws; Q,K = elu(x)+1)" if w.qk == "elu1" else
+                "synthetic (seeded N(0,1) draws; raw Q,K, feature map applied in the op)",
         "config": {"workload": name, "op": w.op, "N": w.N, "H": w.H, "L": w.L, "E": w.E, "M": w.M},
-        "roofline": {"bound": "hbm", "kernel": kernel_name, "achieved": achieved, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": traffic_for(dom, name)},
+        "roofline": roof,
+        "copy": copy,
         "kernels": per_kernel,
         "cold_cache": cold,
     }
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(w)
+        rec["cpu_baseline"] = cpu_baseline(w, host)
     print(json.dumps(rec), flush=True)
     return 0
 

@@ -179,7 +179,8 @@ const char *cp_status_string(int status);
 
 /* Version of this ABI: (major << 16) | minor.  3.0: carried states and the
  * normalised backward; 3.1: CP_F16 and head sizes between the tile sizes
- * (both additions: every 3.0 call behaves as before). */
+ * (both additions: every 3.0 call behaves as before); 4.0: cp_timing_end
+ * takes the capacity of the caller's buffer. */
 int cp_abi_version(void);
 
 /*
@@ -193,15 +194,18 @@ int cp_abi_version(void);
  * is discarded.  CP_ERR_DIM for a bad capacity, CP_ERR_HIP if events cannot be
  * created.
  *
- * cp_timing_end(ms, count): waits for the recorded launches, writes the
- * duration in milliseconds of each, in launch order, to ms[0 .. *count) (ms
- * holds at least `capacity` floats, owned by the caller), releases the events
- * and stops recording.  *count is the number of launches recorded (launches
- * beyond the capacity are not timed).  CP_ERR_NULL for NULL arguments or when
- * no timing was begun; CP_ERR_HIP if waiting fails.
+ * cp_timing_end(ms, ms_capacity, count): waits for the recorded launches,
+ * writes the duration in milliseconds of each, in launch order, to
+ * ms[0 .. *count) (ms holds ms_capacity floats, owned by the caller; at most
+ * that many are written), releases the events and stops recording.  *count is
+ * the number of durations written: the launches recorded (those beyond the
+ * begin capacity are not timed), cut to ms_capacity.  CP_ERR_NULL for NULL
+ * arguments or when the calling thread began no timing; CP_ERR_DIM for
+ * ms_capacity < 1; CP_ERR_HIP if waiting fails.  The timing state is per
+ * thread: a timing begun on one thread is ended on that thread.
  */
 int cp_timing_begin(int capacity);
-int cp_timing_end(float *ms, int *count);
+int cp_timing_end(float *ms, int ms_capacity, int *count);
 
 #ifdef __cplusplus
 }

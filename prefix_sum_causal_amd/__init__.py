@@ -7,11 +7,16 @@ checks tensors, allocates outputs through PyTorch and passes raw device
 pointers and the current HIP stream.  There is no fallback: if the library is
 missing the import fails.
 
-Functions with the ABI's names:
-    causal_product_fwd(q, k, v, out=None, state_out=None)
-    causal_product_bwd(q, k, v, dout, state_in=None, dq=None, dk=None, dv=None)
-    linear_attn_fwd(q, k, v, eps=1e-6, feature_map=1, out=None)
-and autograd wrappers ``causal_product(q, k, v)`` and
+Functions with the ABI's names (optional tensors and outputs are keyword-only):
+    causal_product_fwd(q, k, v, *, out=None, state_in=None, state_out=None)
+    causal_product_bwd(q, k, v, dout, *, state_final=None, state_in=None,
+                       dq=None, dk=None, dv=None, dstate_in=None)
+    linear_attn_fwd(q, k, v, eps=1e-6, feature_map=1, *, out=None, state_in=None,
+                    z_in=None, state_out=None, z_out=None, den_out=None)
+    linear_attn_bwd(q, k, v, out, dout, den, feature_map=1, *, state_in=None,
+                    z_in=None, state_final=None, dq=None, dk=None, dv=None,
+                    dstate_in=None, dz_in=None)
+and autograd wrappers ``causal_product(q, k, v, state0=None)`` and
 ``linear_attention(q, k, v, eps=1e-6, feature_map="elu+1")``.
 
 Tensors are [N, H, L, E] (q, k) and [N, H, L, M] (v), contiguous, on the GPU,
@@ -23,6 +28,7 @@ from __future__ import annotations
 
 import ctypes
 import os
+import threading
 
 import torch
 
@@ -57,7 +63,7 @@ lib.cp_abi_version.argtypes = []
 lib.cp_abi_version.restype = _int
 lib.cp_timing_begin.argtypes = [_int]
 lib.cp_timing_begin.restype = _int
-lib.cp_timing_end.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.POINTER(_int)]
+lib.cp_timing_end.argtypes = [ctypes.POINTER(ctypes.c_float), _int, ctypes.POINTER(_int)]
 lib.cp_timing_end.restype = _int
 
 
@@ -113,20 +119,22 @@ def timing_begin(capacity: int) -> None:
     """Record the start and end of each of the next ``capacity`` kernel
     launches made by this thread (their dispatch timestamps)."""
     _check("cp_timing_begin", lib.cp_timing_begin(int(capacity)))
-    global _timing_capacity
-    _timing_capacity = int(capacity)
+    _timing.capacity = int(capacity)
 
 
 def timing_end() -> list:
-    """Wait for the launches recorded since timing_begin and return their
-    durations in milliseconds, in launch order."""
-    buf = (ctypes.c_float * max(1, _timing_capacity))()
+    """Wait for the launches recorded since this thread's timing_begin and
+    return their durations in milliseconds, in launch order."""
+    cap = max(1, getattr(_timing, "capacity", 0))
+    buf = (ctypes.c_float * cap)()
     n = _int(0)
-    _check("cp_timing_end", lib.cp_timing_end(buf, ctypes.byref(n)))
+    _check("cp_timing_end", lib.cp_timing_end(buf, cap, ctypes.byref(n)))
+    _timing.capacity = 0
     return [buf[i] for i in range(n.value)]
 
 
-_timing_capacity = 0
+# the capacity of this thread's timing (the library keeps its timing state per thread)
+_timing = threading.local()
 
 
 def _check_state(name, t, shape, device):
@@ -136,7 +144,7 @@ def _check_state(name, t, shape, device):
         raise ValueError(f"{name} must be a contiguous float32 {list(shape)} tensor on q's device")
 
 
-def causal_product_fwd(q, k, v, out=None, state_in=None, state_out=None):
+def causal_product_fwd(q, k, v, *, out=None, state_in=None, state_out=None):
     """out_i = q_i^T S_i with S_i = S0 + sum_{j<=i} k_j v_j^T.  ``state_in``
     (fp32 [N,H,E,M], optional, None = zero) is S0; ``state_out`` (optional)
     receives the final state S_{L-1}."""
@@ -154,7 +162,7 @@ def causal_product_fwd(q, k, v, out=None, state_in=None, state_out=None):
     return out
 
 
-def causal_product_bwd(q, k, v, dout, state_final=None, state_in=None, dq=None, dk=None, dv=None,
+def causal_product_bwd(q, k, v, dout, *, state_final=None, state_in=None, dq=None, dk=None, dv=None,
                        dstate_in=None):
     """Gradients (dq, dk, dv) of sum(out * dout) for out = causal_product_fwd(q, k, v, state_in=S0).
     ``state_final``: optional final state from causal_product_fwd's state_out;
@@ -176,7 +184,7 @@ def causal_product_bwd(q, k, v, dout, state_final=None, state_in=None, dq=None, 
     return dq, dk, dv
 
 
-def linear_attn_fwd(q, k, v, eps: float = 1e-6, feature_map: int = 1, out=None, state_in=None, z_in=None,
+def linear_attn_fwd(q, k, v, eps: float = 1e-6, feature_map: int = 1, *, out=None, state_in=None, z_in=None,
                     state_out=None, z_out=None, den_out=None):
     """out_i = phi(q_i)^T S_i / (phi(q_i) . z_i + eps) with phi = elu + 1
     (feature_map=1) or the identity (feature_map=0) applied to the raw q, k.
@@ -199,7 +207,7 @@ def linear_attn_fwd(q, k, v, eps: float = 1e-6, feature_map: int = 1, out=None, 
     return out
 
 
-def linear_attn_bwd(q, k, v, out, dout, den, feature_map: int = 1, state_in=None, z_in=None, state_final=None,
+def linear_attn_bwd(q, k, v, out, dout, den, feature_map: int = 1, *, state_in=None, z_in=None, state_final=None,
                     dq=None, dk=None, dv=None, dstate_in=None, dz_in=None):
     """Gradients (dq, dk, dv) of sum(out * dout) for out = linear_attn_fwd(q, k, v, ...),
     with respect to the raw q, k (through phi), v; ``den`` is the forward's

@@ -17,7 +17,8 @@
 
 namespace {
 
-constexpr int kAbiMajor = 3, kAbiMinor = 1;  // 3.0: carried state, normalised backward; 3.1: fp16 I/O
+constexpr int kAbiMajor = 4, kAbiMinor = 0;  // 3.0: carried state, normalised backward; 3.1: fp16 I/O;
+                                             // 4.0: cp_timing_end bounded by the caller's buffer
 
 struct Range {
     uintptr_t lo, hi;  // [lo, hi)
@@ -149,10 +150,11 @@ int cp_timing_begin(int capacity) {
     return CP_OK;
 }
 
-int cp_timing_end(float *ms, int *count) {
+int cp_timing_end(float *ms, int ms_capacity, int *count) {
     if (!ms || !count || !timing.on) return CP_ERR_NULL;
+    if (ms_capacity < 1) return CP_ERR_DIM;
     int st = CP_OK;
-    const int n = timing.used;
+    const int n = timing.used < ms_capacity ? timing.used : ms_capacity;
     for (int i = 0; i < n && st == CP_OK; ++i) {
         if (hipEventSynchronize(timing.stop[i]) != hipSuccess ||
             hipEventElapsedTime(&ms[i], timing.start[i], timing.stop[i]) != hipSuccess)

@@ -54,20 +54,20 @@ def test_status_strings_and_version(lib):
         assert msg and msg not in seen
         seen.add(msg)
     assert lib.cp_status_string(99).decode() == "unknown status"
-    assert lib.cp_abi_version() == (3 << 16) | 1
+    assert lib.cp_abi_version() == (4 << 16) | 0
 
 
 def test_timing_rejects_bad_arguments_before_any_device_call(lib):
     lib.cp_timing_begin.argtypes = [ctypes.c_int]
-    lib.cp_timing_end.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    lib.cp_timing_end.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
     assert lib.cp_timing_begin(0) == DIM
     assert lib.cp_timing_begin(-3) == DIM
     assert lib.cp_timing_begin(65537) == DIM
     ms = (ctypes.c_float * 4)()
     n = ctypes.c_int(7)
-    assert lib.cp_timing_end(None, ctypes.byref(n)) == NULL
-    assert lib.cp_timing_end(ms, None) == NULL
-    assert lib.cp_timing_end(ms, ctypes.byref(n)) == NULL  # nothing begun
+    assert lib.cp_timing_end(None, 4, ctypes.byref(n)) == NULL
+    assert lib.cp_timing_end(ms, 4, None) == NULL
+    assert lib.cp_timing_end(ms, 4, ctypes.byref(n)) == NULL  # nothing begun
 
 
 # fake, 16-byte aligned, disjoint addresses (never dereferenced)
