@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "cp_validate.hpp"
+
 namespace cp {
 
 struct FwdArgs {
@@ -52,13 +54,5 @@ bwd_fn bwd_f16(int E, int M, bool norm);
 // has a timing in progress (cp_timing_begin), hipExtLaunchKernel with the
 // next pair of timing events.
 hipError_t launch_kernel(const void *kernel, dim3 grid, dim3 block, void **args, hipStream_t stream);
-
-// Index 0..3 of the kernel tile size {16, 32, 64, 128} that runs a head of
-// x features: the smallest one >= x; -1 for x outside [1, 128].  A head
-// narrower than its tile is padded with zero columns on load and its padding
-// is never stored.
-inline int tile_index(int64_t x) {
-    return x < 1 ? -1 : x <= 16 ? 0 : x <= 32 ? 1 : x <= 64 ? 2 : x <= 128 ? 3 : -1;
-}
 
 }  // namespace cp

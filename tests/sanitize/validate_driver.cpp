@@ -1,0 +1,88 @@
+// Exercises the C ABI's argument checks (cp_validate.hpp) on the host, built
+// with -fsanitize=address,undefined by tests/test_sanitizers.py.  Pointers are
+// fake, 16-byte aligned addresses that are never dereferenced.  Prints one
+// line per failed expectation and exits with the number of failures.
+#include <stdint.h>
+#include <stdio.h>
+
+#include "cp_validate.hpp"
+
+static int failures = 0;
+
+static void expect(int got, int want, const char *what) {
+    if (got != want) {
+        printf("FAIL %s: got %d, want %d\n", what, got, want);
+        ++failures;
+    }
+}
+
+static const void *P(int n) { return reinterpret_cast<const void *>(uintptr_t(0x1000000000ull) + uintptr_t(n) * 0x100000000ull); }
+static const float *F(int n) { return static_cast<const float *>(P(n)); }
+
+int main() {
+    using namespace cp;
+    // valid calls over every dtype and tile size, ragged and tiny lengths
+    for (int dt : {CP_F32, CP_BF16, CP_F16})
+        for (int64_t E : {16, 32, 40, 64, 80, 128})
+            for (int64_t M : {16, 32, 64, 96, 128})
+                for (int64_t L : {1, 17, 4096}) {
+                    expect(validate_fwd(P(0), P(1), P(2), P(3), nullptr, nullptr, 2, 3, L, E, M, dt), CP_OK, "fwd ok");
+                    expect(validate_bwd(P(0), P(1), P(2), P(3), F(4), F(5), P(6), P(7), P(8), nullptr, 2, 3, L, E, M,
+                                        dt), CP_OK, "bwd ok");
+                    expect(validate_linattn_fwd(P(0), P(1), P(2), P(3), nullptr, nullptr, F(4), F(5), F(6), 2, 3, L,
+                                                E, M, 1e-6f, 1, dt), CP_OK, "linattn ok");
+                    expect(validate_linattn_bwd(P(0), P(1), P(2), P(3), P(4), F(5), nullptr, nullptr, F(6), P(7), P(8),
+                                                P(9), F(10), F(11), 2, 3, L, E, M, 0, dt), CP_OK, "linattn bwd ok");
+                }
+    // sizes
+    const int64_t big = INT64_MAX;
+    for (int64_t bad : {int64_t(0), int64_t(-1), big}) {
+        expect(validate_fwd(P(0), P(1), P(2), P(3), nullptr, nullptr, bad, 3, 100, 64, 64, CP_BF16), CP_ERR_DIM, "N");
+        expect(validate_fwd(P(0), P(1), P(2), P(3), nullptr, nullptr, 2, bad, 100, 64, 64, CP_BF16), CP_ERR_DIM, "H");
+        expect(validate_fwd(P(0), P(1), P(2), P(3), nullptr, nullptr, 2, 3, bad, 64, 64, CP_BF16), CP_ERR_DIM, "L");
+    }
+    expect(validate_fwd(P(0), P(1), P(2), P(3), nullptr, nullptr, 2, 3, 100, big, 64, CP_BF16), CP_ERR_UNSUPPORTED, "E big");
+    expect(validate_fwd(P(0), P(1), P(2), P(3), nullptr, nullptr, 2, 3, 100, 0, 64, CP_BF16), CP_ERR_DIM, "E 0");
+    expect(validate_fwd(P(0), P(1), P(2), P(3), nullptr, nullptr, INT32_MAX, INT32_MAX, INT32_MAX, 128, 128, CP_F32),
+           CP_ERR_DIM, "overflow");
+    expect(validate_fwd(P(0), P(1), P(2), P(3), nullptr, nullptr, 1 << 16, 1 << 10, int64_t(1) << 30, 128, 128, CP_F32),
+           CP_ERR_DIM, "bytes overflow");
+    expect(validate_fwd(P(0), P(1), P(2), P(3), nullptr, nullptr, 2, 3, 100, 129, 64, CP_BF16), CP_ERR_UNSUPPORTED, "E 129");
+    expect(validate_fwd(P(0), P(1), P(2), P(3), nullptr, nullptr, 2, 3, 100, 60, 64, CP_BF16), CP_ERR_UNSUPPORTED, "E 60 bf16");
+    expect(validate_fwd(P(0), P(1), P(2), P(3), nullptr, nullptr, 2, 3, 100, 60, 64, CP_F32), CP_OK, "E 60 f32");
+    expect(validate_fwd(P(0), P(1), P(2), P(3), nullptr, nullptr, 2, 3, 100, 64, 64, 7), CP_ERR_UNSUPPORTED, "dtype");
+    // pointers
+    expect(validate_fwd(nullptr, P(1), P(2), P(3), nullptr, nullptr, 2, 3, 100, 64, 64, CP_BF16), CP_ERR_NULL, "null Q");
+    expect(validate_fwd(static_cast<const char *>(P(0)) + 8, P(1), P(2), P(3), nullptr, nullptr, 2, 3, 100, 64, 64,
+                        CP_BF16), CP_ERR_ALIGN, "align Q");
+    expect(validate_fwd(P(0), P(1), P(2), P(3), F(4) + 1, nullptr, 2, 3, 100, 64, 64, CP_BF16), CP_ERR_ALIGN,
+           "align S0");
+    // aliasing: output inside an input, two outputs overlapping, an address
+    // range reaching the end of the address space
+    expect(validate_fwd(P(0), P(1), P(2), static_cast<const char *>(P(2)) + 16, nullptr, nullptr, 2, 3, 100, 64, 64,
+                        CP_BF16), CP_ERR_ALIAS, "alias out/v");
+    expect(validate_bwd(P(0), P(1), P(2), P(3), nullptr, nullptr, P(6), P(6), P(8), nullptr, 2, 3, 100, 64, 64,
+                        CP_BF16), CP_ERR_ALIAS, "alias dq/dk");
+    const void *top = reinterpret_cast<const void *>(UINTPTR_MAX & ~uintptr_t(15));
+    expect(validate_fwd(P(0), P(1), P(2), top, nullptr, nullptr, 2, 3, 100, 64, 64, CP_BF16), CP_OK, "top ok");
+    expect(validate_fwd(top, P(1), P(2), static_cast<const char *>(top) - 32, nullptr, nullptr, 2, 3, 100, 64, 64,
+                        CP_BF16), CP_ERR_ALIAS, "top alias");
+    // normalised form: flags and eps
+    expect(validate_linattn_fwd(P(0), P(1), P(2), P(3), nullptr, nullptr, nullptr, nullptr, nullptr, 2, 3, 100, 64, 64,
+                                -1.f, 1, CP_BF16), CP_ERR_UNSUPPORTED, "eps < 0");
+    expect(validate_linattn_fwd(P(0), P(1), P(2), P(3), nullptr, nullptr, nullptr, nullptr, nullptr, 2, 3, 100, 64, 64,
+                                1.f / 0.f, 1, CP_BF16), CP_ERR_UNSUPPORTED, "eps inf");
+    expect(validate_linattn_fwd(P(0), P(1), P(2), P(3), nullptr, nullptr, nullptr, nullptr, nullptr, 2, 3, 100, 64, 64,
+                                1e-6f, 2, CP_BF16), CP_ERR_UNSUPPORTED, "feature map");
+    expect(validate_linattn_bwd(P(0), P(1), P(2), P(3), P(4), nullptr, nullptr, nullptr, nullptr, P(7), P(8), P(9),
+                                nullptr, nullptr, 2, 3, 100, 64, 64, 1, CP_BF16), CP_ERR_NULL, "den required");
+    expect(validate_linattn_bwd(P(0), P(1), P(2), P(3), P(4), F(5), nullptr, nullptr, nullptr, P(7), P(8), P(9),
+                                F(5), nullptr, 2, 3, 100, 64, 64, 1, CP_BF16), CP_ERR_ALIAS, "dS0 over den");
+    for (int64_t x = -3; x <= 200; ++x) {
+        const int t = tile_index(x);
+        const int want = x < 1 ? -1 : x <= 16 ? 0 : x <= 32 ? 1 : x <= 64 ? 2 : x <= 128 ? 3 : -1;
+        expect(t, want, "tile_index");
+    }
+    printf("%d failures\n", failures);
+    return failures;
+}
