@@ -73,7 +73,8 @@ typedef enum {
     CP_ERR_UNSUPPORTED = 3, /* E or M > 128 or rows not 16-byte pieces, bad dtype/flag */
     CP_ERR_ALIGN = 4,       /* a pointer not 16-byte aligned                  */
     CP_ERR_ALIAS = 5,       /* an output overlaps an input or another output  */
-    CP_ERR_HIP = 6          /* the HIP runtime reported an error at launch    */
+    CP_ERR_HIP = 6,         /* the HIP runtime reported an error at launch    */
+    CP_ERR_SCRATCH = 7      /* more scratch than causal_product_fwd_noalloc holds */
 } cp_status;
 
 /*
@@ -91,6 +92,27 @@ int causal_product_fwd(const void *Q, const void *K, const void *V, void *Out,
                        const float *state_in, float *state_out,
                        int64_t N, int64_t H, int64_t L, int64_t E, int64_t M,
                        int dtype, void *stream);
+
+/*
+ * causal_product_fwd_noalloc: causal_product_fwd for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the same arguments, kernels and results,
+ * but the scratch of a forward over sequence segments (taken when N*H slices
+ * are too few to fill the GPU: N*H*segments*(E*M + E) floats) lives in a
+ * static device buffer of 16 MiB that the library holds on every GPU it runs
+ * on until the process ends; the call itself allocates nothing.  A call that
+ * would need more than 16 MiB returns CP_ERR_SCRATCH before anything is
+ * enqueued (for example N*H = 16, L = 16384, E = M = 128).  Every call on one
+ * GPU shares that GPU's buffer, which keeps the last call's contents (each
+ * call writes every part it reads before reading it): calls that may overlap
+ * on one GPU (concurrent streams, or threads) race and must be serialised by
+ * the caller.  The first call on a device looks the buffer's address up and
+ * can report CP_ERR_HIP if that fails.
+ */
+int causal_product_fwd_noalloc(const void *Q, const void *K, const void *V, void *Out,
+                               const float *state_in, float *state_out,
+                               int64_t N, int64_t H, int64_t L, int64_t E, int64_t M,
+                               int dtype, void *stream);
 
 /*
  * causal_product_bwd: gradients of f = sum_i Out_i . dOut_i with respect to
@@ -180,7 +202,8 @@ const char *cp_status_string(int status);
 /* Version of this ABI: (major << 16) | minor.  3.0: carried states and the
  * normalised backward; 3.1: CP_F16 and head sizes between the tile sizes
  * (both additions: every 3.0 call behaves as before); 4.0: cp_timing_end
- * takes the capacity of the caller's buffer. */
+ * takes the capacity of the caller's buffer; 4.1: causal_product_fwd_noalloc
+ * and CP_ERR_SCRATCH. */
 int cp_abi_version(void);
 
 /*

@@ -9,6 +9,7 @@ missing the import fails.
 
 Functions with the ABI's names (optional tensors and outputs are keyword-only):
     causal_product_fwd(q, k, v, *, out=None, state_in=None, state_out=None)
+    causal_product_fwd_noalloc(q, k, v, *, out, state_in=None, state_out=None)
     causal_product_bwd(q, k, v, dout, *, state_final=None, state_in=None,
                        dq=None, dk=None, dv=None, dstate_in=None)
     linear_attn_fwd(q, k, v, eps=1e-6, feature_map=1, *, out=None, state_in=None,
@@ -39,7 +40,7 @@ LIB_PATH = os.environ.get("CAUSALPROD_LIB") or os.path.join(HERE, "libcausalprod
 
 CP_F32, CP_BF16, CP_F16 = 0, 1, 2
 STATUS = {0: "CP_OK", 1: "CP_ERR_NULL", 2: "CP_ERR_DIM", 3: "CP_ERR_UNSUPPORTED", 4: "CP_ERR_ALIGN",
-          5: "CP_ERR_ALIAS", 6: "CP_ERR_HIP"}
+          5: "CP_ERR_ALIAS", 6: "CP_ERR_HIP", 7: "CP_ERR_SCRATCH"}
 # Kernel tile sizes: a head of E (or M) features runs on the smallest tile >= E,
 # its padding columns read as zero and never stored.
 TILE_SIZES = (16, 32, 64, 128)
@@ -51,6 +52,8 @@ lib = ctypes.CDLL(LIB_PATH)
 _vp, _i64, _int = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
 lib.causal_product_fwd.argtypes = [_vp] * 6 + [_i64] * 5 + [_int, _vp]
 lib.causal_product_fwd.restype = _int
+lib.causal_product_fwd_noalloc.argtypes = [_vp] * 6 + [_i64] * 5 + [_int, _vp]
+lib.causal_product_fwd_noalloc.restype = _int
 lib.causal_product_bwd.argtypes = [_vp] * 10 + [_i64] * 5 + [_int, _vp]
 lib.causal_product_bwd.restype = _int
 lib.linear_attn_fwd.argtypes = [_vp] * 9 + [_i64] * 5 + [ctypes.c_float, _int, _int, _vp]
@@ -157,6 +160,24 @@ def causal_product_fwd(q, k, v, *, out=None, state_in=None, state_out=None):
     _check_state("state_in", state_in, (N, H, E, M), q.device)
     _check_state("state_out", state_out, (N, H, E, M), q.device)
     _check("causal_product_fwd", lib.causal_product_fwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(state_in), _ptr(state_out), N, H, L, E, M, _dtype_code(q),
+        _stream(q.device)))
+    return out
+
+
+def causal_product_fwd_noalloc(q, k, v, *, out, state_in=None, state_out=None):
+    """causal_product_fwd for callers that cannot allocate: the caller passes
+    ``out`` (and the optional states); the library allocates nothing and keeps
+    the scratch of a forward over few slices in a static 16 MiB device buffer
+    shared by every call on the GPU (calls that may overlap on one GPU must
+    be serialised)."""
+    N, H, L, E, M = _dims(q, v)
+    if k.shape != q.shape or out.shape != v.shape:
+        raise ValueError("k must have q's shape and out v's shape")
+    _check_tensors(q, k, v, out)
+    _check_state("state_in", state_in, (N, H, E, M), q.device)
+    _check_state("state_out", state_out, (N, H, E, M), q.device)
+    _check("causal_product_fwd_noalloc", lib.causal_product_fwd_noalloc(
         _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(state_in), _ptr(state_out), N, H, L, E, M, _dtype_code(q),
         _stream(q.device)))
     return out
@@ -293,5 +314,5 @@ def linear_attention(q, k, v, eps: float = 1e-6, feature_map: str = "elu+1"):
     return LinearAttention.apply(q, k, v, eps, fm)
 
 
-__all__ = ["causal_product_fwd", "causal_product_bwd", "linear_attn_fwd", "linear_attn_bwd", "causal_product", "linear_attention",
+__all__ = ["causal_product_fwd", "causal_product_fwd_noalloc", "causal_product_bwd", "linear_attn_fwd", "linear_attn_bwd", "causal_product", "linear_attention",
            "CausalProductError", "lib", "LIB_PATH", "timing_begin", "timing_end"]

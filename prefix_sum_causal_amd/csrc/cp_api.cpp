@@ -11,15 +11,27 @@
 #include <cmath>
 #include <cstdint>
 #include <cstdlib>
+#include <mutex>
 #include <vector>
 
 #include "cp_launch.hpp"
 #include "cp_validate.hpp"
 
+// Scratch of causal_product_fwd_noalloc: the per-segment state increments of
+// a forward over sequence segments live in this file-scope device array
+// instead of stream-ordered allocations.  Each GPU the library runs on holds
+// its own copy until the process ends; in host code `scratch` only names the
+// symbol, so the entry point uses the device address that
+// hipGetSymbolAddress returns for it, looked up once per device (with that
+// device current) and kept in scratch_dev.
+constexpr size_t kScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
+
 namespace {
 
-constexpr int kAbiMajor = 4, kAbiMinor = 0;  // 3.0: carried state, normalised backward; 3.1: fp16 I/O;
-                                             // 4.0: cp_timing_end bounded by the caller's buffer
+constexpr int kAbiMajor = 4, kAbiMinor = 1;  // 3.0: carried state, normalised backward; 3.1: fp16 I/O;
+                                             // 4.0: cp_timing_end bounded by the caller's buffer;
+                                             // 4.1: causal_product_fwd_noalloc
 
 cp::fwd_fn pick_fwd(int dtype, int E, int M, bool norm) {
     return dtype == CP_BF16 ? cp::fwd_bf16(E, M, norm) : dtype == CP_F16 ? cp::fwd_f16(E, M, norm) : cp::fwd_f32(E, M, norm);
@@ -46,6 +58,35 @@ struct Timing {
     }
 };
 thread_local Timing timing;
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void *scratch_dev[kMaxDevices] = {};
+
+// The device address of `scratch` on the device that runs `stream` (the
+// current device for the NULL stream).
+int scratch_address(hipStream_t stream, void **addr) {
+    int dev = -1;
+    if (stream) {
+        if (hipStreamGetDevice(stream, &dev) != hipSuccess) return CP_ERR_HIP;
+    } else if (hipGetDevice(&dev) != hipSuccess) {
+        return CP_ERR_HIP;
+    }
+    if (dev < 0 || dev >= kMaxDevices) return CP_ERR_HIP;
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (!scratch_dev[dev]) {
+        int cur = -1;
+        if (hipGetDevice(&cur) != hipSuccess) return CP_ERR_HIP;
+        if (cur != dev && hipSetDevice(dev) != hipSuccess) return CP_ERR_HIP;
+        void *p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur != dev) (void)hipSetDevice(cur);
+        if (e != hipSuccess || !p) return CP_ERR_HIP;
+        scratch_dev[dev] = p;
+    }
+    *addr = scratch_dev[dev];
+    return CP_OK;
+}
 
 }  // namespace
 
@@ -112,6 +153,7 @@ const char *cp_status_string(int status) {
         case CP_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
         case CP_ERR_ALIAS: return "an output overlaps an input or another output";
         case CP_ERR_HIP: return "the HIP runtime reported an error when launching the kernel";
+        case CP_ERR_SCRATCH: return "the call needs more scratch than the no-allocation entry point holds (16 MiB); use causal_product_fwd";
         default: return "unknown status";
     }
 }
@@ -125,6 +167,30 @@ int causal_product_fwd(const void *Q, const void *K, const void *V, void *Out, c
     if (!fn) return CP_ERR_UNSUPPORTED;
     cp::FwdArgs a{Q,      K,      V, Out, state_in, nullptr, state_out, nullptr, nullptr, (int)L, (int)(N * H), 0.f,
                   0,      (int)E, (int)M};
+    return launch_status(fn(a, static_cast<hipStream_t>(stream)));
+}
+
+int causal_product_fwd_noalloc(const void *Q, const void *K, const void *V, void *Out, const float *state_in,
+                               float *state_out, int64_t N, int64_t H, int64_t L, int64_t E, int64_t M, int dtype,
+                               void *stream) {
+    int st = cp::validate_fwd(Q, K, V, Out, state_in, state_out, N, H, L, E, M, dtype);
+    if (st != CP_OK) return st;
+    cp::fwd_fn fn = pick_fwd(dtype, (int)E, (int)M, false);
+    if (!fn) return CP_ERR_UNSUPPORTED;
+    cp::FwdArgs a{Q,      K,      V, Out, state_in, nullptr, state_out, nullptr, nullptr, (int)L, (int)(N * H), 0.f,
+                  0,      (int)E, (int)M};
+    // the scratch this call needs (host arithmetic only, nothing is launched)
+    size_t need = 0;
+    a.ws_need = &need;
+    if (fn(a, static_cast<hipStream_t>(stream)) != hipSuccess) return CP_ERR_HIP;
+    if (need > kScratchBytes) return CP_ERR_SCRATCH;
+    void *ws = nullptr;
+    st = scratch_address(static_cast<hipStream_t>(stream), &ws);
+    if (st != CP_OK) return st;
+    a.ws_need = nullptr;
+    a.ws = static_cast<float *>(ws);
+    a.ws_bytes = kScratchBytes;
+    a.noalloc = true;
     return launch_status(fn(a, static_cast<hipStream_t>(stream)));
 }
 

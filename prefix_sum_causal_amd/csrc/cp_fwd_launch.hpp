@@ -42,13 +42,25 @@ hipError_t launch_fwd_t(const FwdArgs &a, hipStream_t s) {
     const int nchunks = (L + P::FC - 1) / P::FC;
     int seg_len = (nchunks + nseg0 - 1) / nseg0 * P::FC;
     const int nseg = (L + seg_len - 1) / seg_len;
+    // per slice and segment: the E x M increment of the state, then E of z
+    const size_t need = nseg > 1 ? (size_t)NS * nseg * (E * M + E) * sizeof(float) : 0;
+    if (a.ws_need) {
+        *a.ws_need = need;
+        return hipSuccess;
+    }
     float *ws = nullptr;
+    bool owned = false;
     hipError_t e = hipSuccess;
     if (nseg > 1) {
-        // per slice and segment: the E x M increment of the state, then E of z
-        const size_t bytes = (size_t)NS * nseg * (E * M + E) * sizeof(float);
-        e = hipMallocAsync(reinterpret_cast<void **>(&ws), bytes, s);
-        if (e != hipSuccess) return e;
+        if (a.ws) {
+            if (a.ws_bytes < need) return hipErrorInvalidValue;
+            ws = a.ws;
+        } else {
+            if (a.noalloc) return hipErrorInvalidValue;
+            e = hipMallocAsync(reinterpret_cast<void **>(&ws), need, s);
+            if (e != hipSuccess) return e;
+            owned = true;
+        }
         auto k1 = cp_fwd_kernel<T, E, M, P::FC, P::FG, P::FRS, P::FNPF, NORM, FMAP, true>;
         void *args1[] = {&q, &k, &v, &o, &s0, &z0, &st, &zt, &dn, &ws, &L, &NS, &seg_len, &eps, &Ea, &Ma};
         e = launch_kernel(reinterpret_cast<const void *>(k1), dim3(NS * P::FG * nseg), block, args1, s);
@@ -60,7 +72,7 @@ hipError_t launch_fwd_t(const FwdArgs &a, hipStream_t s) {
         void *args2[] = {&q, &k, &v, &o, &s0, &z0, &st, &zt, &dn, &ws, &L, &NS, &seg_len, &eps, &Ea, &Ma};
         e = launch_kernel(reinterpret_cast<const void *>(k2), dim3(NS * P::FG * nseg), block, args2, s);
     }
-    if (ws) {
+    if (owned) {
         const hipError_t f = hipFreeAsync(ws, s);
         if (e == hipSuccess) e = f;
     }

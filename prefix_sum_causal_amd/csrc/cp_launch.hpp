@@ -4,6 +4,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <stddef.h>
 #include <stdint.h>
 
 #include "cp_validate.hpp"
@@ -20,6 +21,16 @@ struct FwdArgs {
     float eps;
     int fmap;
     int Ea, Ma;  // head sizes of the tensors (the kernel runs the next tile size up)
+    // Scratch of a forward over sequence segments.  ws_need != NULL: only
+    // report the bytes the call needs (0 without segments) and launch
+    // nothing.  ws != NULL: use ws_bytes bytes at ws (a call that needs more
+    // fails) and allocate nothing; with ws == NULL and noalloc set, a call
+    // that needs scratch fails; otherwise it comes from the stream-ordered
+    // allocator.
+    size_t *ws_need = nullptr;
+    float *ws = nullptr;
+    size_t ws_bytes = 0;
+    bool noalloc = false;
 };
 
 struct BwdArgs {

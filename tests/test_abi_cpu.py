@@ -13,7 +13,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "causalprod.h")
 LIB = os.path.join(ROOT, "prefix_sum_causal_amd", "libcausalprod.so")
 
-OK, NULL, DIM, UNSUP, ALIGN, ALIAS, HIP = range(7)
+OK, NULL, DIM, UNSUP, ALIGN, ALIAS, HIP, SCRATCH = range(8)
 
 
 @pytest.fixture(scope="module")
@@ -23,6 +23,7 @@ def lib():
     lib = ctypes.CDLL(LIB)
     vp, i64, i = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
     lib.causal_product_fwd.argtypes = [vp] * 6 + [i64] * 5 + [i, vp]
+    lib.causal_product_fwd_noalloc.argtypes = [vp] * 6 + [i64] * 5 + [i, vp]
     lib.causal_product_bwd.argtypes = [vp] * 10 + [i64] * 5 + [i, vp]
     lib.linear_attn_fwd.argtypes = [vp] * 9 + [i64] * 5 + [ctypes.c_float, i, i, vp]
     lib.linear_attn_bwd.argtypes = [vp] * 14 + [i64] * 5 + [i, i, vp]
@@ -38,8 +39,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(
-        ["causal_product_fwd", "causal_product_bwd", "linear_attn_fwd", "linear_attn_bwd", "cp_status_string",
-         "cp_abi_version", "cp_timing_begin", "cp_timing_end"])
+        ["causal_product_fwd", "causal_product_fwd_noalloc", "causal_product_bwd", "linear_attn_fwd",
+         "linear_attn_bwd", "cp_status_string", "cp_abi_version", "cp_timing_begin", "cp_timing_end"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -49,12 +50,12 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_status_strings_and_version(lib):
     seen = set()
-    for s in range(7):
+    for s in range(8):
         msg = lib.cp_status_string(s).decode()
         assert msg and msg not in seen
         seen.add(msg)
     assert lib.cp_status_string(99).decode() == "unknown status"
-    assert lib.cp_abi_version() == (4 << 16) | 0
+    assert lib.cp_abi_version() == (4 << 16) | 1
 
 
 def test_timing_rejects_bad_arguments_before_any_device_call(lib):
@@ -196,3 +197,26 @@ def test_f16_aliasing_uses_two_byte_elements(lib):
     # SHAPE fp16: q is 2*3*100*64*2 = 76800 bytes, as bf16
     assert fwd(lib, o=A[1] + 76800 - 16, dtype=2) == ALIAS
     assert bwd(lib, dq=A[5], dtype=2) == ALIAS
+
+
+def fwd_na(lib, q=A[0], k=A[1], v=A[2], o=A[3], s0=None, st=None, shape=SHAPE, dtype=1):
+    return lib.causal_product_fwd_noalloc(q, k, v, o, s0, st, *shape, dtype, None)
+
+
+def test_noalloc_forward_validates_like_the_forward(lib):
+    assert fwd_na(lib, q=None) == NULL
+    assert fwd_na(lib, shape=(2, 3, 0, 64, 32)) == DIM
+    assert fwd_na(lib, shape=(2, 3, 100, 256, 32)) == UNSUP
+    assert fwd_na(lib, dtype=4) == UNSUP
+    assert fwd_na(lib, v=A[2] + 8) == ALIGN
+    assert fwd_na(lib, o=A[0]) == ALIAS
+    assert fwd_na(lib, s0=A[5], st=A[5]) == ALIAS
+
+
+@pytest.mark.parametrize("dtype", [0, 1, 2])
+def test_noalloc_forward_rejects_more_scratch_than_it_holds(lib, dtype):
+    # 16 slices of 16384 rows with 128-wide heads run as sequence segments
+    # whose increments need 16 slices x 16 segments x (128*128 + 128) floats,
+    # 16.1 MiB > 16 MiB: refused before anything is enqueued (no device here)
+    assert fwd_na(lib, shape=(2, 8, 16384, 128, 128), dtype=dtype) == SCRATCH
+    assert "16 MiB" in lib.cp_status_string(SCRATCH).decode()
