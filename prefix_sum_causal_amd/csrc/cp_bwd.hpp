@@ -79,10 +79,14 @@ __device__ __forceinline__ void dotk_shared(FACC acc, int b0, int b1, FS fs, FO 
 
 // The whole sweep of one wave role.  Every role runs the same staging and
 // barriers; only the math differs, so each wave's loop is straight-line code.
-// The wave owns the NB column blocks b + G x (x = 0 .. NB-1) of its output;
-// the chunk's operand tiles and causal tiles are read and formed once for
-// all of them.
-template <typename T, int E, int M, int C, int G, int NB, int IDLE, int NPF, bool NORM, bool FMAP, int ROLE>
+// The wave owns the NB column blocks b + G x (x = 0 .. NB-1) of its output,
+// for the row blocks of each chunk that row group RGI of RG owns
+// (owns_block): the RG workgroups of a (slice, column group) split the rows,
+// each writing whole rows of its outputs, and all of them carry the states
+// over every row.  The chunk's operand tiles and causal tiles are read and
+// formed once for all of the wave's column blocks.
+template <typename T, int E, int M, int C, int G, int NB, int IDLE, int RG, int RGI, int NPF, bool NORM, bool FMAP,
+          int ROLE>
 __device__ __forceinline__ void bwd_sweep(const T *q_, const T *k_, const T *v_, const T *g_, const float *s0,
                                           const float *st, const float *zc_, const float *dd_, int Lpad, T *out_,
                                           float *ds0, float *dz0, int L, int b, T *lds, int Ea, int Ma) {
@@ -103,6 +107,7 @@ __device__ __forceinline__ void bwd_sweep(const T *q_, const T *k_, const T *v_,
     const int n = (L + C - 1) / C;
     const Diag diag;
     auto bk = [&](int x) { return b + G * x; };  // the wave's column blocks
+    constexpr auto own = [](int I) { return owns_block<C / 16, RG>(RGI, I); };  // the row blocks it writes
 
     // carried state (fp32 accumulator tiles), per column block bk(x)
     //   dQ: W[x][mt] = S^T[ecol_M(mt) + estride_M g + t][16 bk(x) + r]
@@ -300,6 +305,7 @@ __device__ __forceinline__ void bwd_sweep(const T *q_, const T *k_, const T *v_,
                     for (int k = 0; k < EM::STEPS; ++k) vf[J][k] = EM::load(Vs, RM, J, k);
 #pragma unroll
                 for (int I = 0; I < CB; ++I) {
+                    if (!own(I)) continue;
                     typename EM::rf gf[EM::STEPS];
 #pragma unroll
                     for (int k = 0; k < EM::STEPS; ++k) gf[k] = EM::load(Gs, RM, I, k);
@@ -356,6 +362,7 @@ __device__ __forceinline__ void bwd_sweep(const T *q_, const T *k_, const T *v_,
                     for (int k = 0; k < EM::STEPS; ++k) gf[I][k] = EM::load(Gs, RM, I, k);
 #pragma unroll
                 for (int J = 0; J < CB; ++J) {
+                    if (!own(J)) continue;
                     typename EM::rf vf[EM::STEPS];
 #pragma unroll
                     for (int k = 0; k < EM::STEPS; ++k) vf[k] = EM::load(Vs, RM, J, k);
@@ -431,6 +438,7 @@ __device__ __forceinline__ void bwd_sweep(const T *q_, const T *k_, const T *v_,
                     for (int k = 0; k < EE::STEPS; ++k) qf[I][k] = EE::load(Qs, RE, I, k);
 #pragma unroll
                 for (int J = 0; J < CB; ++J) {
+                    if (!own(J)) continue;
                     typename EE::rf kf[EE::STEPS];
 #pragma unroll
                     for (int k = 0; k < EE::STEPS; ++k) kf[k] = EE::load(Ks, RE, J, k);
@@ -470,12 +478,13 @@ __device__ __forceinline__ void bwd_sweep(const T *q_, const T *k_, const T *v_,
 #pragma unroll
                 for (int x = 0; x < NB; ++x)
 #pragma unroll
-                    for (int j = 0; j < CB; ++j) st_out<T>(rp, j, bk(x), pend[x][j], OWa);
+                    for (int j = 0; j < CB; ++j)
+                        if (own(j)) st_out<T>(rp, j, bk(x), pend[x][j], OWa);
             }
         }
     }
     // the gradient of the initial z: r_0, held by the dK waves
-    if constexpr (NORM && ROLE == kDK) {
+    if constexpr (NORM && ROLE == kDK && RGI == 0) {
         if (dz0 && r == 0) {
 #pragma unroll
             for (int x = 0; x < NB; ++x)
@@ -486,7 +495,7 @@ __device__ __forceinline__ void bwd_sweep(const T *q_, const T *k_, const T *v_,
     }
     // the gradient of the initial state: R_0 = sum_i q_i dO_i^T, held by the
     // dV waves (column blocks of M) at the end of the reverse sweep
-    if constexpr (ROLE == kDV) {
+    if constexpr (ROLE == kDV && RGI == 0) {
         if (ds0) {
 #pragma unroll
             for (int x = 0; x < NB; ++x)
@@ -501,11 +510,33 @@ __device__ __forceinline__ void bwd_sweep(const T *q_, const T *k_, const T *v_,
     }
 }
 
+// The wave's role sweep for row group RGI.
+template <typename T, int E, int M, int C, int G, int NB, int IDLE, int RG, int RGI, int NPF, bool NORM, bool FMAP>
+__device__ __forceinline__ void bwd_role(int role, int b, const T *q_, const T *k_, const T *v_, const T *g_,
+                                         const float *s0, const float *st, const float *zc_, const float *dd_,
+                                         int Lpad, T *dq_, T *dk_, T *dv_, float *ds0, float *dz0, int L, T *lds,
+                                         int Ea, int Ma) {
+    constexpr int EB = E / 16, MB = M / 16;
+    if (role == kDQ && b < EB)
+        bwd_sweep<T, E, M, C, G, NB, IDLE, RG, RGI, NPF, NORM, FMAP, kDQ>(q_, k_, v_, g_, s0, st, zc_, dd_, Lpad,
+                                                                          dq_, nullptr, nullptr, L, b, lds, Ea, Ma);
+    else if (role == kDK && b < EB)
+        bwd_sweep<T, E, M, C, G, NB, IDLE, RG, RGI, NPF, NORM, FMAP, kDK>(q_, k_, v_, g_, s0, st, zc_, dd_, Lpad,
+                                                                          dk_, nullptr, dz0, L, b, lds, Ea, Ma);
+    else if (role == kDV && b < MB)
+        bwd_sweep<T, E, M, C, G, NB, IDLE, RG, RGI, NPF, NORM, FMAP, kDV>(q_, k_, v_, g_, s0, st, zc_, dd_, Lpad,
+                                                                          dv_, ds0, nullptr, L, b, lds, Ea, Ma);
+    else
+        bwd_sweep<T, E, M, C, G, NB, IDLE, RG, RGI, NPF, NORM, FMAP, kIdle>(q_, k_, v_, g_, s0, st, zc_, dd_, Lpad,
+                                                                            nullptr, nullptr, nullptr, L, 0, lds, Ea,
+                                                                            Ma);
+}
+
 // NORM (backward of the normalised form, see the launcher): Q, K are the raw
 // inputs (phi applied on load when FMAP), Gr is dn = dO / den, dd the padded
 // per-row dd = -(dO . out) / den, zc the normaliser z before every chunk
 // ([Lpad / C][E] per slice), dz_in the gradient of the initial z.
-template <typename T, int E, int M, int C, int G, int NB, int IDLE, int NPF, bool NORM, bool FMAP>
+template <typename T, int E, int M, int C, int G, int NB, int IDLE, int RG, int NPF, bool NORM, bool FMAP>
 __global__ __launch_bounds__((64 * bwd_waves<E, M, G, NB, IDLE>())) void cp_bwd_kernel(
     const T *__restrict__ Q, const T *__restrict__ K, const T *__restrict__ V, const T *__restrict__ Gr,
     const float *__restrict__ state_in, const float *__restrict__ state_final, const float *__restrict__ zc,
@@ -523,8 +554,10 @@ __global__ __launch_bounds__((64 * bwd_waves<E, M, G, NB, IDLE>())) void cp_bwd_
     constexpr int DDE = NORM ? 2 * C * 4 / (int)sizeof(T) : 0;  // two dd buffers of C floats
     __shared__ __attribute__((aligned(16))) T lds[2 * BUF + DDE];
 
-    int slice, grp;
-    map_block(blockIdx.x, NS, G, slice, grp);
+    static_assert(RG >= 1 && RG <= 2 && RG <= C / 16, "row groups");
+    int slice, part;
+    map_block(blockIdx.x, NS, G * RG, slice, part);
+    const int grp = part % G, rg = part / G;
     const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
     // the tensors' own head sizes Ea <= E, Ma <= M (the kernel's tile sizes)
     const int64_t oe = (int64_t)slice * L * Ea, om = (int64_t)slice * L * Ma, os = (int64_t)slice * Ea * Ma;
@@ -539,18 +572,13 @@ __global__ __launch_bounds__((64 * bwd_waves<E, M, G, NB, IDLE>())) void cp_bwd_
     const int role = w < EG ? kDQ : w < 2 * EG ? kDK : w < 2 * EG + MG ? kDV : kIdle;
     const int lw = role == kDQ ? w : role == kDK ? w - EG : w - 2 * EG;
     const int b = grp + G * NB * lw;
-    if (role == kDQ && b < EB)
-        bwd_sweep<T, E, M, C, G, NB, IDLE, NPF, NORM, FMAP, kDQ>(q_, k_, v_, g_, s0, st, zc_, dd_, Lpad, dQ + oe,
-                                                                 nullptr, nullptr, L, b, lds, Ea, Ma);
-    else if (role == kDK && b < EB)
-        bwd_sweep<T, E, M, C, G, NB, IDLE, NPF, NORM, FMAP, kDK>(q_, k_, v_, g_, s0, st, zc_, dd_, Lpad, dK + oe,
-                                                                 nullptr, dz0, L, b, lds, Ea, Ma);
-    else if (role == kDV && b < MB)
-        bwd_sweep<T, E, M, C, G, NB, IDLE, NPF, NORM, FMAP, kDV>(q_, k_, v_, g_, s0, st, zc_, dd_, Lpad, dV + om,
-                                                                 ds0, nullptr, L, b, lds, Ea, Ma);
+    if (rg == 0 || RG == 1)
+        bwd_role<T, E, M, C, G, NB, IDLE, RG, 0, NPF, NORM, FMAP>(role, b, q_, k_, v_, g_, s0, st, zc_, dd_, Lpad,
+                                                                 dQ + oe, dK + oe, dV + om, ds0, dz0, L, lds, Ea,
+                                                                 Ma);
     else
-        bwd_sweep<T, E, M, C, G, NB, IDLE, NPF, NORM, FMAP, kIdle>(q_, k_, v_, g_, s0, st, zc_, dd_, Lpad,
-                                                                   nullptr, nullptr, nullptr, L, 0, lds, Ea, Ma);
+        bwd_role<T, E, M, C, G, NB, IDLE, RG, (RG > 1 ? 1 : 0), NPF, NORM, FMAP>(
+            role, b, q_, k_, v_, g_, s0, st, zc_, dd_, Lpad, dQ + oe, dK + oe, dV + om, ds0, dz0, L, lds, Ea, Ma);
 }
 
 }  // namespace cp

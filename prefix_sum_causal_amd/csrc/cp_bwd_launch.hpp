@@ -178,9 +178,9 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t s) {
         }
     }
     if (e == hipSuccess) {
-        auto kern = cp_bwd_kernel<T, E, M, C, P::BG, P::BNB, P::BIDLE, P::BNPF, NORM, FMAP>;
+        auto kern = cp_bwd_kernel<T, E, M, C, P::BG, P::BNB, P::BIDLE, P::BRG, P::BNPF, NORM, FMAP>;
         void *args[] = {&q, &k, &v, &g, &s0, &st, &zc, &dd, &Lpad, &dq, &dk, &dv, &ds0, &dz0, &L, &NS, &Ea, &Ma};
-        e = launch_kernel(reinterpret_cast<const void *>(kern), dim3(NS * P::BG),
+        e = launch_kernel(reinterpret_cast<const void *>(kern), dim3(NS * P::BG * P::BRG),
                           dim3(64 * bwd_waves<E, M, P::BG, P::BNB, P::BIDLE>()),
                           args, s);
     }

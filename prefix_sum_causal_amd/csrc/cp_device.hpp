@@ -120,10 +120,11 @@ template <typename H> struct Ops16 {
             lo[t] = (H)(x[t] - (float)hi[t]);
         }
     }
+    // -a: the sign bits flipped, one 32-bit xor per pair of values
     __device__ static __forceinline__ frag neg(frag a) {
-        s16x4 s = __builtin_bit_cast(s16x4, a);
-        s16x4 m = {(short)0x8000, (short)0x8000, (short)0x8000, (short)0x8000};
-        return __builtin_bit_cast(frag, s ^ m);
+        typedef unsigned u32x2 __attribute__((__vector_size__(2 * sizeof(unsigned))));
+        const u32x2 m = {0x80008000u, 0x80008000u};
+        return __builtin_bit_cast(frag, __builtin_bit_cast(u32x2, a) ^ m);
     }
     // lane (g, r) <- X[16 tb + 4g + t][16 cb + r] from a natural LDS copy
     // with row stride rs (elements).
@@ -289,11 +290,22 @@ __device__ __forceinline__ void st_out(const Rows<T> &X, int rb, int cb, f32x4 v
     }
 }
 
-// Row stride (elements) of the LDS copy of a W-column chunk: padded by 16
-// bytes so that consecutive rows start in different banks; a multiple of 16
-// bytes so that every row starts 16-byte aligned.
+// Row stride (elements) of the LDS copy of a W-column chunk, a multiple of
+// 16 bytes so that every row starts 16-byte aligned.  Measured on gfx950
+// (16 rows read as 16-byte pieces at one column, and 4 x 4 rows read as
+// 8-byte pieces by the transposing read): strides of 32 bytes modulo 64 run
+// both at full rate (about 250 and 225 bytes per clock per CU), strides of
+// 16 or 48 bytes modulo 64 at half of it and multiples of 64 bytes at a
+// quarter or less.  16-bit rows are therefore padded to 32 modulo 64 bytes.
+// fp32 rows keep a 16-byte pad: their transposed fragments are 4-byte reads
+// of four rows 4 apart, which a 32-modulo-64 stride would put on the same
+// banks.
 template <typename T, int W>
-constexpr int lds_stride() { return W + 16 / (int)sizeof(T); }
+constexpr int lds_stride() {
+    constexpr int bytes = W * (int)sizeof(T);
+    if constexpr (sizeof(T) == 2) return (bytes + (96 - bytes % 64) % 64) / 2;
+    return W + 16 / (int)sizeof(T);
+}
 
 typedef int i32x4 __attribute__((__vector_size__(4 * sizeof(int))));
 
@@ -480,6 +492,29 @@ template <int E> struct EOps<float, E> {
         return Ops<float>::tr_frag(lds, rs, tb, eb);
     }
 };
+
+// Query row blocks of a chunk of CB row blocks owned by row set h of RS:
+// where the chunk holds whole pairs for every set, the blocks are taken in
+// balanced pairs (k, CB-1-k) -- equal causal work -- dealt round robin to the
+// row sets; otherwise block I goes to set I % RS.
+template <int CB, int RS>
+constexpr bool owns_block(int h, int I) {
+    if constexpr (RS == 1) {
+        return true;
+    } else if constexpr (CB % (2 * RS) == 0) {
+        const int k = I < CB / 2 ? I : CB - 1 - I;
+        return k % RS == h;
+    } else {
+        return I % RS == h;
+    }
+}
+template <int CB, int RS>
+constexpr int last_block(int h) {
+    int last = -1;
+    for (int I = 0; I < CB; ++I)
+        if (owns_block<CB, RS>(h, I)) last = I;
+    return last;
+}
 
 // Workgroup id -> (slice, part).  The P parts of one (n, h) slice read the
 // same rows of the inputs, so they are kept on one XCD (workgroups are

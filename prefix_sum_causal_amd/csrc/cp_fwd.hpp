@@ -40,28 +40,14 @@
 
 namespace cp {
 
-// Query row blocks of a chunk owned by row set h of RSPLIT: the blocks are
-// taken in balanced pairs (k, CB-1-k) -- equal causal work -- dealt round
-// robin to the row sets.
-template <int CB, int RSPLIT>
-constexpr bool owns_block(int h, int I) {
-    const int k = I < CB / 2 ? I : CB - 1 - I;
-    return RSPLIT == 1 || k % RSPLIT == h;
-}
-template <int CB, int RSPLIT>
-constexpr int last_block(int h) {
-    int last = -1;
-    for (int I = 0; I < CB; ++I)
-        if (owns_block<CB, RSPLIT>(h, I)) last = I;
-    return last;
-}
-
 // The chunk loop of one wave over rows [rb, re) of its slice: output column
-// block cb of the workgroup's group, query row blocks of row set H.  Every
-// wave runs the same staging and barriers; the state (S, z: carried in and
-// out by reference) is carried by every row set.  SONLY: only the state is
-// accumulated (no Q, no outputs).
-template <typename T, int E, int M, int C, int NW, int RSPLIT, int NPF, bool NORM, bool FMAP, bool SONLY, int H>
+// block cb of the workgroup's group, query row blocks of row set H of RS
+// (the row sets of a slice: RSPLIT waves of each workgroup times the row
+// groups of workgroups).  Every wave runs the same staging and barriers; the
+// state (S, z: carried in and out by reference) is carried by every row set.
+// SONLY: only the state is accumulated (no Q, no outputs).
+template <typename T, int E, int M, int C, int NW, int RSPLIT, int RS, int NPF, bool NORM, bool FMAP, bool SONLY,
+          int H>
 __device__ __forceinline__ void fwd_sweep(const T *q_, const T *k_, const T *v_, T *o_, float *den_, int rb,
                                           int re, int grp, int cb, float eps, T *lds, f32x4 (&S)[E / 16],
                                           f32x4 (&z)[E / 16], int Ea, int Ma) {
@@ -75,7 +61,7 @@ __device__ __forceinline__ void fwd_sweep(const T *q_, const T *k_, const T *v_,
     using SV = Stage<T, NT, C, MW>;
     constexpr int RQ = SQ::RS, RV = SV::RS;
     constexpr int BUF = 2 * C * RQ + C * RV;  // Q, K, V columns of the group
-    constexpr int JMAX = last_block<CB, RSPLIT>(H);  // key blocks this wave scores: J <= JMAX
+    constexpr int JMAX = last_block<CB, RS>(H);  // key blocks this wave scores: J <= JMAX
 
     const Diag diag;
 
@@ -136,13 +122,13 @@ __device__ __forceinline__ void fwd_sweep(const T *q_, const T *k_, const T *v_,
                 const Rows<T> ro(o_, Ma, row0, re, C);
 #pragma unroll
                 for (int I = 0; I < CB; ++I)
-                    if (owns_block<CB, RSPLIT>(H, I)) st_out<T>(ro, I, grp * NW + cb, pend[I], Ma);
+                    if (owns_block<CB, RS>(H, I)) st_out<T>(ro, I, grp * NW + cb, pend[I], Ma);
                 if constexpr (NORM) {  // the denominators, from the first column block's waves
                     if (den_ && grp * NW + cb == 0 && lane_g() == 0) {
                         const Rows<float> rd(den_, 1, row0, re, C);
 #pragma unroll
                         for (int I = 0; I < CB; ++I)
-                            if (owns_block<CB, RSPLIT>(H, I))
+                            if (owns_block<CB, RS>(H, I))
                                 __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, pden[I]), rd.rsrc,
                                                                       (16 * I + lane_r()) * 4, 0, 0);
                     }
@@ -170,7 +156,7 @@ __device__ __forceinline__ void fwd_sweep(const T *q_, const T *k_, const T *v_,
 
 #pragma unroll
             for (int I = 0; I < CB; ++I) {
-                if (!owns_block<CB, RSPLIT>(H, I)) continue;
+                if (!owns_block<CB, RS>(H, I)) continue;
                 RF qf[KS];
 #pragma unroll
                 for (int k = 0; k < KS; ++k) qf[k] = EO::load(Qs, RQ, I, k);
@@ -252,7 +238,13 @@ constexpr int fwd_min_wg() {
     return NORM && !SONLY && E == 128 && M == 128 && sizeof(T) == 2 ? CP_FWD_WIDE_NORM_MINWG : 1;
 }
 
-template <typename T, int E, int M, int C, int G, int RSPLIT, int NPF, bool NORM, bool FMAP, bool SONLY>
+// Workgroups per (slice, segment): G column groups times RG row groups.  A
+// workgroup of row group rg holds RSPLIT waves per column block, of row sets
+// rg * RSPLIT + h: the RG * RSPLIT row sets of a slice split each chunk's
+// query row blocks (owns_block), so a row of the output is written by the
+// waves of one workgroup only, and every workgroup of a slice carries the
+// whole state of its column group.
+template <typename T, int E, int M, int C, int G, int RSPLIT, int RG, int NPF, bool NORM, bool FMAP, bool SONLY>
 __global__ __launch_bounds__(64 * (M / 16 / G) * RSPLIT, (fwd_min_wg<T, E, M, NORM, SONLY>())) void cp_fwd_kernel(
     const T *__restrict__ Q, const T *__restrict__ K, const T *__restrict__ V, T *__restrict__ Out,
     const float *__restrict__ state_in, const float *__restrict__ z_in, float *__restrict__ state_out,
@@ -262,7 +254,10 @@ __global__ __launch_bounds__(64 * (M / 16 / G) * RSPLIT, (fwd_min_wg<T, E, M, NO
     constexpr int EB = E / 16, MB = M / 16, CB = C / 16;
     static_assert(MB % G == 0, "column groups split the column blocks evenly");
     static_assert(NPF >= 2, "the load ring needs at least two stages");
-    static_assert(RSPLIT == 1 || (RSPLIT == 2 && CB >= 4 && CB % 2 == 0), "row sets need pairs of row blocks");
+    constexpr int RS = RSPLIT * RG;
+    static_assert(RS == 1 || (CB % (2 * RS) == 0), "row sets need pairs of row blocks");
+    static_assert(RS <= 4, "at most four row sets");
+    static_assert(!SONLY || RG == 1, "the state-only pass has no row groups");
     constexpr int NW = MB / G, NT = 64 * NW * RSPLIT, MW = 16 * NW;
     constexpr int RQ = Stage<T, NT, C, E>::RS, RV = Stage<T, NT, C, MW>::RS;
     constexpr int BUF = 2 * C * RQ + C * RV;
@@ -271,8 +266,8 @@ __global__ __launch_bounds__(64 * (M / 16 / G) * RSPLIT, (fwd_min_wg<T, E, M, NO
 
     const int nseg = (L + seg_len - 1) / seg_len;
     int slice, part;
-    map_block(blockIdx.x, NS, G * nseg, slice, part);
-    const int grp = part % G, seg = part / G;
+    map_block(blockIdx.x, NS, G * RG * nseg, slice, part);
+    const int grp = part % G, rg = (part / G) % RG, seg = part / (G * RG);
     if (SONLY && seg == nseg - 1) return;  // the last segment's increment is never needed
     const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
     const int cb = w % NW, h = w / NW;
@@ -319,12 +314,15 @@ __global__ __launch_bounds__(64 * (M / 16 / G) * RSPLIT, (fwd_min_wg<T, E, M, NO
                 }
         }
     }
-    if (h == 0)
-        fwd_sweep<T, E, M, C, NW, RSPLIT, NPF, NORM, FMAP, SONLY, 0>(q_, k_, v_, o_, den_, rb, re, grp, cb, eps, lds, S,
-                                                                     z, Ea, Ma);
-    else
-        fwd_sweep<T, E, M, C, NW, RSPLIT, NPF, NORM, FMAP, SONLY, 1>(q_, k_, v_, o_, den_, rb, re, grp, cb, eps, lds, S,
-                                                                     z, Ea, Ma);
+    const int H = rg * RSPLIT + h;  // the wave's row set
+#define CP_FWD_SWEEP(HH)                                                                                          \
+    fwd_sweep<T, E, M, C, NW, RSPLIT, RS, NPF, NORM, FMAP, SONLY, ((HH) < RS ? (HH) : 0)>(                       \
+        q_, k_, v_, o_, den_, rb, re, grp, cb, eps, lds, S, z, Ea, Ma)
+    if (H == 0 || RS == 1) CP_FWD_SWEEP(0);
+    else if (H == 1 || RS == 2) CP_FWD_SWEEP(1);
+    else if (H == 2 || RS == 3) CP_FWD_SWEEP(2);
+    else CP_FWD_SWEEP(3);
+#undef CP_FWD_SWEEP
 
     if constexpr (SONLY) {
         if (h == 0) {
@@ -339,7 +337,7 @@ __global__ __launch_bounds__(64 * (M / 16 / G) * RSPLIT, (fwd_min_wg<T, E, M, NO
                 }
         }
     } else {
-        if (h == 0 && seg == nseg - 1) {  // the final state of the slice
+        if (H == 0 && seg == nseg - 1) {  // the final state of the slice
             float *st_ = state_out ? state_out + (int64_t)slice * Ea * Ma : nullptr;
             float *zt_ = z_out ? z_out + (int64_t)slice * Ea : nullptr;
 #pragma unroll

@@ -38,7 +38,7 @@ hipError_t launch_fwd_t(const FwdArgs &a, hipStream_t s) {
     float eps = a.eps;
     const dim3 block(64 * (M / 16 / P::FG) * P::FRS);
 
-    const int nseg0 = fwd_segments(L, NS, P::FG, P::FC);
+    const int nseg0 = fwd_segments(L, NS, P::FG * P::FRG, P::FC);
     const int nchunks = (L + P::FC - 1) / P::FC;
     int seg_len = (nchunks + nseg0 - 1) / nseg0 * P::FC;
     const int nseg = (L + seg_len - 1) / seg_len;
@@ -61,16 +61,16 @@ hipError_t launch_fwd_t(const FwdArgs &a, hipStream_t s) {
             if (e != hipSuccess) return e;
             owned = true;
         }
-        auto k1 = cp_fwd_kernel<T, E, M, P::FC, P::FG, P::FRS, P::FNPF, NORM, FMAP, true>;
+        auto k1 = cp_fwd_kernel<T, E, M, P::FC, P::FG, P::FRS, 1, P::FNPF, NORM, FMAP, true>;
         void *args1[] = {&q, &k, &v, &o, &s0, &z0, &st, &zt, &dn, &ws, &L, &NS, &seg_len, &eps, &Ea, &Ma};
         e = launch_kernel(reinterpret_cast<const void *>(k1), dim3(NS * P::FG * nseg), block, args1, s);
     } else {
         seg_len = L;
     }
     if (e == hipSuccess) {
-        auto k2 = cp_fwd_kernel<T, E, M, P::FC, P::FG, P::FRS, P::FNPF, NORM, FMAP, false>;
+        auto k2 = cp_fwd_kernel<T, E, M, P::FC, P::FG, P::FRS, P::FRG, P::FNPF, NORM, FMAP, false>;
         void *args2[] = {&q, &k, &v, &o, &s0, &z0, &st, &zt, &dn, &ws, &L, &NS, &seg_len, &eps, &Ea, &Ma};
-        e = launch_kernel(reinterpret_cast<const void *>(k2), dim3(NS * P::FG * nseg), block, args2, s);
+        e = launch_kernel(reinterpret_cast<const void *>(k2), dim3(NS * P::FG * P::FRG * nseg), block, args2, s);
     }
     if (owned) {
         const hipError_t f = hipFreeAsync(ws, s);

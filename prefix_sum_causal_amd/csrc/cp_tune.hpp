@@ -7,6 +7,10 @@
 //        block of dQ, dK and dV, one wave per block,
 //   FRS  forward row sets: waves per output column block, which split the
 //        chunk's query row blocks,
+//   FRG  forward row groups: workgroups per (slice, column group) that split
+//        the chunk's query row blocks, so that every output row is written
+//        by one workgroup (whole 128-byte lines stream to HBM at a higher
+//        rate than lines whose pieces come from two compute units),
 //   FNPF, BNPF  stages of the forward / backward load ring (NPF-1 chunks are
 //        in flight while one is computed),
 //   BNB  backward column blocks per wave (1 or 2): a wave with two blocks
@@ -14,6 +18,9 @@
 //        both,
 //   BIDLE  extra backward waves that only help copy, for two-block waves (by
 //        default a workgroup of three waves gets a fourth, one per SIMD),
+//   BRG  backward row groups: workgroups per (slice, column group) that split
+//        the chunk's row blocks (each writes whole rows of dQ, dK and dV);
+//        used with two-block waves, whose workgroups then take every column,
 // Each value can be overridden when the library is built (-DCP_BF16_FC=32 ...)
 // for tuning sweeps.
 #pragma once
@@ -22,13 +29,16 @@
 #define CP_BF16_FC 64
 #endif
 #ifndef CP_BF16_FG
-#define CP_BF16_FG 2
+#define CP_BF16_FG 1
+#endif
+#ifndef CP_BF16_FRG
+#define CP_BF16_FRG 2
 #endif
 #ifndef CP_BF16_BC
 #define CP_BF16_BC 64
 #endif
 #ifndef CP_BF16_FRS
-#define CP_BF16_FRS 2
+#define CP_BF16_FRS 1
 #endif
 #ifndef CP_BF16_FNPF
 #define CP_BF16_FNPF 3
@@ -42,11 +52,14 @@
 #ifndef CP_BF16_BNB
 #define CP_BF16_BNB 2
 #endif
+#ifndef CP_BF16_BRG
+#define CP_BF16_BRG 2
+#endif
 #ifndef CP_BF16_BIDLE
 #define CP_BF16_BIDLE -1
 #endif
 #ifndef CP_BF16_NB2_BC
-#define CP_BF16_NB2_BC 32
+#define CP_BF16_NB2_BC 64
 #endif
 #ifndef CP_F32_WIDE_FC
 #define CP_F32_WIDE_FC 32
@@ -104,16 +117,21 @@ template <int E, int M> struct Tune<__bf16, E, M> {
     static constexpr int FG0 = M > 64 && CP_BF16_FG < 2 ? 2 : CP_BF16_FG;
     static constexpr int FG = FG0 > M / 16 ? M / 16 : FG0;
     static constexpr int BC0 = wide && CP_BF16_BC > 32 ? 32 : CP_BF16_BC;
-    static constexpr int FRS = FC >= 64 && E <= 64 ? CP_BF16_FRS : 1;  // E = 128: registers
+    // row sets inside a workgroup: two where the workgroup would otherwise
+    // be a single wave or spans 128 columns (E = 128: registers)
+    static constexpr int FRS = FC >= 64 && E <= 64 ? (M / 16 / FG == 1 || M > 64 ? 2 : CP_BF16_FRS) : 1;
+    // row groups of workgroups (whole output rows per workgroup) where the
+    // chunk has enough pairs of row blocks
+    static constexpr int FRG = M <= 64 && (FC / 16) % (2 * FRS * CP_BF16_FRG) == 0 ? CP_BF16_FRG : 1;
     static constexpr int FNPF = E == 128 && CP_BF16_FNPF > 2 ? 2 : CP_BF16_FNPF;  // E = 128: registers
     static constexpr int BNPF = CP_BF16_BNPF;
-    static constexpr int BG = bwd_groups(E, M, CP_BF16_BG);
     // two blocks per wave where they divide evenly and registers allow; such
-    // waves run shorter chunks (their per-chunk work is twice as long)
-    static constexpr int BNB = CP_BF16_BNB == 2 && E <= 64 && M <= 64 && (E / 16) % (2 * BG) == 0 &&
-                                       (M / 16) % (2 * BG) == 0
-                                   ? 2
-                                   : 1;
+    // waves run shorter chunks (their per-chunk work is twice as long); with
+    // row groups their workgroups take every column and split the rows
+    static constexpr bool NB2 = CP_BF16_BNB == 2 && E <= 64 && M <= 64;
+    static constexpr int BRG = NB2 && (E / 16) % 2 == 0 && (M / 16) % 2 == 0 ? CP_BF16_BRG : 1;
+    static constexpr int BG = BRG > 1 ? 1 : bwd_groups(E, M, CP_BF16_BG);
+    static constexpr int BNB = NB2 && (E / 16) % (2 * BG) == 0 && (M / 16) % (2 * BG) == 0 ? 2 : 1;
     static constexpr int BC = BNB == 2 ? CP_BF16_NB2_BC : BC0;
     static constexpr int BIDLE =
         BNB != 2 ? 0 : CP_BF16_BIDLE >= 0 ? CP_BF16_BIDLE : (4 - bwd_waves<E, M, BG, BNB, 0>() % 4) % 4;
@@ -133,10 +151,12 @@ template <int E, int M> struct Tune<float, E, M> {
     static constexpr int FG = FG0 > M / 16 ? M / 16 : FG0;
     static constexpr int BC = wide ? CP_F32_WIDE_BC : CP_F32_BC;
     static constexpr int FRS = 1;
+    static constexpr int FRG = 1;
     static constexpr int FNPF = CP_F32_FNPF;
     static constexpr int BNPF = CP_F32_BNPF;
     static constexpr int BG = bwd_groups(E, M, CP_F32_BG);
     static constexpr int BNB = 1;
+    static constexpr int BRG = 1;
     static constexpr int BIDLE = 0;
 };
 
