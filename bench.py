@@ -268,10 +268,12 @@ def main() -> int:
     ms = cp.timing_end()
     assert len(ms) == args.steps * per_step, "every hooked launch is recorded"
     # a call's time is the sum of its launches
-    times, off = {}, 0
+    times, launch_us, off = {}, {}, 0
     for kind, nl in zip(kinds, n_launch):
         times[kind] = sum(sum(ms[i * per_step + off:i * per_step + off + nl]) for i in range(args.steps)) \
             / args.steps * 1e-3
+        launch_us[kind] = [sum(ms[i * per_step + off + j] for i in range(args.steps)) / args.steps * 1e3
+                           for j in range(nl)]
         off += nl
     per_kernel = {}
     for kind in kinds:
@@ -279,7 +281,7 @@ def main() -> int:
         f = algorithmic_flops(w, kind)
         per_kernel[kind] = {"avg_us": times[kind] * 1e6, "alg_bytes": b, "GBps": b / times[kind] / 1e9,
                             "alg_flops": f, "TFps": f / times[kind] / 1e12,
-                            "launches": n_launch[kinds.index(kind)]}
+                            "launches": n_launch[kinds.index(kind)], "launch_us": launch_us[kind]}
     # Cold caches: each call again, after reading 1 GiB (more than L2 and
     # the MALL hold), so that no input is found in a cache.  The eviction is a
     # read, not a write: a write would leave the caches full of dirty lines

@@ -40,14 +40,24 @@
 
 namespace cp {
 
-// The chunk loop of one wave over rows [rb, re) of its slice: output column
-// block cb of the workgroup's group, query row blocks of row set H of RS
-// (the row sets of a slice: RSPLIT waves of each workgroup times the row
-// groups of workgroups).  Every wave runs the same staging and barriers; the
-// state (S, z: carried in and out by reference) is carried by every row set.
-// SONLY: only the state is accumulated (no Q, no outputs).
-template <typename T, int E, int M, int C, int NW, int RSPLIT, int RS, int NPF, bool NORM, bool FMAP, bool SONLY,
-          int H>
+// The chunk loop of one wave over rows [rb, re) of its slice, for the query
+// row blocks of row set H of RS (the row sets of a slice: RSPLIT waves of each
+// workgroup times the row groups of workgroups).  Every wave runs the same
+// staging and barriers.
+//   Numerator waves (DEN = false) own output column block cb of the
+//   workgroup's group and carry the state S (by reference) of those columns.
+//   Normalised form, with a denominator wave (DW): that wave (DEN = true,
+//   one per workgroup) carries z instead: per chunk it forms the score tiles
+//   of the workgroup's rows, d_i = phi(q_i) . z_{c-1} + sum_{j<=i in chunk}
+//   A(i, j) + eps, and hands d to the numerator waves through LDS; they
+//   divide and store their tiles of chunk c one step later, after the next
+//   barrier, so the normaliser is computed once per row instead of once per
+//   column block.  Without it (!DW: wide heads, where the extra wave's
+//   registers would halve the workgroups per CU) every numerator wave also
+//   carries z and forms the denominators of its own tiles (z entering the
+//   products as a hi + lo pair of operands).
+template <typename T, int E, int M, int C, int NW, int RSPLIT, int RS, int NPF, bool NORM, bool FMAP, bool DW,
+          bool DEN, int H>
 __device__ __forceinline__ void fwd_sweep(const T *q_, const T *k_, const T *v_, T *o_, float *den_, int rb,
                                           int re, int grp, int cb, float eps, T *lds, f32x4 (&S)[E / 16],
                                           f32x4 (&z)[E / 16], int Ea, int Ma) {
@@ -56,12 +66,17 @@ __device__ __forceinline__ void fwd_sweep(const T *q_, const T *k_, const T *v_,
     using EO = EOps<T, E>;
     using RF = typename EO::rf;
     constexpr int EB = E / 16, CB = C / 16, KS = EO::STEPS;
-    constexpr int NT = 64 * NW * RSPLIT, MW = 16 * NW;
+    constexpr int NT = 64 * (NW * RSPLIT + (NORM && DW ? 1 : 0)), MW = 16 * NW;
+    constexpr bool SELF = NORM && !DW;         // numerator waves form their own denominators
+    constexpr bool DELAY = NORM && DW && !DEN;  // numerator waves divide one step later
     using SQ = Stage<T, NT, C, E>;
     using SV = Stage<T, NT, C, MW>;
     constexpr int RQ = SQ::RS, RV = SV::RS;
     constexpr int BUF = 2 * C * RQ + C * RV;  // Q, K, V columns of the group
     constexpr int JMAX = last_block<CB, RS>(H);  // key blocks this wave scores: J <= JMAX
+    static_assert(!DEN || (NORM && DW), "the denominator wave belongs to the normalised form");
+    // NORM: the denominators of the last two chunks follow the row buffers
+    float *const denbuf = reinterpret_cast<float *>(lds + 2 * BUF);
 
     const Diag diag;
 
@@ -71,20 +86,37 @@ __device__ __forceinline__ void fwd_sweep(const T *q_, const T *k_, const T *v_,
     struct Stages {
         SQ q, k;
         SV v;
-        __device__ __forceinline__ void load(const T *q_, const T *k_, const T *v_, int row0, int re, int col0,
-                                             int Ea, int Ma) {
-            if constexpr (!SONLY) q.load(Rows<T>(q_, Ea, row0, re, C), 0, Ea);
-            k.load(Rows<T>(k_, Ea, row0, re, C), 0, Ea);
-            v.load(Rows<T>(v_, Ma, row0, re, C), col0, Ma);
-        }
     };
     const int col0 = 16 * grp * NW;
     Stages st[NPF];
 #pragma unroll
     for (int s = 0; s < NPF - 1; ++s) {
-        st[s].load(q_, k_, v_, rb + s * C, re, col0, Ea, Ma);
+        st[s].q.load(Rows<T>(q_, Ea, rb + s * C, re, C), 0, Ea);
+        st[s].k.load(Rows<T>(k_, Ea, rb + s * C, re, C), 0, Ea);
+        st[s].v.load(Rows<T>(v_, Ma, rb + s * C, re, C), col0, Ma);
         __builtin_amdgcn_sched_barrier(0);  // stages complete in order
     }
+
+    // NORM numerator waves: the previous chunk's output tiles, divided by its
+    // denominators once they are in LDS
+    f32x4 prev[CB];
+#pragma unroll
+    for (int I = 0; I < CB; ++I) prev[I] = zero4();
+    auto finish_prev = [&](int prow0, int pc) {
+        if constexpr (DELAY) {
+            const float *dn = denbuf + (pc & 1) * C;
+            const Rows<T> ro(o_, Ma, prow0, re, C);
+#pragma unroll
+            for (int I = 0; I < CB; ++I)
+                if (owns_block<CB, RS>(H, I)) {
+                    const float rcp = 1.f / dn[16 * I + lane_r()];
+                    f32x4 o = prev[I];
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) o[t] *= rcp;
+                    st_out<T>(ro, I, grp * NW + cb, o, Ma);
+                }
+        }
+    };
 
     const int nchunks = (re - rb + C - 1) / C;
     const int nsteps = (nchunks + NPF - 1) / NPF * NPF;
@@ -94,7 +126,7 @@ __device__ __forceinline__ void fwd_sweep(const T *q_, const T *k_, const T *v_,
             const int c = c0 + s;
             const int row0 = rb + c * C;
             T *Qs = lds + (c & 1) * BUF, *Ks = Qs + C * RQ, *Vs = Ks + C * RQ;
-            if constexpr (!SONLY) st[s].q.template store<NORM && FMAP>(Qs, row0, re, Ea);
+            st[s].q.template store<NORM && FMAP>(Qs, row0, re, Ea);
             st[s].k.template store<NORM && FMAP>(Ks, row0, re, Ea);
             st[s].v.store(Vs);
             __syncthreads();
@@ -107,11 +139,10 @@ __device__ __forceinline__ void fwd_sweep(const T *q_, const T *k_, const T *v_,
             Stages &nx = st[(s + NPF - 1) % NPF];
             const int nrow0 = row0 + (NPF - 1) * C;
             f32x4 pend[CB];  // this step's output tiles (owned row blocks)
-            float pden[CB];  // NORM: their denominators (row 16 I + r)
+            float pden[CB];  // SELF: their denominators (row 16 I + r)
             int nload = 0;   // arrays of the next chunk whose loads are issued
             auto issue_load = [&]() {
-                if constexpr (!SONLY)
-                    if (nload == 0) nx.q.load(Rows<T>(q_, Ea, nrow0, re, C), 0, Ea);
+                if (nload == 0) nx.q.load(Rows<T>(q_, Ea, nrow0, re, C), 0, Ea);
                 if (nload == 1) nx.k.load(Rows<T>(k_, Ea, nrow0, re, C), 0, Ea);
                 if (nload == 2) nx.v.load(Rows<T>(v_, Ma, nrow0, re, C), col0, Ma);
                 ++nload;
@@ -119,11 +150,13 @@ __device__ __forceinline__ void fwd_sweep(const T *q_, const T *k_, const T *v_,
             };
             // the step's output tiles (after every owned row block is done)
             auto issue_store = [&]() {
-                const Rows<T> ro(o_, Ma, row0, re, C);
+                if constexpr (!NORM || SELF) {
+                    const Rows<T> ro(o_, Ma, row0, re, C);
 #pragma unroll
-                for (int I = 0; I < CB; ++I)
-                    if (owns_block<CB, RS>(H, I)) st_out<T>(ro, I, grp * NW + cb, pend[I], Ma);
-                if constexpr (NORM) {  // the denominators, from the first column block's waves
+                    for (int I = 0; I < CB; ++I)
+                        if (owns_block<CB, RS>(H, I)) st_out<T>(ro, I, grp * NW + cb, pend[I], Ma);
+                }
+                if constexpr (SELF) {  // the denominators, from the first column block's waves
                     if (den_ && grp * NW + cb == 0 && lane_g() == 0) {
                         const Rows<float> rd(den_, 1, row0, re, C);
 #pragma unroll
@@ -136,22 +169,29 @@ __device__ __forceinline__ void fwd_sweep(const T *q_, const T *k_, const T *v_,
                 __builtin_amdgcn_sched_barrier(0);
             };
             issue_load();
+            if constexpr (DELAY) {
+                // the previous chunk, now that its denominators are in LDS
+                if (c > 0) finish_prev(row0 - C, c - 1);
+                __builtin_amdgcn_sched_barrier(0);
+            }
             F vt[CB];  // V_J^T fragments of this wave's columns
+            if constexpr (!DEN) {
 #pragma unroll
-            for (int b = 0; b < CB; ++b) vt[b] = O::tr_frag(Vs, RV, b, cb);
-            if constexpr (!SONLY) {
+                for (int b = 0; b < CB; ++b) vt[b] = O::tr_frag(Vs, RV, b, cb);
+            }
 
             RF kf[CB][KS];
 #pragma unroll
             for (int b = 0; b <= JMAX; ++b)
 #pragma unroll
                 for (int k = 0; k < KS; ++k) kf[b][k] = EO::load(Ks, RQ, b, k);
-            // S_{c-1} (and z_{c-1}) as A operands
+            // S_{c-1} (or, in the denominator wave, z_{c-1}) as A operands;
+            // SELF: z_{c-1} as a hi + lo pair
             RF sa[KS], zh[KS], zl[KS];
 #pragma unroll
             for (int k = 0; k < KS; ++k) {
                 sa[k] = EO::state(S, k);
-                if constexpr (NORM) EO::state_split(z, k, zh[k], zl[k]);
+                if constexpr (SELF) EO::state_split(z, k, zh[k], zl[k]);
             }
 
 #pragma unroll
@@ -160,11 +200,11 @@ __device__ __forceinline__ void fwd_sweep(const T *q_, const T *k_, const T *v_,
                 RF qf[KS];
 #pragma unroll
                 for (int k = 0; k < KS; ++k) qf[k] = EO::load(Qs, RQ, I, k);
+                // inter-chunk: Out^T += S^T Q_I^T (denominator: z . q_i in every row)
                 f32x4 o = zero4(), d = zero4();
-                // inter-chunk: Out^T += S^T Q_I^T
 #pragma unroll
                 for (int k = 0; k < KS; ++k) EO::mma(o, sa[k], qf[k]);
-                if constexpr (NORM) {
+                if constexpr (SELF) {
 #pragma unroll
                     for (int k = 0; k < KS; ++k) {
                         EO::mma(d, zh[k], qf[k]);
@@ -173,6 +213,7 @@ __device__ __forceinline__ void fwd_sweep(const T *q_, const T *k_, const T *v_,
                 }
                 // intra-chunk: Out^T += V^T A^T with A^T(J, I) = K_J Q_I^T
                 // masked on the diagonal, key blocks J <= I taken in pairs
+                // (denominator: the column sums of A^T)
 #pragma unroll
                 for (int J0 = 0; J0 <= I; J0 += 2) {
                     f32x4 a0 = zero4();
@@ -186,69 +227,198 @@ __device__ __forceinline__ void fwd_sweep(const T *q_, const T *k_, const T *v_,
                         for (int k = 0; k < KS; ++k) EO::mma(a1, kf[J0 + 1][k], qf[k]);
                         if (J0 + 1 == I) a1 = diag.keys(a1);
                         at1 = O::cvt(a1);
-                        vt1 = vt[J0 + 1];
+                        if constexpr (!DEN) vt1 = vt[J0 + 1];
                     }
                     const F at0 = O::cvt(a0);
-                    O::mma2(o, vt[J0], vt1, at0, at1);
-                    if constexpr (NORM) O::mma2(d, O::ones(), O::ones(), at0, at1);
+                    if constexpr (DEN) O::mma2(o, O::ones(), O::ones(), at0, at1);
+                    else O::mma2(o, vt[J0], vt1, at0, at1);
+                    if constexpr (SELF) O::mma2(d, O::ones(), O::ones(), at0, at1);
                 }
-                if constexpr (NORM) {
+                if constexpr (SELF) {
+                    // every row of the tile holds the same column sums
+                    const float rcp = 1.f / (d[0] + eps);
 #pragma unroll
-                    for (int t = 0; t < 4; ++t) o[t] = o[t] / (d[t] + eps);
-                    pden[I] = d[0] + eps;  // every row of the tile holds the same column sums
+                    for (int t = 0; t < 4; ++t) o[t] *= rcp;
+                    pden[I] = d[0] + eps;
+                }
+                if constexpr (DEN) {
+                    // lane (g, r) holds d of query row 16 I + r (every row of
+                    // the tile is the same)
+                    const float d = o[0] + eps;
+                    if (lane_g() == 0) {
+                        denbuf[(c & 1) * C + 16 * I + lane_r()] = d;
+                        if (den_) {
+                            const Rows<float> rd(den_, 1, row0, re, C);
+                            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, d), rd.rsrc,
+                                                                  (16 * I + lane_r()) * 4, 0, 0);
+                        }
+                    }
                 }
                 pend[I] = o;
                 issue_load();
             }
-            }
             while (nload < 3) issue_load();
 
-            // S_c = S_{c-1} + K_c^T V_c  (and z_c = z_{c-1} + K_c^T 1)
+            // S_c = S_{c-1} + K_c^T V_c  (denominator wave: z_c = z_{c-1} + K_c^T 1)
 #pragma unroll
             for (int e = 0; e < EB; ++e) {
-                dotk<T>(S[e], 0, CB, [&](int J) { return EO::tr_e(Ks, RQ, J, e); }, [&](int J) { return vt[J]; });
-                // (the state-only sweep stores z from the first column block)
-                if constexpr (NORM)
-                    if (!SONLY || grp * NW + cb == 0)
-                        dotk<T>(z[e], 0, CB, [&](int J) { return EO::tr_e(Ks, RQ, J, e); },
-                                [&](int) { return O::ones(); });
-                if constexpr (!SONLY)
-                    if (e == (EB - 1) / 2) issue_store();
+                if constexpr (DEN)
+                    dotk<T>(S[e], 0, CB, [&](int J) { return EO::tr_e(Ks, RQ, J, e); }, [&](int) { return O::ones(); });
+                else
+                    dotk<T>(S[e], 0, CB, [&](int J) { return EO::tr_e(Ks, RQ, J, e); }, [&](int J) { return vt[J]; });
+                if constexpr (SELF)
+                    dotk<T>(z[e], 0, CB, [&](int J) { return EO::tr_e(Ks, RQ, J, e); }, [&](int) { return O::ones(); });
+                if (e == (EB - 1) / 2) issue_store();
             }
+            if constexpr (DELAY) {
+#pragma unroll
+                for (int I = 0; I < CB; ++I) prev[I] = pend[I];
+            }
+        }
+    }
+    if constexpr (NORM && DW) {
+        // the last chunk: its denominators become visible after one more barrier
+        __syncthreads();
+        if constexpr (DELAY) finish_prev(rb + (nsteps - 1) * C, nsteps - 1);
+    }
+}
+
+// The state increments of the segments of a forward over sequence segments
+// (see below): workgroup (slice s, segment g) sums, over the rows of segment
+// g, dS = sum_j k_j v_j^T and, for the normalised form, dz = sum_j k_j (k =
+// phi of the raw keys when FMAP), and writes them to ws[s][g] (E*M floats of
+// dS, row e and column m, then E floats of dz).  Only K and V are read: per
+// chunk of C rows all threads copy K and V into LDS (one barrier per chunk,
+// NPF-1 chunks in flight), and wave w adds K^T V into the state tiles of its
+// CW column blocks of M (and of its share of the E/16 tiles of dz, as K^T 1).
+// The segments' increments are independent of each other, so this pass runs
+// at the rate of its two input streams; the last segment's increment is never
+// needed and not computed.
+template <typename T, int E, int M, int C, int NW, int NPF, bool NORM, bool FMAP>
+__global__ __launch_bounds__(64 * NW) void cp_seg_state_kernel(const T *__restrict__ K, const T *__restrict__ V,
+                                                               float *__restrict__ ws, int L, int NS, int seg_len,
+                                                               int Ea, int Ma) {
+    using O = Ops<T>;
+    using F = typename O::frag;
+    using EO = EOps<T, E>;
+    constexpr int EB = E / 16, MB = M / 16, CB = C / 16, CW = MB / NW, NT = 64 * NW;
+    static_assert(MB % NW == 0, "waves split the column blocks evenly");
+    static_assert(NPF >= 2, "the load ring needs at least two stages");
+    using SK = Stage<T, NT, C, E>;
+    using SV = Stage<T, NT, C, M>;
+    constexpr int RK = SK::RS, RV = SV::RS;
+    constexpr int BUF = C * RK + C * RV;
+    constexpr int WS = E * M + E;
+    // dz tiles (e-tiles of K^T 1) dealt round robin to the waves
+    constexpr int ZT = (EB + NW - 1) / NW;
+    __shared__ __attribute__((aligned(16))) T lds[2 * BUF];
+
+    const int nseg = (L + seg_len - 1) / seg_len;
+    int slice, seg;
+    map_block(blockIdx.x, NS, nseg - 1, slice, seg);
+    const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    const int g = lane_g(), r = lane_r();
+    const T *k_ = K + (int64_t)slice * L * Ea;
+    const T *v_ = V + (int64_t)slice * L * Ma;
+    const int rb = seg * seg_len, re = rb + seg_len < L ? rb + seg_len : L;
+
+    f32x4 S[CW][EB], Z[ZT];
+#pragma unroll
+    for (int x = 0; x < CW; ++x)
+#pragma unroll
+        for (int e = 0; e < EB; ++e) S[x][e] = zero4();
+#pragma unroll
+    for (int i = 0; i < ZT; ++i) Z[i] = zero4();
+
+    struct Stages {
+        SK k;
+        SV v;
+    };
+    Stages st[NPF];
+#pragma unroll
+    for (int i = 0; i < NPF - 1; ++i) {
+        st[i].k.load(Rows<T>(k_, Ea, rb + i * C, re, C), 0, Ea);
+        st[i].v.load(Rows<T>(v_, Ma, rb + i * C, re, C), 0, Ma);
+        __builtin_amdgcn_sched_barrier(0);  // stages complete in order
+    }
+    const int nchunks = (re - rb + C - 1) / C;
+    const int nsteps = (nchunks + NPF - 1) / NPF * NPF;
+    for (int c0 = 0; c0 < nsteps; c0 += NPF) {
+#pragma unroll
+        for (int i = 0; i < NPF; ++i) {
+            const int c = c0 + i;
+            const int row0 = rb + c * C;
+            T *Ks = lds + (c & 1) * BUF, *Vs = Ks + C * RK;
+            st[i].k.template store<NORM && FMAP>(Ks, row0, re, Ea);
+            st[i].v.store(Vs);
+            __syncthreads();
+            Stages &nx = st[(i + NPF - 1) % NPF];
+            const int nrow0 = row0 + (NPF - 1) * C;
+            nx.k.load(Rows<T>(k_, Ea, nrow0, re, C), 0, Ea);
+            nx.v.load(Rows<T>(v_, Ma, nrow0, re, C), 0, Ma);
+            __builtin_amdgcn_sched_barrier(0);
+            F vt[CW][CB];  // V_J^T fragments of the wave's column blocks
+#pragma unroll
+            for (int x = 0; x < CW; ++x)
+#pragma unroll
+                for (int J = 0; J < CB; ++J) vt[x][J] = O::tr_frag(Vs, RV, J, w * CW + x);
+#pragma unroll
+            for (int e = 0; e < EB; ++e) {
+                F kt[CB];  // K^T fragments of e-tile e, shared by the column blocks
+#pragma unroll
+                for (int J = 0; J < CB; ++J) kt[J] = EO::tr_e(Ks, RK, J, e);
+#pragma unroll
+                for (int x = 0; x < CW; ++x) dotk<T>(S[x][e], 0, CB, [&](int J) { return kt[J]; }, [&](int J) { return vt[x][J]; });
+                if constexpr (NORM)
+                    if (e % NW == w) dotk<T>(Z[e / NW], 0, CB, [&](int J) { return kt[J]; }, [&](int) { return O::ones(); });
+            }
+        }
+    }
+    float *dS = ws + ((int64_t)slice * nseg + seg) * WS, *dz = dS + E * M;
+#pragma unroll
+    for (int x = 0; x < CW; ++x)
+#pragma unroll
+        for (int e = 0; e < EB; ++e)
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                dS[(EO::ecol(e) + EO::estride * g + t) * M + 16 * (w * CW + x) + r] = S[x][e][t];
+    if constexpr (NORM) {
+        if (r == 0) {
+#pragma unroll
+            for (int e = 0; e < EB; ++e)
+                if (e % NW == w)
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) dz[EO::ecol(e) + EO::estride * g + t] = Z[e / NW][t];
         }
     }
 }
 
 // Sequence segments: when slices are too few to fill the GPU, each slice is
 // cut into nseg segments of seg_len rows (a multiple of C) and run in two
-// launches.  The first (SONLY) computes each segment's state increment
-// dS = sum over its rows of k v^T (and dz = sum of phi(k)) into ws; the
-// second starts segment s from the carried-in state (state_in, z_in) plus the
-// exclusive sum of the increments of the segments before it (the chunked
-// scan's carry, one level up) and sweeps only its own rows.  ws holds, per slice and segment, E*M floats of dS (row e,
-// column m) then E floats of dz.  With one segment, ws is unused (NULL).
-#ifndef CP_FWD_WIDE_NORM_MINWG
-#define CP_FWD_WIDE_NORM_MINWG 2
-#endif
-// Workgroups per CU the compiler must leave room for: two for the normalised
-// sweep over 128 x 128 16-bit heads, whose registers otherwise exceed half a
-// SIMD's file (278 VGPRs) and let only one four-wave workgroup onto a CU.
-template <typename T, int E, int M, bool NORM, bool SONLY>
-constexpr int fwd_min_wg() {
-    return NORM && !SONLY && E == 128 && M == 128 && sizeof(T) == 2 ? CP_FWD_WIDE_NORM_MINWG : 1;
-}
-
+// launches.  The first (cp_seg_state_kernel) computes each segment's state
+// increment dS = sum over its rows of k v^T (and dz = sum of phi(k)) into ws;
+// the second starts segment s from the carried-in state (state_in, z_in) plus
+// the exclusive sum of the increments of the segments before it (the chunked
+// scan's carry, one level up) and sweeps only its own rows.  ws holds, per
+// slice and segment, E*M floats of dS (row e, column m) then E floats of dz.
+// With one segment, ws is unused (NULL).
+//
 // Workgroups per (slice, segment): G column groups times RG row groups.  A
 // workgroup of row group rg holds RSPLIT waves per column block, of row sets
 // rg * RSPLIT + h: the RG * RSPLIT row sets of a slice split each chunk's
 // query row blocks (owns_block), so a row of the output is written by the
 // waves of one workgroup only, and every workgroup of a slice carries the
-// whole state of its column group.
-template <typename T, int E, int M, int C, int G, int RSPLIT, int RG, int NPF, bool NORM, bool FMAP, bool SONLY>
-__global__ __launch_bounds__(64 * (M / 16 / G) * RSPLIT, (fwd_min_wg<T, E, M, NORM, SONLY>())) void cp_fwd_kernel(
+// whole state of its column group.  The normalised form (NORM, RSPLIT = 1)
+// adds one denominator wave per workgroup.
+// waves of a workgroup (DWAVE: with a denominator wave)
+template <int M, int G, int RSPLIT, bool DWAVE>
+constexpr int fwd_waves() { return (M / 16 / G) * RSPLIT + (DWAVE ? 1 : 0); }
+
+template <typename T, int E, int M, int C, int G, int RSPLIT, int RG, int NPF, bool NORM, bool FMAP, bool DW>
+__global__ __launch_bounds__((64 * fwd_waves<M, G, RSPLIT, NORM && DW>())) void cp_fwd_kernel(
     const T *__restrict__ Q, const T *__restrict__ K, const T *__restrict__ V, T *__restrict__ Out,
     const float *__restrict__ state_in, const float *__restrict__ z_in, float *__restrict__ state_out,
-    float *__restrict__ z_out, float *__restrict__ den, float *__restrict__ ws, int L, int NS, int seg_len,
+    float *__restrict__ z_out, float *__restrict__ den, const float *__restrict__ ws, int L, int NS, int seg_len,
     float eps, int Ea, int Ma) {
     using EO = EOps<T, E>;
     constexpr int EB = E / 16, MB = M / 16, CB = C / 16;
@@ -257,20 +427,22 @@ __global__ __launch_bounds__(64 * (M / 16 / G) * RSPLIT, (fwd_min_wg<T, E, M, NO
     constexpr int RS = RSPLIT * RG;
     static_assert(RS == 1 || (CB % (2 * RS) == 0), "row sets need pairs of row blocks");
     static_assert(RS <= 4, "at most four row sets");
-    static_assert(!SONLY || RG == 1, "the state-only pass has no row groups");
-    constexpr int NW = MB / G, NT = 64 * NW * RSPLIT, MW = 16 * NW;
+    static_assert(!NORM || !DW || RSPLIT == 1, "a denominator wave serves one row set");
+    constexpr bool DWAVE = NORM && DW;
+    constexpr int NW = MB / G, NT = 64 * (NW * RSPLIT + (DWAVE ? 1 : 0)), MW = 16 * NW;
     constexpr int RQ = Stage<T, NT, C, E>::RS, RV = Stage<T, NT, C, MW>::RS;
     constexpr int BUF = 2 * C * RQ + C * RV;
-    constexpr int WS = E * M + E;  // floats per (slice, segment) in ws
-    __shared__ __attribute__((aligned(16))) T lds[2 * BUF];
+    constexpr int DENB = DWAVE ? 2 * C * 4 / (int)sizeof(T) : 0;  // two chunks of denominators
+    constexpr int WS = E * M + E;                                // floats per (slice, segment) in ws
+    __shared__ __attribute__((aligned(16))) T lds[2 * BUF + DENB];
 
     const int nseg = (L + seg_len - 1) / seg_len;
     int slice, part;
     map_block(blockIdx.x, NS, G * RG * nseg, slice, part);
     const int grp = part % G, rg = (part / G) % RG, seg = part / (G * RG);
-    if (SONLY && seg == nseg - 1) return;  // the last segment's increment is never needed
     const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
-    const int cb = w % NW, h = w / NW;
+    const bool den_wave = DWAVE && w == NW;
+    const int cb = den_wave ? 0 : w % NW, h = den_wave ? 0 : w / NW;
     const int mb = grp * NW + cb;
     const int g = lane_g(), r = lane_r();
     // the tensors' own head sizes Ea <= E, Ma <= M (the kernel's tile sizes)
@@ -280,73 +452,86 @@ __global__ __launch_bounds__(64 * (M / 16 / G) * RSPLIT, (fwd_min_wg<T, E, M, NO
     T *o_ = Out + (int64_t)slice * L * Ma;
     float *den_ = den ? den + (int64_t)slice * L : nullptr;
     const int rb = seg * seg_len, re = rb + seg_len < L ? rb + seg_len : L;
-    float *ws_slice = ws ? ws + (int64_t)slice * nseg * WS : nullptr;
+    const float *ws_slice = ws ? ws + (int64_t)slice * nseg * WS : nullptr;
 
-    f32x4 S[EB];  // S[ecol(eb) + estride g + t][16 mb + r]
-    f32x4 z[EB];  // z[ecol(eb) + estride g + t] (same in every lane r)
+    // Numerator waves: S[ecol(eb) + estride g + t][16 mb + r], and without a
+    // denominator wave also z[ecol(eb) + estride g + t] (the same in every
+    // lane r).  Denominator wave: z, in S.
+    f32x4 S[EB], z[EB];
+    const float *s0 = state_in ? state_in + (int64_t)slice * Ea * Ma : nullptr;
+    const float *z0 = z_in ? z_in + (int64_t)slice * Ea : nullptr;
+    // The carried-in state plus the increments of the segments before this
+    // one (all of one segment's loads issued together).  The element of the
+    // increments a lane adds: its S entry, or for the denominator wave its z
+    // entry; without a denominator wave numerator waves add z as well.
+    constexpr bool SELFZ = NORM && !DW;
 #pragma unroll
-    for (int e = 0; e < EB; ++e) {
-        S[e] = zero4();
-        z[e] = zero4();
-    }
-    if (!SONLY && (state_in || z_in)) {  // the carried-in state before row 0
-        const float *s0 = state_in ? state_in + (int64_t)slice * Ea * Ma : nullptr;
-        const float *z0 = z_in ? z_in + (int64_t)slice * Ea : nullptr;
+    for (int e = 0; e < EB; ++e)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int row = EO::ecol(e) + EO::estride * g + t;
+            float x = 0.f;
+            if (den_wave) x = z0 && row < Ea ? z0[row] : 0.f;
+            else x = s0 && row < Ea && 16 * mb + r < Ma ? s0[row * Ma + 16 * mb + r] : 0.f;
+            S[e][t] = x;
+            z[e][t] = SELFZ && z0 && row < Ea ? z0[row] : 0.f;
+        }
+    for (int p = 0; p < seg; ++p) {
+        const float *inc = ws_slice + (int64_t)p * WS;
 #pragma unroll
         for (int e = 0; e < EB; ++e)
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
                 const int row = EO::ecol(e) + EO::estride * g + t;
-                if (s0 && row < Ea && 16 * mb + r < Ma) S[e][t] = s0[row * Ma + 16 * mb + r];
-                if (NORM && z0 && row < Ea) z[e][t] = z0[row];
+                S[e][t] += inc[den_wave ? E * M + row : row * M + 16 * mb + r];
+                if constexpr (SELFZ) z[e][t] += inc[E * M + row];
             }
     }
-    if (!SONLY && ws_slice) {
-        for (int p = 0; p < seg; ++p) {
-            const float *dS = ws_slice + (int64_t)p * WS, *dz = dS + E * M;
-#pragma unroll
-            for (int e = 0; e < EB; ++e)
-#pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    const int row = EO::ecol(e) + EO::estride * g + t;
-                    S[e][t] += dS[row * M + 16 * mb + r];
-                    if constexpr (NORM) z[e][t] += dz[row];
-                }
-        }
-    }
     const int H = rg * RSPLIT + h;  // the wave's row set
+    if (den_wave) {
+        if constexpr (DWAVE) {
 #define CP_FWD_SWEEP(HH)                                                                                          \
-    fwd_sweep<T, E, M, C, NW, RSPLIT, RS, NPF, NORM, FMAP, SONLY, ((HH) < RS ? (HH) : 0)>(                       \
+    fwd_sweep<T, E, M, C, NW, RSPLIT, RS, NPF, NORM, FMAP, DW, true, ((HH) < RS ? (HH) : 0)>(                    \
         q_, k_, v_, o_, den_, rb, re, grp, cb, eps, lds, S, z, Ea, Ma)
-    if (H == 0 || RS == 1) CP_FWD_SWEEP(0);
-    else if (H == 1 || RS == 2) CP_FWD_SWEEP(1);
-    else if (H == 2 || RS == 3) CP_FWD_SWEEP(2);
-    else CP_FWD_SWEEP(3);
+            if (H == 0 || RS == 1) CP_FWD_SWEEP(0);
+            else if (H == 1 || RS == 2) CP_FWD_SWEEP(1);
+            else if (H == 2 || RS == 3) CP_FWD_SWEEP(2);
+            else CP_FWD_SWEEP(3);
 #undef CP_FWD_SWEEP
-
-    if constexpr (SONLY) {
-        if (h == 0) {
-            float *dS = ws_slice + (int64_t)seg * WS, *dz = dS + E * M;
-#pragma unroll
-            for (int e = 0; e < EB; ++e)
-#pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    const int row = EO::ecol(e) + EO::estride * g + t;
-                    dS[row * M + 16 * mb + r] = S[e][t];
-                    if (NORM && mb == 0 && r == 0) dz[row] = z[e][t];
-                }
         }
     } else {
-        if (H == 0 && seg == nseg - 1) {  // the final state of the slice
-            float *st_ = state_out ? state_out + (int64_t)slice * Ea * Ma : nullptr;
+#define CP_FWD_SWEEP(HH)                                                                                          \
+    fwd_sweep<T, E, M, C, NW, RSPLIT, RS, NPF, NORM, FMAP, DW, false, ((HH) < RS ? (HH) : 0)>(                   \
+        q_, k_, v_, o_, den_, rb, re, grp, cb, eps, lds, S, z, Ea, Ma)
+        if (H == 0 || RS == 1) CP_FWD_SWEEP(0);
+        else if (H == 1 || RS == 2) CP_FWD_SWEEP(1);
+        else if (H == 2 || RS == 3) CP_FWD_SWEEP(2);
+        else CP_FWD_SWEEP(3);
+#undef CP_FWD_SWEEP
+    }
+
+    if (H == 0 && seg == nseg - 1) {  // the final state of the slice
+        if (den_wave) {
             float *zt_ = z_out ? z_out + (int64_t)slice * Ea : nullptr;
+            if (zt_ && r == 0 && grp == 0) {
+#pragma unroll
+                for (int e = 0; e < EB; ++e)
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        const int row = EO::ecol(e) + EO::estride * g + t;
+                        if (row < Ea) zt_[row] = S[e][t];
+                    }
+            }
+        } else {
+            float *st_ = state_out ? state_out + (int64_t)slice * Ea * Ma : nullptr;
+            float *zt_ = NORM && !DW && z_out && mb == 0 ? z_out + (int64_t)slice * Ea : nullptr;
 #pragma unroll
             for (int e = 0; e < EB; ++e)
 #pragma unroll
                 for (int t = 0; t < 4; ++t) {
                     const int row = EO::ecol(e) + EO::estride * g + t;
                     if (st_ && row < Ea && 16 * mb + r < Ma) st_[row * Ma + 16 * mb + r] = S[e][t];
-                    if (NORM && zt_ && mb == 0 && r == 0 && row < Ea) zt_[row] = z[e][t];
+                    if (zt_ && r == 0 && row < Ea) zt_[row] = z[e][t];
                 }
         }
     }

@@ -18,6 +18,13 @@ namespace cp {
 #define CP_SEG_WG_PER_CU 2
 #endif
 constexpr int kCUs = 256, kMinSegChunks = CP_SEG_MIN_CHUNKS, kSegWgPerCU = CP_SEG_WG_PER_CU;
+// stages of the load ring of the segment-increment pass, and its waves (at
+// most four, each owning M/16/waves column blocks of the increment)
+#ifndef CP_SEG_NPF
+#define CP_SEG_NPF 4
+#endif
+template <int M>
+constexpr int seg_state_waves() { return M / 16 >= 4 ? 4 : M / 16; }
 inline int fwd_segments(int L, int NS, int groups, int C) {
     const long wg = (long)NS * groups;
     const int nchunks = (L + C - 1) / C;
@@ -36,9 +43,13 @@ hipError_t launch_fwd_t(const FwdArgs &a, hipStream_t s) {
     float *st = a.state_out, *zt = a.z_out, *dn = a.den_out;
     int L = a.L, NS = a.NS, Ea = a.Ea, Ma = a.Ma;
     float eps = a.eps;
-    const dim3 block(64 * (M / 16 / P::FG) * P::FRS);
+    // the normalised form runs one row set per workgroup (plus, but for the
+    // widest heads, its denominator wave)
+    constexpr bool DW = NORM && P::FDW;
+    constexpr int FRS = NORM ? 1 : P::FRS, FRG = NORM ? P::FRG_N : P::FRG;
+    const dim3 block(64 * ((M / 16 / P::FG) * FRS + (DW ? 1 : 0)));
 
-    const int nseg0 = fwd_segments(L, NS, P::FG * P::FRG, P::FC);
+    const int nseg0 = fwd_segments(L, NS, P::FG * FRG, P::FC);
     const int nchunks = (L + P::FC - 1) / P::FC;
     int seg_len = (nchunks + nseg0 - 1) / nseg0 * P::FC;
     const int nseg = (L + seg_len - 1) / seg_len;
@@ -61,16 +72,17 @@ hipError_t launch_fwd_t(const FwdArgs &a, hipStream_t s) {
             if (e != hipSuccess) return e;
             owned = true;
         }
-        auto k1 = cp_fwd_kernel<T, E, M, P::FC, P::FG, P::FRS, 1, P::FNPF, NORM, FMAP, true>;
-        void *args1[] = {&q, &k, &v, &o, &s0, &z0, &st, &zt, &dn, &ws, &L, &NS, &seg_len, &eps, &Ea, &Ma};
-        e = launch_kernel(reinterpret_cast<const void *>(k1), dim3(NS * P::FG * nseg), block, args1, s);
+        constexpr int SW = seg_state_waves<M>();
+        auto k1 = cp_seg_state_kernel<T, E, M, P::FC, SW, CP_SEG_NPF, NORM, FMAP>;
+        void *args1[] = {&k, &v, &ws, &L, &NS, &seg_len, &Ea, &Ma};
+        e = launch_kernel(reinterpret_cast<const void *>(k1), dim3(NS * (nseg - 1)), dim3(64 * SW), args1, s);
     } else {
         seg_len = L;
     }
     if (e == hipSuccess) {
-        auto k2 = cp_fwd_kernel<T, E, M, P::FC, P::FG, P::FRS, P::FRG, P::FNPF, NORM, FMAP, false>;
+        auto k2 = cp_fwd_kernel<T, E, M, P::FC, P::FG, FRS, FRG, P::FNPF, NORM, FMAP, DW>;
         void *args2[] = {&q, &k, &v, &o, &s0, &z0, &st, &zt, &dn, &ws, &L, &NS, &seg_len, &eps, &Ea, &Ma};
-        e = launch_kernel(reinterpret_cast<const void *>(k2), dim3(NS * P::FG * P::FRG * nseg), block, args2, s);
+        e = launch_kernel(reinterpret_cast<const void *>(k2), dim3(NS * P::FG * FRG * nseg), block, args2, s);
     }
     if (owned) {
         const hipError_t f = hipFreeAsync(ws, s);

@@ -123,6 +123,13 @@ template <int E, int M> struct Tune<__bf16, E, M> {
     // row groups of workgroups (whole output rows per workgroup) where the
     // chunk has enough pairs of row blocks
     static constexpr int FRG = M <= 64 && (FC / 16) % (2 * FRS * CP_BF16_FRG) == 0 ? CP_BF16_FRG : 1;
+    // the normalised forward: one row set per workgroup (its denominator
+    // wave serves the workgroup's rows), row groups as above
+    static constexpr int FRG_N = M <= 64 && (FC / 16) % (2 * CP_BF16_FRG) == 0 ? CP_BF16_FRG : 1;
+    // a denominator wave per workgroup, but for 128 x 128 heads (its
+    // registers would halve the workgroups per CU; there every wave forms
+    // its own denominators)
+    static constexpr bool FDW = !(E == 128 && M == 128);
     static constexpr int FNPF = E == 128 && CP_BF16_FNPF > 2 ? 2 : CP_BF16_FNPF;  // E = 128: registers
     static constexpr int BNPF = CP_BF16_BNPF;
     // two blocks per wave where they divide evenly and registers allow; such
@@ -152,6 +159,8 @@ template <int E, int M> struct Tune<float, E, M> {
     static constexpr int BC = wide ? CP_F32_WIDE_BC : CP_F32_BC;
     static constexpr int FRS = 1;
     static constexpr int FRG = 1;
+    static constexpr int FRG_N = 1;
+    static constexpr bool FDW = !(E == 128 && M == 128);
     static constexpr int FNPF = CP_F32_FNPF;
     static constexpr int BNPF = CP_F32_BNPF;
     static constexpr int BG = bwd_groups(E, M, CP_F32_BG);
