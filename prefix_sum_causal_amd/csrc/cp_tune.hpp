@@ -34,6 +34,9 @@
 #ifndef CP_BF16_FRG
 #define CP_BF16_FRG 2
 #endif
+#ifndef CP_BF16_WIDE_FG
+#define CP_BF16_WIDE_FG 2
+#endif
 #ifndef CP_BF16_BC
 #define CP_BF16_BC 64
 #endif
@@ -114,7 +117,7 @@ template <int E, int M> struct Tune<__bf16, E, M> {
     // shorter chunks keep them in registers
     static constexpr int FC = ((M == 16 && E >= 64) || E == 128) && CP_BF16_FC > 32 ? 32 : CP_BF16_FC;
     // 128 output columns: two workgroups of four waves (registers per wave)
-    static constexpr int FG0 = M > 64 && CP_BF16_FG < 2 ? 2 : CP_BF16_FG;
+    static constexpr int FG0 = M > 64 && CP_BF16_FG < 2 ? CP_BF16_WIDE_FG : CP_BF16_FG;
     static constexpr int FG = FG0 > M / 16 ? M / 16 : FG0;
     static constexpr int BC0 = wide && CP_BF16_BC > 32 ? 32 : CP_BF16_BC;
     // row sets inside a workgroup: two where the workgroup would otherwise
