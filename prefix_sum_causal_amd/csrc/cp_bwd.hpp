@@ -89,7 +89,7 @@ template <typename T, int E, int M, int C, int G, int NB, int IDLE, int RG, int 
           int ROLE>
 __device__ __forceinline__ void bwd_sweep(const T *q_, const T *k_, const T *v_, const T *g_, const float *s0,
                                           const float *st, const float *zc_, const float *dd_, int Lpad, T *out_,
-                                          float *ds0, float *dz0, int L, int b, T *lds, int Ea, int Ma) {
+                                          float *ds0, float *dz0, int L, int b, lds_t<T> *lds, int Ea, int Ma) {
     using O = Ops<T>;
     using F = typename O::frag;
     using EE = EOps<T, E>;  // contraction over e
@@ -174,7 +174,7 @@ __device__ __forceinline__ void bwd_sweep(const T *q_, const T *k_, const T *v_,
         sk.load(Rows<T>(k_, Ea, 0, L, C), 0, Ea);
         sv.load(Rows<T>(v_, Ma, 0, L, C), 0, Ma);
         for (int c = 0; c < n; ++c) {
-            T *Ks = lds + (c & 1) * BUF, *Vs = Ks + C * RE;
+            lds_t<T> *Ks = lds + (c & 1) * BUF, *Vs = Ks + C * RE;
             sk.template store<PHI>(Ks, c * C, L, Ea);
             sv.store(Vs);
             __syncthreads();
@@ -250,7 +250,7 @@ __device__ __forceinline__ void bwd_sweep(const T *q_, const T *k_, const T *v_,
         for (int s = 0; s < NPF; ++s) {
             const int step = sb + s;
             const int row0 = (n - 1 - step) * C;
-            T *Qs = lds + (step & 1) * BUF, *Ks = Qs + C * RE, *Vs = Ks + C * RE, *Gs = Vs + C * RM;
+            lds_t<T> *Qs = lds + (step & 1) * BUF, *Ks = Qs + C * RE, *Vs = Ks + C * RE, *Gs = Vs + C * RM;
             float *dds = ddbuf + (step & 1) * C;  // NORM: dd_i of row row0 + i
             stg[s].q.template store<PHI>(Qs, row0, L, Ea);
             stg[s].k.template store<PHI>(Ks, row0, L, Ea);
@@ -340,7 +340,7 @@ __device__ __forceinline__ void bwd_sweep(const T *q_, const T *k_, const T *v_,
                         if constexpr (PHI) {  // through phi: phi'(x) = min(phi(x), 1)
                             const F ph = lds_nat<T>(Qs, RE, I, bk(x));
 #pragma unroll
-                            for (int t = 0; t < 4; ++t) d[t] *= fminf((float)ph[t], 1.f);
+                            for (int t = 0; t < 4; ++t) d[t] *= fminf(frag_val<T>(ph, t), 1.f);
                         }
                         pend[x][I] = d;
                     }
@@ -394,7 +394,7 @@ __device__ __forceinline__ void bwd_sweep(const T *q_, const T *k_, const T *v_,
                         if constexpr (PHI) {
                             const F ph = lds_nat<T>(Ks, RE, J, bk(x));
 #pragma unroll
-                            for (int t = 0; t < 4; ++t) d[t] *= fminf((float)ph[t], 1.f);
+                            for (int t = 0; t < 4; ++t) d[t] *= fminf(frag_val<T>(ph, t), 1.f);
                         }
                         pend[x][J] = d;
                     }
@@ -514,7 +514,7 @@ __device__ __forceinline__ void bwd_sweep(const T *q_, const T *k_, const T *v_,
 template <typename T, int E, int M, int C, int G, int NB, int IDLE, int RG, int RGI, int NPF, bool NORM, bool FMAP>
 __device__ __forceinline__ void bwd_role(int role, int b, const T *q_, const T *k_, const T *v_, const T *g_,
                                          const float *s0, const float *st, const float *zc_, const float *dd_,
-                                         int Lpad, T *dq_, T *dk_, T *dv_, float *ds0, float *dz0, int L, T *lds,
+                                         int Lpad, T *dq_, T *dk_, T *dv_, float *ds0, float *dz0, int L, lds_t<T> *lds,
                                          int Ea, int Ma) {
     constexpr int EB = E / 16, MB = M / 16;
     if (role == kDQ && b < EB)
@@ -551,8 +551,8 @@ __global__ __launch_bounds__((64 * bwd_waves<E, M, G, NB, IDLE>())) void cp_bwd_
     static_assert(NT <= 1024, "at most 16 waves per workgroup");
     constexpr int RE = Stage<T, NT, C, E>::RS, RM = Stage<T, NT, C, M>::RS;
     constexpr int BUF = 2 * C * RE + 2 * C * RM;
-    constexpr int DDE = NORM ? 2 * C * 4 / (int)sizeof(T) : 0;  // two dd buffers of C floats
-    __shared__ __attribute__((aligned(16))) T lds[2 * BUF + DDE];
+    constexpr int DDE = NORM ? 2 * C * 4 / (int)sizeof(lds_t<T>) : 0;  // two dd buffers of C floats
+    __shared__ __attribute__((aligned(16))) lds_t<T> lds[2 * BUF + DDE];
 
     static_assert(RG >= 1 && RG <= 2 && RG <= C / 16, "row groups");
     int slice, part;

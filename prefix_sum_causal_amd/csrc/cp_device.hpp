@@ -139,82 +139,84 @@ template <typename H> struct Ops16 {
 template <> struct Ops<bf16> : Ops16<bf16> {};
 template <> struct Ops<f16> : Ops16<f16> {};
 
-// fp32 I/O: fragments are 4 floats.  Products run as split bf16 by default
-// (CP_F32_SPLIT): each fp32 operand x is cut into hi = bf16(x) and
-// lo = bf16(x - hi), 16 significant bits together, and a product keeps
-// hi*hi + hi*lo + lo*hi (the dropped lo*lo term is below 2^-16 of it), three
-// bf16 MFMAs of 16x16x32 with fp32 accumulation instead of eight fp32 MFMAs of
-// 16x16x4 -- gfx950's fp32 matrix rate is a sixteenth of its bf16 rate.
-// Values with at most 16 significant bits (small integers among them) are
-// split exactly, so their products are exact.  With CP_F32_SPLIT=0 the fp32
-// MFMA is used: a k-block is then four MFMAs (t = 0..3 pairs k = 4g + t on
-// both operands).
-#ifndef CP_F32_SPLIT
-#define CP_F32_SPLIT 1
-#endif
-template <> struct Ops<float> {
-    using frag = f32x4;
-
-    __device__ static __forceinline__ frag zero() { return zero4(); }
-    __device__ static __forceinline__ frag ones() {
-        f32x4 o = {1.f, 1.f, 1.f, 1.f};
-        return o;
-    }
-    // two k-blocks of fp32 as hi and lo bf16 operands (8 values per lane)
-    __device__ static __forceinline__ void split8(frag x0, frag x1, bf16x8 &hi, bf16x8 &lo) {
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const bf16 h0 = (bf16)x0[t], h1 = (bf16)x1[t];
-            hi[t] = h0;
-            hi[4 + t] = h1;
-            lo[t] = (bf16)(x0[t] - (float)h0);
-            lo[4 + t] = (bf16)(x1[t] - (float)h1);
-        }
-    }
-    __device__ static __forceinline__ void mma2(f32x4 &acc, frag a0, frag a1, frag b0, frag b1) {
-        if constexpr (CP_F32_SPLIT != 0) {
-            bf16x8 ah, al, bh, bl;
-            split8(a0, a1, ah, al);
-            split8(b0, b1, bh, bl);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc, 0, 0, 0);
-        } else {
-#pragma unroll
-            for (int t = 0; t < 4; ++t) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a0[t], b0[t], acc, 0, 0, 0);
-#pragma unroll
-            for (int t = 0; t < 4; ++t) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a1[t], b1[t], acc, 0, 0, 0);
-        }
-    }
-    __device__ static __forceinline__ void mma1(f32x4 &acc, frag a, frag b) {
-        if constexpr (CP_F32_SPLIT != 0) {
-            mma2(acc, a, zero(), b, zero());
-        } else {
-#pragma unroll
-            for (int t = 0; t < 4; ++t) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[t], b[t], acc, 0, 0, 0);
-        }
-    }
-    __device__ static __forceinline__ frag cvt(f32x4 x) { return x; }
-    __device__ static __forceinline__ void split(f32x4 x, frag &hi, frag &lo) {
-        hi = x;
-        lo = zero4();
-    }
-    __device__ static __forceinline__ frag neg(frag a) { return -a; }
-    __device__ static __forceinline__ frag tr_frag(const float *lds, int rs, int tb, int cb) {
-        const int g = lane_g(), r = lane_r();
-        f32x4 v;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) v[t] = lds[(16 * tb + 4 * g + t) * rs + 16 * cb + r];
-        return v;
-    }
+// fp32 I/O: products run as split bf16.  Each fp32 operand x is cut into
+// hi = bf16(x) and lo = bf16(x - hi), 16 significant bits together, and a
+// product keeps hi*hi + hi*lo + lo*hi (the dropped lo*lo term is below 2^-16
+// of it): three bf16 MFMAs of 16x16x32 with fp32 accumulation instead of
+// eight fp32 MFMAs of 16x16x4 -- gfx950's fp32 matrix rate is a sixteenth of
+// its bf16 rate.  Values with at most 16 significant bits (small integers
+// among them) are split exactly, so their products are exact.
+//
+// The inputs are split once, while a chunk is staged: the LDS copy of an
+// fp32 row of W values is a row of 2W bf16, the W hi values then the W lo
+// values (lds_t<float> = bf16), so that every read of an operand is a bf16
+// read of each half and no wave splits what it reads.  A fragment is the pair
+// of bf16 fragments; accumulator tiles fed back as operands are split when
+// converted (cvt).
+struct F32S {
+    bf16x4 h, l;
 };
+
+// Offset (elements) of the lo half of an fp32 LDS row of stride rs: rows of
+// W >= 16 values are 2W bf16 plus a 16-element pad (lds_stride).
+__device__ __forceinline__ int lo_half(int rs) { return (rs - 16) >> 1; }
+
+template <> struct Ops<float> {
+    using frag = F32S;
+    using B = Ops16<bf16>;
+
+    __device__ static __forceinline__ frag zero() { return {B::zero(), B::zero()}; }
+    __device__ static __forceinline__ frag ones() { return {B::ones(), B::zero()}; }
+    __device__ static __forceinline__ void mma2(f32x4 &acc, frag a0, frag a1, frag b0, frag b1) {
+        B::mma2(acc, a0.l, a1.l, b0.h, b1.h);
+        B::mma2(acc, a0.h, a1.h, b0.l, b1.l);
+        B::mma2(acc, a0.h, a1.h, b0.h, b1.h);
+    }
+    __device__ static __forceinline__ void mma1(f32x4 &acc, frag a, frag b) { mma2(acc, a, zero(), b, zero()); }
+    __device__ static __forceinline__ frag cvt(f32x4 x) {
+        frag f;
+        B::split(x, f.h, f.l);
+        return f;
+    }
+    // (fp32 states enter the products as one split operand)
+    __device__ static __forceinline__ void split(f32x4 x, frag &hi, frag &lo) {
+        hi = cvt(x);
+        lo = zero();
+    }
+    __device__ static __forceinline__ frag neg(frag a) { return {B::neg(a.h), B::neg(a.l)}; }
+    __device__ static __forceinline__ frag tr_frag(const bf16 *lds, int rs, int tb, int cb) {
+        return {B::tr_frag(lds, rs, tb, cb), B::tr_frag(lds + lo_half(rs), rs, tb, cb)};
+    }
+    // value t of a fragment
+    __device__ static __forceinline__ float val(frag a, int t) { return (float)a.h[t] + (float)a.l[t]; }
+};
+
+// The element type of the LDS copies of a chunk (see Ops<float>).
+template <typename T> struct LdsOf {
+    using type = T;
+};
+template <> struct LdsOf<float> {
+    using type = bf16;
+};
+template <typename T> using lds_t = typename LdsOf<T>::type;
+
+// value t of a 16-bit fragment
+template <typename T>
+__device__ __forceinline__ float frag_val(typename Ops<T>::frag a, int t) {
+    if constexpr (std::is_same<T, float>::value) return Ops<float>::val(a, t);
+    else return (float)a[t];
+}
 
 // lane (g, r) <- X[16 rb + r][16 cb + 4g + t] from a natural LDS copy with
 // row stride rs (elements).
 template <typename T>
-__device__ __forceinline__ typename Ops<T>::frag lds_nat(const T *lds, int rs, int rb, int cb) {
-    return *reinterpret_cast<const typename Ops<T>::frag *>(lds + (16 * rb + lane_r()) * rs + 16 * cb +
-                                                             4 * lane_g());
+__device__ __forceinline__ typename Ops<T>::frag lds_nat(const lds_t<T> *lds, int rs, int rb, int cb) {
+    const lds_t<T> *p = lds + (16 * rb + lane_r()) * rs + 16 * cb + 4 * lane_g();
+    if constexpr (std::is_same<T, float>::value) {
+        return {*reinterpret_cast<const bf16x4 *>(p), *reinterpret_cast<const bf16x4 *>(p + lo_half(rs))};
+    } else {
+        return *reinterpret_cast<const typename Ops<T>::frag *>(p);
+    }
 }
 
 // acc += sum over k-blocks b in [b0, b1) of A_b * B_b.  For bf16 the blocks
@@ -290,21 +292,19 @@ __device__ __forceinline__ void st_out(const Rows<T> &X, int rb, int cb, f32x4 v
     }
 }
 
-// Row stride (elements) of the LDS copy of a W-column chunk, a multiple of
-// 16 bytes so that every row starts 16-byte aligned.  Measured on gfx950
-// (16 rows read as 16-byte pieces at one column, and 4 x 4 rows read as
-// 8-byte pieces by the transposing read): strides of 32 bytes modulo 64 run
-// both at full rate (about 250 and 225 bytes per clock per CU), strides of
-// 16 or 48 bytes modulo 64 at half of it and multiples of 64 bytes at a
-// quarter or less.  16-bit rows are therefore padded to 32 modulo 64 bytes.
-// fp32 rows keep a 16-byte pad: their transposed fragments are 4-byte reads
-// of four rows 4 apart, which a 32-modulo-64 stride would put on the same
-// banks.
+// Row stride (16-bit elements) of the LDS copy of a W-column chunk, a
+// multiple of 16 bytes so that every row starts 16-byte aligned.  Measured on
+// gfx950 (16 rows read as 16-byte pieces at one column, and 4 x 4 rows read
+// as 8-byte pieces by the transposing read): strides of 32 bytes modulo 64
+// run both at full rate (about 250 and 225 bytes per clock per CU), strides
+// of 16 or 48 bytes modulo 64 at half of it and multiples of 64 bytes at a
+// quarter or less.  Rows are therefore padded to 32 modulo 64 bytes (fp32
+// rows, stored as their bf16 hi and lo halves, by 32 bytes: lo_half relies
+// on it).
 template <typename T, int W>
 constexpr int lds_stride() {
-    constexpr int bytes = W * (int)sizeof(T);
-    if constexpr (sizeof(T) == 2) return (bytes + (96 - bytes % 64) % 64) / 2;
-    return W + 16 / (int)sizeof(T);
+    constexpr int bytes = W * (int)sizeof(T);  // a row of 16-bit values, or the hi + lo halves of fp32 ones
+    return (bytes + (96 - bytes % 64) % 64) / 2;
 }
 
 typedef int i32x4 __attribute__((__vector_size__(4 * sizeof(int))));
@@ -324,6 +324,7 @@ struct Stage {
     static constexpr int NP = (P + NT - 1) / NT;
     static constexpr int RS = lds_stride<T, W>();
     static_assert(W * (int)sizeof(T) % 16 == 0, "rows must be whole 16-byte pieces");
+    static_assert(sizeof(T) == 2 || W % 16 == 0, "fp32 rows of whole 16-value blocks (lo_half)");
     i32x4 v[NP];
 
     static constexpr int VEC = 16 / (int)sizeof(T);  // elements per piece
@@ -341,7 +342,7 @@ struct Stage {
     }
 
     template <bool PHI = false>
-    __device__ __forceinline__ void store(T *lds, int row0 = 0, int L = 0, int wa = W) const {
+    __device__ __forceinline__ void store(lds_t<T> *lds, int row0 = 0, int L = 0, int wa = W) const {
 #pragma unroll
         for (int i = 0; i < NP; ++i) {
             const int p = (int)threadIdx.x + i * NT;
@@ -360,7 +361,15 @@ struct Stage {
                 for (int j = 0; j < n; ++j) e[j] = (T)(phi((float)e[j]) * keep);
                 x = __builtin_bit_cast(i32x4, e);
             }
-            *reinterpret_cast<i32x4 *>(lds + row * RS + cp * (16 / (int)sizeof(T))) = x;
+            if constexpr (std::is_same<T, float>::value) {
+                // the hi and lo halves of the four values
+                F32S f = Ops<float>::cvt(__builtin_bit_cast(f32x4, x));
+                bf16 *dst = lds + row * RS + cp * 4;
+                *reinterpret_cast<bf16x4 *>(dst) = f.h;
+                *reinterpret_cast<bf16x4 *>(dst + W) = f.l;
+            } else {
+                *reinterpret_cast<i32x4 *>(lds + row * RS + cp * (16 / (int)sizeof(T))) = x;
+            }
         }
     }
 };
@@ -414,6 +423,12 @@ template <typename H, int E> struct EOps16 {
     using rf = typename std::conditional<WIDE, typename Half16<H>::x8, x4>::type;
 
     __device__ static __forceinline__ int ecol(int eb) { return WIDE ? 32 * (eb >> 1) + 4 * (eb & 1) : 16 * eb; }
+    __device__ static __forceinline__ rf zero_rf() {
+        rf z;
+#pragma unroll
+        for (int i = 0; i < (int)(sizeof(rf) / sizeof(H)); ++i) z[i] = (H)0.f;
+        return z;
+    }
     // lane (g, r) <- X[16 rb + r][features of step s]
     __device__ static __forceinline__ rf load(const H *lds, int rs, int rb, int s) {
         const H *p = lds + (16 * rb + lane_r()) * rs + (WIDE ? 32 * s : 0) + estride * lane_g();
@@ -459,37 +474,40 @@ template <typename H, int E> struct EOps16 {
 template <int E> struct EOps<bf16, E> : EOps16<bf16, E> {};
 template <int E> struct EOps<f16, E> : EOps16<f16, E> {};
 
+// fp32: the same feature order as the 16-bit operands, each a hi + lo pair.
 template <int E> struct EOps<float, E> {
-    static constexpr int EB = E / 16;
-    static constexpr int STEPS = (EB + 1) / 2;  // two k-blocks per step
-    static constexpr int estride = 4;
+    using B = EOps16<bf16, E>;
+    static constexpr int EB = B::EB;
+    static constexpr bool WIDE = B::WIDE;
+    static constexpr int STEPS = B::STEPS;
+    static constexpr int estride = B::estride;
+    // fp32 states enter the products as one split operand
+    static constexpr bool SPLIT_STATE = false;
     struct rf {
-        f32x4 a, b;
+        typename B::rf h, l;
     };
 
-    __device__ static __forceinline__ int ecol(int eb) { return 16 * eb; }
-    __device__ static __forceinline__ rf load(const float *lds, int rs, int rb, int s) {
-        rf x;
-        x.a = lds_nat<float>(lds, rs, rb, 2 * s);
-        x.b = 2 * s + 1 < EB ? lds_nat<float>(lds, rs, rb, 2 * s + 1) : zero4();
-        return x;
+    __device__ static __forceinline__ int ecol(int eb) { return B::ecol(eb); }
+    __device__ static __forceinline__ rf load(const bf16 *lds, int rs, int rb, int s) {
+        return {B::load(lds, rs, rb, s), B::load(lds + lo_half(rs), rs, rb, s)};
     }
-    __device__ static __forceinline__ void mma(f32x4 &acc, rf x, rf y) { Ops<float>::mma2(acc, x.a, x.b, y.a, y.b); }
+    __device__ static __forceinline__ void mma(f32x4 &acc, rf x, rf y) {
+        B::mma(acc, x.l, y.h);
+        B::mma(acc, x.h, y.l);
+        B::mma(acc, x.h, y.h);
+    }
     __device__ static __forceinline__ rf state(const f32x4 *tiles, int s) {
         rf x;
-        x.a = tiles[2 * s];
-        x.b = 2 * s + 1 < EB ? tiles[2 * s + 1] : zero4();
+        B::state_split(tiles, s, x.h, x.l);
         return x;
     }
-    // fp32 states need no hi/lo pair of operands (the product splits them)
-    static constexpr bool SPLIT_STATE = false;
     __device__ static __forceinline__ void state_split(const f32x4 *tiles, int s, rf &hi, rf &lo) {
         hi = state(tiles, s);
-        lo.a = zero4();
-        lo.b = zero4();
+        lo.h = B::zero_rf();
+        lo.l = B::zero_rf();
     }
-    __device__ static __forceinline__ f32x4 tr_e(const float *lds, int rs, int tb, int eb) {
-        return Ops<float>::tr_frag(lds, rs, tb, eb);
+    __device__ static __forceinline__ F32S tr_e(const bf16 *lds, int rs, int tb, int eb) {
+        return {B::tr_e(lds, rs, tb, eb), B::tr_e(lds + lo_half(rs), rs, tb, eb)};
     }
 };
 

@@ -59,7 +59,7 @@ namespace cp {
 template <typename T, int E, int M, int C, int NW, int RSPLIT, int RS, int NPF, bool NORM, bool FMAP, bool DW,
           bool DEN, int H>
 __device__ __forceinline__ void fwd_sweep(const T *q_, const T *k_, const T *v_, T *o_, float *den_, int rb,
-                                          int re, int grp, int cb, float eps, T *lds, f32x4 (&S)[E / 16],
+                                          int re, int grp, int cb, float eps, lds_t<T> *lds, f32x4 (&S)[E / 16],
                                           f32x4 (&z)[E / 16], int Ea, int Ma) {
     using O = Ops<T>;
     using F = typename O::frag;
@@ -125,7 +125,7 @@ __device__ __forceinline__ void fwd_sweep(const T *q_, const T *k_, const T *v_,
         for (int s = 0; s < NPF; ++s) {
             const int c = c0 + s;
             const int row0 = rb + c * C;
-            T *Qs = lds + (c & 1) * BUF, *Ks = Qs + C * RQ, *Vs = Ks + C * RQ;
+            lds_t<T> *Qs = lds + (c & 1) * BUF, *Ks = Qs + C * RQ, *Vs = Ks + C * RQ;
             st[s].q.template store<NORM && FMAP>(Qs, row0, re, Ea);
             st[s].k.template store<NORM && FMAP>(Ks, row0, re, Ea);
             st[s].v.store(Vs);
@@ -311,7 +311,7 @@ __global__ __launch_bounds__(64 * NW) void cp_seg_state_kernel(const T *__restri
     constexpr int WS = E * M + E;
     // dz tiles (e-tiles of K^T 1) dealt round robin to the waves
     constexpr int ZT = (EB + NW - 1) / NW;
-    __shared__ __attribute__((aligned(16))) T lds[2 * BUF];
+    __shared__ __attribute__((aligned(16))) lds_t<T> lds[2 * BUF];
 
     const int nseg = (L + seg_len - 1) / seg_len;
     int slice, seg;
@@ -348,7 +348,7 @@ __global__ __launch_bounds__(64 * NW) void cp_seg_state_kernel(const T *__restri
         for (int i = 0; i < NPF; ++i) {
             const int c = c0 + i;
             const int row0 = rb + c * C;
-            T *Ks = lds + (c & 1) * BUF, *Vs = Ks + C * RK;
+            lds_t<T> *Ks = lds + (c & 1) * BUF, *Vs = Ks + C * RK;
             st[i].k.template store<NORM && FMAP>(Ks, row0, re, Ea);
             st[i].v.store(Vs);
             __syncthreads();
@@ -432,9 +432,9 @@ __global__ __launch_bounds__((64 * fwd_waves<M, G, RSPLIT, NORM && DW>())) void 
     constexpr int NW = MB / G, NT = 64 * (NW * RSPLIT + (DWAVE ? 1 : 0)), MW = 16 * NW;
     constexpr int RQ = Stage<T, NT, C, E>::RS, RV = Stage<T, NT, C, MW>::RS;
     constexpr int BUF = 2 * C * RQ + C * RV;
-    constexpr int DENB = DWAVE ? 2 * C * 4 / (int)sizeof(T) : 0;  // two chunks of denominators
+    constexpr int DENB = DWAVE ? 2 * C * 4 / (int)sizeof(lds_t<T>) : 0;  // two chunks of denominators
     constexpr int WS = E * M + E;                                // floats per (slice, segment) in ws
-    __shared__ __attribute__((aligned(16))) T lds[2 * BUF + DENB];
+    __shared__ __attribute__((aligned(16))) lds_t<T> lds[2 * BUF + DENB];
 
     const int nseg = (L + seg_len - 1) / seg_len;
     int slice, part;
