@@ -194,6 +194,7 @@ def main() -> int:
     out = torch.empty_like(v)
     state = torch.empty((w.N, w.H, w.E, w.M), device="cuda", dtype=torch.float32)
     den = torch.empty((w.N, w.H, w.L), device="cuda", dtype=torch.float32)
+    zfin = torch.empty((w.N, w.H, w.E), device="cuda", dtype=torch.float32)
     if w.op.endswith("bwd"):
         g = dev["dO"]
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
@@ -203,7 +204,7 @@ def main() -> int:
         if w.op == "linattn":
             cp.linear_attn_fwd(q, k, v, 1e-6, 1, out=out)
         elif w.op == "linattn+bwd":
-            cp.linear_attn_fwd(q, k, v, 1e-6, 1, out=out, state_out=state, den_out=den)
+            cp.linear_attn_fwd(q, k, v, 1e-6, 1, out=out, state_out=state, z_out=zfin, den_out=den)
         else:
             cp.causal_product_fwd(q, k, v, out=out, state_out=state)
 
@@ -211,7 +212,7 @@ def main() -> int:
         if w.op == "fwd+bwd":
             cp.causal_product_bwd(q, k, v, g, state_final=state, dq=dq, dk=dk, dv=dv)
         else:
-            cp.linear_attn_bwd(q, k, v, out, g, den, 1, state_final=state, dq=dq, dk=dk, dv=dv)
+            cp.linear_attn_bwd(q, k, v, out, g, den, 1, state_final=state, z_final=zfin, dq=dq, dk=dk, dv=dv)
 
     calls = [fwd_call] + ([bwd_call] if w.op.endswith("bwd") else [])
     kinds = {"fwd+bwd": ["fwd", "bwd"], "fwd": ["fwd"], "linattn": ["linattn"],

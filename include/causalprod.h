@@ -39,8 +39,7 @@
  *    fill the GPU splits each sequence into segments and takes a scratch
  *    buffer of N*H*segments*(E*M + E) floats from the stream-ordered
  *    allocator (hipMallocAsync), freed on the same stream after its last
- *    use; linear_attn_bwd does the same for its per-row terms; no other call
- *    allocates device memory.
+ *    use; no other call allocates device memory.
  *  * stream is a hipStream_t (NULL = the default stream).  Calls only enqueue
  *    work: they never synchronise the host, and buffers must stay alive until
  *    the stream has run the work.  Calls are stateless, thread-safe and
@@ -176,22 +175,22 @@ int linear_attn_fwd(const void *Q, const void *K, const void *V, void *Out,
  * Out and den (fp32 [N][H][L]) are the forward's output and den_out, both
  * required.  state_in, z_in: the initial states the forward started from
  * (optional, NULL = zero); pass them whenever the forward had them, also
- * together with state_final.  state_final (optional): the forward's final
- * S, which spares a forward pre-pass; with bf16 I/O it then stands in for
- * state_in.  With fp32 I/O it is not read: the query gradient, which peaks
- * at the first rows, recovers the early states by a compensated backward sum
- * from a compensated pre-pass of its own (the forward's plain fp32 sum would
- * leave its rounding error in them).  The normaliser before every chunk is summed forward from z_in by
- * a small scan (recovering it from the final z by subtraction would lose
- * most of the bits of its early values).  dstate_in, dz_in (optional):
- * receive the gradients of the initial states.  The call takes a scratch
- * buffer of N*H*L*M elements (dn) and about 2*N*H*L floats (dd and the
- * chunk-wise z) from the stream-ordered allocator and frees it on the
- * stream.
+ * together with the final states.  state_final, z_final (optional, used only
+ * as a pair): the forward's final S and z (its state_out and z_out), which
+ * spare the query gradient a forward pre-pass over K and V; with bf16 I/O
+ * they then stand in for state_in and z_in, and the states before every
+ * chunk are recovered from them by subtracting the chunks' increments.  With
+ * fp32 I/O they are not read: the query gradient, which peaks at the first
+ * rows, recovers the early states by a compensated backward sum from a
+ * compensated pre-pass of its own (the forward's plain fp32 sums would leave
+ * their rounding error in them).  dn_i and dd_i are formed while dOut is
+ * staged (dn rounded to the I/O type, dd in fp32).  dstate_in, dz_in
+ * (optional): receive the gradients of the initial states.  One kernel, no
+ * scratch: the call allocates nothing.
  */
 int linear_attn_bwd(const void *Q, const void *K, const void *V, const void *Out, const void *dOut,
                     const float *den, const float *state_in, const float *z_in,
-                    const float *state_final,
+                    const float *state_final, const float *z_final,
                     void *dQ, void *dK, void *dV, float *dstate_in, float *dz_in,
                     int64_t N, int64_t H, int64_t L, int64_t E, int64_t M,
                     int feature_map, int dtype, void *stream);
@@ -203,7 +202,8 @@ const char *cp_status_string(int status);
  * normalised backward; 3.1: CP_F16 and head sizes between the tile sizes
  * (both additions: every 3.0 call behaves as before); 4.0: cp_timing_end
  * takes the capacity of the caller's buffer; 4.1: causal_product_fwd_noalloc
- * and CP_ERR_SCRATCH. */
+ * and CP_ERR_SCRATCH; 5.0: linear_attn_bwd takes z_final and allocates
+ * nothing. */
 int cp_abi_version(void);
 
 /*

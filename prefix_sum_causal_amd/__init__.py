@@ -15,8 +15,8 @@ Functions with the ABI's names (optional tensors and outputs are keyword-only):
     linear_attn_fwd(q, k, v, eps=1e-6, feature_map=1, *, out=None, state_in=None,
                     z_in=None, state_out=None, z_out=None, den_out=None)
     linear_attn_bwd(q, k, v, out, dout, den, feature_map=1, *, state_in=None,
-                    z_in=None, state_final=None, dq=None, dk=None, dv=None,
-                    dstate_in=None, dz_in=None)
+                    z_in=None, state_final=None, z_final=None, dq=None,
+                    dk=None, dv=None, dstate_in=None, dz_in=None)
 and autograd wrappers ``causal_product(q, k, v, state0=None)`` and
 ``linear_attention(q, k, v, eps=1e-6, feature_map="elu+1")``.
 
@@ -57,7 +57,7 @@ lib.causal_product_fwd_noalloc.restype = _int
 lib.causal_product_bwd.argtypes = [_vp] * 10 + [_i64] * 5 + [_int, _vp]
 lib.causal_product_bwd.restype = _int
 lib.linear_attn_fwd.argtypes = [_vp] * 9 + [_i64] * 5 + [ctypes.c_float, _int, _int, _vp]
-lib.linear_attn_bwd.argtypes = [_vp] * 14 + [_i64] * 5 + [_int, _int, _vp]
+lib.linear_attn_bwd.argtypes = [_vp] * 15 + [_i64] * 5 + [_int, _int, _vp]
 lib.linear_attn_bwd.restype = _int
 lib.linear_attn_fwd.restype = _int
 lib.cp_status_string.argtypes = [_int]
@@ -229,13 +229,14 @@ def linear_attn_fwd(q, k, v, eps: float = 1e-6, feature_map: int = 1, *, out=Non
 
 
 def linear_attn_bwd(q, k, v, out, dout, den, feature_map: int = 1, *, state_in=None, z_in=None, state_final=None,
-                    dq=None, dk=None, dv=None, dstate_in=None, dz_in=None):
+                    z_final=None, dq=None, dk=None, dv=None, dstate_in=None, dz_in=None):
     """Gradients (dq, dk, dv) of sum(out * dout) for out = linear_attn_fwd(q, k, v, ...),
     with respect to the raw q, k (through phi), v; ``den`` is the forward's
     den_out.  state_in / z_in: the initial states the forward started from
-    (pass them whenever it had them); state_final: the forward's final state,
-    an optional shortcut (read for bf16 only); dstate_in [N,H,E,M] and dz_in
-    [N,H,E] receive the gradients of the initial states."""
+    (pass them whenever it had them); state_final, z_final: the forward's
+    final S and z (its state_out and z_out), an optional shortcut taken as a
+    pair (read for bf16 only); dstate_in [N,H,E,M] and dz_in [N,H,E] receive
+    the gradients of the initial states."""
     N, H, L, E, M = _dims(q, v)
     if k.shape != q.shape or dout.shape != v.shape or out.shape != v.shape:
         raise ValueError("k must have q's shape, out and dout v's shape")
@@ -244,14 +245,14 @@ def linear_attn_bwd(q, k, v, out, dout, den, feature_map: int = 1, *, state_in=N
     dv = torch.empty_like(v) if dv is None else dv
     _check_tensors(q, k, v, out, dout, dq, dk, dv)
     for name, t, shape in (("den", den, (N, H, L)), ("state_in", state_in, (N, H, E, M)), ("z_in", z_in, (N, H, E)),
-                           ("state_final", state_final, (N, H, E, M)), ("dstate_in", dstate_in, (N, H, E, M)),
-                           ("dz_in", dz_in, (N, H, E))):
+                           ("state_final", state_final, (N, H, E, M)), ("z_final", z_final, (N, H, E)),
+                           ("dstate_in", dstate_in, (N, H, E, M)), ("dz_in", dz_in, (N, H, E))):
         _check_state(name, t, shape, q.device)
     if den is None:
         raise ValueError("den (the forward's den_out) is required")
     _check("linear_attn_bwd", lib.linear_attn_bwd(
         _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(den), _ptr(state_in), _ptr(z_in), _ptr(state_final),
-        _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dstate_in), _ptr(dz_in), N, H, L, E, M, int(feature_map),
+        _ptr(z_final), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dstate_in), _ptr(dz_in), N, H, L, E, M, int(feature_map),
         _dtype_code(q), _stream(q.device)))
     return dq, dk, dv
 
@@ -288,23 +289,25 @@ def causal_product(q, k, v, state0=None):
 
 class LinearAttention(torch.autograd.Function):
     """Autograd wrapper of the normalised form: the forward keeps its output,
-    denominators and final state for the backward's single reverse sweep."""
+    denominators and final states for the backward's single reverse sweep."""
 
     @staticmethod
     def forward(ctx, q, k, v, eps, feature_map):
         q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
         N, H, L, E, M = _dims(q, v)
         st = torch.empty((N, H, E, M), device=q.device, dtype=torch.float32)
+        zf = torch.empty((N, H, E), device=q.device, dtype=torch.float32)
         den = torch.empty((N, H, L), device=q.device, dtype=torch.float32)
-        out = linear_attn_fwd(q, k, v, eps, feature_map, state_out=st, den_out=den)
-        ctx.save_for_backward(q, k, v, out, den, st)
+        out = linear_attn_fwd(q, k, v, eps, feature_map, state_out=st, z_out=zf, den_out=den)
+        ctx.save_for_backward(q, k, v, out, den, st, zf)
         ctx.feature_map = feature_map
         return out
 
     @staticmethod
     def backward(ctx, dout):
-        q, k, v, out, den, st = ctx.saved_tensors
-        dq, dk, dv = linear_attn_bwd(q, k, v, out, dout.contiguous(), den, ctx.feature_map, state_final=st)
+        q, k, v, out, den, st, zf = ctx.saved_tensors
+        dq, dk, dv = linear_attn_bwd(q, k, v, out, dout.contiguous(), den, ctx.feature_map, state_final=st,
+                                     z_final=zf)
         return dq, dk, dv, None, None
 
 

@@ -29,9 +29,10 @@ static __device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
 
 namespace {
 
-constexpr int kAbiMajor = 4, kAbiMinor = 1;  // 3.0: carried state, normalised backward; 3.1: fp16 I/O;
+constexpr int kAbiMajor = 5, kAbiMinor = 0;  // 3.0: carried state, normalised backward; 3.1: fp16 I/O;
                                              // 4.0: cp_timing_end bounded by the caller's buffer;
-                                             // 4.1: causal_product_fwd_noalloc
+                                             // 4.1: causal_product_fwd_noalloc;
+                                             // 5.0: linear_attn_bwd takes z_final, allocates nothing
 
 cp::fwd_fn pick_fwd(int dtype, int E, int M, bool norm) {
     return dtype == CP_BF16 ? cp::fwd_bf16(E, M, norm) : dtype == CP_F16 ? cp::fwd_f16(E, M, norm) : cp::fwd_f32(E, M, norm);
@@ -201,8 +202,8 @@ int causal_product_bwd(const void *Q, const void *K, const void *V, const void *
     if (st != CP_OK) return st;
     cp::bwd_fn fn = pick_bwd(dtype, (int)E, (int)M, false);
     if (!fn) return CP_ERR_UNSUPPORTED;
-    cp::BwdArgs a{Q,   K,    V,       dOut,    state_in, state_final, dQ, dK, dV, dstate_in, (int)L, (int)(N * H),
-                  nullptr, nullptr, nullptr, nullptr, 0, (int)E, (int)M};
+    cp::BwdArgs a{Q,       K,       V,       dOut,    state_in, state_final, dQ,     dK,    dV, dstate_in, (int)L,
+                  (int)(N * H), nullptr, nullptr, nullptr, nullptr, nullptr, 0, (int)E, (int)M};
     return launch_status(fn(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -221,15 +222,15 @@ int linear_attn_fwd(const void *Q, const void *K, const void *V, void *Out, cons
 
 int linear_attn_bwd(const void *Q, const void *K, const void *V, const void *Out, const void *dOut,
                     const float *den, const float *state_in, const float *z_in, const float *state_final,
-                    void *dQ, void *dK, void *dV, float *dstate_in, float *dz_in, int64_t N,
+                    const float *z_final, void *dQ, void *dK, void *dV, float *dstate_in, float *dz_in, int64_t N,
                     int64_t H, int64_t L, int64_t E, int64_t M, int feature_map, int dtype, void *stream) {
-    const int st = cp::validate_linattn_bwd(Q, K, V, Out, dOut, den, state_in, z_in, state_final, dQ, dK, dV,
-                                            dstate_in, dz_in, N, H, L, E, M, feature_map, dtype);
+    const int st = cp::validate_linattn_bwd(Q, K, V, Out, dOut, den, state_in, z_in, state_final, z_final, dQ, dK,
+                                            dV, dstate_in, dz_in, N, H, L, E, M, feature_map, dtype);
     if (st != CP_OK) return st;
     cp::bwd_fn fn = pick_bwd(dtype, (int)E, (int)M, true);
     if (!fn) return CP_ERR_UNSUPPORTED;
-    cp::BwdArgs a{Q, K,    V,       dOut,    state_in, state_final, dQ, dK, dV, dstate_in, (int)L, (int)(N * H),
-                  Out, den, z_in, dz_in, feature_map, (int)E, (int)M};
+    cp::BwdArgs a{Q,      K,      V,     dOut,  state_in, state_final, dQ,  dK, dV, dstate_in, (int)L, (int)(N * H),
+                  Out,    den,    z_in,  z_final, dz_in, feature_map, (int)E, (int)M};
     return launch_status(fn(a, static_cast<hipStream_t>(stream)));
 }
 

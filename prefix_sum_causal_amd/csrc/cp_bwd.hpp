@@ -51,6 +51,47 @@ __device__ __forceinline__ float state_at(const float *s, int e, int m, int Ea, 
     return e < Ea && m < Ma ? s[e * Ma + m] : 0.f;
 }
 
+// The normalised form's extra inputs of one slice: the forward's output and
+// denominators (the backward turns dO into dn = dO / den and dd = -(dO . out)
+// / den while staging it), the final normaliser z_{L-1} (optional) and the
+// initial one z_{-1} (optional).
+template <typename T> struct NormIn {
+    const T *o;
+    const float *den;
+    const float *zf, *z0;
+};
+
+// The dn rows of a staged dO chunk and their dd: the pieces of dO and of the
+// forward's output (same layout), and the denominators of the pieces' rows
+// (zero past the sequence).  The PPR lanes of a row (consecutive lanes of one
+// wave) reduce dO . out across the row; dd goes to dds[row], dn to the LDS
+// copy.
+template <typename T, typename SG>
+__device__ __forceinline__ void store_dn(const SG &g, const SG &o, const float (&den)[SG::NP], lds_t<T> *Gs,
+                                         float *dds) {
+    constexpr int VEC = 16 / (int)sizeof(T), PPR = SG::PPR, NT = SG::NT_;
+    static_assert(NT % PPR == 0 && 64 % PPR == 0, "a row's pieces lie in one wave");
+    typedef T tv __attribute__((__vector_size__(16)));
+    SG dn = g;
+#pragma unroll
+    for (int i = 0; i < SG::NP; ++i) {
+        const int p = (int)threadIdx.x + i * NT;
+        const tv gv = __builtin_bit_cast(tv, g.v[i]), ov = __builtin_bit_cast(tv, o.v[i]);
+        float acc = 0.f;
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) acc += (float)gv[j] * (float)ov[j];
+#pragma unroll
+        for (int x = PPR / 2; x >= 1; x >>= 1) acc += __shfl_xor(acc, x, PPR);
+        const float inv = den[i] != 0.f ? 1.f / den[i] : 0.f;
+        tv nv;
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) nv[j] = (T)((float)gv[j] * inv);
+        dn.v[i] = __builtin_bit_cast(i32x4, nv);
+        if (p % PPR == 0 && (SG::P % NT == 0 || p < SG::P)) dds[p / PPR] = -acc * inv;
+    }
+    dn.store(Gs);
+}
+
 // A k-contraction into NB accumulators that share one operand: acc(x) is the
 // x-th accumulator; fs(i) the shared operand (read once), fo(x, i) the x-th
 // own operand.  SHARED_A puts the shared operand on the A side.
@@ -88,8 +129,8 @@ __device__ __forceinline__ void dotk_shared(FACC acc, int b0, int b1, FS fs, FO 
 template <typename T, int E, int M, int C, int G, int NB, int IDLE, int RG, int RGI, int NPF, bool NORM, bool FMAP,
           int ROLE>
 __device__ __forceinline__ void bwd_sweep(const T *q_, const T *k_, const T *v_, const T *g_, const float *s0,
-                                          const float *st, const float *zc_, const float *dd_, int Lpad, T *out_,
-                                          float *ds0, float *dz0, int L, int b, lds_t<T> *lds, int Ea, int Ma) {
+                                          const float *st, NormIn<T> nin, T *out_, float *ds0, float *dz0, int L,
+                                          int b, lds_t<T> *lds, int Ea, int Ma) {
     using O = Ops<T>;
     using F = typename O::frag;
     using EE = EOps<T, E>;  // contraction over e
@@ -139,25 +180,43 @@ __device__ __forceinline__ void bwd_sweep(const T *q_, const T *k_, const T *v_,
     for (int x = 0; x < NX; ++x)
 #pragma unroll
         for (int e = 0; e < EB; ++e) X[x][e] = zero4();
-    // NORM: dQ holds zb[x][t] = z_{c-1}[16 bk(x) + 4g + t] (prefix of phi(k),
-    // read per chunk); dK carries zb[x][t] = r[16 bk(x) + 4g + t] (suffix of
-    // dd_i phi(q_i)); same in every lane r
-    f32x4 zb[NB];
+    // NORM: dQ carries zb[x][t] = z[16 bk(x) + 4g + t], from z_{L-1} down to
+    // z_{c-1} by subtracting each chunk's column sums of phi(K) (compensated,
+    // zlo, with EXACT_PREFIX); dK carries zb[x][t] = r[16 bk(x) + 4g + t]
+    // (suffix of dd_i phi(q_i)); same in every lane r
+    f32x4 zb[NB], zlo[NB];
 #pragma unroll
-    for (int x = 0; x < NB; ++x) zb[x] = zero4();
+    for (int x = 0; x < NB; ++x) zb[x] = zlo[x] = zero4();
+    // column sums of phi(K_c)[:, bk(x)] from the transposed K fragments
+    auto chunk_zsum = [&](const F (&kt)[NB][C / 16], f32x4 (&cs)[NB]) {
+#pragma unroll
+        for (int x = 0; x < NB; ++x) {
+            cs[x] = zero4();
+            dotk<T>(cs[x], 0, CB, [&](int J) { return kt[x][J]; }, [&](int) { return O::ones(); });
+        }
+    };
 
-    if (st && !EXACT_PREFIX) {
+    if (st && (!NORM || nin.zf) && !EXACT_PREFIX) {
         if constexpr (ROLE == kDQ) {
 #pragma unroll
-            for (int x = 0; x < NB; ++x)
+            for (int x = 0; x < NB; ++x) {
 #pragma unroll
                 for (int m = 0; m < MB; ++m)
 #pragma unroll
                     for (int t = 0; t < 4; ++t)
                         W[x][m][t] = state_at(st, 16 * bk(x) + r, EM::ecol(m) + EM::estride * g + t, Ea, Ma);
+                if constexpr (NORM) {
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        const int f = 16 * bk(x) + 4 * g + t;
+                        zb[x][t] = f < Ea ? nin.zf[f] : 0.f;
+                    }
+                }
+            }
         }
     } else {
-        // forward pre-pass: S_{L-1}^T[:, b] = S0^T[:, b] + sum over chunks of V^T K[:, b]
+        // forward pre-pass: S_{L-1}^T[:, b] = S0^T[:, b] + sum over chunks of
+        // V^T K[:, b] (NORM: and z_{L-1} = z_{-1} + the chunks' column sums)
         if constexpr (ROLE == kDQ) {
             if (s0) {
 #pragma unroll
@@ -167,6 +226,17 @@ __device__ __forceinline__ void bwd_sweep(const T *q_, const T *k_, const T *v_,
 #pragma unroll
                         for (int t = 0; t < 4; ++t)
                             W[x][m][t] = state_at(s0, 16 * bk(x) + r, EM::ecol(m) + EM::estride * g + t, Ea, Ma);
+            }
+            if constexpr (NORM) {
+                if (nin.z0) {
+#pragma unroll
+                    for (int x = 0; x < NB; ++x)
+#pragma unroll
+                        for (int t = 0; t < 4; ++t) {
+                            const int f = 16 * bk(x) + 4 * g + t;
+                            zb[x][t] = f < Ea ? nin.z0[f] : 0.f;
+                        }
+                }
             }
         }
         SE sk;
@@ -204,6 +274,15 @@ __device__ __forceinline__ void bwd_sweep(const T *q_, const T *k_, const T *v_,
                                                  [&](int x, int J) { return kt[x][J]; });
                     }
                 }
+                if constexpr (NORM) {
+                    f32x4 cs[NB];
+                    chunk_zsum(kt, cs);
+#pragma unroll
+                    for (int x = 0; x < NB; ++x) {
+                        if constexpr (COMP) two_sum_acc(zb[x], zlo[x], cs[x]);
+                        else zb[x] += cs[x];
+                    }
+                }
             }
         }
         __syncthreads();  // the main sweep reuses the buffers
@@ -214,34 +293,35 @@ __device__ __forceinline__ void bwd_sweep(const T *q_, const T *k_, const T *v_,
     // Ring of NPF register stages (NPF-1 chunks in flight while one is
     // computed); the step loop is padded to a multiple of NPF with chunks
     // before the start of the sequence, which load as zero and store nothing.
-    // NORM: dd of the chunk's rows, C floats as C/4 16-byte pieces (threads
-    // below C/4); dd_ is padded with zeros to Lpad rows, a multiple of C.
+    // NORM: also the forward's output rows and the denominators of the rows
+    // of each thread's dO pieces (zero past the sequence).
     struct Stages {
         SE q, k;
         SM v, g;
-        i32x4 dd;
-        __device__ __forceinline__ void load(const T *q_, const T *k_, const T *v_, const T *g_, const float *dd_,
-                                             int row0, int L, int Lpad, int Ea, int Ma) {
+        SM o;
+        float den[NORM ? SM::NP : 1];
+        __device__ __forceinline__ void load(const T *q_, const T *k_, const T *v_, const T *g_, NormIn<T> nin,
+                                             int row0, int L, int Ea, int Ma) {
             q.load(Rows<T>(q_, Ea, row0, L, C), 0, Ea);
             k.load(Rows<T>(k_, Ea, row0, L, C), 0, Ea);
             v.load(Rows<T>(v_, Ma, row0, L, C), 0, Ma);
             g.load(Rows<T>(g_, Ma, row0, L, C), 0, Ma);
             if constexpr (NORM) {
-                const Rows<float> rd(dd_, 1, row0, Lpad, C);
-                const int t = (int)threadIdx.x;
-                dd = __builtin_amdgcn_raw_buffer_load_b128(rd.rsrc, t < C / 4 ? 16 * t : 0x7FFFFFF0, 0, 0);
-            }
-        }
-        __device__ __forceinline__ void store_dd(float *dst) const {
-            if constexpr (NORM) {
-                if ((int)threadIdx.x < C / 4) *reinterpret_cast<i32x4 *>(dst + 4 * threadIdx.x) = dd;
+                o.load(Rows<T>(nin.o, Ma, row0, L, C), 0, Ma);
+                const Rows<float> rd(nin.den, 1, row0, L, C);
+#pragma unroll
+                for (int i = 0; i < SM::NP; ++i) {
+                    const int p = (int)threadIdx.x + i * NT;
+                    den[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                           rd.rsrc, p < SM::P ? 4 * (p / SM::PPR) : kVoid, 0, 0));
+                }
             }
         }
     };
     Stages stg[NPF];
 #pragma unroll
     for (int s = 0; s < NPF - 1; ++s) {
-        stg[s].load(q_, k_, v_, g_, dd_, (n - 1 - s) * C, L, Lpad, Ea, Ma);
+        stg[s].load(q_, k_, v_, g_, nin, (n - 1 - s) * C, L, Ea, Ma);
         __builtin_amdgcn_sched_barrier(0);  // stages complete in order
     }
     const int nsteps = (n + NPF - 1) / NPF * NPF;
@@ -255,10 +335,10 @@ __device__ __forceinline__ void bwd_sweep(const T *q_, const T *k_, const T *v_,
             stg[s].q.template store<PHI>(Qs, row0, L, Ea);
             stg[s].k.template store<PHI>(Ks, row0, L, Ea);
             stg[s].v.store(Vs);
-            stg[s].g.store(Gs);
-            stg[s].store_dd(dds);
+            if constexpr (NORM) store_dn<T>(stg[s].g, stg[s].o, stg[s].den, Gs, dds);
+            else stg[s].g.store(Gs);
             __syncthreads();
-            stg[(s + NPF - 1) % NPF].load(q_, k_, v_, g_, dd_, row0 - (NPF - 1) * C, L, Lpad, Ea, Ma);
+            stg[(s + NPF - 1) % NPF].load(q_, k_, v_, g_, nin, row0 - (NPF - 1) * C, L, Ea, Ma);
             __builtin_amdgcn_sched_barrier(0);
 
             f32x4 pend[NB][CB];  // this chunk's output tiles (rows 16 I + r) per column block
@@ -286,13 +366,14 @@ __device__ __forceinline__ void bwd_sweep(const T *q_, const T *k_, const T *v_,
                                                  [&](int x, int J) { return O::neg(kt[x][J]); });
                     }
                 }
-                if constexpr (NORM) {  // z_{c-1}, summed forward by the scan kernel (no cancellation)
-                    const int c = row0 / C;
+                if constexpr (NORM) {  // z_{c-1} = z_c - the chunk's column sums
+                    f32x4 cs[NB];
+                    chunk_zsum(kt, cs);
 #pragma unroll
-                    for (int x = 0; x < NB; ++x)
-#pragma unroll
-                        for (int t = 0; t < 4; ++t)
-                            zb[x][t] = c >= 0 ? zc_[(int64_t)c * E + 16 * bk(x) + 4 * g + t] : 0.f;
+                    for (int x = 0; x < NB; ++x) {
+                        if constexpr (COMP) two_sum_acc(zb[x], zlo[x], -cs[x]);
+                        else zb[x] -= cs[x];
+                    }
                 }
                 typename EM::rf wa[NB][EM::STEPS], vf[CB][EM::STEPS];
 #pragma unroll
@@ -334,7 +415,7 @@ __device__ __forceinline__ void bwd_sweep(const T *q_, const T *k_, const T *v_,
                         for (int k = 0; k < EM::STEPS; ++k) EM::mma(d, wa[x][k], gf[k]);
                         if constexpr (NORM) {
 #pragma unroll
-                            for (int t = 0; t < 4; ++t) d[t] += zb[x][t] * ddi;
+                            for (int t = 0; t < 4; ++t) d[t] += (zb[x][t] + zlo[x][t]) * ddi;
                         }
                         dotk<T>(d, 0, I + 1, [&](int J) { return kt[x][J]; }, [&](int J) { return pt[J]; });
                         if constexpr (PHI) {  // through phi: phi'(x) = min(phi(x), 1)
@@ -513,36 +594,35 @@ __device__ __forceinline__ void bwd_sweep(const T *q_, const T *k_, const T *v_,
 // The wave's role sweep for row group RGI.
 template <typename T, int E, int M, int C, int G, int NB, int IDLE, int RG, int RGI, int NPF, bool NORM, bool FMAP>
 __device__ __forceinline__ void bwd_role(int role, int b, const T *q_, const T *k_, const T *v_, const T *g_,
-                                         const float *s0, const float *st, const float *zc_, const float *dd_,
-                                         int Lpad, T *dq_, T *dk_, T *dv_, float *ds0, float *dz0, int L, lds_t<T> *lds,
-                                         int Ea, int Ma) {
+                                         const float *s0, const float *st, NormIn<T> nin, T *dq_, T *dk_, T *dv_,
+                                         float *ds0, float *dz0, int L, lds_t<T> *lds, int Ea, int Ma) {
     constexpr int EB = E / 16, MB = M / 16;
     if (role == kDQ && b < EB)
-        bwd_sweep<T, E, M, C, G, NB, IDLE, RG, RGI, NPF, NORM, FMAP, kDQ>(q_, k_, v_, g_, s0, st, zc_, dd_, Lpad,
-                                                                          dq_, nullptr, nullptr, L, b, lds, Ea, Ma);
+        bwd_sweep<T, E, M, C, G, NB, IDLE, RG, RGI, NPF, NORM, FMAP, kDQ>(q_, k_, v_, g_, s0, st, nin, dq_, nullptr,
+                                                                          nullptr, L, b, lds, Ea, Ma);
     else if (role == kDK && b < EB)
-        bwd_sweep<T, E, M, C, G, NB, IDLE, RG, RGI, NPF, NORM, FMAP, kDK>(q_, k_, v_, g_, s0, st, zc_, dd_, Lpad,
-                                                                          dk_, nullptr, dz0, L, b, lds, Ea, Ma);
+        bwd_sweep<T, E, M, C, G, NB, IDLE, RG, RGI, NPF, NORM, FMAP, kDK>(q_, k_, v_, g_, s0, st, nin, dk_, nullptr,
+                                                                          dz0, L, b, lds, Ea, Ma);
     else if (role == kDV && b < MB)
-        bwd_sweep<T, E, M, C, G, NB, IDLE, RG, RGI, NPF, NORM, FMAP, kDV>(q_, k_, v_, g_, s0, st, zc_, dd_, Lpad,
-                                                                          dv_, ds0, nullptr, L, b, lds, Ea, Ma);
+        bwd_sweep<T, E, M, C, G, NB, IDLE, RG, RGI, NPF, NORM, FMAP, kDV>(q_, k_, v_, g_, s0, st, nin, dv_, ds0,
+                                                                          nullptr, L, b, lds, Ea, Ma);
     else
-        bwd_sweep<T, E, M, C, G, NB, IDLE, RG, RGI, NPF, NORM, FMAP, kIdle>(q_, k_, v_, g_, s0, st, zc_, dd_, Lpad,
-                                                                            nullptr, nullptr, nullptr, L, 0, lds, Ea,
-                                                                            Ma);
+        bwd_sweep<T, E, M, C, G, NB, IDLE, RG, RGI, NPF, NORM, FMAP, kIdle>(q_, k_, v_, g_, s0, st, nin, nullptr,
+                                                                            nullptr, nullptr, L, 0, lds, Ea, Ma);
 }
 
 // NORM (backward of the normalised form, see the launcher): Q, K are the raw
-// inputs (phi applied on load when FMAP), Gr is dn = dO / den, dd the padded
-// per-row dd = -(dO . out) / den, zc the normaliser z before every chunk
-// ([Lpad / C][E] per slice), dz_in the gradient of the initial z.
+// inputs (phi applied on load when FMAP), Gr is dO, O and den the forward's
+// output and denominators, z_final the normaliser after the last row
+// (optional: without it, or with fp32 I/O, the dQ waves sum it in their
+// pre-pass from z_in), dz_in the gradient of the initial z.
 template <typename T, int E, int M, int C, int G, int NB, int IDLE, int RG, int NPF, bool NORM, bool FMAP>
 __global__ __launch_bounds__((64 * bwd_waves<E, M, G, NB, IDLE>())) void cp_bwd_kernel(
     const T *__restrict__ Q, const T *__restrict__ K, const T *__restrict__ V, const T *__restrict__ Gr,
-    const float *__restrict__ state_in, const float *__restrict__ state_final, const float *__restrict__ zc,
-    const float *__restrict__ dd, int Lpad, T *__restrict__ dQ,
-    T *__restrict__ dK, T *__restrict__ dV, float *__restrict__ dstate_in, float *__restrict__ dz_in, int L,
-    int NS, int Ea, int Ma) {
+    const float *__restrict__ state_in, const float *__restrict__ state_final, const T *__restrict__ O,
+    const float *__restrict__ den, const float *__restrict__ z_in, const float *__restrict__ z_final,
+    T *__restrict__ dQ, T *__restrict__ dK, T *__restrict__ dV, float *__restrict__ dstate_in,
+    float *__restrict__ dz_in, int L, int NS, int Ea, int Ma) {
     constexpr int EB = E / 16, MB = M / 16;
     // with several blocks per wave every wave's blocks all exist
     static_assert(NB == 1 || (EB % (G * NB) == 0 && MB % (G * NB) == 0), "blocks per wave");
@@ -564,8 +644,13 @@ __global__ __launch_bounds__((64 * bwd_waves<E, M, G, NB, IDLE>())) void cp_bwd_
     const T *q_ = Q + oe, *k_ = K + oe, *v_ = V + om, *g_ = Gr + om;
     const float *s0 = state_in ? state_in + os : nullptr;
     const float *st = state_final ? state_final + os : nullptr;
-    const float *zc_ = zc ? zc + (int64_t)slice * (Lpad / C) * E : nullptr;
-    const float *dd_ = dd ? dd + (int64_t)slice * Lpad : nullptr;
+    NormIn<T> nin{nullptr, nullptr, nullptr, nullptr};
+    if constexpr (NORM) {
+        nin.o = O + om;
+        nin.den = den + (int64_t)slice * L;
+        nin.zf = z_final ? z_final + (int64_t)slice * Ea : nullptr;
+        nin.z0 = z_in ? z_in + (int64_t)slice * Ea : nullptr;
+    }
     float *ds0 = dstate_in ? dstate_in + os : nullptr;
     float *dz0 = dz_in ? dz_in + (int64_t)slice * Ea : nullptr;
     // wave w: role, and the first of its NB column blocks (b, b + G, ...)
@@ -573,12 +658,11 @@ __global__ __launch_bounds__((64 * bwd_waves<E, M, G, NB, IDLE>())) void cp_bwd_
     const int lw = role == kDQ ? w : role == kDK ? w - EG : w - 2 * EG;
     const int b = grp + G * NB * lw;
     if (rg == 0 || RG == 1)
-        bwd_role<T, E, M, C, G, NB, IDLE, RG, 0, NPF, NORM, FMAP>(role, b, q_, k_, v_, g_, s0, st, zc_, dd_, Lpad,
-                                                                 dQ + oe, dK + oe, dV + om, ds0, dz0, L, lds, Ea,
-                                                                 Ma);
+        bwd_role<T, E, M, C, G, NB, IDLE, RG, 0, NPF, NORM, FMAP>(role, b, q_, k_, v_, g_, s0, st, nin, dQ + oe,
+                                                                 dK + oe, dV + om, ds0, dz0, L, lds, Ea, Ma);
     else
         bwd_role<T, E, M, C, G, NB, IDLE, RG, (RG > 1 ? 1 : 0), NPF, NORM, FMAP>(
-            role, b, q_, k_, v_, g_, s0, st, zc_, dd_, Lpad, dQ + oe, dK + oe, dV + om, ds0, dz0, L, lds, Ea, Ma);
+            role, b, q_, k_, v_, g_, s0, st, nin, dQ + oe, dK + oe, dV + om, ds0, dz0, L, lds, Ea, Ma);
 }
 
 }  // namespace cp

@@ -319,6 +319,7 @@ typedef int i32x4 __attribute__((__vector_size__(4 * sizeof(int))));
 // zero).
 template <typename T, int NT, int C, int W>
 struct Stage {
+    static constexpr int NT_ = NT;
     static constexpr int PPR = W * (int)sizeof(T) / 16;  // pieces per row
     static constexpr int P = C * PPR;
     static constexpr int NP = (P + NT - 1) / NT;

@@ -43,7 +43,8 @@ struct BwdArgs {
     // backward of the normalised form only
     const void *Out;    // the forward's output
     const float *den;   // the forward's denominators [NS][L]
-    const float *z_in;  // optional initial z
+    const float *z_in;     // optional initial z
+    const float *z_final;  // optional z after the last row (with state_final)
     float *dz_in;
     int fmap;
     int Ea, Ma;  // head sizes of the tensors (the kernel runs the next tile size up)

@@ -143,21 +143,21 @@ inline int validate_linattn_fwd(const void *Q, const void *K, const void *V, con
 
 inline int validate_linattn_bwd(const void *Q, const void *K, const void *V, const void *Out, const void *dOut,
                                 const float *den, const float *state_in, const float *z_in, const float *state_final,
-                                const void *dQ, const void *dK, const void *dV, const float *dstate_in,
-                                const float *dz_in, int64_t N, int64_t H, int64_t L, int64_t E, int64_t M,
-                                int feature_map, int dtype) {
+                                const float *z_final, const void *dQ, const void *dK, const void *dV,
+                                const float *dstate_in, const float *dz_in, int64_t N, int64_t H, int64_t L, int64_t E,
+                                int64_t M, int feature_map, int dtype) {
     int64_t ne = 0, nm = 0;
     int st = check_dims(N, H, L, E, M, dtype, ne, nm);
     if (st != CP_OK) return st;
     if (feature_map != 0 && feature_map != 1) return CP_ERR_UNSUPPORTED;
     st = check_ptrs({Q, K, V, Out, dOut, den, dQ, dK, dV});
     if (st != CP_OK) return st;
-    st = check_opt_ptrs({state_in, z_in, state_final, dstate_in, dz_in});
+    st = check_opt_ptrs({state_in, z_in, state_final, z_final, dstate_in, dz_in});
     if (st != CP_OK) return st;
     const int64_t es = elem_bytes(dtype), ns = N * H * E * M * 4, nz = N * H * E * 4, nd = N * H * L * 4;
     return check_alias({span(Q, ne * es), span(K, ne * es), span(V, nm * es), span(Out, nm * es),
                         span(dOut, nm * es), span(den, nd), span(state_in, ns), span(z_in, nz),
-                        span(state_final, ns)},
+                        span(state_final, ns), span(z_final, nz)},
                        {span(dQ, ne * es), span(dK, ne * es), span(dV, nm * es), span(dstate_in, ns),
                         span(dz_in, nz)});
 }

@@ -31,8 +31,9 @@ int main() {
                                         dt), CP_OK, "bwd ok");
                     expect(validate_linattn_fwd(P(0), P(1), P(2), P(3), nullptr, nullptr, F(4), F(5), F(6), 2, 3, L,
                                                 E, M, 1e-6f, 1, dt), CP_OK, "linattn ok");
-                    expect(validate_linattn_bwd(P(0), P(1), P(2), P(3), P(4), F(5), nullptr, nullptr, F(6), P(7), P(8),
-                                                P(9), F(10), F(11), 2, 3, L, E, M, 0, dt), CP_OK, "linattn bwd ok");
+                    expect(validate_linattn_bwd(P(0), P(1), P(2), P(3), P(4), F(5), nullptr, nullptr, F(6), F(12), P(7),
+                                                P(8), P(9), F(10), F(11), 2, 3, L, E, M, 0, dt), CP_OK,
+                           "linattn bwd ok");
                 }
     // sizes
     const int64_t big = INT64_MAX;
@@ -74,10 +75,12 @@ int main() {
                                 1.f / 0.f, 1, CP_BF16), CP_ERR_UNSUPPORTED, "eps inf");
     expect(validate_linattn_fwd(P(0), P(1), P(2), P(3), nullptr, nullptr, nullptr, nullptr, nullptr, 2, 3, 100, 64, 64,
                                 1e-6f, 2, CP_BF16), CP_ERR_UNSUPPORTED, "feature map");
-    expect(validate_linattn_bwd(P(0), P(1), P(2), P(3), P(4), nullptr, nullptr, nullptr, nullptr, P(7), P(8), P(9),
-                                nullptr, nullptr, 2, 3, 100, 64, 64, 1, CP_BF16), CP_ERR_NULL, "den required");
-    expect(validate_linattn_bwd(P(0), P(1), P(2), P(3), P(4), F(5), nullptr, nullptr, nullptr, P(7), P(8), P(9),
-                                F(5), nullptr, 2, 3, 100, 64, 64, 1, CP_BF16), CP_ERR_ALIAS, "dS0 over den");
+    expect(validate_linattn_bwd(P(0), P(1), P(2), P(3), P(4), nullptr, nullptr, nullptr, nullptr, nullptr, P(7), P(8),
+                                P(9), nullptr, nullptr, 2, 3, 100, 64, 64, 1, CP_BF16), CP_ERR_NULL, "den required");
+    expect(validate_linattn_bwd(P(0), P(1), P(2), P(3), P(4), F(5), nullptr, nullptr, nullptr, nullptr, P(7), P(8),
+                                P(9), F(5), nullptr, 2, 3, 100, 64, 64, 1, CP_BF16), CP_ERR_ALIAS, "dS0 over den");
+    expect(validate_linattn_bwd(P(0), P(1), P(2), P(3), P(4), F(5), nullptr, nullptr, nullptr, F(11), P(7), P(8),
+                                P(9), nullptr, F(11), 2, 3, 100, 64, 64, 1, CP_BF16), CP_ERR_ALIAS, "dz0 over z_final");
     for (int64_t x = -3; x <= 200; ++x) {
         const int t = tile_index(x);
         const int want = x < 1 ? -1 : x <= 16 ? 0 : x <= 32 ? 1 : x <= 64 ? 2 : x <= 128 ? 3 : -1;

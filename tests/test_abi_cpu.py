@@ -26,7 +26,7 @@ def lib():
     lib.causal_product_fwd_noalloc.argtypes = [vp] * 6 + [i64] * 5 + [i, vp]
     lib.causal_product_bwd.argtypes = [vp] * 10 + [i64] * 5 + [i, vp]
     lib.linear_attn_fwd.argtypes = [vp] * 9 + [i64] * 5 + [ctypes.c_float, i, i, vp]
-    lib.linear_attn_bwd.argtypes = [vp] * 14 + [i64] * 5 + [i, i, vp]
+    lib.linear_attn_bwd.argtypes = [vp] * 15 + [i64] * 5 + [i, i, vp]
     lib.cp_status_string.restype = ctypes.c_char_p
     return lib
 
@@ -55,7 +55,7 @@ def test_status_strings_and_version(lib):
         assert msg and msg not in seen
         seen.add(msg)
     assert lib.cp_status_string(99).decode() == "unknown status"
-    assert lib.cp_abi_version() == (4 << 16) | 1
+    assert lib.cp_abi_version() == (5 << 16) | 0
 
 
 def test_timing_rejects_bad_arguments_before_any_device_call(lib):
@@ -90,9 +90,9 @@ def lin(lib, q=A[0], k=A[1], v=A[2], o=A[3], s0=None, z0=None, st=None, zt=None,
     return lib.linear_attn_fwd(q, k, v, o, s0, z0, st, zt, den, *shape, eps, fm, dtype, None)
 
 
-def linb(lib, q=A[0], k=A[1], v=A[2], o=A[3], g=A[4], den=A[5], s0=None, z0=None, st=None, dq=A[6], dk=A[7],
-         dv=A[8], ds0=None, dz0=None, shape=SHAPE, fm=1, dtype=1):
-    return lib.linear_attn_bwd(q, k, v, o, g, den, s0, z0, st, dq, dk, dv, ds0, dz0, *shape, fm, dtype, None)
+def linb(lib, q=A[0], k=A[1], v=A[2], o=A[3], g=A[4], den=A[5], s0=None, z0=None, st=None, zt=None, dq=A[6],
+         dk=A[7], dv=A[8], ds0=None, dz0=None, shape=SHAPE, fm=1, dtype=1):
+    return lib.linear_attn_bwd(q, k, v, o, g, den, s0, z0, st, zt, dq, dk, dv, ds0, dz0, *shape, fm, dtype, None)
 
 
 @pytest.mark.parametrize("which", range(4))
@@ -189,6 +189,8 @@ def test_linear_attn_bwd_validation(lib):
     assert linb(lib, dq=A[0]) == ALIAS            # dq overlaps q
     assert linb(lib, dv=A[5]) == ALIAS            # dv overlaps den
     assert linb(lib, ds0=A[9], s0=A[9]) == ALIAS  # gradient over its own state
+    assert linb(lib, zt=A[9] + 4) == ALIGN
+    assert linb(lib, dz0=A[9], zt=A[9]) == ALIAS  # gradient over the final z
     assert lin(lib, den=A[3]) == ALIAS            # den_out overlaps out
     assert lin(lib, den=A[5] + 4) == ALIGN
 

@@ -113,7 +113,8 @@ def test_padded_heads_linattn(cp, orc, dtype, E, M, fm):
         return  # no fp16 normalised backward
     ds0 = torch.empty((N, H, E, M), device="cuda")
     dz0 = torch.empty((N, H, E), device="cuda")
-    got = cp.linear_attn_bwd(q, k, v, out, g, den, fm, state_in=s0, z_in=z0, state_final=st, dstate_in=ds0,
+    got = cp.linear_attn_bwd(q, k, v, out, g, den, fm, state_in=s0, z_in=z0, state_final=st, z_final=zt,
+                             dstate_in=ds0,
                              dz_in=dz0)
     torch.cuda.synchronize()
     bref = orc.linattn_bwd(d["Q"], d["K"], d["V"], d["dO"], 1e-6, fm, S0=d["S0"], z0=d["z0"])

@@ -6,8 +6,8 @@ Same metric and bars as the other parity tests (max|gpu - ref| / max|ref| per
 tensor, 1e-4 for fp32 I/O, 2e-2 for bf16 I/O).  Raw Q, K are N(0,1), so both
 branches of phi = elu + 1 are used; shapes have ragged tails, E != M, a wide
 head and two slices over 1500 rows.  The backward runs from the forward's
-final states and, separately, from the initial states through its own
-forward pre-pass.
+final states (S and z) and, separately, from the initial states through its
+own forward pre-pass (also taken when only S is given).
 """
 import numpy as np
 import pytest
@@ -89,8 +89,9 @@ def test_linattn_bwd(cp, orc, dtype, fm, shape):
     q, k, v, out, st, zt, den, s0, z0 = forward(cp, d, dtype, fm)
     g = dev(d["dO"], dtype)
     ref = orc.linattn_bwd(d["Q"], d["K"], d["V"], d["dO"], 1e-6, fm, S0=d["S0"], z0=d["z0"])
-    for label, kw in (("final states", dict(state_final=st, state_in=s0, z_in=z0)),
-                      ("pre-pass", dict(state_in=s0, z_in=z0))):
+    for label, kw in (("final states", dict(state_final=st, z_final=zt, state_in=s0, z_in=z0)),
+                      ("pre-pass", dict(state_in=s0, z_in=z0)),
+                      ("S only", dict(state_final=st, state_in=s0, z_in=z0))):
         ds0 = torch.empty_like(st)
         dz0 = torch.empty_like(zt)
         got = cp.linear_attn_bwd(q, k, v, out, g, den, fm, dstate_in=ds0, dz_in=dz0, **kw)

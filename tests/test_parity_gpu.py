@@ -283,15 +283,16 @@ def test_workload_full_size(cp, orc, name):
     tol = TOL[w.dtype]
     if w.op.startswith("linattn"):
         st = torch.empty((w.N, w.H, w.E, w.M), device="cuda", dtype=torch.float32)
+        zt = torch.empty((w.N, w.H, w.E), device="cuda", dtype=torch.float32)
         den = torch.empty((w.N, w.H, w.L), device="cuda", dtype=torch.float32)
-        out = cp.linear_attn_fwd(q, k, v, 1e-6, 1, state_out=st, den_out=den)
+        out = cp.linear_attn_fwd(q, k, v, 1e-6, 1, state_out=st, z_out=zt, den_out=den)
         torch.cuda.synchronize()
         err = oracle.max_rel_err(host(out), orc.linattn(d["Q"], d["K"], d["V"], 1e-6, 1))
         say(f"  linattn err {err:.3e}")
         assert err <= tol
         if w.op == "linattn+bwd":
             g = dev(d["dO"], w.dtype)
-            got = cp.linear_attn_bwd(q, k, v, out, g, den, 1, state_final=st)
+            got = cp.linear_attn_bwd(q, k, v, out, g, den, 1, state_final=st, z_final=zt)
             torch.cuda.synchronize()
             ref = orc.linattn_bwd(d["Q"], d["K"], d["V"], d["dO"], 1e-6, 1)
             errs = [oracle.max_rel_err(host(a), b) for a, b in zip(got, ref)]
