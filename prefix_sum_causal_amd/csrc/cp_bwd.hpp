@@ -45,6 +45,13 @@ namespace cp {
 
 enum BwdRole { kDQ = 0, kDK = 1, kDV = 2, kIdle = 3 };
 
+// Rows covered by the normalised backward's restart pre-pass (16-bit I/O,
+// from the final states; see RESTART in bwd_sweep).
+#ifndef CP_RESTART_ROWS
+#define CP_RESTART_ROWS 512
+#endif
+constexpr int kRestartRows = CP_RESTART_ROWS;
+
 // Entry (e, m) of an fp32 [Ea][Ma] state; zero in the padding of a narrower
 // head (e >= Ea or m >= Ma).
 __device__ __forceinline__ float state_at(const float *s, int e, int m, int Ea, int Ma) {
@@ -196,27 +203,31 @@ __device__ __forceinline__ void bwd_sweep(const T *q_, const T *k_, const T *v_,
         }
     };
 
-    if (st && (!NORM || nin.zf) && !EXACT_PREFIX) {
-        if constexpr (ROLE == kDQ) {
-#pragma unroll
-            for (int x = 0; x < NB; ++x) {
-#pragma unroll
-                for (int m = 0; m < MB; ++m)
-#pragma unroll
-                    for (int t = 0; t < 4; ++t)
-                        W[x][m][t] = state_at(st, 16 * bk(x) + r, EM::ecol(m) + EM::estride * g + t, Ea, Ma);
-                if constexpr (NORM) {
-#pragma unroll
-                    for (int t = 0; t < 4; ++t) {
-                        const int f = 16 * bk(x) + 4 * g + t;
-                        zb[x][t] = f < Ea ? nin.zf[f] : 0.f;
-                    }
-                }
-            }
-        }
-    } else {
-        // forward pre-pass: S_{L-1}^T[:, b] = S0^T[:, b] + sum over chunks of
-        // V^T K[:, b] (NORM: and z_{L-1} = z_{-1} + the chunks' column sums)
+    // Where the dQ waves get the states before each chunk.  From the final
+    // states (state_final with, for the normalised form, z_final): by
+    // subtracting the chunks' increments.  Otherwise: from a forward pre-pass
+    // over the whole sequence, starting at S0 (z0).
+    //
+    // RESTART (normalised form, 16-bit I/O, from the final states): the
+    // subtraction leaves in every recovered state an absolute error of the
+    // order of the final state's rounding (its own and the forward's), and
+    // the first rows, whose denominators are smallest and whose dq is a near
+    // cancellation of S_i dn_i against dd_i z_i, magnify it most.  So the
+    // pre-pass also runs over the first npre chunks (about kRestartRows rows):
+    // the dQ waves park those exact-so-far states (S, z after chunk npre - 1)
+    // in LDS and take them back when the reverse sweep reaches that chunk,
+    // so the early rows never see the final state's rounding.
+    constexpr bool RESTART = NORM && !EXACT_PREFIX;
+    const bool from_final = st && (!NORM || nin.zf) && !EXACT_PREFIX;
+    constexpr int kPre = kRestartRows / C > 1 ? kRestartRows / C : 1;
+    const int npre = from_final ? (RESTART ? (n < kPre ? n : kPre) : 0) : n;
+    // the wave's parking slots: f32x4 per lane, MB state tiles then z, per block
+    f32x4 *const park =
+        RESTART && ROLE == kDQ ? reinterpret_cast<f32x4 *>(ddbuf + 2 * C) + (b / (G * NB)) * NB * (MB + 1) * 64
+                               : nullptr;
+    if (npre > 0) {
+        // forward pre-pass over chunks [0, npre): S^T[:, b] = S0^T[:, b] + the
+        // chunks' V^T K[:, b] (NORM: and z = z_{-1} + their column sums)
         if constexpr (ROLE == kDQ) {
             if (s0) {
 #pragma unroll
@@ -243,7 +254,7 @@ __device__ __forceinline__ void bwd_sweep(const T *q_, const T *k_, const T *v_,
         SM sv;
         sk.load(Rows<T>(k_, Ea, 0, L, C), 0, Ea);
         sv.load(Rows<T>(v_, Ma, 0, L, C), 0, Ma);
-        for (int c = 0; c < n; ++c) {
+        for (int c = 0; c < npre; ++c) {
             lds_t<T> *Ks = lds + (c & 1) * BUF, *Vs = Ks + C * RE;
             sk.template store<PHI>(Ks, c * C, L, Ea);
             sv.store(Vs);
@@ -286,6 +297,30 @@ __device__ __forceinline__ void bwd_sweep(const T *q_, const T *k_, const T *v_,
             }
         }
         __syncthreads();  // the main sweep reuses the buffers
+    }
+    if (from_final) {
+        if constexpr (ROLE == kDQ) {
+#pragma unroll
+            for (int x = 0; x < NB; ++x) {
+                if constexpr (RESTART) {
+#pragma unroll
+                    for (int m = 0; m < MB; ++m) park[(x * (MB + 1) + m) * 64 + lane_id()] = W[x][m];
+                    park[(x * (MB + 1) + MB) * 64 + lane_id()] = zb[x];
+                }
+#pragma unroll
+                for (int m = 0; m < MB; ++m)
+#pragma unroll
+                    for (int t = 0; t < 4; ++t)
+                        W[x][m][t] = state_at(st, 16 * bk(x) + r, EM::ecol(m) + EM::estride * g + t, Ea, Ma);
+                if constexpr (NORM) {
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        const int f = 16 * bk(x) + 4 * g + t;
+                        zb[x][t] = f < Ea ? nin.zf[f] : 0.f;
+                    }
+                }
+            }
+        }
     }
 
     constexpr int OW = ROLE == kDV ? M : E;
@@ -343,6 +378,16 @@ __device__ __forceinline__ void bwd_sweep(const T *q_, const T *k_, const T *v_,
 
             f32x4 pend[NB][CB];  // this chunk's output tiles (rows 16 I + r) per column block
             if constexpr (ROLE == kDQ) {
+                if constexpr (RESTART) {  // S_c, z_c of the pre-pass (see RESTART)
+                    if (from_final && row0 == (npre - 1) * C) {
+#pragma unroll
+                        for (int x = 0; x < NB; ++x) {
+#pragma unroll
+                            for (int m = 0; m < MB; ++m) W[x][m] = park[(x * (MB + 1) + m) * 64 + lane_id()];
+                            zb[x] = park[(x * (MB + 1) + MB) * 64 + lane_id()];
+                        }
+                    }
+                }
                 // W = S_{c-1}^T = S_c^T - V_c^T K_c[:, b]
                 F kt[NB][CB];  // K_J[:, b] transposed: lane (g, r) <- K[16 J + 4g + t][16 b + r]
 #pragma unroll
@@ -631,7 +676,10 @@ __global__ __launch_bounds__((64 * bwd_waves<E, M, G, NB, IDLE>())) void cp_bwd_
     static_assert(NT <= 1024, "at most 16 waves per workgroup");
     constexpr int RE = Stage<T, NT, C, E>::RS, RM = Stage<T, NT, C, M>::RS;
     constexpr int BUF = 2 * C * RE + 2 * C * RM;
-    constexpr int DDE = NORM ? 2 * C * 4 / (int)sizeof(lds_t<T>) : 0;  // two dd buffers of C floats
+    // NORM: two dd buffers of C floats; with 16-bit I/O also the dQ waves'
+    // parking slots for the restart states
+    constexpr int PARK = NORM && sizeof(T) == 2 ? EG * NB * (MB + 1) * 64 * 4 : 0;
+    constexpr int DDE = NORM ? (2 * C + PARK) * 4 / (int)sizeof(lds_t<T>) : 0;
     __shared__ __attribute__((aligned(16))) lds_t<T> lds[2 * BUF + DDE];
 
     static_assert(RG >= 1 && RG <= 2 && RG <= C / 16, "row groups");

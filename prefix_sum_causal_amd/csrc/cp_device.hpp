@@ -50,6 +50,7 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 __device__ __forceinline__ int lane_g() { return (threadIdx.x >> 4) & 3; }
 __device__ __forceinline__ int lane_r() { return threadIdx.x & 15; }
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
 __device__ __forceinline__ f32x4 zero4() {
     f32x4 z = {0.f, 0.f, 0.f, 0.f};

@@ -134,6 +134,76 @@ def test_fwd_causality(cp, dtype):
     assert not torch.equal(out1[:, :, 70:], out2[:, :, 70:])
 
 
+# Few slices over a long sequence: the forward splits each slice into
+# sequence segments (a state-increment pass, then sweeps that start from the
+# sum of the earlier segments' increments).
+SEG_SHAPES = [(1, 2, 2085, 64, 64), (1, 1, 4133, 128, 128), (2, 1, 3001, 32, 128)]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", SEG_SHAPES, ids=[str(s) for s in SEG_SHAPES])
+def test_segmented_fwd_integer_bitwise(cp, orc, dtype, shape):
+    """One-hot Q, K rows and V in {0, 1}: scores are 0 or 1, states count
+    rows (a few dozen), outputs stay below 2^24, so every partial sum and
+    every operand is exact; the output matches the oracle rounded once to the
+    I/O type, the final state matches exactly."""
+    say(f"segmented fwd integer bitwise {dtype} {shape}")
+    N, H, L, E, M = shape
+    d = W.onehot_inputs(N, H, L, E, M, seed=L, need_do=False)
+    st = torch.empty((N, H, E, M), device="cuda", dtype=torch.float32)
+    out = cp.causal_product_fwd(dev(d["Q"], dtype), dev(d["K"], dtype), dev(d["V"], dtype), state_out=st)
+    torch.cuda.synchronize()
+    ref, Sref = orc.fwd(d["Q"], d["K"], d["V"], return_state=True)
+    assert Sref.max() <= 256  # exact as a bf16 operand
+    if dtype == "bf16":
+        ref = W.round_bf16(ref.astype(np.float32)).astype(np.float64)
+    assert np.array_equal(host(out), ref)
+    assert np.array_equal(host(st), Sref)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("norm", [False, True])
+def test_segmented_fwd_causality(cp, dtype, norm):
+    """Few slices, long rows (segmented): changing rows j > i of K and V
+    leaves rows <= i bitwise unchanged, across segment boundaries."""
+    say(f"segmented fwd causality {dtype} norm={norm}")
+    d = rand_inputs(1, 2, 3000, 64, 64, dtype, seed=19, qk="raw" if norm else "elu1")
+    q, k, v = (dev(d[n], dtype) for n in "QKV")
+    run = (lambda k_, v_: cp.linear_attn_fwd(q, k_, v_, 1e-6, 1)) if norm else \
+        (lambda k_, v_: cp.causal_product_fwd(q, k_, v_))
+    out1 = run(k, v)
+    k2, v2 = k.clone(), v.clone()
+    k2[:, :, 1501:] *= 3
+    v2[:, :, 1501:] = -v2[:, :, 1501:]
+    out2 = run(k2, v2)
+    torch.cuda.synchronize()
+    assert torch.equal(out1[:, :, :1501], out2[:, :, :1501])
+    assert not torch.equal(out1[:, :, 1501:], out2[:, :, 1501:])
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", SEG_SHAPES[:2], ids=[str(s) for s in SEG_SHAPES[:2]])
+def test_bwd_integer_bitwise_long(cp, orc, dtype, shape):
+    """One-hot Q, K and V, dO in {0, 1} over a long sequence: prefix and
+    suffix states count rows, every product and partial sum is a small exact
+    integer, so dQ, dK, dV match the oracle rounded once to the I/O type
+    (from the forward's final state and through the pre-pass)."""
+    say(f"bwd integer bitwise long {dtype} {shape}")
+    N, H, L, E, M = shape
+    d = W.onehot_inputs(N, H, L, E, M, seed=L + 1)
+    q, k, v, g = (dev(d[n], dtype) for n in ("Q", "K", "V", "dO"))
+    st = torch.empty((N, H, E, M), device="cuda", dtype=torch.float32)
+    cp.causal_product_fwd(q, k, v, state_out=st)
+    ref = orc.bwd(d["Q"], d["K"], d["V"], d["dO"])
+    if dtype == "bf16":
+        ref = [W.round_bf16(r.astype(np.float32)).astype(np.float64) for r in ref]
+    for use in (st, None):
+        got = cp.causal_product_bwd(q, k, v, g, state_final=use)
+        torch.cuda.synchronize()
+        for t, r, name in zip(got, ref, ("dq", "dk", "dv")):
+            assert np.array_equal(host(t), r), f"{name} state_final={use is not None}"
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_fwd_zero_state(cp, dtype):
     """V = 0 or K = 0 gives exactly zero (the zero-state probe)."""

@@ -41,3 +41,15 @@ def test_raw_and_scaled_recipes():
     assert abs(float(d4["V"].std()) - 0.5) < 0.01 and abs(float(d4["dO"].std()) - 0.5) < 0.01
     # E[elu(x)+1] for x ~ N(0,1) is 1.1605
     assert abs(float(d4["Q"].mean()) - 1.1605) < 0.01
+
+
+def test_onehot_inputs():
+    d = W.onehot_inputs(1, 2, 300, 32, 16, seed=3)
+    for n in ("Q", "K"):
+        assert d[n].shape == (1, 2, 300, 32)
+        assert np.array_equal(d[n].sum(-1), np.ones((1, 2, 300)))
+        assert set(np.unique(d[n])) <= {0.0, 1.0}
+    for n in ("V", "dO"):
+        assert d[n].shape == (1, 2, 300, 16) and set(np.unique(d[n])) <= {0.0, 1.0}
+    again = W.onehot_inputs(1, 2, 300, 32, 16, seed=3)
+    assert all(np.array_equal(d[n], again[n]) for n in d)

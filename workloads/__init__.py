@@ -142,3 +142,21 @@ def integer_inputs(N, H, L, E, M, seed=0, lo=0, hi=2, need_do=True) -> dict:
     if need_do:
         d["dO"] = rng.integers(lo, hi + 1, size=(N, H, L, M)).astype(np.float32)
     return d
+
+
+def onehot_inputs(N, H, L, E, M, seed=0, need_do=True) -> dict:
+    """Q and K rows with a single 1 at a random feature, V (and dO) in {0, 1}.
+    Every state entry counts the rows that hit one feature (about L / E of
+    them), so long sequences keep states, scores and every partial sum small
+    integers: exact in fp32 and, as operands, in bf16."""
+    rng = np.random.default_rng(seed)
+
+    def onehot(n):
+        x = np.zeros((N, H, L, n), dtype=np.float32)
+        np.put_along_axis(x, rng.integers(0, n, size=(N, H, L, 1)), 1.0, axis=-1)
+        return x
+
+    d = {"Q": onehot(E), "K": onehot(E), "V": rng.integers(0, 2, size=(N, H, L, M)).astype(np.float32)}
+    if need_do:
+        d["dO"] = rng.integers(0, 2, size=(N, H, L, M)).astype(np.float32)
+    return d
