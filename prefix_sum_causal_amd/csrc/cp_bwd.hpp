@@ -68,6 +68,19 @@ template <typename T> struct NormIn {
     const float *zf, *z0;
 };
 
+// The state carries of a backward over sequence segments, for one slice:
+// per segment s, dS[s] = sum over its rows of k v^T and dR[s] = sum of q dO^T
+// (E x M floats, row e and column m, at a stride of WS floats), written by
+// the segment-increment pass (dS for all but the last segment, dR for all but
+// the first).  Segment seg's dQ waves then end at S0 + sum_{s <= seg} dS[s]
+// (the last segment at the final state, or at the end of its own pre-pass),
+// and its dK, dV waves start from sum_{s > seg} dR[s].  dS == NULL: one
+// segment (seg = 0, nseg = 1).
+struct SegCarry {
+    const float *dS, *dR;
+    int seg, nseg;
+};
+
 // The dn rows of a staged dO chunk and their dd: the pieces of dO and of the
 // forward's output (same layout), and the denominators of the pieces' rows
 // (zero past the sequence).  The PPR lanes of a row (consecutive lanes of one
@@ -136,8 +149,8 @@ __device__ __forceinline__ void dotk_shared(FACC acc, int b0, int b1, FS fs, FO 
 template <typename T, int E, int M, int C, int G, int NB, int IDLE, int RG, int RGI, int NPF, bool NORM, bool FMAP,
           int ROLE>
 __device__ __forceinline__ void bwd_sweep(const T *q_, const T *k_, const T *v_, const T *g_, const float *s0,
-                                          const float *st, NormIn<T> nin, T *out_, float *ds0, float *dz0, int L,
-                                          int b, lds_t<T> *lds, int Ea, int Ma) {
+                                          const float *st, NormIn<T> nin, SegCarry sc, T *out_, float *ds0,
+                                          float *dz0, int L, int b, lds_t<T> *lds, int Ea, int Ma) {
     using O = Ops<T>;
     using F = typename O::frag;
     using EE = EOps<T, E>;  // contraction over e
@@ -218,7 +231,19 @@ __device__ __forceinline__ void bwd_sweep(const T *q_, const T *k_, const T *v_,
     // in LDS and take them back when the reverse sweep reaches that chunk,
     // so the early rows never see the final state's rounding.
     constexpr bool RESTART = NORM && !EXACT_PREFIX;
-    const bool from_final = st && (!NORM || nin.zf) && !EXACT_PREFIX;
+    constexpr int WS = E * M + E;
+    const bool last_seg = sc.seg == sc.nseg - 1;
+    const bool from_final = (!last_seg || (st && (!NORM || nin.zf))) && !EXACT_PREFIX;
+    // S[e][m] at the start of the segment (s0 plus the earlier segments'
+    // increments), and at its end (plus its own; the last segment: st)
+    auto s_begin = [&](int e, int m) {
+        float v = s0 ? state_at(s0, e, m, Ea, Ma) : 0.f;
+        for (int s = 0; s < sc.seg; ++s) v += sc.dS[s * WS + e * M + m];
+        return v;
+    };
+    auto s_end = [&](int e, int m) {
+        return last_seg ? state_at(st, e, m, Ea, Ma) : s_begin(e, m) + sc.dS[sc.seg * WS + e * M + m];
+    };
     constexpr int kPre = kRestartRows / C > 1 ? kRestartRows / C : 1;
     const int npre = from_final ? (RESTART ? (n < kPre ? n : kPre) : 0) : n;
     // the wave's parking slots: f32x4 per lane, MB state tiles then z, per block
@@ -229,14 +254,14 @@ __device__ __forceinline__ void bwd_sweep(const T *q_, const T *k_, const T *v_,
         // forward pre-pass over chunks [0, npre): S^T[:, b] = S0^T[:, b] + the
         // chunks' V^T K[:, b] (NORM: and z = z_{-1} + their column sums)
         if constexpr (ROLE == kDQ) {
-            if (s0) {
+            if (s0 || sc.seg > 0) {
 #pragma unroll
                 for (int x = 0; x < NB; ++x)
 #pragma unroll
                     for (int m = 0; m < MB; ++m)
 #pragma unroll
                         for (int t = 0; t < 4; ++t)
-                            W[x][m][t] = state_at(s0, 16 * bk(x) + r, EM::ecol(m) + EM::estride * g + t, Ea, Ma);
+                            W[x][m][t] = s_begin(16 * bk(x) + r, EM::ecol(m) + EM::estride * g + t);
             }
             if constexpr (NORM) {
                 if (nin.z0) {
@@ -310,8 +335,7 @@ __device__ __forceinline__ void bwd_sweep(const T *q_, const T *k_, const T *v_,
 #pragma unroll
                 for (int m = 0; m < MB; ++m)
 #pragma unroll
-                    for (int t = 0; t < 4; ++t)
-                        W[x][m][t] = state_at(st, 16 * bk(x) + r, EM::ecol(m) + EM::estride * g + t, Ea, Ma);
+                    for (int t = 0; t < 4; ++t) W[x][m][t] = s_end(16 * bk(x) + r, EM::ecol(m) + EM::estride * g + t);
                 if constexpr (NORM) {
 #pragma unroll
                     for (int t = 0; t < 4; ++t) {
@@ -319,6 +343,30 @@ __device__ __forceinline__ void bwd_sweep(const T *q_, const T *k_, const T *v_,
                         zb[x][t] = f < Ea ? nin.zf[f] : 0.f;
                     }
                 }
+            }
+        }
+    }
+
+    // dK, dV: R after the segment, the later segments' increments
+    if (!last_seg) {
+        for (int s = sc.seg + 1; s < sc.nseg; ++s) {
+            const float *dR = sc.dR + s * WS;
+            if constexpr (ROLE == kDK) {
+#pragma unroll
+                for (int x = 0; x < NB; ++x)
+#pragma unroll
+                    for (int m = 0; m < MB; ++m)
+#pragma unroll
+                        for (int t = 0; t < 4; ++t)
+                            W[x][m][t] += dR[(16 * bk(x) + r) * M + EM::ecol(m) + EM::estride * g + t];
+            } else if constexpr (ROLE == kDV) {
+#pragma unroll
+                for (int x = 0; x < NB; ++x)
+#pragma unroll
+                    for (int e = 0; e < EB; ++e)
+#pragma unroll
+                        for (int t = 0; t < 4; ++t)
+                            X[x][e][t] += dR[(EE::ecol(e) + EE::estride * g + t) * M + 16 * bk(x) + r];
             }
         }
     }
@@ -639,20 +687,20 @@ __device__ __forceinline__ void bwd_sweep(const T *q_, const T *k_, const T *v_,
 // The wave's role sweep for row group RGI.
 template <typename T, int E, int M, int C, int G, int NB, int IDLE, int RG, int RGI, int NPF, bool NORM, bool FMAP>
 __device__ __forceinline__ void bwd_role(int role, int b, const T *q_, const T *k_, const T *v_, const T *g_,
-                                         const float *s0, const float *st, NormIn<T> nin, T *dq_, T *dk_, T *dv_,
+                                         const float *s0, const float *st, NormIn<T> nin, SegCarry sc, T *dq_, T *dk_, T *dv_,
                                          float *ds0, float *dz0, int L, lds_t<T> *lds, int Ea, int Ma) {
     constexpr int EB = E / 16, MB = M / 16;
     if (role == kDQ && b < EB)
-        bwd_sweep<T, E, M, C, G, NB, IDLE, RG, RGI, NPF, NORM, FMAP, kDQ>(q_, k_, v_, g_, s0, st, nin, dq_, nullptr,
+        bwd_sweep<T, E, M, C, G, NB, IDLE, RG, RGI, NPF, NORM, FMAP, kDQ>(q_, k_, v_, g_, s0, st, nin, sc, dq_, nullptr,
                                                                           nullptr, L, b, lds, Ea, Ma);
     else if (role == kDK && b < EB)
-        bwd_sweep<T, E, M, C, G, NB, IDLE, RG, RGI, NPF, NORM, FMAP, kDK>(q_, k_, v_, g_, s0, st, nin, dk_, nullptr,
+        bwd_sweep<T, E, M, C, G, NB, IDLE, RG, RGI, NPF, NORM, FMAP, kDK>(q_, k_, v_, g_, s0, st, nin, sc, dk_, nullptr,
                                                                           dz0, L, b, lds, Ea, Ma);
     else if (role == kDV && b < MB)
-        bwd_sweep<T, E, M, C, G, NB, IDLE, RG, RGI, NPF, NORM, FMAP, kDV>(q_, k_, v_, g_, s0, st, nin, dv_, ds0,
+        bwd_sweep<T, E, M, C, G, NB, IDLE, RG, RGI, NPF, NORM, FMAP, kDV>(q_, k_, v_, g_, s0, st, nin, sc, dv_, ds0,
                                                                           nullptr, L, b, lds, Ea, Ma);
     else
-        bwd_sweep<T, E, M, C, G, NB, IDLE, RG, RGI, NPF, NORM, FMAP, kIdle>(q_, k_, v_, g_, s0, st, nin, nullptr,
+        bwd_sweep<T, E, M, C, G, NB, IDLE, RG, RGI, NPF, NORM, FMAP, kIdle>(q_, k_, v_, g_, s0, st, nin, sc, nullptr,
                                                                             nullptr, nullptr, L, 0, lds, Ea, Ma);
 }
 
@@ -667,7 +715,7 @@ __global__ __launch_bounds__((64 * bwd_waves<E, M, G, NB, IDLE>())) void cp_bwd_
     const float *__restrict__ state_in, const float *__restrict__ state_final, const T *__restrict__ O,
     const float *__restrict__ den, const float *__restrict__ z_in, const float *__restrict__ z_final,
     T *__restrict__ dQ, T *__restrict__ dK, T *__restrict__ dV, float *__restrict__ dstate_in,
-    float *__restrict__ dz_in, int L, int NS, int Ea, int Ma) {
+    float *__restrict__ dz_in, const float *__restrict__ ws, int L, int NS, int seg_len, int Ea, int Ma) {
     constexpr int EB = E / 16, MB = M / 16;
     // with several blocks per wave every wave's blocks all exist
     static_assert(NB == 1 || (EB % (G * NB) == 0 && MB % (G * NB) == 0), "blocks per wave");
@@ -683,34 +731,43 @@ __global__ __launch_bounds__((64 * bwd_waves<E, M, G, NB, IDLE>())) void cp_bwd_
     __shared__ __attribute__((aligned(16))) lds_t<T> lds[2 * BUF + DDE];
 
     static_assert(RG >= 1 && RG <= 2 && RG <= C / 16, "row groups");
+    const int nseg = (L + seg_len - 1) / seg_len;
     int slice, part;
-    map_block(blockIdx.x, NS, G * RG, slice, part);
-    const int grp = part % G, rg = part / G;
+    map_block(blockIdx.x, NS, G * RG * nseg, slice, part);
+    const int grp = part % G, rg = (part / G) % RG, seg = part / (G * RG);
     const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
-    // the tensors' own head sizes Ea <= E, Ma <= M (the kernel's tile sizes)
-    const int64_t oe = (int64_t)slice * L * Ea, om = (int64_t)slice * L * Ma, os = (int64_t)slice * Ea * Ma;
+    // rows [rb, re) of the slice; the tensors' own head sizes Ea <= E, Ma <= M
+    // (the kernel's tile sizes)
+    const int rb = seg * seg_len, re = rb + seg_len < L ? rb + seg_len : L;
+    const int64_t oe = ((int64_t)slice * L + rb) * Ea, om = ((int64_t)slice * L + rb) * Ma;
+    const int64_t os = (int64_t)slice * Ea * Ma;
     const T *q_ = Q + oe, *k_ = K + oe, *v_ = V + om, *g_ = Gr + om;
     const float *s0 = state_in ? state_in + os : nullptr;
     const float *st = state_final ? state_final + os : nullptr;
     NormIn<T> nin{nullptr, nullptr, nullptr, nullptr};
     if constexpr (NORM) {
         nin.o = O + om;
-        nin.den = den + (int64_t)slice * L;
+        nin.den = den + (int64_t)slice * L + rb;
         nin.zf = z_final ? z_final + (int64_t)slice * Ea : nullptr;
         nin.z0 = z_in ? z_in + (int64_t)slice * Ea : nullptr;
     }
-    float *ds0 = dstate_in ? dstate_in + os : nullptr;
-    float *dz0 = dz_in ? dz_in + (int64_t)slice * Ea : nullptr;
+    // the gradients of the initial states come from the first segment
+    float *ds0 = dstate_in && seg == 0 ? dstate_in + os : nullptr;
+    float *dz0 = dz_in && seg == 0 ? dz_in + (int64_t)slice * Ea : nullptr;
+    constexpr int WS = E * M + E;
+    const SegCarry sc{ws ? ws + (int64_t)slice * nseg * WS : nullptr,
+                      ws ? ws + ((int64_t)NS + slice) * nseg * WS : nullptr, seg, nseg};
+    const int Ls = re - rb;
     // wave w: role, and the first of its NB column blocks (b, b + G, ...)
     const int role = w < EG ? kDQ : w < 2 * EG ? kDK : w < 2 * EG + MG ? kDV : kIdle;
     const int lw = role == kDQ ? w : role == kDK ? w - EG : w - 2 * EG;
     const int b = grp + G * NB * lw;
     if (rg == 0 || RG == 1)
-        bwd_role<T, E, M, C, G, NB, IDLE, RG, 0, NPF, NORM, FMAP>(role, b, q_, k_, v_, g_, s0, st, nin, dQ + oe,
-                                                                 dK + oe, dV + om, ds0, dz0, L, lds, Ea, Ma);
+        bwd_role<T, E, M, C, G, NB, IDLE, RG, 0, NPF, NORM, FMAP>(role, b, q_, k_, v_, g_, s0, st, nin, sc, dQ + oe,
+                                                                 dK + oe, dV + om, ds0, dz0, Ls, lds, Ea, Ma);
     else
         bwd_role<T, E, M, C, G, NB, IDLE, RG, (RG > 1 ? 1 : 0), NPF, NORM, FMAP>(
-            role, b, q_, k_, v_, g_, s0, st, nin, dQ + oe, dK + oe, dV + om, ds0, dz0, L, lds, Ea, Ma);
+            role, b, q_, k_, v_, g_, s0, st, nin, sc, dQ + oe, dK + oe, dV + om, ds0, dz0, Ls, lds, Ea, Ma);
 }
 
 }  // namespace cp

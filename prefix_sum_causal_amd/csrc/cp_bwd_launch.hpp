@@ -2,16 +2,26 @@
 // normalised form), shared by the bf16, fp16 and fp32 translation units.
 #pragma once
 
+#include <type_traits>
+
 #include "cp_bwd.hpp"
 #include "cp_launch.hpp"
 #include "cp_tune.hpp"
 
 namespace cp {
 
-// One kernel per call, no scratch.  The normalised form's extra terms
-// (dn = dO / den, dd = -(dO . out) / den, the normaliser before each chunk)
-// are formed inside the sweep from the forward's output, denominators and
-// final (or initial) normaliser.
+// One kernel per call, no scratch, when the slices fill the GPU.  The
+// normalised form's extra terms (dn = dO / den, dd = -(dO . out) / den, the
+// normaliser before each chunk) are formed inside the sweep from the
+// forward's output, denominators and final (or initial) normaliser.
+//
+// Few slices (the causal product): each slice is cut into nseg sequence
+// segments of seg_len rows (a multiple of C) and run in two launches, the
+// scan's carry one level up, as in the forward.  The first computes every
+// segment's increments of the prefix state (sum of k v^T, all but the last
+// segment) and of the suffix state (sum of q dO^T, all but the first) into a
+// stream-ordered scratch buffer; the second sweeps each segment with the
+// states at its ends summed from those increments (see SegCarry).
 template <typename T, int E, int M, bool NORM, bool FMAP>
 hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t s) {
     using P = Tune<T, E, M>;
@@ -22,10 +32,37 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t s) {
     T *dq = static_cast<T *>(a.dQ), *dk = static_cast<T *>(a.dK), *dv = static_cast<T *>(a.dV);
     float *ds0 = a.dstate_in, *dz0 = a.dz_in;
     int L = a.L, NS = a.NS, Ea = a.Ea, Ma = a.Ma;
-    auto kern = cp_bwd_kernel<T, E, M, C, P::BG, P::BNB, P::BIDLE, P::BRG, P::BNPF, NORM, FMAP>;
-    void *args[] = {&q, &k, &v, &g, &s0, &st, &o, &den, &z0, &zf, &dq, &dk, &dv, &ds0, &dz0, &L, &NS, &Ea, &Ma};
-    return launch_kernel(reinterpret_cast<const void *>(kern), dim3(NS * P::BG * P::BRG),
-                         dim3(64 * bwd_waves<E, M, P::BG, P::BNB, P::BIDLE>()), args, s);
+
+    const int nseg0 = NORM ? 1 : seq_segments(L, NS, P::BG * P::BRG, C);
+    const int nchunks = (L + C - 1) / C;
+    int seg_len = (nchunks + nseg0 - 1) / nseg0 * C;
+    const int nseg = (L + seg_len - 1) / seg_len;
+    if (nseg == 1) seg_len = L;
+    float *ws = nullptr;
+    hipError_t e = hipSuccess;
+    if (nseg > 1) {
+        constexpr int WS = E * M + E;
+        e = hipMallocAsync(reinterpret_cast<void **>(&ws), (size_t)2 * NS * nseg * WS * sizeof(float), s);
+        if (e != hipSuccess) return e;
+        const SegArgs sa{k, v, ws, q, g, ws + (size_t)NS * nseg * WS, L, NS, seg_len, Ea, Ma};
+        const seg_fn fn = std::is_same<T, float>::value ? seg_f32(E, M)
+                          : std::is_same<T, __bf16>::value ? seg_bf16(E, M)
+                                                           : seg_f16(E, M);
+        e = fn ? fn(sa, s) : hipErrorInvalidValue;
+    }
+    if (e == hipSuccess) {
+        const float *wsc = ws;
+        auto kern = cp_bwd_kernel<T, E, M, C, P::BG, P::BNB, P::BIDLE, P::BRG, P::BNPF, NORM, FMAP>;
+        void *args[] = {&q,   &k,   &v,  &g,  &s0, &st, &o,  &den, &z0, &zf, &dq,     &dk,
+                        &dv,  &ds0, &dz0, &wsc, &L, &NS, &seg_len, &Ea, &Ma};
+        e = launch_kernel(reinterpret_cast<const void *>(kern), dim3(NS * P::BG * P::BRG * nseg),
+                          dim3(64 * bwd_waves<E, M, P::BG, P::BNB, P::BIDLE>()), args, s);
+    }
+    if (ws) {
+        const hipError_t f = hipFreeAsync(ws, s);
+        if (e == hipSuccess) e = f;
+    }
+    return e;
 }
 
 template <typename T, int E, int M, bool NORM>

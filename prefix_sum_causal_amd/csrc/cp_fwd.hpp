@@ -293,11 +293,14 @@ __device__ __forceinline__ void fwd_sweep(const T *q_, const T *k_, const T *v_,
 // CW column blocks of M (and of its share of the E/16 tiles of dz, as K^T 1).
 // The segments' increments are independent of each other, so this pass runs
 // at the rate of its two input streams; the last segment's increment is never
-// needed and not computed.
+// needed and not computed.  An optional second job (K2 != NULL: the backward's
+// suffix carries, sum_j q_j dO_j^T) runs in the same launch, over segments 1
+// .. nseg-1 (the first one's is never needed), into ws2.
 template <typename T, int E, int M, int C, int NW, int NPF, bool NORM, bool FMAP>
-__global__ __launch_bounds__(64 * NW) void cp_seg_state_kernel(const T *__restrict__ K, const T *__restrict__ V,
-                                                               float *__restrict__ ws, int L, int NS, int seg_len,
-                                                               int Ea, int Ma) {
+__global__ __launch_bounds__(64 * NW) void cp_seg_state_kernel(const T *__restrict__ K1, const T *__restrict__ V1,
+                                                               float *__restrict__ ws1, const T *__restrict__ K2,
+                                                               const T *__restrict__ V2, float *__restrict__ ws2,
+                                                               int L, int NS, int seg_len, int Ea, int Ma) {
     using O = Ops<T>;
     using F = typename O::frag;
     using EO = EOps<T, E>;
@@ -314,8 +317,12 @@ __global__ __launch_bounds__(64 * NW) void cp_seg_state_kernel(const T *__restri
     __shared__ __attribute__((aligned(16))) lds_t<T> lds[2 * BUF];
 
     const int nseg = (L + seg_len - 1) / seg_len;
-    int slice, seg;
-    map_block(blockIdx.x, NS, nseg - 1, slice, seg);
+    int slice, part;
+    map_block(blockIdx.x, NS, (K2 ? 2 : 1) * (nseg - 1), slice, part);
+    const bool second = part >= nseg - 1;
+    const int seg = second ? part - (nseg - 1) + 1 : part;
+    const T *K = second ? K2 : K1, *V = second ? V2 : V1;
+    float *ws = second ? ws2 : ws1;
     const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
     const int g = lane_g(), r = lane_r();
     const T *k_ = K + (int64_t)slice * L * Ea;

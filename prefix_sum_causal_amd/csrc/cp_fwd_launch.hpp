@@ -8,32 +8,6 @@
 
 namespace cp {
 
-// Segments per slice for L rows and NS slices: one, unless the slices leave
-// most CUs idle; then enough segments of at least kMinSegChunks chunks for
-// about two workgroups per CU.
-#ifndef CP_SEG_MIN_CHUNKS
-#define CP_SEG_MIN_CHUNKS 4
-#endif
-#ifndef CP_SEG_WG_PER_CU
-#define CP_SEG_WG_PER_CU 2
-#endif
-constexpr int kCUs = 256, kMinSegChunks = CP_SEG_MIN_CHUNKS, kSegWgPerCU = CP_SEG_WG_PER_CU;
-// stages of the load ring of the segment-increment pass, and its waves (at
-// most four, each owning M/16/waves column blocks of the increment)
-#ifndef CP_SEG_NPF
-#define CP_SEG_NPF 4
-#endif
-template <int M>
-constexpr int seg_state_waves() { return M / 16 >= 4 ? 4 : M / 16; }
-inline int fwd_segments(int L, int NS, int groups, int C) {
-    const long wg = (long)NS * groups;
-    const int nchunks = (L + C - 1) / C;
-    if (wg >= kCUs || nchunks < 2 * kMinSegChunks) return 1;
-    long want = ((long)kSegWgPerCU * kCUs + wg - 1) / wg;
-    const long most = nchunks / kMinSegChunks;
-    return (int)(want < most ? want : most);
-}
-
 template <typename T, int E, int M, bool NORM, bool FMAP>
 hipError_t launch_fwd_t(const FwdArgs &a, hipStream_t s) {
     using P = Tune<T, E, M>;
@@ -49,7 +23,7 @@ hipError_t launch_fwd_t(const FwdArgs &a, hipStream_t s) {
     constexpr int FRS = NORM ? 1 : P::FRS, FRG = NORM ? P::FRG_N : P::FRG;
     const dim3 block(64 * ((M / 16 / P::FG) * FRS + (DW ? 1 : 0)));
 
-    const int nseg0 = fwd_segments(L, NS, P::FG * FRG, P::FC);
+    const int nseg0 = seq_segments(L, NS, P::FG * FRG, P::FC);
     const int nchunks = (L + P::FC - 1) / P::FC;
     int seg_len = (nchunks + nseg0 - 1) / nseg0 * P::FC;
     const int nseg = (L + seg_len - 1) / seg_len;
@@ -74,7 +48,9 @@ hipError_t launch_fwd_t(const FwdArgs &a, hipStream_t s) {
         }
         constexpr int SW = seg_state_waves<M>();
         auto k1 = cp_seg_state_kernel<T, E, M, P::FC, SW, CP_SEG_NPF, NORM, FMAP>;
-        void *args1[] = {&k, &v, &ws, &L, &NS, &seg_len, &Ea, &Ma};
+        const T *none = nullptr;
+        float *nows = nullptr;
+        void *args1[] = {&k, &v, &ws, &none, &none, &nows, &L, &NS, &seg_len, &Ea, &Ma};
         e = launch_kernel(reinterpret_cast<const void *>(k1), dim3(NS * (nseg - 1)), dim3(64 * SW), args1, s);
     } else {
         seg_len = L;
@@ -108,6 +84,33 @@ fwd_fn pick_fwd(int E, int M) {
          launch_fwd_fm<T, 64, 128, NORM>},
         {launch_fwd_fm<T, 128, 16, NORM>, launch_fwd_fm<T, 128, 32, NORM>, launch_fwd_fm<T, 128, 64, NORM>,
          launch_fwd_fm<T, 128, 128, NORM>},
+    };
+    const int ie = tile_index(E), im = tile_index(M);
+    return (ie < 0 || im < 0) ? nullptr : table[ie][im];
+}
+
+// The backward's two-job segment-increment pass (see SegArgs).
+template <typename T, int E, int M>
+hipError_t launch_seg_t(const SegArgs &a, hipStream_t s) {
+    const T *k1 = static_cast<const T *>(a.K1), *v1 = static_cast<const T *>(a.V1);
+    const T *k2 = static_cast<const T *>(a.K2), *v2 = static_cast<const T *>(a.V2);
+    float *ws1 = a.ws1, *ws2 = a.ws2;
+    int L = a.L, NS = a.NS, seg_len = a.seg_len, Ea = a.Ea, Ma = a.Ma;
+    const int nseg = (L + seg_len - 1) / seg_len;
+    constexpr int SW = seg_state_waves<M>();
+    auto kern = cp_seg_state_kernel<T, E, M, 64, SW, CP_SEG_NPF, false, false>;
+    void *args[] = {&k1, &v1, &ws1, &k2, &v2, &ws2, &L, &NS, &seg_len, &Ea, &Ma};
+    return launch_kernel(reinterpret_cast<const void *>(kern), dim3(NS * (k2 ? 2 : 1) * (nseg - 1)), dim3(64 * SW),
+                         args, s);
+}
+
+template <typename T>
+seg_fn pick_seg(int E, int M) {
+    static const seg_fn table[4][4] = {
+        {launch_seg_t<T, 16, 16>, launch_seg_t<T, 16, 32>, launch_seg_t<T, 16, 64>, launch_seg_t<T, 16, 128>},
+        {launch_seg_t<T, 32, 16>, launch_seg_t<T, 32, 32>, launch_seg_t<T, 32, 64>, launch_seg_t<T, 32, 128>},
+        {launch_seg_t<T, 64, 16>, launch_seg_t<T, 64, 32>, launch_seg_t<T, 64, 64>, launch_seg_t<T, 64, 128>},
+        {launch_seg_t<T, 128, 16>, launch_seg_t<T, 128, 32>, launch_seg_t<T, 128, 64>, launch_seg_t<T, 128, 128>},
     };
     const int ie = tile_index(E), im = tile_index(M);
     return (ie < 0 || im < 0) ? nullptr : table[ie][im];

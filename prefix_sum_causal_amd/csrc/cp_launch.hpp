@@ -50,10 +50,51 @@ struct BwdArgs {
     int Ea, Ma;  // head sizes of the tensors (the kernel runs the next tile size up)
 };
 
+// Segments per slice for L rows and NS slices (forward and backward): one,
+// unless the slices leave most CUs idle; then enough segments of at least
+// kMinSegChunks chunks for about two workgroups per CU.
+#ifndef CP_SEG_MIN_CHUNKS
+#define CP_SEG_MIN_CHUNKS 4
+#endif
+#ifndef CP_SEG_WG_PER_CU
+#define CP_SEG_WG_PER_CU 2
+#endif
+constexpr int kCUs = 256, kMinSegChunks = CP_SEG_MIN_CHUNKS, kSegWgPerCU = CP_SEG_WG_PER_CU;
+// stages of the load ring of the segment-increment pass, and its waves (at
+// most four, each owning M/16/waves column blocks of the increment)
+#ifndef CP_SEG_NPF
+#define CP_SEG_NPF 4
+#endif
+template <int M>
+constexpr int seg_state_waves() { return M / 16 >= 4 ? 4 : M / 16; }
+inline int seq_segments(int L, int NS, int groups, int C) {
+    const long wg = (long)NS * groups;
+    const int nchunks = (L + C - 1) / C;
+    if (wg >= kCUs || nchunks < 2 * kMinSegChunks) return 1;
+    long want = ((long)kSegWgPerCU * kCUs + wg - 1) / wg;
+    const long most = nchunks / kMinSegChunks;
+    return (int)(want < most ? want : most);
+}
+
 // Each launcher enqueues one kernel on stream and returns hipSuccess or the
 // launch error.  NULL when (E, M) is not instantiated.
 typedef hipError_t (*fwd_fn)(const FwdArgs &, hipStream_t);
 typedef hipError_t (*bwd_fn)(const BwdArgs &, hipStream_t);
+
+// The backward's segment-increment pass (cp_seg_state_kernel with two jobs:
+// sum k v^T over segments 0 .. nseg-2 into ws1, sum q dO^T over segments
+// 1 .. nseg-1 into ws2); its instances live with the forward's.
+struct SegArgs {
+    const void *K1, *V1;
+    float *ws1;
+    const void *K2, *V2;
+    float *ws2;
+    int L, NS, seg_len, Ea, Ma;
+};
+typedef hipError_t (*seg_fn)(const SegArgs &, hipStream_t);
+seg_fn seg_f32(int E, int M);
+seg_fn seg_bf16(int E, int M);
+seg_fn seg_f16(int E, int M);
 
 fwd_fn fwd_f32(int E, int M, bool norm);
 fwd_fn fwd_bf16(int E, int M, bool norm);

@@ -204,6 +204,35 @@ def test_bwd_integer_bitwise_long(cp, orc, dtype, shape):
             assert np.array_equal(host(t), r), f"{name} state_final={use is not None}"
 
 
+SEG_BWD_SHAPES = [(1, 2, 3001, 64, 64), (2, 1, 2500, 32, 128), (1, 1, 5000, 128, 128), (1, 3, 700, 64, 32)]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", SEG_BWD_SHAPES, ids=[str(s) for s in SEG_BWD_SHAPES])
+def test_segmented_bwd(cp, orc, dtype, shape):
+    """Few slices over long rows: the backward runs over sequence segments
+    (segment increments of both carried states, then per-segment sweeps),
+    from an initial state, with and without the forward's final state; dQ,
+    dK, dV and the initial state's gradient against the oracle."""
+    say(f"segmented bwd {dtype} {shape}")
+    N, H, L, E, M = shape
+    d = rand_inputs(N, H, L, E, M, dtype, seed=L + E)
+    S0 = (np.random.default_rng(L).standard_normal((N, H, E, M)) * 3).astype(np.float32)
+    q, k, v, g = (dev(d[n], dtype) for n in ("Q", "K", "V", "dO"))
+    s0 = torch.from_numpy(S0).cuda()
+    st = torch.empty((N, H, E, M), device="cuda", dtype=torch.float32)
+    cp.causal_product_fwd(q, k, v, state_in=s0, state_out=st)
+    ref = orc.bwd(d["Q"], d["K"], d["V"], d["dO"], S0=S0, with_dS0=True)
+    for use in (st, None):
+        ds0 = torch.empty_like(st)
+        got = cp.causal_product_bwd(q, k, v, g, state_final=use, state_in=s0, dstate_in=ds0)
+        torch.cuda.synchronize()
+        for t, r, name in zip(list(got) + [ds0], ref, ("dq", "dk", "dv", "dS0")):
+            err = oracle.max_rel_err(host(t), r)
+            say(f"  {name} state_final={use is not None}: {err:.3e}")
+            assert err <= TOL[dtype], name
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_fwd_zero_state(cp, dtype):
     """V = 0 or K = 0 gives exactly zero (the zero-state probe)."""
