@@ -234,16 +234,74 @@ __device__ __forceinline__ void bwd_sweep(const T *q_, const T *k_, const T *v_,
     constexpr int WS = E * M + E;
     const bool last_seg = sc.seg == sc.nseg - 1;
     const bool from_final = (!last_seg || (st && (!NORM || nin.zf))) && !EXACT_PREFIX;
-    // S[e][m] at the start of the segment (s0 plus the earlier segments'
-    // increments), and at its end (plus its own; the last segment: st)
-    auto s_begin = [&](int e, int m) {
-        float v = s0 ? state_at(s0, e, m, Ea, Ma) : 0.f;
-        for (int s = 0; s < sc.seg; ++s) v += sc.dS[s * WS + e * M + m];
-        return v;
-    };
-    auto s_end = [&](int e, int m) {
-        return last_seg ? state_at(st, e, m, Ea, Ma) : s_begin(e, m) + sc.dS[sc.seg * WS + e * M + m];
-    };
+    // Over sequence segments (sc.dS != NULL, the causal product only) the
+    // starting states are sums of whole E x M tiles: all threads add them up
+    // with 16-byte loads into an fp32 tile in LDS (the ring buffers, not yet
+    // in use), from which each wave takes its fragments.  The dQ waves start
+    // at S after the segment (s0 plus the increments up to and including
+    // this segment's; the last segment: st) or, without it, at S before the
+    // segment for a pre-pass over the segment; the dK and dV waves at R after
+    // the segment (the later segments' increments).
+    const bool staged = sc.dS != nullptr;
+    if (staged) {
+        constexpr int TS = M + 4;  // fp32 row stride of the tile (rows 16 bytes apart mod 128)
+        static_assert(E * TS * 4 <= 2 * BUF * (int)sizeof(lds_t<T>), "the carry tile fits the ring buffers");
+        float *tile = reinterpret_cast<float *>(lds);
+        const int tid = (int)threadIdx.x;
+        const bool use_st = from_final && last_seg;
+        const int upto = from_final ? sc.seg + 1 : sc.seg;
+        for (int p = tid; p < E * M / 4; p += NT) {
+            const int e = p / (M / 4), m = p % (M / 4) * 4;
+            const bool in = e < Ea && m < Ma;
+            f32x4 a = zero4();
+            if (use_st) {
+                if (in) a = *reinterpret_cast<const f32x4 *>(st + e * Ma + m);
+            } else {
+                if (s0 && in) a = *reinterpret_cast<const f32x4 *>(s0 + e * Ma + m);
+                for (int s = 0; s < upto; ++s) a += *reinterpret_cast<const f32x4 *>(sc.dS + s * WS + e * M + m);
+            }
+            *reinterpret_cast<f32x4 *>(tile + e * TS + m) = a;
+        }
+        __syncthreads();
+        if constexpr (ROLE == kDQ) {
+#pragma unroll
+            for (int x = 0; x < NB; ++x)
+#pragma unroll
+                for (int m = 0; m < MB; ++m)
+#pragma unroll
+                    for (int t = 0; t < 4; ++t)
+                        W[x][m][t] = tile[(16 * bk(x) + r) * TS + EM::ecol(m) + EM::estride * g + t];
+        }
+        __syncthreads();
+        if (!last_seg) {
+            for (int p = tid; p < E * M / 4; p += NT) {
+                const int e = p / (M / 4), m = p % (M / 4) * 4;
+                f32x4 a = zero4();
+                for (int s = sc.seg + 1; s < sc.nseg; ++s)
+                    a += *reinterpret_cast<const f32x4 *>(sc.dR + s * WS + e * M + m);
+                *reinterpret_cast<f32x4 *>(tile + e * TS + m) = a;
+            }
+            __syncthreads();
+            if constexpr (ROLE == kDK) {
+#pragma unroll
+                for (int x = 0; x < NB; ++x)
+#pragma unroll
+                    for (int m = 0; m < MB; ++m)
+#pragma unroll
+                        for (int t = 0; t < 4; ++t)
+                            W[x][m][t] = tile[(16 * bk(x) + r) * TS + EM::ecol(m) + EM::estride * g + t];
+            } else if constexpr (ROLE == kDV) {
+#pragma unroll
+                for (int x = 0; x < NB; ++x)
+#pragma unroll
+                    for (int e = 0; e < EB; ++e)
+#pragma unroll
+                        for (int t = 0; t < 4; ++t)
+                            X[x][e][t] = tile[(EE::ecol(e) + EE::estride * g + t) * TS + 16 * bk(x) + r];
+            }
+            __syncthreads();
+        }
+    }
     constexpr int kPre = kRestartRows / C > 1 ? kRestartRows / C : 1;
     const int npre = from_final ? (RESTART ? (n < kPre ? n : kPre) : 0) : n;
     // the wave's parking slots: f32x4 per lane, MB state tiles then z, per block
@@ -254,14 +312,14 @@ __device__ __forceinline__ void bwd_sweep(const T *q_, const T *k_, const T *v_,
         // forward pre-pass over chunks [0, npre): S^T[:, b] = S0^T[:, b] + the
         // chunks' V^T K[:, b] (NORM: and z = z_{-1} + their column sums)
         if constexpr (ROLE == kDQ) {
-            if (s0 || sc.seg > 0) {
+            if (s0 && !staged) {
 #pragma unroll
                 for (int x = 0; x < NB; ++x)
 #pragma unroll
                     for (int m = 0; m < MB; ++m)
 #pragma unroll
                         for (int t = 0; t < 4; ++t)
-                            W[x][m][t] = s_begin(16 * bk(x) + r, EM::ecol(m) + EM::estride * g + t);
+                            W[x][m][t] = state_at(s0, 16 * bk(x) + r, EM::ecol(m) + EM::estride * g + t, Ea, Ma);
             }
             if constexpr (NORM) {
                 if (nin.z0) {
@@ -323,7 +381,7 @@ __device__ __forceinline__ void bwd_sweep(const T *q_, const T *k_, const T *v_,
         }
         __syncthreads();  // the main sweep reuses the buffers
     }
-    if (from_final) {
+    if (from_final && !staged) {
         if constexpr (ROLE == kDQ) {
 #pragma unroll
             for (int x = 0; x < NB; ++x) {
@@ -335,7 +393,8 @@ __device__ __forceinline__ void bwd_sweep(const T *q_, const T *k_, const T *v_,
 #pragma unroll
                 for (int m = 0; m < MB; ++m)
 #pragma unroll
-                    for (int t = 0; t < 4; ++t) W[x][m][t] = s_end(16 * bk(x) + r, EM::ecol(m) + EM::estride * g + t);
+                    for (int t = 0; t < 4; ++t)
+                        W[x][m][t] = state_at(st, 16 * bk(x) + r, EM::ecol(m) + EM::estride * g + t, Ea, Ma);
                 if constexpr (NORM) {
 #pragma unroll
                     for (int t = 0; t < 4; ++t) {
@@ -343,30 +402,6 @@ __device__ __forceinline__ void bwd_sweep(const T *q_, const T *k_, const T *v_,
                         zb[x][t] = f < Ea ? nin.zf[f] : 0.f;
                     }
                 }
-            }
-        }
-    }
-
-    // dK, dV: R after the segment, the later segments' increments
-    if (!last_seg) {
-        for (int s = sc.seg + 1; s < sc.nseg; ++s) {
-            const float *dR = sc.dR + s * WS;
-            if constexpr (ROLE == kDK) {
-#pragma unroll
-                for (int x = 0; x < NB; ++x)
-#pragma unroll
-                    for (int m = 0; m < MB; ++m)
-#pragma unroll
-                        for (int t = 0; t < 4; ++t)
-                            W[x][m][t] += dR[(16 * bk(x) + r) * M + EM::ecol(m) + EM::estride * g + t];
-            } else if constexpr (ROLE == kDV) {
-#pragma unroll
-                for (int x = 0; x < NB; ++x)
-#pragma unroll
-                    for (int e = 0; e < EB; ++e)
-#pragma unroll
-                        for (int t = 0; t < 4; ++t)
-                            X[x][e][t] += dR[(EE::ecol(e) + EE::estride * g + t) * M + 16 * bk(x) + r];
             }
         }
     }

@@ -33,7 +33,7 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t s) {
     float *ds0 = a.dstate_in, *dz0 = a.dz_in;
     int L = a.L, NS = a.NS, Ea = a.Ea, Ma = a.Ma;
 
-    const int nseg0 = NORM ? 1 : seq_segments(L, NS, P::BG * P::BRG, C);
+    const int nseg0 = NORM ? 1 : seq_segments(L, NS, P::BG * P::BRG, C, kBwdSegWgPerCU);
     const int nchunks = (L + C - 1) / C;
     int seg_len = (nchunks + nseg0 - 1) / nseg0 * C;
     const int nseg = (L + seg_len - 1) / seg_len;

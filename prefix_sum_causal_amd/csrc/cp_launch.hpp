@@ -59,7 +59,11 @@ struct BwdArgs {
 #ifndef CP_SEG_WG_PER_CU
 #define CP_SEG_WG_PER_CU 2
 #endif
+#ifndef CP_BWD_SEG_WG_PER_CU
+#define CP_BWD_SEG_WG_PER_CU 1
+#endif
 constexpr int kCUs = 256, kMinSegChunks = CP_SEG_MIN_CHUNKS, kSegWgPerCU = CP_SEG_WG_PER_CU;
+constexpr int kBwdSegWgPerCU = CP_BWD_SEG_WG_PER_CU;  // the backward's workgroups hold a CU each
 // stages of the load ring of the segment-increment pass, and its waves (at
 // most four, each owning M/16/waves column blocks of the increment)
 #ifndef CP_SEG_NPF
@@ -67,11 +71,11 @@ constexpr int kCUs = 256, kMinSegChunks = CP_SEG_MIN_CHUNKS, kSegWgPerCU = CP_SE
 #endif
 template <int M>
 constexpr int seg_state_waves() { return M / 16 >= 4 ? 4 : M / 16; }
-inline int seq_segments(int L, int NS, int groups, int C) {
+inline int seq_segments(int L, int NS, int groups, int C, int wg_per_cu = kSegWgPerCU) {
     const long wg = (long)NS * groups;
     const int nchunks = (L + C - 1) / C;
     if (wg >= kCUs || nchunks < 2 * kMinSegChunks) return 1;
-    long want = ((long)kSegWgPerCU * kCUs + wg - 1) / wg;
+    long want = ((long)wg_per_cu * kCUs + wg - 1) / wg;
     const long most = nchunks / kMinSegChunks;
     return (int)(want < most ? want : most);
 }
