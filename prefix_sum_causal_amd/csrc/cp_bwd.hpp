@@ -58,16 +58,6 @@ __device__ __forceinline__ float state_at(const float *s, int e, int m, int Ea, 
     return e < Ea && m < Ma ? s[e * Ma + m] : 0.f;
 }
 
-// The normalised form's extra inputs of one slice: the forward's output and
-// denominators (the backward turns dO into dn = dO / den and dd = -(dO . out)
-// / den while staging it), the final normaliser z_{L-1} (optional) and the
-// initial one z_{-1} (optional).
-template <typename T> struct NormIn {
-    const T *o;
-    const float *den;
-    const float *zf, *z0;
-};
-
 // The state carries of a backward over sequence segments, for one slice:
 // per segment s, dS[s] = sum over its rows of k v^T and dR[s] = sum of q dO^T
 // (E x M floats, row e and column m, at a stride of WS floats), written by
@@ -80,37 +70,6 @@ struct SegCarry {
     const float *dS, *dR;
     int seg, nseg;
 };
-
-// The dn rows of a staged dO chunk and their dd: the pieces of dO and of the
-// forward's output (same layout), and the denominators of the pieces' rows
-// (zero past the sequence).  The PPR lanes of a row (consecutive lanes of one
-// wave) reduce dO . out across the row; dd goes to dds[row], dn to the LDS
-// copy.
-template <typename T, typename SG>
-__device__ __forceinline__ void store_dn(const SG &g, const SG &o, const float (&den)[SG::NP], lds_t<T> *Gs,
-                                         float *dds) {
-    constexpr int VEC = 16 / (int)sizeof(T), PPR = SG::PPR, NT = SG::NT_;
-    static_assert(NT % PPR == 0 && 64 % PPR == 0, "a row's pieces lie in one wave");
-    typedef T tv __attribute__((__vector_size__(16)));
-    SG dn = g;
-#pragma unroll
-    for (int i = 0; i < SG::NP; ++i) {
-        const int p = (int)threadIdx.x + i * NT;
-        const tv gv = __builtin_bit_cast(tv, g.v[i]), ov = __builtin_bit_cast(tv, o.v[i]);
-        float acc = 0.f;
-#pragma unroll
-        for (int j = 0; j < VEC; ++j) acc += (float)gv[j] * (float)ov[j];
-#pragma unroll
-        for (int x = PPR / 2; x >= 1; x >>= 1) acc += __shfl_xor(acc, x, PPR);
-        const float inv = den[i] != 0.f ? 1.f / den[i] : 0.f;
-        tv nv;
-#pragma unroll
-        for (int j = 0; j < VEC; ++j) nv[j] = (T)((float)gv[j] * inv);
-        dn.v[i] = __builtin_bit_cast(i32x4, nv);
-        if (p % PPR == 0 && (SG::P % NT == 0 || p < SG::P)) dds[p / PPR] = -acc * inv;
-    }
-    dn.store(Gs);
-}
 
 // A k-contraction into NB accumulators that share one operand: acc(x) is the
 // x-th accumulator; fs(i) the shared operand (read once), fo(x, i) the x-th
@@ -234,62 +193,77 @@ __device__ __forceinline__ void bwd_sweep(const T *q_, const T *k_, const T *v_,
     constexpr int WS = E * M + E;
     const bool last_seg = sc.seg == sc.nseg - 1;
     const bool from_final = (!last_seg || (st && (!NORM || nin.zf))) && !EXACT_PREFIX;
-    // Over sequence segments (sc.dS != NULL, the causal product only) the
-    // starting states are sums of whole E x M tiles: all threads add them up
-    // with 16-byte loads into an fp32 tile in LDS (the ring buffers, not yet
-    // in use), from which each wave takes its fragments.  The dQ waves start
-    // at S after the segment (s0 plus the increments up to and including
-    // this segment's; the last segment: st) or, without it, at S before the
-    // segment for a pre-pass over the segment; the dK and dV waves at R after
-    // the segment (the later segments' increments).
+    // Over sequence segments (sc.dS != NULL) the starting states are sums of
+    // whole E x M tiles (and E-vectors of z, r): all threads add them up with
+    // 16-byte loads into an fp32 tile in LDS (the ring buffers, not in use
+    // then), from which each wave takes its fragments.  The dQ waves start at
+    // S, z after the segment (s0, z0 plus the increments up to and including
+    // this segment's; the last segment: st, zf) or, without them, at S, z
+    // before the segment for a pre-pass over the segment; the dK and dV waves
+    // at R, r after the segment (the later segments' increments).
     const bool staged = sc.dS != nullptr;
-    if (staged) {
-        constexpr int TS = M + 4;  // fp32 row stride of the tile (rows 16 bytes apart mod 128)
-        static_assert(E * TS * 4 <= 2 * BUF * (int)sizeof(lds_t<T>), "the carry tile fits the ring buffers");
-        float *tile = reinterpret_cast<float *>(lds);
+    constexpr int TS = M + 4;  // fp32 row stride of the tile (rows 16 bytes apart mod 128)
+    static_assert(E * TS * 4 + E * 4 <= 2 * BUF * (int)sizeof(lds_t<T>), "the carry tile fits the ring buffers");
+    auto stage_carries = [&](bool end) {
+        float *tile = reinterpret_cast<float *>(lds), *zvec = tile + E * TS;
         const int tid = (int)threadIdx.x;
-        const bool use_st = from_final && last_seg;
-        const int upto = from_final ? sc.seg + 1 : sc.seg;
-        for (int p = tid; p < E * M / 4; p += NT) {
-            const int e = p / (M / 4), m = p % (M / 4) * 4;
+        const bool use_st = end && last_seg;
+        const int upto = end ? sc.seg + 1 : sc.seg;
+        for (int p = tid; p < E * M / 4 + (NORM ? E / 4 : 0); p += NT) {
+            const bool zpart = p >= E * M / 4;  // the z vector's pieces follow the tile's
+            const int e = zpart ? 4 * (p - E * M / 4) : p / (M / 4), m = zpart ? 0 : p % (M / 4) * 4;
+            const int widx = zpart ? E * M + e : e * M + m;  // in an increment
+            const float *st_ = zpart ? nin.zf : st, *s0_ = zpart ? nin.z0 : s0;
+            const int64_t off = zpart ? e : (int64_t)e * Ma + m;
             const bool in = e < Ea && m < Ma;
             f32x4 a = zero4();
             if (use_st) {
-                if (in) a = *reinterpret_cast<const f32x4 *>(st + e * Ma + m);
+                if (in) a = *reinterpret_cast<const f32x4 *>(st_ + off);
             } else {
-                if (s0 && in) a = *reinterpret_cast<const f32x4 *>(s0 + e * Ma + m);
-                for (int s = 0; s < upto; ++s) a += *reinterpret_cast<const f32x4 *>(sc.dS + s * WS + e * M + m);
+                if (s0_ && in) a = *reinterpret_cast<const f32x4 *>(s0_ + off);
+                for (int s = 0; s < upto; ++s) a += *reinterpret_cast<const f32x4 *>(sc.dS + s * WS + widx);
             }
-            *reinterpret_cast<f32x4 *>(tile + e * TS + m) = a;
+            *reinterpret_cast<f32x4 *>(zpart ? zvec + e : tile + e * TS + m) = a;
         }
         __syncthreads();
         if constexpr (ROLE == kDQ) {
 #pragma unroll
-            for (int x = 0; x < NB; ++x)
+            for (int x = 0; x < NB; ++x) {
 #pragma unroll
                 for (int m = 0; m < MB; ++m)
 #pragma unroll
                     for (int t = 0; t < 4; ++t)
                         W[x][m][t] = tile[(16 * bk(x) + r) * TS + EM::ecol(m) + EM::estride * g + t];
+                if constexpr (NORM) {
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) zb[x][t] = zvec[16 * bk(x) + 4 * g + t];
+                }
+            }
         }
         __syncthreads();
-        if (!last_seg) {
-            for (int p = tid; p < E * M / 4; p += NT) {
-                const int e = p / (M / 4), m = p % (M / 4) * 4;
+        if (!last_seg) {  // (staged once per sweep: with the start or with the end state)
+            for (int p = tid; p < E * M / 4 + (NORM ? E / 4 : 0); p += NT) {
+                const bool zpart = p >= E * M / 4;
+                const int e = zpart ? 4 * (p - E * M / 4) : p / (M / 4), m = zpart ? 0 : p % (M / 4) * 4;
+                const int widx = zpart ? E * M + e : e * M + m;
                 f32x4 a = zero4();
-                for (int s = sc.seg + 1; s < sc.nseg; ++s)
-                    a += *reinterpret_cast<const f32x4 *>(sc.dR + s * WS + e * M + m);
-                *reinterpret_cast<f32x4 *>(tile + e * TS + m) = a;
+                for (int s = sc.seg + 1; s < sc.nseg; ++s) a += *reinterpret_cast<const f32x4 *>(sc.dR + s * WS + widx);
+                *reinterpret_cast<f32x4 *>(zpart ? zvec + e : tile + e * TS + m) = a;
             }
             __syncthreads();
             if constexpr (ROLE == kDK) {
 #pragma unroll
-                for (int x = 0; x < NB; ++x)
+                for (int x = 0; x < NB; ++x) {
 #pragma unroll
                     for (int m = 0; m < MB; ++m)
 #pragma unroll
                         for (int t = 0; t < 4; ++t)
                             W[x][m][t] = tile[(16 * bk(x) + r) * TS + EM::ecol(m) + EM::estride * g + t];
+                    if constexpr (NORM) {
+#pragma unroll
+                        for (int t = 0; t < 4; ++t) zb[x][t] = zvec[16 * bk(x) + 4 * g + t];
+                    }
+                }
             } else if constexpr (ROLE == kDV) {
 #pragma unroll
                 for (int x = 0; x < NB; ++x)
@@ -301,9 +275,15 @@ __device__ __forceinline__ void bwd_sweep(const T *q_, const T *k_, const T *v_,
             }
             __syncthreads();
         }
-    }
+    };
+    // the last segment without final states: a pre-pass over the segment
+    // from the staged states before it
+    const bool stage_early = staged && !from_final;
+    if (stage_early) stage_carries(false);
+    // pre-pass chunks: the whole sequence (segment) without final states; the
+    // restart rows at the start of the sequence (RESTART)
     constexpr int kPre = kRestartRows / C > 1 ? kRestartRows / C : 1;
-    const int npre = from_final ? (RESTART ? (n < kPre ? n : kPre) : 0) : n;
+    const int npre = from_final ? (RESTART && sc.seg == 0 ? (n < kPre ? n : kPre) : 0) : n;
     // the wave's parking slots: f32x4 per lane, MB state tiles then z, per block
     f32x4 *const park =
         RESTART && ROLE == kDQ ? reinterpret_cast<f32x4 *>(ddbuf + 2 * C) + (b / (G * NB)) * NB * (MB + 1) * 64
@@ -312,7 +292,7 @@ __device__ __forceinline__ void bwd_sweep(const T *q_, const T *k_, const T *v_,
         // forward pre-pass over chunks [0, npre): S^T[:, b] = S0^T[:, b] + the
         // chunks' V^T K[:, b] (NORM: and z = z_{-1} + their column sums)
         if constexpr (ROLE == kDQ) {
-            if (s0 && !staged) {
+            if (s0 && !stage_early) {
 #pragma unroll
                 for (int x = 0; x < NB; ++x)
 #pragma unroll
@@ -322,7 +302,7 @@ __device__ __forceinline__ void bwd_sweep(const T *q_, const T *k_, const T *v_,
                             W[x][m][t] = state_at(s0, 16 * bk(x) + r, EM::ecol(m) + EM::estride * g + t, Ea, Ma);
             }
             if constexpr (NORM) {
-                if (nin.z0) {
+                if (nin.z0 && !stage_early) {
 #pragma unroll
                     for (int x = 0; x < NB; ++x)
 #pragma unroll
@@ -381,15 +361,22 @@ __device__ __forceinline__ void bwd_sweep(const T *q_, const T *k_, const T *v_,
         }
         __syncthreads();  // the main sweep reuses the buffers
     }
-    if (from_final && !staged) {
-        if constexpr (ROLE == kDQ) {
+    if (from_final) {
+        if constexpr (RESTART && ROLE == kDQ) {
+            if (npre > 0) {
 #pragma unroll
-            for (int x = 0; x < NB; ++x) {
-                if constexpr (RESTART) {
+                for (int x = 0; x < NB; ++x) {
 #pragma unroll
                     for (int m = 0; m < MB; ++m) park[(x * (MB + 1) + m) * 64 + lane_id()] = W[x][m];
                     park[(x * (MB + 1) + MB) * 64 + lane_id()] = zb[x];
                 }
+            }
+        }
+        if (staged) {
+            stage_carries(true);
+        } else if constexpr (ROLE == kDQ) {
+#pragma unroll
+            for (int x = 0; x < NB; ++x) {
 #pragma unroll
                 for (int m = 0; m < MB; ++m)
 #pragma unroll
@@ -462,7 +449,7 @@ __device__ __forceinline__ void bwd_sweep(const T *q_, const T *k_, const T *v_,
             f32x4 pend[NB][CB];  // this chunk's output tiles (rows 16 I + r) per column block
             if constexpr (ROLE == kDQ) {
                 if constexpr (RESTART) {  // S_c, z_c of the pre-pass (see RESTART)
-                    if (from_final && row0 == (npre - 1) * C) {
+                    if (from_final && npre > 0 && row0 == (npre - 1) * C) {
 #pragma unroll
                         for (int x = 0; x < NB; ++x) {
 #pragma unroll

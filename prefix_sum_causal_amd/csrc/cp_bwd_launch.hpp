@@ -15,11 +15,12 @@ namespace cp {
 // normaliser before each chunk) are formed inside the sweep from the
 // forward's output, denominators and final (or initial) normaliser.
 //
-// Few slices (the causal product): each slice is cut into nseg sequence
-// segments of seg_len rows (a multiple of C) and run in two launches, the
-// scan's carry one level up, as in the forward.  The first computes every
-// segment's increments of the prefix state (sum of k v^T, all but the last
-// segment) and of the suffix state (sum of q dO^T, all but the first) into a
+// Few slices: each slice is cut into nseg sequence segments of seg_len rows
+// (a multiple of C) and run in two launches, the scan's carry one level up,
+// as in the forward.  The first computes every segment's increments of the
+// prefix state (sum of k v^T, all but the last segment; normalised form: with
+// the sum of phi(k)) and of the suffix state (sum of q dO^T, all but the
+// first; normalised form: of phi(q) dn^T, with the sum of dd phi(q)) into a
 // stream-ordered scratch buffer; the second sweeps each segment with the
 // states at its ends summed from those increments (see SegCarry).
 template <typename T, int E, int M, bool NORM, bool FMAP>
@@ -33,7 +34,7 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t s) {
     float *ds0 = a.dstate_in, *dz0 = a.dz_in;
     int L = a.L, NS = a.NS, Ea = a.Ea, Ma = a.Ma;
 
-    const int nseg0 = NORM ? 1 : seq_segments(L, NS, P::BG * P::BRG, C, kBwdSegWgPerCU);
+    const int nseg0 = seq_segments(L, NS, P::BG * P::BRG, C, kBwdSegWgPerCU);
     const int nchunks = (L + C - 1) / C;
     int seg_len = (nchunks + nseg0 - 1) / nseg0 * C;
     const int nseg = (L + seg_len - 1) / seg_len;
@@ -44,7 +45,7 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t s) {
         constexpr int WS = E * M + E;
         e = hipMallocAsync(reinterpret_cast<void **>(&ws), (size_t)2 * NS * nseg * WS * sizeof(float), s);
         if (e != hipSuccess) return e;
-        const SegArgs sa{k, v, ws, q, g, ws + (size_t)NS * nseg * WS, L, NS, seg_len, Ea, Ma};
+        const SegArgs sa{k, v, ws, q, g, o, den, ws + (size_t)NS * nseg * WS, L, NS, seg_len, Ea, Ma, NORM, FMAP};
         const seg_fn fn = std::is_same<T, float>::value ? seg_f32(E, M)
                           : std::is_same<T, __bf16>::value ? seg_bf16(E, M)
                                                            : seg_f16(E, M);

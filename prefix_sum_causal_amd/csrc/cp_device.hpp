@@ -376,6 +376,47 @@ struct Stage {
     }
 };
 
+// The normalised form's extra inputs of one slice: the forward's output and
+// denominators (the backward turns dO into dn = dO / den and dd = -(dO . out)
+// / den while staging it), the final normaliser z_{L-1} (optional) and the
+// initial one z_{-1} (optional).
+template <typename T> struct NormIn {
+    const T *o;
+    const float *den;
+    const float *zf, *z0;
+};
+
+// The dn rows of a staged dO chunk and their dd: the pieces of dO and of the
+// forward's output (same layout), and the denominators of the pieces' rows
+// (zero past the sequence).  The PPR lanes of a row (consecutive lanes of one
+// wave) reduce dO . out across the row; dd goes to dds[row], dn to the LDS
+// copy.
+template <typename T, typename SG>
+__device__ __forceinline__ void store_dn(const SG &g, const SG &o, const float (&den)[SG::NP], lds_t<T> *Gs,
+                                         float *dds) {
+    constexpr int VEC = 16 / (int)sizeof(T), PPR = SG::PPR, NT = SG::NT_;
+    static_assert(NT % PPR == 0 && 64 % PPR == 0, "a row's pieces lie in one wave");
+    typedef T tv __attribute__((__vector_size__(16)));
+    SG dn = g;
+#pragma unroll
+    for (int i = 0; i < SG::NP; ++i) {
+        const int p = (int)threadIdx.x + i * NT;
+        const tv gv = __builtin_bit_cast(tv, g.v[i]), ov = __builtin_bit_cast(tv, o.v[i]);
+        float acc = 0.f;
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) acc += (float)gv[j] * (float)ov[j];
+#pragma unroll
+        for (int x = PPR / 2; x >= 1; x >>= 1) acc += __shfl_xor(acc, x, PPR);
+        const float inv = den[i] != 0.f ? 1.f / den[i] : 0.f;
+        tv nv;
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) nv[j] = (T)((float)gv[j] * inv);
+        dn.v[i] = __builtin_bit_cast(i32x4, nv);
+        if (p % PPR == 0 && (SG::P % NT == 0 || p < SG::P)) dds[p / PPR] = -acc * inv;
+    }
+    dn.store(Gs);
+}
+
 // Causal masks of a diagonal 16x16 tile.  Lane (g, r) holds rows 4g + t of
 // column r; the keep-predicates depend on the lane only and are computed once.
 struct Diag {

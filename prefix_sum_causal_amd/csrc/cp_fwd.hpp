@@ -293,14 +293,22 @@ __device__ __forceinline__ void fwd_sweep(const T *q_, const T *k_, const T *v_,
 // CW column blocks of M (and of its share of the E/16 tiles of dz, as K^T 1).
 // The segments' increments are independent of each other, so this pass runs
 // at the rate of its two input streams; the last segment's increment is never
-// needed and not computed.  An optional second job (K2 != NULL: the backward's
-// suffix carries, sum_j q_j dO_j^T) runs in the same launch, over segments 1
-// .. nseg-1 (the first one's is never needed), into ws2.
+// needed and not computed.
+//
+// An optional second job (K2 != NULL) runs in the same launch, over segments
+// 1 .. nseg-1 (the first one's is never needed), into ws2: the backward's
+// suffix carries.  Causal product: dR = sum_i q_i dO_i^T (K2 = Q, V2 = dO).
+// Normalised form: dR = sum_i phi(q_i) dn_i^T and dr = sum_i dd_i phi(q_i),
+// with dn_i = dO_i / den_i and dd_i = -(dO_i . out_i) / den_i formed while dO
+// is staged (O2, den2: the forward's output and denominators), dd entering
+// the product K2^T dd as a hi + lo pair of operands.
 template <typename T, int E, int M, int C, int NW, int NPF, bool NORM, bool FMAP>
 __global__ __launch_bounds__(64 * NW) void cp_seg_state_kernel(const T *__restrict__ K1, const T *__restrict__ V1,
                                                                float *__restrict__ ws1, const T *__restrict__ K2,
-                                                               const T *__restrict__ V2, float *__restrict__ ws2,
-                                                               int L, int NS, int seg_len, int Ea, int Ma) {
+                                                               const T *__restrict__ V2, const T *__restrict__ O2,
+                                                               const float *__restrict__ den2,
+                                                               float *__restrict__ ws2, int L, int NS, int seg_len,
+                                                               int Ea, int Ma) {
     using O = Ops<T>;
     using F = typename O::frag;
     using EO = EOps<T, E>;
@@ -312,9 +320,10 @@ __global__ __launch_bounds__(64 * NW) void cp_seg_state_kernel(const T *__restri
     constexpr int RK = SK::RS, RV = SV::RS;
     constexpr int BUF = C * RK + C * RV;
     constexpr int WS = E * M + E;
+    constexpr int DDE = NORM ? 2 * C * 4 / (int)sizeof(lds_t<T>) : 0;  // two chunks of dd (second job)
     // dz tiles (e-tiles of K^T 1) dealt round robin to the waves
     constexpr int ZT = (EB + NW - 1) / NW;
-    __shared__ __attribute__((aligned(16))) lds_t<T> lds[2 * BUF];
+    __shared__ __attribute__((aligned(16))) lds_t<T> lds[2 * BUF + DDE];
 
     const int nseg = (L + seg_len - 1) / seg_len;
     int slice, part;
@@ -328,6 +337,14 @@ __global__ __launch_bounds__(64 * NW) void cp_seg_state_kernel(const T *__restri
     const T *k_ = K + (int64_t)slice * L * Ea;
     const T *v_ = V + (int64_t)slice * L * Ma;
     const int rb = seg * seg_len, re = rb + seg_len < L ? rb + seg_len : L;
+    // normalised second job: dn and dd from dO (v_), the output and den
+    const bool dnj = NORM && second;
+    NormIn<T> nin{nullptr, nullptr, nullptr, nullptr};
+    if (dnj) {
+        nin.o = O2 + (int64_t)slice * L * Ma;
+        nin.den = den2 + (int64_t)slice * L;
+    }
+    float *const ddbuf = reinterpret_cast<float *>(lds + 2 * BUF);
 
     f32x4 S[CW][EB], Z[ZT];
 #pragma unroll
@@ -340,12 +357,30 @@ __global__ __launch_bounds__(64 * NW) void cp_seg_state_kernel(const T *__restri
     struct Stages {
         SK k;
         SV v;
+        SV o;
+        float den[NORM ? SV::NP : 1];
+        __device__ __forceinline__ void load(const T *k_, const T *v_, NormIn<T> nin, bool dnj, int row0, int re,
+                                             int Ea, int Ma) {
+            k.load(Rows<T>(k_, Ea, row0, re, C), 0, Ea);
+            v.load(Rows<T>(v_, Ma, row0, re, C), 0, Ma);
+            if constexpr (NORM) {
+                if (dnj) {
+                    o.load(Rows<T>(nin.o, Ma, row0, re, C), 0, Ma);
+                    const Rows<float> rd(nin.den, 1, row0, re, C);
+#pragma unroll
+                    for (int i = 0; i < SV::NP; ++i) {
+                        const int p = (int)threadIdx.x + i * NT;
+                        den[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                               rd.rsrc, p < SV::P ? 4 * (p / SV::PPR) : kVoid, 0, 0));
+                    }
+                }
+            }
+        }
     };
     Stages st[NPF];
 #pragma unroll
     for (int i = 0; i < NPF - 1; ++i) {
-        st[i].k.load(Rows<T>(k_, Ea, rb + i * C, re, C), 0, Ea);
-        st[i].v.load(Rows<T>(v_, Ma, rb + i * C, re, C), 0, Ma);
+        st[i].load(k_, v_, nin, dnj, rb + i * C, re, Ea, Ma);
         __builtin_amdgcn_sched_barrier(0);  // stages complete in order
     }
     const int nchunks = (re - rb + C - 1) / C;
@@ -356,19 +391,39 @@ __global__ __launch_bounds__(64 * NW) void cp_seg_state_kernel(const T *__restri
             const int c = c0 + i;
             const int row0 = rb + c * C;
             lds_t<T> *Ks = lds + (c & 1) * BUF, *Vs = Ks + C * RK;
+            float *dds = ddbuf + (c & 1) * C;
             st[i].k.template store<NORM && FMAP>(Ks, row0, re, Ea);
-            st[i].v.store(Vs);
+            if constexpr (NORM) {
+                if (dnj) store_dn<T>(st[i].v, st[i].o, st[i].den, Vs, dds);
+                else st[i].v.store(Vs);
+            } else {
+                st[i].v.store(Vs);
+            }
             __syncthreads();
             Stages &nx = st[(i + NPF - 1) % NPF];
-            const int nrow0 = row0 + (NPF - 1) * C;
-            nx.k.load(Rows<T>(k_, Ea, nrow0, re, C), 0, Ea);
-            nx.v.load(Rows<T>(v_, Ma, nrow0, re, C), 0, Ma);
+            nx.load(k_, v_, nin, dnj, row0 + (NPF - 1) * C, re, Ea, Ma);
             __builtin_amdgcn_sched_barrier(0);
             F vt[CW][CB];  // V_J^T fragments of the wave's column blocks
 #pragma unroll
             for (int x = 0; x < CW; ++x)
 #pragma unroll
                 for (int J = 0; J < CB; ++J) vt[x][J] = O::tr_frag(Vs, RV, J, w * CW + x);
+            // dz: the ones column; the normalised second job's dr: dd (hi + lo)
+            F zh[CB], zl[CB];
+            if constexpr (NORM) {
+#pragma unroll
+                for (int J = 0; J < CB; ++J) {
+                    if (dnj) {
+                        f32x4 x;
+#pragma unroll
+                        for (int t = 0; t < 4; ++t) x[t] = dds[16 * J + 4 * g + t];
+                        O::split(x, zh[J], zl[J]);
+                    } else {
+                        zh[J] = O::ones();
+                        zl[J] = O::zero();
+                    }
+                }
+            }
 #pragma unroll
             for (int e = 0; e < EB; ++e) {
                 F kt[CB];  // K^T fragments of e-tile e, shared by the column blocks
@@ -377,7 +432,11 @@ __global__ __launch_bounds__(64 * NW) void cp_seg_state_kernel(const T *__restri
 #pragma unroll
                 for (int x = 0; x < CW; ++x) dotk<T>(S[x][e], 0, CB, [&](int J) { return kt[J]; }, [&](int J) { return vt[x][J]; });
                 if constexpr (NORM)
-                    if (e % NW == w) dotk<T>(Z[e / NW], 0, CB, [&](int J) { return kt[J]; }, [&](int) { return O::ones(); });
+                    if (e % NW == w) {
+                        dotk<T>(Z[e / NW], 0, CB, [&](int J) { return kt[J]; }, [&](int J) { return zh[J]; });
+                        if constexpr (sizeof(T) == 2)
+                            if (dnj) dotk<T>(Z[e / NW], 0, CB, [&](int J) { return kt[J]; }, [&](int J) { return zl[J]; });
+                    }
             }
         }
     }

@@ -49,8 +49,9 @@ hipError_t launch_fwd_t(const FwdArgs &a, hipStream_t s) {
         constexpr int SW = seg_state_waves<M>();
         auto k1 = cp_seg_state_kernel<T, E, M, P::FC, SW, CP_SEG_NPF, NORM, FMAP>;
         const T *none = nullptr;
+        const float *noden = nullptr;
         float *nows = nullptr;
-        void *args1[] = {&k, &v, &ws, &none, &none, &nows, &L, &NS, &seg_len, &Ea, &Ma};
+        void *args1[] = {&k, &v, &ws, &none, &none, &none, &noden, &nows, &L, &NS, &seg_len, &Ea, &Ma};
         e = launch_kernel(reinterpret_cast<const void *>(k1), dim3(NS * (nseg - 1)), dim3(64 * SW), args1, s);
     } else {
         seg_len = L;
@@ -89,19 +90,29 @@ fwd_fn pick_fwd(int E, int M) {
     return (ie < 0 || im < 0) ? nullptr : table[ie][im];
 }
 
-// The backward's two-job segment-increment pass (see SegArgs).
-template <typename T, int E, int M>
-hipError_t launch_seg_t(const SegArgs &a, hipStream_t s) {
+// The backward's two-job segment-increment pass (see SegArgs), on the
+// forward's instances of the kernel.
+template <typename T, int E, int M, bool NORM, bool FMAP>
+hipError_t launch_seg_nf(const SegArgs &a, hipStream_t s) {
+    using P = Tune<T, E, M>;
     const T *k1 = static_cast<const T *>(a.K1), *v1 = static_cast<const T *>(a.V1);
-    const T *k2 = static_cast<const T *>(a.K2), *v2 = static_cast<const T *>(a.V2);
+    const T *k2 = static_cast<const T *>(a.K2), *v2 = static_cast<const T *>(a.V2), *o2 = static_cast<const T *>(a.O2);
+    const float *den2 = a.den2;
     float *ws1 = a.ws1, *ws2 = a.ws2;
     int L = a.L, NS = a.NS, seg_len = a.seg_len, Ea = a.Ea, Ma = a.Ma;
     const int nseg = (L + seg_len - 1) / seg_len;
     constexpr int SW = seg_state_waves<M>();
-    auto kern = cp_seg_state_kernel<T, E, M, 64, SW, CP_SEG_NPF, false, false>;
-    void *args[] = {&k1, &v1, &ws1, &k2, &v2, &ws2, &L, &NS, &seg_len, &Ea, &Ma};
+    auto kern = cp_seg_state_kernel<T, E, M, P::FC, SW, CP_SEG_NPF, NORM, FMAP>;
+    void *args[] = {&k1, &v1, &ws1, &k2, &v2, &o2, &den2, &ws2, &L, &NS, &seg_len, &Ea, &Ma};
     return launch_kernel(reinterpret_cast<const void *>(kern), dim3(NS * (k2 ? 2 : 1) * (nseg - 1)), dim3(64 * SW),
                          args, s);
+}
+
+template <typename T, int E, int M>
+hipError_t launch_seg_t(const SegArgs &a, hipStream_t s) {
+    if (!a.norm) return launch_seg_nf<T, E, M, false, false>(a, s);
+    if (a.fmap) return launch_seg_nf<T, E, M, true, true>(a, s);
+    return launch_seg_nf<T, E, M, true, false>(a, s);
 }
 
 template <typename T>

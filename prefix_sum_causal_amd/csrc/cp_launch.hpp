@@ -86,14 +86,18 @@ typedef hipError_t (*fwd_fn)(const FwdArgs &, hipStream_t);
 typedef hipError_t (*bwd_fn)(const BwdArgs &, hipStream_t);
 
 // The backward's segment-increment pass (cp_seg_state_kernel with two jobs:
-// sum k v^T over segments 0 .. nseg-2 into ws1, sum q dO^T over segments
+// the prefix increments, sum k v^T (and of k), over segments 0 .. nseg-2
+// into ws1; the suffix increments, sum q dO^T (normalised form: of phi(q)
+// dn^T, and of dd phi(q), from the output O2 and den2), over segments
 // 1 .. nseg-1 into ws2); its instances live with the forward's.
 struct SegArgs {
     const void *K1, *V1;
     float *ws1;
-    const void *K2, *V2;
+    const void *K2, *V2, *O2;
+    const float *den2;
     float *ws2;
     int L, NS, seg_len, Ea, Ma;
+    bool norm, fmap;
 };
 typedef hipError_t (*seg_fn)(const SegArgs &, hipStream_t);
 seg_fn seg_f32(int E, int M);

@@ -234,3 +234,26 @@ def test_row_error_profile(cp, orc, dtype):
             print(f"ROWERR {dtype} {name} {band}: band {e.max() / r.max():.2e} worst row {row.max():.2e}",
                   flush=True)
         check(got, ref, dtype, f"{name} {dtype}")
+
+
+SEG_SHAPES = [(1, 2, 3001, 64, 64, "f32"), (1, 2, 3001, 64, 64, "bf16"), (2, 1, 2500, 32, 128, "bf16"),
+              (1, 1, 4133, 128, 128, "bf16"), (1, 3, 700, 64, 32, "f32")]
+
+
+@pytest.mark.parametrize("shape", SEG_SHAPES, ids=[str(s) for s in SEG_SHAPES])
+def test_linattn_bwd_segmented(cp, orc, shape):
+    """Few slices over long rows: the normalised backward runs over sequence
+    segments (segment increments of S, z and of R, r, then per-segment
+    sweeps), from initial states, with the final states and through the
+    pre-pass; all gradients against the oracle."""
+    N, H, L, E, M, dtype = shape
+    d = inputs((N, H, L, E, M), dtype, seed=27 + L, fm=1, carry=True)
+    q, k, v, out, st, zt, den, s0, z0 = forward(cp, d, dtype, 1)
+    g = dev(d["dO"], dtype)
+    ref = orc.linattn_bwd(d["Q"], d["K"], d["V"], d["dO"], 1e-6, 1, S0=d["S0"], z0=d["z0"])
+    for label, kw in (("final states", dict(state_final=st, z_final=zt)), ("pre-pass", {})):
+        ds0, dz0 = torch.empty_like(st), torch.empty_like(zt)
+        got = cp.linear_attn_bwd(q, k, v, out, g, den, 1, state_in=s0, z_in=z0, dstate_in=ds0, dz_in=dz0, **kw)
+        torch.cuda.synchronize()
+        for t, r, name in zip(list(got) + [ds0, dz0], ref, ("dq", "dk", "dv", "dS0", "dz0")):
+            check(host(t), r, dtype, f"{name} ({label}) {shape}")

@@ -55,8 +55,9 @@ class Workload:
 # forward+backward at L=4096 E=M=64 (the headline), bf16 normalised linear
 # attention at L=16384 E=M=128, an fp32 forward+backward with E != M, and the
 # normalised form's forward+backward in bf16 at the headline shape; the
-# headline shape in fp16 and with 80-wide heads; the forward+backward at the
-# normalised workload's few-slice long-row shape.
+# headline shape in fp16 and with 80-wide heads; the forward+backward of the
+# causal product and of the normalised form at the normalised workload's
+# few-slice long-row shape.
 WORKLOADS = {
     w.name: w
     for w in (
@@ -76,6 +77,8 @@ WORKLOADS = {
         # few slices over long rows (16 slices of 16384 rows, 128-wide heads):
         # forward and backward both run over sequence segments
         Workload("fwdbwd_bf16_l16384_e128", "fwd+bwd", "bf16", 2, 8, 16384, 128, 128, seed=8),
+        Workload("linattn_fwdbwd_bf16_l16384_e128", "linattn+bwd", "bf16", 2, 8, 16384, 128, 128, seed=9,
+                 qk="raw"),
     )
 }
 HEADLINE = "fwdbwd_bf16_l4096_e64"
