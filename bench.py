@@ -33,9 +33,16 @@ MFMA_PEAK_TFS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}
 METRIC = "causal-product fwd+bwd tokens·heads/s and % HBM/MFMA roofline, L=4096 E=M=64"
 UNIT = "tokens·heads/s"
 COUNTERS = os.path.join(ROOT, "profiles", "hbm_traffic.json")
-KERNEL_SOURCES = ("cp_device.hpp", "cp_fwd.hpp", "cp_fwd_launch.hpp", "cp_bwd.hpp", "cp_bwd_launch.hpp", "cp_tune.hpp")
-KERNEL_NAME = {"fwd": "cp_fwd_kernel", "bwd": "cp_bwd_kernel", "linattn": "cp_fwd_kernel",
-               "linattn_bwd": "cp_lin_prep_kernel + cp_lin_zscan_kernel + cp_bwd_kernel"}
+KERNEL_SOURCES = ("cp_device.hpp", "cp_fwd.hpp", "cp_fwd_launch.hpp", "cp_bwd.hpp", "cp_bwd_launch.hpp", "cp_tune.hpp",
+                  "cp_launch.hpp")
+# the sweep kernel of each call; over few slices a call is two launches, the
+# segment-increment pass and then the sweeps
+SWEEP_KERNEL = {"fwd": "cp_fwd_kernel", "bwd": "cp_bwd_kernel", "linattn": "cp_fwd_kernel",
+                "linattn_bwd": "cp_bwd_kernel"}
+
+
+def kernel_name(kind: str, launches: int) -> str:
+    return SWEEP_KERNEL[kind] if launches == 1 else "cp_seg_state_kernel + " + SWEEP_KERNEL[kind]
 
 
 def kernel_digest() -> str:
@@ -252,10 +259,9 @@ def main() -> int:
 
     # Per-kernel durations: the same K steps again, each launch with its own
     # start/end events (the timestamps of its dispatch on the stream it runs
-    # on, as a profiler's kernel trace reports them).  Launches per call: a
-    # forward over few slices is two launches (segment states, then the
-    # sweep), the normalised backward three (per-row terms, z scan, sweep);
-    # count them on one untimed step.
+    # on, as a profiler's kernel trace reports them).  Launches per call: one,
+    # or over few slices two (the segments' state increments, then the
+    # sweeps); count them on one untimed step.
     n_launch = []
     for c in calls:
         cp.timing_begin(64)
@@ -310,9 +316,10 @@ def main() -> int:
     hbm_frac = achieved / HBM_PEAK_GBS
     mfma_peak = MFMA_PEAK_TFS[w.dtype]
     mfma_frac = per_kernel[dom]["TFps"] / mfma_peak
-    hbm = {"bound": "hbm", "kernel": KERNEL_NAME[dom], "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+    kname = kernel_name(dom, n_launch[kinds.index(dom)])
+    hbm = {"bound": "hbm", "kernel": kname, "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
            "frac": hbm_frac, "traffic": traffic_for(dom, name), "frac_of_copy": achieved / copy["GBps"]}
-    mfma = {"bound": "mfma", "kernel": KERNEL_NAME[dom], "achieved": per_kernel[dom]["TFps"], "peak": mfma_peak,
+    mfma = {"bound": "mfma", "kernel": kname, "achieved": per_kernel[dom]["TFps"], "peak": mfma_peak,
             "unit": "TFLOP/s", "frac": mfma_frac}
     roof = dict(hbm if hbm_frac >= mfma_frac else mfma)
     roof["other"] = mfma if roof["bound"] == "hbm" else hbm
