@@ -192,22 +192,26 @@ __device__ __forceinline__ void bwd_sweep(const T *q_, const T *k_, const T *v_,
     constexpr bool RESTART = NORM && !EXACT_PREFIX;
     constexpr int WS = E * M + E;
     const bool last_seg = sc.seg == sc.nseg - 1;
-    const bool from_final = (!last_seg || (st && (!NORM || nin.zf))) && !EXACT_PREFIX;
+    // the final states given (and used: not with fp32 I/O in the normalised form)
+    const bool use_final = st && (!NORM || nin.zf) && !EXACT_PREFIX;
+    const bool from_final = (!last_seg || use_final) && !EXACT_PREFIX;
     // Over sequence segments (sc.dS != NULL) the starting states are sums of
     // whole E x M tiles (and E-vectors of z, r): all threads add them up with
     // 16-byte loads into an fp32 tile in LDS (the ring buffers, not in use
     // then), from which each wave takes its fragments.  The dQ waves start at
-    // S, z after the segment (s0, z0 plus the increments up to and including
-    // this segment's; the last segment: st, zf) or, without them, at S, z
-    // before the segment for a pre-pass over the segment; the dK and dV waves
-    // at R, r after the segment (the later segments' increments).
+    // S, z after the segment: with the final states, st, zf minus the later
+    // segments' increments (the increment pass then covers segments 1 ..
+    // nseg-1, and s0, z0 are not needed); without them, s0, z0 plus the
+    // increments up to and including this segment's (segments 0 .. nseg-2),
+    // the last segment starting before itself for a pre-pass over it.  The
+    // dK and dV waves start at R, r after the segment (the later segments'
+    // increments).
     const bool staged = sc.dS != nullptr;
     constexpr int TS = M + 4;  // fp32 row stride of the tile (rows 16 bytes apart mod 128)
     static_assert(E * TS * 4 + E * 4 <= 2 * BUF * (int)sizeof(lds_t<T>), "the carry tile fits the ring buffers");
     auto stage_carries = [&](bool end) {
         float *tile = reinterpret_cast<float *>(lds), *zvec = tile + E * TS;
         const int tid = (int)threadIdx.x;
-        const bool use_st = end && last_seg;
         const int upto = end ? sc.seg + 1 : sc.seg;
         for (int p = tid; p < E * M / 4 + (NORM ? E / 4 : 0); p += NT) {
             const bool zpart = p >= E * M / 4;  // the z vector's pieces follow the tile's
@@ -217,8 +221,9 @@ __device__ __forceinline__ void bwd_sweep(const T *q_, const T *k_, const T *v_,
             const int64_t off = zpart ? e : (int64_t)e * Ma + m;
             const bool in = e < Ea && m < Ma;
             f32x4 a = zero4();
-            if (use_st) {
+            if (use_final) {  // (only ever with end)
                 if (in) a = *reinterpret_cast<const f32x4 *>(st_ + off);
+                for (int s = sc.seg + 1; s < sc.nseg; ++s) a -= *reinterpret_cast<const f32x4 *>(sc.dS + s * WS + widx);
             } else {
                 if (s0_ && in) a = *reinterpret_cast<const f32x4 *>(s0_ + off);
                 for (int s = 0; s < upto; ++s) a += *reinterpret_cast<const f32x4 *>(sc.dS + s * WS + widx);

@@ -45,7 +45,11 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t s) {
         constexpr int WS = E * M + E;
         e = hipMallocAsync(reinterpret_cast<void **>(&ws), (size_t)2 * NS * nseg * WS * sizeof(float), s);
         if (e != hipSuccess) return e;
-        const SegArgs sa{k, v, ws, q, g, o, den, ws + (size_t)NS * nseg * WS, L, NS, seg_len, Ea, Ma, NORM, FMAP};
+        // with the final states used, the sweeps subtract the later segments'
+        // increments from them: the prefix increments of segments 1 .. nseg-1
+        const bool use_final = st && (!NORM || zf) && !(NORM && std::is_same<T, float>::value);
+        const SegArgs sa{k,  v,  ws,      q,  g,  o,  den, ws + (size_t)NS * nseg * WS, L, NS, seg_len,
+                         use_final ? 1 : 0, Ea, Ma, NORM, FMAP};
         const seg_fn fn = std::is_same<T, float>::value ? seg_f32(E, M)
                           : std::is_same<T, __bf16>::value ? seg_bf16(E, M)
                                                            : seg_f16(E, M);

@@ -295,7 +295,10 @@ __device__ __forceinline__ void fwd_sweep(const T *q_, const T *k_, const T *v_,
 // at the rate of its two input streams; the last segment's increment is never
 // needed and not computed.
 //
-// An optional second job (K2 != NULL) runs in the same launch, over segments
+// The first job covers segments first1 .. first1 + nseg - 2 (first1 = 1: the
+// backward from the final state, which subtracts the later segments'
+// increments from it).  An optional second job (K2 != NULL) runs in the same
+// launch, over segments
 // 1 .. nseg-1 (the first one's is never needed), into ws2: the backward's
 // suffix carries.  Causal product: dR = sum_i q_i dO_i^T (K2 = Q, V2 = dO).
 // Normalised form: dR = sum_i phi(q_i) dn_i^T and dr = sum_i dd_i phi(q_i),
@@ -308,7 +311,7 @@ __global__ __launch_bounds__(64 * NW) void cp_seg_state_kernel(const T *__restri
                                                                const T *__restrict__ V2, const T *__restrict__ O2,
                                                                const float *__restrict__ den2,
                                                                float *__restrict__ ws2, int L, int NS, int seg_len,
-                                                               int Ea, int Ma) {
+                                                               int first1, int Ea, int Ma) {
     using O = Ops<T>;
     using F = typename O::frag;
     using EO = EOps<T, E>;
@@ -329,7 +332,7 @@ __global__ __launch_bounds__(64 * NW) void cp_seg_state_kernel(const T *__restri
     int slice, part;
     map_block(blockIdx.x, NS, (K2 ? 2 : 1) * (nseg - 1), slice, part);
     const bool second = part >= nseg - 1;
-    const int seg = second ? part - (nseg - 1) + 1 : part;
+    const int seg = second ? part - (nseg - 1) + 1 : part + first1;
     const T *K = second ? K2 : K1, *V = second ? V2 : V1;
     float *ws = second ? ws2 : ws1;
     const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);

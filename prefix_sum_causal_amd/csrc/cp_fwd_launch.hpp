@@ -51,7 +51,8 @@ hipError_t launch_fwd_t(const FwdArgs &a, hipStream_t s) {
         const T *none = nullptr;
         const float *noden = nullptr;
         float *nows = nullptr;
-        void *args1[] = {&k, &v, &ws, &none, &none, &none, &noden, &nows, &L, &NS, &seg_len, &Ea, &Ma};
+        int first1 = 0;
+        void *args1[] = {&k, &v, &ws, &none, &none, &none, &noden, &nows, &L, &NS, &seg_len, &first1, &Ea, &Ma};
         e = launch_kernel(reinterpret_cast<const void *>(k1), dim3(NS * (nseg - 1)), dim3(64 * SW), args1, s);
     } else {
         seg_len = L;
@@ -99,11 +100,11 @@ hipError_t launch_seg_nf(const SegArgs &a, hipStream_t s) {
     const T *k2 = static_cast<const T *>(a.K2), *v2 = static_cast<const T *>(a.V2), *o2 = static_cast<const T *>(a.O2);
     const float *den2 = a.den2;
     float *ws1 = a.ws1, *ws2 = a.ws2;
-    int L = a.L, NS = a.NS, seg_len = a.seg_len, Ea = a.Ea, Ma = a.Ma;
+    int L = a.L, NS = a.NS, seg_len = a.seg_len, first1 = a.first1, Ea = a.Ea, Ma = a.Ma;
     const int nseg = (L + seg_len - 1) / seg_len;
     constexpr int SW = seg_state_waves<M>();
     auto kern = cp_seg_state_kernel<T, E, M, P::FC, SW, CP_SEG_NPF, NORM, FMAP>;
-    void *args[] = {&k1, &v1, &ws1, &k2, &v2, &o2, &den2, &ws2, &L, &NS, &seg_len, &Ea, &Ma};
+    void *args[] = {&k1, &v1, &ws1, &k2, &v2, &o2, &den2, &ws2, &L, &NS, &seg_len, &first1, &Ea, &Ma};
     return launch_kernel(reinterpret_cast<const void *>(kern), dim3(NS * (k2 ? 2 : 1) * (nseg - 1)), dim3(64 * SW),
                          args, s);
 }

@@ -86,8 +86,8 @@ typedef hipError_t (*fwd_fn)(const FwdArgs &, hipStream_t);
 typedef hipError_t (*bwd_fn)(const BwdArgs &, hipStream_t);
 
 // The backward's segment-increment pass (cp_seg_state_kernel with two jobs:
-// the prefix increments, sum k v^T (and of k), over segments 0 .. nseg-2
-// into ws1; the suffix increments, sum q dO^T (normalised form: of phi(q)
+// the prefix increments, sum k v^T (and of k), over segments first1 ..
+// first1 + nseg-2 into ws1; the suffix increments, sum q dO^T (normalised form: of phi(q)
 // dn^T, and of dd phi(q), from the output O2 and den2), over segments
 // 1 .. nseg-1 into ws2); its instances live with the forward's.
 struct SegArgs {
@@ -96,7 +96,7 @@ struct SegArgs {
     const void *K2, *V2, *O2;
     const float *den2;
     float *ws2;
-    int L, NS, seg_len, Ea, Ma;
+    int L, NS, seg_len, first1, Ea, Ma;
     bool norm, fmap;
 };
 typedef hipError_t (*seg_fn)(const SegArgs &, hipStream_t);
