@@ -57,7 +57,7 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t s) {
     }
     if (e == hipSuccess) {
         const float *wsc = ws;
-        auto kern = cp_bwd_kernel<T, E, M, C, P::BG, P::BNB, P::BIDLE, P::BRG, P::BNPF, NORM, FMAP>;
+        auto kern = cp_bwd_kernel<T, E, M, C, P::BG, P::BNB, P::BIDLE, P::BRG, NORM ? P::BNPF_N : P::BNPF, NORM, FMAP>;
         void *args[] = {&q,   &k,   &v,  &g,  &s0, &st, &o,  &den, &z0, &zf, &dq,     &dk,
                         &dv,  &ds0, &dz0, &wsc, &L, &NS, &seg_len, &Ea, &Ma};
         e = launch_kernel(reinterpret_cast<const void *>(kern), dim3(NS * P::BG * P::BRG * nseg),

@@ -65,12 +65,15 @@ struct BwdArgs {
 constexpr int kCUs = 256, kMinSegChunks = CP_SEG_MIN_CHUNKS, kSegWgPerCU = CP_SEG_WG_PER_CU;
 constexpr int kBwdSegWgPerCU = CP_BWD_SEG_WG_PER_CU;  // the backward's workgroups hold a CU each
 // stages of the load ring of the segment-increment pass, and its waves (at
-// most four, each owning M/16/waves column blocks of the increment)
+// most CP_SEG_MAXW, each owning M/16/waves column blocks of the increment)
 #ifndef CP_SEG_NPF
 #define CP_SEG_NPF 4
 #endif
+#ifndef CP_SEG_MAXW
+#define CP_SEG_MAXW 8  // (8 rather than 4: the L = 16384, 128-wide passes 103 -> 84 us and 36 -> 31 us)
+#endif
 template <int M>
-constexpr int seg_state_waves() { return M / 16 >= 4 ? 4 : M / 16; }
+constexpr int seg_state_waves() { return M / 16 >= CP_SEG_MAXW ? CP_SEG_MAXW : M / 16; }
 inline int seq_segments(int L, int NS, int groups, int C, int wg_per_cu = kSegWgPerCU) {
     const long wg = (long)NS * groups;
     const int nchunks = (L + C - 1) / C;

@@ -12,7 +12,7 @@
 //        by one workgroup (whole 128-byte lines stream to HBM at a higher
 //        rate than lines whose pieces come from two compute units),
 //   FNPF, BNPF  stages of the forward / backward load ring (NPF-1 chunks are
-//        in flight while one is computed),
+//        in flight while one is computed; BNPF_N for the normalised backward),
 //   BNB  backward column blocks per wave (1 or 2): a wave with two blocks
 //        reads the chunk's operand tiles and forms its causal tiles once for
 //        both,
@@ -135,6 +135,11 @@ template <int E, int M> struct Tune<__bf16, E, M> {
     static constexpr bool FDW = !(E == 128 && M == 128);
     static constexpr int FNPF = E == 128 && CP_BF16_FNPF > 2 ? 2 : CP_BF16_FNPF;  // E = 128: registers
     static constexpr int BNPF = CP_BF16_BNPF;
+    // the normalised backward over 128-wide E: its stages also carry the
+    // output rows and denominators, and with four of them the twelve-wave
+    // workgroup spills (181 VGPRs at its 168 cap); two stages: the L = 16384,
+    // E = M = 128 sweep 367 -> 204 us
+    static constexpr int BNPF_N = E == 128 && CP_BF16_BNPF > 2 ? 2 : CP_BF16_BNPF;
     // two blocks per wave where they divide evenly and registers allow; such
     // waves run shorter chunks (their per-chunk work is twice as long); with
     // row groups their workgroups take every column and split the rows
@@ -166,6 +171,7 @@ template <int E, int M> struct Tune<float, E, M> {
     static constexpr bool FDW = !(E == 128 && M == 128);
     static constexpr int FNPF = CP_F32_FNPF;
     static constexpr int BNPF = CP_F32_BNPF;
+    static constexpr int BNPF_N = CP_F32_BNPF;
     static constexpr int BG = bwd_groups(E, M, CP_F32_BG);
     static constexpr int BNB = 1;
     static constexpr int BRG = 1;
