@@ -35,11 +35,13 @@
  *    aligned.  Outputs are fully overwritten (they need not be zeroed) and
  *    must not overlap any input or each other.  States are fp32: S as
  *    [N][H][E][M] (row e, column m), z as [N][H][E].  The library keeps no
- *    pointer after a call returns.  A forward call over too few slices to
- *    fill the GPU splits each sequence into segments and takes a scratch
- *    buffer of N*H*segments*(E*M + E) floats from the stream-ordered
- *    allocator (hipMallocAsync), freed on the same stream after its last
- *    use; no other call allocates device memory.
+ *    pointer after a call returns.  A call over too few slices to fill the
+ *    GPU splits each sequence into segments (a pass computing each
+ *    segment's state increments, then the sweeps of all segments at once)
+ *    and takes a scratch buffer of N*H*segments*(E*M + E) floats (forward)
+ *    or twice that (backward) from the stream-ordered allocator
+ *    (hipMallocAsync), freed on the same stream after its last use; no other
+ *    call allocates device memory.
  *  * stream is a hipStream_t (NULL = the default stream).  Calls only enqueue
  *    work: they never synchronise the host, and buffers must stay alive until
  *    the stream has run the work.  Calls are stateless, thread-safe and
@@ -128,7 +130,9 @@ int causal_product_fwd_noalloc(const void *Q, const void *K, const void *V, void
  * wrote to state_out for the same K, V and S0.  With it every gradient is
  * produced by reverse sweeps that read each input once; with NULL the query
  * gradient runs its own forward sweep from state_in (more input traffic, same
- * result up to rounding).
+ * result up to rounding).  Over sequence segments (few slices) the query
+ * gradient of each segment starts from state_final minus the later
+ * segments' increments, or without it from state_in plus the earlier ones.
  * dstate_in (optional, may be NULL): receives the gradient of f with respect
  * to S0, sum_i q_i dOut_i^T (= R_0), of every slice.
  */
@@ -185,8 +189,9 @@ int linear_attn_fwd(const void *Q, const void *K, const void *V, void *Out,
  * compensated pre-pass of its own (the forward's plain fp32 sums would leave
  * their rounding error in them).  dn_i and dd_i are formed while dOut is
  * staged (dn rounded to the I/O type, dd in fp32).  dstate_in, dz_in
- * (optional): receive the gradients of the initial states.  One kernel, no
- * scratch: the call allocates nothing.
+ * (optional): receive the gradients of the initial states.  One kernel and
+ * no scratch when the slices fill the GPU; over few slices, sequence
+ * segments as for every call (see the conventions above).
  */
 int linear_attn_bwd(const void *Q, const void *K, const void *V, const void *Out, const void *dOut,
                     const float *den, const float *state_in, const float *z_in,
@@ -202,8 +207,8 @@ const char *cp_status_string(int status);
  * normalised backward; 3.1: CP_F16 and head sizes between the tile sizes
  * (both additions: every 3.0 call behaves as before); 4.0: cp_timing_end
  * takes the capacity of the caller's buffer; 4.1: causal_product_fwd_noalloc
- * and CP_ERR_SCRATCH; 5.0: linear_attn_bwd takes z_final and allocates
- * nothing. */
+ * and CP_ERR_SCRATCH; 5.0: linear_attn_bwd takes z_final (and allocates
+ * only over sequence segments). */
 int cp_abi_version(void);
 
 /*

@@ -32,7 +32,7 @@ namespace {
 constexpr int kAbiMajor = 5, kAbiMinor = 0;  // 3.0: carried state, normalised backward; 3.1: fp16 I/O;
                                              // 4.0: cp_timing_end bounded by the caller's buffer;
                                              // 4.1: causal_product_fwd_noalloc;
-                                             // 5.0: linear_attn_bwd takes z_final, allocates nothing
+                                             // 5.0: linear_attn_bwd takes z_final, no scratch unsplit
 
 cp::fwd_fn pick_fwd(int dtype, int E, int M, bool norm) {
     return dtype == CP_BF16 ? cp::fwd_bf16(E, M, norm) : dtype == CP_F16 ? cp::fwd_f16(E, M, norm) : cp::fwd_f32(E, M, norm);
