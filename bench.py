@@ -34,7 +34,7 @@ METRIC = "causal-product fwd+bwd tokens·heads/s and % HBM/MFMA roofline, L=4096
 UNIT = "tokens·heads/s"
 COUNTERS = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 KERNEL_SOURCES = ("cp_device.hpp", "cp_fwd.hpp", "cp_fwd_launch.hpp", "cp_bwd.hpp", "cp_bwd_launch.hpp", "cp_tune.hpp",
-                  "cp_launch.hpp")
+                  "cp_launch.hpp", "cp_plan.hpp")
 # the sweep kernel of each call; over few slices a call is two launches, the
 # segment-increment pass and then the sweeps
 SWEEP_KERNEL = {"fwd": "cp_fwd_kernel", "bwd": "cp_bwd_kernel", "linattn": "cp_fwd_kernel",

@@ -34,11 +34,9 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t s) {
     float *ds0 = a.dstate_in, *dz0 = a.dz_in;
     int L = a.L, NS = a.NS, Ea = a.Ea, Ma = a.Ma;
 
-    const int nseg0 = seq_segments(L, NS, P::BG * P::BRG, C, kBwdSegWgPerCU);
-    const int nchunks = (L + C - 1) / C;
-    int seg_len = (nchunks + nseg0 - 1) / nseg0 * C;
-    const int nseg = (L + seg_len - 1) / seg_len;
-    if (nseg == 1) seg_len = L;
+    const SegPlan plan = plan_segments(L, NS, P::BG * P::BRG, C, kBwdSegWgPerCU);
+    const int nseg = plan.nseg;
+    int seg_len = plan.seg_len;
     float *ws = nullptr;
     hipError_t e = hipSuccess;
     if (nseg > 1) {

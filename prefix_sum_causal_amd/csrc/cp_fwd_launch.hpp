@@ -23,10 +23,9 @@ hipError_t launch_fwd_t(const FwdArgs &a, hipStream_t s) {
     constexpr int FRS = NORM ? 1 : P::FRS, FRG = NORM ? P::FRG_N : P::FRG;
     const dim3 block(64 * ((M / 16 / P::FG) * FRS + (DW ? 1 : 0)));
 
-    const int nseg0 = seq_segments(L, NS, P::FG * FRG, P::FC);
-    const int nchunks = (L + P::FC - 1) / P::FC;
-    int seg_len = (nchunks + nseg0 - 1) / nseg0 * P::FC;
-    const int nseg = (L + seg_len - 1) / seg_len;
+    const SegPlan plan = plan_segments(L, NS, P::FG * FRG, P::FC);
+    const int nseg = plan.nseg;
+    int seg_len = plan.seg_len;
     // per slice and segment: the E x M increment of the state, then E of z
     const size_t need = nseg > 1 ? (size_t)NS * nseg * (E * M + E) * sizeof(float) : 0;
     if (a.ws_need) {
@@ -54,8 +53,6 @@ hipError_t launch_fwd_t(const FwdArgs &a, hipStream_t s) {
         int first1 = 0;
         void *args1[] = {&k, &v, &ws, &none, &none, &none, &noden, &nows, &L, &NS, &seg_len, &first1, &Ea, &Ma};
         e = launch_kernel(reinterpret_cast<const void *>(k1), dim3(NS * (nseg - 1)), dim3(64 * SW), args1, s);
-    } else {
-        seg_len = L;
     }
     if (e == hipSuccess) {
         auto k2 = cp_fwd_kernel<T, E, M, P::FC, P::FG, FRS, FRG, P::FNPF, NORM, FMAP, DW>;

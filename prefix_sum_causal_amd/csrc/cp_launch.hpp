@@ -7,6 +7,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "cp_plan.hpp"
 #include "cp_validate.hpp"
 
 namespace cp {
@@ -50,20 +51,6 @@ struct BwdArgs {
     int Ea, Ma;  // head sizes of the tensors (the kernel runs the next tile size up)
 };
 
-// Segments per slice for L rows and NS slices (forward and backward): one,
-// unless the slices leave most CUs idle; then enough segments of at least
-// kMinSegChunks chunks for about two workgroups per CU.
-#ifndef CP_SEG_MIN_CHUNKS
-#define CP_SEG_MIN_CHUNKS 4
-#endif
-#ifndef CP_SEG_WG_PER_CU
-#define CP_SEG_WG_PER_CU 2
-#endif
-#ifndef CP_BWD_SEG_WG_PER_CU
-#define CP_BWD_SEG_WG_PER_CU 1
-#endif
-constexpr int kCUs = 256, kMinSegChunks = CP_SEG_MIN_CHUNKS, kSegWgPerCU = CP_SEG_WG_PER_CU;
-constexpr int kBwdSegWgPerCU = CP_BWD_SEG_WG_PER_CU;  // the backward's workgroups hold a CU each
 // stages of the load ring of the segment-increment pass, and its waves (at
 // most CP_SEG_MAXW, each owning M/16/waves column blocks of the increment)
 #ifndef CP_SEG_NPF
@@ -74,14 +61,6 @@ constexpr int kBwdSegWgPerCU = CP_BWD_SEG_WG_PER_CU;  // the backward's workgrou
 #endif
 template <int M>
 constexpr int seg_state_waves() { return M / 16 >= CP_SEG_MAXW ? CP_SEG_MAXW : M / 16; }
-inline int seq_segments(int L, int NS, int groups, int C, int wg_per_cu = kSegWgPerCU) {
-    const long wg = (long)NS * groups;
-    const int nchunks = (L + C - 1) / C;
-    if (wg >= kCUs || nchunks < 2 * kMinSegChunks) return 1;
-    long want = ((long)wg_per_cu * kCUs + wg - 1) / wg;
-    const long most = nchunks / kMinSegChunks;
-    return (int)(want < most ? want : most);
-}
 
 // Each launcher enqueues one kernel on stream and returns hipSuccess or the
 // launch error.  NULL when (E, M) is not instantiated.

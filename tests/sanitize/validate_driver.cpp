@@ -1,10 +1,12 @@
-// Exercises the C ABI's argument checks (cp_validate.hpp) on the host, built
+// Exercises the C ABI's argument checks (cp_validate.hpp) and the launchers'
+// segment planning (cp_plan.hpp) on the host, built
 // with -fsanitize=address,undefined by tests/test_sanitizers.py.  Pointers are
 // fake, 16-byte aligned addresses that are never dereferenced.  Prints one
 // line per failed expectation and exits with the number of failures.
 #include <stdint.h>
 #include <stdio.h>
 
+#include "cp_plan.hpp"
 #include "cp_validate.hpp"
 
 static int failures = 0;
@@ -18,6 +20,24 @@ static void expect(int got, int want, const char *what) {
 
 static const void *P(int n) { return reinterpret_cast<const void *>(uintptr_t(0x1000000000ull) + uintptr_t(n) * 0x100000000ull); }
 static const float *F(int n) { return static_cast<const float *>(P(n)); }
+
+// Properties of a segment plan: every row in exactly one non-empty segment,
+// segments of whole chunks, at least kMinSegChunks chunks each, only when the
+// slices leave CUs idle, and the kernels' ceil(L / seg_len) gives nseg back.
+static void check_plan(int L, int NS, int groups, int C, int wpc) {
+    const cp::SegPlan p = cp::plan_segments(L, NS, groups, C, wpc);
+    char what[160];
+    snprintf(what, sizeof what, "plan L=%d NS=%d groups=%d C=%d wpc=%d -> %d x %d", L, NS, groups, C, wpc, p.nseg,
+             p.seg_len);
+    bool ok = p.nseg >= 1 && p.seg_len >= 1;
+    if (ok && p.nseg == 1) ok = p.seg_len == L;
+    if (ok && p.nseg > 1) {
+        const long long covered = (long long)p.nseg * p.seg_len, before_last = (long long)(p.nseg - 1) * p.seg_len;
+        ok = p.seg_len % C == 0 && before_last < L && covered >= L && p.seg_len >= cp::kMinSegChunks * C &&
+             (long long)NS * groups < cp::kCUs && ((long long)L + p.seg_len - 1) / p.seg_len == p.nseg;
+    }
+    expect(ok ? 1 : 0, 1, what);
+}
 
 int main() {
     using namespace cp;
@@ -86,6 +106,15 @@ int main() {
         const int want = x < 1 ? -1 : x <= 16 ? 0 : x <= 32 ? 1 : x <= 64 ? 2 : x <= 128 ? 3 : -1;
         expect(t, want, "tile_index");
     }
+    // segment plans over lengths, slice counts, groups, chunks and targets
+    for (int C : {16, 32, 64, 128})
+        for (int groups : {1, 2, 4})
+            for (int wpc : {1, 2})
+                for (int NS : {1, 2, 3, 7, 16, 33, 100, 127, 128, 255, 256, 1000})
+                    for (long long L : {1LL, 63LL, 64LL, 65LL, 511LL, 512LL, 513LL, 1000LL, 1500LL, 2085LL, 4096LL,
+                                        16384LL, 100003LL, 1LL << 24, (long long)INT32_MAX - 5, (long long)INT32_MAX})
+                        check_plan((int)L, NS, groups, C, wpc);
+
     printf("%d failures\n", failures);
     return failures;
 }
