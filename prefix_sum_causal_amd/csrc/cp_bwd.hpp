@@ -676,11 +676,17 @@ __device__ __forceinline__ void bwd_sweep(const T *q_, const T *k_, const T *v_,
             if constexpr (ROLE != kIdle) {
                 const int OWa = ROLE == kDV ? Ma : Ea;
                 const Rows<T> rp(out_, OWa, row0, L, C);
-#pragma unroll
-                for (int x = 0; x < NB; ++x)
+                if constexpr (sizeof(T) == 2 && NB == 2 && G == 1) {  // adjacent blocks: 16-byte pieces
 #pragma unroll
                     for (int j = 0; j < CB; ++j)
-                        if (own(j)) st_out<T>(rp, j, bk(x), pend[x][j], OWa);
+                        if (own(j)) st_out_pair<T>(rp, j, bk(0), pend[0][j], pend[1][j], OWa);
+                } else {
+#pragma unroll
+                    for (int x = 0; x < NB; ++x)
+#pragma unroll
+                        for (int j = 0; j < CB; ++j)
+                            if (own(j)) st_out<T>(rp, j, bk(x), pend[x][j], OWa);
+                }
             }
         }
     }
