@@ -676,10 +676,12 @@ __device__ __forceinline__ void bwd_sweep(const T *q_, const T *k_, const T *v_,
             if constexpr (ROLE != kIdle) {
                 const int OWa = ROLE == kDV ? Ma : Ea;
                 const Rows<T> rp(out_, OWa, row0, L, C);
-                if constexpr (sizeof(T) == 2 && NB == 2 && G == 1) {  // adjacent blocks: 16-byte pieces
+                // two-block waves: a row block's two 16-bit tiles as 16-byte
+                // pieces (64 contiguous bytes per row with adjacent blocks)
+                if constexpr (sizeof(T) == 2 && NB == 2) {
 #pragma unroll
                     for (int j = 0; j < CB; ++j)
-                        if (own(j)) st_out_pair<T>(rp, j, bk(0), pend[0][j], pend[1][j], OWa);
+                        if (own(j)) st_out_pair<T>(rp, j, bk(0), pend[0][j], j, bk(1), pend[1][j], OWa);
                 } else {
 #pragma unroll
                     for (int x = 0; x < NB; ++x)
