@@ -319,7 +319,12 @@ __device__ __forceinline__ void st_out_pair(const Rows<T> &X, int rbA, int cbA, 
     const int col = even ? 16 * cbA + 4 * g : 16 * cbB + 4 * (g - 1);
     const int row = 16 * (even ? rbA : rbB) + lane_r();
     const int off = col < wa ? (row * X.ld + col) * (int)sizeof(T) : kVoid;
-    __builtin_amdgcn_raw_buffer_store_b128(v, X.rsrc, off, 0, 0);
+    // non-temporal (aux bit 1, nt): these rows are not read again by the call
+    // and written as whole 64-byte pieces; leaving them dirty in the caches
+    // made the next kernel write them back (headline: that forward 63.7 ->
+    // 54.7 us, this backward 104.5 -> 105.7, the step 187 -> 182 us).  (The
+    // 32-byte pieces of st_out measured far slower with nt.)
+    __builtin_amdgcn_raw_buffer_store_b128(v, X.rsrc, off, 0, 2);
 }
 
 // Row stride (16-bit elements) of the LDS copy of a W-column chunk, a
