@@ -71,6 +71,31 @@ struct SegCarry {
     int seg, nseg;
 };
 
+// The slice's three outputs (dQ, dK: E columns; dV: M columns), for the copy
+// waves that store the workgroup's staged output rows (OUTLDS in bwd_sweep).
+template <typename T> struct Outs {
+    T *dq, *dk, *dv;
+};
+
+// The k-th row block (k from 0) of a chunk's CB that row group h of RG owns
+// (owns_block), the position of block j among them, and how many it owns.
+template <int CB, int RG>
+constexpr int owned_block(int h, int k) {
+    for (int I = 0; I < CB; ++I)
+        if (owns_block<CB, RG>(h, I) && k-- == 0) return I;
+    return -1;
+}
+template <int CB, int RG>
+constexpr int owned_index(int h, int j) {
+    int k = 0;
+    for (int I = 0; I < j; ++I) k += owns_block<CB, RG>(h, I) ? 1 : 0;
+    return k;
+}
+template <int CB, int RG>
+constexpr int owned_count(int h) {
+    return owned_index<CB, RG>(h, CB);
+}
+
 // A k-contraction into NB accumulators that share one operand: acc(x) is the
 // x-th accumulator; fs(i) the shared operand (read once), fo(x, i) the x-th
 // own operand.  SHARED_A puts the shared operand on the A side.
@@ -108,8 +133,8 @@ __device__ __forceinline__ void dotk_shared(FACC acc, int b0, int b1, FS fs, FO 
 template <typename T, int E, int M, int C, int G, int NB, int IDLE, int RG, int RGI, int NPF, bool NORM, bool FMAP,
           int ROLE>
 __device__ __forceinline__ void bwd_sweep(const T *q_, const T *k_, const T *v_, const T *g_, const float *s0,
-                                          const float *st, NormIn<T> nin, SegCarry sc, T *out_, float *ds0,
-                                          float *dz0, int L, int b, lds_t<T> *lds, int Ea, int Ma) {
+                                          const float *st, NormIn<T> nin, SegCarry sc, Outs<T> outs, T *out_,
+                                          float *ds0, float *dz0, int L, int b, lds_t<T> *lds, int Ea, int Ma) {
     using O = Ops<T>;
     using F = typename O::frag;
     using EE = EOps<T, E>;  // contraction over e
@@ -400,6 +425,45 @@ __device__ __forceinline__ void bwd_sweep(const T *q_, const T *k_, const T *v_,
 
     constexpr int OW = ROLE == kDV ? M : E;
 
+    // OUTLDS (16-bit I/O, two adjacent column blocks per wave, one column
+    // group, copy-only waves): the role waves write each chunk's output
+    // tiles into an LDS buffer (double buffered, after the ring and the
+    // normalised form's buffers) instead of storing them; after the next
+    // barrier the copy-only waves store that chunk's dQ, dK and dV rows as
+    // whole rows of 16-byte pieces (non-temporal).  A row's 128 bytes then
+    // come from one wave and one instruction instead of 32- or 64-byte pieces
+    // from several waves.
+    constexpr bool OUTLDS = sizeof(T) == 2 && NB == 2 && G == 1 && IDLE > 0;
+    constexpr int OWM = E > M ? E : M;              // widest output row (elements)
+    constexpr int RSO = OWM + 8;                    // LDS row stride of the staged rows
+    constexpr int NOWN = owned_count<CB, RG>(RGI);  // row blocks this row group owns per chunk
+    constexpr int OROWS = 16 * NOWN;                // its output rows per chunk and output
+    constexpr int EG_ = (EB + G * NB - 1) / (G * NB);  // dQ waves (their parking slots precede)
+    lds_t<T> *const outbuf = reinterpret_cast<lds_t<T> *>(ddbuf + 2 * C + (NORM && sizeof(T) == 2 ? EG_ * NB * (MB + 1) * 64 * 4 : 0));
+    // the copy-only waves store chunk step ps's rows
+    auto flush_rows = [&](int ps) {
+        if constexpr (OUTLDS && ROLE == kIdle) {
+            constexpr int PPRO = OWM * 2 / 16;  // 16-byte pieces per staged row
+            constexpr int NPIECE = 3 * OROWS * PPRO, NI = 64 * IDLE;
+            const int il = ((int)(threadIdx.x >> 6) - (NT / 64 - IDLE)) * 64 + lane_id();
+            const int prow0 = (n - 1 - ps) * C;
+            const lds_t<T> *ob = outbuf + (ps & 1) * 3 * OROWS * RSO;
+#pragma unroll
+            for (int i = 0; i < (NPIECE + NI - 1) / NI; ++i) {
+                const int p = il + i * NI;
+                if (NPIECE % NI != 0 && p >= NPIECE) break;
+                const int out = p / (OROWS * PPRO), row = p % (OROWS * PPRO) / PPRO, cp = p % PPRO;
+                const int wt = out < 2 ? E : M, wa = out < 2 ? Ea : Ma;
+                T *base = out == 0 ? outs.dq : out == 1 ? outs.dk : outs.dv;
+                const int j = owned_block<CB, RG>(RGI, row / 16);
+                const Rows<T> X(base, wa, prow0, L, C);
+                const i32x4 v = *reinterpret_cast<const i32x4 *>(ob + (out * OROWS + row) * RSO + cp * 8);
+                const int off = cp * 8 < wt && cp * 8 < wa ? ((16 * j + row % 16) * wa + cp * 8) * (int)sizeof(T) : kVoid;
+                __builtin_amdgcn_raw_buffer_store_b128(v, X.rsrc, off, 0, 2);
+            }
+        }
+    };
+
     // Ring of NPF register stages (NPF-1 chunks in flight while one is
     // computed); the step loop is padded to a multiple of NPF with chunks
     // before the start of the sequence, which load as zero and store nothing.
@@ -450,6 +514,9 @@ __device__ __forceinline__ void bwd_sweep(const T *q_, const T *k_, const T *v_,
             __syncthreads();
             stg[(s + NPF - 1) % NPF].load(q_, k_, v_, g_, nin, row0 - (NPF - 1) * C, L, Ea, Ma);
             __builtin_amdgcn_sched_barrier(0);
+            if constexpr (OUTLDS && ROLE == kIdle) {
+                if (step > 0) flush_rows(step - 1);
+            }
 
             f32x4 pend[NB][CB];  // this chunk's output tiles (rows 16 I + r) per column block
             if constexpr (ROLE == kDQ) {
@@ -678,7 +745,19 @@ __device__ __forceinline__ void bwd_sweep(const T *q_, const T *k_, const T *v_,
                 const Rows<T> rp(out_, OWa, row0, L, C);
                 // two-block waves: a row block's two 16-bit tiles as 16-byte
                 // pieces (64 contiguous bytes per row with adjacent blocks)
-                if constexpr (sizeof(T) == 2 && NB == 2) {
+                if constexpr (OUTLDS) {
+                    lds_t<T> *ob = outbuf + ((step & 1) * 3 + ROLE) * OROWS * RSO;
+                    typedef int i32x2 __attribute__((__vector_size__(2 * sizeof(int))));
+#pragma unroll
+                    for (int j = 0; j < CB; ++j)
+                        if (own(j)) {
+                            const int row = 16 * owned_index<CB, RG>(RGI, j) + r;
+#pragma unroll
+                            for (int x = 0; x < NB; ++x)
+                                *reinterpret_cast<i32x2 *>(ob + row * RSO + 16 * bk(x) + 4 * g) =
+                                    __builtin_bit_cast(i32x2, O::cvt(pend[x][j]));
+                        }
+                } else if constexpr (sizeof(T) == 2 && NB == 2) {
 #pragma unroll
                     for (int j = 0; j < CB; ++j)
                         if (own(j)) st_out_pair<T>(rp, j, bk(0), pend[0][j], j, bk(1), pend[1][j], OWa);
@@ -691,6 +770,10 @@ __device__ __forceinline__ void bwd_sweep(const T *q_, const T *k_, const T *v_,
                 }
             }
         }
+    }
+    if constexpr (OUTLDS) {  // the last step's rows
+        __syncthreads();
+        flush_rows(nsteps - 1);
     }
     // the gradient of the initial z: r_0, held by the dK waves
     if constexpr (NORM && ROLE == kDK && RGI == 0) {
@@ -725,17 +808,18 @@ __device__ __forceinline__ void bwd_role(int role, int b, const T *q_, const T *
                                          const float *s0, const float *st, NormIn<T> nin, SegCarry sc, T *dq_, T *dk_, T *dv_,
                                          float *ds0, float *dz0, int L, lds_t<T> *lds, int Ea, int Ma) {
     constexpr int EB = E / 16, MB = M / 16;
+    const Outs<T> outs{dq_, dk_, dv_};
     if (role == kDQ && b < EB)
-        bwd_sweep<T, E, M, C, G, NB, IDLE, RG, RGI, NPF, NORM, FMAP, kDQ>(q_, k_, v_, g_, s0, st, nin, sc, dq_, nullptr,
+        bwd_sweep<T, E, M, C, G, NB, IDLE, RG, RGI, NPF, NORM, FMAP, kDQ>(q_, k_, v_, g_, s0, st, nin, sc, outs, dq_, nullptr,
                                                                           nullptr, L, b, lds, Ea, Ma);
     else if (role == kDK && b < EB)
-        bwd_sweep<T, E, M, C, G, NB, IDLE, RG, RGI, NPF, NORM, FMAP, kDK>(q_, k_, v_, g_, s0, st, nin, sc, dk_, nullptr,
+        bwd_sweep<T, E, M, C, G, NB, IDLE, RG, RGI, NPF, NORM, FMAP, kDK>(q_, k_, v_, g_, s0, st, nin, sc, outs, dk_, nullptr,
                                                                           dz0, L, b, lds, Ea, Ma);
     else if (role == kDV && b < MB)
-        bwd_sweep<T, E, M, C, G, NB, IDLE, RG, RGI, NPF, NORM, FMAP, kDV>(q_, k_, v_, g_, s0, st, nin, sc, dv_, ds0,
+        bwd_sweep<T, E, M, C, G, NB, IDLE, RG, RGI, NPF, NORM, FMAP, kDV>(q_, k_, v_, g_, s0, st, nin, sc, outs, dv_, ds0,
                                                                           nullptr, L, b, lds, Ea, Ma);
     else
-        bwd_sweep<T, E, M, C, G, NB, IDLE, RG, RGI, NPF, NORM, FMAP, kIdle>(q_, k_, v_, g_, s0, st, nin, sc, nullptr,
+        bwd_sweep<T, E, M, C, G, NB, IDLE, RG, RGI, NPF, NORM, FMAP, kIdle>(q_, k_, v_, g_, s0, st, nin, sc, outs, nullptr,
                                                                             nullptr, nullptr, L, 0, lds, Ea, Ma);
 }
 
@@ -763,7 +847,13 @@ __global__ __launch_bounds__((64 * bwd_waves<E, M, G, NB, IDLE>())) void cp_bwd_
     // parking slots for the restart states
     constexpr int PARK = NORM && sizeof(T) == 2 ? EG * NB * (MB + 1) * 64 * 4 : 0;
     constexpr int DDE = NORM ? (2 * C + PARK) * 4 / (int)sizeof(lds_t<T>) : 0;
-    __shared__ __attribute__((aligned(16))) lds_t<T> lds[2 * BUF + DDE];
+    // staged output rows (OUTLDS in bwd_sweep), after the dd buffers
+    constexpr bool OUTLDS = sizeof(T) == 2 && NB == 2 && G == 1 && IDLE > 0;
+    constexpr int OWM = E > M ? E : M, NOWN0 = owned_count<C / 16, RG>(0), NOWN1 = owned_count<C / 16, RG>(RG - 1);
+    constexpr int OUTE = OUTLDS ? (NORM ? 0 : 2 * C * 4 / (int)sizeof(lds_t<T>)) +
+                                      2 * 3 * 16 * (NOWN0 > NOWN1 ? NOWN0 : NOWN1) * (OWM + 8)
+                                : 0;
+    __shared__ __attribute__((aligned(16))) lds_t<T> lds[2 * BUF + DDE + OUTE];
 
     static_assert(RG >= 1 && RG <= 2 && RG <= C / 16, "row groups");
     const int nseg = (L + seg_len - 1) / seg_len;
