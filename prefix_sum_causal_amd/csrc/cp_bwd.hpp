@@ -77,25 +77,6 @@ template <typename T> struct Outs {
     T *dq, *dk, *dv;
 };
 
-// The k-th row block (k from 0) of a chunk's CB that row group h of RG owns
-// (owns_block), the position of block j among them, and how many it owns.
-template <int CB, int RG>
-constexpr int owned_block(int h, int k) {
-    for (int I = 0; I < CB; ++I)
-        if (owns_block<CB, RG>(h, I) && k-- == 0) return I;
-    return -1;
-}
-template <int CB, int RG>
-constexpr int owned_index(int h, int j) {
-    int k = 0;
-    for (int I = 0; I < j; ++I) k += owns_block<CB, RG>(h, I) ? 1 : 0;
-    return k;
-}
-template <int CB, int RG>
-constexpr int owned_count(int h) {
-    return owned_index<CB, RG>(h, CB);
-}
-
 // A k-contraction into NB accumulators that share one operand: acc(x) is the
 // x-th accumulator; fs(i) the shared operand (read once), fo(x, i) the x-th
 // own operand.  SHARED_A puts the shared operand on the A side.

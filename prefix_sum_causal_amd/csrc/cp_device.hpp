@@ -611,6 +611,25 @@ constexpr int last_block(int h) {
     return last;
 }
 
+// The k-th row block (k from 0) of a chunk's CB that row group h of RG owns
+// (owns_block), the position of block j among them, and how many it owns.
+template <int CB, int RG>
+constexpr int owned_block(int h, int k) {
+    for (int I = 0; I < CB; ++I)
+        if (owns_block<CB, RG>(h, I) && k-- == 0) return I;
+    return -1;
+}
+template <int CB, int RG>
+constexpr int owned_index(int h, int j) {
+    int k = 0;
+    for (int I = 0; I < j; ++I) k += owns_block<CB, RG>(h, I) ? 1 : 0;
+    return k;
+}
+template <int CB, int RG>
+constexpr int owned_count(int h) {
+    return owned_index<CB, RG>(h, CB);
+}
+
 // Workgroup id -> (slice, part).  The P parts of one (n, h) slice read the
 // same rows of the inputs, so they are kept on one XCD (workgroups are
 // dispatched to the 8 XCDs round robin by id) where they share its L2.
