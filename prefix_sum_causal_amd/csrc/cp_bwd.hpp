@@ -296,9 +296,9 @@ __device__ __forceinline__ void bwd_sweep(const T *q_, const T *k_, const T *v_,
     constexpr int kPre = kRestartRows / C > 1 ? kRestartRows / C : 1;
     const int npre = from_final ? (RESTART && sc.seg == 0 ? (n < kPre ? n : kPre) : 0) : n;
     // the wave's parking slots: f32x4 per lane, MB state tiles then z, per block
-    f32x4 *const park =
-        RESTART && ROLE == kDQ ? reinterpret_cast<f32x4 *>(ddbuf + 2 * C) + (b / (G * NB)) * NB * (MB + 1) * 64
-                               : nullptr;
+    f32x4 *const park = RESTART && ROLE == kDQ ? reinterpret_cast<f32x4 *>(ddbuf + 2 * C) +
+                                                     (int)(threadIdx.x >> 6) * NB * (MB + 1) * 64  // dQ waves come first
+                                               : nullptr;
     if (npre > 0) {
         // forward pre-pass over chunks [0, npre): S^T[:, b] = S0^T[:, b] + the
         // chunks' V^T K[:, b] (NORM: and z = z_{-1} + their column sums)
