@@ -174,6 +174,11 @@ def main() -> int:
                     help="after the timed region, this many more steps with every call preceded by a 1 GiB "
                          "read that evicts the caches (the 256 MB MALL included); their per-call times are "
                          "reported as cold_cache")
+    ap.add_argument("--settle-steps", type=int, default=300,
+                    help="after everything else, this many untimed steps back to back, then K more timed "
+                         "ones, reported as steady_state (the GPU's clocks dip for some milliseconds after "
+                         "a burst of load starts, which is where a short timed region right after a few "
+                         "warm-up steps falls); 0 skips it")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="run one plain device-to-device copy of this many MiB first (reference for the "
                          "HBM byte counters of a profiler run)")
@@ -311,6 +316,22 @@ def main() -> int:
                        "GBps": algorithmic_bytes(w, kind) / (acc[kind] / args.cold_steps) / 1e9,
                        "frac": algorithmic_bytes(w, kind) / (acc[kind] / args.cold_steps) / 1e9 / HBM_PEAK_GBS}
                 for kind in kinds}
+    # Steady state: the same K steps once the load has lasted long enough for
+    # the clocks to settle (about 50 ms at the headline workload).  Reported
+    # beside `value`, which stays the K steps right after the W warm-up steps.
+    steady = None
+    if args.settle_steps > 0:
+        for _ in range(args.settle_steps):
+            step()
+        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s0.record()
+        for _ in range(args.steps):
+            step()
+        s1.record()
+        torch.cuda.synchronize()
+        sdev = s0.elapsed_time(s1) * 1e-3
+        steady = {"settle_steps": args.settle_steps, "steps": args.steps,
+                  "ms_per_step": sdev / args.steps * 1e3, "value": args.steps * w.token_heads / sdev}
     dom = max(kinds, key=lambda k: times[k])
     achieved = per_kernel[dom]["GBps"]
     hbm_frac = achieved / HBM_PEAK_GBS
@@ -343,6 +364,7 @@ def main() -> int:
         "copy": copy,
         "kernels": per_kernel,
         "cold_cache": cold,
+        "steady_state": steady,
     }
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, host)

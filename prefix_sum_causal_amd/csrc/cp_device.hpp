@@ -389,13 +389,15 @@ struct Stage {
                 constexpr int n = 16 / (int)sizeof(T);
                 typedef T tn __attribute__((__vector_size__(16)));
                 tn e = __builtin_bit_cast(tn, x);
-                // rows at or past L and padding columns were loaded as zero;
-                // phi(0) = 1 is cancelled by a 0/1 factor rather than a
-                // branch, so the piece is mapped with straight-line code
-                const float keep = row0 + row < L && cp * VEC < wa ? 1.f : 0.f;
 #pragma unroll
-                for (int j = 0; j < n; ++j) e[j] = (T)(phi((float)e[j]) * keep);
+                for (int j = 0; j < n; ++j) e[j] = (T)phi((float)e[j]);
                 x = __builtin_bit_cast(i32x4, e);
+                // rows at or past L and padding columns were loaded as zero,
+                // and phi(0) = 1: such a piece is zeroed again, a select per
+                // 32-bit word rather than a branch
+                const bool keep = row0 + row < L && cp * VEC < wa;
+#pragma unroll
+                for (int d = 0; d < 4; ++d) x[d] = keep ? x[d] : 0;
             }
             if constexpr (std::is_same<T, float>::value) {
                 // the hi and lo halves of the four values
