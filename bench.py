@@ -175,10 +175,11 @@ def main() -> int:
                          "read that evicts the caches (the 256 MB MALL included); their per-call times are "
                          "reported as cold_cache")
     ap.add_argument("--settle-steps", type=int, default=300,
-                    help="after everything else, this many untimed steps back to back, then K more timed "
-                         "ones, reported as steady_state (the GPU's clocks dip for some milliseconds after "
-                         "a burst of load starts, which is where a short timed region right after a few "
-                         "warm-up steps falls); 0 skips it")
+                    help="after the timed region, this many untimed steps back to back, then K more timed "
+                         "ones, reported as steady_state; the per-call durations (and the roofline) are taken "
+                         "right after them (the GPU's clocks dip for some milliseconds after a burst of load "
+                         "starts, which is where a short timed region right after a few warm-up steps falls); "
+                         "0 skips it")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="run one plain device-to-device copy of this many MiB first (reference for the "
                          "HBM byte counters of a profiler run)")
@@ -262,6 +263,26 @@ def main() -> int:
     elapsed = time.perf_counter() - t0
     device_s = ev0.elapsed_time(ev1) * 1e-3
 
+    # Steady state: the same K steps once the load has lasted long enough for
+    # the clocks to settle (about 50 ms at the headline workload; a short
+    # region right after a few warm-up steps falls into a dip of the clocks
+    # that follows the start of a burst of load).  Reported beside `value`,
+    # which stays the K steps right after the W warm-up steps.  The per-call
+    # durations below are taken right after it, at the same clocks.
+    steady = None
+    if args.settle_steps > 0:
+        for _ in range(args.settle_steps):
+            step()
+        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s0.record()
+        for _ in range(args.steps):
+            step()
+        s1.record()
+        torch.cuda.synchronize()
+        sdev = s0.elapsed_time(s1) * 1e-3
+        steady = {"settle_steps": args.settle_steps, "steps": args.steps,
+                  "ms_per_step": sdev / args.steps * 1e3, "value": args.steps * w.token_heads / sdev}
+
     # Per-kernel durations: the same K steps again, each launch with its own
     # start/end events (the timestamps of its dispatch on the stream it runs
     # on, as a profiler's kernel trace reports them).  Launches per call: one,
@@ -316,22 +337,6 @@ def main() -> int:
                        "GBps": algorithmic_bytes(w, kind) / (acc[kind] / args.cold_steps) / 1e9,
                        "frac": algorithmic_bytes(w, kind) / (acc[kind] / args.cold_steps) / 1e9 / HBM_PEAK_GBS}
                 for kind in kinds}
-    # Steady state: the same K steps once the load has lasted long enough for
-    # the clocks to settle (about 50 ms at the headline workload).  Reported
-    # beside `value`, which stays the K steps right after the W warm-up steps.
-    steady = None
-    if args.settle_steps > 0:
-        for _ in range(args.settle_steps):
-            step()
-        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        s0.record()
-        for _ in range(args.steps):
-            step()
-        s1.record()
-        torch.cuda.synchronize()
-        sdev = s0.elapsed_time(s1) * 1e-3
-        steady = {"settle_steps": args.settle_steps, "steps": args.steps,
-                  "ms_per_step": sdev / args.steps * 1e3, "value": args.steps * w.token_heads / sdev}
     dom = max(kinds, key=lambda k: times[k])
     achieved = per_kernel[dom]["GBps"]
     hbm_frac = achieved / HBM_PEAK_GBS

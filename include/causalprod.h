@@ -35,13 +35,22 @@
  *    aligned.  Outputs are fully overwritten (they need not be zeroed) and
  *    must not overlap any input or each other.  States are fp32: S as
  *    [N][H][E][M] (row e, column m), z as [N][H][E].  The library keeps no
- *    pointer after a call returns.  A call over too few slices to fill the
- *    GPU splits each sequence into segments (a pass computing each
- *    segment's state increments, then the sweeps of all segments at once)
- *    and takes a scratch buffer of N*H*segments*(E*M + E) floats (forward)
- *    or twice that (backward) from the stream-ordered allocator
- *    (hipMallocAsync), freed on the same stream after its last use; no other
- *    call allocates device memory.
+ *    pointer after a call returns.
+ *  * Workspace.  A call over too few slices to fill the GPU splits each
+ *    sequence into segments (a pass computing each segment's state
+ *    increments, then the sweeps of all segments at once) and needs a scratch
+ *    buffer of N*H*segments*(E*M + E) floats (forward) or twice that
+ *    (backward); cp_workspace_size reports the bytes (0 when the call needs
+ *    none).  The caller may pass it as workspace (a device pointer, 16-byte
+ *    aligned, of workspace_bytes >= that size, overlapping no tensor of the
+ *    call; its contents need not be initialised and are undefined afterwards;
+ *    it must stay alive until the stream has run the call, and two calls
+ *    that may run at the same time need two workspaces): then the call
+ *    allocates nothing.  With workspace NULL (workspace_bytes ignored), a
+ *    call that needs scratch takes it from the stream-ordered allocator
+ *    (hipMallocAsync) and frees it on the same stream after its last use.
+ *    A workspace smaller than the call needs is CP_ERR_SCRATCH, one not
+ *    16-byte aligned CP_ERR_ALIGN, one overlapping a tensor CP_ERR_ALIAS.
  *  * stream is a hipStream_t (NULL = the default stream).  Calls only enqueue
  *    work: they never synchronise the host, and buffers must stay alive until
  *    the stream has run the work.  Calls are stateless, thread-safe and
@@ -75,8 +84,29 @@ typedef enum {
     CP_ERR_ALIGN = 4,       /* a pointer not 16-byte aligned                  */
     CP_ERR_ALIAS = 5,       /* an output overlaps an input or another output  */
     CP_ERR_HIP = 6,         /* the HIP runtime reported an error at launch    */
-    CP_ERR_SCRATCH = 7      /* more scratch than causal_product_fwd_noalloc holds */
+    CP_ERR_SCRATCH = 7      /* a workspace smaller than the call needs, or more
+                               scratch than causal_product_fwd_noalloc holds  */
 } cp_status;
+
+/* The operations, for cp_workspace_size. */
+typedef enum {
+    CP_OP_CAUSAL_FWD = 0,  /* causal_product_fwd  */
+    CP_OP_CAUSAL_BWD = 1,  /* causal_product_bwd  */
+    CP_OP_LINATTN_FWD = 2, /* linear_attn_fwd     */
+    CP_OP_LINATTN_BWD = 3  /* linear_attn_bwd     */
+} cp_op;
+
+/*
+ * cp_workspace_size: writes to *bytes the workspace that operation op (a
+ * cp_op) needs for these sizes and dtype, 0 when it needs none.  Host
+ * arithmetic only: no device is touched and nothing is enqueued.  The size
+ * depends on op, N*H, L, E, M and dtype only (not on which optional states a
+ * call passes).  CP_ERR_NULL for a NULL bytes, CP_ERR_UNSUPPORTED for an
+ * unknown op, otherwise the size checks of the entry points (CP_ERR_DIM,
+ * CP_ERR_UNSUPPORTED).
+ */
+int cp_workspace_size(int op, int64_t N, int64_t H, int64_t L, int64_t E, int64_t M, int dtype,
+                      int64_t *bytes);
 
 /*
  * causal_product_fwd: out_i = q_i^T S_i for every slice, with
@@ -92,13 +122,13 @@ typedef enum {
 int causal_product_fwd(const void *Q, const void *K, const void *V, void *Out,
                        const float *state_in, float *state_out,
                        int64_t N, int64_t H, int64_t L, int64_t E, int64_t M,
-                       int dtype, void *stream);
+                       int dtype, void *workspace, int64_t workspace_bytes, void *stream);
 
 /*
  * causal_product_fwd_noalloc: causal_product_fwd for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops,
- * harnesses that forbid allocation): the same arguments, kernels and results,
- * but the scratch of a forward over sequence segments (taken when N*H slices
+ * harnesses that forbid allocation) and hold no workspace of their own: the
+ * same arguments but the workspace, the same kernels and results, but the scratch of a forward over sequence segments (taken when N*H slices
  * are too few to fill the GPU: N*H*segments*(E*M + E) floats) lives in a
  * static device buffer of 16 MiB that the library holds on every GPU it runs
  * on until the process ends; the call itself allocates nothing.  A call that
@@ -140,7 +170,7 @@ int causal_product_bwd(const void *Q, const void *K, const void *V, const void *
                        const float *state_in, const float *state_final,
                        void *dQ, void *dK, void *dV, float *dstate_in,
                        int64_t N, int64_t H, int64_t L, int64_t E, int64_t M,
-                       int dtype, void *stream);
+                       int dtype, void *workspace, int64_t workspace_bytes, void *stream);
 
 /*
  * linear_attn_fwd: causal linear attention with its normaliser,
@@ -163,7 +193,8 @@ int linear_attn_fwd(const void *Q, const void *K, const void *V, void *Out,
                     const float *state_in, const float *z_in, float *state_out, float *z_out,
                     float *den_out,
                     int64_t N, int64_t H, int64_t L, int64_t E, int64_t M,
-                    float eps, int feature_map, int dtype, void *stream);
+                    float eps, int feature_map, int dtype,
+                    void *workspace, int64_t workspace_bytes, void *stream);
 
 /*
  * linear_attn_bwd: gradients of f = sum_i Out_i . dOut_i for the normalised
@@ -198,7 +229,8 @@ int linear_attn_bwd(const void *Q, const void *K, const void *V, const void *Out
                     const float *state_final, const float *z_final,
                     void *dQ, void *dK, void *dV, float *dstate_in, float *dz_in,
                     int64_t N, int64_t H, int64_t L, int64_t E, int64_t M,
-                    int feature_map, int dtype, void *stream);
+                    int feature_map, int dtype,
+                    void *workspace, int64_t workspace_bytes, void *stream);
 
 /* Static, NUL-terminated description of a cp_status value (never NULL). */
 const char *cp_status_string(int status);
@@ -208,7 +240,8 @@ const char *cp_status_string(int status);
  * (both additions: every 3.0 call behaves as before); 4.0: cp_timing_end
  * takes the capacity of the caller's buffer; 4.1: causal_product_fwd_noalloc
  * and CP_ERR_SCRATCH; 5.0: linear_attn_bwd takes z_final (and allocates
- * only over sequence segments). */
+ * only over sequence segments); 6.0: the four operations take a caller's
+ * workspace, cp_workspace_size. */
 int cp_abi_version(void);
 
 /*

@@ -3,11 +3,13 @@
 Thin Python binding of the C ABI in ``include/causalprod.h`` (library
 ``libcausalprod.so`` built next to this file by ``build.py``).  Every step of
 the computation runs in the HIP kernels behind that ABI; this module only
-checks tensors, allocates outputs through PyTorch and passes raw device
-pointers and the current HIP stream.  There is no fallback: if the library is
-missing the import fails.
+checks tensors, allocates outputs (and, over few slices, the calls'
+workspaces) through PyTorch and passes raw device pointers and the current
+HIP stream.  There is no fallback: if the library is missing the import
+fails.
 
-Functions with the ABI's names (optional tensors and outputs are keyword-only):
+Functions with the ABI's names (optional tensors and outputs are keyword-only;
+each of the four operations also takes an optional ``workspace`` tensor):
     causal_product_fwd(q, k, v, *, out=None, state_in=None, state_out=None)
     causal_product_fwd_noalloc(q, k, v, *, out, state_in=None, state_out=None)
     causal_product_bwd(q, k, v, dout, *, state_final=None, state_in=None,
@@ -17,6 +19,7 @@ Functions with the ABI's names (optional tensors and outputs are keyword-only):
     linear_attn_bwd(q, k, v, out, dout, den, feature_map=1, *, state_in=None,
                     z_in=None, state_final=None, z_final=None, dq=None,
                     dk=None, dv=None, dstate_in=None, dz_in=None)
+    workspace_size(op, N, H, L, E, M, dtype)   (cp_workspace_size)
 and autograd wrappers ``causal_product(q, k, v, state0=None)`` and
 ``linear_attention(q, k, v, eps=1e-6, feature_map="elu+1")``.
 
@@ -28,6 +31,7 @@ backward), with head sizes E, M <= 128 whose rows are whole 16-byte pieces
 from __future__ import annotations
 
 import ctypes
+import functools
 import os
 import threading
 
@@ -39,6 +43,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("CAUSALPROD_LIB") or os.path.join(HERE, "libcausalprod.so")
 
 CP_F32, CP_BF16, CP_F16 = 0, 1, 2
+CP_OP_CAUSAL_FWD, CP_OP_CAUSAL_BWD, CP_OP_LINATTN_FWD, CP_OP_LINATTN_BWD = 0, 1, 2, 3
 STATUS = {0: "CP_OK", 1: "CP_ERR_NULL", 2: "CP_ERR_DIM", 3: "CP_ERR_UNSUPPORTED", 4: "CP_ERR_ALIGN",
           5: "CP_ERR_ALIAS", 6: "CP_ERR_HIP", 7: "CP_ERR_SCRATCH"}
 # Kernel tile sizes: a head of E (or M) features runs on the smallest tile >= E,
@@ -50,16 +55,18 @@ if not os.path.exists(LIB_PATH):
 lib = ctypes.CDLL(LIB_PATH)
 
 _vp, _i64, _int = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
-lib.causal_product_fwd.argtypes = [_vp] * 6 + [_i64] * 5 + [_int, _vp]
+lib.causal_product_fwd.argtypes = [_vp] * 6 + [_i64] * 5 + [_int, _vp, _i64, _vp]
 lib.causal_product_fwd.restype = _int
 lib.causal_product_fwd_noalloc.argtypes = [_vp] * 6 + [_i64] * 5 + [_int, _vp]
 lib.causal_product_fwd_noalloc.restype = _int
-lib.causal_product_bwd.argtypes = [_vp] * 10 + [_i64] * 5 + [_int, _vp]
+lib.causal_product_bwd.argtypes = [_vp] * 10 + [_i64] * 5 + [_int, _vp, _i64, _vp]
 lib.causal_product_bwd.restype = _int
-lib.linear_attn_fwd.argtypes = [_vp] * 9 + [_i64] * 5 + [ctypes.c_float, _int, _int, _vp]
-lib.linear_attn_bwd.argtypes = [_vp] * 15 + [_i64] * 5 + [_int, _int, _vp]
+lib.linear_attn_fwd.argtypes = [_vp] * 9 + [_i64] * 5 + [ctypes.c_float, _int, _int, _vp, _i64, _vp]
+lib.linear_attn_bwd.argtypes = [_vp] * 15 + [_i64] * 5 + [_int, _int, _vp, _i64, _vp]
 lib.linear_attn_bwd.restype = _int
 lib.linear_attn_fwd.restype = _int
+lib.cp_workspace_size.argtypes = [_int] + [_i64] * 5 + [_int, ctypes.POINTER(_i64)]
+lib.cp_workspace_size.restype = _int
 lib.cp_status_string.argtypes = [_int]
 lib.cp_status_string.restype = ctypes.c_char_p
 lib.cp_abi_version.argtypes = []
@@ -140,6 +147,36 @@ def timing_end() -> list:
 _timing = threading.local()
 
 
+@functools.lru_cache(maxsize=256)
+def workspace_size(op: int, N: int, H: int, L: int, E: int, M: int, dtype: int) -> int:
+    """Bytes of workspace operation ``op`` (CP_OP_*) needs for these sizes
+    and dtype code (0: none); host arithmetic in the library."""
+    n = _i64(0)
+    _check("cp_workspace_size", lib.cp_workspace_size(op, N, H, L, E, M, dtype, ctypes.byref(n)))
+    return n.value
+
+
+_ws_bytes = {}  # (op, sizes, dtype) -> workspace_size, without the cache wrapper's cost per call
+
+
+def _workspace(op, q, N, H, L, E, M, workspace):
+    """(pointer, bytes, tensor) of the workspace of a call: the caller's
+    tensor, or one from PyTorch's allocator on the current stream when the
+    call needs one (it stays valid for the work enqueued on that stream)."""
+    if workspace is not None:
+        if not workspace.is_cuda or not workspace.is_contiguous() or workspace.device != q.device:
+            raise ValueError("workspace must be a contiguous tensor on q's device")
+        return ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size(), workspace
+    key = (op, N, H, L, E, M, q.dtype)
+    n = _ws_bytes.get(key)
+    if n is None:
+        n = _ws_bytes[key] = workspace_size(op, N, H, L, E, M, _dtype_code(q))
+    if n == 0:
+        return None, 0, None
+    t = torch.empty(n, dtype=torch.uint8, device=q.device)
+    return ctypes.c_void_p(t.data_ptr()), n, t
+
+
 def _check_state(name, t, shape, device):
     """An optional fp32 state tensor (None passes)."""
     if t is not None and (t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != shape
@@ -147,10 +184,12 @@ def _check_state(name, t, shape, device):
         raise ValueError(f"{name} must be a contiguous float32 {list(shape)} tensor on q's device")
 
 
-def causal_product_fwd(q, k, v, *, out=None, state_in=None, state_out=None):
+def causal_product_fwd(q, k, v, *, out=None, state_in=None, state_out=None, workspace=None):
     """out_i = q_i^T S_i with S_i = S0 + sum_{j<=i} k_j v_j^T.  ``state_in``
     (fp32 [N,H,E,M], optional, None = zero) is S0; ``state_out`` (optional)
-    receives the final state S_{L-1}."""
+    receives the final state S_{L-1}.  ``workspace`` (optional): a device
+    tensor of at least workspace_size(CP_OP_CAUSAL_FWD, ...) bytes; by default
+    one comes from PyTorch's allocator when the call needs it."""
     N, H, L, E, M = _dims(q, v)
     if k.shape != q.shape:
         raise ValueError("k must have q's shape")
@@ -159,9 +198,10 @@ def causal_product_fwd(q, k, v, *, out=None, state_in=None, state_out=None):
     _check_tensors(q, k, v, out)
     _check_state("state_in", state_in, (N, H, E, M), q.device)
     _check_state("state_out", state_out, (N, H, E, M), q.device)
+    wp, wn, _wt = _workspace(CP_OP_CAUSAL_FWD, q, N, H, L, E, M, workspace)
     _check("causal_product_fwd", lib.causal_product_fwd(
         _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(state_in), _ptr(state_out), N, H, L, E, M, _dtype_code(q),
-        _stream(q.device)))
+        wp, wn, _stream(q.device)))
     return out
 
 
@@ -184,12 +224,13 @@ def causal_product_fwd_noalloc(q, k, v, *, out, state_in=None, state_out=None):
 
 
 def causal_product_bwd(q, k, v, dout, *, state_final=None, state_in=None, dq=None, dk=None, dv=None,
-                       dstate_in=None):
+                       dstate_in=None, workspace=None):
     """Gradients (dq, dk, dv) of sum(out * dout) for out = causal_product_fwd(q, k, v, state_in=S0).
     ``state_final``: optional final state from causal_product_fwd's state_out;
     ``state_in``: the S0 the forward started from (read only without
     state_final); ``dstate_in`` (optional fp32 [N,H,E,M]) receives the
-    gradient of S0, sum_i q_i dout_i^T."""
+    gradient of S0, sum_i q_i dout_i^T.  ``workspace``: as for
+    causal_product_fwd (CP_OP_CAUSAL_BWD)."""
     N, H, L, E, M = _dims(q, v)
     if k.shape != q.shape or dout.shape != v.shape:
         raise ValueError("k must have q's shape and dout v's shape")
@@ -199,19 +240,21 @@ def causal_product_bwd(q, k, v, dout, *, state_final=None, state_in=None, dq=Non
     _check_tensors(q, k, v, dout, dq, dk, dv)
     for name, t in (("state_final", state_final), ("state_in", state_in), ("dstate_in", dstate_in)):
         _check_state(name, t, (N, H, E, M), q.device)
+    wp, wn, _wt = _workspace(CP_OP_CAUSAL_BWD, q, N, H, L, E, M, workspace)
     _check("causal_product_bwd", lib.causal_product_bwd(
         _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(state_in), _ptr(state_final), _ptr(dq), _ptr(dk), _ptr(dv),
-        _ptr(dstate_in), N, H, L, E, M, _dtype_code(q), _stream(q.device)))
+        _ptr(dstate_in), N, H, L, E, M, _dtype_code(q), wp, wn, _stream(q.device)))
     return dq, dk, dv
 
 
 def linear_attn_fwd(q, k, v, eps: float = 1e-6, feature_map: int = 1, *, out=None, state_in=None, z_in=None,
-                    state_out=None, z_out=None, den_out=None):
+                    state_out=None, z_out=None, den_out=None, workspace=None):
     """out_i = phi(q_i)^T S_i / (phi(q_i) . z_i + eps) with phi = elu + 1
     (feature_map=1) or the identity (feature_map=0) applied to the raw q, k.
     Optional fp32 states: state_in [N,H,E,M] and z_in [N,H,E] before the
     first row (None = zero); state_out, z_out receive the final S and z;
-    den_out [N,H,L] receives the denominators (for linear_attn_bwd)."""
+    den_out [N,H,L] receives the denominators (for linear_attn_bwd).
+    ``workspace``: as for causal_product_fwd (CP_OP_LINATTN_FWD)."""
     N, H, L, E, M = _dims(q, v)
     if k.shape != q.shape:
         raise ValueError("k must have q's shape")
@@ -222,21 +265,23 @@ def linear_attn_fwd(q, k, v, eps: float = 1e-6, feature_map: int = 1, *, out=Non
                            ("state_out", state_out, (N, H, E, M)), ("z_out", z_out, (N, H, E)),
                            ("den_out", den_out, (N, H, L))):
         _check_state(name, t, shape, q.device)
+    wp, wn, _wt = _workspace(CP_OP_LINATTN_FWD, q, N, H, L, E, M, workspace)
     _check("linear_attn_fwd", lib.linear_attn_fwd(
         _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(state_in), _ptr(z_in), _ptr(state_out), _ptr(z_out),
-        _ptr(den_out), N, H, L, E, M, float(eps), int(feature_map), _dtype_code(q), _stream(q.device)))
+        _ptr(den_out), N, H, L, E, M, float(eps), int(feature_map), _dtype_code(q), wp, wn, _stream(q.device)))
     return out
 
 
 def linear_attn_bwd(q, k, v, out, dout, den, feature_map: int = 1, *, state_in=None, z_in=None, state_final=None,
-                    z_final=None, dq=None, dk=None, dv=None, dstate_in=None, dz_in=None):
+                    z_final=None, dq=None, dk=None, dv=None, dstate_in=None, dz_in=None, workspace=None):
     """Gradients (dq, dk, dv) of sum(out * dout) for out = linear_attn_fwd(q, k, v, ...),
     with respect to the raw q, k (through phi), v; ``den`` is the forward's
     den_out.  state_in / z_in: the initial states the forward started from
     (pass them whenever it had them); state_final, z_final: the forward's
     final S and z (its state_out and z_out), an optional shortcut taken as a
     pair (read for bf16 only); dstate_in [N,H,E,M] and dz_in [N,H,E] receive
-    the gradients of the initial states."""
+    the gradients of the initial states.  ``workspace``: as for
+    causal_product_fwd (CP_OP_LINATTN_BWD)."""
     N, H, L, E, M = _dims(q, v)
     if k.shape != q.shape or dout.shape != v.shape or out.shape != v.shape:
         raise ValueError("k must have q's shape, out and dout v's shape")
@@ -250,10 +295,11 @@ def linear_attn_bwd(q, k, v, out, dout, den, feature_map: int = 1, *, state_in=N
         _check_state(name, t, shape, q.device)
     if den is None:
         raise ValueError("den (the forward's den_out) is required")
+    wp, wn, _wt = _workspace(CP_OP_LINATTN_BWD, q, N, H, L, E, M, workspace)
     _check("linear_attn_bwd", lib.linear_attn_bwd(
         _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(den), _ptr(state_in), _ptr(z_in), _ptr(state_final),
         _ptr(z_final), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dstate_in), _ptr(dz_in), N, H, L, E, M, int(feature_map),
-        _dtype_code(q), _stream(q.device)))
+        _dtype_code(q), wp, wn, _stream(q.device)))
     return dq, dk, dv
 
 
@@ -317,5 +363,5 @@ def linear_attention(q, k, v, eps: float = 1e-6, feature_map: str = "elu+1"):
     return LinearAttention.apply(q, k, v, eps, fm)
 
 
-__all__ = ["causal_product_fwd", "causal_product_fwd_noalloc", "causal_product_bwd", "linear_attn_fwd", "linear_attn_bwd", "causal_product", "linear_attention",
+__all__ = ["causal_product_fwd", "causal_product_fwd_noalloc", "causal_product_bwd", "linear_attn_fwd", "linear_attn_bwd", "workspace_size", "causal_product", "linear_attention",
            "CausalProductError", "lib", "LIB_PATH", "timing_begin", "timing_end"]

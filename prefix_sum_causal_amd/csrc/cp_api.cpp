@@ -29,10 +29,11 @@ static __device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
 
 namespace {
 
-constexpr int kAbiMajor = 5, kAbiMinor = 0;  // 3.0: carried state, normalised backward; 3.1: fp16 I/O;
+constexpr int kAbiMajor = 6, kAbiMinor = 0;  // 3.0: carried state, normalised backward; 3.1: fp16 I/O;
                                              // 4.0: cp_timing_end bounded by the caller's buffer;
                                              // 4.1: causal_product_fwd_noalloc;
-                                             // 5.0: linear_attn_bwd takes z_final, no scratch unsplit
+                                             // 5.0: linear_attn_bwd takes z_final, no scratch unsplit;
+                                             // 6.0: caller workspaces, cp_workspace_size
 
 cp::fwd_fn pick_fwd(int dtype, int E, int M, bool norm) {
     return dtype == CP_BF16 ? cp::fwd_bf16(E, M, norm) : dtype == CP_F16 ? cp::fwd_f16(E, M, norm) : cp::fwd_f32(E, M, norm);
@@ -43,6 +44,23 @@ cp::bwd_fn pick_bwd(int dtype, int E, int M, bool norm) {
 }
 
 int launch_status(hipError_t e) { return e == hipSuccess ? CP_OK : CP_ERR_HIP; }
+
+// A call with the caller's workspace: the bytes it needs (host arithmetic,
+// nothing launched), then the call itself on that workspace.  Without a
+// workspace the launcher allocates what it needs.
+template <typename Fn, typename Args>
+int run_with_workspace(Fn fn, Args a, void *ws, int64_t ws_bytes, hipStream_t stream) {
+    if (ws) {
+        size_t need = 0;
+        a.ws_need = &need;
+        if (fn(a, stream) != hipSuccess) return CP_ERR_HIP;
+        if (ws_bytes < 0 || need > (uint64_t)ws_bytes) return CP_ERR_SCRATCH;
+        a.ws_need = nullptr;
+        a.ws = static_cast<float *>(ws);
+        a.ws_bytes = (size_t)ws_bytes;
+    }
+    return launch_status(fn(a, stream));
+}
 
 // Per-thread kernel timing (cp_timing_begin / cp_timing_end).
 struct Timing {
@@ -154,21 +172,49 @@ const char *cp_status_string(int status) {
         case CP_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
         case CP_ERR_ALIAS: return "an output overlaps an input or another output";
         case CP_ERR_HIP: return "the HIP runtime reported an error when launching the kernel";
-        case CP_ERR_SCRATCH: return "the call needs more scratch than the no-allocation entry point holds (16 MiB); use causal_product_fwd";
+        case CP_ERR_SCRATCH: return "the workspace is smaller than the call needs (cp_workspace_size), or the call needs more scratch than the no-allocation entry point holds (16 MiB)";
         default: return "unknown status";
     }
 }
 
+int cp_workspace_size(int op, int64_t N, int64_t H, int64_t L, int64_t E, int64_t M, int dtype, int64_t *bytes) {
+    if (!bytes) return CP_ERR_NULL;
+    if (op < CP_OP_CAUSAL_FWD || op > CP_OP_LINATTN_BWD) return CP_ERR_UNSUPPORTED;
+    int64_t ne = 0, nm = 0;
+    const int st = cp::check_dims(N, H, L, E, M, dtype, ne, nm);
+    if (st != CP_OK) return st;
+    const bool norm = op == CP_OP_LINATTN_FWD || op == CP_OP_LINATTN_BWD;
+    size_t need = 0;
+    hipError_t e = hipSuccess;
+    if (op == CP_OP_CAUSAL_FWD || op == CP_OP_LINATTN_FWD) {
+        cp::fwd_fn fn = pick_fwd(dtype, (int)E, (int)M, norm);
+        if (!fn) return CP_ERR_UNSUPPORTED;
+        cp::FwdArgs a{};
+        a.L = (int)L, a.NS = (int)(N * H), a.Ea = (int)E, a.Ma = (int)M, a.ws_need = &need;
+        e = fn(a, nullptr);
+    } else {
+        cp::bwd_fn fn = pick_bwd(dtype, (int)E, (int)M, norm);
+        if (!fn) return CP_ERR_UNSUPPORTED;
+        cp::BwdArgs a{};
+        a.L = (int)L, a.NS = (int)(N * H), a.Ea = (int)E, a.Ma = (int)M, a.ws_need = &need;
+        e = fn(a, nullptr);
+    }
+    if (e != hipSuccess) return CP_ERR_HIP;
+    *bytes = (int64_t)need;
+    return CP_OK;
+}
+
 int causal_product_fwd(const void *Q, const void *K, const void *V, void *Out, const float *state_in,
                        float *state_out, int64_t N, int64_t H, int64_t L, int64_t E, int64_t M, int dtype,
-                       void *stream) {
-    const int st = cp::validate_fwd(Q, K, V, Out, state_in, state_out, N, H, L, E, M, dtype);
+                       void *workspace, int64_t workspace_bytes, void *stream) {
+    const int st = cp::validate_fwd(Q, K, V, Out, state_in, state_out, N, H, L, E, M, dtype, workspace,
+                                    workspace_bytes);
     if (st != CP_OK) return st;
     cp::fwd_fn fn = pick_fwd(dtype, (int)E, (int)M, false);
     if (!fn) return CP_ERR_UNSUPPORTED;
     cp::FwdArgs a{Q,      K,      V, Out, state_in, nullptr, state_out, nullptr, nullptr, (int)L, (int)(N * H), 0.f,
                   0,      (int)E, (int)M};
-    return launch_status(fn(a, static_cast<hipStream_t>(stream)));
+    return run_with_workspace(fn, a, workspace, workspace_bytes, static_cast<hipStream_t>(stream));
 }
 
 int causal_product_fwd_noalloc(const void *Q, const void *K, const void *V, void *Out, const float *state_in,
@@ -197,41 +243,46 @@ int causal_product_fwd_noalloc(const void *Q, const void *K, const void *V, void
 
 int causal_product_bwd(const void *Q, const void *K, const void *V, const void *dOut, const float *state_in,
                        const float *state_final, void *dQ, void *dK, void *dV, float *dstate_in, int64_t N,
-                       int64_t H, int64_t L, int64_t E, int64_t M, int dtype, void *stream) {
-    const int st = cp::validate_bwd(Q, K, V, dOut, state_in, state_final, dQ, dK, dV, dstate_in, N, H, L, E, M, dtype);
+                       int64_t H, int64_t L, int64_t E, int64_t M, int dtype, void *workspace,
+                       int64_t workspace_bytes, void *stream) {
+    const int st = cp::validate_bwd(Q, K, V, dOut, state_in, state_final, dQ, dK, dV, dstate_in, N, H, L, E, M, dtype,
+                                    workspace, workspace_bytes);
     if (st != CP_OK) return st;
     cp::bwd_fn fn = pick_bwd(dtype, (int)E, (int)M, false);
     if (!fn) return CP_ERR_UNSUPPORTED;
     cp::BwdArgs a{Q,       K,       V,       dOut,    state_in, state_final, dQ,     dK,    dV, dstate_in, (int)L,
                   (int)(N * H), nullptr, nullptr, nullptr, nullptr, nullptr, 0, (int)E, (int)M};
-    return launch_status(fn(a, static_cast<hipStream_t>(stream)));
+    return run_with_workspace(fn, a, workspace, workspace_bytes, static_cast<hipStream_t>(stream));
 }
 
 int linear_attn_fwd(const void *Q, const void *K, const void *V, void *Out, const float *state_in,
                     const float *z_in, float *state_out, float *z_out, float *den_out, int64_t N, int64_t H,
-                    int64_t L, int64_t E, int64_t M, float eps, int feature_map, int dtype, void *stream) {
+                    int64_t L, int64_t E, int64_t M, float eps, int feature_map, int dtype, void *workspace,
+                    int64_t workspace_bytes, void *stream) {
     const int st = cp::validate_linattn_fwd(Q, K, V, Out, state_in, z_in, state_out, z_out, den_out, N, H, L, E, M, eps,
-                                            feature_map, dtype);
+                                            feature_map, dtype, workspace, workspace_bytes);
     if (st != CP_OK) return st;
     cp::fwd_fn fn = pick_fwd(dtype, (int)E, (int)M, true);
     if (!fn) return CP_ERR_UNSUPPORTED;
     cp::FwdArgs a{Q,           K,      V,     Out, state_in, z_in, state_out, z_out, den_out, (int)L, (int)(N * H), eps,
                   feature_map, (int)E, (int)M};
-    return launch_status(fn(a, static_cast<hipStream_t>(stream)));
+    return run_with_workspace(fn, a, workspace, workspace_bytes, static_cast<hipStream_t>(stream));
 }
 
 int linear_attn_bwd(const void *Q, const void *K, const void *V, const void *Out, const void *dOut,
                     const float *den, const float *state_in, const float *z_in, const float *state_final,
                     const float *z_final, void *dQ, void *dK, void *dV, float *dstate_in, float *dz_in, int64_t N,
-                    int64_t H, int64_t L, int64_t E, int64_t M, int feature_map, int dtype, void *stream) {
+                    int64_t H, int64_t L, int64_t E, int64_t M, int feature_map, int dtype, void *workspace,
+                    int64_t workspace_bytes, void *stream) {
     const int st = cp::validate_linattn_bwd(Q, K, V, Out, dOut, den, state_in, z_in, state_final, z_final, dQ, dK,
-                                            dV, dstate_in, dz_in, N, H, L, E, M, feature_map, dtype);
+                                            dV, dstate_in, dz_in, N, H, L, E, M, feature_map, dtype, workspace,
+                                            workspace_bytes);
     if (st != CP_OK) return st;
     cp::bwd_fn fn = pick_bwd(dtype, (int)E, (int)M, true);
     if (!fn) return CP_ERR_UNSUPPORTED;
     cp::BwdArgs a{Q,      K,      V,     dOut,  state_in, state_final, dQ,  dK, dV, dstate_in, (int)L, (int)(N * H),
                   Out,    den,    z_in,  z_final, dz_in, feature_map, (int)E, (int)M};
-    return launch_status(fn(a, static_cast<hipStream_t>(stream)));
+    return run_with_workspace(fn, a, workspace, workspace_bytes, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

@@ -20,9 +20,10 @@ namespace cp {
 // as in the forward.  The first computes every segment's increments of the
 // prefix state (sum of k v^T, all but the last segment; normalised form: with
 // the sum of phi(k)) and of the suffix state (sum of q dO^T, all but the
-// first; normalised form: of phi(q) dn^T, with the sum of dd phi(q)) into a
-// stream-ordered scratch buffer; the second sweeps each segment with the
-// states at its ends summed from those increments (see SegCarry).
+// first; normalised form: of phi(q) dn^T, with the sum of dd phi(q)) into
+// the caller's workspace or, without one, a stream-ordered scratch buffer;
+// the second sweeps each segment with the states at its ends summed from
+// those increments (see SegCarry).
 template <typename T, int E, int M, bool NORM, bool FMAP>
 hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t s) {
     using P = Tune<T, E, M>;
@@ -37,12 +38,25 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t s) {
     const SegPlan plan = plan_segments(L, NS, P::BG * P::BRG, C, kBwdSegWgPerCU);
     const int nseg = plan.nseg;
     int seg_len = plan.seg_len;
+    constexpr int WS = E * M + E;
+    // prefix then suffix increments: per slice and segment E x M then E floats each
+    const size_t need = nseg > 1 ? (size_t)2 * NS * nseg * WS * sizeof(float) : 0;
+    if (a.ws_need) {
+        *a.ws_need = need;
+        return hipSuccess;
+    }
     float *ws = nullptr;
+    bool owned = false;
     hipError_t e = hipSuccess;
     if (nseg > 1) {
-        constexpr int WS = E * M + E;
-        e = hipMallocAsync(reinterpret_cast<void **>(&ws), (size_t)2 * NS * nseg * WS * sizeof(float), s);
-        if (e != hipSuccess) return e;
+        if (a.ws) {
+            if (a.ws_bytes < need) return hipErrorInvalidValue;
+            ws = a.ws;
+        } else {
+            e = hipMallocAsync(reinterpret_cast<void **>(&ws), need, s);
+            if (e != hipSuccess) return e;
+            owned = true;
+        }
         // with the final states used, the sweeps subtract the later segments'
         // increments from them: the prefix increments of segments 1 .. nseg-1
         const bool use_final = st && (!NORM || zf) && !(NORM && std::is_same<T, float>::value);
@@ -61,7 +75,7 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t s) {
         e = launch_kernel(reinterpret_cast<const void *>(kern), dim3(NS * P::BG * P::BRG * nseg),
                           dim3(64 * bwd_waves<E, M, P::BG, P::BNB, P::BIDLE>()), args, s);
     }
-    if (ws) {
+    if (owned) {
         const hipError_t f = hipFreeAsync(ws, s);
         if (e == hipSuccess) e = f;
     }

@@ -24,10 +24,10 @@ struct FwdArgs {
     int Ea, Ma;  // head sizes of the tensors (the kernel runs the next tile size up)
     // Scratch of a forward over sequence segments.  ws_need != NULL: only
     // report the bytes the call needs (0 without segments) and launch
-    // nothing.  ws != NULL: use ws_bytes bytes at ws (a call that needs more
-    // fails) and allocate nothing; with ws == NULL and noalloc set, a call
-    // that needs scratch fails; otherwise it comes from the stream-ordered
-    // allocator.
+    // nothing (the pointers are not read).  ws != NULL: use ws_bytes bytes at
+    // ws (a call that needs more fails) and allocate nothing; with ws == NULL
+    // and noalloc set, a call that needs scratch fails; otherwise it comes
+    // from the stream-ordered allocator.
     size_t *ws_need = nullptr;
     float *ws = nullptr;
     size_t ws_bytes = 0;
@@ -49,6 +49,11 @@ struct BwdArgs {
     float *dz_in;
     int fmap;
     int Ea, Ma;  // head sizes of the tensors (the kernel runs the next tile size up)
+    // Scratch of a backward over sequence segments, as for FwdArgs (no
+    // noalloc flag: every backward either gets ws or may allocate).
+    size_t *ws_need = nullptr;
+    float *ws = nullptr;
+    size_t ws_bytes = 0;
 };
 
 // stages of the load ring of the segment-increment pass, and its waves (at

@@ -71,7 +71,8 @@ inline int check_opt_ptrs(std::initializer_list<const void *> ptrs) {
 }
 
 // Every output must be disjoint from every input and from the other outputs
-// (a NULL optional pointer has an empty range and overlaps nothing).
+// (a NULL optional pointer has an empty range and overlaps nothing).  A
+// caller's workspace (ws, ws_bytes) counts as an output.
 inline int check_alias(std::initializer_list<Range> ins, std::initializer_list<Range> outs) {
     for (auto o = outs.begin(); o != outs.end(); ++o) {
         for (const Range &i : ins)
@@ -94,39 +95,42 @@ inline Range span(const void *p, int64_t bytes) {
 inline int64_t elem_bytes(int dtype) { return dtype == CP_F32 ? 4 : 2; }
 
 inline int validate_fwd(const void *Q, const void *K, const void *V, const void *Out, const float *state_in,
-                        const float *state_out, int64_t N, int64_t H, int64_t L, int64_t E, int64_t M, int dtype) {
+                        const float *state_out, int64_t N, int64_t H, int64_t L, int64_t E, int64_t M, int dtype,
+                        const void *ws = nullptr, int64_t ws_bytes = 0) {
     int64_t ne = 0, nm = 0;
     int st = check_dims(N, H, L, E, M, dtype, ne, nm);
     if (st != CP_OK) return st;
     st = check_ptrs({Q, K, V, Out});
     if (st != CP_OK) return st;
-    st = check_opt_ptrs({state_in, state_out});
+    st = check_opt_ptrs({state_in, state_out, ws});
     if (st != CP_OK) return st;
     const int64_t es = elem_bytes(dtype), ns = N * H * E * M * 4;
     return check_alias({span(Q, ne * es), span(K, ne * es), span(V, nm * es), span(state_in, ns)},
-                       {span(Out, nm * es), span(state_out, ns)});
+                       {span(Out, nm * es), span(state_out, ns), span(ws, ws_bytes)});
 }
 
 inline int validate_bwd(const void *Q, const void *K, const void *V, const void *dOut, const float *state_in,
                         const float *state_final, const void *dQ, const void *dK, const void *dV,
-                        const float *dstate_in, int64_t N, int64_t H, int64_t L, int64_t E, int64_t M, int dtype) {
+                        const float *dstate_in, int64_t N, int64_t H, int64_t L, int64_t E, int64_t M, int dtype,
+                        const void *ws = nullptr, int64_t ws_bytes = 0) {
     int64_t ne = 0, nm = 0;
     int st = check_dims(N, H, L, E, M, dtype, ne, nm);
     if (st != CP_OK) return st;
     st = check_ptrs({Q, K, V, dOut, dQ, dK, dV});
     if (st != CP_OK) return st;
-    st = check_opt_ptrs({state_in, state_final, dstate_in});
+    st = check_opt_ptrs({state_in, state_final, dstate_in, ws});
     if (st != CP_OK) return st;
     const int64_t es = elem_bytes(dtype), ns = N * H * E * M * 4;
     return check_alias({span(Q, ne * es), span(K, ne * es), span(V, nm * es), span(dOut, nm * es),
                         span(state_in, ns), span(state_final, ns)},
-                       {span(dQ, ne * es), span(dK, ne * es), span(dV, nm * es), span(dstate_in, ns)});
+                       {span(dQ, ne * es), span(dK, ne * es), span(dV, nm * es), span(dstate_in, ns), span(ws, ws_bytes)});
 }
 
 inline int validate_linattn_fwd(const void *Q, const void *K, const void *V, const void *Out, const float *state_in,
                                 const float *z_in, const float *state_out, const float *z_out, const float *den_out,
                                 int64_t N, int64_t H, int64_t L, int64_t E, int64_t M, float eps, int feature_map,
-                                int dtype) {
+                                int dtype,
+                                const void *ws = nullptr, int64_t ws_bytes = 0) {
     int64_t ne = 0, nm = 0;
     int st = check_dims(N, H, L, E, M, dtype, ne, nm);
     if (st != CP_OK) return st;
@@ -134,32 +138,33 @@ inline int validate_linattn_fwd(const void *Q, const void *K, const void *V, con
     if (!(eps >= 0.f) || !std::isfinite(eps)) return CP_ERR_UNSUPPORTED;
     st = check_ptrs({Q, K, V, Out});
     if (st != CP_OK) return st;
-    st = check_opt_ptrs({state_in, z_in, state_out, z_out, den_out});
+    st = check_opt_ptrs({state_in, z_in, state_out, z_out, den_out, ws});
     if (st != CP_OK) return st;
     const int64_t es = elem_bytes(dtype), ns = N * H * E * M * 4, nz = N * H * E * 4, nd = N * H * L * 4;
     return check_alias({span(Q, ne * es), span(K, ne * es), span(V, nm * es), span(state_in, ns), span(z_in, nz)},
-                       {span(Out, nm * es), span(state_out, ns), span(z_out, nz), span(den_out, nd)});
+                       {span(Out, nm * es), span(state_out, ns), span(z_out, nz), span(den_out, nd), span(ws, ws_bytes)});
 }
 
 inline int validate_linattn_bwd(const void *Q, const void *K, const void *V, const void *Out, const void *dOut,
                                 const float *den, const float *state_in, const float *z_in, const float *state_final,
                                 const float *z_final, const void *dQ, const void *dK, const void *dV,
                                 const float *dstate_in, const float *dz_in, int64_t N, int64_t H, int64_t L, int64_t E,
-                                int64_t M, int feature_map, int dtype) {
+                                int64_t M, int feature_map, int dtype,
+                                const void *ws = nullptr, int64_t ws_bytes = 0) {
     int64_t ne = 0, nm = 0;
     int st = check_dims(N, H, L, E, M, dtype, ne, nm);
     if (st != CP_OK) return st;
     if (feature_map != 0 && feature_map != 1) return CP_ERR_UNSUPPORTED;
     st = check_ptrs({Q, K, V, Out, dOut, den, dQ, dK, dV});
     if (st != CP_OK) return st;
-    st = check_opt_ptrs({state_in, z_in, state_final, z_final, dstate_in, dz_in});
+    st = check_opt_ptrs({state_in, z_in, state_final, z_final, dstate_in, dz_in, ws});
     if (st != CP_OK) return st;
     const int64_t es = elem_bytes(dtype), ns = N * H * E * M * 4, nz = N * H * E * 4, nd = N * H * L * 4;
     return check_alias({span(Q, ne * es), span(K, ne * es), span(V, nm * es), span(Out, nm * es),
                         span(dOut, nm * es), span(den, nd), span(state_in, ns), span(z_in, nz),
                         span(state_final, ns), span(z_final, nz)},
                        {span(dQ, ne * es), span(dK, ne * es), span(dV, nm * es), span(dstate_in, ns),
-                        span(dz_in, nz)});
+                        span(dz_in, nz), span(ws, ws_bytes)});
 }
 
 }  // namespace cp

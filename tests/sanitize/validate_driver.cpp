@@ -88,6 +88,18 @@ int main() {
     expect(validate_fwd(P(0), P(1), P(2), top, nullptr, nullptr, 2, 3, 100, 64, 64, CP_BF16), CP_OK, "top ok");
     expect(validate_fwd(top, P(1), P(2), static_cast<const char *>(top) - 32, nullptr, nullptr, 2, 3, 100, 64, 64,
                         CP_BF16), CP_ERR_ALIAS, "top alias");
+    // a caller's workspace counts as an output: aligned, disjoint from every tensor
+    expect(validate_fwd(P(0), P(1), P(2), P(3), nullptr, nullptr, 2, 3, 100, 64, 64, CP_BF16, P(11), 1 << 20), CP_OK,
+           "ws ok");
+    expect(validate_fwd(P(0), P(1), P(2), P(3), nullptr, nullptr, 2, 3, 100, 64, 64, CP_BF16,
+                        static_cast<const char *>(P(11)) + 4, 64), CP_ERR_ALIGN, "ws align");
+    expect(validate_bwd(P(0), P(1), P(2), P(3), nullptr, nullptr, P(6), P(7), P(8), nullptr, 2, 3, 100, 64, 64, CP_BF16,
+                        static_cast<const char *>(P(7)) + 64, 64), CP_ERR_ALIAS, "ws over dk");
+    expect(validate_linattn_fwd(P(0), P(1), P(2), P(3), nullptr, nullptr, nullptr, nullptr, F(4), 2, 3, 100, 64, 64,
+                                1e-6f, 1, CP_BF16, P(4), 16), CP_ERR_ALIAS, "ws over den_out");
+    expect(validate_linattn_bwd(P(0), P(1), P(2), P(3), P(4), F(5), nullptr, nullptr, nullptr, nullptr, P(7), P(8),
+                                P(9), nullptr, nullptr, 2, 3, 100, 64, 64, 1, CP_BF16, P(3), 16), CP_ERR_ALIAS,
+           "ws over out");
     // normalised form: flags and eps
     expect(validate_linattn_fwd(P(0), P(1), P(2), P(3), nullptr, nullptr, nullptr, nullptr, nullptr, 2, 3, 100, 64, 64,
                                 -1.f, 1, CP_BF16), CP_ERR_UNSUPPORTED, "eps < 0");

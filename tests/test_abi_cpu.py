@@ -22,11 +22,12 @@ def lib():
         pytest.skip("libcausalprod.so not built")
     lib = ctypes.CDLL(LIB)
     vp, i64, i = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
-    lib.causal_product_fwd.argtypes = [vp] * 6 + [i64] * 5 + [i, vp]
+    lib.causal_product_fwd.argtypes = [vp] * 6 + [i64] * 5 + [i, vp, i64, vp]
     lib.causal_product_fwd_noalloc.argtypes = [vp] * 6 + [i64] * 5 + [i, vp]
-    lib.causal_product_bwd.argtypes = [vp] * 10 + [i64] * 5 + [i, vp]
-    lib.linear_attn_fwd.argtypes = [vp] * 9 + [i64] * 5 + [ctypes.c_float, i, i, vp]
-    lib.linear_attn_bwd.argtypes = [vp] * 15 + [i64] * 5 + [i, i, vp]
+    lib.causal_product_bwd.argtypes = [vp] * 10 + [i64] * 5 + [i, vp, i64, vp]
+    lib.linear_attn_fwd.argtypes = [vp] * 9 + [i64] * 5 + [ctypes.c_float, i, i, vp, i64, vp]
+    lib.linear_attn_bwd.argtypes = [vp] * 15 + [i64] * 5 + [i, i, vp, i64, vp]
+    lib.cp_workspace_size.argtypes = [i] + [i64] * 5 + [i, ctypes.POINTER(i64)]
     lib.cp_status_string.restype = ctypes.c_char_p
     return lib
 
@@ -40,7 +41,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(
         ["causal_product_fwd", "causal_product_fwd_noalloc", "causal_product_bwd", "linear_attn_fwd",
-         "linear_attn_bwd", "cp_status_string", "cp_abi_version", "cp_timing_begin", "cp_timing_end"])
+         "linear_attn_bwd", "cp_workspace_size", "cp_status_string", "cp_abi_version", "cp_timing_begin",
+         "cp_timing_end"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -55,7 +57,7 @@ def test_status_strings_and_version(lib):
         assert msg and msg not in seen
         seen.add(msg)
     assert lib.cp_status_string(99).decode() == "unknown status"
-    assert lib.cp_abi_version() == (5 << 16) | 0
+    assert lib.cp_abi_version() == (6 << 16) | 0
 
 
 def test_timing_rejects_bad_arguments_before_any_device_call(lib):
@@ -76,23 +78,24 @@ A = [0x10_0000_0000 + n * 0x1_0000_0000 for n in range(12)]
 SHAPE = (2, 3, 100, 64, 32)
 
 
-def fwd(lib, q=A[0], k=A[1], v=A[2], o=A[3], s0=None, st=None, shape=SHAPE, dtype=1):
-    return lib.causal_product_fwd(q, k, v, o, s0, st, *shape, dtype, None)
+def fwd(lib, q=A[0], k=A[1], v=A[2], o=A[3], s0=None, st=None, shape=SHAPE, dtype=1, ws=None, wsb=0):
+    return lib.causal_product_fwd(q, k, v, o, s0, st, *shape, dtype, ws, wsb, None)
 
 
 def bwd(lib, q=A[0], k=A[1], v=A[2], g=A[3], s0=None, st=None, dq=A[4], dk=A[5], dv=A[6], ds0=None,
-        shape=SHAPE, dtype=1):
-    return lib.causal_product_bwd(q, k, v, g, s0, st, dq, dk, dv, ds0, *shape, dtype, None)
+        shape=SHAPE, dtype=1, ws=None, wsb=0):
+    return lib.causal_product_bwd(q, k, v, g, s0, st, dq, dk, dv, ds0, *shape, dtype, ws, wsb, None)
 
 
 def lin(lib, q=A[0], k=A[1], v=A[2], o=A[3], s0=None, z0=None, st=None, zt=None, den=None, shape=SHAPE, eps=1e-6,
-        fm=1, dtype=1):
-    return lib.linear_attn_fwd(q, k, v, o, s0, z0, st, zt, den, *shape, eps, fm, dtype, None)
+        fm=1, dtype=1, ws=None, wsb=0):
+    return lib.linear_attn_fwd(q, k, v, o, s0, z0, st, zt, den, *shape, eps, fm, dtype, ws, wsb, None)
 
 
 def linb(lib, q=A[0], k=A[1], v=A[2], o=A[3], g=A[4], den=A[5], s0=None, z0=None, st=None, zt=None, dq=A[6],
-         dk=A[7], dv=A[8], ds0=None, dz0=None, shape=SHAPE, fm=1, dtype=1):
-    return lib.linear_attn_bwd(q, k, v, o, g, den, s0, z0, st, zt, dq, dk, dv, ds0, dz0, *shape, fm, dtype, None)
+         dk=A[7], dv=A[8], ds0=None, dz0=None, shape=SHAPE, fm=1, dtype=1, ws=None, wsb=0):
+    return lib.linear_attn_bwd(q, k, v, o, g, den, s0, z0, st, zt, dq, dk, dv, ds0, dz0, *shape, fm, dtype, ws, wsb,
+                               None)
 
 
 @pytest.mark.parametrize("which", range(4))
@@ -222,3 +225,62 @@ def test_noalloc_forward_rejects_more_scratch_than_it_holds(lib, dtype):
     # 16.1 MiB > 16 MiB: refused before anything is enqueued (no device here)
     assert fwd_na(lib, shape=(2, 8, 16384, 128, 128), dtype=dtype) == SCRATCH
     assert "16 MiB" in lib.cp_status_string(SCRATCH).decode()
+
+
+# ---- workspaces (cp_workspace_size and the workspace arguments) ----
+
+FEW = (2, 8, 16384, 128, 128)  # 16 slices of 16384 rows: run as sequence segments
+
+
+def wsize(lib, op, shape, dtype=1):
+    n = ctypes.c_int64(-1)
+    st = lib.cp_workspace_size(op, *shape, dtype, ctypes.byref(n))
+    return st, n.value
+
+
+def test_workspace_size_rejects_bad_arguments(lib):
+    assert lib.cp_workspace_size(0, *SHAPE, 1, None) == NULL
+    assert wsize(lib, 4, SHAPE)[0] == UNSUP
+    assert wsize(lib, -1, SHAPE)[0] == UNSUP
+    assert wsize(lib, 0, (2, 3, 0, 64, 32))[0] == DIM
+    assert wsize(lib, 1, (2, 3, 100, 256, 32))[0] == UNSUP
+    assert wsize(lib, 0, SHAPE, dtype=5)[0] == UNSUP
+    assert wsize(lib, 3, SHAPE, dtype=2)[0] == UNSUP  # no fp16 normalised backward
+
+
+@pytest.mark.parametrize("op", range(4))
+def test_workspace_size_zero_when_the_slices_fill_the_gpu(lib, op):
+    # 128 slices of 4096 rows: one launch per call, no segments, no scratch
+    assert wsize(lib, op, (8, 16, 4096, 64, 64)) == (OK, 0)
+    assert wsize(lib, op, SHAPE) == (OK, 0)  # 100 rows: too short to split
+
+
+@pytest.mark.parametrize("op", range(4))
+def test_workspace_size_of_segmented_calls(lib, op):
+    st, n = wsize(lib, op, FEW)
+    assert st == OK and n > 0
+    per_seg = 16 * (128 * 128 + 128) * 4  # one increment per slice and segment
+    # forward: one increment per segment; backward: prefix and suffix ones
+    unit = per_seg * (1 if op in (0, 2) else 2)
+    assert n % unit == 0 and 2 <= n // unit <= 64
+    if op == 0:  # the figure the no-allocation forward refuses (16.1 MiB)
+        assert n == 16 * 16 * (128 * 128 + 128) * 4
+    # the same for the 16-bit types, and fp32 is planned on its own tiles
+    if op != 3:
+        assert wsize(lib, op, FEW, dtype=2) == (OK, n)
+    assert wsize(lib, op, FEW, dtype=0)[0] == OK
+
+
+def test_workspace_arguments_are_validated_before_any_device_call(lib):
+    # misaligned, overlapping an input or an output: refused by validation
+    assert fwd(lib, ws=A[11] + 8, wsb=1 << 20) == ALIGN
+    assert fwd(lib, ws=A[0], wsb=1 << 20) == ALIAS
+    assert bwd(lib, ws=A[4] + 16, wsb=64) == ALIAS
+    assert lin(lib, ws=A[2], wsb=16) == ALIAS
+    assert linb(lib, ws=A[8], wsb=16) == ALIAS
+    # too small for a segmented call: refused on the host (no device here)
+    for f, op in ((fwd, 0), (bwd, 1), (lin, 2), (linb, 3)):
+        need = wsize(lib, op, FEW)[1]
+        assert f(lib, shape=FEW, ws=A[11], wsb=need - 16) == SCRATCH, op
+        assert f(lib, shape=FEW, ws=A[11], wsb=-1) == SCRATCH, op
+    assert "cp_workspace_size" in lib.cp_status_string(SCRATCH).decode()
