@@ -73,11 +73,12 @@ def algorithmic_bytes(w, kind: str) -> int:
 
 
 def algorithmic_flops(w, kind: str) -> int:
-    """Multiply-adds of the recurrence itself (two flops each), per call:
-    forward 4EM per token*head (state update k v^T, read-out q^T S);
-    backward 10EM (S again, dq, the suffix state R, dk, dv); the normaliser
-    adds its running sum, dot product and division (3E + M), and its backward
-    runs the causal-product backward on M + 1 columns plus the per-row terms."""
+    """Flops of the recurrence itself, per call: the forward's two products of
+    E*M multiply-adds per token*head (state update k v^T, read-out q^T S),
+    4EM flops; the backward's five (S again, dq, the suffix state R, dk, dv),
+    10EM; the normaliser adds its running sum, dot product and division
+    (3E + M), and its backward runs the causal-product backward on M + 1
+    columns plus the per-row terms."""
     th = w.N * w.H * w.L
     E, M = w.E, w.M
     return th * {"fwd": 4 * E * M, "bwd": 10 * E * M, "linattn": 4 * E * M + 3 * E + M,
