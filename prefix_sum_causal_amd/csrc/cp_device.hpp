@@ -344,15 +344,21 @@ constexpr int lds_stride() {
 
 typedef int i32x4 __attribute__((__vector_size__(4 * sizeof(int))));
 
-// One thread's share of a chunk copy: rows [row0, row0 + C) and columns
-// [col0, col0 + W) of a row-major slice, as 16-byte pieces spread over the NT
-// threads of the workgroup (piece p = row * W*sizeof(T)/16 + column piece).
+// Row maps of a chunk copy: staged row r is row RM::map(r) of the chunk.
+struct AllRows {
+    __device__ static constexpr int map(int r) { return r; }
+};
+
+// One thread's share of a chunk copy: C rows (rows RM::map(0 .. C-1) of the
+// chunk at row0; all of them by default) and columns [col0, col0 + W) of a
+// row-major slice, as 16-byte pieces spread over the NT threads of the
+// workgroup (piece p = staged row * W*sizeof(T)/16 + column piece).
 // load() issues the buffer loads (rows outside [0, L) and columns at or past
 // the row's width wa read as zero: a narrower head is padded to W columns);
 // store() writes the pieces into the LDS copy, optionally through phi (the
 // elementwise feature map, with rows at or past L and padded columns kept
 // zero).
-template <typename T, int NT, int C, int W>
+template <typename T, int NT, int C, int W, typename RM = AllRows>
 struct Stage {
     static constexpr int NT_ = NT;
     static constexpr int PPR = W * (int)sizeof(T) / 16;  // pieces per row
@@ -369,7 +375,7 @@ struct Stage {
 #pragma unroll
         for (int i = 0; i < NP; ++i) {
             const int p = (int)threadIdx.x + i * NT;
-            const int row = p / PPR, cp = p % PPR;
+            const int row = RM::map(p / PPR), cp = p % PPR;
             int off = (row * X.ld + col0) * (int)sizeof(T) + cp * 16;
             if constexpr (P % NT != 0) off = p < P ? off : kVoid;  // past the range: zero
             off = col0 + cp * VEC < wa ? off : kVoid;                // padded column: zero
@@ -395,7 +401,7 @@ struct Stage {
                 // rows at or past L and padding columns were loaded as zero,
                 // and phi(0) = 1: such a piece is zeroed again, a select per
                 // 32-bit word rather than a branch
-                const bool keep = row0 + row < L && cp * VEC < wa;
+                const bool keep = row0 + RM::map(row) < L && cp * VEC < wa;
 #pragma unroll
                 for (int d = 0; d < 4; ++d) x[d] = keep ? x[d] : 0;
             }
@@ -631,6 +637,19 @@ template <int CB, int RG>
 constexpr int owned_count(int h) {
     return owned_index<CB, RG>(h, CB);
 }
+
+// Stage row map of the row blocks that row set H of RS owns, in order:
+// staged row r is chunk row 16 owned_block(H, r / 16) + r % 16.
+template <int CB, int RS, int H>
+struct OwnedRows {
+    __device__ static int map(int r) {
+        const int j = r >> 4;
+        int b = 0;
+#pragma unroll
+        for (int k = 0; k < owned_count<CB, RS>(H); ++k) b = j == k ? owned_block<CB, RS>(H, k) : b;
+        return 16 * b + (r & 15);
+    }
+};
 
 // Workgroup id -> (slice, part).  The P parts of one (n, h) slice read the
 // same rows of the inputs, so they are kept on one XCD (workgroups are

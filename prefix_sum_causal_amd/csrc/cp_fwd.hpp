@@ -69,9 +69,15 @@ __device__ __forceinline__ void fwd_sweep(const T *q_, const T *k_, const T *v_,
     constexpr int NT = 64 * (NW * RSPLIT + (NORM && DW ? 1 : 0)), MW = 16 * NW;
     constexpr bool SELF = NORM && !DW;         // numerator waves form their own denominators
     constexpr bool DELAY = NORM && DW && !DEN;  // numerator waves divide one step later
-    using SQ = Stage<T, NT, C, E>;
+    // Q: with one row set per workgroup and row groups, only the rows of the
+    // workgroup's own row blocks are staged (K and V: every row, for the
+    // state update and the scores of earlier key blocks)
+    constexpr bool QOWN = RSPLIT == 1 && RS > 1;
+    constexpr int CQ = QOWN ? 16 * owned_count<CB, RS>(H) : C;
+    using SQ = Stage<T, NT, CQ, E, typename std::conditional<QOWN, OwnedRows<CB, RS, H>, AllRows>::type>;
+    using SK = Stage<T, NT, C, E>;
     using SV = Stage<T, NT, C, MW>;
-    constexpr int RQ = SQ::RS, RV = SV::RS;
+    constexpr int RQ = SK::RS, RV = SV::RS;
     constexpr int BUF = 2 * C * RQ + C * RV;  // Q, K, V columns of the group
     constexpr int JMAX = last_block<CB, RS>(H);  // key blocks this wave scores: J <= JMAX
     static_assert(!DEN || (NORM && DW), "the denominator wave belongs to the normalised form");
@@ -84,7 +90,8 @@ __device__ __forceinline__ void fwd_sweep(const T *q_, const T *k_, const T *v_,
     // computed.  The step loop is padded to a multiple of NPF; padded chunks
     // lie past re, load as zero and store nothing.
     struct Stages {
-        SQ q, k;
+        SQ q;
+        SK k;
         SV v;
     };
     const int col0 = 16 * grp * NW;
@@ -199,7 +206,7 @@ __device__ __forceinline__ void fwd_sweep(const T *q_, const T *k_, const T *v_,
                 if (!owns_block<CB, RS>(H, I)) continue;
                 RF qf[KS];
 #pragma unroll
-                for (int k = 0; k < KS; ++k) qf[k] = EO::load(Qs, RQ, I, k);
+                for (int k = 0; k < KS; ++k) qf[k] = EO::load(Qs, RQ, QOWN ? owned_index<CB, RS>(H, I) : I, k);
                 // inter-chunk: Out^T += S^T Q_I^T (denominator: z . q_i in every row)
                 f32x4 o = zero4(), d = zero4();
 #pragma unroll
