@@ -44,7 +44,7 @@
 #define CP_BF16_FRS 1
 #endif
 #ifndef CP_BF16_FNPF
-#define CP_BF16_FNPF 3
+#define CP_BF16_FNPF 4  // (3 before the forward staged only its own query rows)
 #endif
 #ifndef CP_BF16_BNPF
 #define CP_BF16_BNPF 4
