@@ -68,8 +68,48 @@ __device__ __forceinline__ float state_at(const float *s, int e, int m, int Ea, 
 // segment (seg = 0, nseg = 1).
 struct SegCarry {
     const float *dS, *dR;
-    int seg, nseg;
+    int seg, nseg, sub;  // sub: increment slots per segment (parts of the increment pass)
 };
+
+// The increment slots of a backward over sequence segments made cumulative,
+// in place, so that each sweep reads one slot per carried state instead of
+// summing a run of them: per slice (nslot slots of E*M + E floats), ws1 (the
+// prefix state's increments) becomes inclusive suffix sums over slots
+// [lo1, nslot) when the sweeps start from the final state (suffix1), else
+// inclusive prefix sums over [0, hi1); ws2 (the suffix state's increments)
+// inclusive suffix sums over [lo2, nslot).  One thread per 16-byte piece of
+// a slice's increment and per job.
+template <int E, int M>
+__global__ __launch_bounds__(256) void cp_seg_scan_kernel(float *__restrict__ ws1, float *__restrict__ ws2, int NS,
+                                                          int nslot, int lo1, int hi1, int suffix1, int lo2) {
+    constexpr int WS = E * M + E, NP = WS / 4;
+    static_assert(WS % 4 == 0, "whole 16-byte pieces");
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (t >= (int64_t)2 * NS * NP) return;
+    const bool second = t >= (int64_t)NS * NP;
+    const int64_t q = second ? t - (int64_t)NS * NP : t;
+    const int slice = (int)(q / NP), p = (int)(q % NP);
+    f32x4 *x = reinterpret_cast<f32x4 *>((second ? ws2 : ws1) + (int64_t)slice * nslot * WS) + p;
+    // slots [lo, hi) in scan order (downwards for suffix sums), eight at a
+    // time: the eight loads are issued together, then summed and stored
+    const bool down = second || suffix1;
+    const int lo = down ? (second ? lo2 : lo1) : 0, hi = down ? nslot : hi1;
+    f32x4 acc = zero4();
+    for (int b = 0; b < hi - lo; b += 8) {
+        f32x4 v[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int s = down ? hi - 1 - (b + i) : lo + b + i;
+            v[i] = b + i < hi - lo ? x[(int64_t)s * NP] : zero4();
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int s = down ? hi - 1 - (b + i) : lo + b + i;
+            acc += v[i];
+            if (b + i < hi - lo) x[(int64_t)s * NP] = acc;
+        }
+    }
+}
 
 // The slice's three outputs (dQ, dK: E columns; dV: M columns), for the copy
 // waves that store the workgroup's staged output rows (OUTLDS in bwd_sweep).
@@ -227,12 +267,14 @@ __device__ __forceinline__ void bwd_sweep(const T *q_, const T *k_, const T *v_,
             const int64_t off = zpart ? e : (int64_t)e * Ma + m;
             const bool in = e < Ea && m < Ma;
             f32x4 a = zero4();
-            if (use_final) {  // (only ever with end)
+            // the slots hold cumulative sums (cp_seg_scan_kernel): one read each
+            if (use_final) {  // (only ever with end) minus the later segments' sum
                 if (in) a = *reinterpret_cast<const f32x4 *>(st_ + off);
-                for (int s = sc.seg + 1; s < sc.nseg; ++s) a -= *reinterpret_cast<const f32x4 *>(sc.dS + s * WS + widx);
-            } else {
+                const int s1 = (sc.seg + 1) * sc.sub;
+                if (s1 < sc.nseg * sc.sub) a -= *reinterpret_cast<const f32x4 *>(sc.dS + s1 * WS + widx);
+            } else {  // plus the earlier segments' sum
                 if (s0_ && in) a = *reinterpret_cast<const f32x4 *>(s0_ + off);
-                for (int s = 0; s < upto; ++s) a += *reinterpret_cast<const f32x4 *>(sc.dS + s * WS + widx);
+                if (upto > 0) a += *reinterpret_cast<const f32x4 *>(sc.dS + (upto * sc.sub - 1) * WS + widx);
             }
             *reinterpret_cast<f32x4 *>(zpart ? zvec + e : tile + e * TS + m) = a;
         }
@@ -257,8 +299,7 @@ __device__ __forceinline__ void bwd_sweep(const T *q_, const T *k_, const T *v_,
                 const bool zpart = p >= E * M / 4;
                 const int e = zpart ? 4 * (p - E * M / 4) : p / (M / 4), m = zpart ? 0 : p % (M / 4) * 4;
                 const int widx = zpart ? E * M + e : e * M + m;
-                f32x4 a = zero4();
-                for (int s = sc.seg + 1; s < sc.nseg; ++s) a += *reinterpret_cast<const f32x4 *>(sc.dR + s * WS + widx);
+                const f32x4 a = *reinterpret_cast<const f32x4 *>(sc.dR + (sc.seg + 1) * sc.sub * WS + widx);
                 *reinterpret_cast<f32x4 *>(zpart ? zvec + e : tile + e * TS + m) = a;
             }
             __syncthreads();
@@ -815,7 +856,7 @@ __global__ __launch_bounds__((64 * bwd_waves<E, M, G, NB, IDLE>())) void cp_bwd_
     const float *__restrict__ state_in, const float *__restrict__ state_final, const T *__restrict__ O,
     const float *__restrict__ den, const float *__restrict__ z_in, const float *__restrict__ z_final,
     T *__restrict__ dQ, T *__restrict__ dK, T *__restrict__ dV, float *__restrict__ dstate_in,
-    float *__restrict__ dz_in, const float *__restrict__ ws, int L, int NS, int seg_len, int Ea, int Ma) {
+    float *__restrict__ dz_in, const float *__restrict__ ws, int L, int NS, int seg_len, int sub, int Ea, int Ma) {
     constexpr int EB = E / 16, MB = M / 16;
     // with several blocks per wave every wave's blocks all exist
     static_assert(NB == 1 || (EB % (G * NB) == 0 && MB % (G * NB) == 0), "blocks per wave");
@@ -861,8 +902,8 @@ __global__ __launch_bounds__((64 * bwd_waves<E, M, G, NB, IDLE>())) void cp_bwd_
     float *ds0 = dstate_in && seg == 0 ? dstate_in + os : nullptr;
     float *dz0 = dz_in && seg == 0 ? dz_in + (int64_t)slice * Ea : nullptr;
     constexpr int WS = E * M + E;
-    const SegCarry sc{ws ? ws + (int64_t)slice * nseg * WS : nullptr,
-                      ws ? ws + ((int64_t)NS + slice) * nseg * WS : nullptr, seg, nseg};
+    const SegCarry sc{ws ? ws + (int64_t)slice * nseg * sub * WS : nullptr,
+                      ws ? ws + ((int64_t)NS + slice) * nseg * sub * WS : nullptr, seg, nseg, sub};
     const int Ls = re - rb;
     // wave w: role, and the first of its NB column blocks (b, b + G, ...)
     const int role = w < EG ? kDQ : w < 2 * EG ? kDK : w < 2 * EG + MG ? kDV : kIdle;

@@ -8,6 +8,10 @@
 #include "cp_launch.hpp"
 #include "cp_tune.hpp"
 
+#ifndef CP_BWD_SEG_SUB
+#define CP_BWD_SEG_SUB 2
+#endif
+
 namespace cp {
 
 // One kernel per call, no scratch, when the slices fill the GPU.  The
@@ -39,8 +43,14 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t s) {
     const int nseg = plan.nseg;
     int seg_len = plan.seg_len;
     constexpr int WS = E * M + E;
-    // prefix then suffix increments: per slice and segment E x M then E floats each
-    const size_t need = nseg > 1 ? (size_t)2 * NS * nseg * WS * sizeof(float) : 0;
+    // parts per segment increment: two for the normalised form where the
+    // increment pass's two jobs would leave CUs idle (its second job, which
+    // also reads the output and forms dn and dd, is the longer one; the
+    // causal product's two jobs are even, and a second part costs it more
+    // than it gains)
+    int sub = NORM && nseg > 1 && (long long)2 * (nseg - 1) * NS < kCUs ? CP_BWD_SEG_SUB : 1;
+    // prefix then suffix increments: per slice, segment and part E x M then E floats each
+    const size_t need = nseg > 1 ? (size_t)2 * NS * nseg * sub * WS * sizeof(float) : 0;
     if (a.ws_need) {
         *a.ws_need = need;
         return hipSuccess;
@@ -60,18 +70,26 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t s) {
         // with the final states used, the sweeps subtract the later segments'
         // increments from them: the prefix increments of segments 1 .. nseg-1
         const bool use_final = st && (!NORM || zf) && !(NORM && std::is_same<T, float>::value);
-        const SegArgs sa{k,  v,  ws,      q,  g,  o,  den, ws + (size_t)NS * nseg * WS, L, NS, seg_len,
-                         use_final ? 1 : 0, Ea, Ma, NORM, FMAP};
+        const SegArgs sa{k,  v,  ws,      q,  g,  o,  den, ws + (size_t)NS * nseg * sub * WS, L, NS, seg_len,
+                         sub, use_final ? 1 : 0, Ea, Ma, NORM, FMAP};
         const seg_fn fn = std::is_same<T, float>::value ? seg_f32(E, M)
                           : std::is_same<T, __bf16>::value ? seg_bf16(E, M)
                                                            : seg_f16(E, M);
         e = fn ? fn(sa, s) : hipErrorInvalidValue;
+        if (e == hipSuccess) {  // the slots made cumulative for the sweeps
+            float *w1 = ws, *w2 = ws + (size_t)NS * nseg * sub * WS;
+            int ns = NS, nslot = nseg * sub, lo1 = sub, hi1 = (nseg - 1) * sub, sfx = use_final ? 1 : 0, lo2 = sub;
+            void *sargs[] = {&w1, &w2, &ns, &nslot, &lo1, &hi1, &sfx, &lo2};
+            const long long threads = 2LL * NS * (WS / 4);
+            e = launch_kernel(reinterpret_cast<const void *>(cp_seg_scan_kernel<E, M>),
+                              dim3((unsigned)((threads + 255) / 256)), dim3(256), sargs, s);
+        }
     }
     if (e == hipSuccess) {
         const float *wsc = ws;
         auto kern = cp_bwd_kernel<T, E, M, C, P::BG, P::BNB, P::BIDLE, P::BRG, NORM ? P::BNPF_N : P::BNPF, NORM, FMAP>;
-        void *args[] = {&q,   &k,   &v,  &g,  &s0, &st, &o,  &den, &z0, &zf, &dq,     &dk,
-                        &dv,  &ds0, &dz0, &wsc, &L, &NS, &seg_len, &Ea, &Ma};
+        void *args[] = {&q,  &k,   &v,   &g,   &s0, &st, &o,  &den,     &z0,  &zf, &dq,
+                        &dk, &dv,  &ds0, &dz0, &wsc, &L, &NS, &seg_len, &sub, &Ea, &Ma};
         e = launch_kernel(reinterpret_cast<const void *>(kern), dim3(NS * P::BG * P::BRG * nseg),
                           dim3(64 * bwd_waves<E, M, P::BG, P::BNB, P::BIDLE>()), args, s);
     }

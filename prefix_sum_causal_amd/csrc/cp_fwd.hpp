@@ -312,13 +312,21 @@ __device__ __forceinline__ void fwd_sweep(const T *q_, const T *k_, const T *v_,
 // with dn_i = dO_i / den_i and dd_i = -(dO_i . out_i) / den_i formed while dO
 // is staged (O2, den2: the forward's output and denominators), dd entering
 // the product K2^T dd as a hi + lo pair of operands.
+//
+// Each segment's increment may be computed in sub parts (consecutive runs of
+// whole chunks, the last ones possibly empty) by as many workgroups, into
+// consecutive slots: slot seg * sub + u of the slice holds part u of segment
+// seg, and a consumer sums the slots of the segments it needs.  (Over few
+// slices the increment pass has fewer workgroups than CUs, and the normalised
+// backward's second job, which also reads the output and forms dn and dd,
+// takes longer than the first: finer parts keep every CU busy.)
 template <typename T, int E, int M, int C, int NW, int NPF, bool NORM, bool FMAP>
 __global__ __launch_bounds__(64 * NW) void cp_seg_state_kernel(const T *__restrict__ K1, const T *__restrict__ V1,
                                                                float *__restrict__ ws1, const T *__restrict__ K2,
                                                                const T *__restrict__ V2, const T *__restrict__ O2,
                                                                const float *__restrict__ den2,
                                                                float *__restrict__ ws2, int L, int NS, int seg_len,
-                                                               int first1, int Ea, int Ma) {
+                                                               int sub, int first1, int Ea, int Ma) {
     using O = Ops<T>;
     using F = typename O::frag;
     using EO = EOps<T, E>;
@@ -335,18 +343,24 @@ __global__ __launch_bounds__(64 * NW) void cp_seg_state_kernel(const T *__restri
     constexpr int ZT = (EB + NW - 1) / NW;
     __shared__ __attribute__((aligned(16))) lds_t<T> lds[2 * BUF + DDE];
 
-    const int nseg = (L + seg_len - 1) / seg_len;
+    const int nseg = (L + seg_len - 1) / seg_len, nparts = (nseg - 1) * sub;  // parts per job
     int slice, part;
-    map_block(blockIdx.x, NS, (K2 ? 2 : 1) * (nseg - 1), slice, part);
-    const bool second = part >= nseg - 1;
-    const int seg = second ? part - (nseg - 1) + 1 : part + first1;
+    map_block(blockIdx.x, NS, (K2 ? 2 : 1) * nparts, slice, part);
+    const bool second = part >= nparts;
+    const int pj = second ? part - nparts : part;
+    const int seg = (second ? 1 : first1) + pj / sub, u = pj % sub;
     const T *K = second ? K2 : K1, *V = second ? V2 : V1;
     float *ws = second ? ws2 : ws1;
     const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
     const int g = lane_g(), r = lane_r();
     const T *k_ = K + (int64_t)slice * L * Ea;
     const T *v_ = V + (int64_t)slice * L * Ma;
-    const int rb = seg * seg_len, re = rb + seg_len < L ? rb + seg_len : L;
+    // part u of the segment: a run of whole chunks of this kernel's C (the
+    // segment length is a multiple of the sweep's chunk, which may be
+    // shorter), cut at the segment's end and empty past it
+    const int send = seg * seg_len + seg_len < L ? seg * seg_len + seg_len : L;
+    const int plen = ((seg_len + C - 1) / C + sub - 1) / sub * C, pb = seg * seg_len + u * plen;
+    const int rb = pb < send ? pb : send, re = pb + plen < send ? pb + plen : send;
     // normalised second job: dn and dd from dO (v_), the output and den
     const bool dnj = NORM && second;
     NormIn<T> nin{nullptr, nullptr, nullptr, nullptr};
@@ -450,7 +464,7 @@ __global__ __launch_bounds__(64 * NW) void cp_seg_state_kernel(const T *__restri
             }
         }
     }
-    float *dS = ws + ((int64_t)slice * nseg + seg) * WS, *dz = dS + E * M;
+    float *dS = ws + (((int64_t)slice * nseg + seg) * sub + u) * WS, *dz = dS + E * M;
 #pragma unroll
     for (int x = 0; x < CW; ++x)
 #pragma unroll

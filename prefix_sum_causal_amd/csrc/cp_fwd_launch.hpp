@@ -50,8 +50,8 @@ hipError_t launch_fwd_t(const FwdArgs &a, hipStream_t s) {
         const T *none = nullptr;
         const float *noden = nullptr;
         float *nows = nullptr;
-        int first1 = 0;
-        void *args1[] = {&k, &v, &ws, &none, &none, &none, &noden, &nows, &L, &NS, &seg_len, &first1, &Ea, &Ma};
+        int first1 = 0, sub = 1;
+        void *args1[] = {&k, &v, &ws, &none, &none, &none, &noden, &nows, &L, &NS, &seg_len, &sub, &first1, &Ea, &Ma};
         e = launch_kernel(reinterpret_cast<const void *>(k1), dim3(NS * (nseg - 1)), dim3(64 * SW), args1, s);
     }
     if (e == hipSuccess) {
@@ -97,13 +97,13 @@ hipError_t launch_seg_nf(const SegArgs &a, hipStream_t s) {
     const T *k2 = static_cast<const T *>(a.K2), *v2 = static_cast<const T *>(a.V2), *o2 = static_cast<const T *>(a.O2);
     const float *den2 = a.den2;
     float *ws1 = a.ws1, *ws2 = a.ws2;
-    int L = a.L, NS = a.NS, seg_len = a.seg_len, first1 = a.first1, Ea = a.Ea, Ma = a.Ma;
+    int L = a.L, NS = a.NS, seg_len = a.seg_len, sub = a.sub, first1 = a.first1, Ea = a.Ea, Ma = a.Ma;
     const int nseg = (L + seg_len - 1) / seg_len;
     constexpr int SW = seg_state_waves<M>();
     auto kern = cp_seg_state_kernel<T, E, M, P::FC, SW, CP_SEG_NPF, NORM, FMAP>;
-    void *args[] = {&k1, &v1, &ws1, &k2, &v2, &o2, &den2, &ws2, &L, &NS, &seg_len, &first1, &Ea, &Ma};
-    return launch_kernel(reinterpret_cast<const void *>(kern), dim3(NS * (k2 ? 2 : 1) * (nseg - 1)), dim3(64 * SW),
-                         args, s);
+    void *args[] = {&k1, &v1, &ws1, &k2, &v2, &o2, &den2, &ws2, &L, &NS, &seg_len, &sub, &first1, &Ea, &Ma};
+    return launch_kernel(reinterpret_cast<const void *>(kern), dim3(NS * (k2 ? 2 : 1) * (nseg - 1) * sub),
+                         dim3(64 * SW), args, s);
 }
 
 template <typename T, int E, int M>

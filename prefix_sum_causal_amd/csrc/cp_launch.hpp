@@ -83,7 +83,7 @@ struct SegArgs {
     const void *K2, *V2, *O2;
     const float *den2;
     float *ws2;
-    int L, NS, seg_len, first1, Ea, Ma;
+    int L, NS, seg_len, sub, first1, Ea, Ma;  // sub: parts (workgroups, slots) per segment increment
     bool norm, fmap;
 };
 typedef hipError_t (*seg_fn)(const SegArgs &, hipStream_t);
