@@ -42,7 +42,10 @@ SWEEP_KERNEL = {"fwd": "cp_fwd_kernel", "bwd": "cp_bwd_kernel", "linattn": "cp_f
 
 
 def kernel_name(kind: str, launches: int) -> str:
-    return SWEEP_KERNEL[kind] if launches == 1 else "cp_seg_state_kernel + " + SWEEP_KERNEL[kind]
+    """The kernels of one call: the sweep, after the segment-increment pass
+    (over few slices) and, in the backward, the scan of its increments."""
+    before = {1: [], 2: ["cp_seg_state_kernel"], 3: ["cp_seg_state_kernel", "cp_seg_scan_kernel"]}[launches]
+    return " + ".join(before + [SWEEP_KERNEL[kind]])
 
 
 def kernel_digest() -> str:
