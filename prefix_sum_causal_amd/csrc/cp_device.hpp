@@ -651,6 +651,47 @@ struct OwnedRows {
     }
 };
 
+// The increment slots of a call over sequence segments made cumulative, in
+// place, so that each sweep reads one slot per carried state instead of
+// summing a run of them: per slice (nslot slots of E*M + E floats), ws1 (the
+// prefix state's increments) becomes inclusive suffix sums over slots
+// [lo1, nslot) when the sweeps start from the final state (suffix1), else
+// inclusive prefix sums over [0, hi1); with a second job (ws2, the
+// backward's suffix state's increments) inclusive suffix sums over
+// [lo2, nslot).  One thread per 16-byte piece of a slice's increment and per
+// job.
+template <int E, int M>
+__global__ __launch_bounds__(256) void cp_seg_scan_kernel(float *__restrict__ ws1, float *__restrict__ ws2, int NS,
+                                                          int nslot, int lo1, int hi1, int suffix1, int lo2) {
+    constexpr int WS = E * M + E, NP = WS / 4;
+    static_assert(WS % 4 == 0, "whole 16-byte pieces");
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (t >= (ws2 ? 2 : 1) * (int64_t)NS * NP) return;
+    const bool second = t >= (int64_t)NS * NP;
+    const int64_t q = second ? t - (int64_t)NS * NP : t;
+    const int slice = (int)(q / NP), p = (int)(q % NP);
+    f32x4 *x = reinterpret_cast<f32x4 *>((second ? ws2 : ws1) + (int64_t)slice * nslot * WS) + p;
+    // slots [lo, hi) in scan order (downwards for suffix sums), eight at a
+    // time: the eight loads are issued together, then summed and stored
+    const bool down = second || suffix1;
+    const int lo = down ? (second ? lo2 : lo1) : 0, hi = down ? nslot : hi1;
+    f32x4 acc = zero4();
+    for (int b = 0; b < hi - lo; b += 8) {
+        f32x4 v[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int s = down ? hi - 1 - (b + i) : lo + b + i;
+            v[i] = b + i < hi - lo ? x[(int64_t)s * NP] : zero4();
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int s = down ? hi - 1 - (b + i) : lo + b + i;
+            acc += v[i];
+            if (b + i < hi - lo) x[(int64_t)s * NP] = acc;
+        }
+    }
+}
+
 // Workgroup id -> (slice, part).  The P parts of one (n, h) slice read the
 // same rows of the inputs, so they are kept on one XCD (workgroups are
 // dispatched to the 8 XCDs round robin by id) where they share its L2.

@@ -509,7 +509,7 @@ __global__ __launch_bounds__((64 * fwd_waves<M, G, RSPLIT, NORM && DW>())) void 
     const T *__restrict__ Q, const T *__restrict__ K, const T *__restrict__ V, T *__restrict__ Out,
     const float *__restrict__ state_in, const float *__restrict__ z_in, float *__restrict__ state_out,
     float *__restrict__ z_out, float *__restrict__ den, const float *__restrict__ ws, int L, int NS, int seg_len,
-    float eps, int Ea, int Ma) {
+    int cum, float eps, int Ea, int Ma) {
     using EO = EOps<T, E>;
     constexpr int EB = E / 16, MB = M / 16, CB = C / 16;
     static_assert(MB % G == 0, "column groups split the column blocks evenly");
@@ -566,7 +566,8 @@ __global__ __launch_bounds__((64 * fwd_waves<M, G, RSPLIT, NORM && DW>())) void 
             S[e][t] = x;
             z[e][t] = SELFZ && z0 && row < Ea ? z0[row] : 0.f;
         }
-    for (int p = 0; p < seg; ++p) {
+    // cum: the slots hold inclusive prefix sums (cp_seg_scan_kernel), one read
+    for (int p = cum && seg > 0 ? seg - 1 : 0; p < seg; ++p) {
         const float *inc = ws_slice + (int64_t)p * WS;
 #pragma unroll
         for (int e = 0; e < EB; ++e)

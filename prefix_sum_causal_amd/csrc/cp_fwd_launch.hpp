@@ -6,6 +6,10 @@
 #include "cp_launch.hpp"
 #include "cp_tune.hpp"
 
+#ifndef CP_FWD_SCAN_MIN_SEGS
+#define CP_FWD_SCAN_MIN_SEGS 12
+#endif
+
 namespace cp {
 
 template <typename T, int E, int M, bool NORM, bool FMAP>
@@ -26,6 +30,9 @@ hipError_t launch_fwd_t(const FwdArgs &a, hipStream_t s) {
     const SegPlan plan = plan_segments(L, NS, P::FG * FRG, P::FC);
     const int nseg = plan.nseg;
     int seg_len = plan.seg_len;
+    // many segments: their increments scanned once rather than summed by
+    // every sweep (a third launch, which a call of few segments does not repay)
+    int cum = nseg >= CP_FWD_SCAN_MIN_SEGS ? 1 : 0;
     // per slice and segment: the E x M increment of the state, then E of z
     const size_t need = nseg > 1 ? (size_t)NS * nseg * (E * M + E) * sizeof(float) : 0;
     if (a.ws_need) {
@@ -53,10 +60,17 @@ hipError_t launch_fwd_t(const FwdArgs &a, hipStream_t s) {
         int first1 = 0, sub = 1;
         void *args1[] = {&k, &v, &ws, &none, &none, &none, &noden, &nows, &L, &NS, &seg_len, &sub, &first1, &Ea, &Ma};
         e = launch_kernel(reinterpret_cast<const void *>(k1), dim3(NS * (nseg - 1)), dim3(64 * SW), args1, s);
+        if (e == hipSuccess && cum) {  // inclusive prefix sums of the slots: one read per sweep
+            int nslot = nseg, lo1 = 0, hi1 = nseg - 1, sfx = 0, lo2 = 0;
+            void *sargs[] = {&ws, &nows, &NS, &nslot, &lo1, &hi1, &sfx, &lo2};
+            const long long threads = (long long)NS * ((E * M + E) / 4);
+            e = launch_kernel(reinterpret_cast<const void *>(cp_seg_scan_kernel<E, M>),
+                              dim3((unsigned)((threads + 255) / 256)), dim3(256), sargs, s);
+        }
     }
     if (e == hipSuccess) {
         auto k2 = cp_fwd_kernel<T, E, M, P::FC, P::FG, FRS, FRG, P::FNPF, NORM, FMAP, DW>;
-        void *args2[] = {&q, &k, &v, &o, &s0, &z0, &st, &zt, &dn, &ws, &L, &NS, &seg_len, &eps, &Ea, &Ma};
+        void *args2[] = {&q, &k, &v, &o, &s0, &z0, &st, &zt, &dn, &ws, &L, &NS, &seg_len, &cum, &eps, &Ea, &Ma};
         e = launch_kernel(reinterpret_cast<const void *>(k2), dim3(NS * P::FG * FRG * nseg), block, args2, s);
     }
     if (owned) {
